@@ -1,0 +1,293 @@
+/*
+ * qwg oracle: plain, slow CPU reference. TEST INFRASTRUCTURE ONLY (see
+ * qwg_oracle.h): only tests/, __graft_entry__.smoke() and bench.py's
+ * cpu_baseline leg use it; the HIP library never does.
+ *
+ * Built with -O2 -ffp-contract=off and no fast-math, so every fp32 operation
+ * below is one IEEE round-to-nearest-even operation in the order written.
+ *
+ * Citations name the page and the listing or passage on it:
+ *   [picoLM]  "用 Python 重写 picoLM", dequantize_q4_K listing
+ *   [iq3pack] iq3_pack.py page: module docstring (byte layout) and decode()
+ */
+#include "qwg_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ fp16 */
+
+/*
+ * IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ * e == 0: subnormal, value = m * 2^-24.  e == 31: infinity or NaN.
+ * Otherwise (1024 + m) * 2^(e - 25). Evaluated in double, where every binary16
+ * value is exact, then narrowed to float, where it is exact as well.
+ * [picoLM] reads d and dmin as fp16 fields; [iq3pack] reads d as fp16.
+ */
+float orc_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* ------------------------------------------------------------------ Q4_K */
+
+/*
+ * [picoLM] scale unpack: for sub-block j < 4 the scale is the low six bits of
+ * packed byte j and the min the low six bits of byte j+4. For j >= 4 the
+ * six-bit fields straddle bytes: the low four bits come from byte j+4 (low
+ * nibble for the scale, high nibble for the min) and the top two bits from bits
+ * 6..7 of byte j-4 (scale) or byte j (min).
+ */
+void orc_q4k_unpack_scales(const uint8_t p[12], uint8_t sc[8], uint8_t mn[8])
+{
+    for (int j = 0; j < 8; ++j) {
+        if (j < 4) {
+            sc[j] = p[j] & 63;
+            mn[j] = p[j + 4] & 63;
+        } else {
+            sc[j] = (uint8_t)((p[j + 4] & 0xF) | ((p[j - 4] >> 6) << 4));
+            mn[j] = (uint8_t)((p[j + 4] >> 4) | ((p[j] >> 6) << 4));
+        }
+    }
+}
+
+/*
+ * The inverse of the unpack above (the page prints only the unpack). Each of
+ * the 96 bits of p is written by exactly one field bit, so this is the unique
+ * preimage: bytes 0..3 carry sc[0..3] plus the top two bits of sc[4..7], bytes
+ * 4..7 carry mn[0..3] plus the top two bits of mn[4..7], bytes 8..11 carry the
+ * low nibbles of sc[4..7] (low half) and mn[4..7] (high half).
+ */
+void orc_q4k_pack_scales(const uint8_t sc[8], const uint8_t mn[8], uint8_t p[12])
+{
+    for (int j = 0; j < 4; ++j) {
+        p[j] = (uint8_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
+        p[j + 4] = (uint8_t)((mn[j] & 63) | ((mn[j + 4] >> 4) << 6));
+        p[j + 8] = (uint8_t)((sc[j + 4] & 15) | ((mn[j + 4] & 15) << 4));
+    }
+}
+
+/*
+ * [picoLM] one block: d = fp16 at bytes 0..1, dmin = fp16 at bytes 2..3, the
+ * packed scales at bytes 4..15, 128 quant bytes at 16..143. The quants form four
+ * 32-byte chunks; chunk c holds weights 64c..64c+31 in its low nibbles (sub-block
+ * 2c) and weights 64c+32..64c+63 in its high nibbles (sub-block 2c+1).
+ * Weight value, in fp32 and in this order: (d * sc_j) * q - dmin * mn_j.
+ */
+static void q4k_block(const uint8_t *b, float *out)
+{
+    float d = orc_f16_to_f32((uint16_t)(b[0] | (b[1] << 8)));
+    float dmin = orc_f16_to_f32((uint16_t)(b[2] | (b[3] << 8)));
+    uint8_t sc[8], mn[8];
+    orc_q4k_unpack_scales(b + 4, sc, mn);
+    const uint8_t *qs = b + 16;
+    for (int i = 0; i < ORC_QK; ++i) {
+        int j = i / 32;         /* sub-block */
+        int c = i / 64;         /* 32-byte chunk */
+        uint8_t byte = qs[32 * c + i % 32];
+        int q = (j % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+        float t = (d * (float)sc[j]) * (float)q;
+        float u = dmin * (float)mn[j];
+        out[i] = t - u;
+    }
+}
+
+int orc_dequant_q4k(const uint8_t *src, int64_t n, float *dst)
+{
+    if (!src || !dst)
+        return 1;
+    if (n < 0 || n % ORC_QK)
+        return 2;
+    for (int64_t ib = 0; ib < n / ORC_QK; ++ib)
+        q4k_block(src + ORC_Q4K_BYTES * ib, dst + ORC_QK * ib);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ IQ3 */
+
+/*
+ * [iq3pack] one block: bytes 0..63 are grid indices (one per 4 weights), bytes
+ * 64..95 eight little-endian uint32 words (one per 32-weight sub-block), bytes
+ * 96..97 the fp16 super-scale d. In word ib, bits 7l..7l+6 (l = 0..3) are the
+ * signs of weights 8l..8l+6 of the sub-block (bit set = negative), the sign of
+ * weight 8l+7 is the XOR of those seven bits, and bits 28..31 are the sub-scale
+ * code. Sub-block scale db = d * (0.5 + code) * 0.5, and weight t of sub-block ib
+ * is grid[idx[8ib + t/4]][t % 4] * sign_t * db, with the grid in weight units.
+ * decode() forms db in double (0.5 + an integer promotes), multiplies
+ * magnitude by sign in fp32 and stores the double product as fp32; this does the
+ * same.
+ */
+static void iq3_block(const uint8_t *b, const float *grid, float *out)
+{
+    double d = orc_f16_to_f32((uint16_t)(b[96] | (b[97] << 8)));
+    for (int ib = 0; ib < 8; ++ib) {
+        const uint8_t *wp = b + 64 + 4 * ib;
+        uint32_t word = (uint32_t)wp[0] | ((uint32_t)wp[1] << 8) | ((uint32_t)wp[2] << 16) |
+                        ((uint32_t)wp[3] << 24);
+        uint32_t code = (word >> 28) & 0xF;
+        double db = d * (0.5 + (double)code) * 0.5;
+        float sgn[32];
+        for (int l = 0; l < 4; ++l) {
+            uint32_t seven = (word >> (7 * l)) & 0x7F;
+            int par = 0;
+            for (int j = 0; j < 7; ++j) {
+                int bit = (seven >> j) & 1;
+                sgn[8 * l + j] = bit ? -1.0f : 1.0f;
+                par ^= bit;
+            }
+            sgn[8 * l + 7] = par ? -1.0f : 1.0f;
+        }
+        for (int t = 0; t < 32; ++t) {
+            int idx = b[8 * ib + t / 4];
+            float mag = grid[4 * idx + t % 4];
+            float ms = mag * sgn[t];
+            out[32 * ib + t] = (float)((double)ms * db);
+        }
+    }
+}
+
+int orc_dequant_iq3(const uint8_t *src, const float *grid, int64_t n, float *dst)
+{
+    if (!src || !grid || !dst)
+        return 1;
+    if (n < 0 || n % ORC_QK)
+        return 2;
+    for (int64_t ib = 0; ib < n / ORC_QK; ++ib)
+        iq3_block(src + ORC_IQ3_BYTES * ib, grid, dst + ORC_QK * ib);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ GEMV / GEMM */
+
+static int g_threads = 0;
+
+void orc_set_threads(int n) { g_threads = n; }
+
+int orc_get_threads(void)
+{
+#ifdef _OPENMP
+    return g_threads > 0 ? g_threads : omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* One row: dequantize all of it to fp32, then fp64 dot products against each of
+ * `batch` activation rows, k ascending. */
+static void row_dot(const float *wrow, const float *x, int64_t n_in, int batch, int64_t n_out,
+                    int64_t row, double *y, double *s)
+{
+    for (int bt = 0; bt < batch; ++bt) {
+        const float *xb = x + (int64_t)bt * n_in;
+        double acc = 0.0, abs_acc = 0.0;
+        for (int64_t k = 0; k < n_in; ++k) {
+            double p = (double)wrow[k] * (double)xb[k];
+            acc += p;
+            abs_acc += fabs(p);
+        }
+        y[(int64_t)bt * n_out + row] = acc;
+        if (s)
+            s[(int64_t)bt * n_out + row] = abs_acc;
+    }
+}
+
+typedef void (*block_fn)(const uint8_t *, const float *, float *);
+
+static void q4k_block_g(const uint8_t *b, const float *grid, float *out)
+{
+    (void)grid;
+    q4k_block(b, out);
+}
+
+/* rows == NULL: all n_out rows, outputs indexed by row. Otherwise output i is
+ * row rows[i]. */
+static int gemm_generic(block_fn fn, int nbytes, const uint8_t *w, const float *grid,
+                        const float *x, int64_t n_in, int64_t n_out, int batch,
+                        const int64_t *rows, int64_t nrows, double *y, double *s)
+{
+    if (!w || !x || !y)
+        return 1;
+    if (n_in <= 0 || n_in % ORC_QK || n_out < 1 || batch < 1 || batch > 8)
+        return 2;
+    const int64_t nb = n_in / ORC_QK;
+    const int64_t row_bytes = nb * nbytes;
+    const int64_t count = rows ? nrows : n_out;
+    const int64_t out_stride = rows ? nrows : n_out;
+    int nth = orc_get_threads();
+    int err = 0;
+#pragma omp parallel num_threads(nth)
+    {
+        float *buf = (float *)malloc(sizeof(float) * (size_t)n_in);
+        if (!buf) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t i = 0; i < count; ++i) {
+                int64_t r = rows ? rows[i] : i;
+                const uint8_t *wr = w + r * row_bytes;
+                for (int64_t ib = 0; ib < nb; ++ib)
+                    fn(wr + ib * nbytes, grid, buf + ib * ORC_QK);
+                row_dot(buf, x, n_in, batch, out_stride, i, y, s);
+            }
+            free(buf);
+        }
+    }
+    return err ? 3 : 0;
+}
+
+int orc_gemv_q4k(const uint8_t *w, const float *x, int64_t n_in, int64_t n_out, double *y,
+                 double *s)
+{
+    return gemm_generic(q4k_block_g, ORC_Q4K_BYTES, w, NULL, x, n_in, n_out, 1, NULL, 0, y, s);
+}
+
+int orc_gemv_iq3(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                 int64_t n_out, double *y, double *s)
+{
+    if (!grid)
+        return 1;
+    return gemm_generic(iq3_block, ORC_IQ3_BYTES, w, grid, x, n_in, n_out, 1, NULL, 0, y, s);
+}
+
+int orc_gemm_q4k(const uint8_t *w, const float *x, int64_t n_in, int64_t n_out, int batch,
+                 double *y, double *s)
+{
+    return gemm_generic(q4k_block_g, ORC_Q4K_BYTES, w, NULL, x, n_in, n_out, batch, NULL, 0, y,
+                        s);
+}
+
+int orc_gemv_q4k_rows(const uint8_t *w, const float *x, int64_t n_in, const int64_t *rows,
+                      int64_t nrows, double *y, double *s)
+{
+    if (!rows)
+        return 1;
+    if (nrows < 1)
+        return 2;
+    /* n_out only bounds the batch stride here; rows are trusted to be in range. */
+    return gemm_generic(q4k_block_g, ORC_Q4K_BYTES, w, NULL, x, n_in, 1, 1, rows, nrows, y, s);
+}
+
+int orc_gemv_iq3_rows(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                      const int64_t *rows, int64_t nrows, double *y, double *s)
+{
+    if (!rows || !grid)
+        return 1;
+    if (nrows < 1)
+        return 2;
+    return gemm_generic(iq3_block, ORC_IQ3_BYTES, w, grid, x, n_in, 1, 1, rows, nrows, y, s);
+}

@@ -1,0 +1,375 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test checks the oracle against something the pages or the mathematics fix:
+hand-expanded blocks (tests/golden/), closed forms, exhaustive enumerations,
+library routines for the special cases that reduce to them (numpy's binary16
+conversion, numpy's fp64 matmul), and structural invariants of a matrix-vector
+product. Together they are chosen so that a dropped term, a wrong sign, a wrong
+bit or byte index, or a transposed operand in the oracle fails at least one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from golden_io import floats, hexbytes, ints, load
+from quantized_weight_decode_gemv_amd import synth
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+# ---------------------------------------------------------------- constants
+
+def test_block_sizes_and_density():
+    # "用 Python 重写 picoLM", dequantize_q4_K docstring: 144 bytes, 256 weights, 4.5 bpw.
+    assert 2 + 2 + 12 + 128 == oracle.Q4K_BYTES == 144
+    assert oracle.Q4K_BYTES * 8 / oracle.QK == 4.5
+    # iq3_pack.py: 64 index bytes + 8 words + fp16 d = 98 bytes, 3.0625 bpw.
+    assert 256 // 4 + (256 // 32) * 4 + 2 == oracle.IQ3_BYTES == 98
+    assert oracle.IQ3_BYTES * 8 / oracle.QK == 3.0625
+
+
+# ---------------------------------------------------------------- fp16
+
+def test_f16_known_values():
+    cases = {0x3C00: 1.0, 0x3800: 0.5, 0x4000: 2.0, 0xC000: -2.0, 0x7BFF: 65504.0,
+             0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24, 0x0400: 2.0 ** -14,
+             0x2C00: 0.0625, 0x3400: 0.25, 0x3555: 0.333251953125}
+    for bits, val in cases.items():
+        assert oracle.f16_to_f32(bits) == val, hex(bits)
+    assert np.signbit(oracle.f16_to_f32(0x8000)) and oracle.f16_to_f32(0x8000) == 0.0
+    assert oracle.f16_to_f32(0x7C00) == np.inf and oracle.f16_to_f32(0xFC00) == -np.inf
+    assert np.isnan(oracle.f16_to_f32(0x7E00))
+
+
+def test_f16_all_patterns_match_numpy():
+    # numpy's binary16 -> binary32 widening is a library routine for the same definition.
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.f16_to_f32(int(b)) for b in bits], np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+# ---------------------------------------------------------------- Q4_K scales
+
+@pytest.mark.parametrize("name", ["q4k_block_A.txt", "q4k_block_C.txt"])
+def test_q4k_scale_unpack_hand(name):
+    g = load(name)
+    head = hexbytes(g["head"])
+    sc, mn = oracle.unpack_q4k_scales(np.array(head[4:16], np.uint8))
+    assert list(sc) == ints(g["sc"])
+    assert list(mn) == ints(g["mn"])
+    assert list(oracle.pack_q4k_scales(sc, mn)) == head[4:16]
+
+
+def test_q4k_scale_roundtrip_every_field_value():
+    rng = np.random.default_rng(1)
+    for field in range(16):
+        for v in range(64):
+            sc = rng.integers(0, 64, 8)
+            mn = rng.integers(0, 64, 8)
+            (sc if field < 8 else mn)[field % 8] = v
+            p = oracle.pack_q4k_scales(sc, mn)
+            sc2, mn2 = oracle.unpack_q4k_scales(p)
+            assert list(sc2) == list(sc) and list(mn2) == list(mn)
+
+
+def test_q4k_scale_pack_of_unpack_is_identity():
+    # 96 bits <-> sixteen 6-bit fields is a bijection: every byte string is reached.
+    rng = np.random.default_rng(2)
+    for _ in range(2000):
+        p = rng.integers(0, 256, 12).astype(np.uint8)
+        sc, mn = oracle.unpack_q4k_scales(p)
+        assert sc.max() < 64 and mn.max() < 64
+        assert np.array_equal(oracle.pack_q4k_scales(sc, mn), p)
+
+
+def test_q4k_scale_top_bits_land_in_byte_top():
+    p = oracle.pack_q4k_scales([0, 0, 0, 0, 63, 0, 0, 0], [0] * 8)
+    assert p[0] == 0xC0 and p[8] == 0x0F and not p[1:8].any() and not p[9:].any()
+    p = oracle.pack_q4k_scales([0] * 8, [0, 0, 0, 0, 0, 0, 0, 48])
+    assert p[7] == 0xC0 and p[11] == 0x00 and not p[:7].any()
+
+
+# ---------------------------------------------------------------- Q4_K dequant
+
+@pytest.mark.parametrize("name", ["q4k_block_A.txt", "q4k_block_C.txt"])
+def test_q4k_hand_blocks(name):
+    g = load(name)
+    block = np.array(hexbytes(g["head"]) + [int(g["quant_fill"], 16)] * 128, np.uint8)
+    w = oracle.dequant_q4k(block, 256)
+    want = np.repeat(np.array(floats(g["subblock_values"]), np.float32), 32)
+    assert np.array_equal(w.view(np.uint32), want.view(np.uint32))
+
+
+def test_q4k_nibble_order():
+    g = load("q4k_nibble_order.txt")
+    block = np.array(hexbytes(g["head"]) + list(range(128)), np.uint8)
+    w = oracle.dequant_q4k(block, 256)
+    assert np.array_equal(w, np.array(ints(g["weights"]), np.float32))
+
+
+def test_q4k_zero_quants_give_minus_dmin_mn():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        d = rng.uniform(1e-3, 2e-2, 2).astype(np.float16)
+        sc = rng.integers(0, 64, 8)
+        mn = rng.integers(0, 64, 8)
+        mn[rng.integers(0, 8)] = 0
+        blk = oracle.q4k_block(int(d[0].view(np.uint16)), int(d[1].view(np.uint16)), sc, mn,
+                               np.zeros(256, int))
+        w = oracle.dequant_q4k(blk, 256)
+        dmin = np.float32(d[1])
+        want = np.repeat(-(dmin * mn.astype(np.float32)), 32)
+        want[want == 0] = 0.0  # 0 - 0 is +0 under round-to-nearest
+        assert np.array_equal(w.view(np.uint32), want.astype(np.float32).view(np.uint32))
+
+
+def test_q4k_single_quant_scales_linearly():
+    # With dmin = 0 each weight is d*sc_j*q: moving one quant moves one weight only.
+    rng = np.random.default_rng(4)
+    sc = rng.integers(1, 64, 8)
+    mn = np.zeros(8, int)
+    for i in rng.choice(256, 24, replace=False):
+        q = np.zeros(256, int)
+        q[i] = 7
+        w = oracle.dequant_q4k(oracle.q4k_block(0x3C00, 0, sc, mn, q), 256)
+        nz = np.nonzero(w)[0]
+        assert list(nz) == [i] and w[i] == 7 * sc[i // 32]
+
+
+def test_q4k_fp32_equals_rounded_exact():
+    # The products d*sc*q and dmin*mn are exact in fp32, so the fp32 result is the
+    # fp64 (here: exact) value rounded once.
+    g = synth.rng(99, 0, 0)
+    blocks = synth.q4k_weights(64, 256, 99, 0)
+    w = oracle.dequant_q4k(blocks, 64 * 256).reshape(64, 256)
+    for r in range(64):
+        b = blocks[r]
+        d = float(b[0:2].view(np.float16)[0])
+        dmin = float(b[2:4].view(np.float16)[0])
+        sc, mn = oracle.unpack_q4k_scales(b[4:16])
+        qs = b[16:]
+        for i in g.choice(256, 16, replace=False):
+            j, c = i // 32, i // 64
+            byte = int(qs[32 * c + i % 32])
+            q = byte & 15 if j % 2 == 0 else byte >> 4
+            exact = d * sc[j] * q - dmin * mn[j]
+            assert w[r, i] == np.float32(exact)
+
+
+# ---------------------------------------------------------------- IQ3 dequant
+
+def _grid_from(spec: str) -> np.ndarray:
+    grid = np.full((256, 4), 2.0, np.float32)
+    for item in spec.split():
+        k, _, vals = item.partition(":")
+        grid[int(k)] = [float(v) for v in vals.split(",")]
+    return grid
+
+
+def _iq3_from(g) -> tuple:
+    idx = np.zeros(64, int) if g["idx"] == "zeros" else np.arange(64) % 4
+    words = [int(t, 16) for t in g["words"].split()]
+    return oracle.iq3_block(idx, words, int(g["d_bits"], 16)), _grid_from(g["grid_rows"])
+
+
+def test_iq3_hand_block_B():
+    g = load("iq3_block_B.txt")
+    blk, grid = _iq3_from(g)
+    w = oracle.dequant_iq3(blk, grid, 256)
+    want = np.concatenate([floats(g["weights_sb0"]), np.tile(floats(g["weights_other"]), 56)])
+    assert np.array_equal(w, want.astype(np.float32))
+
+
+def test_iq3_hand_block_D():
+    g = load("iq3_block_D.txt")
+    blk, grid = _iq3_from(g)
+    w = oracle.dequant_iq3(blk, grid, 256)
+    other = floats(g["weights_other"])
+    want = np.concatenate([other, floats(g["weights_sb1"])] + [other] * 6)
+    assert np.array_equal(w, np.array(want, np.float32))
+
+
+def test_iq3_parity_exhaustive():
+    grid = np.full((256, 4), 2.0, np.float32)
+    for l in range(4):
+        for seven in range(128):
+            words = [0] * 8
+            words[3] = seven << (7 * l)
+            w = oracle.dequant_iq3(oracle.iq3_block(np.zeros(64), words, 0x3C00), grid, 256)
+            neg = (w[96 + 8 * l: 96 + 8 * l + 8] < 0)
+            assert neg.sum() % 2 == 0
+            assert list(neg[:7]) == [bool((seven >> j) & 1) for j in range(7)]
+            assert (w < 0).sum() == neg.sum()
+    w = oracle.dequant_iq3(oracle.iq3_block(np.zeros(64), [0x01] + [0] * 7, 0x3C00), grid, 256)
+    assert list(np.nonzero(w < 0)[0]) == [0, 7]
+    w = oracle.dequant_iq3(oracle.iq3_block(np.zeros(64), [0x7F] + [0] * 7, 0x3C00), grid, 256)
+    assert list(np.nonzero(w < 0)[0]) == list(range(8))
+
+
+def test_iq3_code_sweep():
+    grid = np.zeros((256, 4), np.float32)
+    grid[0] = [2, 6, 10, 14]
+    mags = np.tile([2, 6, 10, 14], 8)
+    for first in (0, 8):
+        words = [(first + ib) << 28 for ib in range(8)]
+        w = oracle.dequant_iq3(oracle.iq3_block(np.zeros(64), words, 0x3C00), grid, 256)
+        for ib in range(8):
+            s = first + ib
+            assert np.array_equal(w[32 * ib:32 * ib + 32], ((0.5 + s) * 0.5 * mags).astype(np.float32))
+
+
+def test_iq3_fp32_equals_exact():
+    # d (11 significant bits) * (2*code+1) (5 bits) * magnitude (5 bits) fits in fp32.
+    grid = synth.iq3_grid()
+    blocks = synth.iq3_weights(16, 512, 99, 1)
+    w = oracle.dequant_iq3(blocks, grid, 16 * 512).reshape(16, 2, 256)
+    for r in range(16):
+        for sb in range(2):
+            b = blocks[r, 98 * sb: 98 * sb + 98]
+            d = float(b[96:98].view(np.float16)[0])
+            for ib in range(8):
+                word = int(b[64 + 4 * ib: 68 + 4 * ib].view("<u4")[0])
+                code = word >> 28
+                for t in (0, 5, 7, 13, 23, 31):
+                    l, j = t // 8, t % 8
+                    seven = (word >> (7 * l)) & 0x7F
+                    neg = bin(seven).count("1") % 2 if j == 7 else (seven >> j) & 1
+                    m = grid[b[8 * ib + t // 4], t % 4]
+                    exact = (-1 if neg else 1) * m * d * (0.5 + code) * 0.5
+                    assert w[r, sb, 32 * ib + t] == exact
+
+
+# ---------------------------------------------------------------- GEMV / GEMM
+
+def _q4k_case(n_out, n_in, seed):
+    w = synth.q4k_weights(n_out, n_in, 90, seed)
+    x = synth.activations(n_in, 90, seed)
+    return w, x
+
+
+def test_gemv_one_hot_is_a_column():
+    n_out, n_in = 5, 512
+    w, _ = _q4k_case(n_out, n_in, 1)
+    deq = oracle.dequant_q4k(w, n_out * n_in).reshape(n_out, n_in)
+    for k in (0, 1, 31, 32, 255, 256, 300, 511):
+        x = np.zeros(n_in, np.float32)
+        x[k] = 1.0
+        y, s = oracle.gemv_q4k(w, x, n_in, n_out)
+        assert np.array_equal(y, deq[:, k].astype(np.float64))
+        assert np.array_equal(s, np.abs(deq[:, k]).astype(np.float64))
+
+
+def test_gemv_matches_numpy_matmul():
+    n_out, n_in = 37, 1024
+    w, x = _q4k_case(n_out, n_in, 2)
+    deq = oracle.dequant_q4k(w, n_out * n_in).reshape(n_out, n_in).astype(np.float64)
+    y, s = oracle.gemv_q4k(w, x, n_in, n_out)
+    ref = deq @ x.astype(np.float64)
+    sref = np.abs(deq) @ np.abs(x.astype(np.float64))
+    assert np.allclose(y, ref, rtol=0, atol=1e-12 * sref.max())
+    assert np.allclose(s, sref, rtol=1e-13)
+
+
+def test_gemv_structure():
+    n_out, n_in = 9, 768
+    w, x = _q4k_case(n_out, n_in, 3)
+    y, s = oracle.gemv_q4k(w, x, n_in, n_out)
+    y2, s2 = oracle.gemv_q4k(w, 2 * x, n_in, n_out)
+    assert np.array_equal(y2, 2 * y) and np.array_equal(s2, 2 * s)
+    perm = np.random.default_rng(0).permutation(n_out)
+    yp, _ = oracle.gemv_q4k(np.ascontiguousarray(w[perm]), x, n_in, n_out)
+    assert np.array_equal(yp, y[perm])
+    assert (np.abs(y) <= s).all()
+
+
+def test_gemv_integer_case_exact():
+    # d = dmin = 1, sc and mn in 0..7, integer x: every term and partial sum is an
+    # integer far below 2^53, so the result is the exact integer sum.
+    rng = np.random.default_rng(5)
+    n_out, n_in = 3, 512
+    rows = []
+    ws = []
+    for r in range(n_out):
+        row = []
+        for b in range(n_in // 256):
+            sc = rng.integers(0, 8, 8)
+            mn = rng.integers(0, 8, 8)
+            q = rng.integers(0, 16, 256)
+            row.append(oracle.q4k_block(0x3C00, 0x3C00, sc, mn, q))
+            ws.append([int(sc[i // 32]) * int(q[i]) - int(mn[i // 32]) for i in range(256)])
+        rows.append(np.concatenate(row))
+    w = np.stack(rows)
+    wint = np.array(ws, dtype=np.int64).reshape(n_out, n_in)
+    x = rng.integers(-8, 9, n_in).astype(np.float32)
+    y, s = oracle.gemv_q4k(w, x, n_in, n_out)
+    exact = wint @ x.astype(np.int64)
+    assert np.array_equal(y, exact.astype(np.float64))
+    assert np.array_equal(s, (np.abs(wint) @ np.abs(x.astype(np.int64))).astype(np.float64))
+
+
+def test_gemm_rows_are_gemvs():
+    n_out, n_in = 11, 512
+    w, _ = _q4k_case(n_out, n_in, 4)
+    X = synth.activations(n_in, 90, 5, batch=8)
+    Y, S = oracle.gemm_q4k(w, X, n_in, n_out)
+    for b in range(8):
+        y, s = oracle.gemv_q4k(w, X[b], n_in, n_out)
+        assert np.array_equal(Y[b], y) and np.array_equal(S[b], s)
+    Y1, _ = oracle.gemm_q4k(w, X[:1], n_in, n_out)
+    assert np.array_equal(Y1[0], Y[0])
+
+
+def test_rows_variant_matches_full():
+    n_out, n_in = 20, 512
+    w, x = _q4k_case(n_out, n_in, 6)
+    y, s = oracle.gemv_q4k(w, x, n_in, n_out)
+    rows = np.array([19, 0, 7, 7, 3])
+    yr, sr = oracle.gemv_q4k_rows(w, x, n_in, rows)
+    assert np.array_equal(yr, y[rows]) and np.array_equal(sr, s[rows])
+    grid = synth.iq3_grid()
+    wi = synth.iq3_weights(n_out, n_in, 90, 7)
+    yi, si = oracle.gemv_iq3(wi, grid, x, n_in, n_out)
+    yir, sir = oracle.gemv_iq3_rows(wi, grid, x, n_in, rows)
+    assert np.array_equal(yir, yi[rows]) and np.array_equal(sir, si[rows])
+
+
+def test_gemv_iq3_matches_numpy_matmul():
+    n_out, n_in = 13, 768
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 90, 8)
+    x = synth.activations(n_in, 90, 8)
+    deq = oracle.dequant_iq3(w, grid, n_out * n_in).reshape(n_out, n_in).astype(np.float64)
+    y, s = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    sref = np.abs(deq) @ np.abs(x.astype(np.float64))
+    assert np.allclose(y, deq @ x.astype(np.float64), rtol=0, atol=1e-12 * sref.max())
+    assert np.allclose(s, sref, rtol=1e-13)
+
+
+def test_thread_count_does_not_change_results():
+    n_out, n_in = 64, 1024
+    w, x = _q4k_case(n_out, n_in, 9)
+    old = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
+        y1, _ = oracle.gemv_q4k(w, x, n_in, n_out)
+        oracle.set_threads(4)
+        y4, _ = oracle.gemv_q4k(w, x, n_in, n_out)
+    finally:
+        oracle.set_threads(old)
+    assert np.array_equal(y1, y4)
+
+
+def test_size_errors():
+    with pytest.raises(ValueError):
+        oracle.dequant_q4k(np.zeros(144, np.uint8), 255)
+    L = oracle.lib()
+    buf = np.zeros(1024, np.float64)
+    assert L.orc_gemv_q4k(buf.ctypes.data, buf.ctypes.data, 300, 1, buf.ctypes.data, None) == 2
+    assert L.orc_gemm_q4k(buf.ctypes.data, buf.ctypes.data, 256, 1, 9, buf.ctypes.data, None) == 2
+    assert L.orc_gemv_q4k(None, buf.ctypes.data, 256, 1, buf.ctypes.data, None) == 1
