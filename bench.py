@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Effective HBM bandwidth of the fused Q4_K dequantize-GEMV on one MI355X.
+
+Workload (one "step" = one decoded token's weight stream at batch 1): the
+TinyLlama-1.1B-shaped Q4_K projections of 22 layers (q, o 2048x2048; k, v
+256x2048; gate, up 5632x2048; down 2048x5632) followed by the 2048->32000 LM
+head, 155 GEMVs launched back to back on one stream through the C ABI
+(qwg_gemv_q4k). Weights, activations and outputs are seeded synthetic data
+resident in HBM before timing starts; the 582 MB of distinct weights exceed the
+256 MB last-level cache, so every step streams them from HBM.
+
+Reported: value = algorithmic bytes of the step (weights + x + y) / wall time
+per step, in GB/s; the roofline object for the GEMV kernel (algorithmic bytes /
+kernel time, from HIP events around each launch in a separate pass over the same
+launches); and the CPU oracle's throughput on the host cores (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time budget for the oracle baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the GEMV path has no multi-GPU mode in this build "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_weight_decode_gemv_amd as qwg
+    from quantized_weight_decode_gemv_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = qwg.lib()
+
+    probs = synth.config(5)
+    t0 = time.time()
+    host_w = [synth.weights(p) for p in probs]
+    host_x = [synth.inputs(p) for p in probs]
+    W = [torch.from_numpy(w).to(dev) for w in host_w]
+    X = [torch.from_numpy(x).to(dev) for x in host_x]
+    Y = [torch.empty(p.n_out, dtype=torch.float32, device=dev) for p in probs]
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    stream = torch.cuda.current_stream(dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    calls = [(y.data_ptr(), x.data_ptr(), w.data_ptr(), p.n_in, p.n_out)
+             for p, w, x, y in zip(probs, W, X, Y)]
+    gemv = L.qwg_gemv_q4k
+
+    def step():
+        for yp, xp, wp, n_in, n_out in calls:
+            rc = gemv(yp, xp, wp, n_in, n_out, sptr)
+            if rc:
+                raise RuntimeError(f"qwg_gemv_q4k failed: {rc}")
+
+    step_bytes = sum(p.algorithmic_bytes for p in probs)
+    weight_bytes = sum(p.weight_bytes for p in probs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = step_bytes * args.steps / elapsed / 1e9
+
+    # Roofline pass: HIP events on the launch stream around every GEMV launch.
+    rsteps = max(1, min(args.steps, 10))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(rsteps * len(calls))]
+    torch.cuda.synchronize()
+    i = 0
+    for _ in range(rsteps):
+        for yp, xp, wp, n_in, n_out in calls:
+            ev[i][0].record(stream)
+            gemv(yp, xp, wp, n_in, n_out, sptr)
+            ev[i][1].record(stream)
+            i += 1
+    torch.cuda.synchronize()
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / rsteps
+    launches_per_step = len(calls)
+    achieved = step_bytes / (kernel_ms * 1e-3) / 1e9
+    lm = [j for j, p in enumerate(probs) if p.name == "lm_head"][0]
+    lm_ms = sum(ev[s * launches_per_step + lm][0].elapsed_time(ev[s * launches_per_step + lm][1])
+                for s in range(rsteps)) / rsteps
+
+    result = {
+        "metric": "effective HBM GB/s (% of MI355X peak) for Q4_K/IQ3 GEMV, batch 1",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "TinyLlama-1.1B Q4_K per-token weight stream, batch 1: 22 layers x "
+                        "(q,o 2048x2048; k,v 256x2048; gate,up 5632x2048; down 2048x5632) + "
+                        "LM head 32000x2048, 155 qwg_gemv_q4k launches on one stream",
+            "weight_bytes": weight_bytes,
+            "algorithmic_bytes_per_step": step_bytes,
+            "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "tokens_per_s": round(1e3 / ms_per_step, 1),
+            "launches_per_step": launches_per_step,
+            "setup_s": round(setup_s, 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "q4k_gemv_kernel<1>",
+            "kernel_ms_per_step": round(kernel_ms, 4),
+            "avg_launch_us": round(1e3 * kernel_ms / launches_per_step, 3),
+            "lm_head_us": round(1e3 * lm_ms, 3),
+            "lm_head_gbs": round(probs[lm].algorithmic_bytes / (lm_ms * 1e-3) / 1e9, 1),
+        },
+    }
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(probs, host_w, host_x, Y, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(probs, host_w, host_x, Y, budget_s):
+    """The oracle (plain C, fp64 dot, OpenMP over rows) on the host cores over the
+    same per-token stream, repeated until the budget is spent; the GPU outputs of
+    the last step are compared with it on the way (sampled rows)."""
+    import numpy as np
+    import oracle
+
+    oracle.build(force=False)
+    cores = oracle.get_threads()
+    step_bytes = sum(p.algorithmic_bytes for p in probs)
+    runs, t_total = 0, 0.0
+    worst = 0.0
+    rng = np.random.default_rng(0)
+    while runs == 0 or t_total < budget_s:
+        t0 = time.perf_counter()
+        for j, (p, w, x) in enumerate(zip(probs, host_w, host_x)):
+            y, s = oracle.gemv_q4k(w, x, p.n_in, p.n_out)
+            if runs == 0:
+                rows = rng.integers(0, p.n_out, 16)
+                g = Y[j].cpu().numpy()[rows].astype(np.float64)
+                worst = max(worst, float(np.max(np.abs(g - y[rows]) / s[rows])))
+        t_total += time.perf_counter() - t0
+        runs += 1
+        if runs >= 50:
+            break
+    if worst > 2e-6:
+        raise SystemExit(f"GPU output outside the 2e-6 bound vs the oracle (worst {worst:.3g})")
+    return {
+        "value": round(step_bytes * runs / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{runs} full per-token streams (155 GEMVs, {step_bytes / 1e6:.0f} MB each), "
+                  f"{t_total:.1f} s; GPU rows checked, worst |dy|/sum|wx| = {worst:.2e}",
+    }
+
+
+if __name__ == "__main__":
+    main()

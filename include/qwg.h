@@ -1,0 +1,139 @@
+/*
+ * qwg.h - C ABI of libqwg: fused dequantize + matrix-vector products over
+ * block-quantized weights on AMD Instinct MI355X (gfx950).
+ *
+ * Formats (as the pages define them):
+ *   Q4_K  "用 Python 重写 picoLM" page, dequantize_q4_K listing: 144-byte
+ *         super-block of 256 weights = fp16 d (bytes 0-1), fp16 dmin (2-3),
+ *         twelve bytes of packed 6-bit sub-block scales and mins (4-15) and
+ *         128 bytes of 4-bit quants (16-143). Weight = d*sc_j*q - dmin*mn_j.
+ *   IQ3   iq3_pack.py page, module docstring and decode(): 98-byte grouped
+ *         container of 256 weights = 64 grid indices (0-63), eight
+ *         little-endian uint32 words (64-95: three+one 7-bit sign groups whose
+ *         eighth sign is their parity, 4-bit sub-scale code in bits 28-31) and
+ *         fp16 d (96-97). Weight = grid[idx][t%4] * sign * d*(0.5+code)*0.5,
+ *         grid magnitudes in weight units.
+ *
+ * Common conventions
+ *   - Every pointer argument except `stream` is a DEVICE pointer (HIP memory
+ *     visible to the current device). `stream` is a hipStream_t passed as
+ *     void*; NULL means the default stream.
+ *   - A weight matrix W has n_out rows; each row is n_in/256 consecutive
+ *     blocks; rows are contiguous (row r starts at r * qwg_row_bytes(fmt, n_in)).
+ *     y = W x, the argument order of picoLM's matmul(out, x, W, n_in, n_out,
+ *     type) call in that page's model_forward listing.
+ *   - Vectors are contiguous fp32. Batched inputs and outputs are row-major:
+ *     X is [batch, n_in], Y is [batch, n_out].
+ *   - The caller owns every buffer. Calls only enqueue work on `stream` and
+ *     return; the caller synchronizes. Outputs must not alias inputs.
+ *   - GEMV/GEMM with n_out rows may split the n_in sum across workgroups.
+ *     The partial sums then go through a small per-(device, stream) workspace
+ *     that the library allocates on the first such call on that stream
+ *     (hipMalloc + hipMemset, synchronous) and keeps until the process ends.
+ *     Concurrent calls on different streams never share a workspace. The
+ *     summation order is fixed by the shapes, so results are deterministic.
+ *   - Errors are reported by the returned status (QWG_* below); the library
+ *     never aborts, never throws and writes nothing on a validation error.
+ *     Validation happens on the host before any HIP call.
+ */
+#ifndef QWG_H
+#define QWG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define QWG_OK 0
+#define QWG_ERR_NULL 1     /* a required pointer is NULL */
+#define QWG_ERR_SHAPE 2    /* n_in % 256 != 0, n_in outside [256, QWG_MAX_N_IN], n <= 0, n_out < 1 or too large */
+#define QWG_ERR_ALIGN 3    /* a pointer is not aligned as documented for the call */
+#define QWG_ERR_BATCH 4    /* batch outside 1..QWG_MAX_BATCH */
+#define QWG_ERR_HIP 5      /* the HIP runtime reported an error (launch, allocation) */
+#define QWG_ERR_FORMAT 6   /* unknown format id */
+
+/* format ids */
+#define QWG_FMT_Q4K 0
+#define QWG_FMT_IQ3 1
+
+#define QWG_QK 256
+#define QWG_Q4K_BLOCK_BYTES 144
+#define QWG_IQ3_BLOCK_BYTES 98
+#define QWG_MAX_N_IN 65536          /* 256 super-blocks per row */
+#define QWG_MAX_N_OUT (1 << 24)
+#define QWG_MAX_BATCH 8
+
+/* Library version (major*10000 + minor*100 + patch). */
+int qwg_version(void);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *qwg_strerror(int status);
+
+/* Bytes per row of `n_in` weights in format `fmt` ((n_in/256) * {144, 98}),
+ * or -QWG_ERR_SHAPE / -QWG_ERR_FORMAT. */
+int64_t qwg_row_bytes(int fmt, int64_t n_in);
+
+/*
+ * How a GEMV/GEMM of this shape is decomposed (introspection for tests and
+ * tuning): the number of workgroups that share each 64-row tile by splitting
+ * the n_in sum (1 = no split), or a negative status for invalid sizes.
+ */
+int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out);
+
+/*
+ * Q4_K dequantization ("用 Python 重写 picoLM", dequantize_q4_K listing).
+ * src: n/256 consecutive 144-byte blocks, 16-byte aligned.
+ * dst: n fp32 weights in block order, 16-byte aligned.
+ * n % 256 == 0, n > 0. The result is bit-identical to evaluating, in fp32 with
+ * round-to-nearest-even, (d*sc_j)*q - dmin*mn_j per weight.
+ */
+int qwg_dequant_q4k(const void *src, float *dst, int64_t n, void *stream);
+
+/*
+ * IQ3 dequantization (iq3_pack.py page, docstring and decode()).
+ * src: n/256 consecutive 98-byte blocks, 2-byte aligned.
+ * grid: [256][4] fp32 magnitudes in weight units, 16-byte aligned.
+ * dst: n fp32 weights, 16-byte aligned. n % 256 == 0, n > 0.
+ * Bit-identical to grid[idx][t%4] * sign * (d*(0.5+code)*0.5) rounded to fp32.
+ */
+int qwg_dequant_iq3(const void *src, const float *grid, float *dst, int64_t n, void *stream);
+
+/*
+ * y[r] = sum_k W[r,k] x[k] for Q4_K weights (the fused dequantize-and-dot of
+ * picoLM's matmul for quantized rows).
+ * w: n_out rows of n_in/256 Q4_K blocks, 16-byte aligned.
+ * x: n_in fp32, 16-byte aligned.   y: n_out fp32, 4-byte aligned.
+ * 256 <= n_in <= QWG_MAX_N_IN, n_in % 256 == 0, 1 <= n_out <= QWG_MAX_N_OUT.
+ * Accuracy: |y - exact| <= 2e-6 * sum_k |W[r,k] x[k]| per row for inputs of
+ * ordinary magnitude; summation in fp32 in a fixed order.
+ */
+int qwg_gemv_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                 void *stream);
+
+/*
+ * y = W x for IQ3 weights.
+ * w: n_out rows of n_in/256 IQ3 blocks, 2-byte aligned (98-byte blocks put odd
+ * blocks at 2 mod 4). grid: [256][4] fp32 magnitudes, 16-byte aligned; every
+ * magnitude must be exactly representable in fp16 (true for the integer
+ * magnitudes IQ3 grids use), otherwise the result is the product with the
+ * fp16-rounded grid. x: n_in fp32, 16-byte aligned. y: n_out fp32, 4-byte aligned.
+ * Shape limits as qwg_gemv_q4k.
+ */
+int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                 int64_t n_out, void *stream);
+
+/*
+ * Y[b, r] = sum_k W[r,k] X[b,k] for 1 <= batch <= QWG_MAX_BATCH, Q4_K weights:
+ * every weight is decoded once and applied to all `batch` activation rows.
+ * x: [batch, n_in] fp32 row-major, 16-byte aligned. y: [batch, n_out] fp32
+ * row-major, 4-byte aligned. batch == 1 computes the same as qwg_gemv_q4k.
+ */
+int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                 int batch, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

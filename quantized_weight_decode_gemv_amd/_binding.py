@@ -1,0 +1,182 @@
+"""ctypes binding of libqwg (include/qwg.h). Argument marshalling only: every
+step of the computation runs in the library's HIP kernels. Tensors must be on a
+HIP device; calls enqueue on torch's current stream."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqwg.so")
+
+QWG_FMT_Q4K = 0
+QWG_FMT_IQ3 = 1
+QK = 256
+Q4K_BYTES = 144
+IQ3_BYTES = 98
+MAX_BATCH = 8
+
+_lib = None
+
+
+class QwgError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({lib().qwg_strerror(status).decode()})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqwg.so; raise if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m quantized_weight_decode_gemv_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.qwg_version.restype = I
+        L.qwg_strerror.argtypes = [I]
+        L.qwg_strerror.restype = ctypes.c_char_p
+        L.qwg_row_bytes.argtypes = [I, I64]
+        L.qwg_row_bytes.restype = I64
+        L.qwg_plan_splits.argtypes = [I, I64, I64]
+        L.qwg_plan_splits.restype = I
+        L.qwg_dequant_q4k.argtypes = [P, P, I64, P]
+        L.qwg_dequant_iq3.argtypes = [P, P, P, I64, P]
+        L.qwg_gemv_q4k.argtypes = [P, P, P, I64, I64, P]
+        L.qwg_gemv_iq3.argtypes = [P, P, P, P, I64, I64, P]
+        L.qwg_gemm_q4k.argtypes = [P, P, P, I64, I64, I, P]
+        for f in ("qwg_dequant_q4k", "qwg_dequant_iq3", "qwg_gemv_q4k", "qwg_gemv_iq3",
+                  "qwg_gemm_q4k"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a tensor on a HIP device")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise QwgError(rc, what)
+
+
+def row_bytes(fmt: int, n_in: int) -> int:
+    v = lib().qwg_row_bytes(fmt, n_in)
+    if v < 0:
+        raise ValueError(f"invalid n_in {n_in} for format {fmt}")
+    return v
+
+
+def plan_splits(fmt: int, n_in: int, n_out: int) -> int:
+    """Workgroups sharing each 64-row tile for this GEMV shape (1 = no split)."""
+    v = lib().qwg_plan_splits(fmt, n_in, n_out)
+    if v < 0:
+        raise ValueError(f"invalid shape n_in={n_in} n_out={n_out}")
+    return v
+
+
+def _weights(w: torch.Tensor, n_in: int, block_bytes: int) -> int:
+    _dev(w, "w", torch.uint8)
+    if n_in <= 0 or n_in % QK:
+        raise ValueError(f"n_in must be a positive multiple of {QK}, got {n_in}")
+    rb = (n_in // QK) * block_bytes
+    if w.numel() % rb:
+        raise ValueError(f"w has {w.numel()} bytes, not a whole number of {rb}-byte rows")
+    return w.numel() // rb
+
+
+def dequant_q4k(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed Q4_K blocks (uint8, 144 bytes per 256 weights) -> fp32 weights."""
+    _dev(w, "w", torch.uint8)
+    if w.numel() % Q4K_BYTES:
+        raise ValueError("byte count is not a multiple of 144")
+    n = w.numel() // Q4K_BYTES * QK
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=w.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_dequant_q4k(w.data_ptr(), out.data_ptr(), n, _stream(w)), "qwg_dequant_q4k")
+    return out
+
+
+def dequant_iq3(w: torch.Tensor, grid: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed IQ3 blocks (uint8, 98 bytes per 256 weights) + fp32 grid [256, 4] -> fp32."""
+    _dev(w, "w", torch.uint8)
+    _dev(grid, "grid", torch.float32)
+    if grid.shape != (256, 4):
+        raise ValueError("grid must be [256, 4]")
+    if w.numel() % IQ3_BYTES:
+        raise ValueError("byte count is not a multiple of 98")
+    n = w.numel() // IQ3_BYTES * QK
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=w.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_dequant_iq3(w.data_ptr(), grid.data_ptr(), out.data_ptr(), n, _stream(w)),
+           "qwg_dequant_iq3")
+    return out
+
+
+def gemv_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x; w uint8 [n_out, row_bytes] (or flat), x fp32 [n_in]."""
+    _dev(x, "x", torch.float32)
+    n_in = x.numel()
+    n_out = _weights(w, n_in, Q4K_BYTES)
+    if out is None:
+        out = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n_out:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_gemv_q4k(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out, _stream(x)),
+           "qwg_gemv_q4k")
+    return out
+
+
+def gemv_iq3(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    _dev(x, "x", torch.float32)
+    _dev(grid, "grid", torch.float32)
+    if grid.shape != (256, 4):
+        raise ValueError("grid must be [256, 4]")
+    n_in = x.numel()
+    n_out = _weights(w, n_in, IQ3_BYTES)
+    if out is None:
+        out = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n_out:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_gemv_iq3(out.data_ptr(), x.data_ptr(), w.data_ptr(), grid.data_ptr(), n_in,
+                              n_out, _stream(x)), "qwg_gemv_iq3")
+    return out
+
+
+def gemm_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W^T for X fp32 [batch, n_in] (1 <= batch <= 8) -> [batch, n_out]."""
+    _dev(x, "x", torch.float32)
+    if x.dim() != 2 or not 1 <= x.shape[0] <= MAX_BATCH:
+        raise ValueError("x must be [batch, n_in] with 1 <= batch <= 8")
+    batch, n_in = x.shape
+    n_out = _weights(w, n_in, Q4K_BYTES)
+    if out is None:
+        out = torch.empty(batch, n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.shape != (batch, n_out):
+        raise ValueError("out has the wrong shape")
+    _check(lib().qwg_gemm_q4k(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out, batch,
+                              _stream(x)), "qwg_gemm_q4k")
+    return out

@@ -1,0 +1,93 @@
+// Device-side helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qwg_internal.h"
+
+namespace qwg {
+
+// fp16 bit patterns held in the low / high half of a 32-bit register, widened to
+// fp32. Used as FMA operands, the compiler folds the widening into
+// v_fma_mix_f32 (one VALU op per weight).
+__device__ __forceinline__ float h2f_lo(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+}
+__device__ __forceinline__ float h2f_hi(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// Wave-uniform read-only activations are read through the constant address
+// space, so the compiler fetches them with scalar loads into SGPRs (one operand
+// of every VALU FMA) instead of per-lane vector loads.
+typedef const __attribute__((address_space(4))) float *cfloat_p;
+__device__ __forceinline__ cfloat_p as_scalar(const float *p) { return (cfloat_p)p; }
+
+// Constants hidden from the optimizer so that mask-and-convert patterns are
+// kept as written (otherwise the compiler rewrites byte masks into per-field
+// bit extracts, one more op per weight).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// End of a 64-row tile for one workgroup: `total` is this lane's row sum over
+// the workgroup's super-block range (batch element `bt`). With one split the
+// row is stored directly. Otherwise every split stores its partial, and the
+// workgroup that arrives last at the tile's counter sums the partials in split
+// order (so the result does not depend on arrival order), stores the rows and
+// re-arms the counter for the next launch. Executed by one full wavefront.
+//
+// Cross-workgroup visibility without cache maintenance: the partials are
+// written and read with agent-scope atomic stores/loads (coherent across the
+// XCDs' L2 caches), and the wavefront waits for its stores to complete before it
+// increments the counter; the last workgroup reads them only after its counter
+// update has returned. An agent-scope fence would instead write back and
+// invalidate the whole L2 of the XCD for every workgroup.
+template <int NB>
+__device__ __forceinline__ void tile_epilogue(const GemvArgs &a, int tile, int split,
+                                              const float (&total)[NB]) {
+    const int lane = threadIdx.x & 63;
+    const int row = tile * kTileRows + lane;
+    if (a.splits == 1) {
+        if (row < a.n_out) {
+#pragma unroll
+            for (int bt = 0; bt < NB; ++bt) a.y[(int64_t)bt * a.n_out + row] = total[bt];
+        }
+        return;
+    }
+    const int64_t plane = (int64_t)a.tiles * kTileRows;
+#pragma unroll
+    for (int bt = 0; bt < NB; ++bt)
+        __hip_atomic_store(&a.partial[((int64_t)split * NB + bt) * plane + row], total[bt],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The partials must have reached the coherence point before the count is
+    // taken: wait for every outstanding memory operation of this wavefront.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    uint32_t old = 0;
+    if (lane == 0)
+        old = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != (uint32_t)(a.splits - 1)) return;
+    float acc[NB];
+#pragma unroll
+    for (int bt = 0; bt < NB; ++bt) acc[bt] = 0.0f;
+    for (int s = 0; s < a.splits; ++s) {
+#pragma unroll
+        for (int bt = 0; bt < NB; ++bt)
+            acc[bt] += __hip_atomic_load(&a.partial[((int64_t)s * NB + bt) * plane + row],
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (row < a.n_out) {
+#pragma unroll
+        for (int bt = 0; bt < NB; ++bt) a.y[(int64_t)bt * a.n_out + row] = acc[bt];
+    }
+    if (lane == 0)
+        __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace qwg

@@ -1,0 +1,128 @@
+"""CPU tier of the C ABI: the library loads, exports every entry point its
+header declares, and rejects bad arguments on the host (status codes) before
+any HIP call. No compute call is made here (there is no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qwg.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from quantized_weight_decode_gemv_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from quantized_weight_decode_gemv_amd import build
+        build.build()
+    return _binding.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qwg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for want in ("qwg_dequant_q4k", "qwg_dequant_iq3", "qwg_gemv_q4k", "qwg_gemv_iq3",
+                 "qwg_gemm_q4k", "qwg_strerror", "qwg_row_bytes", "qwg_version",
+                 "qwg_plan_splits"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from quantized_weight_decode_gemv_amd import _binding
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qwg_[a-z0-9_]+)$", out, flags=re.M))
+    for name in declared_symbols():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_version_and_strerror(L):
+    assert L.qwg_version() >= 100
+    for st in range(0, 8):
+        assert len(L.qwg_strerror(st)) > 0
+
+
+def test_row_bytes(L):
+    assert L.qwg_row_bytes(0, 2048) == 8 * 144 == 1152
+    assert L.qwg_row_bytes(0, 5632) == 3168
+    assert L.qwg_row_bytes(1, 2048) == 784
+    assert L.qwg_row_bytes(1, 5632) == 2156
+    assert L.qwg_row_bytes(0, 300) == -2
+    assert L.qwg_row_bytes(7, 256) == -6
+
+
+def test_plan_splits(L):
+    # small row counts split the n_in sum; large ones do not; splits <= blocks per row
+    assert L.qwg_plan_splits(0, 2048, 256) == 8
+    assert L.qwg_plan_splits(0, 2048, 2048) == 8
+    assert 1 <= L.qwg_plan_splits(0, 2048, 32000) <= 8
+    assert L.qwg_plan_splits(0, 256, 1 << 20) == 1
+    assert L.qwg_plan_splits(0, 257, 64) == -2
+    assert L.qwg_plan_splits(0, 65536 + 256, 64) == -2
+    assert L.qwg_plan_splits(3, 256, 64) == -6
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("call,status", [
+    # NULL pointers -> 1
+    (lambda L: L.qwg_gemv_q4k(None, FAKE, FAKE, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_q4k(FAKE, None, FAKE, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_q4k(FAKE, FAKE, None, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_iq3(FAKE, FAKE, FAKE, None, 256, 1, None), 1),
+    (lambda L: L.qwg_gemm_q4k(None, FAKE, FAKE, 256, 1, 2, None), 1),
+    (lambda L: L.qwg_dequant_q4k(None, FAKE, 256, None), 1),
+    (lambda L: L.qwg_dequant_iq3(FAKE, None, FAKE, 256, None), 1),
+    # shapes -> 2
+    (lambda L: L.qwg_gemv_q4k(FAKE, FAKE, FAKE, 300, 1, None), 2),
+    (lambda L: L.qwg_gemv_q4k(FAKE, FAKE, FAKE, 0, 1, None), 2),
+    (lambda L: L.qwg_gemv_q4k(FAKE, FAKE, FAKE, 256, 0, None), 2),
+    (lambda L: L.qwg_gemv_q4k(FAKE, FAKE, FAKE, 65536 + 256, 1, None), 2),
+    (lambda L: L.qwg_gemv_q4k(FAKE, FAKE, FAKE, 256, (1 << 24) + 1, None), 2),
+    (lambda L: L.qwg_gemv_iq3(FAKE, FAKE, FAKE, FAKE, 128, 4, None), 2),
+    (lambda L: L.qwg_dequant_q4k(FAKE, FAKE, 255, None), 2),
+    (lambda L: L.qwg_dequant_iq3(FAKE, FAKE, FAKE, -256, None), 2),
+    # batch -> 4
+    (lambda L: L.qwg_gemm_q4k(FAKE, FAKE, FAKE, 256, 1, 0, None), 4),
+    (lambda L: L.qwg_gemm_q4k(FAKE, FAKE, FAKE, 256, 1, 9, None), 4),
+    # alignment -> 3
+    (lambda L: L.qwg_gemv_q4k(FAKE, FAKE, FAKE + 8, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_q4k(FAKE, FAKE + 4, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_q4k(FAKE + 2, FAKE, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3(FAKE, FAKE, FAKE + 1, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3(FAKE, FAKE, FAKE, FAKE + 4, 256, 1, None), 3),
+    (lambda L: L.qwg_dequant_q4k(FAKE + 4, FAKE, 256, None), 3),
+    (lambda L: L.qwg_dequant_q4k(FAKE, FAKE + 4, 256, None), 3),
+    (lambda L: L.qwg_dequant_iq3(FAKE + 1, FAKE, FAKE, 256, None), 3),
+])
+def test_validation_errors(L, call, status):
+    assert call(L) == status
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    import quantized_weight_decode_gemv_amd as qwg
+    w = torch.zeros(144, dtype=torch.uint8)
+    x = torch.zeros(256)
+    with pytest.raises(ValueError):
+        qwg.gemv_q4k(w, x)
+    with pytest.raises(ValueError):
+        qwg.dequant_q4k(w)
+
+
+def test_binding_has_no_fallback(monkeypatch, tmp_path):
+    from quantized_weight_decode_gemv_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        _binding.lib()

@@ -1,0 +1,317 @@
+"""GPU parity: the HIP kernels, called through the C ABI (ctypes binding), against
+the CPU oracle on the same seeded inputs.
+
+Bars: dequantization is bit-exact; a GEMV/GEMM output passes when
+|y_gpu - y_oracle| <= 2e-6 * sum_k |w_k x_k| for every row (the oracle sums in
+fp64); integer-valued and one-hot cases must match exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_weight_decode_gemv_amd as qwg
+from golden_io import floats, hexbytes, ints, load
+from quantized_weight_decode_gemv_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _ready():
+    oracle.build(force=False)
+    qwg.lib()
+
+
+def dev(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_bound(y_gpu, y_ref, s_ref, what=""):
+    y_gpu = np.asarray(y_gpu, np.float64).reshape(y_ref.shape)
+    err = np.abs(y_gpu - y_ref)
+    bad = err > TOL * s_ref
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / np.maximum(s_ref, 1e-300)), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} rows outside the bound; worst at {i}: "
+                             f"gpu {y_gpu[i]!r} oracle {y_ref[i]!r} sum|wx| {s_ref[i]!r}")
+
+
+def assert_bits(a, b, what=""):
+    a = np.ascontiguousarray(a, np.float32).view(np.uint32)
+    b = np.ascontiguousarray(b, np.float32).view(np.uint32)
+    diff = np.nonzero(a != b)[0]
+    assert diff.size == 0, f"{what}: {diff.size} mismatching words, first at {diff[:5]}"
+
+
+# ---------------------------------------------------------------- dequant
+
+def test_dequant_q4k_hand_blocks():
+    for name in ("q4k_block_A.txt", "q4k_block_C.txt"):
+        g = load(name)
+        blk = np.array(hexbytes(g["head"]) + [int(g["quant_fill"], 16)] * 128, np.uint8)
+        w = host(qwg.dequant_q4k(dev(blk)))
+        assert_bits(w, np.repeat(np.array(floats(g["subblock_values"]), np.float32), 32), name)
+    g = load("q4k_nibble_order.txt")
+    blk = np.array(hexbytes(g["head"]) + list(range(128)), np.uint8)
+    assert_bits(host(qwg.dequant_q4k(dev(blk))), np.array(ints(g["weights"]), np.float32))
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 512), (2048, 2048), (256, 2048),
+                                        (5632, 2048), (2048, 5632)])
+def test_dequant_q4k_matches_oracle(n_out, n_in):
+    w = synth.q4k_weights(n_out, n_in, 91, n_out + n_in)
+    got = host(qwg.dequant_q4k(dev(w)))
+    assert_bits(got, oracle.dequant_q4k(w, n_out * n_in), f"{n_out}x{n_in}")
+
+
+def test_dequant_q4k_special_scales():
+    # subnormal, negative, zero and large fp16 d / dmin
+    rng = np.random.default_rng(11)
+    blocks = synth.q4k_weights(64, 256, 92, 0).copy()
+    specials = [0x0001, 0x03FF, 0x0400, 0x8001, 0xBC00, 0x0000, 0x8000, 0x7BFF, 0xFBFF, 0x3C00]
+    for r in range(64):
+        d, dm = specials[r % len(specials)], specials[(3 * r + 1) % len(specials)]
+        blocks[r, 0], blocks[r, 1] = d & 0xFF, d >> 8
+        blocks[r, 2], blocks[r, 3] = dm & 0xFF, dm >> 8
+    got = host(qwg.dequant_q4k(dev(blocks)))
+    ref = oracle.dequant_q4k(blocks, 64 * 256)
+    # signed zeros may differ only where both sides are zero (x - x with negative d)
+    both0 = (got == 0) & (ref == 0)
+    got = np.where(both0, 0.0, got).astype(np.float32)
+    ref = np.where(both0, 0.0, ref).astype(np.float32)
+    assert_bits(got, ref, "special scales")
+    del rng
+
+
+def _grid_from(spec):
+    grid = np.full((256, 4), 2.0, np.float32)
+    for item in spec.split():
+        k, _, vals = item.partition(":")
+        grid[int(k)] = [float(v) for v in vals.split(",")]
+    return grid
+
+
+def test_dequant_iq3_hand_blocks():
+    for name in ("iq3_block_B.txt", "iq3_block_D.txt"):
+        g = load(name)
+        idx = np.zeros(64, int) if g["idx"] == "zeros" else np.arange(64) % 4
+        blk = oracle.iq3_block(idx, [int(t, 16) for t in g["words"].split()], int(g["d_bits"], 16))
+        grid = _grid_from(g["grid_rows"])
+        got = host(qwg.dequant_iq3(dev(blk), dev(grid)))
+        assert_bits(got, oracle.dequant_iq3(blk, grid, 256), name)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 768), (5632, 2048), (2048, 5632)])
+def test_dequant_iq3_matches_oracle(n_out, n_in):
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 93, n_out + n_in)
+    got = host(qwg.dequant_iq3(dev(w), dev(grid)))
+    assert_bits(got, oracle.dequant_iq3(w, grid, n_out * n_in), f"{n_out}x{n_in}")
+
+
+# ---------------------------------------------------------------- Q4_K GEMV
+
+def _gemv_q4k_case(n_out, n_in, cfg=94, tensor=0):
+    w = synth.q4k_weights(n_out, n_in, cfg, tensor)
+    x = synth.activations(n_in, cfg, tensor)
+    return w, x
+
+
+@pytest.mark.parametrize("p", synth.config(1) + synth.config(2) + synth.config(3)[:1],
+                         ids=lambda p: f"c{p.cfg}-{p.name}")
+def test_gemv_q4k_configs(p):
+    w, x = synth.weights(p), synth.inputs(p)
+    y = host(qwg.gemv_q4k(dev(w), dev(x)))
+    yr, sr = oracle.gemv_q4k(w, x, p.n_in, p.n_out)
+    assert_bound(y, yr, sr, p.name)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (2, 256), (63, 512), (64, 768), (65, 1024),
+                                        (127, 1280), (200, 5632), (1000, 2048), (4097, 256),
+                                        (131072 + 5, 256), (3, 65536)])
+def test_gemv_q4k_ragged(n_out, n_in):
+    w, x = _gemv_q4k_case(n_out, n_in, 95, n_out)
+    y = host(qwg.gemv_q4k(dev(w), dev(x)))
+    yr, sr = oracle.gemv_q4k(w, x, n_in, n_out)
+    assert_bound(y, yr, sr, f"{n_out}x{n_in} splits={qwg.plan_splits(0, n_in, n_out)}")
+
+
+def test_gemv_q4k_covers_split_and_unsplit_plans():
+    assert qwg.plan_splits(0, 256, 131072 + 5) == 1
+    assert qwg.plan_splits(0, 2048, 2048) > 1
+    assert qwg.plan_splits(0, 65536, 3) > 8
+
+
+def _integer_q4k(n_out, n_in, seed):
+    # d = dmin = 1, every 6-bit scale/min in 0..7: bytes 4..11 masked to 0x07,
+    # bytes 12..15 (low nibbles of scales 4..7 and mins 4..7) to 0x77.
+    w = synth.q4k_weights(n_out, n_in, 96, seed).reshape(-1, 144).copy()
+    w[:, 0:4] = [0x00, 0x3C, 0x00, 0x3C]
+    w[:, 4:12] &= 0x07
+    w[:, 12:16] &= 0x77
+    return w.reshape(n_out, -1)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(64, 2048), (300, 5632), (7, 256)])
+def test_gemv_q4k_integer_exact(n_out, n_in):
+    w = _integer_q4k(n_out, n_in, n_out)
+    x = np.random.default_rng(n_in).integers(-8, 9, n_in).astype(np.float32)
+    y = host(qwg.gemv_q4k(dev(w), dev(x)))
+    yr, _ = oracle.gemv_q4k(w, x, n_in, n_out)
+    assert np.array_equal(y.astype(np.float64), yr)
+
+
+def test_gemv_q4k_one_hot_is_exact_column():
+    n_out, n_in = 130, 1024
+    w, _ = _gemv_q4k_case(n_out, n_in, 97, 1)
+    deq = oracle.dequant_q4k(w, n_out * n_in).reshape(n_out, n_in)
+    wd = dev(w)
+    for k in (0, 31, 32, 63, 64, 100, 255, 256, 511, 700, 1023):
+        x = np.zeros(n_in, np.float32)
+        x[k] = 1.0
+        y = host(qwg.gemv_q4k(wd, dev(x)))
+        assert_bits(y + 0.0, deq[:, k] + 0.0, f"k={k}")
+
+
+def test_gemv_q4k_deterministic_and_stream_aware():
+    n_out, n_in = 2048, 2048
+    w, x = _gemv_q4k_case(n_out, n_in, 98, 2)
+    wd, xd = dev(w), dev(x)
+    y1 = host(qwg.gemv_q4k(wd, xd))
+    y2 = host(qwg.gemv_q4k(wd, xd))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y3 = qwg.gemv_q4k(wd, xd)
+    s.synchronize()
+    assert_bits(y1, y2)
+    assert_bits(y1, host(y3))
+
+
+def test_gemv_q4k_c5_stream_sampled_rows():
+    # The full per-token stream (22 layers x 7 projections + LM head) at its real
+    # shapes, launched back to back as bench.py does; the oracle checks sampled rows.
+    probs = synth.config(5)
+    rng = np.random.default_rng(5)
+    outs = []
+    for p in probs:
+        w, x = synth.weights(p), synth.inputs(p)
+        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 24)]))
+        outs.append((p, w, x, rows, qwg.gemv_q4k(dev(w), dev(x))))
+    torch.cuda.synchronize()
+    for p, w, x, rows, y in outs:
+        yr, sr = oracle.gemv_q4k_rows(w, x, p.n_in, rows)
+        assert_bound(y.cpu().numpy()[rows], yr, sr, p.name)
+
+
+def test_gemv_q4k_misaligned_input_is_an_error():
+    w, x = _gemv_q4k_case(4, 256, 99, 0)
+    xd = dev(np.concatenate([[0.0], x]).astype(np.float32))[1:]
+    with pytest.raises(qwg.QwgError) as e:
+        qwg.gemv_q4k(dev(w), xd)
+    assert e.value.status == 3
+
+
+# ---------------------------------------------------------------- GEMM
+
+@pytest.mark.parametrize("batch", range(1, 9))
+def test_gemm_q4k_batches(batch):
+    n_out, n_in = 333, 1536
+    w, _ = _gemv_q4k_case(n_out, n_in, 100, batch)
+    X = synth.activations(n_in, 100, 50 + batch, batch=batch)
+    Y = host(qwg.gemm_q4k(dev(w), dev(X)))
+    Yr, Sr = oracle.gemm_q4k(w, X, n_in, n_out)
+    assert_bound(Y, Yr, Sr, f"batch {batch}")
+    if batch == 1:
+        assert_bits(Y[0], host(qwg.gemv_q4k(dev(w), dev(X[0]))))
+
+
+def test_gemm_q4k_lm_head_b8():
+    p = synth.config(3)[1]
+    w, X = synth.weights(p), synth.inputs(p)
+    Y = host(qwg.gemm_q4k(dev(w), dev(X)))
+    Yr, Sr = oracle.gemm_q4k(w, X, p.n_in, p.n_out)
+    assert_bound(Y, Yr, Sr, "lm_head b8")
+
+
+def test_gemm_q4k_integer_exact():
+    n_out, n_in = 100, 2048
+    w = _integer_q4k(n_out, n_in, 7)
+    X = np.random.default_rng(3).integers(-8, 9, (8, n_in)).astype(np.float32)
+    Y = host(qwg.gemm_q4k(dev(w), dev(X)))
+    Yr, _ = oracle.gemm_q4k(w, X, n_in, n_out)
+    assert np.array_equal(Y.astype(np.float64), Yr)
+
+
+# ---------------------------------------------------------------- IQ3 GEMV
+
+@pytest.mark.parametrize("p", synth.config(4), ids=lambda p: p.name)
+def test_gemv_iq3_configs(p):
+    grid = synth.iq3_grid()
+    w, x = synth.weights(p), synth.inputs(p)
+    y = host(qwg.gemv_iq3(dev(w), dev(x), dev(grid)))
+    yr, sr = oracle.gemv_iq3(w, grid, x, p.n_in, p.n_out)
+    assert_bound(y, yr, sr, p.name)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 256), (65, 768), (100, 1280), (129, 5632),
+                                        (2000, 768), (131072 + 3, 256)])
+def test_gemv_iq3_ragged(n_out, n_in):
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 101, n_out)
+    x = synth.activations(n_in, 101, n_out)
+    y = host(qwg.gemv_iq3(dev(w), dev(x), dev(grid)))
+    yr, sr = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    assert_bound(y, yr, sr, f"{n_out}x{n_in}")
+
+
+def test_gemv_iq3_two_byte_aligned_base():
+    # rows of 98-byte blocks at a base address that is 2 mod 4
+    n_out, n_in = 70, 768
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 102, 0)
+    buf = torch.zeros(w.size + 16, dtype=torch.uint8, device=DEV)
+    buf[2:2 + w.size] = dev(w.reshape(-1))
+    wd = buf[2:2 + w.size]
+    assert wd.data_ptr() % 4 == 2
+    x = synth.activations(n_in, 102, 0)
+    y = host(qwg.gemv_iq3(wd, dev(x), dev(grid)))
+    yr, sr = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    assert_bound(y, yr, sr, "2 mod 4 base")
+    got = host(qwg.dequant_iq3(wd, dev(grid)))
+    assert_bits(got, oracle.dequant_iq3(w, grid, n_out * n_in), "dequant 2 mod 4 base")
+
+
+def test_gemv_iq3_integer_exact():
+    # d = 4 and code in 0..3 make every sub-block scale an odd integer (1, 3, 5, 7)
+    n_out, n_in = 150, 2048
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 103, 0).reshape(-1, 98).copy()
+    w[:, 96], w[:, 97] = 0x00, 0x44
+    words = w[:, 64:96].copy().view("<u4") & np.uint32(0x3FFFFFFF)
+    w[:, 64:96] = words.view(np.uint8)
+    w = w.reshape(n_out, -1)
+    x = np.random.default_rng(9).integers(-8, 9, n_in).astype(np.float32)
+    y = host(qwg.gemv_iq3(dev(w), dev(x), dev(grid)))
+    yr, _ = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    assert np.array_equal(y.astype(np.float64), yr)
+
+
+def test_gemv_iq3_one_hot_is_exact_column():
+    n_out, n_in = 66, 512
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 104, 0)
+    deq = oracle.dequant_iq3(w, grid, n_out * n_in).reshape(n_out, n_in)
+    wd, gd = dev(w), dev(grid)
+    for k in (0, 3, 4, 7, 8, 31, 32, 100, 255, 256, 511):
+        x = np.zeros(n_in, np.float32)
+        x[k] = 1.0
+        y = host(qwg.gemv_iq3(wd, dev(x), gd))
+        assert_bits(y + 0.0, deq[:, k] + 0.0, f"k={k}")
