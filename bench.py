@@ -4,15 +4,21 @@
 Workload (one "step" = one decoded token's weight stream at batch 1): the
 TinyLlama-1.1B-shaped Q4_K projections of 22 layers (q, o 2048x2048; k, v
 256x2048; gate, up 5632x2048; down 2048x5632) followed by the 2048->32000 LM
-head, 155 GEMVs launched back to back on one stream through the C ABI
-(qwg_gemv_q4k). Weights, activations and outputs are seeded synthetic data
-resident in HBM before timing starts; the 582 MB of distinct weights exceed the
-256 MB last-level cache, so every step streams them from HBM.
+head: 155 GEMVs, 582 MB of distinct packed weights (more than the 256 MB
+last-level cache, so every step streams them from HBM). Weights, activations
+and outputs are seeded synthetic data resident in HBM before timing starts.
+
+The headline runs the step as one grouped launch through the C ABI
+(qwg_group_run over the 155 independent GEMVs). Two more schedules of the same
+step are timed and reported beside it: "layered" (the launches a decoder whose
+layers depend on each other would make: per layer q|k|v grouped, o, gate|up
+grouped, down; then the LM head: 89 launches) and "per_call" (155
+qwg_gemv_q4k calls).
 
 Reported: value = algorithmic bytes of the step (weights + x + y) / wall time
-per step, in GB/s; the roofline object for the GEMV kernel (algorithmic bytes /
-kernel time, from HIP events around each launch in a separate pass over the same
-launches); and the CPU oracle's throughput on the host cores (cpu_baseline).
+per step, in GB/s; the roofline object for the grouped kernel (algorithmic bytes
+/ kernel time from HIP events around each launch on its stream); and the CPU
+oracle's throughput on the host cores (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 """
@@ -36,11 +42,30 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time budget for the oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 10 plain device-to-device copies of MIB "
+                         "MiB (reference for scaling hardware traffic counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_copy": 4 * n,
+                      "copy_calibration_bytes_written_per_copy": 4 * n, "copies": 10}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the GEMV path has no multi-GPU mode in this build "
               "(run with --gpus 1).", file=sys.stderr)
@@ -68,49 +93,71 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     sptr = ctypes.c_void_p(stream.cuda_stream)
+    step_bytes = sum(p.algorithmic_bytes for p in probs)
+    weight_bytes = sum(p.weight_bytes for p in probs)
+
+    group = qwg.Q4kGroup(zip(W, X, Y))
+    layered = []
+    i = 0
+    while i < len(probs):
+        name = probs[i].name.split(".")[-1]
+        if name in ("q", "gate"):
+            n = 3 if name == "q" else 2
+            layered.append(qwg.Q4kGroup(zip(W[i:i + n], X[i:i + n], Y[i:i + n])))
+            i += n
+        else:
+            layered.append(qwg.Q4kGroup([(W[i], X[i], Y[i])]))
+            i += 1
     calls = [(y.data_ptr(), x.data_ptr(), w.data_ptr(), p.n_in, p.n_out)
              for p, w, x, y in zip(probs, W, X, Y)]
     gemv = L.qwg_gemv_q4k
 
-    def step():
+    def step_grouped():
+        group.run(stream)
+
+    def step_layered():
+        for g in layered:
+            g.run(stream)
+
+    def step_per_call():
         for yp, xp, wp, n_in, n_out in calls:
             rc = gemv(yp, xp, wp, n_in, n_out, sptr)
             if rc:
                 raise RuntimeError(f"qwg_gemv_q4k failed: {rc}")
 
-    step_bytes = sum(p.algorithmic_bytes for p in probs)
-    weight_bytes = sum(p.weight_bytes for p in probs)
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    value = step_bytes * args.steps / elapsed / 1e9
+    sec = timed(step_grouped, args.steps, args.warmup)
+    ms_per_step = 1e3 * sec
+    value = step_bytes / sec / 1e9
+    sec_layered = timed(step_layered, max(5, args.steps // 5), 2)
+    sec_percall = timed(step_per_call, max(5, args.steps // 5), 2)
 
-    # Roofline pass: HIP events on the launch stream around every GEMV launch.
-    rsteps = max(1, min(args.steps, 10))
+    # Roofline: HIP events on the launch stream around every grouped launch.
+    rsteps = max(1, min(args.steps, 20))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(rsteps * len(calls))]
+          for _ in range(rsteps)]
     torch.cuda.synchronize()
-    i = 0
-    for _ in range(rsteps):
-        for yp, xp, wp, n_in, n_out in calls:
-            ev[i][0].record(stream)
-            gemv(yp, xp, wp, n_in, n_out, sptr)
-            ev[i][1].record(stream)
-            i += 1
+    for a, b in ev:
+        a.record(stream)
+        group.run(stream)
+        b.record(stream)
     torch.cuda.synchronize()
     kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / rsteps
-    launches_per_step = len(calls)
     achieved = step_bytes / (kernel_ms * 1e-3) / 1e9
-    lm = [j for j, p in enumerate(probs) if p.name == "lm_head"][0]
-    lm_ms = sum(ev[s * launches_per_step + lm][0].elapsed_time(ev[s * launches_per_step + lm][1])
-                for s in range(rsteps)) / rsteps
+
+    def sched(sec_, launches):
+        return {"us_per_step": round(1e6 * sec_, 1), "GBps": round(step_bytes / sec_ / 1e9, 1),
+                "pct_of_hbm_peak": round(100 * step_bytes / sec_ / 1e9 / HBM_PEAK_GBS, 1),
+                "tokens_per_s": round(1.0 / sec_, 1), "launches": launches}
 
     result = {
         "metric": "effective HBM GB/s (% of MI355X peak) for Q4_K/IQ3 GEMV, batch 1",
@@ -128,13 +175,18 @@ def main():
         "config": {
             "workload": "TinyLlama-1.1B Q4_K per-token weight stream, batch 1: 22 layers x "
                         "(q,o 2048x2048; k,v 256x2048; gate,up 5632x2048; down 2048x5632) + "
-                        "LM head 32000x2048, 155 qwg_gemv_q4k launches on one stream",
+                        "LM head 32000x2048 = 155 GEMVs, one grouped launch (qwg_group_run)",
             "weight_bytes": weight_bytes,
             "algorithmic_bytes_per_step": step_bytes,
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
             "tokens_per_s": round(1e3 / ms_per_step, 1),
-            "launches_per_step": launches_per_step,
+            "workgroups_per_launch": group.workgroups,
             "setup_s": round(setup_s, 1),
+            "schedules": {
+                "grouped": sched(sec, 1),
+                "layered": sched(sec_layered, len(layered)),
+                "per_call": sched(sec_percall, len(calls)),
+            },
         },
         "roofline": {
             "bound": "hbm",
@@ -143,11 +195,9 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "q4k_gemv_kernel<1>",
-            "kernel_ms_per_step": round(kernel_ms, 4),
-            "avg_launch_us": round(1e3 * kernel_ms / launches_per_step, 3),
-            "lm_head_us": round(1e3 * lm_ms, 3),
-            "lm_head_gbs": round(probs[lm].algorithmic_bytes / (lm_ms * 1e-3) / 1e9, 1),
+            "kernel": "q4k_stream_kernel<4,2> (grouped, 155 GEMVs per launch)",
+            "bytes_per_launch": step_bytes,
+            "kernel_us": round(1e3 * kernel_ms, 2),
         },
     }
 

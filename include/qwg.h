@@ -64,6 +64,7 @@ extern "C" {
 #define QWG_MAX_N_IN 65536          /* 256 super-blocks per row */
 #define QWG_MAX_N_OUT (1 << 24)
 #define QWG_MAX_BATCH 8
+#define QWG_MAX_GROUP 65536         /* GEMVs per grouped launch */
 
 /* Library version (major*10000 + minor*100 + patch). */
 int qwg_version(void);
@@ -132,6 +133,53 @@ int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int
  */
 int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
                  int batch, void *stream);
+
+/*
+ * qwg_gemm_q4k with an explicit work decomposition (tuning and testing):
+ * `waves` wavefronts per 64-row tile (4, 8 or 16; 0 = automatic) and `splits`
+ * workgroups sharing each tile's n_in sum (1..n_in/256; 0 = automatic). The
+ * result satisfies the same bound for every choice; the summation order (so
+ * the rounding) depends on it. Returns QWG_ERR_SHAPE for an unsupported
+ * choice (also when splits*batch*ceil(n_out/64)*64 partial sums exceed the
+ * split workspace of 2*2048*8*64 floats, or ceil(n_out/64) > 4096 with splits > 1).
+ */
+int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                    int batch, int waves, int splits, void *stream);
+
+/*
+ * Grouped GEMV: many independent Q4_K GEMVs in one launch (one grid whose
+ * workgroups belong to different matrices), for streams of independent
+ * weight-bound products such as the q/k/v or gate/up projections that share an
+ * activation vector, or a whole decode step's weight stream when its inputs are
+ * independent. Same math and accuracy as qwg_gemv_q4k for every member.
+ *
+ * qwg_gemv_desc: one member, fields as the qwg_gemv_q4k arguments (device
+ * pointers, same alignment and shape rules).
+ * qwg_group_create_q4k: validates every member (the first failing member's
+ * status is returned, nothing is allocated), then copies the launch plan to a
+ * device buffer owned by the group (hipMalloc + hipMemcpy: synchronous).
+ * `descs` is a host array of `count` members (1..QWG_MAX_GROUP) and is not
+ * kept. The member pointers are baked into the plan: reuse the same buffers
+ * (e.g. fixed activation/output buffers of a decode loop) on every run.
+ * qwg_group_run: enqueues the whole group on `stream` (asynchronous).
+ * qwg_group_workgroups: number of workgroups of one run, or a negative status.
+ * qwg_group_destroy: frees the plan (hipFree: synchronous; no run of the group
+ * may be pending). NULL is accepted.
+ */
+typedef struct qwg_gemv_desc {
+    float *y;
+    const float *x;
+    const void *w;
+    int64_t n_in;
+    int64_t n_out;
+} qwg_gemv_desc;
+
+typedef struct qwg_group qwg_group;
+
+int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **group);
+int qwg_group_run(const qwg_group *group, void *stream);
+int qwg_group_workgroups(const qwg_group *group);
+int qwg_group_destroy(qwg_group *group);
 
 #ifdef __cplusplus
 }

@@ -48,8 +48,14 @@ def lib() -> ctypes.CDLL:
         L.qwg_gemv_q4k.argtypes = [P, P, P, I64, I64, P]
         L.qwg_gemv_iq3.argtypes = [P, P, P, P, I64, I64, P]
         L.qwg_gemm_q4k.argtypes = [P, P, P, I64, I64, I, P]
+        L.qwg_gemm_q4k_ex.argtypes = [P, P, P, I64, I64, I, I, I, P]
+        L.qwg_group_create_q4k.argtypes = [P, I, ctypes.POINTER(P)]
+        L.qwg_group_run.argtypes = [P, P]
+        L.qwg_group_workgroups.argtypes = [P]
+        L.qwg_group_destroy.argtypes = [P]
         for f in ("qwg_dequant_q4k", "qwg_dequant_iq3", "qwg_gemv_q4k", "qwg_gemv_iq3",
-                  "qwg_gemm_q4k"):
+                  "qwg_gemm_q4k", "qwg_gemm_q4k_ex", "qwg_group_create_q4k", "qwg_group_run", "qwg_group_workgroups",
+                  "qwg_group_destroy"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -165,8 +171,10 @@ def gemv_iq3(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
     return out
 
 
-def gemm_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Y = X W^T for X fp32 [batch, n_in] (1 <= batch <= 8) -> [batch, n_out]."""
+def gemm_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+             waves: int = 0, splits: int = 0) -> torch.Tensor:
+    """Y = X W^T for X fp32 [batch, n_in] (1 <= batch <= 8) -> [batch, n_out].
+    waves/splits force the work decomposition (0 = automatic)."""
     _dev(x, "x", torch.float32)
     if x.dim() != 2 or not 1 <= x.shape[0] <= MAX_BATCH:
         raise ValueError("x must be [batch, n_in] with 1 <= batch <= 8")
@@ -177,6 +185,67 @@ def gemm_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) 
     _dev(out, "out", torch.float32)
     if out.shape != (batch, n_out):
         raise ValueError("out has the wrong shape")
-    _check(lib().qwg_gemm_q4k(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out, batch,
-                              _stream(x)), "qwg_gemm_q4k")
+    if waves or splits:
+        _check(lib().qwg_gemm_q4k_ex(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out, batch,
+                                     waves, splits, _stream(x)), "qwg_gemm_q4k_ex")
+    else:
+        _check(lib().qwg_gemm_q4k(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out, batch,
+                                  _stream(x)), "qwg_gemm_q4k")
     return out
+
+
+class GemvDesc(ctypes.Structure):
+    """qwg_gemv_desc: one member of a grouped launch."""
+    _fields_ = [("y", ctypes.c_void_p), ("x", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("n_in", ctypes.c_int64), ("n_out", ctypes.c_int64)]
+
+
+class Q4kGroup:
+    """Many independent Q4_K GEMVs y_i = W_i x_i run by one launch.
+
+    members: sequence of (w, x, y) device tensors (uint8 weights, fp32 x [n_in],
+    fp32 y [n_out]). The tensors are referenced by the plan (kept alive here) and
+    must stay in place; run() recomputes every y_i from the current x_i.
+    """
+
+    def __init__(self, members):
+        members = list(members)
+        if not members:
+            raise ValueError("a group needs at least one member")
+        descs = (GemvDesc * len(members))()
+        for i, (w, x, y) in enumerate(members):
+            _dev(x, "x", torch.float32)
+            _dev(y, "y", torch.float32)
+            n_in = x.numel()
+            n_out = _weights(w, n_in, Q4K_BYTES)
+            if y.numel() != n_out:
+                raise ValueError(f"member {i}: y has {y.numel()} elements, expected {n_out}")
+            descs[i] = GemvDesc(y.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out)
+        self._members = members
+        self._device = members[0][1].device
+        handle = ctypes.c_void_p()
+        _check(lib().qwg_group_create_q4k(descs, len(members), ctypes.byref(handle)),
+               "qwg_group_create_q4k")
+        self._handle = handle
+
+    @property
+    def workgroups(self) -> int:
+        return lib().qwg_group_workgroups(self._handle)
+
+    def run(self, stream=None) -> None:
+        if self._handle is None:
+            raise RuntimeError("group destroyed")
+        s = stream if stream is not None else torch.cuda.current_stream(self._device)
+        _check(lib().qwg_group_run(self._handle, ctypes.c_void_p(s.cuda_stream)), "qwg_group_run")
+
+    def close(self) -> None:
+        if self._handle is not None:
+            torch.cuda.synchronize(self._device)
+            _check(lib().qwg_group_destroy(self._handle), "qwg_group_destroy")
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

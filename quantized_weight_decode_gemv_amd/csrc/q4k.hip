@@ -6,36 +6,31 @@
 // 16+32c .. +31) gives weights 64c+t from its low nibbles (sub-block 2c) and
 // 64c+32+t from its high nibbles (sub-block 2c+1). Weight = d*sc_j*q - dmin*mn_j.
 //
-// GEMV design (one 64-row tile per workgroup, 4 wavefronts):
-//   * lane r of every wavefront owns output row (tile*64 + r); wavefront g owns
-//     quant chunk g (sub-blocks 2g, 2g+1) of every super-block, so all lanes of a
-//     wavefront need the same 64 activations at any moment: they come through
-//     scalar loads (SGPR operands), never through LDS or VGPRs;
-//   * the tile's 64 x 144-byte blocks of one super-block column are fetched with
-//     coalesced 16-byte loads (each row's block is contiguous) into registers one
-//     column ahead, then written to a double-buffered LDS stage and read back per
-//     lane (row stride 144 B = 36 dwords: conflict-free for 16-byte reads);
+// GEMV design (one 64-row tile per workgroup of W = 4, 8 or 16 wavefronts):
+//   * lane r of every wavefront owns output row tile*64 + r; wavefront 4j+G owns
+//     quant chunk G (sub-blocks 2G, 2G+1) of the j-th super-block of each
+//     pipeline stage, so all lanes of a wavefront need the same 64 activations:
+//     they come through scalar loads as SGPR operands, never through LDS/VGPRs;
+//   * each stage (64 rows x W/4 super-blocks) is copied into LDS by LDS-DMA
+//     (global_load_lds_dwordx4, 16 bytes per lane, coalesced: a row's block is
+//     contiguous) while the previous stage is computed; every wavefront counts
+//     its own copies (s_waitcnt vmcnt) before the stage barrier;
 //   * a nibble is placed in an fp16 register half as a subnormal bit pattern
 //     (value q*2^-24, or q*2^-20 for a high nibble masked in place), which
 //     v_fma_mix_f32 widens exactly inside the FMA: one VALU op per weight;
 //   * per sub-block the sum is factored: d*sc*sum(q*x) - dmin*mn*sum(x), with
 //     sum(x) per 32-weight sub-block computed once per workgroup into LDS;
-//   * a row's super-block range may be split over several workgroups (the
-//     partial sums meet in tile_epilogue) so that small matrices still occupy
-//     every compute unit.
+//   * the W wavefronts' row sums meet in LDS; for small matrices a row's
+//     super-block range may also be split over several workgroups (the partial
+//     sums meet in tile_epilogue) so that every compute unit gets work. A
+//     grouped launch runs many independent GEMVs in one grid.
 #include "qwg_device.h"
 
 namespace qwg {
 
 namespace {
 
-constexpr int kThreads = 256;                        // 4 wavefronts
 constexpr int kStageBytes = kTileRows * kQ4kBytes;   // 9216: one super-block column of a tile
-constexpr int kStageChunks = kStageBytes / 16;       // 576 16-byte chunks
-static_assert(kStageChunks == 2 * kThreads + 64, "stage = two chunks per thread + one per lane of wavefront 0");
-
-// Super-blocks whose per-sub-block activation sums fit the 16 KB sum buffer.
-__host__ __device__ constexpr int sx_chunk_blocks(int nb_batch) { return 512 / nb_batch; }
 
 // ------------------------------------------------------------------ dequant
 
@@ -106,8 +101,8 @@ __device__ __forceinline__ void q4k_scales(const uint4 &h, uint32_t &sc0, uint32
 // Wavefront G's share of one super-block for this lane's row: quant chunk G.
 // xg points at x[256*b + 64*G] of batch element 0 (uniform across the wave).
 template <int G, int NB>
-__device__ __forceinline__ void q4k_chunk(const uint8_t *rowp, cfloat_p xg,
-                                          int n_in, const float *sx, int sx_stride,
+__device__ __forceinline__ void q4k_chunk(const uint8_t *rowp, cfloat_p xg, int n_in,
+                                          const float (&sx0)[NB], const float (&sx1)[NB],
                                           uint32_t mlo, uint32_t mhi, float (&acc)[NB]) {
     const uint4 h = *(const uint4 *)rowp;
     const uint4 qa = *(const uint4 *)(rowp + 16 + 32 * G);
@@ -142,74 +137,82 @@ __device__ __forceinline__ void q4k_chunk(const uint8_t *rowp, cfloat_p xg,
             s1 = __builtin_fmaf(h2f_hi(eh), xb[32 + 4 * m + 2], s1);
             s1 = __builtin_fmaf(h2f_hi(oh), xb[32 + 4 * m + 3], s1);
         }
-        const float sx0 = sx[bt * sx_stride + 2 * G];
-        const float sx1 = sx[bt * sx_stride + 2 * G + 1];
         float a = acc[bt];
         a = __builtin_fmaf(dsc0, s0, a);
         a = __builtin_fmaf(dsc1, s1, a);
-        a = __builtin_fmaf(-dmn0, sx0, a);
-        a = __builtin_fmaf(-dmn1, sx1, a);
+        a = __builtin_fmaf(-dmn0, sx0[bt], a);
+        a = __builtin_fmaf(-dmn1, sx1[bt], a);
         acc[bt] = a;
     }
 }
 
-template <int G, int NB>
+// One pipeline stage holds BPS = W/4 super-block columns of the 64-row tile,
+// laid out [block j][row r][144 B]: a row stride of 144 B (36 dwords) puts the
+// 16-byte reads of 16 consecutive lanes in distinct banks. Wavefront w = 4j+G
+// copies rows 16G..16G+15 of block j into the stage (144 chunks of 16 bytes:
+// LDS-DMA instructions of 64, 64 and 16 lanes) and computes quant chunk G of
+// block j for all 64 rows. Two stage buffers: the copy of stage s+1 runs while
+// stage s is computed.
+template <int G, int NB, int W>
 __device__ __forceinline__ void q4k_tile(const GemvArgs &a, uint8_t *smem, int tile, int split) {
+    constexpr int BPS = W / 4;
+    constexpr int SBYTES = BPS * kStageBytes;
+    // sum(x) is kept for SXB super-blocks at a time (16 KB), a multiple of BPS.
+    constexpr int SXB = ((512 / NB) / BPS) * BPS;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    const int j = __builtin_amdgcn_readfirstlane(tid >> 8);   // block within the stage
+    const int wave = 4 * j + G;
     const int kb0 = (int)((int64_t)split * a.nb / a.splits);
     const int kb1 = (int)((int64_t)(split + 1) * a.nb / a.splits);
     const int nblk = kb1 - kb0;
+    const int nst = (nblk + BPS - 1) / BPS;
     const int row0 = tile * kTileRows;
 
-    uint8_t *stage = smem;                                     // [2][kStageBytes]
-    float *sx = (float *)(smem + 2 * kStageBytes);             // [NB][8*chunk]
-    // sum(x) is kept for at most kSxChunk(NB) super-blocks at a time.
-    const int chunk = min(nblk, sx_chunk_blocks(NB));
-    const int sx_stride = 8 * chunk;
+    float *sx = (float *)(smem + 2 * SBYTES);               // [NB][8 * min(nblk, SXB)]
+    const int sx_stride = 8 * min(nblk, SXB);
 
-    // 16-byte chunks this thread moves per stage: chunk c is byte 16*(c%9) of
-    // the block of tile row c/9 (rows past n_out re-read the last row). Chunks
-    // tid and tid+256 for everyone, tid+512 for wavefront 0 (576 in all).
-    auto chunk_off = [&](int c) -> int64_t {
-        const int r = c / 9;
-        const int part = c - 9 * r;
-        const int rg = min(row0 + r, a.n_out - 1);
-        return (int64_t)rg * a.row_bytes + 16 * part;
-    };
-    const int64_t goff0 = chunk_off(tid);
-    const int64_t goff1 = chunk_off(tid + kThreads);
-    const int64_t goff2 = chunk_off(G == 0 ? tid + 2 * kThreads : tid);
-
-    // sum(x) over each 32-weight sub-block of super-blocks [c0, c0 + chunk),
-    // k ascending. The barrier that publishes it is the first one of the stage
-    // loop below.
-    auto sum_x = [&](int c0, int c1) {
-        const int n = 8 * (c1 - c0);
-        for (int j = tid; j < NB * n; j += kThreads) {
-            const int bt = j / n;
-            const int sb = j - bt * n;
-            const float4 *xp = (const float4 *)(a.x + (int64_t)bt * a.n_in + 32 * (8 * c0 + sb));
-            float s = 0.0f;
+    // This wavefront's 16-byte chunks k = 64i + lane (i = 0, 1) and 128 + lane
+    // (lanes 0..15): tile row 16G + k/9, byte 16*(k%9) of the block. Rows past
+    // n_out re-read the last row.
+    int64_t goff[3];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 v = xp[i];
-                s += v.x;
-                s += v.y;
-                s += v.z;
-                s += v.w;
-            }
-            sx[bt * sx_stride + sb] = s;
+    for (int i = 0; i < 3; ++i) {
+        const int k = (i < 2 || lane < 16) ? 64 * i + lane : 128;
+        const int r = 16 * G + k / 9;
+        goff[i] = (int64_t)min(row0 + r, a.n_out - 1) * a.row_bytes + 16 * (k % 9);
+    }
+    const uint32_t lds_base = (uint32_t)(uintptr_t)smem + j * kStageBytes + 2304 * G;
+    auto issue = [&](int s) {
+        const int b = kb0 + s * BPS + j;
+        if (b < kb1) {
+            const uint8_t *base = a.w + (int64_t)b * kQ4kBytes;
+            const uint32_t dst = lds_base + (s & 1) * SBYTES;
+            dma16(base + goff[0], dst);
+            dma16(base + goff[1], dst + 1024);
+            if (lane < 16) dma16(base + goff[2], dst + 2048);
         }
     };
 
-    uint4 r0, r1, r2 = make_uint4(0, 0, 0, 0);
-    {
-        const uint8_t *base = a.w + (int64_t)kb0 * kQ4kBytes;
-        r0 = *(const uint4 *)(base + goff0);
-        r1 = *(const uint4 *)(base + goff1);
-        if constexpr (G == 0) r2 = *(const uint4 *)(base + goff2);
-    }
+    // sum(x) over each 32-weight sub-block of super-blocks [c0, c1), k ascending.
+    auto sum_x = [&](int c0, int c1) {
+        const int n = 8 * (c1 - c0);
+        for (int q = tid; q < NB * n; q += W * 64) {
+            const int bt = q / n;
+            const int sb = q - bt * n;
+            const float4 *xp = (const float4 *)(a.x + (int64_t)bt * a.n_in + 32 * (8 * c0 + sb));
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 v = xp[i];
+                sum += v.x;
+                sum += v.y;
+                sum += v.z;
+                sum += v.w;
+            }
+            sx[bt * sx_stride + sb] = sum;
+        }
+    };
 
     const uint32_t mlo = opaque(0x000F000Fu);
     const uint32_t mhi = opaque(0x00F000F0u);
@@ -217,63 +220,300 @@ __device__ __forceinline__ void q4k_tile(const GemvArgs &a, uint8_t *smem, int t
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) acc[bt] = 0.0f;
 
-    int cend = kb0;
-    for (int b = kb0; b < kb1; ++b) {
-        if (b == cend) {
-            // New sum(x) chunk; past the first, wait until every wavefront has
-            // finished with the previous chunk's sums.
-            if (b != kb0) __syncthreads();
-            cend = min(b + chunk, kb1);
-            sum_x(b, cend);
+    issue(0);
+    for (int s = 0; s < nst; ++s) {
+        // New sum(x) chunk: every wavefront is past the previous stage's barrier.
+        if ((s * BPS) % SXB == 0) sum_x(kb0 + s * BPS, min(kb0 + s * BPS + SXB, kb1));
+        if (s + 1 < nst) issue(s + 1);
+        // This wavefront's copies of stage s are done once at most the copies of
+        // stage s+1 (3 instructions, if it issued any) are outstanding.
+        if (s + 1 < nst && kb0 + (s + 1) * BPS + j < kb1)
+            wait_vmcnt<3>();
+        else
+            wait_vmcnt<0>();
+        lds_barrier();  // stage s and the sums are complete for every wavefront
+        const int b = kb0 + s * BPS + j;
+        if (b < kb1) {
+            const uint8_t *rowp = smem + (s & 1) * SBYTES + j * kStageBytes + lane * kQ4kBytes;
+            const float *sxb = sx + 8 * ((b - kb0) % SXB) + 2 * G;
+            float sx0[NB], sx1[NB];
+#pragma unroll
+            for (int bt = 0; bt < NB; ++bt) {
+                sx0[bt] = sxb[bt * sx_stride];
+                sx1[bt] = sxb[bt * sx_stride + 1];
+            }
+            q4k_chunk<G, NB>(rowp, as_scalar(a.x) + (int64_t)kQK * b + 64 * G, a.n_in, sx0, sx1,
+                             mlo, mhi, acc);
         }
-        uint8_t *buf = stage + ((b - kb0) & 1) * kStageBytes;
-        *(uint4 *)(buf + 16 * tid) = r0;
-        *(uint4 *)(buf + 16 * (tid + kThreads)) = r1;
-        if constexpr (G == 0) *(uint4 *)(buf + 16 * (tid + 2 * kThreads)) = r2;
-        if (b + 1 < kb1) {
-            const uint8_t *base = a.w + (int64_t)(b + 1) * kQ4kBytes;
-            r0 = *(const uint4 *)(base + goff0);
-            r1 = *(const uint4 *)(base + goff1);
-            if constexpr (G == 0) r2 = *(const uint4 *)(base + goff2);
-        }
-        __syncthreads();
-        cfloat_p xg = as_scalar(a.x) + (int64_t)kQK * b + 64 * G;
-        q4k_chunk<G, NB>(buf + lane * kQ4kBytes, xg, a.n_in, sx + 8 * ((b - kb0) % chunk),
-                         sx_stride, mlo, mhi, acc);
+        lds_barrier();  // stage buffer s&1 and the sums may be overwritten
     }
 
-    // Cross-wavefront sum of the four chunks, in chunk order. The red buffer
-    // overlays stage 0, which nobody reads after the barrier below.
-    __syncthreads();
-    float *red = (float *)smem;  // [4][NB][64]
+    // Cross-wavefront sum in wavefront order (blocks j, then chunks G). The
+    // buffer overlays stage 0, idle after the last barrier.
+    float *red = (float *)smem;  // [W][NB][64]
 #pragma unroll
-    for (int bt = 0; bt < NB; ++bt) red[(G * NB + bt) * 64 + lane] = acc[bt];
-    __syncthreads();
-    if constexpr (G == 0) {
+    for (int bt = 0; bt < NB; ++bt) red[(wave * NB + bt) * 64 + lane] = acc[bt];
+    lds_barrier();
+    if (wave == 0) {
         float total[NB];
 #pragma unroll
         for (int bt = 0; bt < NB; ++bt) {
-            float t = red[(0 * NB + bt) * 64 + lane];
-            t += red[(1 * NB + bt) * 64 + lane];
-            t += red[(2 * NB + bt) * 64 + lane];
-            t += red[(3 * NB + bt) * 64 + lane];
+            float t = red[bt * 64 + lane];
+            for (int w = 1; w < W; ++w) t += red[(w * NB + bt) * 64 + lane];
             total[bt] = t;
         }
         tile_epilogue<NB>(a, tile, split, total);
     }
 }
 
-template <int NB>
-__global__ __launch_bounds__(kThreads) void q4k_gemv_kernel(GemvArgs a) {
+template <int NB, int W>
+__device__ __forceinline__ void q4k_dispatch(const GemvArgs &a, uint8_t *smem, int tile, int split) {
+    switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
+        case 0: q4k_tile<0, NB, W>(a, smem, tile, split); break;
+        case 1: q4k_tile<1, NB, W>(a, smem, tile, split); break;
+        case 2: q4k_tile<2, NB, W>(a, smem, tile, split); break;
+        default: q4k_tile<3, NB, W>(a, smem, tile, split); break;
+    }
+}
+
+template <int NB, int W>
+__global__ __launch_bounds__(W * 64) void q4k_gemv_kernel(GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tile = blockIdx.x / a.splits;
-    const int split = blockIdx.x - tile * a.splits;
-    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-        case 0: q4k_tile<0, NB>(a, smem, tile, split); break;
-        case 1: q4k_tile<1, NB>(a, smem, tile, split); break;
-        case 2: q4k_tile<2, NB>(a, smem, tile, split); break;
-        default: q4k_tile<3, NB>(a, smem, tile, split); break;
+    q4k_dispatch<NB, W>(a, smem, tile, blockIdx.x - tile * a.splits);
+}
+
+typedef const __attribute__((address_space(4))) GemvArgs *cargs_p;
+typedef const __attribute__((address_space(4))) uint32_t *cu32_p;
+
+__device__ __forceinline__ void load_args(GemvArgs &a, cargs_p pa) {
+    a.w = pa->w;
+    a.x = pa->x;
+    a.grid = pa->grid;
+    a.y = pa->y;
+    a.partial = pa->partial;
+    a.counters = pa->counters;
+    a.row_bytes = pa->row_bytes;
+    a.n_in = pa->n_in;
+    a.n_out = pa->n_out;
+    a.nb = pa->nb;
+    a.tiles = pa->tiles;
+    a.splits = pa->splits;
+    a.wg_begin = pa->wg_begin;
+}
+
+// Grouped launch (one workgroup per item): each workgroup reads its problem
+// index and descriptor with scalar loads, then runs the same tile pipeline.
+
+template <int W>
+__global__ __launch_bounds__(W * 64) void q4k_group_kernel(GroupArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    GemvArgs a;
+    load_args(a, (cargs_p)g.problems + ((cu32_p)g.map)[blockIdx.x]);
+    const int local = blockIdx.x - a.wg_begin;
+    const int tile = local / a.splits;
+    q4k_dispatch<1, W>(a, smem, tile, local - tile * a.splits);
+}
+
+// ------------------------------------------------------------------ stream engine
+//
+// Persistent variant for batch 1: a grid of about one workgroup per LDS slot of
+// the chip walks a list of "items" (one 64-row tile of one matrix, all or part
+// of its super-block range), item k, k + gridDim.x, ... . The LDS ring of R
+// stages runs ahead across item boundaries, so a workgroup's copy engine never
+// idles between tiles. Each stage copy also brings the 64 activations of every
+// wavefront's quant chunk (lanes 16..31 of its third DMA instruction), from
+// which the wavefront forms its two 32-weight activation sums with a DPP
+// reduction: no per-item prologue and no shared sum buffer.
+template <int W, int R>
+struct StreamCfg {
+    static constexpr int kBps = W / 4;
+    static constexpr int kQuarter = 16 * kQ4kBytes + 256;   // 16 rows + 64 activations
+    static constexpr int kBlock = 4 * kQuarter;             // 10240
+    static constexpr int kSlot = kBps * kBlock;
+    static constexpr int kRed = R * kSlot;                  // [W][64] fp32 row sums
+    static constexpr int kLds = kRed + W * 64 * 4;
+};
+
+// One item as seen by a cursor (stream items are never split: the whole row).
+struct Item {
+    const uint8_t *w;
+    const float *x;
+    float *y;
+    int64_t row_bytes;
+    int n_out;
+    int nb;
+    int nst;   // stages = ceil(nb / BPS)
+    int row0;
+};
+
+template <int BPS>
+__device__ __forceinline__ void load_item(Item &it, int k, const GroupArgs &g, const GemvArgs &single) {
+    if (g.problems == nullptr) {
+        it.w = single.w;
+        it.x = single.x;
+        it.y = single.y;
+        it.row_bytes = single.row_bytes;
+        it.n_out = single.n_out;
+        it.nb = single.nb;
+        it.row0 = k * kTileRows;
+    } else {
+        const cargs_p pa = (cargs_p)g.problems + ((cu32_p)g.map)[k];
+        it.w = pa->w;
+        it.x = pa->x;
+        it.y = pa->y;
+        it.row_bytes = pa->row_bytes;
+        it.n_out = pa->n_out;
+        it.nb = pa->nb;
+        it.row0 = (k - pa->wg_begin) * kTileRows;
     }
+    it.nst = (it.nb + BPS - 1) / BPS;
+}
+
+// Sum of v over lanes 0..31 and over lanes 32..63 (each lane gets its half's
+// sum; the butterfly makes every lane's value bitwise identical).
+__device__ __forceinline__ float half_wave_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    v += __shfl_xor(v, 16);
+    return v;
+}
+
+template <int G, int W, int R>
+__device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &single, int nitems,
+                                           uint8_t *smem) {
+    static_assert(R >= 2 && R <= 3, "ring of two or three stages");
+    using C = StreamCfg<W, R>;
+    constexpr int BPS = C::kBps;
+    const int lane = threadIdx.x & 63;
+    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+    const int wave = 4 * j + G;
+    const int stride = gridDim.x;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    // This wavefront's copy lanes: chunks k = 64i + lane of its 16 rows (row
+    // 16G + k/9, byte 16*(k%9)); lanes 16..31 of the third instruction copy the
+    // 64 activations of quant chunk G instead (4 per lane).
+    int crow[3], cpart[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int k = (i < 2 || lane < 16) ? 64 * i + lane : 128;
+        crow[i] = 16 * G + k / 9;
+        cpart[i] = 16 * (k % 9);
+    }
+    const int64_t xoff = 4 * (64 * G + 4 * (lane - 16));   // bytes, lanes 16..31
+
+    int kc = blockIdx.x;  // item being computed
+    if (kc >= nitems) return;
+    Item c;
+    load_item<BPS>(c, kc, g, single);
+
+    // copy cursor: next stage sd of item kd goes to ring slot slot_d
+    int kd = kc, sd = 0, slot_d = 0, pending = 0;
+    Item d = c;
+    int64_t doff[3];
+    auto prep_copy = [&]() {
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            doff[i] = (int64_t)min(d.row0 + crow[i], d.n_out - 1) * d.row_bytes + cpart[i];
+    };
+    prep_copy();
+    uint32_t flags = 0;  // bit k: this wavefront's copies are in ring slot k
+    auto issue_next = [&]() {
+        if (kd >= nitems) return;
+        const int b = sd * BPS + j;
+        if (b < d.nb) {
+            const uint32_t base = lds0 + slot_d * C::kSlot + j * C::kBlock + G * C::kQuarter;
+            const uint8_t *wb = d.w + (int64_t)b * kQ4kBytes;
+            dma16(wb + doff[0], base);
+            dma16(wb + doff[1], base + 1024);
+            if (lane < 32) {
+                const uint8_t *src = lane < 16 ? wb + doff[2]
+                                               : (const uint8_t *)d.x + (int64_t)(kQK * 4) * b + xoff;
+                dma16(src, base + 2048);
+            }
+            flags |= 1u << slot_d;
+        } else {
+            flags &= ~(1u << slot_d);
+        }
+        ++pending;
+        slot_d = slot_d + 1 == R ? 0 : slot_d + 1;
+        if (++sd == d.nst) {
+            sd = 0;
+            kd += stride;
+            if (kd < nitems) {
+                load_item<BPS>(d, kd, g, single);
+                prep_copy();
+            }
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) issue_next();
+
+    const uint32_t mlo = opaque(0x000F000Fu);
+    const uint32_t mhi = opaque(0x00F000F0u);
+    float *red = (float *)(smem + C::kRed);
+    int slot_c = 0;
+    for (;;) {
+        float acc[1] = {0.0f};
+        for (int s = 0; s < c.nst; ++s) {
+            // With three slots, the next stage may already be in flight: allow
+            // its three copies (if this wavefront issued any) to stay pending.
+            const int nxt = slot_c + 1 == R ? 0 : slot_c + 1;
+            if (R == 3 && pending > 1 && ((flags >> nxt) & 1u))
+                wait_vmcnt<3>();
+            else
+                wait_vmcnt<0>();
+            lds_barrier();   // stage in slot_c complete for every wavefront
+            issue_next();    // refill the slot computed in the previous step
+            const int b = s * BPS + j;
+            if (b < c.nb) {
+                const uint8_t *blk = smem + slot_c * C::kSlot + j * C::kBlock;
+                const uint8_t *rowp = blk + (lane >> 4) * C::kQuarter + (lane & 15) * kQ4kBytes;
+                const float xs = ((const float *)(blk + G * C::kQuarter + 16 * kQ4kBytes))[lane];
+                const float hs = half_wave_sum(xs);
+                const float sx0[1] = {__builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hs), 0))};
+                const float sx1[1] = {__builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hs), 32))};
+                q4k_chunk<G, 1>(rowp, as_scalar(c.x) + (int64_t)kQK * b + 64 * G, 0, sx0, sx1, mlo,
+                                mhi, acc);
+            }
+            --pending;
+            slot_c = nxt;
+        }
+        // row sums of the W wavefronts, in wavefront order
+        red[wave * 64 + lane] = acc[0];
+        lds_barrier();
+        if (wave == 0) {
+            float tsum = red[lane];
+            for (int w = 1; w < W; ++w) tsum += red[w * 64 + lane];
+            if (c.row0 + lane < c.n_out) c.y[c.row0 + lane] = tsum;
+        }
+        kc += stride;
+        if (kc >= nitems) break;
+        load_item<BPS>(c, kc, g, single);
+    }
+}
+
+template <int W, int R>
+__global__ __launch_bounds__(W * 64) void q4k_stream_kernel(GroupArgs g, GemvArgs single, int nitems) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
+        case 0: q4k_stream<0, W, R>(g, single, nitems, smem); break;
+        case 1: q4k_stream<1, W, R>(g, single, nitems, smem); break;
+        case 2: q4k_stream<2, W, R>(g, single, nitems, smem); break;
+        default: q4k_stream<3, W, R>(g, single, nitems, smem); break;
+    }
+}
+
+template <int W>
+size_t q4k_lds_bytes(int batch, int max_blk) {
+    const int sxb = ((512 / batch) / (W / 4)) * (W / 4);
+    if (max_blk > sxb) max_blk = sxb;
+    return 2 * (size_t)(W / 4) * kStageBytes + sizeof(float) * (size_t)batch * 8 * max_blk;
 }
 
 }  // namespace
@@ -286,25 +526,72 @@ hipError_t launch_q4k_dequant(const uint8_t *src, float *dst, int64_t nblocks, h
     return hipGetLastError();
 }
 
-hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, hipStream_t s) {
-    if (batch < 1 || batch > 8) return hipErrorInvalidValue;
-    int max_blk = (a.nb + a.splits - 1) / a.splits;
-    if (max_blk > sx_chunk_blocks(batch)) max_blk = sx_chunk_blocks(batch);
-    size_t lds = 2 * (size_t)kStageBytes + sizeof(float) * (size_t)batch * 8 * max_blk;
-    const size_t red = sizeof(float) * 4 * (size_t)batch * 64;
-    if (lds < red) lds = red;
-    const dim3 grid((unsigned)(a.tiles * a.splits));
+template <int W>
+hipError_t launch_q4k_gemv_w(const GemvArgs &a, int batch, hipStream_t s) {
+    const size_t lds = q4k_lds_bytes<W>(batch, (a.nb + a.splits - 1) / a.splits);
+    const dim3 grid((unsigned)(a.tiles * a.splits)), block(W * 64);
     switch (batch) {
-        case 1: hipLaunchKernelGGL(q4k_gemv_kernel<1>, grid, dim3(kThreads), lds, s, a); break;
-        case 2: hipLaunchKernelGGL(q4k_gemv_kernel<2>, grid, dim3(kThreads), lds, s, a); break;
-        case 3: hipLaunchKernelGGL(q4k_gemv_kernel<3>, grid, dim3(kThreads), lds, s, a); break;
-        case 4: hipLaunchKernelGGL(q4k_gemv_kernel<4>, grid, dim3(kThreads), lds, s, a); break;
-        case 5: hipLaunchKernelGGL(q4k_gemv_kernel<5>, grid, dim3(kThreads), lds, s, a); break;
-        case 6: hipLaunchKernelGGL(q4k_gemv_kernel<6>, grid, dim3(kThreads), lds, s, a); break;
-        case 7: hipLaunchKernelGGL(q4k_gemv_kernel<7>, grid, dim3(kThreads), lds, s, a); break;
-        case 8: hipLaunchKernelGGL(q4k_gemv_kernel<8>, grid, dim3(kThreads), lds, s, a); break;
+        case 1: hipLaunchKernelGGL((q4k_gemv_kernel<1, W>), grid, block, lds, s, a); break;
+        case 2: hipLaunchKernelGGL((q4k_gemv_kernel<2, W>), grid, block, lds, s, a); break;
+        case 3: hipLaunchKernelGGL((q4k_gemv_kernel<3, W>), grid, block, lds, s, a); break;
+        case 4: hipLaunchKernelGGL((q4k_gemv_kernel<4, W>), grid, block, lds, s, a); break;
+        case 5: hipLaunchKernelGGL((q4k_gemv_kernel<5, W>), grid, block, lds, s, a); break;
+        case 6: hipLaunchKernelGGL((q4k_gemv_kernel<6, W>), grid, block, lds, s, a); break;
+        case 7: hipLaunchKernelGGL((q4k_gemv_kernel<7, W>), grid, block, lds, s, a); break;
+        case 8: hipLaunchKernelGGL((q4k_gemv_kernel<8, W>), grid, block, lds, s, a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, int waves, hipStream_t s) {
+    switch (waves) {
+        case 4: return launch_q4k_gemv_w<4>(a, batch, s);
+        case 8: return launch_q4k_gemv_w<8>(a, batch, s);
+        case 16: return launch_q4k_gemv_w<16>(a, batch, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int W, int R>
+hipError_t launch_stream_wr(const GroupArgs &g, const GemvArgs &single, int nitems, hipStream_t s) {
+    using C = StreamCfg<W, R>;
+    static int per_cu = -1, cus = 0;
+    if (per_cu < 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, q4k_stream_kernel<W, R>, W * 64,
+                                                         C::kLds) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        if (cus < 1) cus = 256;
+    }
+    int grid = per_cu * cus;
+    if (grid > nitems) grid = nitems;
+    hipLaunchKernelGGL((q4k_stream_kernel<W, R>), dim3((unsigned)grid), dim3(W * 64), C::kLds, s, g,
+                       single, nitems);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nitems, int waves,
+                             int ring, hipStream_t s) {
+    switch (waves * 10 + ring) {
+        case 42: return launch_stream_wr<4, 2>(g, single, nitems, s);
+        case 43: return launch_stream_wr<4, 3>(g, single, nitems, s);
+        case 82: return launch_stream_wr<8, 2>(g, single, nitems, s);
+        case 83: return launch_stream_wr<8, 3>(g, single, nitems, s);
+        case 162: return launch_stream_wr<16, 2>(g, single, nitems, s);
+        case 163: return launch_stream_wr<16, 3>(g, single, nitems, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_q4k_group(const GroupArgs &g, int total_workgroups, int max_nb, hipStream_t s) {
+    constexpr int W = kQ4kWavesLarge;
+    const size_t lds = q4k_lds_bytes<W>(1, max_nb);
+    hipLaunchKernelGGL((q4k_group_kernel<W>), dim3((unsigned)total_workgroups), dim3(W * 64), lds, s,
+                       g);
     return hipGetLastError();
 }
 

@@ -3,7 +3,10 @@
 // so a rejected call touches neither the device nor the output buffers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
+#include <new>
+#include <vector>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -23,36 +26,82 @@ int check_gemv_shape(int64_t n_in, int64_t n_out) {
     return QWG_OK;
 }
 
-// Workgroups wanted per launch: enough 4-wavefront groups to give every one of
-// the 256 compute units several, so small matrices split their rows' block
-// ranges rather than idle most of the chip. QWG_TARGET_WGS overrides it (tuning).
-int target_workgroups() {
-    static int v = [] {
-        const char *e = getenv("QWG_TARGET_WGS");
-        int t = e ? atoi(e) : 0;
-        return t > 0 ? t : 2048;
-    }();
+int env_int(const char *name, int dflt) {
+    const char *e = getenv(name);
+    const int v = e ? atoi(e) : 0;
+    return v > 0 ? v : dflt;
+}
+
+// Work decomposition of one GEMV/GEMM: W wavefronts per 64-row tile (W/4
+// super-blocks per pipeline stage) and the number of workgroups that split each
+// tile's super-block range. Matrices with many tiles use 16-wavefront groups
+// and no split; small ones use 4-wavefront groups and split the row sums so the
+// grid still covers every compute unit (about kSplitTargetWgs workgroups).
+// QWG_WAVES / QWG_TARGET_WGS override the choice (tuning experiments).
+constexpr int kLargeTiles = 256;
+constexpr int kSplitTargetWgs = 2048;
+constexpr size_t kWsPartialFloats = (size_t)2 * kSplitTargetWgs * QWG_MAX_BATCH * kTileRows;
+constexpr size_t kWsCounters = 2 * kSplitTargetWgs;
+
+struct Plan {
+    int waves;
+    int splits;
+};
+
+Plan choose_plan(int tiles, int nb, int batch) {
+    static const int env_waves = env_int("QWG_WAVES", 0);
+    static const int env_target = env_int("QWG_TARGET_WGS", 0);
+    Plan p;
+    p.waves = env_waves ? env_waves : (tiles >= kLargeTiles ? kQ4kWavesLarge : kQ4kWavesSmall);
+    if (p.waves != 4 && p.waves != 8 && p.waves != 16) p.waves = kQ4kWavesSmall;
+    const int target = env_target ? env_target : (tiles >= kLargeTiles ? 1 : kSplitTargetWgs);
+    int s = (target + tiles - 1) / tiles;
+    if (s > nb) s = nb;
+    if (s < 1) s = 1;
+    // keep the partial sums inside the workspace
+    while (s > 1 && ((size_t)s * batch * tiles * kTileRows > kWsPartialFloats ||
+                     (size_t)tiles > kWsCounters))
+        --s;
+    p.splits = s;
+    return p;
+}
+
+int choose_splits(int tiles, int nb) { return choose_plan(tiles, nb, 1).splits; }
+
+// Persistent stream engine shape (wavefronts per workgroup, LDS ring stages).
+// Measured on MI355X: grouped streams run best with 4-wavefront workgroups and
+// a 2-stage ring (more resident workgroups per CU); a single large matrix, with
+// fewer tiles than workgroup slots, with 8 wavefronts per tile.
+// QWG_STREAM_WAVES / QWG_STREAM_RING override both (tuning experiments).
+struct StreamShape {
+    int waves;
+    int ring;
+};
+
+StreamShape stream_shape(bool grouped) {
+    static const int env_w = env_int("QWG_STREAM_WAVES", 0);
+    static const int env_r = env_int("QWG_STREAM_RING", 0);
+    StreamShape sh;
+    sh.waves = env_w ? env_w : (grouped ? 4 : 8);
+    sh.ring = env_r ? env_r : 2;
+    return sh;
+}
+
+bool use_stream_engine() {
+    static const bool v = env_int("QWG_TILE_ENGINE", 0) == 0;
     return v;
 }
 
-int choose_splits(int tiles, int nb) {
-    int s = (target_workgroups() + tiles - 1) / tiles;
-    if (s > nb) s = nb;
-    if (s < 1) s = 1;
-    return s;
-}
-
 // Split-sum workspace, one per (device, stream): partial sums [splits][batch]
-// [tiles*64] fp32 followed by one counter per tile. Sized for the largest use:
-// splits > 1 only when tiles < target (so splits*tiles < 2*target), times the
-// batch and 64 rows, plus counters.
+// [tiles*64] fp32 followed by one counter per tile (choose_plan keeps every
+// plan inside these sizes).
 struct Workspace {
     float *partial = nullptr;
     uint32_t *counters = nullptr;
 };
 
-size_t workspace_partial_floats() { return (size_t)2 * target_workgroups() * QWG_MAX_BATCH * kTileRows; }
-size_t workspace_counters() { return (size_t)target_workgroups(); }
+size_t workspace_partial_floats() { return kWsPartialFloats; }
+size_t workspace_counters() { return kWsCounters; }
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
@@ -84,8 +133,8 @@ int get_workspace(hipStream_t stream, Workspace *out) {
     return QWG_OK;
 }
 
-int fill_gemv_args(GemvArgs &a, const void *w, const float *x, const float *grid, float *y,
-                   int64_t n_in, int64_t n_out, int block_bytes, int batch, hipStream_t stream) {
+void fill_shape(GemvArgs &a, const void *w, const float *x, const float *grid, float *y,
+                int64_t n_in, int64_t n_out, int block_bytes) {
     a.w = (const uint8_t *)w;
     a.x = x;
     a.grid = grid;
@@ -95,16 +144,23 @@ int fill_gemv_args(GemvArgs &a, const void *w, const float *x, const float *grid
     a.nb = (int)(n_in / kQK);
     a.row_bytes = (int64_t)a.nb * block_bytes;
     a.tiles = (int)((n_out + kTileRows - 1) / kTileRows);
-    a.splits = choose_splits(a.tiles, a.nb);
+    a.splits = 1;
+    a.wg_begin = 0;
     a.partial = nullptr;
     a.counters = nullptr;
+}
+
+int fill_gemv_args(GemvArgs &a, const void *w, const float *x, const float *grid, float *y,
+                   int64_t n_in, int64_t n_out, int block_bytes, int batch, hipStream_t stream,
+                   int *waves) {
+    fill_shape(a, w, x, grid, y, n_in, n_out, block_bytes);
+    const Plan plan = choose_plan(a.tiles, a.nb, batch);
+    a.splits = plan.splits;
+    if (waves) *waves = plan.waves;
     if (a.splits > 1) {
         Workspace ws;
         int rc = get_workspace(stream, &ws);
         if (rc != QWG_OK) return rc;
-        if ((size_t)a.splits * batch * a.tiles * kTileRows > workspace_partial_floats() ||
-            (size_t)a.tiles > workspace_counters())
-            return QWG_ERR_SHAPE;  // unreachable by construction of choose_splits
         a.partial = ws.partial;
         a.counters = ws.counters;
     }
@@ -168,9 +224,45 @@ int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
     if (batch < 1 || batch > QWG_MAX_BATCH) return QWG_ERR_BATCH;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
     GemvArgs a;
-    rc = fill_gemv_args(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes, batch, (hipStream_t)stream);
+    int waves = kQ4kWavesSmall;
+    rc = fill_gemv_args(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes, batch, (hipStream_t)stream,
+                        &waves);
     if (rc) return rc;
-    return hip_status(launch_q4k_gemv(a, batch, (hipStream_t)stream));
+    if (batch == 1 && a.splits == 1 && use_stream_engine()) {
+        const StreamShape sh = stream_shape(false);
+        const GroupArgs none = {nullptr, nullptr};
+        return hip_status(
+            launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, (hipStream_t)stream));
+    }
+    return hip_status(launch_q4k_gemv(a, batch, waves, (hipStream_t)stream));
+}
+
+int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                    int batch, int waves, int splits, void *stream) {
+    if (!y || !x || !w) return QWG_ERR_NULL;
+    int rc = check_gemv_shape(n_in, n_out);
+    if (rc) return rc;
+    if (batch < 1 || batch > QWG_MAX_BATCH) return QWG_ERR_BATCH;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
+    GemvArgs a;
+    fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
+    const Plan autoplan = choose_plan(a.tiles, a.nb, batch);
+    if (waves == 0) waves = autoplan.waves;
+    if (splits == 0) splits = autoplan.splits;
+    if (waves != 4 && waves != 8 && waves != 16) return QWG_ERR_SHAPE;
+    if (splits < 1 || splits > a.nb) return QWG_ERR_SHAPE;
+    if (splits > 1 && ((size_t)splits * batch * a.tiles * kTileRows > kWsPartialFloats ||
+                       (size_t)a.tiles > kWsCounters))
+        return QWG_ERR_SHAPE;
+    a.splits = splits;
+    if (splits > 1) {
+        Workspace ws;
+        rc = get_workspace((hipStream_t)stream, &ws);
+        if (rc) return rc;
+        a.partial = ws.partial;
+        a.counters = ws.counters;
+    }
+    return hip_status(launch_q4k_gemv(a, batch, waves, (hipStream_t)stream));
 }
 
 int qwg_gemv_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
@@ -186,9 +278,95 @@ int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int
     if (!aligned(w, 2) || !aligned(x, 16) || !aligned(grid, 16) || !aligned(y, 4))
         return QWG_ERR_ALIGN;
     GemvArgs a;
-    rc = fill_gemv_args(a, w, x, grid, y, n_in, n_out, kIq3Bytes, 1, (hipStream_t)stream);
+    rc = fill_gemv_args(a, w, x, grid, y, n_in, n_out, kIq3Bytes, 1, (hipStream_t)stream,
+                        nullptr);
     if (rc) return rc;
     return hip_status(launch_iq3_gemv(a, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------------ grouped GEMV
+
+struct qwg_group {
+    int device;
+    void *dev_mem;        // GemvArgs[count] followed by uint32_t map[workgroups]
+    GroupArgs args;
+    int count;
+    int workgroups;
+    int max_nb;
+};
+
+int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **out) {
+    if (!descs || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    std::vector<GemvArgs> probs((size_t)count);
+    int64_t total = 0;
+    int max_nb = 1;
+    for (int i = 0; i < count; ++i) {
+        const qwg_gemv_desc &d = descs[i];
+        if (!d.y || !d.x || !d.w) return QWG_ERR_NULL;
+        int rc = check_gemv_shape(d.n_in, d.n_out);
+        if (rc) return rc;
+        if (!aligned(d.w, 16) || !aligned(d.x, 16) || !aligned(d.y, 4)) return QWG_ERR_ALIGN;
+        fill_shape(probs[i], d.w, d.x, nullptr, d.y, d.n_in, d.n_out, kQ4kBytes);
+        total += probs[i].tiles;
+        if (probs[i].nb > max_nb) max_nb = probs[i].nb;
+    }
+    if (total > (int64_t)1 << 30) return QWG_ERR_SHAPE;
+    // Workgroups of the longest rows first, so that short ones fill the tail.
+    std::vector<int> order((size_t)count);
+    for (int i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return probs[a].nb > probs[b].nb; });
+    std::vector<uint32_t> map((size_t)total);
+    int64_t wg = 0;
+    for (int i : order) {
+        probs[i].wg_begin = (int)wg;
+        for (int t = 0; t < probs[i].tiles; ++t) map[wg++] = (uint32_t)i;
+    }
+    const size_t pbytes = sizeof(GemvArgs) * (size_t)count;
+    const size_t mbytes = sizeof(uint32_t) * (size_t)total;
+    qwg_group *g = new (std::nothrow) qwg_group();
+    if (!g) return QWG_ERR_HIP;
+    if (hipGetDevice(&g->device) != hipSuccess || hipMalloc(&g->dev_mem, pbytes + mbytes) != hipSuccess) {
+        delete g;
+        return QWG_ERR_HIP;
+    }
+    if (hipMemcpy(g->dev_mem, probs.data(), pbytes, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy((uint8_t *)g->dev_mem + pbytes, map.data(), mbytes, hipMemcpyHostToDevice) !=
+            hipSuccess) {
+        (void)hipFree(g->dev_mem);
+        delete g;
+        return QWG_ERR_HIP;
+    }
+    g->args.problems = (const GemvArgs *)g->dev_mem;
+    g->args.map = (const uint32_t *)((uint8_t *)g->dev_mem + pbytes);
+    g->count = count;
+    g->workgroups = (int)total;
+    g->max_nb = max_nb;
+    *out = g;
+    return QWG_OK;
+}
+
+int qwg_group_run(const qwg_group *g, void *stream) {
+    if (!g) return QWG_ERR_NULL;
+    if (use_stream_engine()) {
+        const StreamShape sh = stream_shape(true);
+        GemvArgs unused;
+        fill_shape(unused, nullptr, nullptr, nullptr, nullptr, kQK, 1, kQ4kBytes);
+        return hip_status(launch_q4k_stream(g->args, unused, g->workgroups, sh.waves, sh.ring,
+                                            (hipStream_t)stream));
+    }
+    return hip_status(launch_q4k_group(g->args, g->workgroups, g->max_nb, (hipStream_t)stream));
+}
+
+int qwg_group_workgroups(const qwg_group *g) { return g ? g->workgroups : -QWG_ERR_NULL; }
+
+int qwg_group_destroy(qwg_group *g) {
+    if (!g) return QWG_OK;
+    const hipError_t e = hipFree(g->dev_mem);
+    delete g;
+    return hip_status(e);
 }
 
 }  // extern "C"

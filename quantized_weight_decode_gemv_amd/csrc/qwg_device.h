@@ -24,6 +24,28 @@ __device__ __forceinline__ float h2f_hi(uint32_t v) {
 typedef const __attribute__((address_space(4))) float *cfloat_p;
 __device__ __forceinline__ cfloat_p as_scalar(const float *p) { return (cfloat_p)p; }
 
+// Asynchronous 16-byte global -> LDS copy (LDS DMA) of every active lane: lane
+// i's 16 bytes land at LDS byte address lds + 16*i. Issued from inline asm so
+// that the compiler does not guard later LDS reads with a wait for all
+// outstanding loads; the kernels count these copies themselves (wait_vmcnt).
+// The leading s_nop covers the M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"{m0}"(lds), "v"(g) : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier after this wavefront's LDS and scalar operations have
+// completed; outstanding vector-memory operations (LDS DMA) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Constants hidden from the optimizer so that mask-and-convert patterns are
 // kept as written (otherwise the compiler rewrites byte masks into per-field
 // bit extracts, one more op per weight).

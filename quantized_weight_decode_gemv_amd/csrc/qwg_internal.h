@@ -26,16 +26,34 @@ struct GemvArgs {
     int64_t row_bytes;
     int n_in;
     int n_out;
-    int nb;       // super-blocks per row
-    int tiles;    // ceil(n_out / 64)
-    int splits;   // 1..nb
+    int nb;        // super-blocks per row
+    int tiles;     // ceil(n_out / 64)
+    int splits;    // 1..nb
+    int wg_begin;  // first workgroup of this problem in a grouped launch
 };
+
+// A grouped launch: problems[map[blockIdx.x]] is the problem of each
+// workgroup (both arrays in device memory).
+struct GroupArgs {
+    const GemvArgs *problems;
+    const uint32_t *map;
+};
+
+// Wavefronts per workgroup of the Q4_K GEMV (4, 8 or 16: one, two or four
+// super-blocks of a 64-row tile per pipeline stage).
+constexpr int kQ4kWavesSmall = 4;
+constexpr int kQ4kWavesLarge = 16;
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_q4k_dequant(const uint8_t *src, float *dst, int64_t nblocks, hipStream_t s);
 hipError_t launch_iq3_dequant(const uint8_t *src, const float *grid, float *dst,
                               int64_t nblocks, hipStream_t s);
-hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, hipStream_t s);
+hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, int waves, hipStream_t s);
+hipError_t launch_q4k_group(const GroupArgs &g, int total_workgroups, int max_nb, hipStream_t s);
+// Persistent stream engine (batch 1): `nitems` tiles of the group (g.problems
+// != nullptr) or of `single`; waves in {4, 8, 16}, ring stages in {2, 3, 4}.
+hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nitems, int waves,
+                             int ring, hipStream_t s);
 hipError_t launch_iq3_gemv(const GemvArgs &a, hipStream_t s);
 
 }  // namespace qwg

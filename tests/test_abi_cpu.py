@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     names = declared_symbols()
     for want in ("qwg_dequant_q4k", "qwg_dequant_iq3", "qwg_gemv_q4k", "qwg_gemv_iq3",
                  "qwg_gemm_q4k", "qwg_strerror", "qwg_row_bytes", "qwg_version",
-                 "qwg_plan_splits"):
+                 "qwg_plan_splits", "qwg_gemm_q4k_ex", "qwg_group_create_q4k", "qwg_group_run",
+                 "qwg_group_workgroups", "qwg_group_destroy"):
         assert want in names
 
 
@@ -92,6 +93,10 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_gemv_iq3(FAKE, FAKE, FAKE, FAKE, 128, 4, None), 2),
     (lambda L: L.qwg_dequant_q4k(FAKE, FAKE, 255, None), 2),
     (lambda L: L.qwg_dequant_iq3(FAKE, FAKE, FAKE, -256, None), 2),
+    (lambda L: L.qwg_gemm_q4k_ex(None, FAKE, FAKE, 256, 1, 1, 4, 1, None), 1),
+    (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 200, 1, 1, 4, 1, None), 2),
+    (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 256, 1, 9, 4, 1, None), 4),
+    (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE + 4, FAKE, 256, 1, 1, 4, 1, None), 3),
     # batch -> 4
     (lambda L: L.qwg_gemm_q4k(FAKE, FAKE, FAKE, 256, 1, 0, None), 4),
     (lambda L: L.qwg_gemm_q4k(FAKE, FAKE, FAKE, 256, 1, 9, None), 4),
@@ -107,6 +112,38 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
 ])
 def test_validation_errors(L, call, status):
     assert call(L) == status
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("y", ctypes.c_void_p), ("x", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("n_in", ctypes.c_int64), ("n_out", ctypes.c_int64)]
+
+
+@pytest.mark.parametrize("desc,status", [
+    ((0, FAKE, FAKE, 256, 1), 1),
+    ((FAKE, FAKE, FAKE, 300, 1), 2),
+    ((FAKE, FAKE, FAKE, 256, 0), 2),
+    ((FAKE, FAKE + 4, FAKE, 256, 1), 3),
+    ((FAKE, FAKE, FAKE + 8, 256, 1), 3),
+    ((FAKE + 2, FAKE, FAKE, 256, 1), 3),
+])
+def test_group_validation_errors(L, desc, status):
+    arr = (_Desc * 2)(_Desc(FAKE, FAKE, FAKE, 256, 64), _Desc(*desc))
+    out = ctypes.c_void_p(123)
+    assert L.qwg_group_create_q4k(arr, 2, ctypes.byref(out)) == status
+    assert out.value is None  # nothing allocated, handle cleared
+
+
+def test_group_null_and_count_errors(L):
+    out = ctypes.c_void_p()
+    arr = (_Desc * 1)(_Desc(FAKE, FAKE, FAKE, 256, 64))
+    assert L.qwg_group_create_q4k(None, 1, ctypes.byref(out)) == 1
+    assert L.qwg_group_create_q4k(arr, 1, None) == 1
+    assert L.qwg_group_create_q4k(arr, 0, ctypes.byref(out)) == 2
+    assert L.qwg_group_create_q4k(arr, 65537, ctypes.byref(out)) == 2
+    assert L.qwg_group_run(None, None) == 1
+    assert L.qwg_group_workgroups(None) == -1
+    assert L.qwg_group_destroy(None) == 0
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -144,6 +144,30 @@ def test_gemv_q4k_ragged(n_out, n_in):
     assert_bound(y, yr, sr, f"{n_out}x{n_in} splits={qwg.plan_splits(0, n_in, n_out)}")
 
 
+@pytest.mark.parametrize("waves", [4, 8, 16])
+@pytest.mark.parametrize("n_out,n_in,splits", [(70, 256, 1), (70, 2048, 1), (70, 2048, 3),
+                                               (130, 5632, 1), (130, 5632, 5), (130, 5632, 22),
+                                               (1, 1024, 4), (300, 1280, 2)])
+def test_gemv_q4k_every_plan(waves, n_out, n_in, splits):
+    w, x = _gemv_q4k_case(n_out, n_in, 107, n_out + splits)
+    wd, xd = dev(w), dev(x)
+    yr, sr = oracle.gemv_q4k(w, x, n_in, n_out)
+    y = host(qwg.gemm_q4k(wd, xd.reshape(1, -1), waves=waves, splits=splits))
+    assert_bound(y[0], yr, sr, f"waves={waves} splits={splits}")
+    X = synth.activations(n_in, 107, 500 + n_out, batch=3)
+    Yr, Sr = oracle.gemm_q4k(w, X, n_in, n_out)
+    Y = host(qwg.gemm_q4k(wd, dev(X), waves=waves, splits=splits))
+    assert_bound(Y, Yr, Sr, f"batch 3 waves={waves} splits={splits}")
+
+
+def test_gemm_q4k_ex_rejects_bad_plans():
+    w, x = _gemv_q4k_case(64, 512, 108, 0)
+    for waves, splits in [(2, 1), (32, 1), (4, 3), (16, -1)]:
+        with pytest.raises(qwg.QwgError) as e:
+            qwg.gemm_q4k(dev(w), dev(x).reshape(1, -1), waves=waves, splits=splits)
+        assert e.value.status == 2
+
+
 def test_gemv_q4k_covers_split_and_unsplit_plans():
     assert qwg.plan_splits(0, 256, 131072 + 5) == 1
     assert qwg.plan_splits(0, 2048, 2048) > 1
@@ -217,6 +241,78 @@ def test_gemv_q4k_misaligned_input_is_an_error():
     with pytest.raises(qwg.QwgError) as e:
         qwg.gemv_q4k(dev(w), xd)
     assert e.value.status == 3
+
+
+def test_group_c2_layer_and_repeat_runs():
+    # One TinyLlama layer's seven projections as one grouped launch, run twice
+    # (the plan is reusable; the second run sees a changed x in place).
+    probs = synth.config(2)
+    ws = [synth.weights(p) for p in probs]
+    xs = [synth.inputs(p) for p in probs]
+    W = [dev(w) for w in ws]
+    X = [dev(x) for x in xs]
+    Y = [torch.full((p.n_out,), float("nan"), device=DEV) for p in probs]
+    g = qwg.Q4kGroup(zip(W, X, Y))
+    assert g.workgroups == sum((p.n_out + 63) // 64 for p in probs)
+    g.run()
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        yr, sr = oracle.gemv_q4k(w, x, p.n_in, p.n_out)
+        assert_bound(host(y), yr, sr, "group " + p.name)
+    X[0].mul_(-0.5)
+    g.run()
+    yr, sr = oracle.gemv_q4k(ws[0], -0.5 * xs[0], probs[0].n_in, probs[0].n_out)
+    assert_bound(host(Y[0]), yr, sr, "group rerun")
+    g.close()
+
+
+def test_group_and_single_calls_are_within_bound_and_deterministic():
+    # Large members run through the persistent stream engine in both entry
+    # points (different workgroup shapes, so different summation orders): both
+    # must meet the bound, and each must be bitwise reproducible.
+    shapes = [(16384 + 7, 256), (32000, 2048)]
+    ws = [synth.q4k_weights(o, i, 105, k) for k, (o, i) in enumerate(shapes)]
+    xs = [synth.activations(i, 105, k) for k, (o, i) in enumerate(shapes)]
+    W, X = [dev(w) for w in ws], [dev(x) for x in xs]
+    Y = [torch.empty(o, device=DEV) for o, _ in shapes]
+    g = qwg.Q4kGroup(zip(W, X, Y))
+    g.run()
+    first = [host(y).copy() for y in Y]
+    g.run()
+    for (o, i), w, x, wd, xd, y, y0 in zip(shapes, ws, xs, W, X, Y, first):
+        assert qwg.plan_splits(0, i, o) == 1
+        yr, sr = oracle.gemv_q4k(w, x, i, o)
+        assert_bound(y0, yr, sr, f"group {o}x{i}")
+        assert_bits(host(y), y0, f"group rerun {o}x{i}")
+        ys = host(qwg.gemv_q4k(wd, xd))
+        assert_bound(ys, yr, sr, f"single {o}x{i}")
+        assert_bits(host(qwg.gemv_q4k(wd, xd)), ys, f"single rerun {o}x{i}")
+
+
+def test_group_ragged_members():
+    shapes = [(1, 256), (65, 512), (200, 5632), (3, 65536), (4097, 768), (64, 2048)]
+    ws = [synth.q4k_weights(o, i, 106, k) for k, (o, i) in enumerate(shapes)]
+    xs = [synth.activations(i, 106, k) for k, (o, i) in enumerate(shapes)]
+    Y = [torch.empty(o, device=DEV) for o, _ in shapes]
+    g = qwg.Q4kGroup(zip([dev(w) for w in ws], [dev(x) for x in xs], Y))
+    g.run()
+    for (o, i), w, x, y in zip(shapes, ws, xs, Y):
+        yr, sr = oracle.gemv_q4k(w, x, i, o)
+        assert_bound(host(y), yr, sr, f"group member {o}x{i}")
+
+
+def test_group_c5_stream_sampled_rows():
+    probs = synth.config(5)
+    rng = np.random.default_rng(6)
+    ws = [synth.weights(p) for p in probs]
+    xs = [synth.inputs(p) for p in probs]
+    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    g = qwg.Q4kGroup(zip([dev(w) for w in ws], [dev(x) for x in xs], Y))
+    for _ in range(3):
+        g.run()
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 24)]))
+        yr, sr = oracle.gemv_q4k_rows(w, x, p.n_in, rows)
+        assert_bound(host(y)[rows], yr, sr, "group " + p.name)
 
 
 # ---------------------------------------------------------------- GEMM
