@@ -32,6 +32,31 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
+                  "quantized_weight_decode_gemv_amd/csrc/qwg_device.h",
+                  "quantized_weight_decode_gemv_amd/csrc/qwg_internal.h"]
+# HBM bytes per grouped launch of the stream, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# runs of this script, each scaled by the same counter on a plain device copy of known size
+# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
+# the kernel sources with this hash; otherwise traffic is reported as null.
+TRAFFIC = {"sources_sha256": "cf33c3aa40187151480f7bc7a24eaf74fa55739ec122de85ec23c64369cbc809",
+           "fetch_bytes": 686743121, "write_bytes": 1704960}
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_bytes():
+    if TRAFFIC["sources_sha256"] and TRAFFIC["sources_sha256"] == kernel_sources_sha256():
+        return TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+    return None
 
 
 def parse():
@@ -42,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time budget for the oracle baseline")
+    ap.add_argument("--print-kernel-hash", action="store_true",
+                    help="print the hash of the kernel sources the traffic figure is tied to")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 10 plain device-to-device copies of MIB "
                          "MiB (reference for scaling hardware traffic counters) and exit")
@@ -63,6 +90,9 @@ def copy_calibration(mib: int) -> None:
 
 def main():
     args = parse()
+    if args.print_kernel_hash:
+        print(kernel_sources_sha256())
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -194,7 +224,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic_bytes(),
             "kernel": "q4k_stream_kernel<4,2> (grouped, 155 GEMVs per launch)",
             "bytes_per_launch": step_bytes,
             "kernel_us": round(1e3 * kernel_ms, 2),
