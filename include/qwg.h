@@ -114,16 +114,30 @@ int qwg_gemv_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
                  void *stream);
 
 /*
- * y = W x for IQ3 weights.
+ * y = W x for IQ3 weights (the fused decode-and-dot of the iq3_pack.py page's
+ * decode() followed by the product).
  * w: n_out rows of n_in/256 IQ3 blocks, 2-byte aligned (98-byte blocks put odd
- * blocks at 2 mod 4). grid: [256][4] fp32 magnitudes, 16-byte aligned; every
- * magnitude must be exactly representable in fp16 (true for the integer
- * magnitudes IQ3 grids use), otherwise the result is the product with the
- * fp16-rounded grid. x: n_in fp32, 16-byte aligned. y: n_out fp32, 4-byte aligned.
- * Shape limits as qwg_gemv_q4k.
+ * blocks at 2 mod 4). The kernel reads whole 16-byte-aligned granules of w but
+ * never one that reaches outside [w, w + n_out*row_bytes).
+ * grid: [256][4] fp32 magnitudes, 16-byte aligned; every magnitude must be
+ * exactly representable in fp16 (true for the integer magnitudes IQ3 grids
+ * use), otherwise the result is the product with the fp16-rounded grid.
+ * x: n_in fp32, 16-byte aligned. y: n_out fp32, 4-byte aligned.
+ * Shape limits and accuracy as qwg_gemv_q4k.
  */
 int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                  int64_t n_out, void *stream);
+
+/*
+ * qwg_gemv_iq3 with an explicit work decomposition (tuning and testing):
+ * `waves` wavefronts per workgroup (4, 8 or 16; 0 = automatic) and `splits`
+ * workgroups sharing each 64-row tile's n_in sum (1..n_in/256; 0 = automatic).
+ * Same bound for every choice. QWG_ERR_SHAPE for an unsupported choice (also
+ * when splits*ceil(n_out/64)*64 partial sums exceed the split workspace, or
+ * ceil(n_out/64) > 4096 with splits > 1).
+ */
+int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                    int64_t n_out, int waves, int splits, void *stream);
 
 /*
  * Y[b, r] = sum_k W[r,k] X[b,k] for 1 <= batch <= QWG_MAX_BATCH, Q4_K weights:
@@ -147,22 +161,26 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
                     int batch, int waves, int splits, void *stream);
 
 /*
- * Grouped GEMV: many independent Q4_K GEMVs in one launch (one grid whose
- * workgroups belong to different matrices), for streams of independent
+ * Grouped GEMV: many independent GEMVs of one format in one launch (one grid
+ * whose workgroups belong to different matrices), for streams of independent
  * weight-bound products such as the q/k/v or gate/up projections that share an
  * activation vector, or a whole decode step's weight stream when its inputs are
- * independent. Same math and accuracy as qwg_gemv_q4k for every member.
+ * independent. Same math and accuracy as qwg_gemv_q4k / qwg_gemv_iq3 for every
+ * member.
  *
- * qwg_gemv_desc: one member, fields as the qwg_gemv_q4k arguments (device
- * pointers, same alignment and shape rules).
- * qwg_group_create_q4k: validates every member (the first failing member's
- * status is returned, nothing is allocated), then copies the launch plan to a
- * device buffer owned by the group (hipMalloc + hipMemcpy: synchronous).
- * `descs` is a host array of `count` members (1..QWG_MAX_GROUP) and is not
- * kept. The member pointers are baked into the plan: reuse the same buffers
- * (e.g. fixed activation/output buffers of a decode loop) on every run.
+ * qwg_gemv_desc: one member, fields as the qwg_gemv_q4k / qwg_gemv_iq3
+ * arguments (device pointers, same alignment and shape rules).
+ * qwg_group_create_q4k / qwg_group_create_iq3: validate every member (the
+ * first failing member's status is returned, nothing is allocated), then copy
+ * the launch plan to a device buffer owned by the group (hipMalloc +
+ * hipMemcpy: synchronous). `descs` is a host array of `count` members
+ * (1..QWG_MAX_GROUP) and is not kept. The member pointers (and the IQ3 grid,
+ * shared by all members, rules as for qwg_gemv_iq3) are baked into the plan:
+ * reuse the same buffers (e.g. fixed activation/output buffers of a decode
+ * loop) on every run.
  * qwg_group_run: enqueues the whole group on `stream` (asynchronous).
- * qwg_group_workgroups: number of workgroups of one run, or a negative status.
+ * qwg_group_workgroups: number of work items (64-row tiles) of one run, or a
+ * negative status.
  * qwg_group_destroy: frees the plan (hipFree: synchronous; no run of the group
  * may be pending). NULL is accepted.
  */
@@ -177,6 +195,8 @@ typedef struct qwg_gemv_desc {
 typedef struct qwg_group qwg_group;
 
 int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **group);
+int qwg_group_create_iq3(const qwg_gemv_desc *descs, int count, const float *grid,
+                         qwg_group **group);
 int qwg_group_run(const qwg_group *group, void *stream);
 int qwg_group_workgroups(const qwg_group *group);
 int qwg_group_destroy(qwg_group *group);

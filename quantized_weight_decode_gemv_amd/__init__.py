@@ -4,8 +4,10 @@ The compute path is the HIP library ``libqwg.so`` (C ABI in ``include/qwg.h``);
 this package only marshals torch tensors into its calls. Importing the package
 does not load the library; the first call does, and raises if it is missing.
 """
-from ._binding import (MAX_BATCH, QWG_FMT_IQ3, QWG_FMT_Q4K, Q4kGroup, QwgError, dequant_iq3, dequant_q4k,
-                       gemm_q4k, gemv_iq3, gemv_q4k, lib, plan_splits, row_bytes)
+from ._binding import (MAX_BATCH, QWG_FMT_IQ3, QWG_FMT_Q4K, Group, Iq3Group, Q4kGroup, QwgError,
+                       dequant_iq3, dequant_q4k, gemm_q4k, gemv_iq3, gemv_q4k, lib, plan_splits,
+                       row_bytes)
 
-__all__ = ["MAX_BATCH", "QWG_FMT_IQ3", "QWG_FMT_Q4K", "Q4kGroup", "QwgError", "dequant_iq3", "dequant_q4k",
-           "gemm_q4k", "gemv_iq3", "gemv_q4k", "lib", "plan_splits", "row_bytes"]
+__all__ = ["MAX_BATCH", "QWG_FMT_IQ3", "QWG_FMT_Q4K", "Group", "Iq3Group", "Q4kGroup", "QwgError",
+           "dequant_iq3", "dequant_q4k", "gemm_q4k", "gemv_iq3", "gemv_q4k", "lib", "plan_splits",
+           "row_bytes"]

@@ -49,12 +49,15 @@ def lib() -> ctypes.CDLL:
         L.qwg_gemv_iq3.argtypes = [P, P, P, P, I64, I64, P]
         L.qwg_gemm_q4k.argtypes = [P, P, P, I64, I64, I, P]
         L.qwg_gemm_q4k_ex.argtypes = [P, P, P, I64, I64, I, I, I, P]
+        L.qwg_gemv_iq3_ex.argtypes = [P, P, P, P, I64, I64, I, I, P]
         L.qwg_group_create_q4k.argtypes = [P, I, ctypes.POINTER(P)]
+        L.qwg_group_create_iq3.argtypes = [P, I, P, ctypes.POINTER(P)]
         L.qwg_group_run.argtypes = [P, P]
         L.qwg_group_workgroups.argtypes = [P]
         L.qwg_group_destroy.argtypes = [P]
         for f in ("qwg_dequant_q4k", "qwg_dequant_iq3", "qwg_gemv_q4k", "qwg_gemv_iq3",
-                  "qwg_gemm_q4k", "qwg_gemm_q4k_ex", "qwg_group_create_q4k", "qwg_group_run", "qwg_group_workgroups",
+                  "qwg_gemv_iq3_ex", "qwg_gemm_q4k", "qwg_gemm_q4k_ex", "qwg_group_create_q4k",
+                  "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
                   "qwg_group_destroy"):
             getattr(L, f).restype = I
         _lib = L
@@ -153,12 +156,18 @@ def gemv_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) 
     return out
 
 
-def gemv_iq3(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
-             out: torch.Tensor | None = None) -> torch.Tensor:
-    _dev(x, "x", torch.float32)
+def _grid(grid: torch.Tensor) -> None:
     _dev(grid, "grid", torch.float32)
     if grid.shape != (256, 4):
         raise ValueError("grid must be [256, 4]")
+
+
+def gemv_iq3(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
+             out: torch.Tensor | None = None, waves: int = 0, splits: int = 0) -> torch.Tensor:
+    """y = W x for IQ3 weights; w uint8 [n_out, row_bytes] (or flat), x fp32 [n_in],
+    grid fp32 [256, 4]. waves/splits force the work decomposition (0 = automatic)."""
+    _dev(x, "x", torch.float32)
+    _grid(grid)
     n_in = x.numel()
     n_out = _weights(w, n_in, IQ3_BYTES)
     if out is None:
@@ -166,8 +175,12 @@ def gemv_iq3(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
     _dev(out, "out", torch.float32)
     if out.numel() != n_out:
         raise ValueError("out has the wrong size")
-    _check(lib().qwg_gemv_iq3(out.data_ptr(), x.data_ptr(), w.data_ptr(), grid.data_ptr(), n_in,
-                              n_out, _stream(x)), "qwg_gemv_iq3")
+    if waves or splits:
+        _check(lib().qwg_gemv_iq3_ex(out.data_ptr(), x.data_ptr(), w.data_ptr(), grid.data_ptr(),
+                                     n_in, n_out, waves, splits, _stream(x)), "qwg_gemv_iq3_ex")
+    else:
+        _check(lib().qwg_gemv_iq3(out.data_ptr(), x.data_ptr(), w.data_ptr(), grid.data_ptr(), n_in,
+                                  n_out, _stream(x)), "qwg_gemv_iq3")
     return out
 
 
@@ -200,32 +213,46 @@ class GemvDesc(ctypes.Structure):
                 ("n_in", ctypes.c_int64), ("n_out", ctypes.c_int64)]
 
 
-class Q4kGroup:
-    """Many independent Q4_K GEMVs y_i = W_i x_i run by one launch.
+class Group:
+    """Many independent GEMVs y_i = W_i x_i of one format run by one launch.
 
     members: sequence of (w, x, y) device tensors (uint8 weights, fp32 x [n_in],
-    fp32 y [n_out]). The tensors are referenced by the plan (kept alive here) and
-    must stay in place; run() recomputes every y_i from the current x_i.
+    fp32 y [n_out]); fmt QWG_FMT_Q4K or QWG_FMT_IQ3 (then `grid`, fp32 [256, 4],
+    is shared by every member). The tensors are referenced by the plan (kept
+    alive here) and must stay in place; run() recomputes every y_i from the
+    current x_i.
     """
 
-    def __init__(self, members):
+    def __init__(self, members, fmt: int = QWG_FMT_Q4K, grid: torch.Tensor | None = None):
         members = list(members)
         if not members:
             raise ValueError("a group needs at least one member")
+        if fmt not in (QWG_FMT_Q4K, QWG_FMT_IQ3):
+            raise ValueError(f"unknown format {fmt}")
+        if fmt == QWG_FMT_IQ3:
+            if grid is None:
+                raise ValueError("an IQ3 group needs the grid")
+            _grid(grid)
+        block_bytes = Q4K_BYTES if fmt == QWG_FMT_Q4K else IQ3_BYTES
         descs = (GemvDesc * len(members))()
         for i, (w, x, y) in enumerate(members):
             _dev(x, "x", torch.float32)
             _dev(y, "y", torch.float32)
             n_in = x.numel()
-            n_out = _weights(w, n_in, Q4K_BYTES)
+            n_out = _weights(w, n_in, block_bytes)
             if y.numel() != n_out:
                 raise ValueError(f"member {i}: y has {y.numel()} elements, expected {n_out}")
             descs[i] = GemvDesc(y.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out)
         self._members = members
+        self._grid = grid
         self._device = members[0][1].device
         handle = ctypes.c_void_p()
-        _check(lib().qwg_group_create_q4k(descs, len(members), ctypes.byref(handle)),
-               "qwg_group_create_q4k")
+        if fmt == QWG_FMT_Q4K:
+            _check(lib().qwg_group_create_q4k(descs, len(members), ctypes.byref(handle)),
+                   "qwg_group_create_q4k")
+        else:
+            _check(lib().qwg_group_create_iq3(descs, len(members), grid.data_ptr(),
+                                              ctypes.byref(handle)), "qwg_group_create_iq3")
         self._handle = handle
 
     @property
@@ -249,3 +276,17 @@ class Q4kGroup:
             self.close()
         except Exception:
             pass
+
+
+class Q4kGroup(Group):
+    """Group of Q4_K GEMVs (members as for Group)."""
+
+    def __init__(self, members):
+        super().__init__(members, QWG_FMT_Q4K)
+
+
+class Iq3Group(Group):
+    """Group of IQ3 GEMVs sharing one grid (members as for Group)."""
+
+    def __init__(self, members, grid: torch.Tensor):
+        super().__init__(members, QWG_FMT_IQ3, grid)

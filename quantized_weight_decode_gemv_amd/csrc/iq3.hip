@@ -8,31 +8,16 @@
 // Weight = grid[idx][t%4] * sign * db, db = d*(0.5+code)*0.5; every factor has
 // few enough significant bits that the fp32 product is exact.
 //
-// GEMV design (one 64-row tile per workgroup, 4 wavefronts):
-//   * lane r owns row tile*64 + r; wavefront g owns sub-blocks 2g and 2g+1 of
-//     every block, so activations are wave-uniform and come through scalar loads;
-//   * the tile's 64 blocks of one column are staged through LDS as 25-dword
-//     windows starting at the dword below each block (blocks are only 2-byte
-//     aligned); lanes re-align their words with v_alignbyte;
-//   * the grid is expanded once per workgroup into a sign-folded fp16 table
-//     T[s][idx] = (+-g0, +-g1, +-g2, +-g3) for the 16 sign patterns s of a group
-//     of four weights, so four weights cost one v_perm (table index from the
-//     index byte and the sign nibble), one shift, one 8-byte LDS read and four
-//     v_fma_mix_f32;
-//   * the eighth sign of each 8-weight group is rebuilt for all four groups of a
-//     word at once with byte-parallel XOR folding.
+// GEMV: a persistent stream engine (described above iq3_stream below) with the
+// grid expanded once per workgroup into a sign-folded table in LDS, so that four
+// weights cost one v_perm, one LDS read and four FMAs; the eighth sign of each
+// 8-weight group is rebuilt for all four groups of a word at once with
+// byte-parallel XOR folding.
 #include "qwg_device.h"
 
 namespace qwg {
 
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kWinDwords = 25;                              // 100-byte window per block
-constexpr int kStageDwords = kTileRows * kWinDwords;        // 1600
-constexpr int kStageBytes = kStageDwords * 4;               // 6400
-constexpr int kTableBytes = 16 * 256 * 8;                   // 32 KB sign-folded grid
-constexpr int kLoadsPerThread = (kStageDwords + kThreads - 1) / kThreads;  // 7
 
 __device__ __forceinline__ uint32_t load_u16(const uint8_t *p) {
     return *(const uint16_t *)p;
@@ -85,152 +70,377 @@ __global__ __launch_bounds__(256) void iq3_dequant_kernel(const uint8_t *__restr
 }
 
 // ------------------------------------------------------------------ GEMV
+//
+// Persistent stream engine: a grid of about one workgroup per resident slot of
+// the chip walks work items k, k + grid, ...; an item is one 64-row tile of one
+// matrix over a contiguous range of super-blocks (the whole row, or one of
+// `splits` ranges whose partial sums meet in tile_epilogue). Wavefront 4j + G
+// computes sub-blocks 2G and 2G+1 of the j-th super-block of every pipeline
+// stage for all 64 rows (lane r = row r of the tile), so its 64 activations
+// are wave-uniform and come through scalar loads. An R-slot LDS ring, filled by
+// LDS-DMA, runs ahead across item boundaries.
+//
+// Staging: a 98-byte block starts at any even address, so each row's block is
+// copied as the seven naturally aligned 16-byte granules that cover it (a
+// 112-byte window: 14 + 98 <= 7*16) and lanes re-align with v_alignbyte. Every
+// granule address is clamped into the granules lying wholly inside the weight
+// buffer, so nothing outside it is read. Only two granules can be affected:
+// the first one of a buffer that starts off a 16-byte boundary (row 0's first
+// block) and the last one of a buffer that ends off one (the last row's last
+// block); the lane of that row takes that block's bytes from direct 2-byte
+// loads instead.
+//
+// Grid: the workgroup stages the [256][4] fp32 grid in LDS once and expands it
+// into a sign-folded fp16 table T[s][i] = (+-g_i0, +-g_i1, +-g_i2, +-g_i3) for
+// the 16 sign patterns s of a group of four weights (bit c of s negates
+// component c), entry (s, i) at LDS byte s*2048 + i*8 (32 KB), so four weights
+// cost one v_perm (s*256 + i from the sign nibble and the index byte), one
+// shift, one 8-byte LDS read and four FMAs. fp16 holds the magnitudes exactly
+// when they are fp16 values (the small integers IQ3 grids use). A 64 KB layout
+// with the address straight out of the v_perm (entry at i*256 + s*16) measured
+// slower: its bank depends on s alone, so lanes collide far more often.
+template <int W, int R>
+struct Iq3Cfg {
+    static constexpr int kBps = W / 4;                   // super-blocks per stage
+    static constexpr int kWin = 112;                     // bytes per row window
+    static constexpr int kCol = kTileRows * kWin;        // 7168: one super-block of a tile
+    static constexpr int kSlot = kBps * kCol;
+    static constexpr int kTable = 32768;                 // at LDS address 0
+    static constexpr int kGrid = kTable;                 // staged fp32 grid, 4 KB
+    static constexpr int kRing = kGrid + 256 * 16;
+    static constexpr int kRed = kRing + R * kSlot;       // [W][64] fp32 row sums
+    static constexpr int kLds = kRed + W * 64 * 4;
+};
 
-// Wavefront G's two sub-blocks (2G, 2G+1) of one block for this lane's row.
-// win: this row's 25-dword window (LDS), sh: byte offset of the block in it
-// (0 or 2). xg: x[256*b + 64*G] (wave-uniform). table: sign-folded fp16 grid.
+// One work item as a cursor sees it.
+struct Iq3Item {
+    GemvArgs a;
+    const uint8_t *sb;  // the tile's first row, rounded down to 16 bytes
+    uint32_t sb_off;    // that row's offset from sb (0..15)
+    uint32_t lo;        // first 16-byte granule wholly inside the weights, relative to sb (>= 0)
+    uint32_t hi;        // last one (capped; the tile's granules lie far below the cap)
+    int tile, split, kb0, kb1, nst, row0;
+    bool head;        // holds row 0's block 0 and the buffer starts off a granule
+    bool tail;        // holds the last row's last block and the buffer ends off a granule
+};
+
+template <int BPS>
+__device__ __forceinline__ void iq3_load_item(Iq3Item &it, int k, const GroupArgs &g,
+                                              const GemvArgs &single) {
+    int local;
+    if (g.problems == nullptr) {
+        it.a = single;
+        local = k;
+    } else {
+        load_args(it.a, (cargs_p)g.problems + ((cu32_p)g.map)[k]);
+        local = k - it.a.wg_begin;
+    }
+    const int splits = it.a.splits;
+    if (splits == 1) {
+        it.tile = local;
+        it.split = 0;
+        it.kb0 = 0;
+        it.kb1 = it.a.nb;
+    } else {
+        it.tile = local / splits;
+        it.split = local - it.tile * splits;
+        it.kb0 = it.split * it.a.nb / splits;
+        it.kb1 = (it.split + 1) * it.a.nb / splits;
+    }
+    it.nst = (it.kb1 - it.kb0 + BPS - 1) / BPS;
+    it.row0 = it.tile * kTileRows;
+    const uintptr_t wb = (uintptr_t)it.a.w;
+    const uintptr_t we = wb + (uintptr_t)it.a.n_out * (uintptr_t)it.a.row_bytes;
+    const uintptr_t base0 = wb + (uintptr_t)it.row0 * (uintptr_t)it.a.row_bytes;
+    const uintptr_t sb = base0 & ~(uintptr_t)15;
+    it.sb = (const uint8_t *)sb;
+    it.sb_off = (uint32_t)(base0 & 15);
+    // The buffer holds >= 98 bytes, so wb <= lo16 < hi16 and hi16 + 16 <= we; the
+    // tile's granules start at sb (>= lo16 - 16) and end below hi16 + 98 + 16.
+    const uintptr_t lo16 = (wb + 15) & ~(uintptr_t)15;
+    const uintptr_t hi16 = (we & ~(uintptr_t)15) - 16;
+    it.lo = lo16 > sb ? (uint32_t)(lo16 - sb) : 0u;
+    it.hi = hi16 - sb < 0x40000000u ? (uint32_t)(hi16 - sb) : 0x40000000u;
+    it.head = (wb & 15) != 0 && it.row0 == 0 && it.kb0 == 0;
+    it.tail = (we & 15) != 0 && it.row0 + kTileRows >= it.a.n_out && it.kb1 == it.a.nb;
+}
+
+// The bytes of one block that wavefront G uses, 32-bit aligned to the block:
+// index bytes 16G..16G+15, sign/scale words 2G and 2G+1, and d (low 16 bits).
+struct Iq3Raw {
+    uint32_t idx[4];
+    uint32_t words[2];
+    uint32_t d16;
+};
+
+// From a row window in LDS: `win` = window + (sh & 12), sh = block offset in it.
 template <int G>
-__device__ __forceinline__ float iq3_chunk(const uint32_t *win, uint32_t sh,
-                                           cfloat_p xg, const uint8_t *table,
-                                           float acc) {
-    // Block dwords 4G..4G+3 (indices) and 16+2G, 17+2G (words), re-aligned.
-    uint32_t w[8];
+__device__ __forceinline__ void iq3_fetch(const uint8_t *win, uint32_t sh, Iq3Raw &r) {
+    const uint32_t *p = (const uint32_t *)win;
+    uint32_t a[5], v[3];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) w[i] = win[4 * G + i];
-    uint32_t v[3];
+    for (int i = 0; i < 5; ++i) a[i] = p[4 * G + i];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) v[i] = win[16 + 2 * G + i];
-    const uint32_t dwin = win[24];
-    uint32_t idx[4], words[2];
+    for (int i = 0; i < 3; ++i) v[i] = p[16 + 2 * G + i];
+    const uint32_t dw = p[24];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) idx[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
+    for (int i = 0; i < 4; ++i) r.idx[i] = __builtin_amdgcn_alignbyte(a[i + 1], a[i], sh);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) words[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], sh);
-    const float d = h2f_lo(dwin >> (8 * sh));
-    const float dq = d * 0.25f;   // d*(0.5+code)*0.5 == (d/4)*(2*code+1), exact
+    for (int i = 0; i < 2; ++i) r.words[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], sh);
+    r.d16 = dw >> ((sh & 2u) << 3);
+}
+
+// From global memory, 2 bytes at a time (the block is 2-byte aligned).
+template <int G>
+__device__ __forceinline__ void iq3_fetch_direct(const uint8_t *blk, Iq3Raw &r) {
+    const uint16_t *h = (const uint16_t *)blk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r.idx[i] = (uint32_t)h[8 * G + 2 * i] | ((uint32_t)h[8 * G + 2 * i + 1] << 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        r.words[i] = (uint32_t)h[32 + 4 * G + 2 * i] | ((uint32_t)h[32 + 4 * G + 2 * i + 1] << 16);
+    r.d16 = h[48];
+}
+
+// acc + sum over wavefront G's 64 weights of this lane's row of w*x.
+// xg: x[256*b + 64*G] (wave-uniform). The sign-folded grid table sits at LDS
+// address 0. Two interleaved partial sums per sub-block keep consecutive FMAs
+// independent.
+template <int G>
+__device__ __forceinline__ float iq3_dot(const Iq3Raw &r, cfloat_p xg, float acc) {
+    const float dq = h2f_lo(r.d16) * 0.25f;   // d*(0.5+code)*0.5 == (d/4)*(2*code+1), exact
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        const uint32_t word = words[half];
+        const uint32_t word = r.words[half];
         const uint32_t s8 = iq3_signs(word);
-        const uint32_t ne = s8 & 0x0F0F0F0Fu;          // sign nibbles of groups 0,2,4,6
-        const uint32_t no = (s8 >> 4) & 0x0F0F0F0Fu;   // groups 1,3,5,7
+        // sign nibble of 4-weight group k: low nibble of byte k/2 of ne (k even) or no (k odd)
+        const uint32_t ne = s8 & 0x0F0F0F0Fu;
+        const uint32_t no = (s8 >> 4) & 0x0F0F0F0Fu;
         const float db = dq * (float)(2u * (word >> 28) + 1u);
-        cfloat_p xs = xg + 32 * half;
-        float s = 0.0f;
+        const cfloat_p xs = xg + 32 * half;
+        float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            // table index = nibble*256 + idx: byte 0 = index byte k, byte 1 = nibble k
+            // byte 0 = index byte, byte 1 = nibble: entry (s*256 + i) * 8
             const uint32_t sel = (uint32_t)(k & 3) | ((uint32_t)(4 + (k >> 1)) << 8) | 0x0C0C0000u;
-            const uint32_t ti = __builtin_amdgcn_perm((k & 1) ? no : ne, idx[2 * half + (k >> 2)], sel);
-            const uint2 e = *(const uint2 *)(table + (ti << 3));
-            s = __builtin_fmaf(h2f_lo(e.x), xs[4 * k + 0], s);
-            s = __builtin_fmaf(h2f_hi(e.x), xs[4 * k + 1], s);
-            s = __builtin_fmaf(h2f_lo(e.y), xs[4 * k + 2], s);
-            s = __builtin_fmaf(h2f_hi(e.y), xs[4 * k + 3], s);
+            const uint32_t ti = __builtin_amdgcn_perm((k & 1) ? no : ne, r.idx[2 * half + (k >> 2)], sel);
+            const u32x2 v = lds_load<u32x2>(ti << 3);
+            s0 = __builtin_fmaf(h2f_lo(v.x), xs[4 * k + 0], s0);
+            s1 = __builtin_fmaf(h2f_hi(v.x), xs[4 * k + 1], s1);
+            s0 = __builtin_fmaf(h2f_lo(v.y), xs[4 * k + 2], s0);
+            s1 = __builtin_fmaf(h2f_hi(v.y), xs[4 * k + 3], s1);
         }
-        acc = __builtin_fmaf(db, s, acc);
+        acc = __builtin_fmaf(db, s0 + s1, acc);
     }
     return acc;
 }
 
-template <int G>
-__device__ __forceinline__ void iq3_tile(const GemvArgs &a, uint8_t *smem, int tile, int split) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int kb0 = (int)((int64_t)split * a.nb / a.splits);
-    const int kb1 = (int)((int64_t)(split + 1) * a.nb / a.splits);
-    const int row0 = tile * kTileRows;
+template <typename T>
+__device__ __forceinline__ void lds_store(uint32_t addr, T v) {
+    *(__attribute__((address_space(3))) T *)(size_t)addr = v;
+}
 
-    uint8_t *table = smem;                                   // [16][256] x 8 bytes
-    uint32_t *stage = (uint32_t *)(smem + kTableBytes);      // [2][64][25] dwords
-
-    // Sign-folded fp16 table: entry (s, i) = grid row i with component c negated
-    // when bit c of s is set.
-    for (int e = tid; e < 16 * 256; e += kThreads) {
-        const int s = e >> 8, i = e & 255;
-        const float4 g = *(const float4 *)(a.grid + 4 * i);
-        const float gv[4] = {g.x, g.y, g.z, g.w};
-        uint32_t hb[4];
+// Entry (s, i) of the sign-folded table (at LDS address 0) from grid row g.
+__device__ __forceinline__ void iq3_table_entry(int s, int i, float4 g) {
+    const float v[4] = {(s & 1) ? -g.x : g.x, (s & 2) ? -g.y : g.y, (s & 4) ? -g.z : g.z,
+                        (s & 8) ? -g.w : g.w};
+    uint32_t hb[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const _Float16 hv = (_Float16)(((s >> c) & 1) ? -gv[c] : gv[c]);
-            hb[c] = __builtin_bit_cast(uint16_t, hv);
+    for (int c = 0; c < 4; ++c) hb[c] = __builtin_bit_cast(uint16_t, (_Float16)v[c]);
+    const u32x2 e = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+    lds_store<u32x2>(s * 2048 + i * 8, e);
+}
+
+template <int G, int W, int R>
+__device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &single,
+                                           const float *grid, int nitems, uint8_t *smem) {
+    static_assert(R >= 2 && R <= 4, "ring of two to four stages");
+    using C = Iq3Cfg<W, R>;
+    constexpr int BPS = C::kBps;
+    const int lane = threadIdx.x & 63;
+    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+    const int wave = 4 * j + G;
+    const int stride = gridDim.x;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    int kc = blockIdx.x;  // item being computed (the grid never exceeds nitems)
+    if (kc >= nitems) return;
+
+    // Wavefronts 0..3 stage the grid's 4 KB (lane l of wavefront w: bytes
+    // 16*(64w + l)) ahead of any stage copy, so waiting for it leaves those in flight.
+    if (wave < 4)
+        dma16((const uint8_t *)grid + 16 * (64 * wave + lane), lds0 + C::kGrid + 1024 * wave);
+
+    // This wavefront's copy lanes: granule k = 64i + lane (k < 112) of its 16
+    // rows, i.e. granule k%7 of the window of row 16G + k/7, which lands at
+    // LDS byte 16k of the wavefront's quarter of the block column.
+    int crow[2];
+    uint32_t cgran[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int k = min(64 * i + lane, 111);
+        crow[i] = 16 * G + k / 7;
+        cgran[i] = 16u * (uint32_t)(k % 7);
+    }
+
+    Iq3Item c;
+    iq3_load_item<BPS>(c, kc, g, single);
+
+    // copy cursor: next stage sd of item kd goes to ring slot slot_d
+    int kd = kc, sd = 0, slot_d = 0, pending = 0;
+    Iq3Item d = c;
+    uint32_t doff[2];  // this lane's granule of block 0 of its row, relative to d.sb (< 2 MB)
+    auto prep_copy = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            doff[i] = d.sb_off +
+                      (uint32_t)(min(d.row0 + crow[i], d.a.n_out - 1) - d.row0) *
+                          (uint32_t)d.a.row_bytes +
+                      cgran[i];
+    };
+    prep_copy();
+    uint32_t flags = 0;  // bit k: this wavefront's copies are in ring slot k
+    auto issue_next = [&]() {
+        if (kd >= nitems) return;
+        const int b = d.kb0 + sd * BPS + j;
+        if (b < d.kb1) {
+            const uint32_t base =
+                lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol + G * (16 * C::kWin);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (i == 0 || lane < 48) {
+                    // (offset + a multiple of 16) & ~15 keeps the granule index
+                    const uint32_t off = min(max((doff[i] + (uint32_t)(kIq3Bytes * b)) & ~15u, d.lo), d.hi);
+                    dma16(d.sb, off, base + 1024 * i);
+                }
+            }
+            flags |= 1u << slot_d;
+        } else {
+            flags &= ~(1u << slot_d);
         }
-        *(uint2 *)(table + 8 * e) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-    }
-
-    // Staging: dword c of the stage is dword c%25 of the window of tile row c/25.
-    // The window of the block at byte offset o starts at o & ~3; when o is a
-    // multiple of 4 its last dword would cover two bytes past the block, so that
-    // dword is read as 16 bits (the two bytes of d) to stay inside the buffer.
-    int64_t rowoff[kLoadsPerThread];
-    int dwi[kLoadsPerThread];
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-        const int c = tid + kThreads * i;
-        const int r = c / kWinDwords;
-        dwi[i] = c - kWinDwords * r;
-        rowoff[i] = (int64_t)min(row0 + r, a.n_out - 1) * a.row_bytes;
-    }
-    // Windows are aligned on absolute addresses, so every window dword is a
-    // naturally aligned 32-bit load (the weights are at least 2-byte aligned).
-    const uintptr_t wbase = (uintptr_t)a.w;
-    auto load_stage = [&](int b, uint32_t (&dst)[kLoadsPerThread]) {
-#pragma unroll
-        for (int i = 0; i < kLoadsPerThread; ++i) {
-            if (tid + kThreads * i < kStageDwords) {
-                const uintptr_t o = wbase + (uintptr_t)(rowoff[i] + (int64_t)b * kIq3Bytes);
-                const uintptr_t p = (o & ~(uintptr_t)3) + 4 * dwi[i];
-                if (dwi[i] == kWinDwords - 1 && (o & 3) == 0)
-                    dst[i] = load_u16((const uint8_t *)p);
-                else
-                    dst[i] = *(const uint32_t *)p;
+        ++pending;
+        slot_d = slot_d + 1 == R ? 0 : slot_d + 1;
+        if (++sd == d.nst) {
+            sd = 0;
+            kd += stride;
+            if (kd < nitems) {
+                iq3_load_item<BPS>(d, kd, g, single);
+                prep_copy();
             }
         }
     };
-
-    uint32_t r[kLoadsPerThread];
-    load_stage(kb0, r);
-    float acc = 0.0f;
-    const int64_t my_rowoff = (int64_t)min(row0 + lane, a.n_out - 1) * a.row_bytes;
-    for (int b = kb0; b < kb1; ++b) {
-        uint32_t *buf = stage + ((b - kb0) & 1) * kStageDwords;
 #pragma unroll
-        for (int i = 0; i < kLoadsPerThread; ++i)
-            if (tid + kThreads * i < kStageDwords) buf[tid + kThreads * i] = r[i];
-        if (b + 1 < kb1) load_stage(b + 1, r);
-        __syncthreads();
-        const uint32_t sh = (uint32_t)((wbase + (uintptr_t)(my_rowoff + (int64_t)b * kIq3Bytes)) & 3);
-        acc = iq3_chunk<G>(buf + lane * kWinDwords, sh, as_scalar(a.x) + (int64_t)kQK * b + 64 * G,
-                           table, acc);
+    for (int i = 0; i < R - 1; ++i) issue_next();
+
+    // Grid staged (this wavefront's part: its stage copies, two per stage, may
+    // stay in flight), then the sign-folded table from it.
+    if (wave < 4) wait_vmcnt_upto(2 * __builtin_popcount(flags));
+    lds_barrier();
+    {
+        const int t = threadIdx.x;
+        const int i = t & 255;
+        const float4 gv = *(const float4 *)(smem + C::kGrid + 16 * i);
+        for (int s = t >> 8; s < 16; s += W / 4) iq3_table_entry(s, i, gv);
     }
 
-    __syncthreads();
-    float *red = (float *)stage;  // [4][64], overlays stage 0
-    red[G * 64 + lane] = acc;
-    __syncthreads();
-    if constexpr (G == 0) {
-        float total[1];
-        float t = red[lane];
-        t += red[64 + lane];
-        t += red[128 + lane];
-        t += red[192 + lane];
-        total[0] = t;
-        tile_epilogue<1>(a, tile, split, total);
+    float *red = (float *)(smem + C::kRed);
+    int slot_c = 0;
+    for (;;) {
+        const int row = c.row0 + lane;
+        // low bits of this lane's row address (block offsets within granules)
+        const uint32_t rlo = (uint32_t)(uintptr_t)c.a.w +
+                             (uint32_t)min(row, c.a.n_out - 1) * (uint32_t)c.a.row_bytes;
+        float acc = 0.0f;
+        for (int s = 0; s < c.nst; ++s) {
+            // Copies of the stages after this one may stay in flight.
+            const int nxt = slot_c + 1 == R ? 0 : slot_c + 1;
+            int younger = 0;
+            if (R >= 3 && pending > 1) younger += 2 * (int)((flags >> nxt) & 1u);
+            if (R >= 4 && pending > 2) younger += 2 * (int)((flags >> (nxt + 1 == R ? 0 : nxt + 1)) & 1u);
+            wait_vmcnt_upto(younger);
+            lds_barrier();   // stage in slot_c complete for every wavefront (and the table)
+            issue_next();    // refill the slot computed in the previous step
+            const int b = c.kb0 + s * BPS + j;
+            if (b < c.kb1) {
+                const uint32_t sh = (rlo + (uint32_t)(kIq3Bytes * b)) & 15u;
+                const uint8_t *win = smem + C::kRing + slot_c * C::kSlot + j * C::kCol +
+                                     lane * C::kWin + (sh & 12u);
+                Iq3Raw raw;
+                iq3_fetch<G>(win, sh, raw);
+                const bool head = c.head && b == 0;
+                const bool tail = c.tail && b == c.a.nb - 1;
+                if (head || tail) {   // wave-uniform, at most twice per matrix
+                    if ((head && row == 0) || (tail && row == c.a.n_out - 1))
+                        iq3_fetch_direct<G>(c.a.w + (int64_t)row * c.a.row_bytes + kIq3Bytes * b, raw);
+                }
+                acc = iq3_dot<G>(raw, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
+            }
+            --pending;
+            slot_c = nxt;
+        }
+        // row sums of the W wavefronts, in wavefront order
+        red[wave * 64 + lane] = acc;
+        lds_barrier();
+        if (wave == 0) {
+            float tsum = red[lane];
+            for (int w = 1; w < W; ++w) tsum += red[w * 64 + lane];
+            const float total[1] = {tsum};
+            tile_epilogue<1>(c.a, c.tile, c.split, total);
+        }
+        kc += stride;
+        if (kc >= nitems) break;
+        iq3_load_item<BPS>(c, kc, g, single);
     }
 }
 
-__global__ __launch_bounds__(kThreads) void iq3_gemv_kernel(GemvArgs a) {
+template <int W, int R>
+__global__ __launch_bounds__(W * 64) void iq3_stream_kernel(GroupArgs g, GemvArgs single,
+                                                            const float *grid, int nitems) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int tile = blockIdx.x / a.splits;
-    const int split = blockIdx.x - tile * a.splits;
-    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-        case 0: iq3_tile<0>(a, smem, tile, split); break;
-        case 1: iq3_tile<1>(a, smem, tile, split); break;
-        case 2: iq3_tile<2>(a, smem, tile, split); break;
-        default: iq3_tile<3>(a, smem, tile, split); break;
+    switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
+        case 0: iq3_stream<0, W, R>(g, single, grid, nitems, smem); break;
+        case 1: iq3_stream<1, W, R>(g, single, grid, nitems, smem); break;
+        case 2: iq3_stream<2, W, R>(g, single, grid, nitems, smem); break;
+        default: iq3_stream<3, W, R>(g, single, grid, nitems, smem); break;
     }
 }
+
+// Resident workgroups of one kernel variant on the current device (cached).
+template <int W, int R>
+int iq3_slots() {
+    static int slots = 0;
+    if (slots == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        constexpr size_t lds = Iq3Cfg<W, R>::kLds;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, iq3_stream_kernel<W, R>,
+                                                         W * 64, lds) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        slots = per_cu * cus;
+    }
+    return slots;
+}
+
+template <int W, int R>
+hipError_t iq3_launch(const GroupArgs &g, const GemvArgs &single, const float *grid, int nitems,
+                      hipStream_t s) {
+    int n = iq3_slots<W, R>();
+    if (n > nitems) n = nitems;
+    constexpr size_t lds = Iq3Cfg<W, R>::kLds;
+    hipLaunchKernelGGL((iq3_stream_kernel<W, R>), dim3((unsigned)n), dim3(W * 64), lds, s, g,
+                       single, grid, nitems);
+    return hipGetLastError();
+}
+
+// Variant table: (waves, ring stages).
+#define QWG_IQ3_VARIANTS(X) X(4, 2) X(4, 3) X(4, 4) X(8, 2) X(8, 3) X(16, 2) X(16, 3)
+
+constexpr int iq3_key(int w, int r) { return w * 10 + r; }
 
 }  // namespace
 
@@ -243,11 +453,25 @@ hipError_t launch_iq3_dequant(const uint8_t *src, const float *grid, float *dst,
     return hipGetLastError();
 }
 
-hipError_t launch_iq3_gemv(const GemvArgs &a, hipStream_t s) {
-    const size_t lds = kTableBytes + 2 * (size_t)kStageBytes;
-    hipLaunchKernelGGL(iq3_gemv_kernel, dim3((unsigned)(a.tiles * a.splits)), dim3(kThreads), lds,
-                       s, a);
-    return hipGetLastError();
+int iq3_stream_slots(const Iq3Shape &sh) {
+    switch (iq3_key(sh.waves, sh.ring)) {
+#define X(w, r) \
+    case iq3_key(w, r): return iq3_slots<w, r>();
+        QWG_IQ3_VARIANTS(X)
+#undef X
+        default: return 0;
+    }
+}
+
+hipError_t launch_iq3_stream(const GroupArgs &g, const GemvArgs &single, const float *grid,
+                             int nitems, const Iq3Shape &sh, hipStream_t s) {
+    switch (iq3_key(sh.waves, sh.ring)) {
+#define X(w, r) \
+    case iq3_key(w, r): return iq3_launch<w, r>(g, single, grid, nitems, s);
+        QWG_IQ3_VARIANTS(X)
+#undef X
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace qwg

@@ -283,25 +283,6 @@ __global__ __launch_bounds__(W * 64) void q4k_gemv_kernel(GemvArgs a) {
     q4k_dispatch<NB, W>(a, smem, tile, blockIdx.x - tile * a.splits);
 }
 
-typedef const __attribute__((address_space(4))) GemvArgs *cargs_p;
-typedef const __attribute__((address_space(4))) uint32_t *cu32_p;
-
-__device__ __forceinline__ void load_args(GemvArgs &a, cargs_p pa) {
-    a.w = pa->w;
-    a.x = pa->x;
-    a.grid = pa->grid;
-    a.y = pa->y;
-    a.partial = pa->partial;
-    a.counters = pa->counters;
-    a.row_bytes = pa->row_bytes;
-    a.n_in = pa->n_in;
-    a.n_out = pa->n_out;
-    a.nb = pa->nb;
-    a.tiles = pa->tiles;
-    a.splits = pa->splits;
-    a.wg_begin = pa->wg_begin;
-}
-
 // Grouped launch (one workgroup per item): each workgroup reads its problem
 // index and descriptor with scalar loads, then runs the same tile pipeline.
 

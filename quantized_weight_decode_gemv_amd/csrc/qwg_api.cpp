@@ -92,6 +92,26 @@ bool use_stream_engine() {
     return v;
 }
 
+// IQ3 stream engine shape. Measured on MI355X: grouped streams run best with
+// 8-wavefront workgroups (two per CU), single GEMVs with 16 (one per CU, four
+// super-blocks per stage), both with a 2-stage ring. `waves` (if nonzero)
+// overrides the wavefront count; QWG_IQ3_WAVES / QWG_IQ3_RING override both
+// (tuning experiments). An unsupported combination falls back to the default.
+Iq3Shape iq3_shape(bool grouped, int waves) {
+    static const int env_w = env_int("QWG_IQ3_WAVES", 0);
+    static const int env_r = env_int("QWG_IQ3_RING", 0);
+    const Iq3Shape dflt = {grouped ? 8 : 16, 2};
+    Iq3Shape sh = dflt;
+    if (env_w) sh.waves = env_w;
+    if (env_r) sh.ring = env_r;
+    if (waves) sh.waves = waves;
+    if (iq3_stream_slots(sh) == 0) {
+        sh.ring = dflt.ring;
+        if (iq3_stream_slots(sh) == 0) sh = dflt;
+    }
+    return sh;
+}
+
 // Split-sum workspace, one per (device, stream): partial sums [splits][batch]
 // [tiles*64] fp32 followed by one counter per tile (choose_plan keeps every
 // plan inside these sizes).
@@ -167,6 +187,19 @@ int fill_gemv_args(GemvArgs &a, const void *w, const float *x, const float *grid
     return QWG_OK;
 }
 
+// Splits of an IQ3 GEMV: enough work items (tiles x splits) to give every
+// resident workgroup of the stream engine one, at most one split per
+// super-block, and partial sums inside the workspace.
+int iq3_splits(int tiles, int nb, int slots) {
+    if (tiles >= slots) return 1;
+    int s = slots / tiles;
+    if (s > nb) s = nb;
+    if (s < 1) s = 1;
+    while (s > 1 && ((size_t)s * tiles * kTileRows > kWsPartialFloats || (size_t)tiles > kWsCounters))
+        --s;
+    return s;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? QWG_OK : QWG_ERR_HIP; }
 
 }  // namespace
@@ -198,7 +231,13 @@ int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
     if (fmt != QWG_FMT_Q4K && fmt != QWG_FMT_IQ3) return -QWG_ERR_FORMAT;
     int rc = check_gemv_shape(n_in, n_out);
     if (rc) return -rc;
-    return choose_splits((int)((n_out + kTileRows - 1) / kTileRows), (int)(n_in / kQK));
+    const int tiles = (int)((n_out + kTileRows - 1) / kTileRows);
+    if (fmt == QWG_FMT_IQ3) {
+        const int slots = iq3_stream_slots(iq3_shape(false, 0));
+        if (slots <= 0) return -QWG_ERR_HIP;
+        return iq3_splits(tiles, (int)(n_in / kQK), slots);
+    }
+    return choose_splits(tiles, (int)(n_in / kQK));
 }
 
 int qwg_dequant_q4k(const void *src, float *dst, int64_t n, void *stream) {
@@ -270,24 +309,48 @@ int qwg_gemv_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
     return qwg_gemm_q4k(y, x, w, n_in, n_out, 1, stream);
 }
 
-int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
-                 int64_t n_out, void *stream) {
+int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                    int64_t n_out, int waves, int splits, void *stream) {
     if (!y || !x || !w || !grid) return QWG_ERR_NULL;
     int rc = check_gemv_shape(n_in, n_out);
     if (rc) return rc;
     if (!aligned(w, 2) || !aligned(x, 16) || !aligned(grid, 16) || !aligned(y, 4))
         return QWG_ERR_ALIGN;
+    if (waves != 0 && waves != 4 && waves != 8 && waves != 16) return QWG_ERR_SHAPE;
     GemvArgs a;
-    rc = fill_gemv_args(a, w, x, grid, y, n_in, n_out, kIq3Bytes, 1, (hipStream_t)stream,
-                        nullptr);
-    if (rc) return rc;
-    return hip_status(launch_iq3_gemv(a, (hipStream_t)stream));
+    fill_shape(a, w, x, grid, y, n_in, n_out, kIq3Bytes);
+    if (splits < 0 || splits > a.nb) return QWG_ERR_SHAPE;
+    if (splits > 1 && ((size_t)splits * a.tiles * kTileRows > kWsPartialFloats ||
+                       (size_t)a.tiles > kWsCounters))
+        return QWG_ERR_SHAPE;
+    const Iq3Shape sh = iq3_shape(false, waves);
+    const int slots = iq3_stream_slots(sh);
+    if (slots <= 0) return QWG_ERR_HIP;
+    if (splits == 0) splits = iq3_splits(a.tiles, a.nb, slots);
+    a.splits = splits;
+    if (splits > 1) {
+        Workspace ws;
+        rc = get_workspace((hipStream_t)stream, &ws);
+        if (rc) return rc;
+        a.partial = ws.partial;
+        a.counters = ws.counters;
+    }
+    const GroupArgs none = {nullptr, nullptr};
+    return hip_status(
+        launch_iq3_stream(none, a, grid, a.tiles * splits, sh, (hipStream_t)stream));
+}
+
+int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                 int64_t n_out, void *stream) {
+    return qwg_gemv_iq3_ex(y, x, w, grid, n_in, n_out, 0, 0, stream);
 }
 
 // ------------------------------------------------------------------ grouped GEMV
 
 struct qwg_group {
     int device;
+    int fmt;              // QWG_FMT_Q4K or QWG_FMT_IQ3
+    const float *grid;    // IQ3: the grid every member uses
     void *dev_mem;        // GemvArgs[count] followed by uint32_t map[workgroups]
     GroupArgs args;
     int count;
@@ -295,10 +358,13 @@ struct qwg_group {
     int max_nb;
 };
 
-int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **out) {
-    if (!descs || !out) return QWG_ERR_NULL;
-    *out = nullptr;
-    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+namespace {
+
+int group_create(int fmt, const qwg_gemv_desc *descs, int count, const float *grid,
+                 qwg_group **out) {
+    const bool iq3 = fmt == QWG_FMT_IQ3;
+    const int block_bytes = iq3 ? kIq3Bytes : kQ4kBytes;
+    const uintptr_t w_align = iq3 ? 2 : 16;
     std::vector<GemvArgs> probs((size_t)count);
     int64_t total = 0;
     int max_nb = 1;
@@ -307,8 +373,8 @@ int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **out)
         if (!d.y || !d.x || !d.w) return QWG_ERR_NULL;
         int rc = check_gemv_shape(d.n_in, d.n_out);
         if (rc) return rc;
-        if (!aligned(d.w, 16) || !aligned(d.x, 16) || !aligned(d.y, 4)) return QWG_ERR_ALIGN;
-        fill_shape(probs[i], d.w, d.x, nullptr, d.y, d.n_in, d.n_out, kQ4kBytes);
+        if (!aligned(d.w, w_align) || !aligned(d.x, 16) || !aligned(d.y, 4)) return QWG_ERR_ALIGN;
+        fill_shape(probs[i], d.w, d.x, grid, d.y, d.n_in, d.n_out, block_bytes);
         total += probs[i].tiles;
         if (probs[i].nb > max_nb) max_nb = probs[i].nb;
     }
@@ -339,6 +405,8 @@ int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **out)
         delete g;
         return QWG_ERR_HIP;
     }
+    g->fmt = fmt;
+    g->grid = grid;
     g->args.problems = (const GemvArgs *)g->dev_mem;
     g->args.map = (const uint32_t *)((uint8_t *)g->dev_mem + pbytes);
     g->count = count;
@@ -348,12 +416,33 @@ int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **out)
     return QWG_OK;
 }
 
+}  // namespace
+
+int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **out) {
+    if (!descs || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    return group_create(QWG_FMT_Q4K, descs, count, nullptr, out);
+}
+
+int qwg_group_create_iq3(const qwg_gemv_desc *descs, int count, const float *grid,
+                         qwg_group **out) {
+    if (!descs || !grid || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    if (!aligned(grid, 16)) return QWG_ERR_ALIGN;
+    return group_create(QWG_FMT_IQ3, descs, count, grid, out);
+}
+
 int qwg_group_run(const qwg_group *g, void *stream) {
     if (!g) return QWG_ERR_NULL;
+    GemvArgs unused;
+    fill_shape(unused, nullptr, nullptr, nullptr, nullptr, kQK, 1, kQ4kBytes);
+    if (g->fmt == QWG_FMT_IQ3)
+        return hip_status(launch_iq3_stream(g->args, unused, g->grid, g->workgroups,
+                                            iq3_shape(true, 0), (hipStream_t)stream));
     if (use_stream_engine()) {
         const StreamShape sh = stream_shape(true);
-        GemvArgs unused;
-        fill_shape(unused, nullptr, nullptr, nullptr, nullptr, kQK, 1, kQ4kBytes);
         return hip_status(launch_q4k_stream(g->args, unused, g->workgroups, sh.waves, sh.ring,
                                             (hipStream_t)stream));
     }

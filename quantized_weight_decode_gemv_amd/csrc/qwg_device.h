@@ -24,6 +24,27 @@ __device__ __forceinline__ float h2f_hi(uint32_t v) {
 typedef const __attribute__((address_space(4))) float *cfloat_p;
 __device__ __forceinline__ cfloat_p as_scalar(const float *p) { return (cfloat_p)p; }
 
+// Problem descriptors and workgroup maps of a grouped launch are read through
+// the constant address space (scalar loads).
+typedef const __attribute__((address_space(4))) GemvArgs *cargs_p;
+typedef const __attribute__((address_space(4))) uint32_t *cu32_p;
+
+__device__ __forceinline__ void load_args(GemvArgs &a, cargs_p pa) {
+    a.w = pa->w;
+    a.x = pa->x;
+    a.grid = pa->grid;
+    a.y = pa->y;
+    a.partial = pa->partial;
+    a.counters = pa->counters;
+    a.row_bytes = pa->row_bytes;
+    a.n_in = pa->n_in;
+    a.n_out = pa->n_out;
+    a.nb = pa->nb;
+    a.tiles = pa->tiles;
+    a.splits = pa->splits;
+    a.wg_begin = pa->wg_begin;
+}
+
 // Asynchronous 16-byte global -> LDS copy (LDS DMA) of every active lane: lane
 // i's 16 bytes land at LDS byte address lds + 16*i. Issued from inline asm so
 // that the compiler does not guard later LDS reads with a wait for all
@@ -33,11 +54,42 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"{m0}"(lds), "v"(g) : "memory");
 }
 
+// The same with a 64-bit scalar base and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"{m0}"(lds), "v"(voff), "s"(sbase)
+                 : "memory");
+}
+
+// Loads from an absolute LDS byte address (kernels whose dynamic LDS is their
+// only LDS, so it starts at address 0). The address goes straight into the
+// ds_read instruction, with no base register to add.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ T lds_load(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) T *)(size_t)addr;
+}
+
 // Wait until at most N vector-memory operations of this wavefront are
 // outstanding (they complete in issue order).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait_vmcnt with a wavefront-uniform count in 0..7 (larger counts wait for
+// everything, which is always safe).
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+    switch (__builtin_amdgcn_readfirstlane(n)) {
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
 }
 
 // Workgroup barrier after this wavefront's LDS and scalar operations have

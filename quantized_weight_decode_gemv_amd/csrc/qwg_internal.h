@@ -54,6 +54,18 @@ hipError_t launch_q4k_group(const GroupArgs &g, int total_workgroups, int max_nb
 // != nullptr) or of `single`; waves in {4, 8, 16}, ring stages in {2, 3, 4}.
 hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nitems, int waves,
                              int ring, hipStream_t s);
-hipError_t launch_iq3_gemv(const GemvArgs &a, hipStream_t s);
+
+// IQ3 stream engine shape: wavefronts per workgroup (4, 8, 16) and LDS ring
+// stages (2, 3; 4 with 4 wavefronts).
+struct Iq3Shape {
+    int waves;
+    int ring;
+};
+// Resident workgroups of that variant on the current device (0 if unsupported).
+int iq3_stream_slots(const Iq3Shape &sh);
+// `nitems` work items (tile x split) of the group or of `single`; all members
+// of a group share `grid`.
+hipError_t launch_iq3_stream(const GroupArgs &g, const GemvArgs &single, const float *grid,
+                             int nitems, const Iq3Shape &sh, hipStream_t s);
 
 }  // namespace qwg

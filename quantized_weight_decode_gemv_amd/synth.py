@@ -125,7 +125,8 @@ def config(cfg: int) -> list[Problem]:
     """The five workloads: 1 = Q4_K 2048x2048; 2 = one TinyLlama-1.1B layer's
     seven projections; 3 = LM head 2048->32000 as GEMV and as B=8 GEMM; 4 = IQ3
     5632x2048 and 2048x5632; 5 = the full per-token stream (22 layers x 7
-    projections + LM head)."""
+    projections + LM head). Two more at the same shapes in IQ3: 6 = the
+    per-token stream, 7 = one layer's seven projections."""
     if cfg == 1:
         return [Problem("q4k_2048x2048", "q4k", DIM, DIM, 1, 1, 0)]
     if cfg == 2:
@@ -143,6 +144,15 @@ def config(cfg: int) -> list[Problem]:
                 out.append(Problem(f"L{layer}.{n}", "q4k", o, i, 1, 5, 7 * layer + p))
         out.append(Problem("lm_head", "q4k", VOCAB, DIM, 1, 5, 7 * LAYERS))
         return out
+    if cfg == 6:
+        out = []
+        for layer in range(LAYERS):
+            for p, (n, o, i) in enumerate(PROJ):
+                out.append(Problem(f"L{layer}.{n}", "iq3", o, i, 1, 6, 7 * layer + p))
+        out.append(Problem("lm_head", "iq3", VOCAB, DIM, 1, 6, 7 * LAYERS))
+        return out
+    if cfg == 7:
+        return [Problem(n, "iq3", o, i, 1, 7, t) for t, (n, o, i) in enumerate(PROJ)]
     raise ValueError(cfg)
 
 

@@ -31,8 +31,9 @@ def test_header_declares_the_entry_points():
     names = declared_symbols()
     for want in ("qwg_dequant_q4k", "qwg_dequant_iq3", "qwg_gemv_q4k", "qwg_gemv_iq3",
                  "qwg_gemm_q4k", "qwg_strerror", "qwg_row_bytes", "qwg_version",
-                 "qwg_plan_splits", "qwg_gemm_q4k_ex", "qwg_group_create_q4k", "qwg_group_run",
-                 "qwg_group_workgroups", "qwg_group_destroy"):
+                 "qwg_plan_splits", "qwg_gemm_q4k_ex", "qwg_gemv_iq3_ex", "qwg_group_create_q4k",
+                 "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
+                 "qwg_group_destroy"):
         assert want in names
 
 
@@ -109,6 +110,16 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_dequant_q4k(FAKE + 4, FAKE, 256, None), 3),
     (lambda L: L.qwg_dequant_q4k(FAKE, FAKE + 4, 256, None), 3),
     (lambda L: L.qwg_dequant_iq3(FAKE + 1, FAKE, FAKE, 256, None), 3),
+    # IQ3 with an explicit decomposition
+    (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, None, 256, 1, 4, 1, None), 1),
+    (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 384, 1, 4, 1, None), 2),
+    (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 256, 1, 2, 1, None), 2),
+    (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 256, 1, 32, 1, None), 2),
+    (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 512, 1, 4, 3, None), 2),
+    (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 512, 1, 4, -1, None), 2),
+    (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE + 3, FAKE, 256, 1, 4, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE + 8, FAKE, FAKE, 256, 1, 4, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE + 8, 256, 1, 4, 1, None), 3),
 ])
 def test_validation_errors(L, call, status):
     assert call(L) == status
@@ -132,6 +143,24 @@ def test_group_validation_errors(L, desc, status):
     out = ctypes.c_void_p(123)
     assert L.qwg_group_create_q4k(arr, 2, ctypes.byref(out)) == status
     assert out.value is None  # nothing allocated, handle cleared
+
+
+@pytest.mark.parametrize("desc,status", [
+    ((0, FAKE, FAKE, 256, 1), 1),
+    ((FAKE, FAKE, FAKE, 300, 1), 2),
+    ((FAKE, FAKE + 4, FAKE, 256, 1), 3),
+    ((FAKE, FAKE, FAKE + 1, 256, 1), 3),   # IQ3 weights need only 2-byte alignment
+    ((FAKE + 2, FAKE, FAKE, 256, 1), 3),
+])
+def test_iq3_group_validation_errors(L, desc, status):
+    arr = (_Desc * 2)(_Desc(FAKE, FAKE, FAKE + 2, 256, 64), _Desc(*desc))
+    out = ctypes.c_void_p(123)
+    assert L.qwg_group_create_iq3(arr, 2, FAKE, ctypes.byref(out)) == status
+    assert out.value is None
+    ok = (_Desc * 1)(_Desc(FAKE, FAKE, FAKE + 2, 256, 64))
+    assert L.qwg_group_create_iq3(ok, 1, None, ctypes.byref(out)) == 1
+    assert L.qwg_group_create_iq3(ok, 1, FAKE + 4, ctypes.byref(out)) == 3
+    assert L.qwg_group_create_iq3(ok, 0, FAKE, ctypes.byref(out)) == 2
 
 
 def test_group_null_and_count_errors(L):

@@ -411,3 +411,140 @@ def test_gemv_iq3_one_hot_is_exact_column():
         x[k] = 1.0
         y = host(qwg.gemv_iq3(wd, dev(x), gd))
         assert_bits(y + 0.0, deq[:, k] + 0.0, f"k={k}")
+
+
+@pytest.mark.parametrize("waves", [4, 8, 16])
+@pytest.mark.parametrize("n_out,n_in,splits", [(70, 256, 1), (70, 2048, 1), (70, 2048, 3),
+                                               (130, 5632, 1), (130, 5632, 5), (130, 5632, 22),
+                                               (1, 1024, 4), (300, 1280, 2), (2000, 768, 1)])
+def test_gemv_iq3_every_plan(waves, n_out, n_in, splits):
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 110, n_out + splits)
+    x = synth.activations(n_in, 110, n_out + splits)
+    y = host(qwg.gemv_iq3(dev(w), dev(x), dev(grid), waves=waves, splits=splits))
+    yr, sr = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    assert_bound(y, yr, sr, f"waves={waves} splits={splits}")
+
+
+def test_gemv_iq3_ex_rejects_bad_plans():
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(64, 512, 111, 0)
+    x = synth.activations(512, 111, 0)
+    for waves, splits in [(2, 1), (32, 1), (4, 3), (16, -1)]:
+        with pytest.raises(qwg.QwgError) as e:
+            qwg.gemv_iq3(dev(w), dev(x), dev(grid), waves=waves, splits=splits)
+        assert e.value.status == 2
+
+
+def _guarded_iq3(w: np.ndarray, offset: int, fill: int = 0xFF):
+    """w placed at `offset` bytes past a 256-byte boundary inside a larger
+    buffer whose other bytes are `fill` (0xFF: NaN as an fp16 scale), so that
+    any use of a byte outside w shows in the result."""
+    buf = torch.full((w.size + offset + 64,), fill, dtype=torch.uint8, device=DEV)
+    buf[offset:offset + w.size] = dev(w.reshape(-1))
+    wd = buf[offset:offset + w.size]
+    assert wd.data_ptr() % 256 == offset
+    return wd
+
+
+@pytest.mark.parametrize("offset", [0, 2, 4, 6, 8, 10, 12, 14, 18, 30])
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 512), (65, 768), (64, 5632), (129, 2048)])
+def test_gemv_iq3_buffer_edges(offset, n_out, n_in):
+    # The first and last 16-byte granules of w reach outside it unless w starts
+    # and ends on a granule boundary; those bytes must never reach the result,
+    # and y must be written only inside its own range.
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 112, offset)
+    x = synth.activations(n_in, 112, offset)
+    wd, xd, gd = _guarded_iq3(w, offset), dev(x), dev(grid)
+    yr, sr = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    ybuf = torch.full((n_out + 130,), -7.0, device=DEV)
+    for waves, splits in [(0, 0), (4, 1), (16, 1), (8, n_in // 256)]:
+        y = ybuf[64:64 + n_out]
+        qwg.gemv_iq3(wd, xd, gd, out=y, waves=waves, splits=splits)
+        yb = host(ybuf)
+        assert_bound(yb[64:64 + n_out], yr, sr, f"offset={offset} waves={waves} splits={splits}")
+        assert (yb[:64] == -7.0).all() and (yb[64 + n_out:] == -7.0).all(), "write outside y"
+
+
+@pytest.mark.parametrize("waves", [4, 8, 16])
+def test_gemv_iq3_integer_exact_every_shape(waves):
+    # d = 4 and code in 0..3: every partial sum is an exact integer, so every
+    # decomposition must give the oracle's value exactly
+    n_out, n_in = 130, 5632
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 113, 0).reshape(-1, 98).copy()
+    w[:, 96], w[:, 97] = 0x00, 0x44
+    words = w[:, 64:96].copy().view("<u4") & np.uint32(0x3FFFFFFF)
+    w[:, 64:96] = words.view(np.uint8)
+    w = w.reshape(n_out, -1)
+    x = np.random.default_rng(10).integers(-8, 9, n_in).astype(np.float32)
+    yr, _ = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    for splits in (1, 2, 7, 22):
+        y = host(qwg.gemv_iq3(dev(w), dev(x), dev(grid), waves=waves, splits=splits))
+        assert np.array_equal(y.astype(np.float64), yr), f"splits={splits}"
+
+
+def test_gemv_iq3_deterministic():
+    p = synth.config(4)[1]
+    grid = dev(synth.iq3_grid())
+    w, x = dev(synth.weights(p)), dev(synth.inputs(p))
+    y0 = host(qwg.gemv_iq3(w, x, grid)).copy()
+    for _ in range(3):
+        assert_bits(host(qwg.gemv_iq3(w, x, grid)), y0, "rerun")
+
+
+# ---------------------------------------------------------------- IQ3 groups
+
+def test_iq3_group_layer_and_repeat_runs():
+    probs = synth.config(7)
+    grid = synth.iq3_grid()
+    ws = [synth.weights(p) for p in probs]
+    xs = [synth.inputs(p) for p in probs]
+    W, X = [dev(w) for w in ws], [dev(x) for x in xs]
+    Y = [torch.full((p.n_out,), float("nan"), device=DEV) for p in probs]
+    g = qwg.Iq3Group(zip(W, X, Y), dev(grid))
+    assert g.workgroups == sum((p.n_out + 63) // 64 for p in probs)
+    g.run()
+    first = [host(y).copy() for y in Y]
+    for p, w, x, y in zip(probs, ws, xs, first):
+        yr, sr = oracle.gemv_iq3(w, grid, x, p.n_in, p.n_out)
+        assert_bound(y, yr, sr, "iq3 group " + p.name)
+    g.run()
+    for p, y, y0 in zip(probs, Y, first):
+        assert_bits(host(y), y0, "iq3 group rerun " + p.name)
+    X[4].mul_(-0.5)
+    g.run()
+    yr, sr = oracle.gemv_iq3(ws[4], grid, -0.5 * xs[4], probs[4].n_in, probs[4].n_out)
+    assert_bound(host(Y[4]), yr, sr, "iq3 group rerun with new x")
+    g.close()
+
+
+def test_iq3_group_ragged_members_at_odd_offsets():
+    shapes = [(1, 256), (65, 512), (200, 5632), (3, 65536), (4097, 768), (64, 2048)]
+    grid = synth.iq3_grid()
+    ws = [synth.iq3_weights(o, i, 114, k) for k, (o, i) in enumerate(shapes)]
+    xs = [synth.activations(i, 114, k) for k, (o, i) in enumerate(shapes)]
+    W = [_guarded_iq3(w, 2 * k + 2) for k, w in enumerate(ws)]
+    Y = [torch.empty(o, device=DEV) for o, _ in shapes]
+    g = qwg.Iq3Group(zip(W, [dev(x) for x in xs], Y), dev(grid))
+    g.run()
+    for (o, i), w, x, y in zip(shapes, ws, xs, Y):
+        yr, sr = oracle.gemv_iq3(w, grid, x, i, o)
+        assert_bound(host(y), yr, sr, f"iq3 group member {o}x{i}")
+
+
+def test_iq3_group_stream_sampled_rows():
+    probs = synth.config(6)
+    grid = synth.iq3_grid()
+    rng = np.random.default_rng(7)
+    ws = [synth.weights(p) for p in probs]
+    xs = [synth.inputs(p) for p in probs]
+    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    g = qwg.Iq3Group(zip([dev(w) for w in ws], [dev(x) for x in xs], Y), dev(grid))
+    for _ in range(3):
+        g.run()
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 16)]))
+        yr, sr = oracle.gemv_iq3_rows(w, grid, x, p.n_in, rows)
+        assert_bound(host(y)[rows], yr, sr, "iq3 group " + p.name)
