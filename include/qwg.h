@@ -161,6 +161,27 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
                     int batch, int waves, int splits, void *stream);
 
 /*
+ * Tile layout for Q4_K (a one-time, load-time reordering of the same 144-byte
+ * blocks for the GEMV's streaming pattern): for each 64-row tile, for each
+ * block column b, the tile's 64 blocks of column b back to back (9216 bytes);
+ * rows past n_out in the last tile are zero blocks. Block (r, b) of the
+ * row-major matrix moves to byte ((r/64)*(n_in/256) + b)*9216 + (r%64)*144.
+ * A stage of the GEMV then copies one contiguous 9216-byte run instead of 64
+ * rows' 144-byte pieces.
+ *
+ * qwg_tiled_bytes: bytes of the tile layout (ceil(n_out/64)*64 rows), or a
+ * negative status (QWG_FMT_Q4K only).
+ * qwg_pack_q4k_tiles: src (row-major, as qwg_gemv_q4k takes it) -> dst (tile
+ * layout, qwg_tiled_bytes bytes); both 16-byte aligned, must not overlap.
+ * qwg_gemv_q4k_tiled: qwg_gemv_q4k on tile-layout weights (same arguments,
+ * alignment and accuracy).
+ */
+int64_t qwg_tiled_bytes(int fmt, int64_t n_in, int64_t n_out);
+int qwg_pack_q4k_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
+int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                       void *stream);
+
+/*
  * Grouped GEMV: many independent GEMVs of one format in one launch (one grid
  * whose workgroups belong to different matrices), for streams of independent
  * weight-bound products such as the q/k/v or gate/up projections that share an
@@ -197,6 +218,8 @@ typedef struct qwg_group qwg_group;
 int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **group);
 int qwg_group_create_iq3(const qwg_gemv_desc *descs, int count, const float *grid,
                          qwg_group **group);
+/* As qwg_group_create_q4k, every member's weights in the tile layout. */
+int qwg_group_create_q4k_tiled(const qwg_gemv_desc *descs, int count, qwg_group **group);
 int qwg_group_run(const qwg_group *group, void *stream);
 int qwg_group_workgroups(const qwg_group *group);
 int qwg_group_destroy(qwg_group *group);

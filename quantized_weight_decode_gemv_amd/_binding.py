@@ -51,12 +51,18 @@ def lib() -> ctypes.CDLL:
         L.qwg_gemm_q4k_ex.argtypes = [P, P, P, I64, I64, I, I, I, P]
         L.qwg_gemv_iq3_ex.argtypes = [P, P, P, P, I64, I64, I, I, P]
         L.qwg_group_create_q4k.argtypes = [P, I, ctypes.POINTER(P)]
+        L.qwg_group_create_q4k_tiled.argtypes = [P, I, ctypes.POINTER(P)]
+        L.qwg_tiled_bytes.argtypes = [I, I64, I64]
+        L.qwg_tiled_bytes.restype = I64
+        L.qwg_pack_q4k_tiles.argtypes = [P, P, I64, I64, P]
+        L.qwg_gemv_q4k_tiled.argtypes = [P, P, P, I64, I64, P]
         L.qwg_group_create_iq3.argtypes = [P, I, P, ctypes.POINTER(P)]
         L.qwg_group_run.argtypes = [P, P]
         L.qwg_group_workgroups.argtypes = [P]
         L.qwg_group_destroy.argtypes = [P]
         for f in ("qwg_dequant_q4k", "qwg_dequant_iq3", "qwg_gemv_q4k", "qwg_gemv_iq3",
                   "qwg_gemv_iq3_ex", "qwg_gemm_q4k", "qwg_gemm_q4k_ex", "qwg_group_create_q4k",
+                  "qwg_group_create_q4k_tiled", "qwg_pack_q4k_tiles", "qwg_gemv_q4k_tiled",
                   "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
                   "qwg_group_destroy"):
             getattr(L, f).restype = I
@@ -156,6 +162,46 @@ def gemv_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) 
     return out
 
 
+def tiled_bytes(n_in: int, n_out: int) -> int:
+    v = lib().qwg_tiled_bytes(QWG_FMT_Q4K, n_in, n_out)
+    if v < 0:
+        raise ValueError(f"invalid shape n_in={n_in} n_out={n_out}")
+    return v
+
+
+def pack_q4k_tiles(w: torch.Tensor, n_in: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-major Q4_K weights (uint8, n_out rows) -> the tile layout (uint8,
+    tiled_bytes(n_in, n_out) bytes) that gemv_q4k_tiled and tiled groups take."""
+    n_out = _weights(w, n_in, Q4K_BYTES)
+    nbytes = tiled_bytes(n_in, n_out)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _dev(out, "out", torch.uint8)
+    if out.numel() != nbytes:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_pack_q4k_tiles(out.data_ptr(), w.data_ptr(), n_in, n_out, _stream(w)),
+           "qwg_pack_q4k_tiles")
+    return out
+
+
+def gemv_q4k_tiled(w: torch.Tensor, x: torch.Tensor, n_out: int,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x for weights in the tile layout (pack_q4k_tiles)."""
+    _dev(w, "w", torch.uint8)
+    _dev(x, "x", torch.float32)
+    n_in = x.numel()
+    if w.numel() != tiled_bytes(n_in, n_out):
+        raise ValueError("w is not a tile-layout matrix of this shape")
+    if out is None:
+        out = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n_out:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_gemv_q4k_tiled(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out,
+                                    _stream(x)), "qwg_gemv_q4k_tiled")
+    return out
+
+
 def _grid(grid: torch.Tensor) -> None:
     _dev(grid, "grid", torch.float32)
     if grid.shape != (256, 4):
@@ -223,7 +269,8 @@ class Group:
     current x_i.
     """
 
-    def __init__(self, members, fmt: int = QWG_FMT_Q4K, grid: torch.Tensor | None = None):
+    def __init__(self, members, fmt: int = QWG_FMT_Q4K, grid: torch.Tensor | None = None,
+                 tiled: bool = False):
         members = list(members)
         if not members:
             raise ValueError("a group needs at least one member")
@@ -233,13 +280,21 @@ class Group:
             if grid is None:
                 raise ValueError("an IQ3 group needs the grid")
             _grid(grid)
+        if tiled and fmt != QWG_FMT_Q4K:
+            raise ValueError("the tile layout is a Q4_K layout")
         block_bytes = Q4K_BYTES if fmt == QWG_FMT_Q4K else IQ3_BYTES
         descs = (GemvDesc * len(members))()
         for i, (w, x, y) in enumerate(members):
             _dev(x, "x", torch.float32)
             _dev(y, "y", torch.float32)
             n_in = x.numel()
-            n_out = _weights(w, n_in, block_bytes)
+            if tiled:
+                _dev(w, "w", torch.uint8)
+                n_out = y.numel()
+                if w.numel() != tiled_bytes(n_in, n_out):
+                    raise ValueError(f"member {i}: w is not a tile-layout matrix of this shape")
+            else:
+                n_out = _weights(w, n_in, block_bytes)
             if y.numel() != n_out:
                 raise ValueError(f"member {i}: y has {y.numel()} elements, expected {n_out}")
             descs[i] = GemvDesc(y.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out)
@@ -247,7 +302,10 @@ class Group:
         self._grid = grid
         self._device = members[0][1].device
         handle = ctypes.c_void_p()
-        if fmt == QWG_FMT_Q4K:
+        if fmt == QWG_FMT_Q4K and tiled:
+            _check(lib().qwg_group_create_q4k_tiled(descs, len(members), ctypes.byref(handle)),
+                   "qwg_group_create_q4k_tiled")
+        elif fmt == QWG_FMT_Q4K:
             _check(lib().qwg_group_create_q4k(descs, len(members), ctypes.byref(handle)),
                    "qwg_group_create_q4k")
         else:
@@ -279,10 +337,11 @@ class Group:
 
 
 class Q4kGroup(Group):
-    """Group of Q4_K GEMVs (members as for Group)."""
+    """Group of Q4_K GEMVs (members as for Group; tiled: weights in the tile
+    layout, y giving each member's n_out)."""
 
-    def __init__(self, members):
-        super().__init__(members, QWG_FMT_Q4K)
+    def __init__(self, members, tiled: bool = False):
+        super().__init__(members, QWG_FMT_Q4K, tiled=tiled)
 
 
 class Iq3Group(Group):

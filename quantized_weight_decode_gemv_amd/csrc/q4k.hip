@@ -74,6 +74,25 @@ __global__ __launch_bounds__(256) void q4k_dequant_kernel(const uint8_t *__restr
     }
 }
 
+// ------------------------------------------------------------------ tile layout
+
+// One workgroup per (tile, block column): the 64 rows' block b (row-major
+// source) written back to back; rows past n_out become zero blocks.
+__global__ __launch_bounds__(256) void q4k_pack_tiles_kernel(const uint8_t *__restrict__ src,
+                                                             uint8_t *__restrict__ dst, int nb,
+                                                             int n_out) {
+    const int b = blockIdx.x % nb;
+    const int tile = blockIdx.x / nb;
+    const int64_t row_bytes = (int64_t)nb * kQ4kBytes;
+    uint8_t *out = dst + (int64_t)blockIdx.x * kStageBytes;
+    for (int k = threadIdx.x; k < kStageBytes / 16; k += blockDim.x) {
+        const int r = tile * kTileRows + k / 9;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < n_out) v = *(const uint4 *)(src + r * row_bytes + b * kQ4kBytes + 16 * (k % 9));
+        *(uint4 *)(out + 16 * k) = v;
+    }
+}
+
 // ------------------------------------------------------------------ GEMV / GEMM
 
 // Scale and min of sub-blocks 2G and 2G+1 from the packed bytes p[0..11]
@@ -326,6 +345,7 @@ struct Item {
     int nb;
     int nst;   // stages = ceil(nb / BPS)
     int row0;
+    int layout;
 };
 
 template <int BPS>
@@ -338,6 +358,7 @@ __device__ __forceinline__ void load_item(Item &it, int k, const GroupArgs &g, c
         it.n_out = single.n_out;
         it.nb = single.nb;
         it.row0 = k * kTileRows;
+        it.layout = single.layout;
     } else {
         const cargs_p pa = (cargs_p)g.problems + ((cu32_p)g.map)[k];
         it.w = pa->w;
@@ -347,6 +368,7 @@ __device__ __forceinline__ void load_item(Item &it, int k, const GroupArgs &g, c
         it.n_out = pa->n_out;
         it.nb = pa->nb;
         it.row0 = (k - pa->wg_begin) * kTileRows;
+        it.layout = pa->layout;
     }
     it.nst = (it.nb + BPS - 1) / BPS;
 }
@@ -394,11 +416,26 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
     // copy cursor: next stage sd of item kd goes to ring slot slot_d
     int kd = kc, sd = 0, slot_d = 0, pending = 0;
     Item d = c;
+    // Block b of this wavefront's copy granule i comes from dbase + b*dstride +
+    // doff[i]: in the row layout the rows are row_bytes apart (rows past n_out
+    // repeat the last row); in the tile layout a tile's block column is 9216
+    // contiguous bytes in copy order.
     int64_t doff[3];
+    const uint8_t *dbase = nullptr;
+    int dstride = 0;
     auto prep_copy = [&]() {
+        if (d.layout == kLayoutTiles) {
+            dbase = d.w + (int64_t)(d.row0 / kTileRows) * d.nb * kStageBytes;
+            dstride = kStageBytes;
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
-            doff[i] = (int64_t)min(d.row0 + crow[i], d.n_out - 1) * d.row_bytes + cpart[i];
+            for (int i = 0; i < 3; ++i) doff[i] = (int64_t)crow[i] * kQ4kBytes + cpart[i];
+        } else {
+            dbase = d.w;
+            dstride = kQ4kBytes;
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+                doff[i] = (int64_t)min(d.row0 + crow[i], d.n_out - 1) * d.row_bytes + cpart[i];
+        }
     };
     prep_copy();
     uint32_t flags = 0;  // bit k: this wavefront's copies are in ring slot k
@@ -407,7 +444,7 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
         const int b = sd * BPS + j;
         if (b < d.nb) {
             const uint32_t base = lds0 + slot_d * C::kSlot + j * C::kBlock + G * C::kQuarter;
-            const uint8_t *wb = d.w + (int64_t)b * kQ4kBytes;
+            const uint8_t *wb = dbase + (int64_t)b * dstride;
             dma16(wb + doff[0], base);
             dma16(wb + doff[1], base + 1024);
             if (lane < 32) {
@@ -504,6 +541,13 @@ hipError_t launch_q4k_dequant(const uint8_t *src, float *dst, int64_t nblocks, h
     if (groups > 65536) groups = 65536;
     hipLaunchKernelGGL(q4k_dequant_kernel, dim3((unsigned)groups), dim3(256), 0, s, src, dst,
                        nblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, hipStream_t s) {
+    const int64_t tiles = ((int64_t)n_out + kTileRows - 1) / kTileRows;
+    hipLaunchKernelGGL(q4k_pack_tiles_kernel, dim3((unsigned)(tiles * nb)), dim3(256), 0, s, src,
+                       dst, nb, n_out);
     return hipGetLastError();
 }
 

@@ -84,6 +84,9 @@ StreamShape stream_shape(bool grouped) {
     StreamShape sh;
     sh.waves = env_w ? env_w : (grouped ? 4 : 8);
     sh.ring = env_r ? env_r : 2;
+    const bool built = (sh.waves == 4 || sh.waves == 8 || sh.waves == 16) &&
+                       (sh.ring == 2 || sh.ring == 3);
+    if (!built) sh = {grouped ? 4 : 8, 2};  // an override with no compiled variant
     return sh;
 }
 
@@ -168,6 +171,7 @@ void fill_shape(GemvArgs &a, const void *w, const float *x, const float *grid, f
     a.wg_begin = 0;
     a.partial = nullptr;
     a.counters = nullptr;
+    a.layout = kLayoutRows;
 }
 
 int fill_gemv_args(GemvArgs &a, const void *w, const float *x, const float *grid, float *y,
@@ -309,6 +313,36 @@ int qwg_gemv_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
     return qwg_gemm_q4k(y, x, w, n_in, n_out, 1, stream);
 }
 
+int64_t qwg_tiled_bytes(int fmt, int64_t n_in, int64_t n_out) {
+    if (fmt != QWG_FMT_Q4K) return -QWG_ERR_FORMAT;
+    const int rc = check_gemv_shape(n_in, n_out);
+    if (rc) return -rc;
+    return ((n_out + kTileRows - 1) / kTileRows) * kTileRows * (n_in / kQK) * kQ4kBytes;
+}
+
+int qwg_pack_q4k_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
+    if (!dst || !src) return QWG_ERR_NULL;
+    const int rc = check_gemv_shape(n_in, n_out);
+    if (rc) return rc;
+    if (!aligned(dst, 16) || !aligned(src, 16)) return QWG_ERR_ALIGN;
+    return hip_status(launch_q4k_pack_tiles((const uint8_t *)src, (uint8_t *)dst, (int)(n_in / kQK),
+                                            (int)n_out, (hipStream_t)stream));
+}
+
+int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                       void *stream) {
+    if (!y || !x || !w) return QWG_ERR_NULL;
+    const int rc = check_gemv_shape(n_in, n_out);
+    if (rc) return rc;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
+    GemvArgs a;
+    fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
+    a.layout = kLayoutTiles;
+    const StreamShape sh = stream_shape(false);
+    const GroupArgs none = {nullptr, nullptr};
+    return hip_status(launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, (hipStream_t)stream));
+}
+
 int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                     int64_t n_out, int waves, int splits, void *stream) {
     if (!y || !x || !w || !grid) return QWG_ERR_NULL;
@@ -350,6 +384,7 @@ int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int
 struct qwg_group {
     int device;
     int fmt;              // QWG_FMT_Q4K or QWG_FMT_IQ3
+    int layout;           // kLayoutRows or kLayoutTiles
     const float *grid;    // IQ3: the grid every member uses
     void *dev_mem;        // GemvArgs[count] followed by uint32_t map[workgroups]
     GroupArgs args;
@@ -360,7 +395,7 @@ struct qwg_group {
 
 namespace {
 
-int group_create(int fmt, const qwg_gemv_desc *descs, int count, const float *grid,
+int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, const float *grid,
                  qwg_group **out) {
     const bool iq3 = fmt == QWG_FMT_IQ3;
     const int block_bytes = iq3 ? kIq3Bytes : kQ4kBytes;
@@ -375,6 +410,7 @@ int group_create(int fmt, const qwg_gemv_desc *descs, int count, const float *gr
         if (rc) return rc;
         if (!aligned(d.w, w_align) || !aligned(d.x, 16) || !aligned(d.y, 4)) return QWG_ERR_ALIGN;
         fill_shape(probs[i], d.w, d.x, grid, d.y, d.n_in, d.n_out, block_bytes);
+        probs[i].layout = layout;
         total += probs[i].tiles;
         if (probs[i].nb > max_nb) max_nb = probs[i].nb;
     }
@@ -406,6 +442,7 @@ int group_create(int fmt, const qwg_gemv_desc *descs, int count, const float *gr
         return QWG_ERR_HIP;
     }
     g->fmt = fmt;
+    g->layout = layout;
     g->grid = grid;
     g->args.problems = (const GemvArgs *)g->dev_mem;
     g->args.map = (const uint32_t *)((uint8_t *)g->dev_mem + pbytes);
@@ -422,7 +459,14 @@ int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **out)
     if (!descs || !out) return QWG_ERR_NULL;
     *out = nullptr;
     if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
-    return group_create(QWG_FMT_Q4K, descs, count, nullptr, out);
+    return group_create(QWG_FMT_Q4K, kLayoutRows, descs, count, nullptr, out);
+}
+
+int qwg_group_create_q4k_tiled(const qwg_gemv_desc *descs, int count, qwg_group **out) {
+    if (!descs || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    return group_create(QWG_FMT_Q4K, kLayoutTiles, descs, count, nullptr, out);
 }
 
 int qwg_group_create_iq3(const qwg_gemv_desc *descs, int count, const float *grid,
@@ -431,7 +475,7 @@ int qwg_group_create_iq3(const qwg_gemv_desc *descs, int count, const float *gri
     *out = nullptr;
     if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
     if (!aligned(grid, 16)) return QWG_ERR_ALIGN;
-    return group_create(QWG_FMT_IQ3, descs, count, grid, out);
+    return group_create(QWG_FMT_IQ3, kLayoutRows, descs, count, grid, out);
 }
 
 int qwg_group_run(const qwg_group *g, void *stream) {
@@ -441,7 +485,7 @@ int qwg_group_run(const qwg_group *g, void *stream) {
     if (g->fmt == QWG_FMT_IQ3)
         return hip_status(launch_iq3_stream(g->args, unused, g->grid, g->workgroups,
                                             iq3_shape(true, 0), (hipStream_t)stream));
-    if (use_stream_engine()) {
+    if (use_stream_engine() || g->layout == kLayoutTiles) {
         const StreamShape sh = stream_shape(true);
         return hip_status(launch_q4k_stream(g->args, unused, g->workgroups, sh.waves, sh.ring,
                                             (hipStream_t)stream));

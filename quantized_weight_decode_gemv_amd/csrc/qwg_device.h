@@ -43,6 +43,7 @@ __device__ __forceinline__ void load_args(GemvArgs &a, cargs_p pa) {
     a.tiles = pa->tiles;
     a.splits = pa->splits;
     a.wg_begin = pa->wg_begin;
+    a.layout = pa->layout;
 }
 
 // Asynchronous 16-byte global -> LDS copy (LDS DMA) of every active lane: lane
@@ -55,8 +56,16 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds) {
 }
 
 // The same with a 64-bit scalar base and a 32-bit per-lane byte offset.
+// The base must be wavefront-uniform; readfirstlane states that to the compiler
+// (it folds away where uniformity is already known).
 __device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"{m0}"(lds), "v"(voff), "s"(sbase)
+    // (readfirstlane returns int: widen through uint32_t, never by sign extension)
+    const uint64_t p = (uint64_t)(uintptr_t)sbase;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const uint64_t u = (uint64_t)lo | (uint64_t)hi << 32;
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"{m0}"(lds), "v"(voff),
+                 "s"((const void *)(uintptr_t)u)
                  : "memory");
 }
 

@@ -30,7 +30,16 @@ struct GemvArgs {
     int tiles;     // ceil(n_out / 64)
     int splits;    // 1..nb
     int wg_begin;  // first workgroup of this problem in a grouped launch
+    int layout;    // kLayoutRows or kLayoutTiles (stream engine only)
 };
+
+// Weight layouts. Rows: row r is n_in/256 consecutive blocks, rows contiguous.
+// Tiles (Q4_K): the same blocks ordered tile-major: for each 64-row tile, for
+// each block column b, the 64 rows' block b back to back (9216 bytes); rows
+// past n_out in the last tile are zero blocks. Block (r, b) sits at byte
+// ((r/64)*nb + b)*9216 + (r%64)*144.
+constexpr int kLayoutRows = 0;
+constexpr int kLayoutTiles = 1;
 
 // A grouped launch: problems[map[blockIdx.x]] is the problem of each
 // workgroup (both arrays in device memory).
@@ -46,6 +55,8 @@ constexpr int kQ4kWavesLarge = 16;
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_q4k_dequant(const uint8_t *src, float *dst, int64_t nblocks, hipStream_t s);
+// Row-major Q4_K weights -> tile layout (dst: tiles*64*nb*144 bytes).
+hipError_t launch_q4k_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, hipStream_t s);
 hipError_t launch_iq3_dequant(const uint8_t *src, const float *grid, float *dst,
                               int64_t nblocks, hipStream_t s);
 hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, int waves, hipStream_t s);

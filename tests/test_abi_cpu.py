@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
                  "qwg_gemm_q4k", "qwg_strerror", "qwg_row_bytes", "qwg_version",
                  "qwg_plan_splits", "qwg_gemm_q4k_ex", "qwg_gemv_iq3_ex", "qwg_group_create_q4k",
                  "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
-                 "qwg_group_destroy"):
+                 "qwg_group_destroy", "qwg_tiled_bytes", "qwg_pack_q4k_tiles",
+                 "qwg_gemv_q4k_tiled", "qwg_group_create_q4k_tiled"):
         assert want in names
 
 
@@ -60,6 +61,14 @@ def test_row_bytes(L):
     assert L.qwg_row_bytes(1, 5632) == 2156
     assert L.qwg_row_bytes(0, 300) == -2
     assert L.qwg_row_bytes(7, 256) == -6
+
+
+def test_tiled_bytes(L):
+    assert L.qwg_tiled_bytes(0, 2048, 2048) == 2048 * 1152
+    assert L.qwg_tiled_bytes(0, 2048, 65) == 128 * 1152      # rows rounded up to whole tiles
+    assert L.qwg_tiled_bytes(0, 5632, 1) == 64 * 3168
+    assert L.qwg_tiled_bytes(1, 2048, 64) == -6
+    assert L.qwg_tiled_bytes(0, 300, 64) == -2
 
 
 def test_plan_splits(L):
@@ -110,6 +119,15 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_dequant_q4k(FAKE + 4, FAKE, 256, None), 3),
     (lambda L: L.qwg_dequant_q4k(FAKE, FAKE + 4, 256, None), 3),
     (lambda L: L.qwg_dequant_iq3(FAKE + 1, FAKE, FAKE, 256, None), 3),
+    # tile layout
+    (lambda L: L.qwg_pack_q4k_tiles(None, FAKE, 256, 1, None), 1),
+    (lambda L: L.qwg_pack_q4k_tiles(FAKE, FAKE, 300, 1, None), 2),
+    (lambda L: L.qwg_pack_q4k_tiles(FAKE + 8, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_pack_q4k_tiles(FAKE, FAKE + 4, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_q4k_tiled(FAKE, FAKE, None, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_q4k_tiled(FAKE, FAKE, FAKE, 256, 0, None), 2),
+    (lambda L: L.qwg_gemv_q4k_tiled(FAKE, FAKE, FAKE + 8, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_q4k_tiled(FAKE, FAKE + 4, FAKE, 256, 1, None), 3),
     # IQ3 with an explicit decomposition
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, None, 256, 1, 4, 1, None), 1),
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 384, 1, 4, 1, None), 2),
@@ -161,6 +179,15 @@ def test_iq3_group_validation_errors(L, desc, status):
     assert L.qwg_group_create_iq3(ok, 1, None, ctypes.byref(out)) == 1
     assert L.qwg_group_create_iq3(ok, 1, FAKE + 4, ctypes.byref(out)) == 3
     assert L.qwg_group_create_iq3(ok, 0, FAKE, ctypes.byref(out)) == 2
+
+
+def test_tiled_group_validation_errors(L):
+    arr = (_Desc * 2)(_Desc(FAKE, FAKE, FAKE, 256, 64), _Desc(FAKE, FAKE, FAKE + 8, 256, 1))
+    out = ctypes.c_void_p(123)
+    assert L.qwg_group_create_q4k_tiled(arr, 2, ctypes.byref(out)) == 3
+    assert out.value is None
+    assert L.qwg_group_create_q4k_tiled(None, 1, ctypes.byref(out)) == 1
+    assert L.qwg_group_create_q4k_tiled(arr, 0, ctypes.byref(out)) == 2
 
 
 def test_group_null_and_count_errors(L):

@@ -548,3 +548,73 @@ def test_iq3_group_stream_sampled_rows():
         rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 16)]))
         yr, sr = oracle.gemv_iq3_rows(w, grid, x, p.n_in, rows)
         assert_bound(host(y)[rows], yr, sr, "iq3 group " + p.name)
+
+
+# ---------------------------------------------------------------- Q4_K tile layout
+
+def _tile_layout(w: np.ndarray, n_in: int) -> np.ndarray:
+    """The tile layout written out: block (r, b) at ((r//64)*nb + b)*9216 + (r%64)*144,
+    rows past n_out as zero blocks."""
+    n_out, nb = w.shape[0], n_in // 256
+    tiles = (n_out + 63) // 64
+    blocks = np.zeros((tiles * 64, nb, 144), np.uint8)
+    blocks[:n_out] = w.reshape(n_out, nb, 144)
+    return blocks.reshape(tiles, 64, nb, 144).transpose(0, 2, 1, 3).reshape(-1)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (64, 512), (65, 768), (300, 2048), (2048, 5632)])
+def test_pack_q4k_tiles_is_the_layout(n_out, n_in):
+    w = synth.q4k_weights(n_out, n_in, 120, n_out)
+    got = host(qwg.pack_q4k_tiles(dev(w), n_in))
+    assert np.array_equal(got, _tile_layout(w, n_in))
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 512), (65, 768), (130, 5632), (2048, 2048),
+                                        (32000, 2048), (4097, 1280)])
+def test_gemv_q4k_tiled(n_out, n_in):
+    w, x = _gemv_q4k_case(n_out, n_in, 121, n_out)
+    wt = qwg.pack_q4k_tiles(dev(w), n_in)
+    xd = dev(x)
+    yr, sr = oracle.gemv_q4k(w, x, n_in, n_out)
+    y = host(qwg.gemv_q4k_tiled(wt, xd, n_out))
+    assert_bound(y, yr, sr, f"tiled {n_out}x{n_in}")
+    assert_bits(host(qwg.gemv_q4k_tiled(wt, xd, n_out)), y, "tiled rerun")
+
+
+def test_q4k_tiled_group_layer_and_integer_exact():
+    probs = synth.config(2)
+    ws = [synth.weights(p) for p in probs]
+    xs = [synth.inputs(p) for p in probs]
+    W = [qwg.pack_q4k_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
+    Y = [torch.full((p.n_out,), float("nan"), device=DEV) for p in probs]
+    g = qwg.Q4kGroup(zip(W, [dev(x) for x in xs], Y), tiled=True)
+    g.run()
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        yr, sr = oracle.gemv_q4k(w, x, p.n_in, p.n_out)
+        assert_bound(host(y), yr, sr, "tiled group " + p.name)
+    g.close()
+    # integer-valued weights and activations: every order of summation is exact
+    n_out, n_in = 129, 5632
+    w = _integer_q4k(n_out, n_in, 122)
+    x = np.random.default_rng(12).integers(-8, 9, n_in).astype(np.float32)
+    yr, _ = oracle.gemv_q4k(w, x, n_in, n_out)
+    y = torch.empty(n_out, device=DEV)
+    g = qwg.Q4kGroup([(qwg.pack_q4k_tiles(dev(w), n_in), dev(x), y)], tiled=True)
+    g.run()
+    assert np.array_equal(host(y).astype(np.float64), yr)
+
+
+def test_q4k_tiled_group_stream_sampled_rows():
+    probs = synth.config(5)
+    rng = np.random.default_rng(8)
+    ws = [synth.weights(p) for p in probs]
+    xs = [synth.inputs(p) for p in probs]
+    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    W = [qwg.pack_q4k_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
+    g = qwg.Q4kGroup(zip(W, [dev(x) for x in xs], Y), tiled=True)
+    for _ in range(3):
+        g.run()
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 16)]))
+        yr, sr = oracle.gemv_q4k_rows(w, x, p.n_in, rows)
+        assert_bound(host(y)[rows], yr, sr, "tiled group " + p.name)
