@@ -8,12 +8,16 @@ head: 155 GEMVs, 582 MB of distinct packed weights (more than the 256 MB
 last-level cache, so every step streams them from HBM). Weights, activations
 and outputs are seeded synthetic data resident in HBM before timing starts.
 
-The headline runs the step as one grouped launch through the C ABI
-(qwg_group_run over the 155 independent GEMVs). Two more schedules of the same
-step are timed and reported beside it: "layered" (the launches a decoder whose
-layers depend on each other would make: per layer q|k|v grouped, o, gate|up
-grouped, down; then the LM head: 89 launches) and "per_call" (155
-qwg_gemv_q4k calls).
+Weights are held in the library's tile-major order (every 64-row tile stored
+block column by block column; qwg_pack_q4k_tiles repacks the row-major tensors
+once, before timing; each 144-byte block is unchanged, and the byte count is the
+same because every shape here is a whole number of tiles). The headline runs the
+step as one grouped launch through the C ABI (qwg_group_run over the 155
+independent GEMVs). Further schedules of the same step are timed and reported
+beside it: "grouped_row_major" (the same launch on the row-major tensors),
+"layered" (the launches a decoder whose layers depend on each other would make:
+per layer q|k|v grouped, o, gate|up grouped, down; then the LM head: 89
+launches) and "per_call" (155 qwg_gemv_q4k_tiled calls).
 
 Reported: value = algorithmic bytes of the step (weights + x + y) / wall time
 per step, in GB/s; the roofline object for the grouped kernel (algorithmic bytes
@@ -36,12 +40,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
                   "quantized_weight_decode_gemv_amd/csrc/qwg_device.h",
                   "quantized_weight_decode_gemv_amd/csrc/qwg_internal.h"]
-# HBM bytes per grouped launch of the stream, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# HBM bytes per grouped launch of the stream (tile layout), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
 # runs of this script, each scaled by the same counter on a plain device copy of known size
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "cf33c3aa40187151480f7bc7a24eaf74fa55739ec122de85ec23c64369cbc809",
-           "fetch_bytes": 686743121, "write_bytes": 1704960}
+TRAFFIC = {"sources_sha256": "7a7f001a5b77cce23a668a5d12da2690f3a4f6ce0afb7f8f01e144b2ab08c7ff",
+           "fetch_bytes": 594966411, "write_bytes": 1704960}
 
 
 def kernel_sources_sha256() -> str:
@@ -62,8 +66,8 @@ def traffic_bytes():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time budget for the oracle baseline")
@@ -118,6 +122,7 @@ def main():
     W = [torch.from_numpy(w).to(dev) for w in host_w]
     X = [torch.from_numpy(x).to(dev) for x in host_x]
     Y = [torch.empty(p.n_out, dtype=torch.float32, device=dev) for p in probs]
+    WT = [qwg.pack_q4k_tiles(w, p.n_in) for p, w in zip(probs, W)]
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
@@ -126,21 +131,23 @@ def main():
     step_bytes = sum(p.algorithmic_bytes for p in probs)
     weight_bytes = sum(p.weight_bytes for p in probs)
 
-    group = qwg.Q4kGroup(zip(W, X, Y))
+    group = qwg.Q4kGroup(zip(WT, X, Y), tiled=True)
+    Y_rows = [torch.empty_like(y) for y in Y]
+    group_rows = qwg.Q4kGroup(zip(W, X, Y_rows))
     layered = []
     i = 0
     while i < len(probs):
         name = probs[i].name.split(".")[-1]
         if name in ("q", "gate"):
             n = 3 if name == "q" else 2
-            layered.append(qwg.Q4kGroup(zip(W[i:i + n], X[i:i + n], Y[i:i + n])))
+            layered.append(qwg.Q4kGroup(zip(WT[i:i + n], X[i:i + n], Y[i:i + n]), tiled=True))
             i += n
         else:
-            layered.append(qwg.Q4kGroup([(W[i], X[i], Y[i])]))
+            layered.append(qwg.Q4kGroup([(WT[i], X[i], Y[i])], tiled=True))
             i += 1
     calls = [(y.data_ptr(), x.data_ptr(), w.data_ptr(), p.n_in, p.n_out)
-             for p, w, x, y in zip(probs, W, X, Y)]
-    gemv = L.qwg_gemv_q4k
+             for p, w, x, y in zip(probs, WT, X, Y)]
+    gemv = L.qwg_gemv_q4k_tiled
 
     def step_grouped():
         group.run(stream)
@@ -153,7 +160,7 @@ def main():
         for yp, xp, wp, n_in, n_out in calls:
             rc = gemv(yp, xp, wp, n_in, n_out, sptr)
             if rc:
-                raise RuntimeError(f"qwg_gemv_q4k failed: {rc}")
+                raise RuntimeError(f"qwg_gemv_q4k_tiled failed: {rc}")
 
     def timed(fn, steps, warmup):
         for _ in range(warmup):
@@ -168,6 +175,7 @@ def main():
     sec = timed(step_grouped, args.steps, args.warmup)
     ms_per_step = 1e3 * sec
     value = step_bytes / sec / 1e9
+    sec_rows = timed(lambda: group_rows.run(stream), args.steps, args.warmup)
     sec_layered = timed(step_layered, max(5, args.steps // 5), 2)
     sec_percall = timed(step_per_call, max(5, args.steps // 5), 2)
 
@@ -205,7 +213,9 @@ def main():
         "config": {
             "workload": "TinyLlama-1.1B Q4_K per-token weight stream, batch 1: 22 layers x "
                         "(q,o 2048x2048; k,v 256x2048; gate,up 5632x2048; down 2048x5632) + "
-                        "LM head 32000x2048 = 155 GEMVs, one grouped launch (qwg_group_run)",
+                        "LM head 32000x2048 = 155 GEMVs, one grouped launch (qwg_group_run), "
+                        "weights in tile-major order",
+            "layout": "tile-major Q4_K (qwg_pack_q4k_tiles, repacked once before timing)",
             "weight_bytes": weight_bytes,
             "algorithmic_bytes_per_step": step_bytes,
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -214,6 +224,7 @@ def main():
             "setup_s": round(setup_s, 1),
             "schedules": {
                 "grouped": sched(sec, 1),
+                "grouped_row_major": sched(sec_rows, 1),
                 "layered": sched(sec_layered, len(layered)),
                 "per_call": sched(sec_percall, len(calls)),
             },
@@ -225,21 +236,21 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_bytes(),
-            "kernel": "q4k_stream_kernel<4,2> (grouped, 155 GEMVs per launch)",
+            "kernel": "q4k_stream_kernel<4,2> (grouped, 155 GEMVs per launch, tile layout)",
             "bytes_per_launch": step_bytes,
             "kernel_us": round(1e3 * kernel_ms, 2),
         },
     }
 
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(probs, host_w, host_x, Y, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(probs, host_w, host_x, (Y, Y_rows), args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(probs, host_w, host_x, Y, budget_s):
+def cpu_baseline(probs, host_w, host_x, outputs, budget_s):
     """The oracle (plain C, fp64 dot, OpenMP over rows) on the host cores over the
     same per-token stream, repeated until the budget is spent; the GPU outputs of
-    the last step are compared with it on the way (sampled rows)."""
+    the last step of each layout are compared with it on the way (sampled rows)."""
     import numpy as np
     import oracle
 
@@ -255,8 +266,9 @@ def cpu_baseline(probs, host_w, host_x, Y, budget_s):
             y, s = oracle.gemv_q4k(w, x, p.n_in, p.n_out)
             if runs == 0:
                 rows = rng.integers(0, p.n_out, 16)
-                g = Y[j].cpu().numpy()[rows].astype(np.float64)
-                worst = max(worst, float(np.max(np.abs(g - y[rows]) / s[rows])))
+                for Y in outputs:
+                    g = Y[j].cpu().numpy()[rows].astype(np.float64)
+                    worst = max(worst, float(np.max(np.abs(g - y[rows]) / s[rows])))
         t_total += time.perf_counter() - t0
         runs += 1
         if runs >= 50:
