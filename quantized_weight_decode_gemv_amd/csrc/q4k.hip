@@ -348,6 +348,14 @@ struct Item {
     int layout;
 };
 
+// First position from k on (k, k + stride, ...) that holds work, or a
+// position >= nitems.
+__device__ __forceinline__ int skip_holes(int k, int stride, int nitems, const GroupArgs &g) {
+    if (g.tile != nullptr)
+        while (k < nitems && ((cu32_p)g.map)[k] == kNoItem) k += stride;
+    return k;
+}
+
 template <int BPS>
 __device__ __forceinline__ void load_item(Item &it, int k, const GroupArgs &g, const GemvArgs &single) {
     if (g.problems == nullptr) {
@@ -367,7 +375,7 @@ __device__ __forceinline__ void load_item(Item &it, int k, const GroupArgs &g, c
         it.row_bytes = pa->row_bytes;
         it.n_out = pa->n_out;
         it.nb = pa->nb;
-        it.row0 = (k - pa->wg_begin) * kTileRows;
+        it.row0 = (g.tile != nullptr ? (int)((cu32_p)g.tile)[k] : k - pa->wg_begin) * kTileRows;
         it.layout = pa->layout;
     }
     it.nst = (it.nb + BPS - 1) / BPS;
@@ -408,7 +416,7 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
     }
     const int64_t xoff = 4 * (64 * G + 4 * (lane - 16));   // bytes, lanes 16..31
 
-    int kc = blockIdx.x;  // item being computed
+    int kc = skip_holes(blockIdx.x, stride, nitems, g);  // item being computed
     if (kc >= nitems) return;
     Item c;
     load_item<BPS>(c, kc, g, single);
@@ -460,7 +468,7 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
         slot_d = slot_d + 1 == R ? 0 : slot_d + 1;
         if (++sd == d.nst) {
             sd = 0;
-            kd += stride;
+            kd = skip_holes(kd + stride, stride, nitems, g);
             if (kd < nitems) {
                 load_item<BPS>(d, kd, g, single);
                 prep_copy();
@@ -510,14 +518,21 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
             for (int w = 1; w < W; ++w) tsum += red[w * 64 + lane];
             if (c.row0 + lane < c.n_out) c.y[c.row0 + lane] = tsum;
         }
-        kc += stride;
+        kc = skip_holes(kc + stride, stride, nitems, g);
         if (kc >= nitems) break;
         load_item<BPS>(c, kc, g, single);
     }
 }
 
+// The SGPR budget keeps seven 4-wavefront workgroups resident per CU: the x
+// operands of a quant chunk take 64 SGPRs, and measured on gfx950 a kernel
+// whose last SGPR is s94 or higher fits only six wavefronts per SIMD (the
+// occupancy query still reports seven, so a grid sized by it would leave a
+// seventh of the workgroups waiting for a slot). A budget of 96 ends at s87;
+// the few spills go to VGPR lanes outside the inner loop.
 template <int W, int R>
-__global__ __launch_bounds__(W * 64) void q4k_stream_kernel(GroupArgs g, GemvArgs single, int nitems) {
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_num_sgpr(96))) void q4k_stream_kernel(
+    GroupArgs g, GemvArgs single, int nitems) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
         case 0: q4k_stream<0, W, R>(g, single, nitems, smem); break;
@@ -579,7 +594,7 @@ hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, int waves, hipStream_t 
 }
 
 template <int W, int R>
-hipError_t launch_stream_wr(const GroupArgs &g, const GemvArgs &single, int nitems, hipStream_t s) {
+int stream_residency(int *cus_out) {
     using C = StreamCfg<W, R>;
     static int per_cu = -1, cus = 0;
     if (per_cu < 0) {
@@ -592,6 +607,15 @@ hipError_t launch_stream_wr(const GroupArgs &g, const GemvArgs &single, int nite
             per_cu = 1;
         if (cus < 1) cus = 256;
     }
+    *cus_out = cus;
+    return per_cu;
+}
+
+template <int W, int R>
+hipError_t launch_stream_wr(const GroupArgs &g, const GemvArgs &single, int nitems, hipStream_t s) {
+    using C = StreamCfg<W, R>;
+    int cus = 0;
+    const int per_cu = stream_residency<W, R>(&cus);
     int grid = per_cu * cus;
     if (grid > nitems) grid = nitems;
     hipLaunchKernelGGL((q4k_stream_kernel<W, R>), dim3((unsigned)grid), dim3(W * 64), C::kLds, s, g,
@@ -609,6 +633,18 @@ hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nit
         case 162: return launch_stream_wr<16, 2>(g, single, nitems, s);
         case 163: return launch_stream_wr<16, 3>(g, single, nitems, s);
         default: return hipErrorInvalidValue;
+    }
+}
+
+int q4k_stream_residency(int waves, int ring, int *cus) {
+    switch (waves * 10 + ring) {
+        case 42: return stream_residency<4, 2>(cus);
+        case 43: return stream_residency<4, 3>(cus);
+        case 82: return stream_residency<8, 2>(cus);
+        case 83: return stream_residency<8, 3>(cus);
+        case 162: return stream_residency<16, 2>(cus);
+        case 163: return stream_residency<16, 3>(cus);
+        default: *cus = 0; return 0;
     }
 }
 

@@ -9,6 +9,7 @@
 #include <vector>
 #include <map>
 #include <mutex>
+#include <queue>
 #include <utility>
 
 #include "../../include/qwg.h"
@@ -273,7 +274,7 @@ int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
     if (rc) return rc;
     if (batch == 1 && a.splits == 1 && use_stream_engine()) {
         const StreamShape sh = stream_shape(false);
-        const GroupArgs none = {nullptr, nullptr};
+        const GroupArgs none = {nullptr, nullptr, nullptr};
         return hip_status(
             launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, (hipStream_t)stream));
     }
@@ -339,7 +340,7 @@ int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, in
     fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
     a.layout = kLayoutTiles;
     const StreamShape sh = stream_shape(false);
-    const GroupArgs none = {nullptr, nullptr};
+    const GroupArgs none = {nullptr, nullptr, nullptr};
     return hip_status(launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, (hipStream_t)stream));
 }
 
@@ -369,7 +370,7 @@ int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, 
         a.partial = ws.partial;
         a.counters = ws.counters;
     }
-    const GroupArgs none = {nullptr, nullptr};
+    const GroupArgs none = {nullptr, nullptr, nullptr};
     return hip_status(
         launch_iq3_stream(none, a, grid, a.tiles * splits, sh, (hipStream_t)stream));
 }
@@ -386,14 +387,91 @@ struct qwg_group {
     int fmt;              // QWG_FMT_Q4K or QWG_FMT_IQ3
     int layout;           // kLayoutRows or kLayoutTiles
     const float *grid;    // IQ3: the grid every member uses
-    void *dev_mem;        // GemvArgs[count] followed by uint32_t map[workgroups]
+    void *dev_mem;        // GemvArgs[count], uint32_t map[positions] (and tile[positions])
     GroupArgs args;
     int count;
-    int workgroups;
+    int workgroups;       // 64-row tiles of one run
+    int positions;        // work-list length of a launch (tiles, plus holes of a schedule)
     int max_nb;
 };
 
 namespace {
+
+// Static schedule of a grouped Q4_K stream launch. Resident workgroup b walks
+// positions b, b + G, b + 2G, ... (G = resident workgroups of the launch).
+// Measured on MI355X, workgroups that share a CU do not progress at the same
+// rate: wavefronts issue oldest first, so the workgroup dispatched first to a
+// CU streams its tiles about three times as fast as the seventh, and equal
+// shares leave the young ones running alone at the end with too few bytes in
+// flight. Workgroup b is the (b / CUs)-th to arrive on its CU, so its share is
+// weighted by a ramp from 1 + skew (first) to 1 - skew (last); tiles, longest
+// rows first, go one by one to the workgroup furthest below its weighted share.
+// Positions past the end of a workgroup's list hold kNoItem. Measured on the
+// 155-GEMV TinyLlama stream: skew 0 (plain longest-first balance) 106.4 us,
+// 0.3 104.3, 0.5 102.3, 0.7 101.7, 0.85 101.9; equal round-robin shares 104.8.
+// QWG_STREAM_SKEW overrides it (tuning experiments).
+constexpr double kAgeSkew = 0.7;
+
+double age_skew() {
+    static const double v = [] {
+        const char *e = getenv("QWG_STREAM_SKEW");
+        const double d = e ? atof(e) : kAgeSkew;
+        return d < 0.0 ? 0.0 : (d > 0.95 ? 0.95 : d);
+    }();
+    return v;
+}
+
+void stream_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> &order,
+                     int64_t total, const StreamShape &sh, std::vector<uint32_t> &map,
+                     std::vector<uint32_t> &tile) {
+    int cus = 0;
+    const int per_cu = q4k_stream_residency(sh.waves, sh.ring, &cus);
+    const int64_t grid = (int64_t)per_cu * cus;
+    if (grid < 1 || total <= grid) {
+        // one item (or none) per workgroup: the sorted list itself
+        map.resize((size_t)total);
+        tile.resize((size_t)total);
+        size_t k = 0;
+        for (int i : order)
+            for (int t = 0; t < probs[i].tiles; ++t, ++k) {
+                map[k] = (uint32_t)i;
+                tile[k] = (uint32_t)t;
+            }
+        return;
+    }
+    const double skew = per_cu > 1 ? age_skew() : 0.0;
+    std::vector<double> target((size_t)grid);
+    double wsum = 0.0;
+    for (int64_t b = 0; b < grid; ++b) {
+        const int rank = (int)(b / cus);
+        target[b] = 1.0 + skew * (double)(per_cu - 1 - 2 * rank) / (double)(per_cu - 1 > 0 ? per_cu - 1 : 1);
+        wsum += target[b];
+    }
+    double work = 0.0;
+    for (int i : order) work += (double)probs[i].tiles * probs[i].nb;
+    for (double &t : target) t *= work / wsum;
+    std::priority_queue<std::pair<double, int64_t>> deficit;
+    for (int64_t b = 0; b < grid; ++b) deficit.push({target[b], -b});
+    std::vector<double> load((size_t)grid, 0.0);
+    std::vector<std::vector<std::pair<uint32_t, uint32_t>>> lists((size_t)grid);
+    size_t longest = 0;
+    for (int i : order)
+        for (int t = 0; t < probs[i].tiles; ++t) {
+            const int64_t b = -deficit.top().second;
+            deficit.pop();
+            lists[b].push_back({(uint32_t)i, (uint32_t)t});
+            load[b] += probs[i].nb;
+            deficit.push({target[b] - load[b], -b});
+            longest = std::max(longest, lists[b].size());
+        }
+    map.assign((size_t)grid * longest, kNoItem);
+    tile.assign((size_t)grid * longest, 0u);
+    for (int64_t b = 0; b < grid; ++b)
+        for (size_t j = 0; j < lists[b].size(); ++j) {
+            map[j * grid + b] = lists[b][j].first;
+            tile[j * grid + b] = lists[b][j].second;
+        }
+}
 
 int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, const float *grid,
                  qwg_group **out) {
@@ -415,28 +493,42 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
         if (probs[i].nb > max_nb) max_nb = probs[i].nb;
     }
     if (total > (int64_t)1 << 30) return QWG_ERR_SHAPE;
-    // Workgroups of the longest rows first, so that short ones fill the tail.
+    // Work items of the longest rows first, so that short ones fill the tail.
     std::vector<int> order((size_t)count);
     for (int i = 0; i < count; ++i) order[i] = i;
     std::stable_sort(order.begin(), order.end(),
                      [&](int a, int b) { return probs[a].nb > probs[b].nb; });
-    std::vector<uint32_t> map((size_t)total);
     int64_t wg = 0;
     for (int i : order) {
         probs[i].wg_begin = (int)wg;
-        for (int t = 0; t < probs[i].tiles; ++t) map[wg++] = (uint32_t)i;
+        wg += probs[i].tiles;
     }
+    std::vector<uint32_t> map, tile;
+    const bool stream = !iq3 && (layout == kLayoutTiles || use_stream_engine());
+    if (stream) {
+        stream_schedule(probs, order, total, stream_shape(true), map, tile);
+    } else {
+        map.resize((size_t)total);
+        for (int i : order)
+            for (int t = 0; t < probs[i].tiles; ++t) map[(size_t)probs[i].wg_begin + t] = (uint32_t)i;
+    }
+    const int64_t positions = (int64_t)map.size();
+    if (positions > (int64_t)1 << 30) return QWG_ERR_SHAPE;
     const size_t pbytes = sizeof(GemvArgs) * (size_t)count;
-    const size_t mbytes = sizeof(uint32_t) * (size_t)total;
+    const size_t mbytes = sizeof(uint32_t) * (size_t)positions;
+    const size_t tbytes = tile.empty() ? 0 : mbytes;
     qwg_group *g = new (std::nothrow) qwg_group();
     if (!g) return QWG_ERR_HIP;
-    if (hipGetDevice(&g->device) != hipSuccess || hipMalloc(&g->dev_mem, pbytes + mbytes) != hipSuccess) {
+    if (hipGetDevice(&g->device) != hipSuccess ||
+        hipMalloc(&g->dev_mem, pbytes + mbytes + tbytes) != hipSuccess) {
         delete g;
         return QWG_ERR_HIP;
     }
-    if (hipMemcpy(g->dev_mem, probs.data(), pbytes, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy((uint8_t *)g->dev_mem + pbytes, map.data(), mbytes, hipMemcpyHostToDevice) !=
-            hipSuccess) {
+    uint8_t *base = (uint8_t *)g->dev_mem;
+    if (hipMemcpy(base, probs.data(), pbytes, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(base + pbytes, map.data(), mbytes, hipMemcpyHostToDevice) != hipSuccess ||
+        (tbytes && hipMemcpy(base + pbytes + mbytes, tile.data(), tbytes, hipMemcpyHostToDevice) !=
+                       hipSuccess)) {
         (void)hipFree(g->dev_mem);
         delete g;
         return QWG_ERR_HIP;
@@ -445,9 +537,11 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     g->layout = layout;
     g->grid = grid;
     g->args.problems = (const GemvArgs *)g->dev_mem;
-    g->args.map = (const uint32_t *)((uint8_t *)g->dev_mem + pbytes);
+    g->args.map = (const uint32_t *)(base + pbytes);
+    g->args.tile = tbytes ? (const uint32_t *)(base + pbytes + mbytes) : nullptr;
     g->count = count;
     g->workgroups = (int)total;
+    g->positions = (int)positions;
     g->max_nb = max_nb;
     *out = g;
     return QWG_OK;
@@ -487,7 +581,7 @@ int qwg_group_run(const qwg_group *g, void *stream) {
                                             iq3_shape(true, 0), (hipStream_t)stream));
     if (use_stream_engine() || g->layout == kLayoutTiles) {
         const StreamShape sh = stream_shape(true);
-        return hip_status(launch_q4k_stream(g->args, unused, g->workgroups, sh.waves, sh.ring,
+        return hip_status(launch_q4k_stream(g->args, unused, g->positions, sh.waves, sh.ring,
                                             (hipStream_t)stream));
     }
     return hip_status(launch_q4k_group(g->args, g->workgroups, g->max_nb, (hipStream_t)stream));

@@ -41,12 +41,17 @@ struct GemvArgs {
 constexpr int kLayoutRows = 0;
 constexpr int kLayoutTiles = 1;
 
-// A grouped launch: problems[map[blockIdx.x]] is the problem of each
-// workgroup (both arrays in device memory).
+// A grouped launch: problems[map[k]] is the problem of work item k (arrays in
+// device memory). Without `tile`, the items of problem p are consecutive from
+// problems[p].wg_begin and item k is tile k - wg_begin. With `tile` (the Q4_K
+// stream engine's schedule), item k is tile tile[k] of problem map[k], and
+// map[k] == kNoItem marks a position with no work.
 struct GroupArgs {
     const GemvArgs *problems;
     const uint32_t *map;
+    const uint32_t *tile;
 };
+constexpr uint32_t kNoItem = 0xFFFFFFFFu;
 
 // Wavefronts per workgroup of the Q4_K GEMV (4, 8 or 16: one, two or four
 // super-blocks of a 64-row tile per pipeline stage).
@@ -65,6 +70,10 @@ hipError_t launch_q4k_group(const GroupArgs &g, int total_workgroups, int max_nb
 // != nullptr) or of `single`; waves in {4, 8, 16}, ring stages in {2, 3, 4}.
 hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nitems, int waves,
                              int ring, hipStream_t s);
+// Resident workgroups per CU of that stream variant and the number of CUs
+// (the launch grid is their product, capped by the item count); 0 if the
+// variant does not exist.
+int q4k_stream_residency(int waves, int ring, int *cus);
 
 // IQ3 stream engine shape: wavefronts per workgroup (4, 8, 16) and LDS ring
 // stages (2, 3; 4 with 4 wavefronts).

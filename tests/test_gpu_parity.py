@@ -618,3 +618,33 @@ def test_q4k_tiled_group_stream_sampled_rows():
         rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 16)]))
         yr, sr = oracle.gemv_q4k_rows(w, x, p.n_in, rows)
         assert_bound(host(y)[rows], yr, sr, "tiled group " + p.name)
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_q4k_group_many_items_repeat_runs(tiled):
+    # Many more items than resident workgroups, one-stage items (n_in = 256)
+    # mixed with 22-block ones, ragged row counts. Each run uses new
+    # activations and NaN-filled outputs, so a skipped or repeated item shows
+    # up as stale or NaN rows.
+    shapes = [(64 * 8000 + 5, 256), (64 * 300, 5632), (64 * 700 - 3, 2048)]
+    ws = [synth.q4k_weights(n_out, n_in, 123, i) for i, (n_out, n_in) in enumerate(shapes)]
+    W = [qwg.pack_q4k_tiles(dev(w), n_in) if tiled else dev(w) for w, (_, n_in) in zip(ws, shapes)]
+    X = [torch.empty(n_in, device=DEV) for _, n_in in shapes]
+    Y = [torch.empty(n_out, device=DEV) for n_out, _ in shapes]
+    g = qwg.Q4kGroup(zip(W, X, Y), tiled=tiled)
+    assert g.workgroups > 4 * 2048
+    rng = np.random.default_rng(13)
+    for run in range(4):
+        xs = [synth.activations(n_in, 123, 10 * run + i) for i, (_, n_in) in enumerate(shapes)]
+        for xd, x in zip(X, xs):
+            xd.copy_(torch.from_numpy(x))
+        for y in Y:
+            y.fill_(float("nan"))
+        g.run()
+        for (n_out, n_in), w, x, y in zip(shapes, ws, xs, Y):
+            yh = host(y)
+            assert not np.isnan(yh).any(), f"run {run}: rows left unwritten"
+            rows = np.unique(np.concatenate([[0, n_out - 1], rng.integers(0, n_out, 24)]))
+            yr, sr = oracle.gemv_q4k_rows(w, x, n_in, rows)
+            assert_bound(yh[rows], yr, sr, f"run {run} {n_out}x{n_in}")
+    g.close()
