@@ -44,8 +44,8 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
 # runs of this script, each scaled by the same counter on a plain device copy of known size
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "7a7f001a5b77cce23a668a5d12da2690f3a4f6ce0afb7f8f01e144b2ab08c7ff",
-           "fetch_bytes": 594966411, "write_bytes": 1704960}
+TRAFFIC = {"sources_sha256": "011d9ef26361554b8b8d1ba8cddfede2632e8c893031bff871d23b94e2f79e8d",
+           "fetch_bytes": 595971167, "write_bytes": 1704960}
 
 
 def kernel_sources_sha256() -> str:
@@ -220,7 +220,7 @@ def main():
             "algorithmic_bytes_per_step": step_bytes,
             "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
             "tokens_per_s": round(1e3 / ms_per_step, 1),
-            "workgroups_per_launch": group.workgroups,
+            "tiles_per_launch": group.workgroups,
             "setup_s": round(setup_s, 1),
             "schedules": {
                 "grouped": sched(sec, 1),
