@@ -25,6 +25,12 @@ per step, in GB/s; the roofline object for the grouped kernel (algorithmic bytes
 oracle's throughput on the host cores (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --workload iq3_stream|lm_head [--steps K] [--warmup W]
+The second form measures the other hot-path rows on their own (one JSON line each, for the
+record and for profiling): "iq3_stream" = the same 155 GEMV shapes in the IQ3 container as one
+grouped launch; "lm_head" = the 32000x2048 Q4_K LM head at batch 1..8 (qwg_gemv_q4k,
+qwg_gemv_q4k_tiled, qwg_gemm_q4k), cycling over enough weight copies that every launch streams
+from HBM rather than the last-level cache.
 """
 from __future__ import annotations
 
@@ -73,6 +79,8 @@ def parse():
                     help="minimum CPU time budget for the oracle baseline")
     ap.add_argument("--print-kernel-hash", action="store_true",
                     help="print the hash of the kernel sources the traffic figure is tied to")
+    ap.add_argument("--workload", default="q4k_stream", choices=["q4k_stream", "iq3_stream", "lm_head"],
+                    help="q4k_stream: the headline (default); the others: see the module docstring")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 10 plain device-to-device copies of MIB "
                          "MiB (reference for scaling hardware traffic counters) and exit")
@@ -104,6 +112,12 @@ def main():
         print("bench.py measures one GPU: the GEMV path has no multi-GPU mode in this build "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "iq3_stream":
+        bench_iq3_stream(args)
+        return
+    if args.workload == "lm_head":
+        bench_lm_head(args)
+        return
 
     import numpy as np
     import torch
@@ -245,6 +259,101 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(probs, host_w, host_x, (Y, Y_rows), args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _event_us(fn, stream, steps, warmup):
+    """Average time of fn() over `steps` back-to-back calls, from HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / steps
+
+
+def bench_iq3_stream(args):
+    import torch
+    import quantized_weight_decode_gemv_amd as qwg
+    from quantized_weight_decode_gemv_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    probs = synth.config(6)
+    grid = torch.from_numpy(synth.iq3_grid()).to(dev)
+    W = [torch.from_numpy(synth.weights(p)).to(dev) for p in probs]
+    X = [torch.from_numpy(synth.inputs(p)).to(dev) for p in probs]
+    Y = [torch.empty(p.n_out, dtype=torch.float32, device=dev) for p in probs]
+    group = qwg.Iq3Group(zip(W, X, Y), grid)
+    stream = torch.cuda.current_stream(dev)
+    step_bytes = sum(p.algorithmic_bytes for p in probs)
+    us = _event_us(lambda: group.run(stream), stream, args.steps, args.warmup)
+    gbs = step_bytes / us / 1e3
+    print(json.dumps({
+        "metric": "effective HBM GB/s, IQ3 GEMV stream, batch 1", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 4), "higher_is_better": True, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "TinyLlama-1.1B-shaped per-token stream in the 98-byte IQ3 "
+                               "container: 155 GEMVs, one grouped launch (qwg_group_run)",
+                   "algorithmic_bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "iq3_stream_kernel (grouped)",
+                     "kernel_us": round(us, 2)}}), flush=True)
+
+
+def bench_lm_head(args):
+    import torch
+    import quantized_weight_decode_gemv_amd as qwg
+    from quantized_weight_decode_gemv_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    p = synth.config(3)[0]
+    w = torch.from_numpy(synth.weights(p)).to(dev)
+    copies = 16  # 16 x 36.9 MB: more than the last-level cache
+    wr = w.reshape(1, -1).repeat(copies, 1)
+    wt = torch.stack([qwg.pack_q4k_tiles(w, p.n_in)] * copies)
+    xs = torch.from_numpy(synth.activations(p.n_in, 3, 1, batch=8)).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    wbytes = p.weight_bytes
+    out = {}
+    i = [0]
+
+    def cycle(fn):
+        def run():
+            fn(i[0] % copies)
+            i[0] += 1
+        return run
+
+    for batch in range(1, 9):
+        x = xs[:batch].contiguous()
+        y = torch.empty(batch, p.n_out, device=dev)
+        if batch == 1:
+            us = _event_us(cycle(lambda k: qwg.gemv_q4k(wr[k].view(p.n_out, -1), x[0], out=y[0])),
+                           stream, args.steps, args.warmup)
+            ust = _event_us(cycle(lambda k: qwg.gemv_q4k_tiled(wt[k], x[0], p.n_out, out=y[0])),
+                            stream, args.steps, args.warmup)
+            out["b1_tiled_us"] = round(ust, 2)
+        else:
+            us = _event_us(cycle(lambda k: qwg.gemm_q4k(wr[k].view(p.n_out, -1), x, out=y)),
+                           stream, args.steps, args.warmup)
+        nbytes = wbytes + 4 * batch * (p.n_in + p.n_out)
+        out[f"b{batch}_us"] = round(us, 2)
+        out[f"b{batch}_GBs"] = round(nbytes / us / 1e3, 1)
+    b8 = out["b8_us"]
+    flops8 = 2.0 * 8 * p.n_in * p.n_out
+    print(json.dumps({
+        "metric": "LM head 32000x2048 Q4_K time per call, batch 1..8", "value": b8, "unit": "us (batch 8)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "Q4_K LM head 2048->32000, cold weights (16 copies cycled)", **out,
+                   "b8_TFLOPs": round(flops8 / b8 / 1e6, 2)},
+    }), flush=True)
 
 
 def cpu_baseline(probs, host_w, host_x, outputs, budget_s):

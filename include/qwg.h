@@ -144,13 +144,18 @@ int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, 
  * every weight is decoded once and applied to all `batch` activation rows.
  * x: [batch, n_in] fp32 row-major, 16-byte aligned. y: [batch, n_out] fp32
  * row-major, 4-byte aligned. batch == 1 computes the same as qwg_gemv_q4k.
+ * batch >= 2 runs on the matrix cores (bf16 MFMA with the activations split
+ * exactly into three bf16 parts and the quants entered as exact integers; only
+ * the fp32 accumulation rounds), within the same bound.
  */
 int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
                  int batch, void *stream);
 
 /*
  * qwg_gemm_q4k with an explicit work decomposition (tuning and testing):
- * `waves` wavefronts per 64-row tile (4, 8 or 16; 0 = automatic) and `splits`
+ * `waves` selects the engine: 4, 8 or 16 wavefronts per 64-row tile on the
+ * vector ALUs, 1 = the matrix-core engine (batch >= 2 only; 4 wavefronts per
+ * tile), 0 = automatic (matrix cores for batch >= 2); `splits`
  * workgroups sharing each tile's n_in sum (1..n_in/256; 0 = automatic). The
  * result satisfies the same bound for every choice; the summation order (so
  * the rounding) depends on it. Returns QWG_ERR_SHAPE for an unsupported

@@ -22,6 +22,8 @@ ARCH = os.environ.get("QWG_ARCH", "gfx950")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # matrix-core results in ordinary VGPRs (no copies out of AGPRs)
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
 
 

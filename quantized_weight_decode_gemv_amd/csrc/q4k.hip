@@ -302,6 +302,246 @@ __global__ __launch_bounds__(W * 64) void q4k_gemv_kernel(GemvArgs a) {
     q4k_dispatch<NB, W>(a, smem, tile, blockIdx.x - tile * a.splits);
 }
 
+// ------------------------------------------------------------------ batched GEMM on matrix cores
+//
+// For 2 <= batch <= 8 the product is a dense contraction: per 32-weight
+// sub-block, P[b][r] = sum_k x[b][k] q[r][k] for every batch row b and weight
+// row r, then y[b][r] += d*sc * P - dmin*mn * sum_k x[b][k]. The sums go to
+// v_mfma_f32_16x16x32_bf16 exactly:
+//  * weights enter as bf16(16 + q) = 0x4180 | q << 3 (a mask and an OR per
+//    pair), so the MFMA forms sum (16 + q) x and the 16*sum(x) is taken off in
+//    the scale step: y += d*sc * C - (16*d*sc + dmin*mn) * S;
+//  * x enters as three bf16 parts x = hi + mid + lo, each the top 16 bits of
+//    the remainder (exact for normal fp32), accumulated into the same fp32 C;
+//  * S = sum x over the sub-block comes from the same MFMA with all-ones weights.
+// Every product (4-bit integer times 8-bit significand) is exact; only the fp32
+// accumulation rounds, as in the scalar path.
+//
+// Operand layout of the 16x16x32 instruction (measured): lane l holds A[l%16][k]
+// and B[k][l%16] for k = 8*(l/16) .. 8*(l/16)+7, and C[4*(l/16)+i][l%16].
+// Here A = x: row m of A is batch m%8 of sub-block 2G (m < 8) or 2G+1 (m >= 8);
+// B = the weights of 16 tile rows (column n = row). Wavefront G of a 4-wavefront
+// workgroup computes quant chunk G (sub-blocks 2G, 2G+1) of every super-block
+// for all 64 rows of the tile (4 groups of 16): C1 = A B(2G), C2 = A B(2G+1);
+// lanes 0-31 keep C1's rows 0-7, lanes 32-63 C2's rows 8-15, so each lane ends
+// with one weight row, one sub-block and four batch rows.
+//
+// A stage holds one super-block column: the 64 rows' blocks (9216 B, copied as
+// in the tiled engine) and, per wavefront, its 64 activations of each of the 8
+// batch rows (2 KB, 16-byte granule of (batch b, k/4 = c) at slot
+// 16*(c%8) + 8*(c/8) + b, so that the 16 lanes of a k-group read 16 distinct
+// bank quads). Batch rows past `batch` copy row 0 and are zeroed in A. R stages
+// form a ring, R - 1 of them in flight while one is computed (a workgroup does
+// only a few stages, so the copies, not the math, set its pace).
+constexpr int kXSlice = 2048;
+constexpr int kMfmaStage = kStageBytes + 4 * kXSlice;   // 17408
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// bf16 from the top halves of two fp32 bit patterns: (lo >> 16) | (hi & 0xFFFF0000).
+__device__ __forceinline__ uint32_t bf16_pack(uint32_t lo, uint32_t hi) {
+    return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
+// Three-part split of 8 activations into A fragments (slot order 0,2,1,3,4,6,5,7,
+// matching q4k_bf16_quants).
+__device__ __forceinline__ void split_x(const float (&v)[8], bool live, u32x4_t &a_hi,
+                                        u32x4_t &a_mid, u32x4_t &a_lo) {
+    uint32_t h[8], m[8], l[8];
+    const uint32_t top = opaque(0xFFFF0000u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x = live ? v[i] : 0.0f;
+        h[i] = __builtin_bit_cast(uint32_t, x) & top;
+        const float r = x - __builtin_bit_cast(float, h[i]);
+        m[i] = __builtin_bit_cast(uint32_t, r) & top;
+        l[i] = __builtin_bit_cast(uint32_t, r - __builtin_bit_cast(float, m[i])) & top;
+    }
+    constexpr int ord[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a_hi[i] = bf16_pack(h[ord[2 * i]], h[ord[2 * i + 1]]);
+        a_mid[i] = bf16_pack(m[ord[2 * i]], m[ord[2 * i + 1]]);
+        a_lo[i] = bf16_pack(l[ord[2 * i]], l[ord[2 * i + 1]]);
+    }
+}
+
+// B fragments of 8 quant bytes e0..e7 (one k-group of a row): low nibbles
+// (sub-block 2G) and high nibbles (2G+1) as bf16(16 + q), in slot order
+// (e0,e2), (e1,e3), (e4,e6), (e5,e7).
+__device__ __forceinline__ void q4k_bf16_quants(uint2 e, uint32_t mask, uint32_t bias,
+                                                u32x4_t &b_lo, u32x4_t &b_hi) {
+    const uint32_t d[2] = {e.x, e.y};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        b_lo[2 * i] = ((d[i] << 3) & mask) | bias;
+        b_lo[2 * i + 1] = ((d[i] >> 5) & mask) | bias;
+        b_hi[2 * i] = ((d[i] >> 1) & mask) | bias;
+        b_hi[2 * i + 1] = ((d[i] >> 9) & mask) | bias;
+    }
+}
+
+// Wait until this wavefront's copies of a stage have landed while the copies of
+// `newer` later stages (five instructions each) may still be in flight.
+__device__ __forceinline__ void wait_stage_copies(int newer) {
+    switch (__builtin_amdgcn_readfirstlane(newer)) {
+        case 1: wait_vmcnt<5>(); break;
+        case 2: wait_vmcnt<10>(); break;
+        case 3: wait_vmcnt<15>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
+template <int G, int NB, int R>
+__device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, int tile, int split) {
+    static_assert(R >= 2 && R <= 4, "ring of two to four stages");
+    const int lane = threadIdx.x & 63;
+    const int kb0 = (int)((int64_t)split * a.nb / a.splits);
+    const int kb1 = (int)((int64_t)(split + 1) * a.nb / a.splits);
+    const int nst = kb1 - kb0;
+    const int row0 = tile * kTileRows;
+
+    // Copy lanes: weights as in the tiled engine (rows 16G..16G+15, rows past
+    // n_out re-read the last row); activations: slots 64t + lane.
+    int64_t goff[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int k = (i < 2 || lane < 16) ? 64 * i + lane : 128;
+        const int r = 16 * G + k / 9;
+        goff[i] = (int64_t)min(row0 + r, a.n_out - 1) * a.row_bytes + 16 * (k % 9);
+    }
+    int64_t xoff[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int sl = 64 * t + lane;
+        const int bt = sl & 7;
+        const int c = 8 * ((sl >> 3) & 1) + (sl >> 4);
+        xoff[t] = (int64_t)(bt < NB ? bt : 0) * a.n_in + 64 * G + 4 * c;
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const uint32_t wdst = lds0 + 2304 * G;
+    const uint32_t xdst = lds0 + kStageBytes + kXSlice * G;
+    auto issue = [&](int s) {
+        const int b = kb0 + s;
+        const uint32_t off = (uint32_t)(s % R) * kMfmaStage;
+        const uint8_t *wb = a.w + (int64_t)b * kQ4kBytes;
+        dma16(wb + goff[0], wdst + off);
+        dma16(wb + goff[1], wdst + off + 1024);
+        if (lane < 16) dma16(wb + goff[2], wdst + off + 2048);
+        const float *xb = a.x + (int64_t)kQK * b;
+        dma16(xb + xoff[0], xdst + off);
+        dma16(xb + xoff[1], xdst + off + 1024);
+    };
+
+    // A-operand role of this lane and its activation slots
+    const int am = lane & 15;          // A row: batch am%8, sub-block 2G + am/8
+    const int kg = lane >> 4;          // k-group: k = 8kg .. 8kg+7
+    const bool alive = (am & 7) < NB;
+    const uint32_t xslot0 = 16u * (2 * kg) + 8u * (am >> 3) + (am & 7);
+    // C role: weight row n of each 16-row group, sub-block parity, batch rows 4(kg&1)+i
+    const int n = lane & 15;
+    const bool upper = lane >= 32;
+
+    const uint32_t mask = opaque(0x00780078u);
+    const uint32_t bias = opaque(0x41804180u);
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t acc[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[g] = zero4;
+
+    for (int s = 0; s < R - 1 && s < nst; ++s) issue(s);
+    for (int s = 0; s < nst; ++s) {
+        if (s + R - 1 < nst) issue(s + R - 1);   // into the slot computed in step s - 1
+        wait_stage_copies(min(R - 1, nst - 1 - s));
+        lds_barrier();
+        const uint8_t *stage = smem + (s % R) * kMfmaStage;
+        const float *xs = (const float *)(stage + kStageBytes + kXSlice * G);
+        float xv[8];
+        const float4 x0 = *(const float4 *)(xs + 4 * xslot0);
+        const float4 x1 = *(const float4 *)(xs + 4 * (xslot0 + 16));
+        xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
+        xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
+        u32x4_t ah, am_, al;
+        split_x(xv, alive, ah, am_, al);
+        f32x4_t sx = mfma_bf16(ah, ones, zero4);
+        sx = mfma_bf16(am_, ones, sx);
+        sx = mfma_bf16(al, ones, sx);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint8_t *rowp = stage + (16 * g + n) * kQ4kBytes;
+            const uint2 e = *(const uint2 *)(rowp + 16 + 32 * G + 8 * kg);
+            u32x4_t b_lo, b_hi;
+            q4k_bf16_quants(e, mask, bias, b_lo, b_hi);
+            f32x4_t c1 = mfma_bf16(ah, b_lo, zero4);
+            c1 = mfma_bf16(am_, b_lo, c1);
+            c1 = mfma_bf16(al, b_lo, c1);
+            f32x4_t c2 = mfma_bf16(ah, b_hi, zero4);
+            c2 = mfma_bf16(am_, b_hi, c2);
+            c2 = mfma_bf16(al, b_hi, c2);
+            const uint4 h = *(const uint4 *)rowp;
+            uint32_t sc0, sc1, mn0, mn1;
+            q4k_scales<G>(h, sc0, sc1, mn0, mn1);
+            const float d = h2f_lo(h.x);
+            const float dmin = h2f_hi(h.x);
+            const float dsc = d * (float)(upper ? sc1 : sc0);
+            const float off = __builtin_fmaf(dmin, (float)(upper ? mn1 : mn0), 16.0f * dsc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float c = upper ? c2[i] : c1[i];
+                float v = __builtin_fmaf(dsc, c, acc[g][i]);
+                acc[g][i] = __builtin_fmaf(-off, sx[i], v);
+            }
+        }
+        lds_barrier();  // slot s % R may be overwritten
+    }
+
+    // Sub-blocks 2G and 2G+1 (lanes l and l^32), then the four wavefronts in
+    // order through LDS (overlaying stage 0, idle after the last barrier).
+    float *red = (float *)smem;  // [wave][batch 8][row 64]
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = acc[g][i] + __shfl_xor(acc[g][i], 32);
+            const int bt = 4 * (kg & 1) + i;
+            if (!upper && bt < NB) red[(G * 8 + bt) * 64 + 16 * g + n] = v;
+        }
+    }
+    lds_barrier();
+    if (G == 0) {
+        float total[NB];
+#pragma unroll
+        for (int bt = 0; bt < NB; ++bt) {
+            float t = red[bt * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) t += red[(w * 8 + bt) * 64 + lane];
+            total[bt] = t;
+        }
+        tile_epilogue<NB>(a, tile, split, total);
+    }
+}
+
+template <int NB, int R>
+__global__ __launch_bounds__(256) void q4k_mfma_kernel(GemvArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tile = blockIdx.x / a.splits;
+    const int split = blockIdx.x - tile * a.splits;
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+        case 0: q4k_mfma_tile<0, NB, R>(a, smem, tile, split); break;
+        case 1: q4k_mfma_tile<1, NB, R>(a, smem, tile, split); break;
+        case 2: q4k_mfma_tile<2, NB, R>(a, smem, tile, split); break;
+        default: q4k_mfma_tile<3, NB, R>(a, smem, tile, split); break;
+    }
+}
+
 // Grouped launch (one workgroup per item): each workgroup reads its problem
 // index and descriptor with scalar loads, then runs the same tile pipeline.
 
@@ -632,6 +872,32 @@ hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nit
         case 83: return launch_stream_wr<8, 3>(g, single, nitems, s);
         case 162: return launch_stream_wr<16, 2>(g, single, nitems, s);
         case 163: return launch_stream_wr<16, 3>(g, single, nitems, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int R>
+hipError_t launch_mfma_r(const GemvArgs &a, int batch, hipStream_t s) {
+    const size_t lds = R * (size_t)kMfmaStage;
+    const dim3 grid((unsigned)(a.tiles * a.splits)), block(256);
+    switch (batch) {
+        case 2: hipLaunchKernelGGL((q4k_mfma_kernel<2, R>), grid, block, lds, s, a); break;
+        case 3: hipLaunchKernelGGL((q4k_mfma_kernel<3, R>), grid, block, lds, s, a); break;
+        case 4: hipLaunchKernelGGL((q4k_mfma_kernel<4, R>), grid, block, lds, s, a); break;
+        case 5: hipLaunchKernelGGL((q4k_mfma_kernel<5, R>), grid, block, lds, s, a); break;
+        case 6: hipLaunchKernelGGL((q4k_mfma_kernel<6, R>), grid, block, lds, s, a); break;
+        case 7: hipLaunchKernelGGL((q4k_mfma_kernel<7, R>), grid, block, lds, s, a); break;
+        case 8: hipLaunchKernelGGL((q4k_mfma_kernel<8, R>), grid, block, lds, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, hipStream_t s) {
+    switch (ring) {
+        case 2: return launch_mfma_r<2>(a, batch, s);
+        case 3: return launch_mfma_r<3>(a, batch, s);
+        case 4: return launch_mfma_r<4>(a, batch, s);
         default: return hipErrorInvalidValue;
     }
 }

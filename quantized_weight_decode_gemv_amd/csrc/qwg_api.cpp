@@ -69,6 +69,40 @@ Plan choose_plan(int tiles, int nb, int batch) {
 
 int choose_splits(int tiles, int nb) { return choose_plan(tiles, nb, 1).splits; }
 
+// Splits of a matrix-core GEMM (batch >= 2): at least kMfmaTargetWgs workgroups,
+// at most one split per super-block, partial sums inside the workspace.
+// Measured on the 32000 x 2048 LM head at batch 8 (500 tiles): 1 split 17.0 us,
+// 2 splits 18.1 us, 3 splits 20.7 us; the kernel is bound by its vector-ALU
+// work per weight, which splitting does not reduce, while every split adds a
+// partial-sum round trip. QWG_MFMA_TARGET overrides the target (tuning).
+constexpr int kMfmaTargetWgs = 256;
+
+int mfma_splits(int tiles, int nb, int batch) {
+    static const int env_target = env_int("QWG_MFMA_TARGET", 0);
+    const int target = env_target ? env_target : kMfmaTargetWgs;
+    int s = (target + tiles - 1) / tiles;
+    if (s > nb) s = nb;
+    if (s < 1) s = 1;
+    while (s > 1 && ((size_t)s * batch * tiles * kTileRows > kWsPartialFloats ||
+                     (size_t)tiles > kWsCounters))
+        --s;
+    return s;
+}
+
+// waves argument of qwg_gemm_q4k_ex that selects the matrix-core engine
+constexpr int kWavesMfma = 1;
+
+// Ring stages of the matrix-core engine. Measured (LM head, batch 8, one
+// split): 2 stages 17.0 us, 3 stages 17.6 us, 4 stages 18.5 us; deeper rings
+// only cost occupancy. QWG_MFMA_RING overrides it (tuning).
+int mfma_ring() {
+    static const int v = [] {
+        const int r = env_int("QWG_MFMA_RING", 2);
+        return r >= 2 && r <= 4 ? r : 2;
+    }();
+    return v;
+}
+
 // Persistent stream engine shape (wavefronts per workgroup, LDS ring stages).
 // Measured on MI355X: grouped streams run best with 4-wavefront workgroups and
 // a 2-stage ring (more resident workgroups per CU); a single large matrix, with
@@ -268,6 +302,18 @@ int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
     if (batch < 1 || batch > QWG_MAX_BATCH) return QWG_ERR_BATCH;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
     GemvArgs a;
+    if (batch >= 2) {
+        fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
+        a.splits = mfma_splits(a.tiles, a.nb, batch);
+        if (a.splits > 1) {
+            Workspace ws;
+            rc = get_workspace((hipStream_t)stream, &ws);
+            if (rc) return rc;
+            a.partial = ws.partial;
+            a.counters = ws.counters;
+        }
+        return hip_status(launch_q4k_mfma(a, batch, mfma_ring(), (hipStream_t)stream));
+    }
     int waves = kQ4kWavesSmall;
     rc = fill_gemv_args(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes, batch, (hipStream_t)stream,
                         &waves);
@@ -290,10 +336,12 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
     GemvArgs a;
     fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
+    if (waves == kWavesMfma && batch < 2) return QWG_ERR_SHAPE;
+    if (waves == 0 && batch >= 2) waves = kWavesMfma;
     const Plan autoplan = choose_plan(a.tiles, a.nb, batch);
+    if (splits == 0) splits = waves == kWavesMfma ? mfma_splits(a.tiles, a.nb, batch) : autoplan.splits;
     if (waves == 0) waves = autoplan.waves;
-    if (splits == 0) splits = autoplan.splits;
-    if (waves != 4 && waves != 8 && waves != 16) return QWG_ERR_SHAPE;
+    if (waves != kWavesMfma && waves != 4 && waves != 8 && waves != 16) return QWG_ERR_SHAPE;
     if (splits < 1 || splits > a.nb) return QWG_ERR_SHAPE;
     if (splits > 1 && ((size_t)splits * batch * a.tiles * kTileRows > kWsPartialFloats ||
                        (size_t)a.tiles > kWsCounters))
@@ -306,6 +354,7 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
         a.partial = ws.partial;
         a.counters = ws.counters;
     }
+    if (waves == kWavesMfma) return hip_status(launch_q4k_mfma(a, batch, mfma_ring(), (hipStream_t)stream));
     return hip_status(launch_q4k_gemv(a, batch, waves, (hipStream_t)stream));
 }
 

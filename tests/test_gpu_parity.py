@@ -346,6 +346,60 @@ def test_gemm_q4k_integer_exact():
     assert np.array_equal(Y.astype(np.float64), Yr)
 
 
+# ---------------------------------------------------------------- batched GEMM on matrix cores
+
+@pytest.mark.parametrize("batch", [2, 3, 5, 8])
+@pytest.mark.parametrize("n_out,n_in", [(333, 1536), (64, 256), (130, 5632), (1, 512)])
+def test_gemm_q4k_mfma_every_split(batch, n_out, n_in):
+    w, _ = _gemv_q4k_case(n_out, n_in, 101, batch)
+    X = synth.activations(n_in, 101, 60 + batch, batch=batch)
+    Yr, Sr = oracle.gemm_q4k(w, X, n_in, n_out)
+    wd, xd = dev(w), dev(X)
+    nb = n_in // 256
+    for splits in sorted({1, 2, nb} & set(range(1, nb + 1))):
+        Y = host(qwg.gemm_q4k(wd, xd, waves=1, splits=splits))
+        assert_bound(Y, Yr, Sr, f"mfma batch {batch} splits {splits}")
+        assert_bits(host(qwg.gemm_q4k(wd, xd, waves=1, splits=splits)), Y, "mfma rerun")
+    # the vector-ALU engine on the same problem, same bound
+    assert_bound(host(qwg.gemm_q4k(wd, xd, waves=4, splits=1)), Yr, Sr, "valu engine")
+
+
+def test_gemm_q4k_mfma_wide_range_activations():
+    # magnitudes from 1e-30 to 1e30 in one row: every bf16 part of the split matters
+    n_out, n_in, batch = 200, 2048, 8
+    w, _ = _gemv_q4k_case(n_out, n_in, 102, 0)
+    g = np.random.default_rng(21)
+    X = (g.standard_normal((batch, n_in)) * 10.0 ** g.integers(-30, 31, (batch, n_in))).astype(np.float32)
+    Y = host(qwg.gemm_q4k(dev(w), dev(X)))
+    Yr, Sr = oracle.gemm_q4k(w, X, n_in, n_out)
+    assert_bound(Y, Yr, Sr, "wide range")
+
+
+@pytest.mark.parametrize("batch", [2, 4, 7])
+def test_gemm_q4k_mfma_integer_exact(batch):
+    n_out, n_in = 190, 5632
+    w = _integer_q4k(n_out, n_in, 8 + batch)
+    X = np.random.default_rng(batch).integers(-8, 9, (batch, n_in)).astype(np.float32)
+    Yr, _ = oracle.gemm_q4k(w, X, n_in, n_out)
+    for splits in (1, 3):
+        Y = host(qwg.gemm_q4k(dev(w), dev(X), waves=1, splits=splits))
+        assert np.array_equal(Y.astype(np.float64), Yr), f"splits {splits}"
+
+
+def test_gemm_q4k_mfma_one_hot_columns():
+    # x = e_k in batch row b picks column k of the dequantized matrix exactly
+    n_out, n_in = 96, 1024
+    w, _ = _gemv_q4k_case(n_out, n_in, 103, 1)
+    deq = oracle.dequant_q4k(w, n_out * n_in).reshape(n_out, n_in)
+    cols = [0, 31, 32, 255, 256, 700, 1023, 513]
+    X = np.zeros((8, n_in), np.float32)
+    for b, k in enumerate(cols):
+        X[b, k] = 1.0
+    Y = host(qwg.gemm_q4k(dev(w), dev(X)))
+    for b, k in enumerate(cols):
+        assert np.array_equal(Y[b], deq[:, k]), f"column {k}"
+
+
 # ---------------------------------------------------------------- IQ3 GEMV
 
 @pytest.mark.parametrize("p", synth.config(4), ids=lambda p: p.name)
