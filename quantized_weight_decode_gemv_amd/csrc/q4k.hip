@@ -335,6 +335,7 @@ __global__ __launch_bounds__(W * 64) void q4k_gemv_kernel(GemvArgs a) {
 // only a few stages, so the copies, not the math, set its pace).
 constexpr int kXSlice = 2048;
 constexpr int kMfmaStage = kStageBytes + 4 * kXSlice;   // 17408
+constexpr int kMfmaScales = 1024;                        // per wavefront: [64 rows][2][d*sc, offset]
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -449,6 +450,7 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
     const int n = lane & 15;
     const bool upper = lane >= 32;
 
+    float *scales = (float *)(smem + R * kMfmaStage + kMfmaScales * G);
     const uint32_t mask = opaque(0x00780078u);
     const uint32_t bias = opaque(0x41804180u);
     const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -463,6 +465,25 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
         wait_stage_copies(min(R - 1, nst - 1 - s));
         lds_barrier();
         const uint8_t *stage = smem + (s % R) * kMfmaStage;
+        // Scale terms of sub-blocks 2G and 2G+1 for every tile row, decoded once
+        // (lane r: row r) and read back below by the lanes that hold that row.
+        {
+            const uint4 h = *(const uint4 *)(stage + lane * kQ4kBytes);
+            uint32_t sc0, sc1, mn0, mn1;
+            q4k_scales<G>(h, sc0, sc1, mn0, mn1);
+            const float d = h2f_lo(h.x);
+            const float dmin = h2f_hi(h.x);
+            const float dsc0 = d * (float)sc0;
+            const float dsc1 = d * (float)sc1;
+            float4 t;
+            t.x = dsc0;
+            t.y = __builtin_fmaf(dmin, (float)mn0, 16.0f * dsc0);
+            t.z = dsc1;
+            t.w = __builtin_fmaf(dmin, (float)mn1, 16.0f * dsc1);
+            *(float4 *)(scales + 4 * lane) = t;
+            // (read back by other lanes of this wavefront: LDS keeps a wavefront's order)
+            asm volatile("" ::: "memory");
+        }
         const float *xs = (const float *)(stage + kStageBytes + kXSlice * G);
         float xv[8];
         const float4 x0 = *(const float4 *)(xs + 4 * xslot0);
@@ -486,13 +507,9 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
             f32x4_t c2 = mfma_bf16(ah, b_hi, zero4);
             c2 = mfma_bf16(am_, b_hi, c2);
             c2 = mfma_bf16(al, b_hi, c2);
-            const uint4 h = *(const uint4 *)rowp;
-            uint32_t sc0, sc1, mn0, mn1;
-            q4k_scales<G>(h, sc0, sc1, mn0, mn1);
-            const float d = h2f_lo(h.x);
-            const float dmin = h2f_hi(h.x);
-            const float dsc = d * (float)(upper ? sc1 : sc0);
-            const float off = __builtin_fmaf(dmin, (float)(upper ? mn1 : mn0), 16.0f * dsc);
+            const float2 so = *(const float2 *)(scales + 4 * (16 * g + n) + 2 * (int)upper);
+            const float dsc = so.x;
+            const float off = so.y;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float c = upper ? c2[i] : c1[i];
@@ -878,7 +895,7 @@ hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nit
 
 template <int R>
 hipError_t launch_mfma_r(const GemvArgs &a, int batch, hipStream_t s) {
-    const size_t lds = R * (size_t)kMfmaStage;
+    const size_t lds = R * (size_t)kMfmaStage + 4 * kMfmaScales;
     const dim3 grid((unsigned)(a.tiles * a.splits)), block(256);
     switch (batch) {
         case 2: hipLaunchKernelGGL((q4k_mfma_kernel<2, R>), grid, block, lds, s, a); break;
