@@ -28,7 +28,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --workload iq3_stream|lm_head [--steps K] [--warmup W]
 The second form measures the other hot-path rows on their own (one JSON line each, for the
 record and for profiling): "iq3_stream" = the same 155 GEMV shapes in the IQ3 container as one
-grouped launch; "lm_head" = the 32000x2048 Q4_K LM head at batch 1..8 (qwg_gemv_q4k,
+grouped launch (IQ3 tile layout; the row-major launch beside it); "lm_head" = the 32000x2048 Q4_K LM head at batch 1..8 (qwg_gemv_q4k,
 qwg_gemv_q4k_tiled, qwg_gemm_q4k), cycling over enough weight copies that every launch streams
 from HBM rather than the last-level cache.
 """
@@ -288,10 +288,13 @@ def bench_iq3_stream(args):
     W = [torch.from_numpy(synth.weights(p)).to(dev) for p in probs]
     X = [torch.from_numpy(synth.inputs(p)).to(dev) for p in probs]
     Y = [torch.empty(p.n_out, dtype=torch.float32, device=dev) for p in probs]
-    group = qwg.Iq3Group(zip(W, X, Y), grid)
+    WT = [qwg.pack_iq3_tiles(w, p.n_in) for p, w in zip(probs, W)]
+    group = qwg.Iq3Group(zip(WT, X, Y), grid, tiled=True)
+    group_rows = qwg.Iq3Group(zip(W, X, [torch.empty_like(y) for y in Y]), grid)
     stream = torch.cuda.current_stream(dev)
     step_bytes = sum(p.algorithmic_bytes for p in probs)
     us = _event_us(lambda: group.run(stream), stream, args.steps, args.warmup)
+    us_rows = _event_us(lambda: group_rows.run(stream), stream, args.steps, args.warmup)
     gbs = step_bytes / us / 1e3
     print(json.dumps({
         "metric": "effective HBM GB/s, IQ3 GEMV stream, batch 1", "value": round(gbs, 2),
@@ -299,10 +302,15 @@ def bench_iq3_stream(args):
         "ms_per_step": round(us / 1e3, 4), "higher_is_better": True, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "TinyLlama-1.1B-shaped per-token stream in the 98-byte IQ3 "
-                               "container: 155 GEMVs, one grouped launch (qwg_group_run)",
-                   "algorithmic_bytes_per_step": step_bytes},
+                               "container: 155 GEMVs, one grouped launch (qwg_group_run), "
+                               "weights in the IQ3 tile layout",
+                   "layout": "IQ3 tile layout (qwg_pack_iq3_tiles, repacked once before timing)",
+                   "algorithmic_bytes_per_step": step_bytes,
+                   "row_major_us": round(us_rows, 2),
+                   "row_major_GBs": round(step_bytes / us_rows / 1e3, 1)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "iq3_stream_kernel (grouped)",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "kernel": "iq3_stream_kernel<8,2,tile layout> (grouped)",
                      "kernel_us": round(us, 2)}}), flush=True)
 
 

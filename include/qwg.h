@@ -174,17 +174,31 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
  * A stage of the GEMV then copies one contiguous 9216-byte run instead of 64
  * rows' 144-byte pieces.
  *
- * qwg_tiled_bytes: bytes of the tile layout (ceil(n_out/64)*64 rows), or a
- * negative status (QWG_FMT_Q4K only).
+ * Tile layout for IQ3: the same tile and column order (column (t, b) at
+ * (t*(n_in/256) + b)*6272), each 6272-byte column regrouped by field so that
+ * every read of the GEMV is aligned and conflict-free: the 64 rows' index
+ * bytes 16G..16G+15 for G = 0..3 ([G][row][16], 4096 bytes), their sign/scale
+ * words 2G, 2G+1 ([G][row][8], 2048 bytes), then their d ([row][2], 128 bytes).
+ * The bytes of every block are kept, only regrouped.
+ *
+ * qwg_tiled_bytes: bytes of the tile layout (ceil(n_out/64)*64 rows) for
+ * QWG_FMT_Q4K or QWG_FMT_IQ3, or a negative status.
  * qwg_pack_q4k_tiles: src (row-major, as qwg_gemv_q4k takes it) -> dst (tile
  * layout, qwg_tiled_bytes bytes); both 16-byte aligned, must not overlap.
  * qwg_gemv_q4k_tiled: qwg_gemv_q4k on tile-layout weights (same arguments,
  * alignment and accuracy).
+ * qwg_pack_iq3_tiles: as qwg_pack_q4k_tiles for IQ3 (src 2-byte aligned, dst
+ * 16-byte aligned).
+ * qwg_gemv_iq3_tiled: qwg_gemv_iq3 on tile-layout weights (w 16-byte aligned;
+ * otherwise the same arguments and accuracy).
  */
 int64_t qwg_tiled_bytes(int fmt, int64_t n_in, int64_t n_out);
 int qwg_pack_q4k_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
 int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
                        void *stream);
+int qwg_pack_iq3_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
+int qwg_gemv_iq3_tiled(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                       int64_t n_out, void *stream);
 
 /*
  * Grouped GEMV: many independent GEMVs of one format in one launch (one grid
@@ -223,8 +237,11 @@ typedef struct qwg_group qwg_group;
 int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **group);
 int qwg_group_create_iq3(const qwg_gemv_desc *descs, int count, const float *grid,
                          qwg_group **group);
-/* As qwg_group_create_q4k, every member's weights in the tile layout. */
+/* As qwg_group_create_q4k / _iq3, every member's weights in the tile layout
+ * (16-byte aligned). */
 int qwg_group_create_q4k_tiled(const qwg_gemv_desc *descs, int count, qwg_group **group);
+int qwg_group_create_iq3_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
+                               qwg_group **group);
 int qwg_group_run(const qwg_group *group, void *stream);
 int qwg_group_workgroups(const qwg_group *group);
 int qwg_group_destroy(qwg_group *group);

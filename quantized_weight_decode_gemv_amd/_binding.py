@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
         L.qwg_tiled_bytes.restype = I64
         L.qwg_pack_q4k_tiles.argtypes = [P, P, I64, I64, P]
         L.qwg_gemv_q4k_tiled.argtypes = [P, P, P, I64, I64, P]
+        L.qwg_pack_iq3_tiles.argtypes = [P, P, I64, I64, P]
+        L.qwg_gemv_iq3_tiled.argtypes = [P, P, P, P, I64, I64, P]
+        L.qwg_group_create_iq3_tiled.argtypes = [P, I, P, ctypes.POINTER(P)]
         L.qwg_group_create_iq3.argtypes = [P, I, P, ctypes.POINTER(P)]
         L.qwg_group_run.argtypes = [P, P]
         L.qwg_group_workgroups.argtypes = [P]
@@ -63,6 +66,7 @@ def lib() -> ctypes.CDLL:
         for f in ("qwg_dequant_q4k", "qwg_dequant_iq3", "qwg_gemv_q4k", "qwg_gemv_iq3",
                   "qwg_gemv_iq3_ex", "qwg_gemm_q4k", "qwg_gemm_q4k_ex", "qwg_group_create_q4k",
                   "qwg_group_create_q4k_tiled", "qwg_pack_q4k_tiles", "qwg_gemv_q4k_tiled",
+                  "qwg_pack_iq3_tiles", "qwg_gemv_iq3_tiled", "qwg_group_create_iq3_tiled",
                   "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
                   "qwg_group_destroy"):
             getattr(L, f).restype = I
@@ -162,8 +166,8 @@ def gemv_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) 
     return out
 
 
-def tiled_bytes(n_in: int, n_out: int) -> int:
-    v = lib().qwg_tiled_bytes(QWG_FMT_Q4K, n_in, n_out)
+def tiled_bytes(n_in: int, n_out: int, fmt: int = QWG_FMT_Q4K) -> int:
+    v = lib().qwg_tiled_bytes(fmt, n_in, n_out)
     if v < 0:
         raise ValueError(f"invalid shape n_in={n_in} n_out={n_out}")
     return v
@@ -199,6 +203,40 @@ def gemv_q4k_tiled(w: torch.Tensor, x: torch.Tensor, n_out: int,
         raise ValueError("out has the wrong size")
     _check(lib().qwg_gemv_q4k_tiled(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out,
                                     _stream(x)), "qwg_gemv_q4k_tiled")
+    return out
+
+
+def pack_iq3_tiles(w: torch.Tensor, n_in: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-major IQ3 weights (uint8, n_out rows) -> the IQ3 tile layout that
+    gemv_iq3_tiled and tiled IQ3 groups take."""
+    n_out = _weights(w, n_in, IQ3_BYTES)
+    nbytes = tiled_bytes(n_in, n_out, QWG_FMT_IQ3)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _dev(out, "out", torch.uint8)
+    if out.numel() != nbytes:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_pack_iq3_tiles(out.data_ptr(), w.data_ptr(), n_in, n_out, _stream(w)),
+           "qwg_pack_iq3_tiles")
+    return out
+
+
+def gemv_iq3_tiled(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor, n_out: int,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x for IQ3 weights in the tile layout (pack_iq3_tiles)."""
+    _dev(w, "w", torch.uint8)
+    _dev(x, "x", torch.float32)
+    _grid(grid)
+    n_in = x.numel()
+    if w.numel() != tiled_bytes(n_in, n_out, QWG_FMT_IQ3):
+        raise ValueError("w is not an IQ3 tile-layout matrix of this shape")
+    if out is None:
+        out = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n_out:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_gemv_iq3_tiled(out.data_ptr(), x.data_ptr(), w.data_ptr(), grid.data_ptr(),
+                                    n_in, n_out, _stream(x)), "qwg_gemv_iq3_tiled")
     return out
 
 
@@ -280,8 +318,6 @@ class Group:
             if grid is None:
                 raise ValueError("an IQ3 group needs the grid")
             _grid(grid)
-        if tiled and fmt != QWG_FMT_Q4K:
-            raise ValueError("the tile layout is a Q4_K layout")
         block_bytes = Q4K_BYTES if fmt == QWG_FMT_Q4K else IQ3_BYTES
         descs = (GemvDesc * len(members))()
         for i, (w, x, y) in enumerate(members):
@@ -291,7 +327,7 @@ class Group:
             if tiled:
                 _dev(w, "w", torch.uint8)
                 n_out = y.numel()
-                if w.numel() != tiled_bytes(n_in, n_out):
+                if w.numel() != tiled_bytes(n_in, n_out, fmt):
                     raise ValueError(f"member {i}: w is not a tile-layout matrix of this shape")
             else:
                 n_out = _weights(w, n_in, block_bytes)
@@ -308,6 +344,10 @@ class Group:
         elif fmt == QWG_FMT_Q4K:
             _check(lib().qwg_group_create_q4k(descs, len(members), ctypes.byref(handle)),
                    "qwg_group_create_q4k")
+        elif tiled:
+            _check(lib().qwg_group_create_iq3_tiled(descs, len(members), grid.data_ptr(),
+                                                    ctypes.byref(handle)),
+                   "qwg_group_create_iq3_tiled")
         else:
             _check(lib().qwg_group_create_iq3(descs, len(members), grid.data_ptr(),
                                               ctypes.byref(handle)), "qwg_group_create_iq3")
@@ -345,7 +385,8 @@ class Q4kGroup(Group):
 
 
 class Iq3Group(Group):
-    """Group of IQ3 GEMVs sharing one grid (members as for Group)."""
+    """Group of IQ3 GEMVs sharing one grid (members as for Group; tiled: weights
+    in the IQ3 tile layout, y giving each member's n_out)."""
 
-    def __init__(self, members, grid: torch.Tensor):
-        super().__init__(members, QWG_FMT_IQ3, grid)
+    def __init__(self, members, grid: torch.Tensor, tiled: bool = False):
+        super().__init__(members, QWG_FMT_IQ3, grid, tiled=tiled)

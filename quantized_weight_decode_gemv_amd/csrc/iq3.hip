@@ -99,11 +99,22 @@ __global__ __launch_bounds__(256) void iq3_dequant_kernel(const uint8_t *__restr
 // when they are fp16 values (the small integers IQ3 grids use). A 64 KB layout
 // with the address straight out of the v_perm (entry at i*256 + s*16) measured
 // slower: its bank depends on s alone, so lanes collide far more often.
-template <int W, int R>
+// Tile layout (qwg_pack_iq3_tiles): for each 64-row tile and block column b,
+// 6272 bytes = the 64 rows' blocks regrouped by field and wavefront role:
+// index bytes [G][row][16] (bytes 16G..16G+15 of each block, 4 x 1024 B), sign/
+// scale words [G][row][8] (words 2G, 2G+1, 4 x 512 B), then d [row][2] (128 B).
+// Column (t, b) starts at (t*nb + b) * 6272; rows past n_out are zero blocks.
+// A stage copy is contiguous, and wavefront G's lanes (rows) read consecutive
+// 16-, 8- and 2-byte pieces: no realignment, no bank conflicts, no clamping.
+constexpr int kIq3TileCol = kTileRows * kIq3Bytes;   // 6272
+constexpr int kIq3TileWords = 4096;
+constexpr int kIq3TileD = 6144;
+
+template <int W, int R, bool TL>
 struct Iq3Cfg {
     static constexpr int kBps = W / 4;                   // super-blocks per stage
     static constexpr int kWin = 112;                     // bytes per row window
-    static constexpr int kCol = kTileRows * kWin;        // 7168: one super-block of a tile
+    static constexpr int kCol = TL ? kIq3TileCol : kTileRows * kWin;  // one super-block of a tile
     static constexpr int kSlot = kBps * kCol;
     static constexpr int kTable = 32768;                 // at LDS address 0
     static constexpr int kGrid = kTable;                 // staged fp32 grid, 4 KB
@@ -124,7 +135,7 @@ struct Iq3Item {
     bool tail;        // holds the last row's last block and the buffer ends off a granule
 };
 
-template <int BPS>
+template <int BPS, bool TL>
 __device__ __forceinline__ void iq3_load_item(Iq3Item &it, int k, const GroupArgs &g,
                                               const GemvArgs &single) {
     int local;
@@ -149,6 +160,16 @@ __device__ __forceinline__ void iq3_load_item(Iq3Item &it, int k, const GroupArg
     }
     it.nst = (it.kb1 - it.kb0 + BPS - 1) / BPS;
     it.row0 = it.tile * kTileRows;
+    if constexpr (TL) {
+        // column 0 of the tile; no partial granules anywhere in this layout
+        it.sb = it.a.w + (int64_t)it.tile * it.a.nb * kIq3TileCol;
+        it.sb_off = 0;
+        it.lo = 0;
+        it.hi = 0;
+        it.head = false;
+        it.tail = false;
+        return;
+    }
     const uintptr_t wb = (uintptr_t)it.a.w;
     const uintptr_t we = wb + (uintptr_t)it.a.n_out * (uintptr_t)it.a.row_bytes;
     const uintptr_t base0 = wb + (uintptr_t)it.row0 * (uintptr_t)it.a.row_bytes;
@@ -188,6 +209,20 @@ __device__ __forceinline__ void iq3_fetch(const uint8_t *win, uint32_t sh, Iq3Ra
 #pragma unroll
     for (int i = 0; i < 2; ++i) r.words[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], sh);
     r.d16 = dw >> ((sh & 2u) << 3);
+}
+
+// From a tile-layout stage column (this lane's row).
+template <int G>
+__device__ __forceinline__ void iq3_fetch_tiled(const uint8_t *col, int lane, Iq3Raw &r) {
+    const uint4 q = *(const uint4 *)(col + G * 1024 + 16 * lane);
+    const uint2 w = *(const uint2 *)(col + kIq3TileWords + G * 512 + 8 * lane);
+    r.idx[0] = q.x;
+    r.idx[1] = q.y;
+    r.idx[2] = q.z;
+    r.idx[3] = q.w;
+    r.words[0] = w.x;
+    r.words[1] = w.y;
+    r.d16 = *(const uint16_t *)(col + kIq3TileD + 2 * lane);
 }
 
 // From global memory, 2 bytes at a time (the block is 2-byte aligned).
@@ -252,11 +287,11 @@ __device__ __forceinline__ void iq3_table_entry(int s, int i, float4 g) {
     lds_store<u32x2>(s * 2048 + i * 8, e);
 }
 
-template <int G, int W, int R>
+template <int G, int W, int R, bool TL>
 __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &single,
                                            const float *grid, int nitems, uint8_t *smem) {
     static_assert(R >= 2 && R <= 4, "ring of two to four stages");
-    using C = Iq3Cfg<W, R>;
+    using C = Iq3Cfg<W, R, TL>;
     constexpr int BPS = C::kBps;
     const int lane = threadIdx.x & 63;
     const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
@@ -285,13 +320,14 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
     }
 
     Iq3Item c;
-    iq3_load_item<BPS>(c, kc, g, single);
+    iq3_load_item<BPS, TL>(c, kc, g, single);
 
     // copy cursor: next stage sd of item kd goes to ring slot slot_d
     int kd = kc, sd = 0, slot_d = 0, pending = 0;
     Iq3Item d = c;
     uint32_t doff[2];  // this lane's granule of block 0 of its row, relative to d.sb (< 2 MB)
     auto prep_copy = [&]() {
+        if constexpr (TL) return;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             doff[i] = d.sb_off +
@@ -299,20 +335,33 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
                           (uint32_t)d.a.row_bytes +
                       cgran[i];
     };
+    // Tile layout: wavefront G copies its index bytes (1 KB, every lane) and its
+    // words (512 B, lanes 0..31); wavefront 3's lanes 32..39 also copy the d
+    // values, which follow its words in the column.
+    const uint32_t t_off0 = (uint32_t)(G * 1024 + 16 * lane);
+    const uint32_t t_off1 = (uint32_t)(kIq3TileWords + G * 512 + 16 * lane);
+    const bool t_second = lane < (G == 3 ? 40 : 32);
     prep_copy();
     uint32_t flags = 0;  // bit k: this wavefront's copies are in ring slot k
     auto issue_next = [&]() {
         if (kd >= nitems) return;
         const int b = d.kb0 + sd * BPS + j;
         if (b < d.kb1) {
-            const uint32_t base =
-                lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol + G * (16 * C::kWin);
+            if constexpr (TL) {
+                const uint32_t colb = lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol;
+                const uint8_t *src = d.sb + (int64_t)b * kIq3TileCol;
+                dma16(src + t_off0, colb + G * 1024);
+                if (t_second) dma16(src + t_off1, colb + kIq3TileWords + G * 512);
+            } else {
+                const uint32_t base =
+                    lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol + G * (16 * C::kWin);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                if (i == 0 || lane < 48) {
-                    // (offset + a multiple of 16) & ~15 keeps the granule index
-                    const uint32_t off = min(max((doff[i] + (uint32_t)(kIq3Bytes * b)) & ~15u, d.lo), d.hi);
-                    dma16(d.sb, off, base + 1024 * i);
+                for (int i = 0; i < 2; ++i) {
+                    if (i == 0 || lane < 48) {
+                        // (offset + a multiple of 16) & ~15 keeps the granule index
+                        const uint32_t off = min(max((doff[i] + (uint32_t)(kIq3Bytes * b)) & ~15u, d.lo), d.hi);
+                        dma16(d.sb, off, base + 1024 * i);
+                    }
                 }
             }
             flags |= 1u << slot_d;
@@ -325,7 +374,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
             sd = 0;
             kd += stride;
             if (kd < nitems) {
-                iq3_load_item<BPS>(d, kd, g, single);
+                iq3_load_item<BPS, TL>(d, kd, g, single);
                 prep_copy();
             }
         }
@@ -362,7 +411,11 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
             lds_barrier();   // stage in slot_c complete for every wavefront (and the table)
             issue_next();    // refill the slot computed in the previous step
             const int b = c.kb0 + s * BPS + j;
-            if (b < c.kb1) {
+            if (TL && b < c.kb1) {
+                Iq3Raw raw;
+                iq3_fetch_tiled<G>(smem + C::kRing + slot_c * C::kSlot + j * C::kCol, lane, raw);
+                acc = iq3_dot<G>(raw, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
+            } else if (b < c.kb1) {
                 const uint32_t sh = (rlo + (uint32_t)(kIq3Bytes * b)) & 15u;
                 const uint8_t *win = smem + C::kRing + slot_c * C::kSlot + j * C::kCol +
                                      lane * C::kWin + (sh & 12u);
@@ -390,24 +443,24 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
         }
         kc += stride;
         if (kc >= nitems) break;
-        iq3_load_item<BPS>(c, kc, g, single);
+        iq3_load_item<BPS, TL>(c, kc, g, single);
     }
 }
 
-template <int W, int R>
+template <int W, int R, bool TL>
 __global__ __launch_bounds__(W * 64) void iq3_stream_kernel(GroupArgs g, GemvArgs single,
                                                             const float *grid, int nitems) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
-        case 0: iq3_stream<0, W, R>(g, single, grid, nitems, smem); break;
-        case 1: iq3_stream<1, W, R>(g, single, grid, nitems, smem); break;
-        case 2: iq3_stream<2, W, R>(g, single, grid, nitems, smem); break;
-        default: iq3_stream<3, W, R>(g, single, grid, nitems, smem); break;
+        case 0: iq3_stream<0, W, R, TL>(g, single, grid, nitems, smem); break;
+        case 1: iq3_stream<1, W, R, TL>(g, single, grid, nitems, smem); break;
+        case 2: iq3_stream<2, W, R, TL>(g, single, grid, nitems, smem); break;
+        default: iq3_stream<3, W, R, TL>(g, single, grid, nitems, smem); break;
     }
 }
 
 // Resident workgroups of one kernel variant on the current device (cached).
-template <int W, int R>
+template <int W, int R, bool TL>
 int iq3_slots() {
     static int slots = 0;
     if (slots == 0) {
@@ -416,8 +469,8 @@ int iq3_slots() {
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus < 1)
             cus = 256;
-        constexpr size_t lds = Iq3Cfg<W, R>::kLds;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, iq3_stream_kernel<W, R>,
+        constexpr size_t lds = Iq3Cfg<W, R, TL>::kLds;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, iq3_stream_kernel<W, R, TL>,
                                                          W * 64, lds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
@@ -428,13 +481,49 @@ int iq3_slots() {
 
 template <int W, int R>
 hipError_t iq3_launch(const GroupArgs &g, const GemvArgs &single, const float *grid, int nitems,
-                      hipStream_t s) {
-    int n = iq3_slots<W, R>();
+                      bool tiled, hipStream_t s) {
+    int n = tiled ? iq3_slots<W, R, true>() : iq3_slots<W, R, false>();
     if (n > nitems) n = nitems;
-    constexpr size_t lds = Iq3Cfg<W, R>::kLds;
-    hipLaunchKernelGGL((iq3_stream_kernel<W, R>), dim3((unsigned)n), dim3(W * 64), lds, s, g,
-                       single, grid, nitems);
+    if (tiled) {
+        constexpr size_t lds = Iq3Cfg<W, R, true>::kLds;
+        hipLaunchKernelGGL((iq3_stream_kernel<W, R, true>), dim3((unsigned)n), dim3(W * 64), lds, s,
+                           g, single, grid, nitems);
+    } else {
+        constexpr size_t lds = Iq3Cfg<W, R, false>::kLds;
+        hipLaunchKernelGGL((iq3_stream_kernel<W, R, false>), dim3((unsigned)n), dim3(W * 64), lds,
+                           s, g, single, grid, nitems);
+    }
     return hipGetLastError();
+}
+
+// Row-major IQ3 weights -> tile layout, one workgroup per (tile, block column),
+// 2-byte units (the source blocks are only 2-byte aligned).
+__global__ __launch_bounds__(256) void iq3_pack_tiles_kernel(const uint8_t *__restrict__ src,
+                                                             uint8_t *__restrict__ dst, int nb,
+                                                             int n_out) {
+    const int b = blockIdx.x % nb;
+    const int tile = blockIdx.x / nb;
+    const int64_t row_bytes = (int64_t)nb * kIq3Bytes;
+    uint16_t *out = (uint16_t *)(dst + (int64_t)blockIdx.x * kIq3TileCol);
+    for (int u = threadIdx.x; u < kIq3TileCol / 2; u += blockDim.x) {
+        const int o = 2 * u;
+        int rr, sbyte;
+        if (o < kIq3TileWords) {
+            rr = (o & 1023) >> 4;
+            sbyte = 16 * (o >> 10) + (o & 15);
+        } else if (o < kIq3TileD) {
+            const int o2 = o - kIq3TileWords;
+            rr = (o2 & 511) >> 3;
+            sbyte = 64 + 8 * (o2 >> 9) + (o2 & 7);
+        } else {
+            rr = (o - kIq3TileD) >> 1;
+            sbyte = 96;
+        }
+        const int r = tile * kTileRows + rr;
+        uint16_t v = 0;
+        if (r < n_out) v = *(const uint16_t *)(src + r * row_bytes + (int64_t)b * kIq3Bytes + sbyte);
+        out[u] = v;
+    }
 }
 
 // Variant table: (waves, ring stages).
@@ -453,10 +542,17 @@ hipError_t launch_iq3_dequant(const uint8_t *src, const float *grid, float *dst,
     return hipGetLastError();
 }
 
-int iq3_stream_slots(const Iq3Shape &sh) {
+hipError_t launch_iq3_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, hipStream_t s) {
+    const int64_t tiles = ((int64_t)n_out + kTileRows - 1) / kTileRows;
+    hipLaunchKernelGGL(iq3_pack_tiles_kernel, dim3((unsigned)(tiles * nb)), dim3(256), 0, s, src,
+                       dst, nb, n_out);
+    return hipGetLastError();
+}
+
+int iq3_stream_slots(const Iq3Shape &sh, bool tiled) {
     switch (iq3_key(sh.waves, sh.ring)) {
 #define X(w, r) \
-    case iq3_key(w, r): return iq3_slots<w, r>();
+    case iq3_key(w, r): return tiled ? iq3_slots<w, r, true>() : iq3_slots<w, r, false>();
         QWG_IQ3_VARIANTS(X)
 #undef X
         default: return 0;
@@ -464,10 +560,10 @@ int iq3_stream_slots(const Iq3Shape &sh) {
 }
 
 hipError_t launch_iq3_stream(const GroupArgs &g, const GemvArgs &single, const float *grid,
-                             int nitems, const Iq3Shape &sh, hipStream_t s) {
+                             int nitems, const Iq3Shape &sh, bool tiled, hipStream_t s) {
     switch (iq3_key(sh.waves, sh.ring)) {
 #define X(w, r) \
-    case iq3_key(w, r): return iq3_launch<w, r>(g, single, grid, nitems, s);
+    case iq3_key(w, r): return iq3_launch<w, r>(g, single, grid, nitems, tiled, s);
         QWG_IQ3_VARIANTS(X)
 #undef X
         default: return hipErrorInvalidValue;

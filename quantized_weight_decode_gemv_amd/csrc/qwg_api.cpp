@@ -143,9 +143,9 @@ Iq3Shape iq3_shape(bool grouped, int waves) {
     if (env_w) sh.waves = env_w;
     if (env_r) sh.ring = env_r;
     if (waves) sh.waves = waves;
-    if (iq3_stream_slots(sh) == 0) {
+    if (iq3_stream_slots(sh, false) == 0) {
         sh.ring = dflt.ring;
-        if (iq3_stream_slots(sh) == 0) sh = dflt;
+        if (iq3_stream_slots(sh, false) == 0) sh = dflt;
     }
     return sh;
 }
@@ -272,7 +272,7 @@ int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
     if (rc) return -rc;
     const int tiles = (int)((n_out + kTileRows - 1) / kTileRows);
     if (fmt == QWG_FMT_IQ3) {
-        const int slots = iq3_stream_slots(iq3_shape(false, 0));
+        const int slots = iq3_stream_slots(iq3_shape(false, 0), false);
         if (slots <= 0) return -QWG_ERR_HIP;
         return iq3_splits(tiles, (int)(n_in / kQK), slots);
     }
@@ -364,10 +364,11 @@ int qwg_gemv_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
 }
 
 int64_t qwg_tiled_bytes(int fmt, int64_t n_in, int64_t n_out) {
-    if (fmt != QWG_FMT_Q4K) return -QWG_ERR_FORMAT;
+    if (fmt != QWG_FMT_Q4K && fmt != QWG_FMT_IQ3) return -QWG_ERR_FORMAT;
     const int rc = check_gemv_shape(n_in, n_out);
     if (rc) return -rc;
-    return ((n_out + kTileRows - 1) / kTileRows) * kTileRows * (n_in / kQK) * kQ4kBytes;
+    return ((n_out + kTileRows - 1) / kTileRows) * kTileRows * (n_in / kQK) *
+           (fmt == QWG_FMT_Q4K ? kQ4kBytes : kIq3Bytes);
 }
 
 int qwg_pack_q4k_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
@@ -393,12 +394,14 @@ int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, in
     return hip_status(launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, (hipStream_t)stream));
 }
 
-int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
-                    int64_t n_out, int waves, int splits, void *stream) {
+namespace {
+
+int iq3_gemv(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+             int64_t n_out, int waves, int splits, bool tiled, void *stream) {
     if (!y || !x || !w || !grid) return QWG_ERR_NULL;
     int rc = check_gemv_shape(n_in, n_out);
     if (rc) return rc;
-    if (!aligned(w, 2) || !aligned(x, 16) || !aligned(grid, 16) || !aligned(y, 4))
+    if (!aligned(w, tiled ? 16 : 2) || !aligned(x, 16) || !aligned(grid, 16) || !aligned(y, 4))
         return QWG_ERR_ALIGN;
     if (waves != 0 && waves != 4 && waves != 8 && waves != 16) return QWG_ERR_SHAPE;
     GemvArgs a;
@@ -407,8 +410,9 @@ int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, 
     if (splits > 1 && ((size_t)splits * a.tiles * kTileRows > kWsPartialFloats ||
                        (size_t)a.tiles > kWsCounters))
         return QWG_ERR_SHAPE;
+    a.layout = tiled ? kLayoutTiles : kLayoutRows;
     const Iq3Shape sh = iq3_shape(false, waves);
-    const int slots = iq3_stream_slots(sh);
+    const int slots = iq3_stream_slots(sh, tiled);
     if (slots <= 0) return QWG_ERR_HIP;
     if (splits == 0) splits = iq3_splits(a.tiles, a.nb, slots);
     a.splits = splits;
@@ -421,12 +425,33 @@ int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, 
     }
     const GroupArgs none = {nullptr, nullptr, nullptr};
     return hip_status(
-        launch_iq3_stream(none, a, grid, a.tiles * splits, sh, (hipStream_t)stream));
+        launch_iq3_stream(none, a, grid, a.tiles * splits, sh, tiled, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                    int64_t n_out, int waves, int splits, void *stream) {
+    return iq3_gemv(y, x, w, grid, n_in, n_out, waves, splits, false, stream);
 }
 
 int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                  int64_t n_out, void *stream) {
-    return qwg_gemv_iq3_ex(y, x, w, grid, n_in, n_out, 0, 0, stream);
+    return iq3_gemv(y, x, w, grid, n_in, n_out, 0, 0, false, stream);
+}
+
+int qwg_gemv_iq3_tiled(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                       int64_t n_out, void *stream) {
+    return iq3_gemv(y, x, w, grid, n_in, n_out, 0, 0, true, stream);
+}
+
+int qwg_pack_iq3_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
+    if (!dst || !src) return QWG_ERR_NULL;
+    const int rc = check_gemv_shape(n_in, n_out);
+    if (rc) return rc;
+    if (!aligned(dst, 16) || !aligned(src, 2)) return QWG_ERR_ALIGN;
+    return hip_status(launch_iq3_pack_tiles((const uint8_t *)src, (uint8_t *)dst, (int)(n_in / kQK),
+                                            (int)n_out, (hipStream_t)stream));
 }
 
 // ------------------------------------------------------------------ grouped GEMV
@@ -526,7 +551,7 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
                  qwg_group **out) {
     const bool iq3 = fmt == QWG_FMT_IQ3;
     const int block_bytes = iq3 ? kIq3Bytes : kQ4kBytes;
-    const uintptr_t w_align = iq3 ? 2 : 16;
+    const uintptr_t w_align = iq3 && layout == kLayoutRows ? 2 : 16;
     std::vector<GemvArgs> probs((size_t)count);
     int64_t total = 0;
     int max_nb = 1;
@@ -621,13 +646,23 @@ int qwg_group_create_iq3(const qwg_gemv_desc *descs, int count, const float *gri
     return group_create(QWG_FMT_IQ3, kLayoutRows, descs, count, grid, out);
 }
 
+int qwg_group_create_iq3_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
+                               qwg_group **out) {
+    if (!descs || !grid || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    if (!aligned(grid, 16)) return QWG_ERR_ALIGN;
+    return group_create(QWG_FMT_IQ3, kLayoutTiles, descs, count, grid, out);
+}
+
 int qwg_group_run(const qwg_group *g, void *stream) {
     if (!g) return QWG_ERR_NULL;
     GemvArgs unused;
     fill_shape(unused, nullptr, nullptr, nullptr, nullptr, kQK, 1, kQ4kBytes);
     if (g->fmt == QWG_FMT_IQ3)
         return hip_status(launch_iq3_stream(g->args, unused, g->grid, g->workgroups,
-                                            iq3_shape(true, 0), (hipStream_t)stream));
+                                            iq3_shape(true, 0), g->layout == kLayoutTiles,
+                                            (hipStream_t)stream));
     if (use_stream_engine() || g->layout == kLayoutTiles) {
         const StreamShape sh = stream_shape(true);
         return hip_status(launch_q4k_stream(g->args, unused, g->positions, sh.waves, sh.ring,

@@ -37,7 +37,8 @@ struct GemvArgs {
 // Tiles (Q4_K): the same blocks ordered tile-major: for each 64-row tile, for
 // each block column b, the 64 rows' block b back to back (9216 bytes); rows
 // past n_out in the last tile are zero blocks. Block (r, b) sits at byte
-// ((r/64)*nb + b)*9216 + (r%64)*144.
+// ((r/64)*nb + b)*9216 + (r%64)*144. Tiles (IQ3): the same column order, each
+// 6272-byte column regrouped by field (described in iq3.hip).
 constexpr int kLayoutRows = 0;
 constexpr int kLayoutTiles = 1;
 
@@ -84,11 +85,14 @@ struct Iq3Shape {
     int waves;
     int ring;
 };
-// Resident workgroups of that variant on the current device (0 if unsupported).
-int iq3_stream_slots(const Iq3Shape &sh);
+// Resident workgroups of that variant on the current device (0 if unsupported),
+// for row-major or tile-layout weights.
+int iq3_stream_slots(const Iq3Shape &sh, bool tiled);
 // `nitems` work items (tile x split) of the group or of `single`; all members
-// of a group share `grid`.
+// of a group share `grid` and the layout.
 hipError_t launch_iq3_stream(const GroupArgs &g, const GemvArgs &single, const float *grid,
-                             int nitems, const Iq3Shape &sh, hipStream_t s);
+                             int nitems, const Iq3Shape &sh, bool tiled, hipStream_t s);
+// Row-major IQ3 weights -> tile layout (dst: tiles*64*nb*98 bytes).
+hipError_t launch_iq3_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, hipStream_t s);
 
 }  // namespace qwg

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
                  "qwg_plan_splits", "qwg_gemm_q4k_ex", "qwg_gemv_iq3_ex", "qwg_group_create_q4k",
                  "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
                  "qwg_group_destroy", "qwg_tiled_bytes", "qwg_pack_q4k_tiles",
-                 "qwg_gemv_q4k_tiled", "qwg_group_create_q4k_tiled"):
+                 "qwg_gemv_q4k_tiled", "qwg_group_create_q4k_tiled", "qwg_pack_iq3_tiles",
+                 "qwg_gemv_iq3_tiled", "qwg_group_create_iq3_tiled"):
         assert want in names
 
 
@@ -67,7 +68,9 @@ def test_tiled_bytes(L):
     assert L.qwg_tiled_bytes(0, 2048, 2048) == 2048 * 1152
     assert L.qwg_tiled_bytes(0, 2048, 65) == 128 * 1152      # rows rounded up to whole tiles
     assert L.qwg_tiled_bytes(0, 5632, 1) == 64 * 3168
-    assert L.qwg_tiled_bytes(1, 2048, 64) == -6
+    assert L.qwg_tiled_bytes(1, 2048, 64) == 64 * 8 * 98
+    assert L.qwg_tiled_bytes(1, 2048, 65) == 128 * 8 * 98
+    assert L.qwg_tiled_bytes(2, 2048, 64) == -6
     assert L.qwg_tiled_bytes(0, 300, 64) == -2
 
 
@@ -132,6 +135,14 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_gemv_q4k_tiled(FAKE, FAKE, FAKE, 256, 0, None), 2),
     (lambda L: L.qwg_gemv_q4k_tiled(FAKE, FAKE, FAKE + 8, 256, 1, None), 3),
     (lambda L: L.qwg_gemv_q4k_tiled(FAKE, FAKE + 4, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_pack_iq3_tiles(FAKE, None, 256, 1, None), 1),
+    (lambda L: L.qwg_pack_iq3_tiles(FAKE, FAKE, 256, 0, None), 2),
+    (lambda L: L.qwg_pack_iq3_tiles(FAKE + 2, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_pack_iq3_tiles(FAKE, FAKE + 1, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3_tiled(FAKE, FAKE, FAKE, None, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_iq3_tiled(FAKE, FAKE, FAKE, FAKE, 100, 1, None), 2),
+    (lambda L: L.qwg_gemv_iq3_tiled(FAKE, FAKE, FAKE + 2, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3_tiled(FAKE, FAKE, FAKE, FAKE + 8, 256, 1, None), 3),
     # IQ3 with an explicit decomposition
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, None, 256, 1, 4, 1, None), 1),
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 384, 1, 4, 1, None), 2),
@@ -190,6 +201,10 @@ def test_tiled_group_validation_errors(L):
     out = ctypes.c_void_p(123)
     assert L.qwg_group_create_q4k_tiled(arr, 2, ctypes.byref(out)) == 3
     assert out.value is None
+    # IQ3 tile layout: 16-byte aligned weights (row-major IQ3 accepts 2-byte)
+    arr3 = (_Desc * 1)(_Desc(FAKE, FAKE, FAKE + 2, 256, 1))
+    assert L.qwg_group_create_iq3_tiled(arr3, 1, FAKE, ctypes.byref(out)) == 3
+    assert L.qwg_group_create_iq3_tiled(arr3, 1, None, ctypes.byref(out)) == 1
     assert L.qwg_group_create_q4k_tiled(None, 1, ctypes.byref(out)) == 1
     assert L.qwg_group_create_q4k_tiled(arr, 0, ctypes.byref(out)) == 2
 

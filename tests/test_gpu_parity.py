@@ -702,3 +702,87 @@ def test_q4k_group_many_items_repeat_runs(tiled):
             yr, sr = oracle.gemv_q4k_rows(w, x, n_in, rows)
             assert_bound(yh[rows], yr, sr, f"run {run} {n_out}x{n_in}")
     g.close()
+
+
+# ---------------------------------------------------------------- IQ3 tile layout
+
+def _iq3_tile_layout(w: np.ndarray, n_in: int) -> np.ndarray:
+    """The IQ3 tile layout written out: per (tile, block column), index bytes
+    [G][row][16], words [G][row][8], d [row][2]; rows past n_out as zero blocks."""
+    n_out, nb = w.shape[0], n_in // 256
+    tiles = (n_out + 63) // 64
+    blk = np.zeros((tiles * 64, nb, 98), np.uint8)
+    blk[:n_out] = w.reshape(n_out, nb, 98)
+    blk = blk.reshape(tiles, 64, nb, 98).transpose(0, 2, 1, 3)       # [t][b][row][98]
+    idx = blk[..., :64].reshape(tiles, nb, 64, 4, 16).transpose(0, 1, 3, 2, 4)
+    words = blk[..., 64:96].reshape(tiles, nb, 64, 4, 8).transpose(0, 1, 3, 2, 4)
+    d = blk[..., 96:98]
+    return np.concatenate([idx.reshape(tiles, nb, -1), words.reshape(tiles, nb, -1),
+                           d.reshape(tiles, nb, -1)], axis=2).reshape(-1)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (64, 512), (65, 768), (300, 2048), (2048, 5632)])
+def test_pack_iq3_tiles_is_the_layout(n_out, n_in):
+    w = synth.iq3_weights(n_out, n_in, 130, n_out)
+    got = host(qwg.pack_iq3_tiles(dev(w), n_in))
+    assert np.array_equal(got, _iq3_tile_layout(w, n_in))
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 512), (65, 768), (130, 5632), (2048, 2048),
+                                        (32000, 2048), (4097, 1280)])
+def test_gemv_iq3_tiled(n_out, n_in):
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 131, n_out)
+    x = synth.activations(n_in, 131, n_out)
+    wt = qwg.pack_iq3_tiles(dev(w), n_in)
+    gd, xd = dev(grid), dev(x)
+    yr, sr = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    y = host(qwg.gemv_iq3_tiled(wt, xd, gd, n_out))
+    assert_bound(y, yr, sr, f"iq3 tiled {n_out}x{n_in}")
+    assert_bits(host(qwg.gemv_iq3_tiled(wt, xd, gd, n_out)), y, "iq3 tiled rerun")
+
+
+def test_iq3_tiled_integer_exact_and_group_layer():
+    grid = synth.iq3_grid()
+    gd = dev(grid)
+    # integer case (as test_gemv_iq3_integer_exact): exact in every summation order
+    n_out, n_in = 150, 2048
+    w = synth.iq3_weights(n_out, n_in, 103, 0).reshape(-1, 98).copy()
+    w[:, 96], w[:, 97] = 0x00, 0x44
+    words = w[:, 64:96].copy().view("<u4") & np.uint32(0x3FFFFFFF)
+    w[:, 64:96] = words.view(np.uint8)
+    w = w.reshape(n_out, -1)
+    x = np.random.default_rng(9).integers(-8, 9, n_in).astype(np.float32)
+    yr, _ = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    y = host(qwg.gemv_iq3_tiled(qwg.pack_iq3_tiles(dev(w), n_in), dev(x), gd, n_out))
+    assert np.array_equal(y.astype(np.float64), yr)
+    # one layer's seven projections as a tiled group, three runs
+    probs = synth.config(7)
+    ws = [synth.weights(p) for p in probs]
+    xs = [synth.inputs(p) for p in probs]
+    W = [qwg.pack_iq3_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
+    Y = [torch.full((p.n_out,), float("nan"), device=DEV) for p in probs]
+    g = qwg.Iq3Group(zip(W, [dev(x) for x in xs], Y), gd, tiled=True)
+    for _ in range(3):
+        g.run()
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        yr, sr = oracle.gemv_iq3(w, grid, x, p.n_in, p.n_out)
+        assert_bound(host(y), yr, sr, "iq3 tiled group " + p.name)
+    g.close()
+
+
+def test_iq3_tiled_group_stream_sampled_rows():
+    grid = synth.iq3_grid()
+    probs = synth.config(6)
+    rng = np.random.default_rng(31)
+    ws = [synth.weights(p) for p in probs]
+    xs = [synth.inputs(p) for p in probs]
+    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    W = [qwg.pack_iq3_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
+    g = qwg.Iq3Group(zip(W, [dev(x) for x in xs], Y), dev(grid), tiled=True)
+    for _ in range(2):
+        g.run()
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 12)]))
+        yr, sr = oracle.gemv_iq3_rows(w, grid, x, p.n_in, rows)
+        assert_bound(host(y)[rows], yr, sr, "iq3 tiled stream " + p.name)
