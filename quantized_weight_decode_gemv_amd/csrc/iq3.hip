@@ -144,7 +144,7 @@ __device__ __forceinline__ void iq3_load_item(Iq3Item &it, int k, const GroupArg
         local = k;
     } else {
         load_args(it.a, (cargs_p)g.problems + ((cu32_p)g.map)[k]);
-        local = k - it.a.wg_begin;
+        local = g.tile != nullptr ? (int)((cu32_p)g.tile)[k] : k - it.a.wg_begin;
     }
     const int splits = it.a.splits;
     if (splits == 1) {
@@ -299,7 +299,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
     const int stride = gridDim.x;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
 
-    int kc = blockIdx.x;  // item being computed (the grid never exceeds nitems)
+    int kc = skip_holes(blockIdx.x, stride, nitems, g);  // item being computed
     if (kc >= nitems) return;
 
     // Wavefronts 0..3 stage the grid's 4 KB (lane l of wavefront w: bytes
@@ -372,7 +372,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
         slot_d = slot_d + 1 == R ? 0 : slot_d + 1;
         if (++sd == d.nst) {
             sd = 0;
-            kd += stride;
+            kd = skip_holes(kd + stride, stride, nitems, g);
             if (kd < nitems) {
                 iq3_load_item<BPS, TL>(d, kd, g, single);
                 prep_copy();
@@ -441,7 +441,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
             const float total[1] = {tsum};
             tile_epilogue<1>(c.a, c.tile, c.split, total);
         }
-        kc += stride;
+        kc = skip_holes(kc + stride, stride, nitems, g);
         if (kc >= nitems) break;
         iq3_load_item<BPS, TL>(c, kc, g, single);
     }

@@ -605,14 +605,6 @@ struct Item {
     int layout;
 };
 
-// First position from k on (k, k + stride, ...) that holds work, or a
-// position >= nitems.
-__device__ __forceinline__ int skip_holes(int k, int stride, int nitems, const GroupArgs &g) {
-    if (g.tile != nullptr)
-        while (k < nitems && ((cu32_p)g.map)[k] == kNoItem) k += stride;
-    return k;
-}
-
 template <int BPS>
 __device__ __forceinline__ void load_item(Item &it, int k, const GroupArgs &g, const GemvArgs &single) {
     if (g.problems == nullptr) {

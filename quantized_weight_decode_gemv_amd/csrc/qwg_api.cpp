@@ -486,20 +486,15 @@ namespace {
 // QWG_STREAM_SKEW overrides it (tuning experiments).
 constexpr double kAgeSkew = 0.7;
 
-double age_skew() {
-    static const double v = [] {
-        const char *e = getenv("QWG_STREAM_SKEW");
-        const double d = e ? atof(e) : kAgeSkew;
-        return d < 0.0 ? 0.0 : (d > 0.95 ? 0.95 : d);
-    }();
-    return v;
+double skew_env(const char *name, double dflt) {
+    const char *e = getenv(name);
+    const double d = e ? atof(e) : dflt;
+    return d < 0.0 ? 0.0 : (d > 0.95 ? 0.95 : d);
 }
 
 void stream_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> &order,
-                     int64_t total, const StreamShape &sh, std::vector<uint32_t> &map,
-                     std::vector<uint32_t> &tile) {
-    int cus = 0;
-    const int per_cu = q4k_stream_residency(sh.waves, sh.ring, &cus);
+                     int64_t total, int per_cu, int cus, double skew_arg,
+                     std::vector<uint32_t> &map, std::vector<uint32_t> &tile) {
     const int64_t grid = (int64_t)per_cu * cus;
     if (grid < 1 || total <= grid) {
         // one item (or none) per workgroup: the sorted list itself
@@ -513,7 +508,7 @@ void stream_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> 
             }
         return;
     }
-    const double skew = per_cu > 1 ? age_skew() : 0.0;
+    const double skew = per_cu > 1 ? skew_arg : 0.0;
     std::vector<double> target((size_t)grid);
     double wsum = 0.0;
     for (int64_t b = 0; b < grid; ++b) {
@@ -577,10 +572,17 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
         probs[i].wg_begin = (int)wg;
         wg += probs[i].tiles;
     }
+    // IQ3 groups keep the plain longest-first round robin: measured on the IQ3
+    // stream (two workgroups per CU) the balanced schedule ran 126 us against
+    // 114 us, and any age skew only slowed it further.
     std::vector<uint32_t> map, tile;
     const bool stream = !iq3 && (layout == kLayoutTiles || use_stream_engine());
     if (stream) {
-        stream_schedule(probs, order, total, stream_shape(true), map, tile);
+        static const double skew = skew_env("QWG_STREAM_SKEW", kAgeSkew);
+        const StreamShape sh = stream_shape(true);
+        int cus = 0;
+        const int per_cu = q4k_stream_residency(sh.waves, sh.ring, &cus);
+        stream_schedule(probs, order, total, per_cu, cus, skew, map, tile);
     } else {
         map.resize((size_t)total);
         for (int i : order)
@@ -660,7 +662,7 @@ int qwg_group_run(const qwg_group *g, void *stream) {
     GemvArgs unused;
     fill_shape(unused, nullptr, nullptr, nullptr, nullptr, kQK, 1, kQ4kBytes);
     if (g->fmt == QWG_FMT_IQ3)
-        return hip_status(launch_iq3_stream(g->args, unused, g->grid, g->workgroups,
+        return hip_status(launch_iq3_stream(g->args, unused, g->grid, g->positions,
                                             iq3_shape(true, 0), g->layout == kLayoutTiles,
                                             (hipStream_t)stream));
     if (use_stream_engine() || g->layout == kLayoutTiles) {

@@ -115,6 +115,14 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     return v;
 }
 
+// First position from k on (k, k + stride, ...) that holds work, or a
+// position >= nitems.
+__device__ __forceinline__ int skip_holes(int k, int stride, int nitems, const GroupArgs &g) {
+    if (g.tile != nullptr)
+        while (k < nitems && ((cu32_p)g.map)[k] == kNoItem) k += stride;
+    return k;
+}
+
 // End of a 64-row tile for one workgroup: `total` is this lane's row sum over
 // the workgroup's super-block range (batch element `bt`). With one split the
 // row is stored directly. Otherwise every split stores its partial, and the
