@@ -50,8 +50,8 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
 # runs of this script, each scaled by the same counter on a plain device copy of known size
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "011d9ef26361554b8b8d1ba8cddfede2632e8c893031bff871d23b94e2f79e8d",
-           "fetch_bytes": 595971167, "write_bytes": 1704960}
+TRAFFIC = {"sources_sha256": "6024e910c8748acd360cd7fba04da6b4ece351c1138541fd31edba6d685c08e6",
+           "fetch_bytes": 595995230, "write_bytes": 1704960}
 
 
 def kernel_sources_sha256() -> str:
