@@ -350,8 +350,8 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
             if constexpr (TL) {
                 const uint32_t colb = lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol;
                 const uint8_t *src = d.sb + (int64_t)b * kIq3TileCol;
-                dma16(src + t_off0, colb + G * 1024);
-                if (t_second) dma16(src + t_off1, colb + kIq3TileWords + G * 512);
+                dma16_stream(src + t_off0, colb + G * 1024);
+                if (t_second) dma16_stream(src + t_off1, colb + kIq3TileWords + G * 512);
             } else {
                 const uint32_t base =
                     lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol + G * (16 * C::kWin);
