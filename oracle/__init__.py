@@ -8,6 +8,8 @@ What it computes, and where the pages define it:
 
 * Q4_K dequant: "用 Python 重写 picoLM" page, ``dequantize_q4_K`` listing.
 * IQ3 ("fmt=5") dequant: iq3_pack.py page, module docstring and ``decode()``.
+* IQ3_XXS in llama.cpp's byte order: codebook.py page, the format table of its
+  docstring, ``get_d``, ``get_s``, ``eff_np`` and ``dequant``.
 * GEMV / GEMM: ``y = W @ x`` over the fp32 dequantized rows, accumulated in fp64
   with k ascending, plus ``s = sum |w * x|`` for the per-row error bound
   (argument order of picoLM's ``matmul(out, x, W, n_in, n_out, type)`` call in
@@ -58,6 +60,9 @@ def lib():
         L.orc_q4k_pack_scales.argtypes = [P, P, P]
         L.orc_dequant_q4k.argtypes = [P, I64, P]
         L.orc_dequant_iq3.argtypes = [P, P, I64, P]
+        L.orc_dequant_iq3_xxs.argtypes = [P, P, I64, P]
+        L.orc_gemv_iq3_xxs.argtypes = [P, P, P, I64, I64, P, P]
+        L.orc_gemv_iq3_xxs_rows.argtypes = [P, P, P, I64, P, I64, P, P]
         L.orc_gemv_q4k.argtypes = [P, P, I64, I64, P, P]
         L.orc_gemv_iq3.argtypes = [P, P, P, I64, I64, P, P]
         L.orc_gemm_q4k.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
@@ -66,7 +71,8 @@ def lib():
         L.orc_set_threads.argtypes = [ctypes.c_int]
         L.orc_get_threads.restype = ctypes.c_int
         for name in ("orc_dequant_q4k", "orc_dequant_iq3", "orc_gemv_q4k", "orc_gemv_iq3",
-                     "orc_gemm_q4k", "orc_gemv_q4k_rows", "orc_gemv_iq3_rows"):
+                     "orc_gemm_q4k", "orc_gemv_q4k_rows", "orc_gemv_iq3_rows",
+                     "orc_dequant_iq3_xxs", "orc_gemv_iq3_xxs", "orc_gemv_iq3_xxs_rows"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -145,6 +151,19 @@ def dequant_iq3(blocks, grid, n: int) -> np.ndarray:
     return out
 
 
+def dequant_iq3_xxs(blocks, grid, n: int) -> np.ndarray:
+    """IQ3_XXS blocks in llama.cpp's byte order (codebook.py page)."""
+    blocks = _u8(blocks)
+    grid = _f32(grid)
+    if grid.shape != (256, 4):
+        raise ValueError("grid must be [256, 4]")
+    if blocks.size * QK != n * IQ3_BYTES:
+        raise ValueError("byte count does not match n")
+    out = np.empty(n, np.float32)
+    _check(lib().orc_dequant_iq3_xxs(_ptr(blocks), _ptr(grid), n, _ptr(out)), "dequant_iq3_xxs")
+    return out
+
+
 def gemv_q4k(w, x, n_in: int, n_out: int) -> tuple[np.ndarray, np.ndarray]:
     """(y, s) in fp64, each [n_out]."""
     w = _u8(w)
@@ -167,6 +186,19 @@ def gemv_iq3(w, grid, x, n_in: int, n_out: int) -> tuple[np.ndarray, np.ndarray]
     s = np.empty(n_out, np.float64)
     _check(lib().orc_gemv_iq3(_ptr(w), _ptr(grid), _ptr(x), n_in, n_out, _ptr(y), _ptr(s)),
            "gemv_iq3")
+    return y, s
+
+
+def gemv_iq3_xxs(w, grid, x, n_in: int, n_out: int) -> tuple[np.ndarray, np.ndarray]:
+    w = _u8(w)
+    x = _f32(x)
+    grid = _f32(grid)
+    if w.size != n_out * (n_in // QK) * IQ3_BYTES or x.size != n_in or grid.shape != (256, 4):
+        raise ValueError("shape mismatch")
+    y = np.empty(n_out, np.float64)
+    s = np.empty(n_out, np.float64)
+    _check(lib().orc_gemv_iq3_xxs(_ptr(w), _ptr(grid), _ptr(x), n_in, n_out, _ptr(y), _ptr(s)),
+           "gemv_iq3_xxs")
     return y, s
 
 
@@ -216,6 +248,21 @@ def gemv_iq3_rows(w, grid, x, n_in: int, rows) -> tuple[np.ndarray, np.ndarray]:
     return y, s
 
 
+def gemv_iq3_xxs_rows(w, grid, x, n_in: int, rows) -> tuple[np.ndarray, np.ndarray]:
+    w = _u8(w)
+    x = _f32(x)
+    grid = _f32(grid)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    row_bytes = (n_in // QK) * IQ3_BYTES
+    if rows.size == 0 or rows.min() < 0 or (rows.max() + 1) * row_bytes > w.size:
+        raise ValueError("rows out of range")
+    y = np.empty(rows.size, np.float64)
+    s = np.empty(rows.size, np.float64)
+    _check(lib().orc_gemv_iq3_xxs_rows(_ptr(w), _ptr(grid), _ptr(x), n_in, _ptr(rows),
+                                       rows.size, _ptr(y), _ptr(s)), "gemv_iq3_xxs_rows")
+    return y, s
+
+
 # ---------------------------------------------------------------- block builders (tests)
 
 def q4k_block(d_bits: int, dmin_bits: int, sc, mn, q) -> np.ndarray:
@@ -249,4 +296,19 @@ def iq3_block(idx, words, d_bits: int) -> np.ndarray:
         for k in range(4):
             b[64 + 4 * ib + k] = (w >> (8 * k)) & 0xFF
     b[96], b[97] = d_bits & 0xFF, (d_bits >> 8) & 0xFF
+    return b
+
+
+def iq3_xxs_block(idx, words, d_bits: int) -> np.ndarray:
+    """One 98-byte IQ3_XXS block in llama.cpp's order: fp16 d, 64 grid indices,
+    8 uint32 words (little-endian)."""
+    idx = np.asarray(idx, dtype=np.int64).reshape(64)
+    words = np.asarray(words, dtype=np.uint64).reshape(8)
+    b = np.zeros(IQ3_BYTES, np.uint8)
+    b[0], b[1] = d_bits & 0xFF, (d_bits >> 8) & 0xFF
+    b[2:66] = idx.astype(np.uint8)
+    for ib in range(8):
+        w = int(words[ib])
+        for k in range(4):
+            b[66 + 4 * ib + k] = (w >> (8 * k)) & 0xFF
     return b

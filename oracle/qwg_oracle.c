@@ -9,6 +9,8 @@
  * Citations name the page and the listing or passage on it:
  *   [picoLM]  "用 Python 重写 picoLM", dequantize_q4_K listing
  *   [iq3pack] iq3_pack.py page: module docstring (byte layout) and decode()
+ *   [codebook] codebook.py page: the format table of its module docstring,
+ *             get_d, get_s, eff_np and dequant (llama.cpp's IQ3_XXS blocks)
  */
 #include "qwg_oracle.h"
 
@@ -171,6 +173,65 @@ int orc_dequant_iq3(const uint8_t *src, const float *grid, int64_t n, float *dst
     return 0;
 }
 
+/*
+ * [codebook] IQ3_XXS in llama.cpp's own byte order, 98 bytes per 256 weights:
+ * the fp16 d at bytes 0..1 (get_d), the sub-scale s of 32-weight sub-block ib
+ * in the top four bits of the little-endian uint32 at bytes 66+4ib (get_s),
+ * and the codes in the remaining bytes. The effective sub-block scale is
+ * eff = d * (0.5 + s) * 0.5, formed in fp32 in that order (eff_np), and each
+ * weight is its integer value v (a codebook entry times its sign) times eff,
+ * one fp32 product (dequant).
+ *
+ * The page leaves the code bytes to llama.cpp; the reading taken here is the
+ * same field structure as the 98-byte container of the iq3_pack.py page with
+ * the page's positions: the 64 grid indices at bytes 2..65 (index 8ib + t/4
+ * for weight t of sub-block ib), and the signs in the low 28 bits of each
+ * uint32, seven per group of eight weights (bit 7l+j negates weight 8l+j),
+ * the eighth chosen so that a group has an even number of negatives (the
+ * page's free-code section states that rule). The grid is the codebook as the
+ * caller passes it (for llama.cpp's table, its integer entries 4..62).
+ */
+static void iq3_xxs_block(const uint8_t *b, const float *grid, float *out)
+{
+    float d = orc_f16_to_f32((uint16_t)(b[0] | (b[1] << 8)));
+    for (int ib = 0; ib < 8; ++ib) {
+        const uint8_t *wp = b + 66 + 4 * ib;
+        uint32_t word = (uint32_t)wp[0] | ((uint32_t)wp[1] << 8) | ((uint32_t)wp[2] << 16) |
+                        ((uint32_t)wp[3] << 24);
+        uint32_t s = word >> 28;
+        float eff = d * (0.5f + (float)s);
+        eff = eff * 0.5f;
+        for (int l = 0; l < 4; ++l) {
+            uint32_t seven = (word >> (7 * l)) & 0x7F;
+            int negatives = 0;
+            for (int j = 0; j < 8; ++j) {
+                int neg;
+                if (j < 7) {
+                    neg = (seven >> j) & 1;
+                    negatives += neg;
+                } else {
+                    neg = negatives & 1;   /* makes the count even */
+                }
+                int t = 8 * l + j;
+                float entry = grid[4 * b[2 + 8 * ib + t / 4] + t % 4];
+                float v = neg ? -entry : entry;
+                out[32 * ib + t] = v * eff;
+            }
+        }
+    }
+}
+
+int orc_dequant_iq3_xxs(const uint8_t *src, const float *grid, int64_t n, float *dst)
+{
+    if (!src || !grid || !dst)
+        return 1;
+    if (n < 0 || n % ORC_QK)
+        return 2;
+    for (int64_t ib = 0; ib < n / ORC_QK; ++ib)
+        iq3_xxs_block(src + ORC_IQ3_BYTES * ib, grid, dst + ORC_QK * ib);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ GEMV / GEMM */
 
 static int g_threads = 0;
@@ -290,4 +351,24 @@ int orc_gemv_iq3_rows(const uint8_t *w, const float *grid, const float *x, int64
     if (nrows < 1)
         return 2;
     return gemm_generic(iq3_block, ORC_IQ3_BYTES, w, grid, x, n_in, 1, 1, rows, nrows, y, s);
+}
+
+int orc_gemv_iq3_xxs(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                     int64_t n_out, double *y, double *s)
+{
+    if (!grid)
+        return 1;
+    return gemm_generic(iq3_xxs_block, ORC_IQ3_BYTES, w, grid, x, n_in, n_out, 1, NULL, 0, y,
+                        s);
+}
+
+int orc_gemv_iq3_xxs_rows(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                          const int64_t *rows, int64_t nrows, double *y, double *s)
+{
+    if (!rows || !grid)
+        return 1;
+    if (nrows < 1)
+        return 2;
+    return gemm_generic(iq3_xxs_block, ORC_IQ3_BYTES, w, grid, x, n_in, 1, 1, rows, nrows, y,
+                        s);
 }

@@ -11,6 +11,8 @@
  *           dequantize_q4_K listing: 144-byte super-block of 256 weights.
  *   IQ3   - the iq3_pack.py page, module docstring (layout) and decode():
  *           98-byte grouped container of 256 weights.
+ *   IQ3_XXS - the codebook.py page (format table, get_d, get_s, eff_np,
+ *           dequant): the same 98 bytes in llama.cpp's order (d first).
  *
  * Every entry point returns 0 on success, 2 when a size is invalid
  * (n % 256 != 0, n < 0, n_out < 1, batch outside 1..8), 1 on a NULL pointer.
@@ -38,6 +40,7 @@ void orc_q4k_pack_scales(const uint8_t sc[8], const uint8_t mn[8], uint8_t p[12]
 /* Decode n weights (n % 256 == 0) from n/256 consecutive blocks into fp32. */
 int orc_dequant_q4k(const uint8_t *src, int64_t n, float *dst);
 int orc_dequant_iq3(const uint8_t *src, const float *grid, int64_t n, float *dst);
+int orc_dequant_iq3_xxs(const uint8_t *src, const float *grid, int64_t n, float *dst);
 
 /*
  * y[n] = sum_k w[n,k] * x[k] in fp64 over the fp32 dequantized row, k ascending;
@@ -48,6 +51,8 @@ int orc_gemv_q4k(const uint8_t *w, const float *x, int64_t n_in, int64_t n_out,
                  double *y, double *s);
 int orc_gemv_iq3(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
                  int64_t n_out, double *y, double *s);
+int orc_gemv_iq3_xxs(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                     int64_t n_out, double *y, double *s);
 
 /* Y[b, n] = sum_k w[n,k] * X[b,k], X [batch, n_in], Y and S [batch, n_out]. */
 int orc_gemm_q4k(const uint8_t *w, const float *x, int64_t n_in, int64_t n_out,
@@ -58,6 +63,8 @@ int orc_gemv_q4k_rows(const uint8_t *w, const float *x, int64_t n_in, const int6
                       int64_t nrows, double *y, double *s);
 int orc_gemv_iq3_rows(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
                       const int64_t *rows, int64_t nrows, double *y, double *s);
+int orc_gemv_iq3_xxs_rows(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                          const int64_t *rows, int64_t nrows, double *y, double *s);
 
 /* OpenMP thread count used by the GEMVs (rows are independent, so the result
  * does not depend on it). */

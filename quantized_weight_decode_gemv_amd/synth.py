@@ -18,6 +18,10 @@ role])``, role 0 = weight fields, 1 = activations, 2 = IQ3 grid):
 * IQ3 grid: 256 distinct 4-tuples over the eight magnitudes
   {2, 6, 10, 14, 18, 22, 26, 31} (the published grid is absent; this is a
   stand-in with the same value range), fp32 [256, 4].
+* IQ3_XXS blocks in llama.cpp's byte order: the same draws as the IQ3 blocks of
+  the same (cfg, tensor), placed as d (bytes 0-1), indices (2-65), words
+  (66-97); their grid is the IQ3 grid doubled (integer entries 4..62, the
+  convention of llama.cpp's own table).
 * Activations: fp32 standard normal.
 
 The published TinyLlama-1.1B Q4_K_M weights and real IQ3 tensors are absent; the
@@ -73,6 +77,22 @@ def iq3_weights(n_out: int, n_in: int, cfg: int, tensor: int) -> np.ndarray:
     blocks[:, 64:96] = words.view(np.uint8).reshape(nb, 32)
     blocks[:, 96:98] = d.view(np.uint8).reshape(nb, 2)
     return blocks.reshape(n_out, -1)
+
+
+def iq3_xxs_weights(n_out: int, n_in: int, cfg: int, tensor: int) -> np.ndarray:
+    """uint8 [n_out, n_in/256*98], llama.cpp byte order; the bytes of
+    iq3_weights(n_out, n_in, cfg, tensor), block by block, in that order."""
+    src = iq3_weights(n_out, n_in, cfg, tensor).reshape(-1, IQ3_BYTES)
+    blocks = np.empty_like(src)
+    blocks[:, 0:2] = src[:, 96:98]
+    blocks[:, 2:66] = src[:, 0:64]
+    blocks[:, 66:98] = src[:, 64:96]
+    return blocks.reshape(n_out, -1)
+
+
+def iq3_xxs_grid(cfg: int = 4, tensor: int = 0) -> np.ndarray:
+    """fp32 [256, 4]: iq3_grid doubled (entries in {4, 12, ..., 62})."""
+    return iq3_grid(cfg, tensor) * np.float32(2)
 
 
 def iq3_grid(cfg: int = 4, tensor: int = 0) -> np.ndarray:

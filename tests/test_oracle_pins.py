@@ -245,6 +245,118 @@ def test_iq3_fp32_equals_exact():
                     assert w[r, sb, 32 * ib + t] == exact
 
 
+# ---------------------------------------------------------------- IQ3_XXS, llama.cpp byte order
+# Pins from the codebook.py page: its format table (98 bytes; eff = d*(0.5+s)*0.5;
+# d at bytes 0-1; s in the top four bits of the uint32s at bytes 66-97; the
+# decode unit 0.25 = eff at d = 1, s = 0), the even-negatives sign rule of its
+# free-code section, and the iq3_pack.py page's statement that its container is
+# the same scheme with the grid stored halved.
+
+def _xxs(idx, words, d_bits, grid):
+    return oracle.dequant_iq3_xxs(oracle.iq3_xxs_block(idx, words, d_bits), grid, 256)
+
+
+def test_iq3_xxs_unit_and_scale_table():
+    grid = np.zeros((256, 4), np.float32)
+    grid[0] = [4, 12, 20, 62]
+    mags = np.tile([4, 12, 20, 62], 8).astype(np.float64)
+    # d = 1, s = 0: every weight is 0.25 x its codebook value (the page's decode unit)
+    w = _xxs(np.zeros(64), [0] * 8, 0x3C00, grid)
+    assert np.array_equal(w, np.tile(0.25 * mags, 8).astype(np.float32))
+    # s = 0..15 across two blocks: eff = (0.5 + s) * 0.5 per sub-block, d = 2
+    for first in (0, 8):
+        w = _xxs(np.zeros(64), [(first + ib) << 28 for ib in range(8)], 0x4000, grid)
+        for ib in range(8):
+            s = first + ib
+            assert np.array_equal(w[32 * ib:32 * ib + 32],
+                                  (2.0 * (0.5 + s) * 0.5 * mags).astype(np.float32))
+
+
+def test_iq3_xxs_field_positions():
+    grid = np.arange(1024, dtype=np.float32).reshape(256, 4) % 61 + 1
+    idx = np.zeros(64, int)
+    idx[8 * 5 + 3] = 200        # sub-block 5, weights 12..15
+    b = oracle.iq3_xxs_block(idx, [0] * 8, 0x3C00)
+    assert b[2 + 8 * 5 + 3] == 200 and b[0] == 0x00 and b[1] == 0x3C
+    w = oracle.dequant_iq3_xxs(b, grid, 256)
+    assert np.array_equal(w[32 * 5 + 12:32 * 5 + 16], 0.25 * grid[200])
+    assert np.array_equal(np.delete(w, np.arange(172, 176)),
+                          np.delete(np.tile(0.25 * np.tile(grid[0], 8), 8), np.arange(172, 176)))
+    # s of sub-block 6 lives in the top nibble of byte 66 + 4*6 + 3
+    b = oracle.iq3_xxs_block(np.zeros(64), [0] * 8, 0x3C00)
+    b[66 + 4 * 6 + 3] = 0x30
+    w = oracle.dequant_iq3_xxs(b, grid, 256)
+    assert np.array_equal(w[192:224], (3.5 * 0.5 * np.tile(grid[0], 8)).astype(np.float32))
+    assert np.array_equal(w[:192], np.tile(0.25 * grid[0], 48))
+    # d is the fp16 at bytes 0-1: 0x4400 = 4.0
+    b[0], b[1] = 0x00, 0x44
+    assert np.array_equal(oracle.dequant_iq3_xxs(b, grid, 256), 4.0 * w)
+
+
+def test_iq3_xxs_signs_even_negatives_exhaustive():
+    grid = np.full((256, 4), 4.0, np.float32)
+    for l in range(4):
+        for seven in range(128):
+            words = [0] * 8
+            words[2] = seven << (7 * l)
+            w = _xxs(np.zeros(64), words, 0x3C00, grid)
+            neg = w[64 + 8 * l: 64 + 8 * l + 8] < 0
+            assert neg.sum() % 2 == 0
+            assert list(neg[:7]) == [bool((seven >> j) & 1) for j in range(7)]
+            assert (w < 0).sum() == neg.sum()
+
+
+def test_iq3_xxs_is_the_iq3_container_with_a_doubled_grid():
+    # Same random fields in both orders; the llama.cpp convention's grid is the
+    # container's grid doubled, so every weight doubles exactly.
+    n_out, n_in = 6, 768
+    fmt5 = synth.iq3_weights(n_out, n_in, 91, 3)
+    xxs = synth.iq3_xxs_weights(n_out, n_in, 91, 3)
+    a = fmt5.reshape(-1, 98)
+    b = xxs.reshape(-1, 98)
+    assert np.array_equal(b[:, 0:2], a[:, 96:98]) and np.array_equal(b[:, 2:66], a[:, 0:64])
+    assert np.array_equal(b[:, 66:98], a[:, 64:96])
+    w5 = oracle.dequant_iq3(fmt5, synth.iq3_grid(), n_out * n_in)
+    wx = oracle.dequant_iq3_xxs(xxs, synth.iq3_xxs_grid(), n_out * n_in)
+    assert np.array_equal(wx, 2 * w5)
+    # and with the same grid passed to both, the weights agree exactly
+    assert np.array_equal(oracle.dequant_iq3_xxs(xxs, synth.iq3_grid(), n_out * n_in), w5)
+
+
+def test_iq3_xxs_fp32_equals_exact():
+    grid = synth.iq3_xxs_grid()
+    blocks = synth.iq3_xxs_weights(8, 512, 99, 2)
+    w = oracle.dequant_iq3_xxs(blocks, grid, 8 * 512).reshape(8, 2, 256)
+    for r in range(8):
+        for sb in range(2):
+            b = blocks[r, 98 * sb: 98 * sb + 98]
+            d = float(b[0:2].view(np.float16)[0])
+            for ib in range(8):
+                word = int(b[66 + 4 * ib: 70 + 4 * ib].view("<u4")[0])
+                s = word >> 28
+                for t in (0, 6, 7, 14, 25, 31):
+                    l, j = t // 8, t % 8
+                    seven = (word >> (7 * l)) & 0x7F
+                    neg = bin(seven).count("1") % 2 if j == 7 else (seven >> j) & 1
+                    v = (-1 if neg else 1) * grid[b[2 + 8 * ib + t // 4], t % 4]
+                    assert w[r, sb, 32 * ib + t] == v * d * (0.5 + s) * 0.5
+
+
+def test_gemv_iq3_xxs_matches_numpy_matmul():
+    n_out, n_in = 11, 1024
+    grid = synth.iq3_xxs_grid()
+    w = synth.iq3_xxs_weights(n_out, n_in, 90, 9)
+    x = synth.activations(n_in, 90, 9)
+    deq = oracle.dequant_iq3_xxs(w, grid, n_out * n_in).reshape(n_out, n_in).astype(np.float64)
+    y, s = oracle.gemv_iq3_xxs(w, grid, x, n_in, n_out)
+    sref = np.abs(deq) @ np.abs(x.astype(np.float64))
+    assert np.allclose(y, deq @ x.astype(np.float64), rtol=0, atol=1e-12 * sref.max())
+    assert np.allclose(s, sref, rtol=1e-13)
+    rows = np.array([10, 0, 4])
+    yr, sr = oracle.gemv_iq3_xxs_rows(w, grid, x, n_in, rows)
+    assert np.array_equal(yr, y[rows]) and np.array_equal(sr, s[rows])
+
+
 # ---------------------------------------------------------------- GEMV / GEMM
 
 def _q4k_case(n_out, n_in, seed):
