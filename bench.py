@@ -26,10 +26,11 @@ back-to-back launches); and the CPU oracle's throughput on the host cores
 (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--headline-only]
-       python bench.py --workload iq3_stream|lm_head [--steps K] [--warmup W]
+       python bench.py --workload iq3_stream|iq3_xxs|lm_head [--steps K] [--warmup W]
 The second form measures the other hot-path rows on their own (one JSON line each, for the
 record and for profiling): "iq3_stream" = the same 155 GEMV shapes in the IQ3 container as one
-grouped launch (IQ3 tile layout; the row-major launch beside it); "lm_head" = the 32000x2048 Q4_K LM head at batch 1..8 (qwg_gemv_q4k,
+grouped launch (IQ3 tile layout; the row-major launch beside it); "iq3_xxs" = IQ3_XXS blocks in
+llama.cpp's byte order (single GEMVs row-major and repacked, and the stream repacked); "lm_head" = the 32000x2048 Q4_K LM head at batch 1..8 (qwg_gemv_q4k,
 qwg_gemv_q4k_tiled, qwg_gemm_q4k), cycling over enough weight copies that every launch streams
 from HBM rather than the last-level cache.
 """
@@ -82,7 +83,8 @@ def parse():
                     help="minimum CPU time budget for the oracle baseline")
     ap.add_argument("--print-kernel-hash", action="store_true",
                     help="print the hash of the kernel sources the traffic figure is tied to")
-    ap.add_argument("--workload", default="q4k_stream", choices=["q4k_stream", "iq3_stream", "lm_head"],
+    ap.add_argument("--workload", default="q4k_stream",
+                    choices=["q4k_stream", "iq3_stream", "iq3_xxs", "lm_head"],
                     help="q4k_stream: the headline (default); the others: see the module docstring")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline launch (no row-major, layered or per-call "
@@ -123,6 +125,9 @@ def main():
         return
     if args.workload == "lm_head":
         bench_lm_head(args)
+        return
+    if args.workload == "iq3_xxs":
+        bench_iq3_xxs(args)
         return
 
     import numpy as np
@@ -324,6 +329,75 @@ def bench_iq3_stream(args):
                    "algorithmic_bytes_per_step": step_bytes,
                    "row_major_us": round(us_rows, 2),
                    "row_major_GBs": round(step_bytes / us_rows / 1e3, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "kernel": "iq3_stream_kernel<8,2,tile layout> (grouped)",
+                     "kernel_us": round(us, 2)}}), flush=True)
+
+
+def bench_iq3_xxs(args):
+    """IQ3_XXS blocks in llama.cpp's byte order: the two single GEMV shapes of the
+    IQ3 configuration (5632x2048, 2048x5632; cold weights, copies cycled), row-major
+    in that order, row-major in the container order, and repacked to the tile
+    layout; then the per-token stream's 155 GEMVs repacked from that order as one
+    grouped launch."""
+    import torch
+    import quantized_weight_decode_gemv_amd as qwg
+    from quantized_weight_decode_gemv_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    grid = torch.from_numpy(synth.iq3_xxs_grid()).to(dev)
+    copies = 64  # 64 x 4.4 MB: more than the last-level cache
+    singles = {}
+    i = [0]
+
+    def cycle(fn):
+        def run():
+            fn(i[0] % copies)
+            i[0] += 1
+        return run
+
+    for p in synth.config(4):
+        wx = torch.from_numpy(synth.iq3_xxs_weights(p.n_out, p.n_in, p.cfg, p.tensor)).to(dev)
+        w5 = torch.from_numpy(synth.weights(p)).to(dev)
+        x = torch.from_numpy(synth.inputs(p)).to(dev)
+        y = torch.empty(p.n_out, device=dev)
+        WX = wx.reshape(1, -1).repeat(copies, 1)
+        W5 = w5.reshape(1, -1).repeat(copies, 1)
+        WT = torch.stack([qwg.pack_iq3_xxs_tiles(wx, p.n_in)] * copies)
+        us_x = _event_us(cycle(lambda k: qwg.gemv_iq3_xxs(WX[k], x, grid, out=y)), stream,
+                         args.steps, args.warmup)
+        us_5 = _event_us(cycle(lambda k: qwg.gemv_iq3(W5[k], x, grid, out=y)), stream,
+                         args.steps, args.warmup)
+        us_t = _event_us(cycle(lambda k: qwg.gemv_iq3_tiled(WT[k], x, grid, p.n_out, out=y)),
+                         stream, args.steps, args.warmup)
+        b = p.algorithmic_bytes
+        singles[p.name] = {"xxs_rows_us": round(us_x, 2), "xxs_rows_GBs": round(b / us_x / 1e3, 1),
+                           "container_rows_us": round(us_5, 2),
+                           "xxs_tiled_us": round(us_t, 2), "xxs_tiled_GBs": round(b / us_t / 1e3, 1)}
+        del WX, W5, WT
+
+    probs = synth.config(6)
+    X = [torch.from_numpy(synth.inputs(p)).to(dev) for p in probs]
+    Y = [torch.empty(p.n_out, dtype=torch.float32, device=dev) for p in probs]
+    WT = [qwg.pack_iq3_xxs_tiles(torch.from_numpy(
+        synth.iq3_xxs_weights(p.n_out, p.n_in, p.cfg, p.tensor)).to(dev), p.n_in) for p in probs]
+    group = qwg.Iq3Group(zip(WT, X, Y), grid, tiled=True)
+    step_bytes = sum(p.algorithmic_bytes for p in probs)
+    us = _event_us(lambda: group.run(stream), stream, args.steps, args.warmup)
+    gbs = step_bytes / us / 1e3
+    print(json.dumps({
+        "metric": "effective HBM GB/s, IQ3_XXS (llama.cpp byte order) GEMV stream, batch 1",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 4), "higher_is_better": True,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "TinyLlama-1.1B-shaped per-token stream of IQ3_XXS blocks in "
+                               "llama.cpp's byte order, repacked once (qwg_pack_iq3_xxs_tiles) "
+                               "and run as one grouped launch; single GEMVs of the IQ3 "
+                               "configuration beside it",
+                   "algorithmic_bytes_per_step": step_bytes, "singles": singles},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "kernel": "iq3_stream_kernel<8,2,tile layout> (grouped)",

@@ -13,6 +13,13 @@
  *         eighth sign is their parity, 4-bit sub-scale code in bits 28-31) and
  *         fp16 d (96-97). Weight = grid[idx][t%4] * sign * d*(0.5+code)*0.5,
  *         grid magnitudes in weight units.
+ *   IQ3_XXS  codebook.py page, format table of its docstring, get_d, get_s,
+ *         eff_np and dequant: llama.cpp's own IQ3_XXS block, the same 98 bytes
+ *         in another order = fp16 d (0-1), 64 grid indices (2-65), eight
+ *         uint32 words (66-97, sub-scale s in bits 28-31). Weight = v * eff with
+ *         eff = d*(0.5+s)*0.5 and v = grid[idx][t%4] * sign, the grid being
+ *         llama.cpp's table as is (entries 4..62; the iq3_pack container stores
+ *         the same scheme with the grid halved).
  *
  * Common conventions
  *   - Every pointer argument except `stream` is a DEVICE pointer (HIP memory
@@ -57,6 +64,7 @@ extern "C" {
 /* format ids */
 #define QWG_FMT_Q4K 0
 #define QWG_FMT_IQ3 1
+#define QWG_FMT_IQ3_XXS 2   /* IQ3 blocks in llama.cpp's byte order */
 
 #define QWG_QK 256
 #define QWG_Q4K_BLOCK_BYTES 144
@@ -72,7 +80,7 @@ int qwg_version(void);
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *qwg_strerror(int status);
 
-/* Bytes per row of `n_in` weights in format `fmt` ((n_in/256) * {144, 98}),
+/* Bytes per row of `n_in` weights in format `fmt` ((n_in/256) * {144, 98, 98}),
  * or -QWG_ERR_SHAPE / -QWG_ERR_FORMAT. */
 int64_t qwg_row_bytes(int fmt, int64_t n_in);
 
@@ -102,6 +110,16 @@ int qwg_dequant_q4k(const void *src, float *dst, int64_t n, void *stream);
 int qwg_dequant_iq3(const void *src, const float *grid, float *dst, int64_t n, void *stream);
 
 /*
+ * IQ3_XXS dequantization in llama.cpp's byte order (codebook.py page: format
+ * table, get_d, get_s, eff_np, dequant). Arguments, alignment and errors as
+ * qwg_dequant_iq3; grid is the codebook in the caller's units (llama.cpp's
+ * table: entries 4..62). Bit-identical to (sign * grid[idx][t%4]) *
+ * ((d*(0.5+s))*0.5) rounded to fp32 (the scale factor is exact in fp32).
+ */
+int qwg_dequant_iq3_xxs(const void *src, const float *grid, float *dst, int64_t n,
+                        void *stream);
+
+/*
  * y[r] = sum_k W[r,k] x[k] for Q4_K weights (the fused dequantize-and-dot of
  * picoLM's matmul for quantized rows).
  * w: n_out rows of n_in/256 Q4_K blocks, 16-byte aligned.
@@ -127,6 +145,14 @@ int qwg_gemv_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
  */
 int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                  int64_t n_out, void *stream);
+
+/*
+ * y = W x for IQ3_XXS weights in llama.cpp's byte order (codebook.py page, as
+ * qwg_dequant_iq3_xxs). Arguments, alignment, the fp16-exact grid requirement,
+ * the reads of w, shape limits and accuracy as qwg_gemv_iq3.
+ */
+int qwg_gemv_iq3_xxs(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                     int64_t n_out, void *stream);
 
 /*
  * qwg_gemv_iq3 with an explicit work decomposition (tuning and testing):
@@ -182,7 +208,7 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
  * The bytes of every block are kept, only regrouped.
  *
  * qwg_tiled_bytes: bytes of the tile layout (ceil(n_out/64)*64 rows) for
- * QWG_FMT_Q4K or QWG_FMT_IQ3, or a negative status.
+ * QWG_FMT_Q4K, QWG_FMT_IQ3 or QWG_FMT_IQ3_XXS, or a negative status.
  * qwg_pack_q4k_tiles: src (row-major, as qwg_gemv_q4k takes it) -> dst (tile
  * layout, qwg_tiled_bytes bytes); both 16-byte aligned, must not overlap.
  * qwg_gemv_q4k_tiled: qwg_gemv_q4k on tile-layout weights (same arguments,
@@ -191,6 +217,10 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
  * 16-byte aligned).
  * qwg_gemv_iq3_tiled: qwg_gemv_iq3 on tile-layout weights (w 16-byte aligned;
  * otherwise the same arguments and accuracy).
+ * qwg_pack_iq3_xxs_tiles: as qwg_pack_iq3_tiles for row-major IQ3_XXS blocks
+ * in llama.cpp's order; the result is the same IQ3 tile layout (each field
+ * moved to its place), so qwg_gemv_iq3_tiled and the tiled IQ3 groups take
+ * it, with llama.cpp's grid.
  */
 int64_t qwg_tiled_bytes(int fmt, int64_t n_in, int64_t n_out);
 int qwg_pack_q4k_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
@@ -199,6 +229,8 @@ int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, in
 int qwg_pack_iq3_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
 int qwg_gemv_iq3_tiled(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                        int64_t n_out, void *stream);
+int qwg_pack_iq3_xxs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out,
+                           void *stream);
 
 /*
  * Grouped GEMV: many independent GEMVs of one format in one launch (one grid

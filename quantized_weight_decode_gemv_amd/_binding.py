@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(PKG, "libqwg.so")
 
 QWG_FMT_Q4K = 0
 QWG_FMT_IQ3 = 1
+QWG_FMT_IQ3_XXS = 2   # IQ3 blocks in llama.cpp's byte order (d, indices, words)
 QK = 256
 Q4K_BYTES = 144
 IQ3_BYTES = 98
@@ -45,6 +46,9 @@ def lib() -> ctypes.CDLL:
         L.qwg_plan_splits.restype = I
         L.qwg_dequant_q4k.argtypes = [P, P, I64, P]
         L.qwg_dequant_iq3.argtypes = [P, P, P, I64, P]
+        L.qwg_dequant_iq3_xxs.argtypes = [P, P, P, I64, P]
+        L.qwg_gemv_iq3_xxs.argtypes = [P, P, P, P, I64, I64, P]
+        L.qwg_pack_iq3_xxs_tiles.argtypes = [P, P, I64, I64, P]
         L.qwg_gemv_q4k.argtypes = [P, P, P, I64, I64, P]
         L.qwg_gemv_iq3.argtypes = [P, P, P, P, I64, I64, P]
         L.qwg_gemm_q4k.argtypes = [P, P, P, I64, I64, I, P]
@@ -134,6 +138,16 @@ def dequant_q4k(w: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tenso
 
 def dequant_iq3(w: torch.Tensor, grid: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """Packed IQ3 blocks (uint8, 98 bytes per 256 weights) + fp32 grid [256, 4] -> fp32."""
+    return _dequant_iq3(w, grid, out, "qwg_dequant_iq3")
+
+
+def dequant_iq3_xxs(w: torch.Tensor, grid: torch.Tensor,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """IQ3_XXS blocks in llama.cpp's byte order + its grid (fp32 [256, 4]) -> fp32."""
+    return _dequant_iq3(w, grid, out, "qwg_dequant_iq3_xxs")
+
+
+def _dequant_iq3(w, grid, out, fn: str) -> torch.Tensor:
     _dev(w, "w", torch.uint8)
     _dev(grid, "grid", torch.float32)
     if grid.shape != (256, 4):
@@ -146,8 +160,7 @@ def dequant_iq3(w: torch.Tensor, grid: torch.Tensor, out: torch.Tensor | None = 
     _dev(out, "out", torch.float32)
     if out.numel() != n:
         raise ValueError("out has the wrong size")
-    _check(lib().qwg_dequant_iq3(w.data_ptr(), grid.data_ptr(), out.data_ptr(), n, _stream(w)),
-           "qwg_dequant_iq3")
+    _check(getattr(lib(), fn)(w.data_ptr(), grid.data_ptr(), out.data_ptr(), n, _stream(w)), fn)
     return out
 
 
@@ -209,6 +222,16 @@ def gemv_q4k_tiled(w: torch.Tensor, x: torch.Tensor, n_out: int,
 def pack_iq3_tiles(w: torch.Tensor, n_in: int, out: torch.Tensor | None = None) -> torch.Tensor:
     """Row-major IQ3 weights (uint8, n_out rows) -> the IQ3 tile layout that
     gemv_iq3_tiled and tiled IQ3 groups take."""
+    return _pack_iq3(w, n_in, out, "qwg_pack_iq3_tiles")
+
+
+def pack_iq3_xxs_tiles(w: torch.Tensor, n_in: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-major IQ3_XXS weights in llama.cpp's byte order -> the same IQ3 tile
+    layout (gemv_iq3_tiled and tiled IQ3 groups take it, with llama.cpp's grid)."""
+    return _pack_iq3(w, n_in, out, "qwg_pack_iq3_xxs_tiles")
+
+
+def _pack_iq3(w, n_in, out, fn: str) -> torch.Tensor:
     n_out = _weights(w, n_in, IQ3_BYTES)
     nbytes = tiled_bytes(n_in, n_out, QWG_FMT_IQ3)
     if out is None:
@@ -216,8 +239,7 @@ def pack_iq3_tiles(w: torch.Tensor, n_in: int, out: torch.Tensor | None = None) 
     _dev(out, "out", torch.uint8)
     if out.numel() != nbytes:
         raise ValueError("out has the wrong size")
-    _check(lib().qwg_pack_iq3_tiles(out.data_ptr(), w.data_ptr(), n_in, n_out, _stream(w)),
-           "qwg_pack_iq3_tiles")
+    _check(getattr(lib(), fn)(out.data_ptr(), w.data_ptr(), n_in, n_out, _stream(w)), fn)
     return out
 
 
@@ -265,6 +287,24 @@ def gemv_iq3(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
     else:
         _check(lib().qwg_gemv_iq3(out.data_ptr(), x.data_ptr(), w.data_ptr(), grid.data_ptr(), n_in,
                                   n_out, _stream(x)), "qwg_gemv_iq3")
+    return out
+
+
+def gemv_iq3_xxs(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x for IQ3_XXS weights in llama.cpp's byte order; w uint8 [n_out,
+    row_bytes] (or flat), x fp32 [n_in], grid fp32 [256, 4] (llama.cpp's table)."""
+    _dev(x, "x", torch.float32)
+    _grid(grid)
+    n_in = x.numel()
+    n_out = _weights(w, n_in, IQ3_BYTES)
+    if out is None:
+        out = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n_out:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_gemv_iq3_xxs(out.data_ptr(), x.data_ptr(), w.data_ptr(), grid.data_ptr(),
+                                  n_in, n_out, _stream(x)), "qwg_gemv_iq3_xxs")
     return out
 
 

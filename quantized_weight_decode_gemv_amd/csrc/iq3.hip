@@ -39,6 +39,17 @@ __device__ __forceinline__ uint32_t iq3_signs(uint32_t word) {
     return u | ((p & 0x01010101u) << 7);
 }
 
+// Field offsets of a 98-byte block in the two byte orders: the iq3_pack
+// container (indices at 0, words at 64, d at 96) and llama.cpp's IQ3_XXS
+// (d at 0, indices at 2, words at 66), which the codebook.py page's format
+// table describes. The fields and the decode are the same.
+struct Iq3Order {
+    int idx, words, d;
+};
+__device__ __forceinline__ Iq3Order iq3_order(bool xxs) {
+    return xxs ? Iq3Order{2, 66, 0} : Iq3Order{0, 64, 96};
+}
+
 // ------------------------------------------------------------------ dequant
 
 // One wavefront per block: lane l produces weights 4l..4l+3, i.e. the four
@@ -46,7 +57,8 @@ __device__ __forceinline__ uint32_t iq3_signs(uint32_t word) {
 __global__ __launch_bounds__(256) void iq3_dequant_kernel(const uint8_t *__restrict__ src,
                                                           const float *__restrict__ grid,
                                                           float *__restrict__ dst,
-                                                          int64_t nblocks) {
+                                                          int64_t nblocks, bool xxs) {
+    const Iq3Order fo = iq3_order(xxs);
     const int lane = threadIdx.x & 63;
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
     const int ib = lane >> 3;         // sub-block
@@ -54,12 +66,12 @@ __global__ __launch_bounds__(256) void iq3_dequant_kernel(const uint8_t *__restr
     for (int64_t blk = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
          blk < nblocks; blk += nwaves) {
         const uint8_t *b = src + blk * kIq3Bytes;
-        const float d = h2f_lo(load_u16(b + 96));
-        const uint32_t word = load_u32_a2(b + 64 + 4 * ib);
+        const float d = h2f_lo(load_u16(b + fo.d));
+        const uint32_t word = load_u32_a2(b + fo.words + 4 * ib);
         const uint32_t code = word >> 28;
         const float db = __fmul_rn(__fmul_rn(d, 0.5f + (float)code), 0.5f);
         const uint32_t s8 = iq3_signs(word);
-        const float4 g = *(const float4 *)(grid + 4 * b[lane]);
+        const float4 g = *(const float4 *)(grid + 4 * b[fo.idx + lane]);
         float4 o;
         o.x = __fmul_rn(((s8 >> (t0 + 0)) & 1u) ? -g.x : g.x, db);
         o.y = __fmul_rn(((s8 >> (t0 + 1)) & 1u) ? -g.y : g.y, db);
@@ -194,7 +206,8 @@ struct Iq3Raw {
     uint32_t d16;
 };
 
-// From a row window in LDS: `win` = window + (sh & 12), sh = block offset in it.
+// From a row window in LDS: `win` = window + (sh & 12), sh = block offset in it
+// (even). Container order: the fields start at block bytes 0, 64 and 96.
 template <int G>
 __device__ __forceinline__ void iq3_fetch(const uint8_t *win, uint32_t sh, Iq3Raw &r) {
     const uint32_t *p = (const uint32_t *)win;
@@ -211,6 +224,30 @@ __device__ __forceinline__ void iq3_fetch(const uint8_t *win, uint32_t sh, Iq3Ra
     r.d16 = dw >> ((sh & 2u) << 3);
 }
 
+// The same for llama.cpp's order (d at 0, indices at 2, words at 66). The index
+// and word fields start (sh & 3) + 2 bytes into their dword runs: one dword on
+// and aligned when sh & 2 (shift 0), else 2 bytes in (shift 2). The dword
+// after each field is only needed with shift 2; the one read in its place
+// with shift 0 is never used. Every read lies inside the 112-byte window: the
+// last starts at window byte (sh & 12) + 96 <= 108.
+template <int G>
+__device__ __forceinline__ void iq3_fetch_xxs(const uint8_t *win, uint32_t sh, Iq3Raw &r) {
+    const uint32_t *p = (const uint32_t *)win;
+    const uint32_t up = (sh >> 1) & 1u;
+    const uint32_t shift = (sh + 2u) & 3u;
+    uint32_t a[5], v[3];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) a[i] = p[4 * G + up + i];
+    v[0] = p[16 + 2 * G + up];
+    v[1] = p[17 + 2 * G + up];
+    v[2] = p[18 + 2 * G];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.idx[i] = __builtin_amdgcn_alignbyte(a[i + 1], a[i], shift);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r.words[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], shift);
+    r.d16 = p[0] >> ((sh & 2u) << 3);
+}
+
 // From a tile-layout stage column (this lane's row).
 template <int G>
 __device__ __forceinline__ void iq3_fetch_tiled(const uint8_t *col, int lane, Iq3Raw &r) {
@@ -225,17 +262,19 @@ __device__ __forceinline__ void iq3_fetch_tiled(const uint8_t *col, int lane, Iq
     r.d16 = *(const uint16_t *)(col + kIq3TileD + 2 * lane);
 }
 
-// From global memory, 2 bytes at a time (the block is 2-byte aligned).
+// From global memory, 2 bytes at a time (the block is 2-byte aligned), in
+// either byte order.
 template <int G>
-__device__ __forceinline__ void iq3_fetch_direct(const uint8_t *blk, Iq3Raw &r) {
+__device__ __forceinline__ void iq3_fetch_direct(const uint8_t *blk, bool xxs, Iq3Raw &r) {
     const uint16_t *h = (const uint16_t *)blk;
+    const int hi = xxs ? 1 : 0, hw = xxs ? 33 : 32, hd = xxs ? 0 : 48;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        r.idx[i] = (uint32_t)h[8 * G + 2 * i] | ((uint32_t)h[8 * G + 2 * i + 1] << 16);
+        r.idx[i] = (uint32_t)h[hi + 8 * G + 2 * i] | ((uint32_t)h[hi + 8 * G + 2 * i + 1] << 16);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        r.words[i] = (uint32_t)h[32 + 4 * G + 2 * i] | ((uint32_t)h[32 + 4 * G + 2 * i + 1] << 16);
-    r.d16 = h[48];
+        r.words[i] = (uint32_t)h[hw + 4 * G + 2 * i] | ((uint32_t)h[hw + 4 * G + 2 * i + 1] << 16);
+    r.d16 = h[hd];
 }
 
 // acc + sum over wavefront G's 64 weights of this lane's row of w*x.
@@ -419,13 +458,18 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
                 const uint32_t sh = (rlo + (uint32_t)(kIq3Bytes * b)) & 15u;
                 const uint8_t *win = smem + C::kRing + slot_c * C::kSlot + j * C::kCol +
                                      lane * C::kWin + (sh & 12u);
+                const bool xxs = c.a.layout == kLayoutRowsXxs;
                 Iq3Raw raw;
-                iq3_fetch<G>(win, sh, raw);
+                if (xxs)
+                    iq3_fetch_xxs<G>(win, sh, raw);
+                else
+                    iq3_fetch<G>(win, sh, raw);
                 const bool head = c.head && b == 0;
                 const bool tail = c.tail && b == c.a.nb - 1;
                 if (head || tail) {   // wave-uniform, at most twice per matrix
                     if ((head && row == 0) || (tail && row == c.a.n_out - 1))
-                        iq3_fetch_direct<G>(c.a.w + (int64_t)row * c.a.row_bytes + kIq3Bytes * b, raw);
+                        iq3_fetch_direct<G>(c.a.w + (int64_t)row * c.a.row_bytes + kIq3Bytes * b,
+                                            xxs, raw);
                 }
                 acc = iq3_dot<G>(raw, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
             }
@@ -500,7 +544,8 @@ hipError_t iq3_launch(const GroupArgs &g, const GemvArgs &single, const float *g
 // 2-byte units (the source blocks are only 2-byte aligned).
 __global__ __launch_bounds__(256) void iq3_pack_tiles_kernel(const uint8_t *__restrict__ src,
                                                              uint8_t *__restrict__ dst, int nb,
-                                                             int n_out) {
+                                                             int n_out, bool xxs) {
+    const Iq3Order fo = iq3_order(xxs);
     const int b = blockIdx.x % nb;
     const int tile = blockIdx.x / nb;
     const int64_t row_bytes = (int64_t)nb * kIq3Bytes;
@@ -510,14 +555,14 @@ __global__ __launch_bounds__(256) void iq3_pack_tiles_kernel(const uint8_t *__re
         int rr, sbyte;
         if (o < kIq3TileWords) {
             rr = (o & 1023) >> 4;
-            sbyte = 16 * (o >> 10) + (o & 15);
+            sbyte = fo.idx + 16 * (o >> 10) + (o & 15);
         } else if (o < kIq3TileD) {
             const int o2 = o - kIq3TileWords;
             rr = (o2 & 511) >> 3;
-            sbyte = 64 + 8 * (o2 >> 9) + (o2 & 7);
+            sbyte = fo.words + 8 * (o2 >> 9) + (o2 & 7);
         } else {
             rr = (o - kIq3TileD) >> 1;
-            sbyte = 96;
+            sbyte = fo.d;
         }
         const int r = tile * kTileRows + rr;
         uint16_t v = 0;
@@ -534,18 +579,19 @@ constexpr int iq3_key(int w, int r) { return w * 10 + r; }
 }  // namespace
 
 hipError_t launch_iq3_dequant(const uint8_t *src, const float *grid, float *dst,
-                              int64_t nblocks, hipStream_t s) {
+                              int64_t nblocks, bool xxs, hipStream_t s) {
     int64_t groups = (nblocks + 3) / 4;
     if (groups > 65536) groups = 65536;
     hipLaunchKernelGGL(iq3_dequant_kernel, dim3((unsigned)groups), dim3(256), 0, s, src, grid,
-                       dst, nblocks);
+                       dst, nblocks, xxs);
     return hipGetLastError();
 }
 
-hipError_t launch_iq3_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, hipStream_t s) {
+hipError_t launch_iq3_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, bool xxs,
+                                 hipStream_t s) {
     const int64_t tiles = ((int64_t)n_out + kTileRows - 1) / kTileRows;
     hipLaunchKernelGGL(iq3_pack_tiles_kernel, dim3((unsigned)(tiles * nb)), dim3(256), 0, s, src,
-                       dst, nb, n_out);
+                       dst, nb, n_out, xxs);
     return hipGetLastError();
 }
 

@@ -260,18 +260,26 @@ const char *qwg_strerror(int status) {
     }
 }
 
+namespace {
+
+bool known_format(int fmt) {
+    return fmt == QWG_FMT_Q4K || fmt == QWG_FMT_IQ3 || fmt == QWG_FMT_IQ3_XXS;
+}
+
+}  // namespace
+
 int64_t qwg_row_bytes(int fmt, int64_t n_in) {
-    if (fmt != QWG_FMT_Q4K && fmt != QWG_FMT_IQ3) return -QWG_ERR_FORMAT;
+    if (!known_format(fmt)) return -QWG_ERR_FORMAT;
     if (n_in <= 0 || n_in % kQK) return -QWG_ERR_SHAPE;
     return (n_in / kQK) * (fmt == QWG_FMT_Q4K ? kQ4kBytes : kIq3Bytes);
 }
 
 int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
-    if (fmt != QWG_FMT_Q4K && fmt != QWG_FMT_IQ3) return -QWG_ERR_FORMAT;
+    if (!known_format(fmt)) return -QWG_ERR_FORMAT;
     int rc = check_gemv_shape(n_in, n_out);
     if (rc) return -rc;
     const int tiles = (int)((n_out + kTileRows - 1) / kTileRows);
-    if (fmt == QWG_FMT_IQ3) {
+    if (fmt != QWG_FMT_Q4K) {
         const int slots = iq3_stream_slots(iq3_shape(false, 0), false);
         if (slots <= 0) return -QWG_ERR_HIP;
         return iq3_splits(tiles, (int)(n_in / kQK), slots);
@@ -286,12 +294,25 @@ int qwg_dequant_q4k(const void *src, float *dst, int64_t n, void *stream) {
     return hip_status(launch_q4k_dequant((const uint8_t *)src, dst, n / kQK, (hipStream_t)stream));
 }
 
-int qwg_dequant_iq3(const void *src, const float *grid, float *dst, int64_t n, void *stream) {
+namespace {
+
+int iq3_dequant(const void *src, const float *grid, float *dst, int64_t n, bool xxs,
+                void *stream) {
     if (!src || !grid || !dst) return QWG_ERR_NULL;
     if (n <= 0 || n % kQK) return QWG_ERR_SHAPE;
     if (!aligned(src, 2) || !aligned(grid, 16) || !aligned(dst, 16)) return QWG_ERR_ALIGN;
     return hip_status(
-        launch_iq3_dequant((const uint8_t *)src, grid, dst, n / kQK, (hipStream_t)stream));
+        launch_iq3_dequant((const uint8_t *)src, grid, dst, n / kQK, xxs, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int qwg_dequant_iq3(const void *src, const float *grid, float *dst, int64_t n, void *stream) {
+    return iq3_dequant(src, grid, dst, n, false, stream);
+}
+
+int qwg_dequant_iq3_xxs(const void *src, const float *grid, float *dst, int64_t n, void *stream) {
+    return iq3_dequant(src, grid, dst, n, true, stream);
 }
 
 int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out, int batch,
@@ -364,7 +385,7 @@ int qwg_gemv_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
 }
 
 int64_t qwg_tiled_bytes(int fmt, int64_t n_in, int64_t n_out) {
-    if (fmt != QWG_FMT_Q4K && fmt != QWG_FMT_IQ3) return -QWG_ERR_FORMAT;
+    if (!known_format(fmt)) return -QWG_ERR_FORMAT;
     const int rc = check_gemv_shape(n_in, n_out);
     if (rc) return -rc;
     return ((n_out + kTileRows - 1) / kTileRows) * kTileRows * (n_in / kQK) *
@@ -397,7 +418,8 @@ int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, in
 namespace {
 
 int iq3_gemv(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
-             int64_t n_out, int waves, int splits, bool tiled, void *stream) {
+             int64_t n_out, int waves, int splits, int layout, void *stream) {
+    const bool tiled = layout == kLayoutTiles;
     if (!y || !x || !w || !grid) return QWG_ERR_NULL;
     int rc = check_gemv_shape(n_in, n_out);
     if (rc) return rc;
@@ -410,7 +432,7 @@ int iq3_gemv(float *y, const float *x, const void *w, const float *grid, int64_t
     if (splits > 1 && ((size_t)splits * a.tiles * kTileRows > kWsPartialFloats ||
                        (size_t)a.tiles > kWsCounters))
         return QWG_ERR_SHAPE;
-    a.layout = tiled ? kLayoutTiles : kLayoutRows;
+    a.layout = layout;
     const Iq3Shape sh = iq3_shape(false, waves);
     const int slots = iq3_stream_slots(sh, tiled);
     if (slots <= 0) return QWG_ERR_HIP;
@@ -432,26 +454,43 @@ int iq3_gemv(float *y, const float *x, const void *w, const float *grid, int64_t
 
 int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                     int64_t n_out, int waves, int splits, void *stream) {
-    return iq3_gemv(y, x, w, grid, n_in, n_out, waves, splits, false, stream);
+    return iq3_gemv(y, x, w, grid, n_in, n_out, waves, splits, kLayoutRows, stream);
 }
 
 int qwg_gemv_iq3(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                  int64_t n_out, void *stream) {
-    return iq3_gemv(y, x, w, grid, n_in, n_out, 0, 0, false, stream);
+    return iq3_gemv(y, x, w, grid, n_in, n_out, 0, 0, kLayoutRows, stream);
+}
+
+int qwg_gemv_iq3_xxs(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                     int64_t n_out, void *stream) {
+    return iq3_gemv(y, x, w, grid, n_in, n_out, 0, 0, kLayoutRowsXxs, stream);
 }
 
 int qwg_gemv_iq3_tiled(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                        int64_t n_out, void *stream) {
-    return iq3_gemv(y, x, w, grid, n_in, n_out, 0, 0, true, stream);
+    return iq3_gemv(y, x, w, grid, n_in, n_out, 0, 0, kLayoutTiles, stream);
 }
 
-int qwg_pack_iq3_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
+namespace {
+
+int iq3_pack(void *dst, const void *src, int64_t n_in, int64_t n_out, bool xxs, void *stream) {
     if (!dst || !src) return QWG_ERR_NULL;
     const int rc = check_gemv_shape(n_in, n_out);
     if (rc) return rc;
     if (!aligned(dst, 16) || !aligned(src, 2)) return QWG_ERR_ALIGN;
     return hip_status(launch_iq3_pack_tiles((const uint8_t *)src, (uint8_t *)dst, (int)(n_in / kQK),
-                                            (int)n_out, (hipStream_t)stream));
+                                            (int)n_out, xxs, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int qwg_pack_iq3_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
+    return iq3_pack(dst, src, n_in, n_out, false, stream);
+}
+
+int qwg_pack_iq3_xxs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
+    return iq3_pack(dst, src, n_in, n_out, true, stream);
 }
 
 // ------------------------------------------------------------------ grouped GEMV

@@ -38,9 +38,12 @@ struct GemvArgs {
 // each block column b, the 64 rows' block b back to back (9216 bytes); rows
 // past n_out in the last tile are zero blocks. Block (r, b) sits at byte
 // ((r/64)*nb + b)*9216 + (r%64)*144. Tiles (IQ3): the same column order, each
-// 6272-byte column regrouped by field (described in iq3.hip).
+// 6272-byte column regrouped by field (described in iq3.hip). RowsXxs (IQ3
+// only): row-major blocks in llama.cpp's IQ3_XXS byte order (d, indices, words)
+// instead of the container's (indices, words, d).
 constexpr int kLayoutRows = 0;
 constexpr int kLayoutTiles = 1;
+constexpr int kLayoutRowsXxs = 2;
 
 // A grouped launch: problems[map[k]] is the problem of work item k (arrays in
 // device memory). Without `tile`, the items of problem p are consecutive from
@@ -63,8 +66,9 @@ constexpr int kQ4kWavesLarge = 16;
 hipError_t launch_q4k_dequant(const uint8_t *src, float *dst, int64_t nblocks, hipStream_t s);
 // Row-major Q4_K weights -> tile layout (dst: tiles*64*nb*144 bytes).
 hipError_t launch_q4k_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, hipStream_t s);
+// xxs: blocks in llama.cpp's IQ3_XXS byte order.
 hipError_t launch_iq3_dequant(const uint8_t *src, const float *grid, float *dst,
-                              int64_t nblocks, hipStream_t s);
+                              int64_t nblocks, bool xxs, hipStream_t s);
 hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, int waves, hipStream_t s);
 hipError_t launch_q4k_group(const GroupArgs &g, int total_workgroups, int max_nb, hipStream_t s);
 // Batched GEMM on matrix cores (2 <= batch <= 8): 4-wavefront workgroups, one
@@ -92,7 +96,9 @@ int iq3_stream_slots(const Iq3Shape &sh, bool tiled);
 // of a group share `grid` and the layout.
 hipError_t launch_iq3_stream(const GroupArgs &g, const GemvArgs &single, const float *grid,
                              int nitems, const Iq3Shape &sh, bool tiled, hipStream_t s);
-// Row-major IQ3 weights -> tile layout (dst: tiles*64*nb*98 bytes).
-hipError_t launch_iq3_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, hipStream_t s);
+// Row-major IQ3 weights (container or, with xxs, llama.cpp order) -> tile
+// layout (dst: tiles*64*nb*98 bytes; the same layout for both orders).
+hipError_t launch_iq3_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, bool xxs,
+                                 hipStream_t s);
 
 }  // namespace qwg

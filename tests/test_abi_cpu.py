@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                  "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
                  "qwg_group_destroy", "qwg_tiled_bytes", "qwg_pack_q4k_tiles",
                  "qwg_gemv_q4k_tiled", "qwg_group_create_q4k_tiled", "qwg_pack_iq3_tiles",
-                 "qwg_gemv_iq3_tiled", "qwg_group_create_iq3_tiled"):
+                 "qwg_gemv_iq3_tiled", "qwg_group_create_iq3_tiled", "qwg_dequant_iq3_xxs",
+                 "qwg_gemv_iq3_xxs", "qwg_pack_iq3_xxs_tiles"):
         assert want in names
 
 
@@ -61,6 +62,9 @@ def test_row_bytes(L):
     assert L.qwg_row_bytes(1, 2048) == 784
     assert L.qwg_row_bytes(1, 5632) == 2156
     assert L.qwg_row_bytes(0, 300) == -2
+    assert L.qwg_row_bytes(2, 2048) == 784       # IQ3_XXS: the same 98-byte blocks
+    assert L.qwg_row_bytes(2, 5632) == 2156
+    assert L.qwg_row_bytes(3, 256) == -6
     assert L.qwg_row_bytes(7, 256) == -6
 
 
@@ -70,7 +74,8 @@ def test_tiled_bytes(L):
     assert L.qwg_tiled_bytes(0, 5632, 1) == 64 * 3168
     assert L.qwg_tiled_bytes(1, 2048, 64) == 64 * 8 * 98
     assert L.qwg_tiled_bytes(1, 2048, 65) == 128 * 8 * 98
-    assert L.qwg_tiled_bytes(2, 2048, 64) == -6
+    assert L.qwg_tiled_bytes(2, 2048, 65) == 128 * 8 * 98
+    assert L.qwg_tiled_bytes(3, 2048, 64) == -6
     assert L.qwg_tiled_bytes(0, 300, 64) == -2
 
 
@@ -143,6 +148,24 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_gemv_iq3_tiled(FAKE, FAKE, FAKE, FAKE, 100, 1, None), 2),
     (lambda L: L.qwg_gemv_iq3_tiled(FAKE, FAKE, FAKE + 2, FAKE, 256, 1, None), 3),
     (lambda L: L.qwg_gemv_iq3_tiled(FAKE, FAKE, FAKE, FAKE + 8, 256, 1, None), 3),
+    # IQ3_XXS (llama.cpp byte order): the same rules as the container entry points
+    (lambda L: L.qwg_dequant_iq3_xxs(None, FAKE, FAKE, 256, None), 1),
+    (lambda L: L.qwg_dequant_iq3_xxs(FAKE, None, FAKE, 256, None), 1),
+    (lambda L: L.qwg_dequant_iq3_xxs(FAKE, FAKE, FAKE, 100, None), 2),
+    (lambda L: L.qwg_dequant_iq3_xxs(FAKE + 1, FAKE, FAKE, 256, None), 3),
+    (lambda L: L.qwg_dequant_iq3_xxs(FAKE, FAKE + 4, FAKE, 256, None), 3),
+    (lambda L: L.qwg_dequant_iq3_xxs(FAKE, FAKE, FAKE + 4, 256, None), 3),
+    (lambda L: L.qwg_gemv_iq3_xxs(FAKE, FAKE, FAKE, None, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_iq3_xxs(None, FAKE, FAKE, FAKE, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_iq3_xxs(FAKE, FAKE, FAKE, FAKE, 384, 1, None), 2),
+    (lambda L: L.qwg_gemv_iq3_xxs(FAKE, FAKE, FAKE, FAKE, 256, 0, None), 2),
+    (lambda L: L.qwg_gemv_iq3_xxs(FAKE, FAKE, FAKE + 1, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3_xxs(FAKE, FAKE + 4, FAKE, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3_xxs(FAKE, FAKE, FAKE, FAKE + 4, 256, 1, None), 3),
+    (lambda L: L.qwg_pack_iq3_xxs_tiles(None, FAKE, 256, 1, None), 1),
+    (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE, FAKE, 0, 1, None), 2),
+    (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE + 4, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE, FAKE + 1, 256, 1, None), 3),
     # IQ3 with an explicit decomposition
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, None, 256, 1, 4, 1, None), 1),
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 384, 1, 4, 1, None), 2),

@@ -786,3 +786,107 @@ def test_iq3_tiled_group_stream_sampled_rows():
         rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 12)]))
         yr, sr = oracle.gemv_iq3_rows(w, grid, x, p.n_in, rows)
         assert_bound(host(y)[rows], yr, sr, "iq3 tiled stream " + p.name)
+
+
+# ---------------------------------------------------------------- IQ3_XXS, llama.cpp byte order
+# synth.iq3_xxs_weights(n_out, n_in, cfg, t) holds the bytes of
+# synth.iq3_weights(n_out, n_in, cfg, t) in llama.cpp's order, and
+# synth.iq3_xxs_grid() is the container grid doubled (llama.cpp's convention).
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 768), (5632, 2048), (2048, 5632)])
+def test_dequant_iq3_xxs_matches_oracle(n_out, n_in):
+    grid = synth.iq3_xxs_grid()
+    w = synth.iq3_xxs_weights(n_out, n_in, 140, n_out + n_in)
+    got = host(qwg.dequant_iq3_xxs(dev(w), dev(grid)))
+    assert_bits(got, oracle.dequant_iq3_xxs(w, grid, n_out * n_in), f"{n_out}x{n_in}")
+
+
+def test_dequant_iq3_xxs_two_byte_aligned_base():
+    n_out, n_in = 5, 768
+    grid = synth.iq3_xxs_grid()
+    w = synth.iq3_xxs_weights(n_out, n_in, 141, 0)
+    wd = _guarded_iq3(w, 6)
+    got = host(qwg.dequant_iq3_xxs(wd, dev(grid)))
+    assert_bits(got, oracle.dequant_iq3_xxs(w, grid, n_out * n_in), "2 mod 4 base")
+
+
+@pytest.mark.parametrize("p", synth.config(4), ids=lambda p: p.name)
+def test_gemv_iq3_xxs_configs(p):
+    grid = synth.iq3_xxs_grid()
+    w = synth.iq3_xxs_weights(p.n_out, p.n_in, p.cfg, p.tensor)
+    x = synth.inputs(p)
+    y = host(qwg.gemv_iq3_xxs(dev(w), dev(x), dev(grid)))
+    yr, sr = oracle.gemv_iq3_xxs(w, grid, x, p.n_in, p.n_out)
+    assert_bound(y, yr, sr, p.name)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 256), (65, 768), (100, 1280), (129, 5632),
+                                        (2000, 768), (32000, 2048)])
+def test_gemv_iq3_xxs_ragged(n_out, n_in):
+    grid = synth.iq3_xxs_grid()
+    w = synth.iq3_xxs_weights(n_out, n_in, 142, n_out)
+    x = synth.activations(n_in, 142, n_out)
+    y = host(qwg.gemv_iq3_xxs(dev(w), dev(x), dev(grid)))
+    if n_out > 4096:
+        rows = np.unique(np.concatenate([[0, n_out - 1],
+                                         np.random.default_rng(n_out).integers(0, n_out, 64)]))
+        yr, sr = oracle.gemv_iq3_xxs_rows(w, grid, x, n_in, rows)
+        assert_bound(y[rows], yr, sr, f"{n_out}x{n_in} sampled")
+    else:
+        yr, sr = oracle.gemv_iq3_xxs(w, grid, x, n_in, n_out)
+        assert_bound(y, yr, sr, f"{n_out}x{n_in}")
+
+
+@pytest.mark.parametrize("offset", [0, 2, 4, 6, 8, 10, 12, 14, 18, 30])
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 512), (65, 768), (64, 5632), (129, 2048)])
+def test_gemv_iq3_xxs_buffer_edges(offset, n_out, n_in):
+    # as test_gemv_iq3_buffer_edges: bytes outside w (0xFF) must never reach y
+    grid = synth.iq3_xxs_grid()
+    w = synth.iq3_xxs_weights(n_out, n_in, 143, offset)
+    x = synth.activations(n_in, 143, offset)
+    wd = _guarded_iq3(w, offset)
+    yr, sr = oracle.gemv_iq3_xxs(w, grid, x, n_in, n_out)
+    ybuf = torch.full((n_out + 130,), -7.0, device=DEV)
+    qwg.gemv_iq3_xxs(wd, dev(x), dev(grid), out=ybuf[64:64 + n_out])
+    yb = host(ybuf)
+    assert_bound(yb[64:64 + n_out], yr, sr, f"offset={offset}")
+    assert (yb[:64] == -7.0).all() and (yb[64 + n_out:] == -7.0).all(), "write outside y"
+
+
+def test_gemv_iq3_xxs_integer_exact():
+    # d = 4 and s in 0..3 make every sub-block scale an odd integer with the
+    # doubled grid's integer entries: every partial sum is an exact integer
+    n_out, n_in = 150, 5632
+    grid = synth.iq3_xxs_grid()
+    w = synth.iq3_xxs_weights(n_out, n_in, 144, 0).reshape(-1, 98).copy()
+    w[:, 0], w[:, 1] = 0x00, 0x44
+    words = w[:, 66:98].copy().view("<u4") & np.uint32(0x3FFFFFFF)
+    w[:, 66:98] = words.view(np.uint8)
+    w = w.reshape(n_out, -1)
+    x = np.random.default_rng(11).integers(-8, 9, n_in).astype(np.float32)
+    yr, _ = oracle.gemv_iq3_xxs(w, grid, x, n_in, n_out)
+    y = host(qwg.gemv_iq3_xxs(dev(w), dev(x), dev(grid)))
+    assert np.array_equal(y.astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(65, 768), (5632, 2048), (2048, 5632)])
+def test_gemv_iq3_xxs_is_the_container_gemv(n_out, n_in):
+    # the same fields in the two byte orders with the same grid: identical sums
+    grid = dev(synth.iq3_xxs_grid())
+    x = dev(synth.activations(n_in, 145, n_out))
+    y5 = host(qwg.gemv_iq3(dev(synth.iq3_weights(n_out, n_in, 145, n_out)), x, grid)).copy()
+    yx = host(qwg.gemv_iq3_xxs(dev(synth.iq3_xxs_weights(n_out, n_in, 145, n_out)), x, grid))
+    assert_bits(yx, y5, f"{n_out}x{n_in}")
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (65, 768), (300, 2048), (2048, 5632)])
+def test_pack_iq3_xxs_tiles_is_the_iq3_tile_layout(n_out, n_in):
+    wx = synth.iq3_xxs_weights(n_out, n_in, 146, n_out)
+    w5 = synth.iq3_weights(n_out, n_in, 146, n_out)
+    got = host(qwg.pack_iq3_xxs_tiles(dev(wx), n_in))
+    assert np.array_equal(got, _iq3_tile_layout(w5, n_in))
+    grid = synth.iq3_xxs_grid()
+    x = synth.activations(n_in, 146, n_out)
+    y = host(qwg.gemv_iq3_tiled(dev(got), dev(x), dev(grid), n_out))
+    yr, sr = oracle.gemv_iq3_xxs(wx, grid, x, n_in, n_out)
+    assert_bound(y, yr, sr, f"xxs tiled {n_out}x{n_in}")
