@@ -249,10 +249,15 @@ int qwg_pack_iq3_xxs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_o
  * (1..QWG_MAX_GROUP) and is not kept. The member pointers (and the IQ3 grid,
  * shared by all members, rules as for qwg_gemv_iq3) are baked into the plan:
  * reuse the same buffers (e.g. fixed activation/output buffers of a decode
- * loop) on every run.
+ * loop) on every run. A group with fewer 64-row tiles than the workgroups the
+ * device holds at once (a few layers' projections rather than a whole decode
+ * step) splits its members' n_in sums across workgroups; the partial sums
+ * and tile counters then live in the group's device buffer (the counters are
+ * zeroed at creation and every run leaves them at zero), so runs of one such
+ * group must not overlap in time (e.g. on two streams): they would race.
  * qwg_group_run: enqueues the whole group on `stream` (asynchronous).
- * qwg_group_workgroups: number of work items (64-row tiles) of one run, or a
- * negative status.
+ * qwg_group_workgroups: number of 64-row tiles of one run, or a negative
+ * status.
  * qwg_group_destroy: frees the plan (hipFree: synchronous; no run of the group
  * may be pending). NULL is accepted.
  */

@@ -118,11 +118,12 @@ __device__ __forceinline__ void q4k_scales(const uint4 &h, uint32_t &sc0, uint32
 }
 
 // Wavefront G's share of one super-block for this lane's row: quant chunk G.
-// xg points at x[256*b + 64*G] of batch element 0 (uniform across the wave).
-template <int G, int NB>
-__device__ __forceinline__ void q4k_chunk(const uint8_t *rowp, cfloat_p xg, int n_in,
-                                          const float (&sx0)[NB], const float (&sx1)[NB],
-                                          uint32_t mlo, uint32_t mhi, float (&acc)[NB]) {
+// xat(bt, i) is activation 256*b + 64*G + i of batch element bt (uniform
+// across the wave).
+template <int G, int NB, typename XAt>
+__device__ __forceinline__ void q4k_chunk_at(const uint8_t *rowp, XAt xat,
+                                             const float (&sx0)[NB], const float (&sx1)[NB],
+                                             uint32_t mlo, uint32_t mhi, float (&acc)[NB]) {
     const uint4 h = *(const uint4 *)rowp;
     const uint4 qa = *(const uint4 *)(rowp + 16 + 32 * G);
     const uint4 qb = *(const uint4 *)(rowp + 32 + 32 * G);
@@ -139,7 +140,6 @@ __device__ __forceinline__ void q4k_chunk(const uint8_t *rowp, cfloat_p xg, int 
     const uint32_t q[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) {
-        cfloat_p xb = xg + (int64_t)bt * n_in;
         float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -147,14 +147,14 @@ __device__ __forceinline__ void q4k_chunk(const uint8_t *rowp, cfloat_p xg, int 
             const uint32_t o = (q[m] >> 8) & mlo;     // bytes 1, 3: low nibbles
             const uint32_t eh = q[m] & mhi;           // bytes 0, 2: high nibbles << 4
             const uint32_t oh = (q[m] >> 8) & mhi;    // bytes 1, 3: high nibbles << 4
-            s0 = __builtin_fmaf(h2f_lo(e), xb[4 * m + 0], s0);
-            s0 = __builtin_fmaf(h2f_lo(o), xb[4 * m + 1], s0);
-            s0 = __builtin_fmaf(h2f_hi(e), xb[4 * m + 2], s0);
-            s0 = __builtin_fmaf(h2f_hi(o), xb[4 * m + 3], s0);
-            s1 = __builtin_fmaf(h2f_lo(eh), xb[32 + 4 * m + 0], s1);
-            s1 = __builtin_fmaf(h2f_lo(oh), xb[32 + 4 * m + 1], s1);
-            s1 = __builtin_fmaf(h2f_hi(eh), xb[32 + 4 * m + 2], s1);
-            s1 = __builtin_fmaf(h2f_hi(oh), xb[32 + 4 * m + 3], s1);
+            s0 = __builtin_fmaf(h2f_lo(e), xat(bt, 4 * m + 0), s0);
+            s0 = __builtin_fmaf(h2f_lo(o), xat(bt, 4 * m + 1), s0);
+            s0 = __builtin_fmaf(h2f_hi(e), xat(bt, 4 * m + 2), s0);
+            s0 = __builtin_fmaf(h2f_hi(o), xat(bt, 4 * m + 3), s0);
+            s1 = __builtin_fmaf(h2f_lo(eh), xat(bt, 32 + 4 * m + 0), s1);
+            s1 = __builtin_fmaf(h2f_lo(oh), xat(bt, 32 + 4 * m + 1), s1);
+            s1 = __builtin_fmaf(h2f_hi(eh), xat(bt, 32 + 4 * m + 2), s1);
+            s1 = __builtin_fmaf(h2f_hi(oh), xat(bt, 32 + 4 * m + 3), s1);
         }
         float a = acc[bt];
         a = __builtin_fmaf(dsc0, s0, a);
@@ -163,6 +163,16 @@ __device__ __forceinline__ void q4k_chunk(const uint8_t *rowp, cfloat_p xg, int 
         a = __builtin_fmaf(-dmn1, sx1[bt], a);
         acc[bt] = a;
     }
+}
+
+// The same with xg pointing at x[256*b + 64*G] of batch element 0, rows n_in
+// apart.
+template <int G, int NB>
+__device__ __forceinline__ void q4k_chunk(const uint8_t *rowp, cfloat_p xg, int n_in,
+                                          const float (&sx0)[NB], const float (&sx1)[NB],
+                                          uint32_t mlo, uint32_t mhi, float (&acc)[NB]) {
+    q4k_chunk_at<G, NB>(
+        rowp, [&](int bt, int i) { return xg[(int64_t)bt * n_in + i]; }, sx0, sx1, mlo, mhi, acc);
 }
 
 // One pipeline stage holds BPS = W/4 super-block columns of the 64-row tile,
@@ -592,7 +602,11 @@ struct StreamCfg {
     static constexpr int kLds = kRed + W * 64 * 4;
 };
 
-// One item as seen by a cursor (stream items are never split: the whole row).
+// One item as seen by a cursor: one 64-row tile over super-blocks [kb0, kb1).
+// Without SPLIT an item is the whole row (kb0 = 0, kb1 = nb). With SPLIT, item
+// index `local` of a problem with `splits` ranges is tile local / splits, range
+// local % splits, and the partial sums meet in tile_epilogue (prob: the
+// problem's descriptor index, -1 for a single GEMV).
 struct Item {
     const uint8_t *w;
     const float *x;
@@ -600,34 +614,74 @@ struct Item {
     int64_t row_bytes;
     int n_out;
     int nb;
-    int nst;   // stages = ceil(nb / BPS)
+    int nst;   // stages = ceil((kb1 - kb0) / BPS)
     int row0;
     int layout;
+    int kb0, kb1, split, prob;
 };
 
-template <int BPS>
+template <int BPS, bool SPLIT>
 __device__ __forceinline__ void load_item(Item &it, int k, const GroupArgs &g, const GemvArgs &single) {
-    if (g.problems == nullptr) {
-        it.w = single.w;
-        it.x = single.x;
-        it.y = single.y;
-        it.row_bytes = single.row_bytes;
-        it.n_out = single.n_out;
-        it.nb = single.nb;
-        it.row0 = k * kTileRows;
-        it.layout = single.layout;
+    if constexpr (!SPLIT) {
+        if (g.problems == nullptr) {
+            it.w = single.w;
+            it.x = single.x;
+            it.y = single.y;
+            it.row_bytes = single.row_bytes;
+            it.n_out = single.n_out;
+            it.nb = single.nb;
+            it.row0 = k * kTileRows;
+            it.layout = single.layout;
+        } else {
+            const cargs_p pa = (cargs_p)g.problems + ((cu32_p)g.map)[k];
+            it.w = pa->w;
+            it.x = pa->x;
+            it.y = pa->y;
+            it.row_bytes = pa->row_bytes;
+            it.n_out = pa->n_out;
+            it.nb = pa->nb;
+            it.row0 = (g.tile != nullptr ? (int)((cu32_p)g.tile)[k] : k - pa->wg_begin) * kTileRows;
+            it.layout = pa->layout;
+        }
+        it.kb0 = 0;
+        it.kb1 = it.nb;
+        it.split = 0;
+        it.prob = -1;
+        it.nst = (it.nb + BPS - 1) / BPS;
     } else {
-        const cargs_p pa = (cargs_p)g.problems + ((cu32_p)g.map)[k];
-        it.w = pa->w;
-        it.x = pa->x;
-        it.y = pa->y;
-        it.row_bytes = pa->row_bytes;
-        it.n_out = pa->n_out;
-        it.nb = pa->nb;
-        it.row0 = (g.tile != nullptr ? (int)((cu32_p)g.tile)[k] : k - pa->wg_begin) * kTileRows;
-        it.layout = pa->layout;
+        int local, splits;
+        if (g.problems == nullptr) {
+            it.w = single.w;
+            it.x = single.x;
+            it.y = single.y;
+            it.row_bytes = single.row_bytes;
+            it.n_out = single.n_out;
+            it.nb = single.nb;
+            it.layout = single.layout;
+            local = k;
+            it.prob = -1;
+            splits = single.splits;
+        } else {
+            const int pi = (int)((cu32_p)g.map)[k];
+            const cargs_p pa = (cargs_p)g.problems + pi;
+            it.w = pa->w;
+            it.x = pa->x;
+            it.y = pa->y;
+            it.row_bytes = pa->row_bytes;
+            it.n_out = pa->n_out;
+            it.nb = pa->nb;
+            it.layout = pa->layout;
+            local = g.tile != nullptr ? (int)((cu32_p)g.tile)[k] : k - pa->wg_begin;
+            it.prob = pi;
+            splits = pa->splits;
+        }
+        const int tile = local / splits;
+        it.split = local - tile * splits;
+        it.row0 = tile * kTileRows;
+        it.kb0 = it.split * it.nb / splits;
+        it.kb1 = (it.split + 1) * it.nb / splits;
+        it.nst = (it.kb1 - it.kb0 + BPS - 1) / BPS;
     }
-    it.nst = (it.nb + BPS - 1) / BPS;
 }
 
 // Sum of v over lanes 0..31 and over lanes 32..63 (each lane gets its half's
@@ -641,7 +695,7 @@ __device__ __forceinline__ float half_wave_sum(float v) {
     return v;
 }
 
-template <int G, int W, int R>
+template <int G, int W, int R, bool SPLIT>
 __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &single, int nitems,
                                            uint8_t *smem) {
     static_assert(R >= 2 && R <= 3, "ring of two or three stages");
@@ -668,7 +722,7 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
     int kc = skip_holes(blockIdx.x, stride, nitems, g);  // item being computed
     if (kc >= nitems) return;
     Item c;
-    load_item<BPS>(c, kc, g, single);
+    load_item<BPS, SPLIT>(c, kc, g, single);
 
     // copy cursor: next stage sd of item kd goes to ring slot slot_d
     int kd = kc, sd = 0, slot_d = 0, pending = 0;
@@ -698,8 +752,8 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
     uint32_t flags = 0;  // bit k: this wavefront's copies are in ring slot k
     auto issue_next = [&]() {
         if (kd >= nitems) return;
-        const int b = sd * BPS + j;
-        if (b < d.nb) {
+        const int b = d.kb0 + sd * BPS + j;
+        if (b < d.kb1) {
             const uint32_t base = lds0 + slot_d * C::kSlot + j * C::kBlock + G * C::kQuarter;
             const uint8_t *wb = dbase + (int64_t)b * dstride;
             // Tile-layout stages are whole lines read once: stream them past the
@@ -727,7 +781,7 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
             sd = 0;
             kd = skip_holes(kd + stride, stride, nitems, g);
             if (kd < nitems) {
-                load_item<BPS>(d, kd, g, single);
+                load_item<BPS, SPLIT>(d, kd, g, single);
                 prep_copy();
             }
         }
@@ -742,6 +796,7 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
     for (;;) {
         float acc[1] = {0.0f};
         for (int s = 0; s < c.nst; ++s) {
+            const int b = c.kb0 + s * BPS + j;
             // With three slots, the next stage may already be in flight: allow
             // its three copies (if this wavefront issued any) to stay pending.
             const int nxt = slot_c + 1 == R ? 0 : slot_c + 1;
@@ -751,8 +806,7 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
                 wait_vmcnt<0>();
             lds_barrier();   // stage in slot_c complete for every wavefront
             issue_next();    // refill the slot computed in the previous step
-            const int b = s * BPS + j;
-            if (b < c.nb) {
+            if (b < c.kb1) {
                 const uint8_t *blk = smem + slot_c * C::kSlot + j * C::kBlock;
                 const uint8_t *rowp = blk + (lane >> 4) * C::kQuarter + (lane & 15) * kQ4kBytes;
                 const float xs = ((const float *)(blk + G * C::kQuarter + 16 * kQ4kBytes))[lane];
@@ -773,11 +827,21 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
         if (wave == 0) {
             float tsum = red[lane];
             for (int w = 1; w < W; ++w) tsum += red[w * 64 + lane];
-            if (c.row0 + lane < c.n_out) c.y[c.row0 + lane] = tsum;
+            if (SPLIT) {
+                GemvArgs ea;
+                if (c.prob >= 0)
+                    load_args(ea, (cargs_p)g.problems + c.prob);
+                else
+                    ea = single;
+                const float total[1] = {tsum};
+                tile_epilogue<1>(ea, c.row0 / kTileRows, c.split, total);
+            } else if (c.row0 + lane < c.n_out) {
+                c.y[c.row0 + lane] = tsum;
+            }
         }
         kc = skip_holes(kc + stride, stride, nitems, g);
         if (kc >= nitems) break;
-        load_item<BPS>(c, kc, g, single);
+        load_item<BPS, SPLIT>(c, kc, g, single);
     }
 }
 
@@ -787,15 +851,19 @@ __device__ __forceinline__ void q4k_stream(const GroupArgs &g, const GemvArgs &s
 // occupancy query still reports seven, so a grid sized by it would leave a
 // seventh of the workgroups waiting for a slot). A budget of 96 ends at s87;
 // the few spills go to VGPR lanes outside the inner loop.
-template <int W, int R>
+//
+// SPLIT: items may cover part of a row (problems with splits > 1), whose sums
+// meet through the problem's partial-sum workspace; the variant without it is
+// the one that streams whole rows (no epilogue round trip, fewer registers).
+template <int W, int R, bool SPLIT>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_num_sgpr(96))) void q4k_stream_kernel(
     GroupArgs g, GemvArgs single, int nitems) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
-        case 0: q4k_stream<0, W, R>(g, single, nitems, smem); break;
-        case 1: q4k_stream<1, W, R>(g, single, nitems, smem); break;
-        case 2: q4k_stream<2, W, R>(g, single, nitems, smem); break;
-        default: q4k_stream<3, W, R>(g, single, nitems, smem); break;
+        case 0: q4k_stream<0, W, R, SPLIT>(g, single, nitems, smem); break;
+        case 1: q4k_stream<1, W, R, SPLIT>(g, single, nitems, smem); break;
+        case 2: q4k_stream<2, W, R, SPLIT>(g, single, nitems, smem); break;
+        default: q4k_stream<3, W, R, SPLIT>(g, single, nitems, smem); break;
     }
 }
 
@@ -858,8 +926,8 @@ int stream_residency(int *cus_out) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, q4k_stream_kernel<W, R>, W * 64,
-                                                         C::kLds) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, q4k_stream_kernel<W, R, false>,
+                                                         W * 64, C::kLds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
         if (cus < 1) cus = 256;
@@ -869,26 +937,31 @@ int stream_residency(int *cus_out) {
 }
 
 template <int W, int R>
-hipError_t launch_stream_wr(const GroupArgs &g, const GemvArgs &single, int nitems, hipStream_t s) {
+hipError_t launch_stream_wr(const GroupArgs &g, const GemvArgs &single, int nitems, bool split,
+                            hipStream_t s) {
     using C = StreamCfg<W, R>;
     int cus = 0;
     const int per_cu = stream_residency<W, R>(&cus);
     int grid = per_cu * cus;
     if (grid > nitems) grid = nitems;
-    hipLaunchKernelGGL((q4k_stream_kernel<W, R>), dim3((unsigned)grid), dim3(W * 64), C::kLds, s, g,
-                       single, nitems);
+    if (split)
+        hipLaunchKernelGGL((q4k_stream_kernel<W, R, true>), dim3((unsigned)grid), dim3(W * 64),
+                           C::kLds, s, g, single, nitems);
+    else
+        hipLaunchKernelGGL((q4k_stream_kernel<W, R, false>), dim3((unsigned)grid), dim3(W * 64),
+                           C::kLds, s, g, single, nitems);
     return hipGetLastError();
 }
 
 hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nitems, int waves,
-                             int ring, hipStream_t s) {
+                             int ring, bool split, hipStream_t s) {
     switch (waves * 10 + ring) {
-        case 42: return launch_stream_wr<4, 2>(g, single, nitems, s);
-        case 43: return launch_stream_wr<4, 3>(g, single, nitems, s);
-        case 82: return launch_stream_wr<8, 2>(g, single, nitems, s);
-        case 83: return launch_stream_wr<8, 3>(g, single, nitems, s);
-        case 162: return launch_stream_wr<16, 2>(g, single, nitems, s);
-        case 163: return launch_stream_wr<16, 3>(g, single, nitems, s);
+        case 42: return launch_stream_wr<4, 2>(g, single, nitems, split, s);
+        case 43: return launch_stream_wr<4, 3>(g, single, nitems, split, s);
+        case 82: return launch_stream_wr<8, 2>(g, single, nitems, split, s);
+        case 83: return launch_stream_wr<8, 3>(g, single, nitems, split, s);
+        case 162: return launch_stream_wr<16, 2>(g, single, nitems, split, s);
+        case 163: return launch_stream_wr<16, 3>(g, single, nitems, split, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -125,6 +125,11 @@ StreamShape stream_shape(bool grouped) {
     return sh;
 }
 
+bool stream_shape_overridden() {
+    static const bool v = env_int("QWG_STREAM_WAVES", 0) != 0 || env_int("QWG_STREAM_RING", 0) != 0;
+    return v;
+}
+
 bool use_stream_engine() {
     static const bool v = env_int("QWG_TILE_ENGINE", 0) == 0;
     return v;
@@ -239,6 +244,20 @@ int iq3_splits(int tiles, int nb, int slots) {
     return s;
 }
 
+// Splits of a stream-engine problem that would leave workgroup slots idle:
+// `factor` items per tile at most (the slots over the launch's tiles), and no
+// more than one pipeline stage (`bps` super-blocks) per item, since an item's
+// stages run one after another while separate items run side by side.
+// Measured on MI355X: a dependent launch of 2048 x 5632 (32 tiles of 22
+// super-blocks) took 16 us streaming whole rows.
+int stream_splits(int nb, int bps, int64_t factor) {
+    static const int env_max = env_int("QWG_STREAM_SPLIT_MAX", 0);  // tuning experiments
+    int s = (nb + bps - 1) / bps;
+    if ((int64_t)s > factor) s = (int)factor;
+    if (env_max && s > env_max) s = env_max;
+    return s < 1 ? 1 : s;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? QWG_OK : QWG_ERR_HIP; }
 
 }  // namespace
@@ -343,7 +362,7 @@ int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
         const StreamShape sh = stream_shape(false);
         const GroupArgs none = {nullptr, nullptr, nullptr};
         return hip_status(
-            launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, (hipStream_t)stream));
+            launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, false, (hipStream_t)stream));
     }
     return hip_status(launch_q4k_gemv(a, batch, waves, (hipStream_t)stream));
 }
@@ -411,8 +430,25 @@ int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, in
     fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
     a.layout = kLayoutTiles;
     const StreamShape sh = stream_shape(false);
+    int cus = 0;
+    const int64_t slots = (int64_t)q4k_stream_residency(sh.waves, sh.ring, &cus) * cus;
+    if (slots > 2 * (int64_t)a.tiles) {
+        int sp = stream_splits(a.nb, sh.waves / 4, slots / a.tiles);
+        while (sp > 1 && ((size_t)sp * a.tiles * kTileRows > kWsPartialFloats ||
+                          (size_t)a.tiles > kWsCounters))
+            --sp;
+        a.splits = sp;
+    }
+    if (a.splits > 1) {
+        Workspace ws;
+        const int wrc = get_workspace((hipStream_t)stream, &ws);
+        if (wrc) return wrc;
+        a.partial = ws.partial;
+        a.counters = ws.counters;
+    }
     const GroupArgs none = {nullptr, nullptr, nullptr};
-    return hip_status(launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, (hipStream_t)stream));
+    return hip_status(launch_q4k_stream(none, a, a.tiles * a.splits, sh.waves, sh.ring,
+                                        a.splits > 1, (hipStream_t)stream));
 }
 
 namespace {
@@ -500,12 +536,15 @@ struct qwg_group {
     int fmt;              // QWG_FMT_Q4K or QWG_FMT_IQ3
     int layout;           // kLayoutRows or kLayoutTiles
     const float *grid;    // IQ3: the grid every member uses
-    void *dev_mem;        // GemvArgs[count], uint32_t map[positions] (and tile[positions])
+    void *dev_mem;        // GemvArgs[count], uint32_t map[positions] (and tile[positions]),
+                          // then the split members' partial sums and tile counters
     GroupArgs args;
     int count;
     int workgroups;       // 64-row tiles of one run
-    int positions;        // work-list length of a launch (tiles, plus holes of a schedule)
+    int positions;        // work-list length of a launch (items, plus holes of a schedule)
     int max_nb;
+    bool split;           // some member splits its rows' sums
+    int waves, ring;      // Q4_K stream engine shape of the launch
 };
 
 namespace {
@@ -541,7 +580,7 @@ void stream_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> 
         tile.resize((size_t)total);
         size_t k = 0;
         for (int i : order)
-            for (int t = 0; t < probs[i].tiles; ++t, ++k) {
+            for (int t = 0; t < probs[i].tiles * probs[i].splits; ++t, ++k) {
                 map[k] = (uint32_t)i;
                 tile[k] = (uint32_t)t;
             }
@@ -557,6 +596,9 @@ void stream_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> 
     }
     double work = 0.0;
     for (int i : order) work += (double)probs[i].tiles * probs[i].nb;
+    auto item_blocks = [&](int i) {
+        return (double)((probs[i].nb + probs[i].splits - 1) / probs[i].splits);
+    };
     for (double &t : target) t *= work / wsum;
     std::priority_queue<std::pair<double, int64_t>> deficit;
     for (int64_t b = 0; b < grid; ++b) deficit.push({target[b], -b});
@@ -564,11 +606,11 @@ void stream_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> 
     std::vector<std::vector<std::pair<uint32_t, uint32_t>>> lists((size_t)grid);
     size_t longest = 0;
     for (int i : order)
-        for (int t = 0; t < probs[i].tiles; ++t) {
+        for (int t = 0; t < probs[i].tiles * probs[i].splits; ++t) {
             const int64_t b = -deficit.top().second;
             deficit.pop();
             lists[b].push_back({(uint32_t)i, (uint32_t)t});
-            load[b] += probs[i].nb;
+            load[b] += item_blocks(i);
             deficit.push({target[b] - load[b], -b});
             longest = std::max(longest, lists[b].size());
         }
@@ -601,6 +643,46 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
         if (probs[i].nb > max_nb) max_nb = probs[i].nb;
     }
     if (total > (int64_t)1 << 30) return QWG_ERR_SHAPE;
+    const bool stream = !iq3 && (layout == kLayoutTiles || use_stream_engine());
+    // Launches with fewer tiles than resident workgroups split the row sums of
+    // their members (at most one pipeline stage per item), as a single GEMV
+    // does; a member's partial sums and tile counters live in the group's
+    // device memory.
+    int64_t slots = 0, bps = 1;
+    int per_cu = 0, cus = 0;
+    StreamShape ssh = {4, 2};
+    if (iq3) {
+        const Iq3Shape ish = iq3_shape(true, 0);
+        slots = iq3_stream_slots(ish, layout == kLayoutTiles);
+        bps = ish.waves / 4;
+    } else if (stream) {
+        ssh = stream_shape(true);
+        per_cu = q4k_stream_residency(ssh.waves, ssh.ring, &cus);
+        slots = (int64_t)per_cu * cus;
+        // A launch that has to split its sums runs 8-wavefront workgroups (two
+        // super-blocks per stage): measured on the dependent per-layer
+        // launches of the TinyLlama stream, 723 us with 4 wavefronts, 610 us
+        // with 8.
+        if (slots > 2 * total && !stream_shape_overridden()) {
+            ssh = {8, 2};
+            per_cu = q4k_stream_residency(ssh.waves, ssh.ring, &cus);
+            slots = (int64_t)per_cu * cus;
+        }
+        bps = ssh.waves / 4;
+    }
+    size_t partial_floats = 0, counters = 0;
+    int64_t items = 0;
+    bool split = false;
+    for (int i = 0; i < count; ++i) {
+        if (slots > 2 * total) probs[i].splits = stream_splits(probs[i].nb, (int)bps, slots / total);
+        if (probs[i].splits > 1) {
+            split = true;
+            partial_floats += (size_t)probs[i].splits * probs[i].tiles * kTileRows;
+            counters += (size_t)probs[i].tiles;
+        }
+        items += (int64_t)probs[i].tiles * probs[i].splits;
+    }
+    if (items > (int64_t)1 << 30) return QWG_ERR_SHAPE;
     // Work items of the longest rows first, so that short ones fill the tail.
     std::vector<int> order((size_t)count);
     for (int i = 0; i < count; ++i) order[i] = i;
@@ -609,38 +691,49 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     int64_t wg = 0;
     for (int i : order) {
         probs[i].wg_begin = (int)wg;
-        wg += probs[i].tiles;
+        wg += (int64_t)probs[i].tiles * probs[i].splits;
     }
     // IQ3 groups keep the plain longest-first round robin: measured on the IQ3
     // stream (two workgroups per CU) the balanced schedule ran 126 us against
     // 114 us, and any age skew only slowed it further.
     std::vector<uint32_t> map, tile;
-    const bool stream = !iq3 && (layout == kLayoutTiles || use_stream_engine());
     if (stream) {
         static const double skew = skew_env("QWG_STREAM_SKEW", kAgeSkew);
-        const StreamShape sh = stream_shape(true);
-        int cus = 0;
-        const int per_cu = q4k_stream_residency(sh.waves, sh.ring, &cus);
-        stream_schedule(probs, order, total, per_cu, cus, skew, map, tile);
+        stream_schedule(probs, order, items, per_cu, cus, skew, map, tile);
     } else {
-        map.resize((size_t)total);
+        map.resize((size_t)items);
         for (int i : order)
-            for (int t = 0; t < probs[i].tiles; ++t) map[(size_t)probs[i].wg_begin + t] = (uint32_t)i;
+            for (int64_t t = 0; t < (int64_t)probs[i].tiles * probs[i].splits; ++t)
+                map[(size_t)(probs[i].wg_begin + t)] = (uint32_t)i;
     }
     const int64_t positions = (int64_t)map.size();
     if (positions > (int64_t)1 << 30) return QWG_ERR_SHAPE;
     const size_t pbytes = sizeof(GemvArgs) * (size_t)count;
     const size_t mbytes = sizeof(uint32_t) * (size_t)positions;
     const size_t tbytes = tile.empty() ? 0 : mbytes;
+    const size_t wbase = (pbytes + mbytes + tbytes + 255) & ~(size_t)255;
+    const size_t cbase = wbase + partial_floats * sizeof(float);
+    const size_t all = cbase + counters * sizeof(uint32_t);
     qwg_group *g = new (std::nothrow) qwg_group();
     if (!g) return QWG_ERR_HIP;
-    if (hipGetDevice(&g->device) != hipSuccess ||
-        hipMalloc(&g->dev_mem, pbytes + mbytes + tbytes) != hipSuccess) {
+    if (hipGetDevice(&g->device) != hipSuccess || hipMalloc(&g->dev_mem, all) != hipSuccess) {
         delete g;
         return QWG_ERR_HIP;
     }
     uint8_t *base = (uint8_t *)g->dev_mem;
-    if (hipMemcpy(base, probs.data(), pbytes, hipMemcpyHostToDevice) != hipSuccess ||
+    if (split) {
+        size_t pf = 0, ct = 0;
+        for (int i = 0; i < count; ++i) {
+            if (probs[i].splits < 2) continue;
+            probs[i].partial = (float *)(base + wbase) + pf;
+            probs[i].counters = (uint32_t *)(base + cbase) + ct;
+            pf += (size_t)probs[i].splits * probs[i].tiles * kTileRows;
+            ct += (size_t)probs[i].tiles;
+        }
+    }
+    // Counters start at zero; every run leaves them at zero again.
+    if ((counters && hipMemset(base + cbase, 0, counters * sizeof(uint32_t)) != hipSuccess) ||
+        hipMemcpy(base, probs.data(), pbytes, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(base + pbytes, map.data(), mbytes, hipMemcpyHostToDevice) != hipSuccess ||
         (tbytes && hipMemcpy(base + pbytes + mbytes, tile.data(), tbytes, hipMemcpyHostToDevice) !=
                        hipSuccess)) {
@@ -658,6 +751,9 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     g->workgroups = (int)total;
     g->positions = (int)positions;
     g->max_nb = max_nb;
+    g->split = split;
+    g->waves = ssh.waves;
+    g->ring = ssh.ring;
     *out = g;
     return QWG_OK;
 }
@@ -704,11 +800,9 @@ int qwg_group_run(const qwg_group *g, void *stream) {
         return hip_status(launch_iq3_stream(g->args, unused, g->grid, g->positions,
                                             iq3_shape(true, 0), g->layout == kLayoutTiles,
                                             (hipStream_t)stream));
-    if (use_stream_engine() || g->layout == kLayoutTiles) {
-        const StreamShape sh = stream_shape(true);
-        return hip_status(launch_q4k_stream(g->args, unused, g->positions, sh.waves, sh.ring,
-                                            (hipStream_t)stream));
-    }
+    if (use_stream_engine() || g->layout == kLayoutTiles)
+        return hip_status(launch_q4k_stream(g->args, unused, g->positions, g->waves, g->ring,
+                                            g->split, (hipStream_t)stream));
     return hip_status(launch_q4k_group(g->args, g->workgroups, g->max_nb, (hipStream_t)stream));
 }
 

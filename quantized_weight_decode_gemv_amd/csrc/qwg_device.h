@@ -150,6 +150,25 @@ __device__ __forceinline__ int skip_holes(int k, int stride, int nitems, const G
 // increments the counter; the last workgroup reads them only after its counter
 // update has returned. An agent-scope fence would instead write back and
 // invalidate the whole L2 of the XCD for every workgroup.
+// Eight agent-coherent 4-byte loads (the form a relaxed agent-scope atomic
+// load takes on this target), issued back to back with one wait for all.
+__device__ __forceinline__ void load8_agent(const float *const (&p)[8], float (&v)[8]) {
+    asm volatile(
+        "global_load_dword %0, %8, off sc1\n\t"
+        "global_load_dword %1, %9, off sc1\n\t"
+        "global_load_dword %2, %10, off sc1\n\t"
+        "global_load_dword %3, %11, off sc1\n\t"
+        "global_load_dword %4, %12, off sc1\n\t"
+        "global_load_dword %5, %13, off sc1\n\t"
+        "global_load_dword %6, %14, off sc1\n\t"
+        "global_load_dword %7, %15, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+        : "memory");
+}
+
 template <int NB>
 __device__ __forceinline__ void tile_epilogue(const GemvArgs &a, int tile, int split,
                                               const float (&total)[NB]) {
@@ -178,14 +197,32 @@ __device__ __forceinline__ void tile_epilogue(const GemvArgs &a, int tile, int s
                                      __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);
     if (old != (uint32_t)(a.splits - 1)) return;
+    // Sum in split order. For one vector the partials are fetched eight at a
+    // time by one asm block (agent-coherent loads, one wait): the compiler
+    // keeps atomic loads in order and waited one memory round trip per split
+    // (measured: 15 us for 22 splits of one launch).
     float acc[NB];
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) acc[bt] = 0.0f;
-    for (int s = 0; s < a.splits; ++s) {
+    if constexpr (NB == 1) {
+        for (int s0 = 0; s0 < a.splits; s0 += 8) {
+            const float *p[8];
 #pragma unroll
-        for (int bt = 0; bt < NB; ++bt)
-            acc[bt] += __hip_atomic_load(&a.partial[((int64_t)s * NB + bt) * plane + row],
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int u = 0; u < 8; ++u)
+                p[u] = &a.partial[(int64_t)(s0 + u < a.splits ? s0 + u : s0) * plane + row];
+            float v[8];
+            load8_agent(p, v);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s0 + u < a.splits) acc[0] += v[u];
+        }
+    } else {
+        for (int s = 0; s < a.splits; ++s) {
+#pragma unroll
+            for (int bt = 0; bt < NB; ++bt)
+                acc[bt] += __hip_atomic_load(&a.partial[((int64_t)s * NB + bt) * plane + row],
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     if (row < a.n_out) {
 #pragma unroll

@@ -74,10 +74,12 @@ hipError_t launch_q4k_group(const GroupArgs &g, int total_workgroups, int max_nb
 // Batched GEMM on matrix cores (2 <= batch <= 8): 4-wavefront workgroups, one
 // per (tile, split), with a ring of `ring` (2..4) stages.
 hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, hipStream_t s);
-// Persistent stream engine (batch 1): `nitems` tiles of the group (g.problems
-// != nullptr) or of `single`; waves in {4, 8, 16}, ring stages in {2, 3, 4}.
+// Persistent stream engine (batch 1): `nitems` work items of the group
+// (g.problems != nullptr) or of `single`; waves in {4, 8, 16}, ring stages in
+// {2, 3}. split: some problem has splits > 1 (items are tile x range; each such
+// problem carries its partial-sum workspace and zeroed tile counters).
 hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nitems, int waves,
-                             int ring, hipStream_t s);
+                             int ring, bool split, hipStream_t s);
 // Resident workgroups per CU of that stream variant and the number of CUs
 // (the launch grid is their product, capped by the item count); 0 if the
 // variant does not exist.

@@ -890,3 +890,92 @@ def test_pack_iq3_xxs_tiles_is_the_iq3_tile_layout(n_out, n_in):
     y = host(qwg.gemv_iq3_tiled(dev(got), dev(x), dev(grid), n_out))
     yr, sr = oracle.gemv_iq3_xxs(wx, grid, x, n_in, n_out)
     assert_bound(y, yr, sr, f"xxs tiled {n_out}x{n_in}")
+
+
+# ---------------------------------------------------------------- split sums in stream launches
+# A grouped launch (or a tiled single GEMV) with fewer 64-row tiles than
+# resident workgroups splits each member's super-block range across
+# workgroups; the partial sums meet in the member's own workspace.
+
+def _integer_iq3(n_out, n_in, seed):
+    # d = 4 and code in 0..3: every sub-block scale is an odd integer
+    w = synth.iq3_weights(n_out, n_in, 150, seed).reshape(-1, 98).copy()
+    w[:, 96], w[:, 97] = 0x00, 0x44
+    words = w[:, 64:96].copy().view("<u4") & np.uint32(0x3FFFFFFF)
+    w[:, 64:96] = words.view(np.uint8)
+    return w.reshape(n_out, -1)
+
+
+@pytest.mark.parametrize("fmt,tiled", [("q4k", False), ("q4k", True), ("iq3", False), ("iq3", True)])
+def test_split_group_integer_exact_repeat_runs(fmt, tiled):
+    # Integer data: every summation order gives the oracle's value exactly.
+    # Members with one super-block per row are never split, so split and
+    # whole-row members share the launch. Each run has new activations and
+    # NaN-filled outputs: a tile counter that did not return to zero, or a
+    # partial sum from the previous run, shows up as a wrong or NaN row.
+    shapes = [(2048, 5632), (256, 2048), (65, 256), (1, 768), (130, 1280), (2048, 2048)]
+    grid = synth.iq3_grid()
+    if fmt == "q4k":
+        ws = [_integer_q4k(o, i, 151 + k) for k, (o, i) in enumerate(shapes)]
+        pack = qwg.pack_q4k_tiles
+    else:
+        ws = [_integer_iq3(o, i, 151 + k) for k, (o, i) in enumerate(shapes)]
+        pack = qwg.pack_iq3_tiles
+    W = [pack(dev(w), i) if tiled else dev(w) for w, (_, i) in zip(ws, shapes)]
+    X = [torch.empty(i, device=DEV) for _, i in shapes]
+    Y = [torch.empty(o, device=DEV) for o, _ in shapes]
+    members = list(zip(W, X, Y))
+    g = qwg.Q4kGroup(members, tiled=tiled) if fmt == "q4k" else \
+        qwg.Iq3Group(members, dev(grid), tiled=tiled)
+    assert g.workgroups == sum((o + 63) // 64 for o, _ in shapes)
+    rng = np.random.default_rng(152)
+    for run in range(4):
+        xs = [rng.integers(-8, 9, i).astype(np.float32) for _, i in shapes]
+        for xd, x in zip(X, xs):
+            xd.copy_(torch.from_numpy(x))
+        for y in Y:
+            y.fill_(float("nan"))
+        g.run()
+        for (o, i), w, x, y in zip(shapes, ws, xs, Y):
+            if fmt == "q4k":
+                yr, _ = oracle.gemv_q4k(w, x, i, o)
+            else:
+                yr, _ = oracle.gemv_iq3(w, grid, x, i, o)
+            assert np.array_equal(host(y).astype(np.float64), yr), f"run {run} {o}x{i}"
+    g.close()
+
+
+@pytest.mark.parametrize("n_out,n_in", [(7, 256), (64, 2048), (130, 5632), (2048, 5632),
+                                        (300, 65536), (5632, 2048)])
+def test_gemv_q4k_tiled_split_integer_exact(n_out, n_in):
+    w = _integer_q4k(n_out, n_in, 153)
+    wt = qwg.pack_q4k_tiles(dev(w), n_in)
+    rng = np.random.default_rng(n_out + n_in)
+    for _ in range(2):
+        x = rng.integers(-8, 9, n_in).astype(np.float32)
+        yr, _ = oracle.gemv_q4k(w, x, n_in, n_out)
+        y = host(qwg.gemv_q4k_tiled(wt, dev(x), n_out))
+        assert np.array_equal(y.astype(np.float64), yr)
+
+
+def test_layered_decode_groups_within_bound():
+    # The dependent per-layer launches of a decoder (q|k|v, o, gate|up, down),
+    # each a small split group, on tile-layout weights.
+    probs = synth.config(2)
+    ws = [synth.weights(p) for p in probs]
+    xs = [synth.inputs(p) for p in probs]
+    W = [qwg.pack_q4k_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
+    X = [dev(x) for x in xs]
+    Y = [torch.full((p.n_out,), float("nan"), device=DEV) for p in probs]
+    names = [p.name.split(".")[-1] for p in probs]
+    parts = [[0, 1, 2], [3], [4, 5], [6]] if names[:4] == ["q", "k", "v", "o"] else \
+        [[i] for i in range(len(probs))]
+    groups = [qwg.Q4kGroup([(W[i], X[i], Y[i]) for i in part], tiled=True) for part in parts]
+    for _ in range(3):
+        for g in groups:
+            g.run()
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        yr, sr = oracle.gemv_q4k(w, x, p.n_in, p.n_out)
+        assert_bound(host(y), yr, sr, "layered " + p.name)
+    for g in groups:
+        g.close()
