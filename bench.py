@@ -52,8 +52,8 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
 # runs of this script, each scaled by the same counter on a plain device copy of known size
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "39b6778404ce837f7c27aa8b66a862274666583a6940b4ade0894c1269c992fb",
-           "fetch_bytes": 594938509, "write_bytes": 1704960}
+TRAFFIC = {"sources_sha256": "15dec1d9dae84a6a846f5857f7e01762791fbd0a2b5658303b83877381ee3bc0",
+           "fetch_bytes": 594958800, "write_bytes": 1704960}
 
 
 def kernel_sources_sha256() -> str:
