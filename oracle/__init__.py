@@ -10,6 +10,8 @@ What it computes, and where the pages define it:
 * IQ3 ("fmt=5") dequant: iq3_pack.py page, module docstring and ``decode()``.
 * IQ3_XXS in llama.cpp's byte order: codebook.py page, the format table of its
   docstring, ``get_d``, ``get_s``, ``eff_np`` and ``dequant``.
+* IQ3_S and IQ4_XS: the same page (format table, ``get_s``, ``eff_np``,
+  ``dequant``; the IQ3_S branch of ``encode`` for its code bytes).
 * GEMV / GEMM: ``y = W @ x`` over the fp32 dequantized rows, accumulated in fp64
   with k ascending, plus ``s = sum |w * x|`` for the per-row error bound
   (argument order of picoLM's ``matmul(out, x, W, n_in, n_out, type)`` call in
@@ -30,6 +32,8 @@ LIB = os.path.join(HERE, "liborc.so")
 QK = 256
 Q4K_BYTES = 144
 IQ3_BYTES = 98
+IQ3S_BYTES = 110
+IQ4XS_BYTES = 136
 
 _lib = None
 
@@ -63,6 +67,10 @@ def lib():
         L.orc_dequant_iq3_xxs.argtypes = [P, P, I64, P]
         L.orc_gemv_iq3_xxs.argtypes = [P, P, P, I64, I64, P, P]
         L.orc_gemv_iq3_xxs_rows.argtypes = [P, P, P, I64, P, I64, P, P]
+        for f in ("iq3s", "iq4xs"):
+            getattr(L, f"orc_dequant_{f}").argtypes = [P, P, I64, P]
+            getattr(L, f"orc_gemv_{f}").argtypes = [P, P, P, I64, I64, P, P]
+            getattr(L, f"orc_gemv_{f}_rows").argtypes = [P, P, P, I64, P, I64, P, P]
         L.orc_gemv_q4k.argtypes = [P, P, I64, I64, P, P]
         L.orc_gemv_iq3.argtypes = [P, P, P, I64, I64, P, P]
         L.orc_gemm_q4k.argtypes = [P, P, I64, I64, ctypes.c_int, P, P]
@@ -72,7 +80,9 @@ def lib():
         L.orc_get_threads.restype = ctypes.c_int
         for name in ("orc_dequant_q4k", "orc_dequant_iq3", "orc_gemv_q4k", "orc_gemv_iq3",
                      "orc_gemm_q4k", "orc_gemv_q4k_rows", "orc_gemv_iq3_rows",
-                     "orc_dequant_iq3_xxs", "orc_gemv_iq3_xxs", "orc_gemv_iq3_xxs_rows"):
+                     "orc_dequant_iq3_xxs", "orc_gemv_iq3_xxs", "orc_gemv_iq3_xxs_rows",
+                     "orc_dequant_iq3s", "orc_gemv_iq3s", "orc_gemv_iq3s_rows",
+                     "orc_dequant_iq4xs", "orc_gemv_iq4xs", "orc_gemv_iq4xs_rows"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -162,6 +172,82 @@ def dequant_iq3_xxs(blocks, grid, n: int) -> np.ndarray:
     out = np.empty(n, np.float32)
     _check(lib().orc_dequant_iq3_xxs(_ptr(blocks), _ptr(grid), n, _ptr(out)), "dequant_iq3_xxs")
     return out
+
+
+# codebook formats with a table argument: (block bytes, table shape)
+_TABLED = {"iq3s": (IQ3S_BYTES, (512, 4)), "iq4xs": (IQ4XS_BYTES, (16,))}
+
+
+def _tabled_dequant(fmt, blocks, table, n):
+    nbytes, tshape = _TABLED[fmt]
+    blocks = _u8(blocks)
+    table = _f32(table)
+    if table.shape != tshape:
+        raise ValueError(f"table must be {list(tshape)}")
+    if blocks.size * QK != n * nbytes:
+        raise ValueError("byte count does not match n")
+    out = np.empty(n, np.float32)
+    _check(getattr(lib(), f"orc_dequant_{fmt}")(_ptr(blocks), _ptr(table), n, _ptr(out)),
+           f"dequant_{fmt}")
+    return out
+
+
+def _tabled_gemv(fmt, w, table, x, n_in, n_out):
+    nbytes, tshape = _TABLED[fmt]
+    w = _u8(w)
+    x = _f32(x)
+    table = _f32(table)
+    if w.size != n_out * (n_in // QK) * nbytes or x.size != n_in or table.shape != tshape:
+        raise ValueError("shape mismatch")
+    y = np.empty(n_out, np.float64)
+    s = np.empty(n_out, np.float64)
+    _check(getattr(lib(), f"orc_gemv_{fmt}")(_ptr(w), _ptr(table), _ptr(x), n_in, n_out, _ptr(y),
+                                              _ptr(s)), f"gemv_{fmt}")
+    return y, s
+
+
+def _tabled_rows(fmt, w, table, x, n_in, rows):
+    nbytes, tshape = _TABLED[fmt]
+    w = _u8(w)
+    x = _f32(x)
+    table = _f32(table)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    row_bytes = (n_in // QK) * nbytes
+    if rows.size == 0 or rows.min() < 0 or (rows.max() + 1) * row_bytes > w.size:
+        raise ValueError("rows out of range")
+    if table.shape != tshape:
+        raise ValueError(f"table must be {list(tshape)}")
+    y = np.empty(rows.size, np.float64)
+    s = np.empty(rows.size, np.float64)
+    _check(getattr(lib(), f"orc_gemv_{fmt}_rows")(_ptr(w), _ptr(table), _ptr(x), n_in, _ptr(rows),
+                                                   rows.size, _ptr(y), _ptr(s)), f"gemv_{fmt}_rows")
+    return y, s
+
+
+def dequant_iq3s(blocks, grid, n: int) -> np.ndarray:
+    """IQ3_S blocks (110 bytes) with a [512, 4] grid (codebook.py page)."""
+    return _tabled_dequant("iq3s", blocks, grid, n)
+
+
+def dequant_iq4xs(blocks, table, n: int) -> np.ndarray:
+    """IQ4_XS blocks (136 bytes) with a 16-value table (codebook.py page)."""
+    return _tabled_dequant("iq4xs", blocks, table, n)
+
+
+def gemv_iq3s(w, grid, x, n_in: int, n_out: int):
+    return _tabled_gemv("iq3s", w, grid, x, n_in, n_out)
+
+
+def gemv_iq4xs(w, table, x, n_in: int, n_out: int):
+    return _tabled_gemv("iq4xs", w, table, x, n_in, n_out)
+
+
+def gemv_iq3s_rows(w, grid, x, n_in: int, rows):
+    return _tabled_rows("iq3s", w, grid, x, n_in, rows)
+
+
+def gemv_iq4xs_rows(w, table, x, n_in: int, rows):
+    return _tabled_rows("iq4xs", w, table, x, n_in, rows)
 
 
 def gemv_q4k(w, x, n_in: int, n_out: int) -> tuple[np.ndarray, np.ndarray]:
@@ -311,4 +397,43 @@ def iq3_xxs_block(idx, words, d_bits: int) -> np.ndarray:
         w = int(words[ib])
         for k in range(4):
             b[66 + 4 * ib + k] = (w >> (8 * k)) & 0xFF
+    return b
+
+
+def iq3s_block(idx, neg, s, d_bits: int) -> np.ndarray:
+    """One 110-byte IQ3_S block from 64 nine-bit grid indices, 256 sign flags
+    (True = negative) and 8 four-bit sub-scales, placed as the codebook.py
+    page's encode writes them (packbits little-endian for the ninth bits and
+    the signs, sub-scales as nibbles, low nibble first)."""
+    idx = np.asarray(idx, dtype=np.int64).reshape(64)
+    neg = np.asarray(neg, dtype=bool).reshape(256)
+    s = np.asarray(s, dtype=np.int64).reshape(8)
+    if idx.min() < 0 or idx.max() > 511 or s.min() < 0 or s.max() > 15:
+        raise ValueError("field out of range")
+    b = np.zeros(IQ3S_BYTES, np.uint8)
+    b[0], b[1] = d_bits & 0xFF, (d_bits >> 8) & 0xFF
+    b[2:66] = (idx & 0xFF).astype(np.uint8)
+    b[66:74] = np.packbits(((idx >> 8) & 1).astype(np.uint8), bitorder="little")
+    b[74:106] = np.packbits(neg.astype(np.uint8), bitorder="little")
+    b[106:110] = (s[0::2] | (s[1::2] << 4)).astype(np.uint8)
+    return b
+
+
+def iq4xs_block(q, s, d_bits: int) -> np.ndarray:
+    """One 136-byte IQ4_XS block from 256 four-bit codes (weight order) and 8
+    six-bit sub-scales: s split as the codebook.py page's set_s writes it (low
+    four bits as nibbles at bytes 4-7, top two bits at bits 2ib of the uint16 at
+    bytes 2-3), codes in the IQ4_NL nibble order of that page's encode, per
+    32-weight sub-block at bytes 8 + 16 ib."""
+    q = np.asarray(q, dtype=np.int64).reshape(8, 32)
+    s = np.asarray(s, dtype=np.int64).reshape(8)
+    if q.min() < 0 or q.max() > 15 or s.min() < 0 or s.max() > 63:
+        raise ValueError("field out of range")
+    b = np.zeros(IQ4XS_BYTES, np.uint8)
+    b[0], b[1] = d_bits & 0xFF, (d_bits >> 8) & 0xFF
+    hi = int(sum(((int(s[ib]) >> 4) & 3) << (2 * ib) for ib in range(8)))
+    b[2], b[3] = hi & 0xFF, (hi >> 8) & 0xFF
+    lo = s & 15
+    b[4:8] = (lo[0::2] | (lo[1::2] << 4)).astype(np.uint8)
+    b[8:] = (q[:, :16] | (q[:, 16:] << 4)).reshape(128).astype(np.uint8)
     return b

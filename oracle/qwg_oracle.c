@@ -232,6 +232,85 @@ int orc_dequant_iq3_xxs(const uint8_t *src, const float *grid, int64_t n, float 
     return 0;
 }
 
+/*
+ * [codebook] IQ3_S, 110 bytes per 256 weights: fp16 d at bytes 0..1 (get_d);
+ * the 64 grid indices are 9 bits, their low eight bits at bytes 2..65 (index
+ * k at byte 2+k) and their ninth bits packed little-endian at bytes 66..73
+ * (bit k%8 of byte 66+k/8); one sign bit per weight packed little-endian at
+ * bytes 74..105 (bit t%8 of byte 74+t/8 set = weight t negative); the 4-bit
+ * sub-scales of the eight 32-weight sub-blocks as nibbles at bytes 106..109,
+ * low nibble first (get_s). All positions as the page's encode writes them.
+ * eff = d * (1 + 2s) in fp32 (eff_np); weight t = v * eff with v = grid entry
+ * (index t/4, component t%4) times its sign (dequant). The grid has 512 rows.
+ */
+static void iq3s_block(const uint8_t *b, const float *grid, float *out)
+{
+    float d = orc_f16_to_f32((uint16_t)(b[0] | (b[1] << 8)));
+    for (int ib = 0; ib < 8; ++ib) {
+        int s = (b[106 + ib / 2] >> (4 * (ib % 2))) & 15;
+        float eff = d * (1.0f + 2.0f * (float)s);
+        for (int j = 0; j < 32; ++j) {
+            int t = 32 * ib + j;
+            int k = t / 4;
+            int idx = b[2 + k] | (((b[66 + k / 8] >> (k % 8)) & 1) << 8);
+            int neg = (b[74 + t / 8] >> (t % 8)) & 1;
+            float entry = grid[4 * idx + t % 4];
+            float v = neg ? -entry : entry;
+            out[t] = v * eff;
+        }
+    }
+}
+
+/*
+ * [codebook] IQ4_XS, 136 bytes per 256 weights: fp16 d at bytes 0..1; the
+ * 6-bit sub-scale s of sub-block ib has its low four bits in nibble ib of
+ * bytes 4..7 (low nibble first) and its top two bits at bits 2ib..2ib+1 of
+ * the little-endian uint16 at bytes 2..3 (get_s). eff = d * (s - 32) in fp32
+ * (eff_np); weight = v * eff, v = table[q] for the weight's 4-bit code q
+ * (dequant; the 16-value table as the caller passes it). The page leaves the
+ * code bytes to llama.cpp; the reading taken here: bytes 8..135, sixteen per
+ * sub-block in the nibble order the page's encode writes for IQ4_NL: byte
+ * 8+16ib+j holds weight j of sub-block ib in its low nibble and weight j+16
+ * in its high nibble (j < 16).
+ */
+static void iq4xs_block(const uint8_t *b, const float *table, float *out)
+{
+    float d = orc_f16_to_f32((uint16_t)(b[0] | (b[1] << 8)));
+    unsigned hi = (unsigned)(b[2] | (b[3] << 8));
+    for (int ib = 0; ib < 8; ++ib) {
+        int lo = (b[4 + ib / 2] >> (4 * (ib % 2))) & 15;
+        int s = lo | (((hi >> (2 * ib)) & 3) << 4);
+        float eff = d * ((float)s - 32.0f);
+        for (int j = 0; j < 32; ++j) {
+            uint8_t byte = b[8 + 16 * ib + j % 16];
+            int q = j < 16 ? (byte & 15) : (byte >> 4);
+            out[32 * ib + j] = table[q] * eff;
+        }
+    }
+}
+
+int orc_dequant_iq3s(const uint8_t *src, const float *grid, int64_t n, float *dst)
+{
+    if (!src || !grid || !dst)
+        return 1;
+    if (n < 0 || n % ORC_QK)
+        return 2;
+    for (int64_t ib = 0; ib < n / ORC_QK; ++ib)
+        iq3s_block(src + ORC_IQ3S_BYTES * ib, grid, dst + ORC_QK * ib);
+    return 0;
+}
+
+int orc_dequant_iq4xs(const uint8_t *src, const float *table, int64_t n, float *dst)
+{
+    if (!src || !table || !dst)
+        return 1;
+    if (n < 0 || n % ORC_QK)
+        return 2;
+    for (int64_t ib = 0; ib < n / ORC_QK; ++ib)
+        iq4xs_block(src + ORC_IQ4XS_BYTES * ib, table, dst + ORC_QK * ib);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ GEMV / GEMM */
 
 static int g_threads = 0;
@@ -371,4 +450,40 @@ int orc_gemv_iq3_xxs_rows(const uint8_t *w, const float *grid, const float *x, i
         return 2;
     return gemm_generic(iq3_xxs_block, ORC_IQ3_BYTES, w, grid, x, n_in, 1, 1, rows, nrows, y,
                         s);
+}
+
+int orc_gemv_iq3s(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                  int64_t n_out, double *y, double *s)
+{
+    if (!grid)
+        return 1;
+    return gemm_generic(iq3s_block, ORC_IQ3S_BYTES, w, grid, x, n_in, n_out, 1, NULL, 0, y, s);
+}
+
+int orc_gemv_iq4xs(const uint8_t *w, const float *table, const float *x, int64_t n_in,
+                   int64_t n_out, double *y, double *s)
+{
+    if (!table)
+        return 1;
+    return gemm_generic(iq4xs_block, ORC_IQ4XS_BYTES, w, table, x, n_in, n_out, 1, NULL, 0, y, s);
+}
+
+int orc_gemv_iq3s_rows(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                       const int64_t *rows, int64_t nrows, double *y, double *s)
+{
+    if (!rows || !grid)
+        return 1;
+    if (nrows < 1)
+        return 2;
+    return gemm_generic(iq3s_block, ORC_IQ3S_BYTES, w, grid, x, n_in, 1, 1, rows, nrows, y, s);
+}
+
+int orc_gemv_iq4xs_rows(const uint8_t *w, const float *table, const float *x, int64_t n_in,
+                        const int64_t *rows, int64_t nrows, double *y, double *s)
+{
+    if (!rows || !table)
+        return 1;
+    if (nrows < 1)
+        return 2;
+    return gemm_generic(iq4xs_block, ORC_IQ4XS_BYTES, w, table, x, n_in, 1, 1, rows, nrows, y, s);
 }

@@ -13,6 +13,8 @@
  *           98-byte grouped container of 256 weights.
  *   IQ3_XXS - the codebook.py page (format table, get_d, get_s, eff_np,
  *           dequant): the same 98 bytes in llama.cpp's order (d first).
+ *   IQ3_S, IQ4_XS - the codebook.py page (format table, get_s, eff_np,
+ *           dequant, and the IQ3_S branch of encode): 110 and 136 bytes.
  *
  * Every entry point returns 0 on success, 2 when a size is invalid
  * (n % 256 != 0, n < 0, n_out < 1, batch outside 1..8), 1 on a NULL pointer.
@@ -29,6 +31,8 @@ extern "C" {
 #define ORC_QK 256          /* weights per super-block (both formats) */
 #define ORC_Q4K_BYTES 144   /* 2 + 2 + 12 + 128 */
 #define ORC_IQ3_BYTES 98    /* 64 + 32 + 2 */
+#define ORC_IQ3S_BYTES 110  /* 2 + 64 + 8 + 32 + 4 */
+#define ORC_IQ4XS_BYTES 136 /* 2 + 2 + 4 + 128 */
 
 /* IEEE 754 binary16 -> binary32, exact (subnormals, infinities, NaN). */
 float orc_f16_to_f32(uint16_t h);
@@ -41,6 +45,9 @@ void orc_q4k_pack_scales(const uint8_t sc[8], const uint8_t mn[8], uint8_t p[12]
 int orc_dequant_q4k(const uint8_t *src, int64_t n, float *dst);
 int orc_dequant_iq3(const uint8_t *src, const float *grid, int64_t n, float *dst);
 int orc_dequant_iq3_xxs(const uint8_t *src, const float *grid, int64_t n, float *dst);
+/* grid: [512][4] fp32; table: [16] fp32 */
+int orc_dequant_iq3s(const uint8_t *src, const float *grid, int64_t n, float *dst);
+int orc_dequant_iq4xs(const uint8_t *src, const float *table, int64_t n, float *dst);
 
 /*
  * y[n] = sum_k w[n,k] * x[k] in fp64 over the fp32 dequantized row, k ascending;
@@ -53,6 +60,10 @@ int orc_gemv_iq3(const uint8_t *w, const float *grid, const float *x, int64_t n_
                  int64_t n_out, double *y, double *s);
 int orc_gemv_iq3_xxs(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
                      int64_t n_out, double *y, double *s);
+int orc_gemv_iq3s(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                  int64_t n_out, double *y, double *s);
+int orc_gemv_iq4xs(const uint8_t *w, const float *table, const float *x, int64_t n_in,
+                   int64_t n_out, double *y, double *s);
 
 /* Y[b, n] = sum_k w[n,k] * X[b,k], X [batch, n_in], Y and S [batch, n_out]. */
 int orc_gemm_q4k(const uint8_t *w, const float *x, int64_t n_in, int64_t n_out,
@@ -65,6 +76,10 @@ int orc_gemv_iq3_rows(const uint8_t *w, const float *grid, const float *x, int64
                       const int64_t *rows, int64_t nrows, double *y, double *s);
 int orc_gemv_iq3_xxs_rows(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
                           const int64_t *rows, int64_t nrows, double *y, double *s);
+int orc_gemv_iq3s_rows(const uint8_t *w, const float *grid, const float *x, int64_t n_in,
+                       const int64_t *rows, int64_t nrows, double *y, double *s);
+int orc_gemv_iq4xs_rows(const uint8_t *w, const float *table, const float *x, int64_t n_in,
+                        const int64_t *rows, int64_t nrows, double *y, double *s);
 
 /* OpenMP thread count used by the GEMVs (rows are independent, so the result
  * does not depend on it). */

@@ -22,6 +22,12 @@ role])``, role 0 = weight fields, 1 = activations, 2 = IQ3 grid):
   the same (cfg, tensor), placed as d (bytes 0-1), indices (2-65), words
   (66-97); their grid is the IQ3 grid doubled (integer entries 4..62, the
   convention of llama.cpp's own table).
+* IQ3_S blocks (110 B): fp16 d as above, bytes 2..109 uniform (every index,
+  sign pattern and 4-bit sub-scale is valid). Grid: 512 distinct 4-tuples over
+  the eight odd magnitudes 1..15 (the published table is absent).
+* IQ4_XS blocks (136 B): fp16 d as above, bytes 2..135 uniform (uniform 6-bit
+  sub-scales and 4-bit codes). Table: 16 distinct integers in [-127, 127],
+  ascending (the published table is absent).
 * Activations: fp32 standard normal.
 
 The published TinyLlama-1.1B Q4_K_M weights and real IQ3 tensors are absent; the
@@ -37,6 +43,9 @@ QK = 256
 Q4K_BYTES = 144
 IQ3_BYTES = 98
 IQ3_LEVELS = (2, 6, 10, 14, 18, 22, 26, 31)
+IQ3S_BYTES = 110
+IQ4XS_BYTES = 136
+IQ3S_LEVELS = (1, 3, 5, 7, 9, 11, 13, 15)
 
 ROLE_W, ROLE_X, ROLE_GRID = 0, 1, 2
 
@@ -93,6 +102,42 @@ def iq3_xxs_weights(n_out: int, n_in: int, cfg: int, tensor: int) -> np.ndarray:
 def iq3_xxs_grid(cfg: int = 4, tensor: int = 0) -> np.ndarray:
     """fp32 [256, 4]: iq3_grid doubled (entries in {4, 12, ..., 62})."""
     return iq3_grid(cfg, tensor) * np.float32(2)
+
+
+def _d_then_uniform(n_out: int, n_in: int, cfg: int, tensor: int, nbytes: int) -> np.ndarray:
+    if n_in % QK:
+        raise ValueError("n_in must be a multiple of 256")
+    nb = n_out * (n_in // QK)
+    g = rng(cfg, tensor, ROLE_W)
+    d = _fp16_uniform(g, nb)
+    blocks = np.empty((nb, nbytes), np.uint8)
+    blocks[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    blocks[:, 2:] = g.integers(0, 256, (nb, nbytes - 2), dtype=np.uint8)
+    return blocks.reshape(n_out, -1)
+
+
+def iq3s_weights(n_out: int, n_in: int, cfg: int, tensor: int) -> np.ndarray:
+    """uint8 [n_out, n_in/256*110] IQ3_S blocks."""
+    return _d_then_uniform(n_out, n_in, cfg, tensor, IQ3S_BYTES)
+
+
+def iq4xs_weights(n_out: int, n_in: int, cfg: int, tensor: int) -> np.ndarray:
+    """uint8 [n_out, n_in/256*136] IQ4_XS blocks."""
+    return _d_then_uniform(n_out, n_in, cfg, tensor, IQ4XS_BYTES)
+
+
+def iq3s_grid(cfg: int = 4, tensor: int = 0) -> np.ndarray:
+    """fp32 [512, 4]: 512 distinct base-8 4-digit tuples mapped onto IQ3S_LEVELS."""
+    g = rng(cfg, tensor, ROLE_GRID)
+    pick = g.choice(4096, 512, replace=False)
+    digits = np.stack([(pick >> (3 * i)) & 7 for i in range(4)], axis=1)
+    return np.asarray(IQ3S_LEVELS, np.float32)[digits]
+
+
+def iq4nl_table(cfg: int = 4, tensor: int = 0) -> np.ndarray:
+    """fp32 [16]: 16 distinct integers in [-127, 127], ascending."""
+    g = rng(cfg, tensor, ROLE_GRID)
+    return np.sort(g.choice(255, 16, replace=False) - 127).astype(np.float32)
 
 
 def iq3_grid(cfg: int = 4, tensor: int = 0) -> np.ndarray:

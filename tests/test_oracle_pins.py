@@ -357,6 +357,150 @@ def test_gemv_iq3_xxs_matches_numpy_matmul():
     assert np.array_equal(yr, y[rows]) and np.array_equal(sr, s[rows])
 
 
+# ---------------------------------------------------------------- IQ3_S and IQ4_XS
+# Pins from the codebook.py page: its format table (110 and 136 bytes; eff =
+# d*(1+2s) and d*(s-32); the Format rows' neutral sub-scale and decode unit:
+# IQ3_S s = 0 gives eff = d, IQ4_XS s = 33 gives eff = d), get_s's field
+# positions (written here by the test-side builders, which follow set_s and the
+# IQ3_S branch of encode), and exactness.
+
+def test_iq3s_iq4xs_block_sizes():
+    assert oracle.IQ3S_BYTES == 2 + 64 + 8 + 32 + 4 == 110
+    assert oracle.IQ4XS_BYTES == 2 + 2 + 4 + 128 == 136
+    assert oracle.IQ3S_BYTES * 8 / 256 == 3.4375 and oracle.IQ4XS_BYTES * 8 / 256 == 4.25
+
+
+def _iq3s_grid_seq():
+    return (np.arange(2048, dtype=np.float32).reshape(512, 4) % 15) + 1
+
+
+def test_iq3s_unit_scale_sweep_and_signs():
+    grid = _iq3s_grid_seq()
+    idx = (np.arange(64) * 37) % 512
+    want = grid[idx].reshape(256).astype(np.float64)
+    # d = 1, s = 0: eff = 1, every weight is its grid value (the page's unit 1.0)
+    w = oracle.dequant_iq3s(oracle.iq3s_block(idx, np.zeros(256, bool), [0] * 8, 0x3C00), grid, 256)
+    assert np.array_equal(w, want.astype(np.float32))
+    # s = 0..15 over two blocks: eff = 1 + 2s per sub-block (d = 0.5)
+    for first in (0, 8):
+        s = [first + ib for ib in range(8)]
+        w = oracle.dequant_iq3s(oracle.iq3s_block(idx, np.zeros(256, bool), s, 0x3800), grid, 256)
+        for ib in range(8):
+            assert np.array_equal(w[32 * ib:32 * ib + 32],
+                                  (0.5 * (1 + 2 * s[ib]) * want[32 * ib:32 * ib + 32]).astype(np.float32))
+    # every sign bit negates exactly its own weight
+    rng = np.random.default_rng(5)
+    neg = rng.random(256) < 0.5
+    w = oracle.dequant_iq3s(oracle.iq3s_block(idx, neg, [0] * 8, 0x3C00), grid, 256)
+    assert np.array_equal(w, np.where(neg, -want, want).astype(np.float32))
+
+
+def test_iq3s_ninth_index_bit():
+    grid = _iq3s_grid_seq()
+    for k in (0, 7, 8, 31, 63):
+        idx = np.zeros(64, int)
+        idx[k] = 256 + 5
+        b = oracle.iq3s_block(idx, np.zeros(256, bool), [0] * 8, 0x3C00)
+        assert b[66 + k // 8] == 1 << (k % 8) and b[2 + k] == 5
+        w = oracle.dequant_iq3s(b, grid, 256)
+        assert np.array_equal(w[4 * k:4 * k + 4], grid[261])
+        assert np.array_equal(np.delete(w, np.arange(4 * k, 4 * k + 4)),
+                              np.tile(grid[0], 63))
+
+
+def test_iq3s_random_fields_roundtrip_exact():
+    grid = synth.iq3s_grid()
+    rng = np.random.default_rng(6)
+    for _ in range(20):
+        idx = rng.integers(0, 512, 64)
+        neg = rng.random(256) < 0.5
+        s = rng.integers(0, 16, 8)
+        d_bits = int(rng.integers(0x0400, 0x5000))
+        d = float(np.array([d_bits], np.uint16).view(np.float16)[0])
+        w = oracle.dequant_iq3s(oracle.iq3s_block(idx, neg, s, d_bits), grid, 256)
+        for t in range(256):
+            v = (-1 if neg[t] else 1) * grid[idx[t // 4], t % 4]
+            assert w[t] == v * d * (1 + 2 * s[t // 32])
+
+
+def test_iq4xs_unit_and_scale_sweep():
+    table = synth.iq4nl_table()
+    q = (np.arange(256) * 7) % 16
+    want = table[q].astype(np.float64)
+    # d = 1, s = 33: eff = 1, every weight is its table value (neutral s, unit 1.0)
+    w = oracle.dequant_iq4xs(oracle.iq4xs_block(q, [33] * 8, 0x3C00), table, 256)
+    assert np.array_equal(w, want.astype(np.float32))
+    # s = 0..63 in every sub-block position: eff = s - 32 (d = 2)
+    for s0 in range(0, 64, 8):
+        s = [(s0 + 5 * ib) % 64 for ib in range(8)]
+        w = oracle.dequant_iq4xs(oracle.iq4xs_block(q, s, 0x4000), table, 256)
+        for ib in range(8):
+            assert np.array_equal(w[32 * ib:32 * ib + 32],
+                                  (2.0 * (s[ib] - 32) * want[32 * ib:32 * ib + 32]).astype(np.float32))
+
+
+def test_iq4xs_scale_and_nibble_positions():
+    table = np.arange(16, dtype=np.float32) - 8.0
+    # the top two bits of sub-block ib's scale at bits 2ib of bytes 2-3, the low
+    # four in nibble ib of bytes 4-7
+    for ib in range(8):
+        s = [32] * 8
+        s[ib] = 32 + 16      # only bit 4 set beyond 32's bit 5
+        b = oracle.iq4xs_block(np.full(256, 9), s, 0x3C00)
+        hi = int(b[2]) | (int(b[3]) << 8)
+        assert (hi >> (2 * ib)) & 3 == 3 and b[4 + ib // 2] >> (4 * (ib % 2)) & 15 == 0
+        w = oracle.dequant_iq4xs(b, table, 256)
+        assert np.array_equal(w[32 * ib:32 * ib + 32], np.full(32, 16.0, np.float32))
+        assert np.array_equal(np.delete(w, np.arange(32 * ib, 32 * ib + 32)), np.zeros(224, np.float32))
+    # byte 8 + 16ib + j: weight j in the low nibble, weight j + 16 in the high one
+    q = np.zeros(256, int)
+    q[32 * 3 + 5] = 1
+    q[32 * 3 + 16 + 5] = 2
+    b = oracle.iq4xs_block(q, [33] * 8, 0x3C00)
+    assert b[8 + 16 * 3 + 5] == 0x21
+    w = oracle.dequant_iq4xs(b, table, 256)
+    assert w[32 * 3 + 5] == -7.0 and w[32 * 3 + 21] == -6.0
+    assert (np.delete(w, [101, 117]) == -8.0).all()
+
+
+def test_iq4xs_fp32_equals_exact():
+    table = synth.iq4nl_table()
+    blocks = synth.iq4xs_weights(4, 512, 99, 3)
+    w = oracle.dequant_iq4xs(blocks, table, 4 * 512).reshape(4, 2, 256)
+    for r in range(4):
+        for sb in range(2):
+            b = blocks[r, 136 * sb: 136 * sb + 136]
+            d = float(b[0:2].view(np.float16)[0])
+            hi = int(b[2]) | (int(b[3]) << 8)
+            for ib in range(8):
+                s = ((b[4 + ib // 2] >> (4 * (ib % 2))) & 15) | (((hi >> (2 * ib)) & 3) << 4)
+                for j in (0, 5, 15, 16, 30, 31):
+                    byte = b[8 + 16 * ib + j % 16]
+                    q = byte & 15 if j < 16 else byte >> 4
+                    assert w[r, sb, 32 * ib + j] == table[q] * d * (int(s) - 32)
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+def test_gemv_codebook_formats_match_numpy_matmul(fmt):
+    n_out, n_in = 9, 768
+    if fmt == "iq3s":
+        tab, w = synth.iq3s_grid(), synth.iq3s_weights(n_out, n_in, 90, 10)
+        deq = oracle.dequant_iq3s(w, tab, n_out * n_in)
+        y, s = oracle.gemv_iq3s(w, tab, synth.activations(n_in, 90, 10), n_in, n_out)
+        yr, sr = oracle.gemv_iq3s_rows(w, tab, synth.activations(n_in, 90, 10), n_in, [8, 0, 3])
+    else:
+        tab, w = synth.iq4nl_table(), synth.iq4xs_weights(n_out, n_in, 90, 11)
+        deq = oracle.dequant_iq4xs(w, tab, n_out * n_in)
+        y, s = oracle.gemv_iq4xs(w, tab, synth.activations(n_in, 90, 10), n_in, n_out)
+        yr, sr = oracle.gemv_iq4xs_rows(w, tab, synth.activations(n_in, 90, 10), n_in, [8, 0, 3])
+    x = synth.activations(n_in, 90, 10).astype(np.float64)
+    deq = deq.reshape(n_out, n_in).astype(np.float64)
+    sref = np.abs(deq) @ np.abs(x)
+    assert np.allclose(y, deq @ x, rtol=0, atol=1e-12 * sref.max())
+    assert np.allclose(s, sref, rtol=1e-13)
+    assert np.array_equal(yr, y[[8, 0, 3]]) and np.array_equal(sr, s[[8, 0, 3]])
+
+
 # ---------------------------------------------------------------- GEMV / GEMM
 
 def _q4k_case(n_out, n_in, seed):
