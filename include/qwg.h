@@ -20,6 +20,18 @@
  *         eff = d*(0.5+s)*0.5 and v = grid[idx][t%4] * sign, the grid being
  *         llama.cpp's table as is (entries 4..62; the iq3_pack container stores
  *         the same scheme with the grid halved).
+ *   IQ3_S  codebook.py page (format table, get_s, eff_np, dequant, the IQ3_S
+ *         branch of encode): 110 bytes = fp16 d (0-1), the low bytes of 64
+ *         nine-bit grid indices (2-65), their ninth bits packed little-endian
+ *         (66-73), one sign bit per weight packed little-endian (74-105),
+ *         eight 4-bit sub-scales as nibbles, low first (106-109).
+ *         Weight = sign * grid[idx][t%4] * d*(1+2s), grid [512][4].
+ *   IQ4_XS codebook.py page (format table, get_s, eff_np, dequant): 136 bytes
+ *         = fp16 d (0-1), the top two bits of eight 6-bit sub-scales at bits
+ *         2ib of the uint16 at 2-3, their low four bits as nibbles (4-7), 256
+ *         4-bit codes (8-135: byte 8+16ib+j holds weight j of sub-block ib in
+ *         its low nibble and weight j+16 in its high nibble, the IQ4_NL order
+ *         of that page's encode). Weight = table[q] * d*(s-32), table [16].
  *
  * Common conventions
  *   - Every pointer argument except `stream` is a DEVICE pointer (HIP memory
@@ -65,10 +77,14 @@ extern "C" {
 #define QWG_FMT_Q4K 0
 #define QWG_FMT_IQ3 1
 #define QWG_FMT_IQ3_XXS 2   /* IQ3 blocks in llama.cpp's byte order */
+#define QWG_FMT_IQ3_S 3
+#define QWG_FMT_IQ4_XS 4
 
 #define QWG_QK 256
 #define QWG_Q4K_BLOCK_BYTES 144
 #define QWG_IQ3_BLOCK_BYTES 98
+#define QWG_IQ3S_BLOCK_BYTES 110
+#define QWG_IQ4XS_BLOCK_BYTES 136
 #define QWG_MAX_N_IN 65536          /* 256 super-blocks per row */
 #define QWG_MAX_N_OUT (1 << 24)
 #define QWG_MAX_BATCH 8
@@ -80,8 +96,8 @@ int qwg_version(void);
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *qwg_strerror(int status);
 
-/* Bytes per row of `n_in` weights in format `fmt` ((n_in/256) * {144, 98, 98}),
- * or -QWG_ERR_SHAPE / -QWG_ERR_FORMAT. */
+/* Bytes per row of `n_in` weights in format `fmt` ((n_in/256) * {144, 98, 98,
+ * 110, 136}), or -QWG_ERR_SHAPE / -QWG_ERR_FORMAT. */
 int64_t qwg_row_bytes(int fmt, int64_t n_in);
 
 /*
@@ -155,6 +171,39 @@ int qwg_gemv_iq3_xxs(float *y, const float *x, const void *w, const float *grid,
                      int64_t n_out, void *stream);
 
 /*
+ * IQ3_S and IQ4_XS (codebook.py page; layouts above).
+ * qwg_dequant_iq3s: src n/256 blocks of 110 bytes (2-byte aligned), grid
+ * [512][4] fp32 (16-byte aligned), dst n fp32 (16-byte aligned).
+ * qwg_dequant_iq4xs: src n/256 blocks of 136 bytes (4-byte aligned), table
+ * [16] fp32 (16-byte aligned), dst as above.
+ * Both bit-identical to (sign * entry) * eff rounded to fp32, eff exact.
+ *
+ * The GEMVs of these formats run on a tile layout made once at load time:
+ * qwg_pack_iq3s_tiles / qwg_pack_iq4xs_tiles take row-major blocks (src
+ * 2-byte aligned, n_out rows of n_in/256 blocks) and write
+ * qwg_tiled_bytes(fmt, n_in, n_out) bytes (dst 16-byte aligned): for each
+ * 64-row tile and block column, the 64 rows' blocks regrouped by field (IQ3_S:
+ * index bytes [G][row][16], sign bytes [G][row][8], ninth-bit bytes
+ * [G][row][2], sub-scale bytes [row][4], d [row][2]; IQ4_XS: code bytes
+ * [G][row][32], bytes 0-7 [row][8]; G = 0..3 is the pair of sub-blocks 2G,
+ * 2G+1); rows past n_out are zero blocks. Every byte of every block is kept.
+ * qwg_gemv_iq3s_tiled / qwg_gemv_iq4xs_tiled: y = W x on that layout (w
+ * 16-byte aligned; x 16-byte aligned, y 4-byte aligned, the grid/table
+ * 16-byte aligned). Every grid or table value must be exactly representable
+ * in fp16 (true for the integer values of these codebooks), otherwise the
+ * result uses the fp16-rounded values. Shape limits and accuracy as
+ * qwg_gemv_q4k.
+ */
+int qwg_dequant_iq3s(const void *src, const float *grid, float *dst, int64_t n, void *stream);
+int qwg_dequant_iq4xs(const void *src, const float *table, float *dst, int64_t n, void *stream);
+int qwg_pack_iq3s_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
+int qwg_pack_iq4xs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
+int qwg_gemv_iq3s_tiled(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                        int64_t n_out, void *stream);
+int qwg_gemv_iq4xs_tiled(float *y, const float *x, const void *w, const float *table,
+                         int64_t n_in, int64_t n_out, void *stream);
+
+/*
  * qwg_gemv_iq3 with an explicit work decomposition (tuning and testing):
  * `waves` wavefronts per workgroup (4, 8 or 16; 0 = automatic) and `splits`
  * workgroups sharing each 64-row tile's n_in sum (1..n_in/256; 0 = automatic).
@@ -208,7 +257,7 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
  * The bytes of every block are kept, only regrouped.
  *
  * qwg_tiled_bytes: bytes of the tile layout (ceil(n_out/64)*64 rows) for
- * QWG_FMT_Q4K, QWG_FMT_IQ3 or QWG_FMT_IQ3_XXS, or a negative status.
+ * any QWG_FMT_* format, or a negative status.
  * qwg_pack_q4k_tiles: src (row-major, as qwg_gemv_q4k takes it) -> dst (tile
  * layout, qwg_tiled_bytes bytes); both 16-byte aligned, must not overlap.
  * qwg_gemv_q4k_tiled: qwg_gemv_q4k on tile-layout weights (same arguments,
@@ -279,6 +328,12 @@ int qwg_group_create_iq3(const qwg_gemv_desc *descs, int count, const float *gri
 int qwg_group_create_q4k_tiled(const qwg_gemv_desc *descs, int count, qwg_group **group);
 int qwg_group_create_iq3_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
                                qwg_group **group);
+/* Tiled groups of IQ3_S (grid [512][4]) or IQ4_XS (table [16]) members, rules
+ * as for the tiled IQ3 group; the grid/table is shared by all members. */
+int qwg_group_create_iq3s_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
+                                qwg_group **group);
+int qwg_group_create_iq4xs_tiled(const qwg_gemv_desc *descs, int count, const float *table,
+                                 qwg_group **group);
 int qwg_group_run(const qwg_group *group, void *stream);
 int qwg_group_workgroups(const qwg_group *group);
 int qwg_group_destroy(qwg_group *group);

@@ -14,6 +14,12 @@ LIB_PATH = os.path.join(PKG, "libqwg.so")
 QWG_FMT_Q4K = 0
 QWG_FMT_IQ3 = 1
 QWG_FMT_IQ3_XXS = 2   # IQ3 blocks in llama.cpp's byte order (d, indices, words)
+QWG_FMT_IQ3_S = 3
+QWG_FMT_IQ4_XS = 4
+IQ3S_BYTES = 110
+IQ4XS_BYTES = 136
+# table argument shape and row-major source alignment of the codebook formats
+_CB = {QWG_FMT_IQ3_S: ("iq3s", (512, 4), IQ3S_BYTES, 2), QWG_FMT_IQ4_XS: ("iq4xs", (16,), IQ4XS_BYTES, 4)}
 QK = 256
 Q4K_BYTES = 144
 IQ3_BYTES = 98
@@ -49,6 +55,11 @@ def lib() -> ctypes.CDLL:
         L.qwg_dequant_iq3_xxs.argtypes = [P, P, P, I64, P]
         L.qwg_gemv_iq3_xxs.argtypes = [P, P, P, P, I64, I64, P]
         L.qwg_pack_iq3_xxs_tiles.argtypes = [P, P, I64, I64, P]
+        for name in ("iq3s", "iq4xs"):
+            getattr(L, f"qwg_dequant_{name}").argtypes = [P, P, P, I64, P]
+            getattr(L, f"qwg_pack_{name}_tiles").argtypes = [P, P, I64, I64, P]
+            getattr(L, f"qwg_gemv_{name}_tiled").argtypes = [P, P, P, P, I64, I64, P]
+            getattr(L, f"qwg_group_create_{name}_tiled").argtypes = [P, I, P, ctypes.POINTER(P)]
         L.qwg_gemv_q4k.argtypes = [P, P, P, I64, I64, P]
         L.qwg_gemv_iq3.argtypes = [P, P, P, P, I64, I64, P]
         L.qwg_gemm_q4k.argtypes = [P, P, P, I64, I64, I, P]
@@ -308,6 +319,94 @@ def gemv_iq3_xxs(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
     return out
 
 
+def _cb_table(fmt: int, tab: torch.Tensor) -> None:
+    _dev(tab, "grid" if fmt == QWG_FMT_IQ3_S else "table", torch.float32)
+    if tuple(tab.shape) != _CB[fmt][1]:
+        raise ValueError(f"{_CB[fmt][0]} needs a table of shape {list(_CB[fmt][1])}")
+
+
+def _cb_dequant(fmt, w, tab, out):
+    name, _, nbytes, _ = _CB[fmt]
+    _dev(w, "w", torch.uint8)
+    _cb_table(fmt, tab)
+    if w.numel() % nbytes:
+        raise ValueError(f"byte count is not a multiple of {nbytes}")
+    n = w.numel() // nbytes * QK
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=w.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n:
+        raise ValueError("out has the wrong size")
+    _check(getattr(lib(), f"qwg_dequant_{name}")(w.data_ptr(), tab.data_ptr(), out.data_ptr(), n,
+                                                  _stream(w)), f"qwg_dequant_{name}")
+    return out
+
+
+def _cb_pack(fmt, w, n_in, out):
+    name, _, nbytes, _ = _CB[fmt]
+    n_out = _weights(w, n_in, nbytes)
+    size = tiled_bytes(n_in, n_out, fmt)
+    if out is None:
+        out = torch.empty(size, dtype=torch.uint8, device=w.device)
+    _dev(out, "out", torch.uint8)
+    if out.numel() != size:
+        raise ValueError("out has the wrong size")
+    _check(getattr(lib(), f"qwg_pack_{name}_tiles")(out.data_ptr(), w.data_ptr(), n_in, n_out,
+                                                     _stream(w)), f"qwg_pack_{name}_tiles")
+    return out
+
+
+def _cb_gemv_tiled(fmt, w, x, tab, n_out, out):
+    name = _CB[fmt][0]
+    _dev(w, "w", torch.uint8)
+    _dev(x, "x", torch.float32)
+    _cb_table(fmt, tab)
+    n_in = x.numel()
+    if w.numel() != tiled_bytes(n_in, n_out, fmt):
+        raise ValueError(f"w is not a {name} tile-layout matrix of this shape")
+    if out is None:
+        out = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n_out:
+        raise ValueError("out has the wrong size")
+    _check(getattr(lib(), f"qwg_gemv_{name}_tiled")(out.data_ptr(), x.data_ptr(), w.data_ptr(),
+                                                     tab.data_ptr(), n_in, n_out, _stream(x)),
+           f"qwg_gemv_{name}_tiled")
+    return out
+
+
+def dequant_iq3s(w: torch.Tensor, grid: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """IQ3_S blocks (uint8, 110 bytes per 256 weights) + fp32 grid [512, 4] -> fp32."""
+    return _cb_dequant(QWG_FMT_IQ3_S, w, grid, out)
+
+
+def dequant_iq4xs(w: torch.Tensor, table: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """IQ4_XS blocks (uint8, 136 bytes per 256 weights) + fp32 table [16] -> fp32."""
+    return _cb_dequant(QWG_FMT_IQ4_XS, w, table, out)
+
+
+def pack_iq3s_tiles(w: torch.Tensor, n_in: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-major IQ3_S weights -> the IQ3_S tile layout that gemv_iq3s_tiled takes."""
+    return _cb_pack(QWG_FMT_IQ3_S, w, n_in, out)
+
+
+def pack_iq4xs_tiles(w: torch.Tensor, n_in: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Row-major IQ4_XS weights -> the IQ4_XS tile layout that gemv_iq4xs_tiled takes."""
+    return _cb_pack(QWG_FMT_IQ4_XS, w, n_in, out)
+
+
+def gemv_iq3s_tiled(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor, n_out: int,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x for IQ3_S weights in the tile layout (pack_iq3s_tiles)."""
+    return _cb_gemv_tiled(QWG_FMT_IQ3_S, w, x, grid, n_out, out)
+
+
+def gemv_iq4xs_tiled(w: torch.Tensor, x: torch.Tensor, table: torch.Tensor, n_out: int,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x for IQ4_XS weights in the tile layout (pack_iq4xs_tiles)."""
+    return _cb_gemv_tiled(QWG_FMT_IQ4_XS, w, x, table, n_out, out)
+
+
 def gemm_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
              waves: int = 0, splits: int = 0) -> torch.Tensor:
     """Y = X W^T for X fp32 [batch, n_in] (1 <= batch <= 8) -> [batch, n_out].
@@ -341,8 +440,9 @@ class Group:
     """Many independent GEMVs y_i = W_i x_i of one format run by one launch.
 
     members: sequence of (w, x, y) device tensors (uint8 weights, fp32 x [n_in],
-    fp32 y [n_out]); fmt QWG_FMT_Q4K or QWG_FMT_IQ3 (then `grid`, fp32 [256, 4],
-    is shared by every member). The tensors are referenced by the plan (kept
+    fp32 y [n_out]); fmt QWG_FMT_Q4K, QWG_FMT_IQ3 (then `grid`, fp32 [256, 4], is
+    shared by every member), or, tiled only, QWG_FMT_IQ3_S (grid [512, 4]) or
+    QWG_FMT_IQ4_XS (`grid` is the 16-value table). The tensors are referenced by the plan (kept
     alive here) and must stay in place; run() recomputes every y_i from the
     current x_i.
     """
@@ -352,9 +452,15 @@ class Group:
         members = list(members)
         if not members:
             raise ValueError("a group needs at least one member")
-        if fmt not in (QWG_FMT_Q4K, QWG_FMT_IQ3):
+        if fmt not in (QWG_FMT_Q4K, QWG_FMT_IQ3, QWG_FMT_IQ3_S, QWG_FMT_IQ4_XS):
             raise ValueError(f"unknown format {fmt}")
-        if fmt == QWG_FMT_IQ3:
+        if fmt in _CB:
+            if not tiled:
+                raise ValueError("IQ3_S and IQ4_XS groups take tile-layout weights")
+            if grid is None:
+                raise ValueError("the group needs its grid or table")
+            _cb_table(fmt, grid)
+        elif fmt == QWG_FMT_IQ3:
             if grid is None:
                 raise ValueError("an IQ3 group needs the grid")
             _grid(grid)
@@ -378,7 +484,10 @@ class Group:
         self._grid = grid
         self._device = members[0][1].device
         handle = ctypes.c_void_p()
-        if fmt == QWG_FMT_Q4K and tiled:
+        if fmt in _CB:
+            fn = f"qwg_group_create_{_CB[fmt][0]}_tiled"
+            _check(getattr(lib(), fn)(descs, len(members), grid.data_ptr(), ctypes.byref(handle)), fn)
+        elif fmt == QWG_FMT_Q4K and tiled:
             _check(lib().qwg_group_create_q4k_tiled(descs, len(members), ctypes.byref(handle)),
                    "qwg_group_create_q4k_tiled")
         elif fmt == QWG_FMT_Q4K:
@@ -430,3 +539,17 @@ class Iq3Group(Group):
 
     def __init__(self, members, grid: torch.Tensor, tiled: bool = False):
         super().__init__(members, QWG_FMT_IQ3, grid, tiled=tiled)
+
+
+class Iq3sGroup(Group):
+    """Group of IQ3_S GEMVs on tile-layout weights sharing one [512, 4] grid."""
+
+    def __init__(self, members, grid: torch.Tensor):
+        super().__init__(members, QWG_FMT_IQ3_S, grid, tiled=True)
+
+
+class Iq4xsGroup(Group):
+    """Group of IQ4_XS GEMVs on tile-layout weights sharing one 16-value table."""
+
+    def __init__(self, members, table: torch.Tensor):
+        super().__init__(members, QWG_FMT_IQ4_XS, table, tiled=True)

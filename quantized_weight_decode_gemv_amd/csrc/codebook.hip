@@ -1,0 +1,492 @@
+// Codebook formats of the codebook.py page beyond IQ3_XXS (its format table,
+// get_s, eff_np, dequant, and the IQ3_S branch of encode):
+//   IQ3_S  110-byte blocks: fp16 d (bytes 0-1), 64 nine-bit grid indices (low
+//          bytes at 2-65, ninth bits packed little-endian at 66-73), one sign
+//          bit per weight (74-105), 4-bit sub-scales as nibbles (106-109);
+//          eff = d*(1+2s), weight = +-grid[idx][t%4] * eff; grid [512][4].
+//   IQ4_XS 136-byte blocks: fp16 d (0-1), 6-bit sub-scales (top two bits at
+//          bits 2ib of the uint16 at 2-3, low four as nibbles at 4-7), 4-bit
+//          codes at 8-135 (byte 8+16ib+j: weight j in the low nibble, weight
+//          j+16 in the high one); eff = d*(s-32), weight = table[q] * eff.
+// Dequantization is bit-exact. The GEMV runs on a tile layout (each 64-row
+// block column regrouped by field, as for IQ3) with a 16-wavefront stream
+// engine whose decode table lives in LDS.
+#include "qwg_device.h"
+
+namespace qwg {
+
+namespace {
+
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t *p) { return *(const uint16_t *)p; }
+
+// ------------------------------------------------------------------ dequant
+
+// One wavefront per block; lane l produces weights 4l..4l+3 (grid index l).
+__global__ __launch_bounds__(256) void iq3s_dequant_kernel(const uint8_t *__restrict__ src,
+                                                           const float *__restrict__ grid,
+                                                           float *__restrict__ dst,
+                                                           int64_t nblocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int ib = lane >> 3;
+    for (int64_t blk = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+         blk < nblocks; blk += nwaves) {
+        const uint8_t *b = src + blk * kIq3sBytes;
+        const float d = h2f_lo(ld_u16(b));
+        const uint32_t idx = (uint32_t)b[2 + lane] | (((uint32_t)b[66 + (lane >> 3)] >> (lane & 7)) & 1u) << 8;
+        const uint32_t sg = ((uint32_t)b[74 + (lane >> 1)] >> (4 * (lane & 1))) & 15u;
+        const uint32_t s = ((uint32_t)b[106 + (ib >> 1)] >> (4 * (ib & 1))) & 15u;
+        const float eff = __fmul_rn(d, __fadd_rn(1.0f, __fmul_rn(2.0f, (float)s)));
+        const float4 g = *(const float4 *)(grid + 4 * idx);
+        float4 o;
+        o.x = __fmul_rn((sg & 1u) ? -g.x : g.x, eff);
+        o.y = __fmul_rn((sg & 2u) ? -g.y : g.y, eff);
+        o.z = __fmul_rn((sg & 4u) ? -g.z : g.z, eff);
+        o.w = __fmul_rn((sg & 8u) ? -g.w : g.w, eff);
+        *(float4 *)(dst + blk * kQK + 4 * lane) = o;
+    }
+}
+
+// One wavefront per block; lane l produces weights 4m..4m+3 of sub-block l/8
+// (m = l%8): low nibbles of code bytes 4m.. for m < 4, high nibbles of bytes
+// 4(m-4).. otherwise. Blocks are 8-byte multiples, so with a 4-byte aligned
+// source every code dword is aligned.
+__global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__restrict__ src,
+                                                            const float *__restrict__ table,
+                                                            float *__restrict__ dst,
+                                                            int64_t nblocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int ib = lane >> 3, m = lane & 7;
+    for (int64_t blk = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+         blk < nblocks; blk += nwaves) {
+        const uint8_t *b = src + blk * kIq4xsBytes;
+        const float d = h2f_lo(ld_u16(b));
+        const uint32_t hi = ld_u16(b + 2);
+        const uint32_t lo = ((uint32_t)b[4 + (ib >> 1)] >> (4 * (ib & 1))) & 15u;
+        const uint32_t s = lo | ((hi >> (2 * ib)) & 3u) << 4;
+        const float eff = __fmul_rn(d, __fsub_rn((float)s, 32.0f));
+        const uint32_t word = *(const uint32_t *)(b + 8 + 16 * ib + 4 * (m & 3));
+        const uint32_t sh = m >= 4 ? 4u : 0u;
+        float4 o;
+        o.x = __fmul_rn(table[(word >> sh) & 15u], eff);
+        o.y = __fmul_rn(table[(word >> (8 + sh)) & 15u], eff);
+        o.z = __fmul_rn(table[(word >> (16 + sh)) & 15u], eff);
+        o.w = __fmul_rn(table[(word >> (24 + sh)) & 15u], eff);
+        *(float4 *)(dst + blk * kQK + 32 * ib + 4 * m) = o;
+    }
+}
+
+// ------------------------------------------------------------------ tile layouts
+//
+// Column (t, b) of a tile-layout matrix (64 rows of block b) starts at
+// (t*nb + b) * kCol; rows past n_out are zero blocks. Within a column the
+// fields are grouped so that wavefront G (sub-blocks 2G and 2G+1) reads its
+// row's pieces with aligned, conflict-free LDS reads.
+
+// IQ3_S, 7040 bytes: indices [G][row][16] (bytes 2+16G..), signs [G][row][8]
+// (74+8G..), ninth bits [G][row][2] (66+2G..), sub-scale bytes [row][4]
+// (106..109), d [row][2] (0..1).
+struct Iq3sFmt {
+    static constexpr int kBytes = kIq3sBytes;
+    static constexpr int kCol = kTileRows * kIq3sBytes;
+    static constexpr int kIdx = 0, kSign = 4096, kHb = 6144, kScale = 6656, kD = 6912;
+
+    // Source byte of column byte o (even) and its row.
+    __device__ static void source(int o, int &row, int &sbyte) {
+        if (o < kSign) {
+            row = (o >> 4) & 63;
+            sbyte = 2 + 16 * (o >> 10) + (o & 15);
+        } else if (o < kHb) {
+            const int p = o - kSign;
+            row = (p >> 3) & 63;
+            sbyte = 74 + 8 * (p >> 9) + (p & 7);
+        } else if (o < kScale) {
+            const int p = o - kHb;
+            row = (p >> 1) & 63;
+            sbyte = 66 + 2 * (p >> 7);
+        } else if (o < kD) {
+            const int p = o - kScale;
+            row = p >> 2;
+            sbyte = 106 + (p & 3);
+        } else {
+            row = (o - kD) >> 1;
+            sbyte = 0;
+        }
+    }
+
+    // Sign-folded fp16 grid table at LDS address 0: entry e = (s4 << 9) | i
+    // (8 bytes at e*8) holds grid row i with component c negated when bit c of
+    // s4 is set. 8192 entries, 64 KB.
+    __device__ static void build_table(const float *grid, int t, int nthreads) {
+        for (int e = t; e < 8192; e += nthreads) {
+            const float4 g = *(const float4 *)(grid + 4 * (e & 511));
+            const int s4 = e >> 9;
+            const float v[4] = {(s4 & 1) ? -g.x : g.x, (s4 & 2) ? -g.y : g.y,
+                                (s4 & 4) ? -g.z : g.z, (s4 & 8) ? -g.w : g.w};
+            uint32_t hb[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) hb[c] = __builtin_bit_cast(uint16_t, (_Float16)v[c]);
+            const u32x2 ent = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+            *(__attribute__((address_space(3))) u32x2 *)(size_t)(e * 8) = ent;
+        }
+    }
+
+    // acc + this lane's row sum over wavefront G's 64 weights. Group k (four
+    // weights) of sub-block h: table entry ((sign nibble k) << 9 | ninth bit <<
+    // 8 | index byte), assembled by one v_perm from the index dword and a
+    // dword of bytes (sign nibble << 1 | ninth bit) built once per sub-block.
+    template <int G>
+    __device__ static float dot(const uint8_t *col, int lane, cfloat_p xg, float acc) {
+        const uint4 q = *(const uint4 *)(col + kIdx + G * 1024 + 16 * lane);
+        const uint2 sg = *(const uint2 *)(col + kSign + G * 512 + 8 * lane);
+        const uint32_t hb = ld_u16(col + kHb + G * 128 + 2 * lane);
+        const uint32_t sc = *(const uint32_t *)(col + kScale + 4 * lane);
+        const float d = h2f_lo(ld_u16(col + kD + 2 * lane));
+        const uint32_t idx[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t S = h ? sg.y : sg.x;
+            const uint32_t e2 = (S << 1) & 0x1E1E1E1Eu;   // nibbles 0, 2, 4, 6, doubled
+            const uint32_t o2 = (S >> 3) & 0x1E1E1E1Eu;   // nibbles 1, 3, 5, 7, doubled
+            const uint32_t H = hb >> (8 * h);
+            const uint32_t ca = __builtin_amdgcn_perm(o2, e2, 0x05010400u) |
+                                (((H & 15u) * 0x00204081u) & 0x01010101u);
+            const uint32_t cb = __builtin_amdgcn_perm(o2, e2, 0x07030602u) |
+                                ((((H >> 4) & 15u) * 0x00204081u) & 0x01010101u);
+            const uint32_t s = (sc >> (8 * G + 4 * h)) & 15u;
+            const float eff = d * (1.0f + 2.0f * (float)s);
+            const cfloat_p x = xg + 32 * h;
+            float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t sel = (uint32_t)(k & 3) | ((uint32_t)(4 + (k & 3)) << 8) | 0x0C0C0000u;
+                const uint32_t ti = __builtin_amdgcn_perm(k < 4 ? ca : cb, idx[2 * h + (k >> 2)], sel);
+                const u32x2 v = lds_load<u32x2>(ti << 3);
+                s0 = __builtin_fmaf(h2f_lo(v.x), x[4 * k + 0], s0);
+                s1 = __builtin_fmaf(h2f_hi(v.x), x[4 * k + 1], s1);
+                s0 = __builtin_fmaf(h2f_lo(v.y), x[4 * k + 2], s0);
+                s1 = __builtin_fmaf(h2f_hi(v.y), x[4 * k + 3], s1);
+            }
+            acc = __builtin_fmaf(eff, s0 + s1, acc);
+        }
+        return acc;
+    }
+};
+
+// IQ4_XS, 8704 bytes: codes [G][row][32] (bytes 8+32G..), header [row][8]
+// (bytes 0..7: d, the scales' top bits, their low nibbles).
+struct Iq4xsFmt {
+    static constexpr int kBytes = kIq4xsBytes;
+    static constexpr int kCol = kTileRows * kIq4xsBytes;
+    static constexpr int kCodes = 0, kHead = 8192;
+
+    __device__ static void source(int o, int &row, int &sbyte) {
+        if (o < kHead) {
+            row = (o >> 5) & 63;
+            sbyte = 8 + 32 * (o >> 11) + (o & 31);
+        } else {
+            row = (o - kHead) >> 3;
+            sbyte = (o - kHead) & 7;
+        }
+    }
+
+    // Pair table at LDS address 0, one copy per lane: entry (code byte b,
+    // lane c) at b*256 + 4c holds (table[b & 15], table[b >> 4]) in fp16, so
+    // the 64 lanes of a read always hit 64 different banks. 64 KB.
+    __device__ static void build_table(const float *table, int t, int nthreads) {
+        for (int e = t; e < 16384; e += nthreads) {
+            const int b = e >> 6;
+            const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)table[b & 15]);
+            const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)table[b >> 4]);
+            *(__attribute__((address_space(3))) uint32_t *)(size_t)(e * 4) = lo | (hi << 16);
+        }
+    }
+
+    // Byte j of sub-block h's sixteen code bytes gives weights j (low nibble)
+    // and j + 16 (high nibble): one v_perm forms b*256 + 4*lane, one LDS read
+    // returns both table values.
+    template <int G>
+    __device__ static float dot(const uint8_t *col, int lane, cfloat_p xg, float acc) {
+        const uint4 qa = *(const uint4 *)(col + kCodes + G * 2048 + 32 * lane);
+        const uint4 qb = *(const uint4 *)(col + kCodes + G * 2048 + 32 * lane + 16);
+        const uint2 hd = *(const uint2 *)(col + kHead + 8 * lane);
+        const float d = h2f_lo(hd.x);
+        const uint32_t sh = hd.x >> 16;
+        const uint32_t lofs = (uint32_t)lane * 4u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            constexpr int kIb0 = 2 * G;
+            const int ib = kIb0 + h;
+            const uint32_t s = ((hd.y >> (4 * ib)) & 15u) | (((sh >> (2 * ib)) & 3u) << 4);
+            const float eff = d * ((float)s - 32.0f);
+            const uint32_t Q[4] = {h ? qb.x : qa.x, h ? qb.y : qa.y, h ? qb.z : qa.z,
+                                   h ? qb.w : qa.w};
+            const cfloat_p x = xg + 32 * h;
+            float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t sel = 0x0C0C0004u | ((uint32_t)(j & 3) << 8);
+                const uint32_t ti = __builtin_amdgcn_perm(lofs, Q[j >> 2], sel);
+                const uint32_t v = lds_load<uint32_t>(ti);
+                s0 = __builtin_fmaf(h2f_lo(v), x[j], s0);
+                s1 = __builtin_fmaf(h2f_hi(v), x[16 + j], s1);
+            }
+            acc = __builtin_fmaf(eff, s0 + s1, acc);
+        }
+        return acc;
+    }
+};
+
+// Row-major blocks -> tile layout, one workgroup per (tile, block column), in
+// 2-byte units (IQ3_S blocks are only 2-byte aligned).
+template <class F>
+__global__ __launch_bounds__(256) void cb_pack_tiles_kernel(const uint8_t *__restrict__ src,
+                                                            uint8_t *__restrict__ dst, int nb,
+                                                            int n_out) {
+    const int b = blockIdx.x % nb;
+    const int tile = blockIdx.x / nb;
+    const int64_t row_bytes = (int64_t)nb * F::kBytes;
+    uint16_t *out = (uint16_t *)(dst + (int64_t)blockIdx.x * F::kCol);
+    for (int u = threadIdx.x; u < F::kCol / 2; u += blockDim.x) {
+        int rr, sbyte;
+        F::source(2 * u, rr, sbyte);
+        const int r = tile * kTileRows + rr;
+        uint16_t v = 0;
+        if (r < n_out)
+            v = *(const uint16_t *)(src + r * row_bytes + (int64_t)b * F::kBytes + sbyte);
+        out[u] = v;
+    }
+}
+
+// ------------------------------------------------------------------ stream engine
+//
+// As the IQ3 engine on its tile layout: persistent workgroups walk work items
+// (64-row tile x super-block range); wavefront 4j + G computes sub-blocks 2G,
+// 2G+1 of super-block j of each stage for the 64 rows (lane = row), with the
+// activations as scalar operands; an R-slot ring filled by LDS-DMA runs ahead
+// across items. 16 wavefronts (four super-blocks per stage) share the 64 KB
+// decode table: one workgroup per CU.
+template <class F, int W, int R>
+struct CbCfg {
+    static constexpr int kBps = W / 4;
+    static constexpr int kGran = F::kCol / 16;        // 16-byte granules per column
+    static constexpr int kTable = 65536;              // at LDS address 0
+    static constexpr int kRing = kTable;
+    static constexpr int kSlot = kBps * F::kCol;
+    static constexpr int kRed = kRing + R * kSlot;    // [W][64] fp32 row sums
+    static constexpr int kLds = kRed + W * 64 * 4;
+    static_assert(F::kCol % 16 == 0, "columns are whole granules");
+    static_assert(kGran <= 3 * 256, "a column takes at most three copy rounds");
+    // copy instructions per stage of wavefront G: rounds i with 256i + 64G < kGran
+    static constexpr int copies(int G) {
+        return (64 * G < kGran) + (256 + 64 * G < kGran) + (512 + 64 * G < kGran);
+    }
+};
+
+struct CbItem {
+    GemvArgs a;
+    const uint8_t *sb;   // the tile's column 0
+    int tile, split, kb0, kb1, nst;
+};
+
+template <class F, int BPS>
+__device__ __forceinline__ void cb_load_item(CbItem &it, int k, const GroupArgs &g,
+                                             const GemvArgs &single) {
+    int local;
+    if (g.problems == nullptr) {
+        it.a = single;
+        local = k;
+    } else {
+        load_args(it.a, (cargs_p)g.problems + ((cu32_p)g.map)[k]);
+        local = g.tile != nullptr ? (int)((cu32_p)g.tile)[k] : k - it.a.wg_begin;
+    }
+    const int splits = it.a.splits;
+    it.tile = local / splits;
+    it.split = local - it.tile * splits;
+    it.kb0 = it.split * it.a.nb / splits;
+    it.kb1 = (it.split + 1) * it.a.nb / splits;
+    it.nst = (it.kb1 - it.kb0 + BPS - 1) / BPS;
+    it.sb = it.a.w + (int64_t)it.tile * it.a.nb * F::kCol;
+}
+
+template <class F, int G, int W, int R>
+__device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &single,
+                                          const float *tab, int nitems, uint8_t *smem) {
+    static_assert(R >= 2 && R <= 3, "ring of two or three stages");
+    using C = CbCfg<F, W, R>;
+    constexpr int BPS = C::kBps;
+    constexpr int kCp = C::copies(G);
+    const int lane = threadIdx.x & 63;
+    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+    const int wave = 4 * j + G;
+    const int stride = gridDim.x;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    int kc = skip_holes(blockIdx.x, stride, nitems, g);
+    if (kc >= nitems) return;
+    CbItem c;
+    cb_load_item<F, BPS>(c, kc, g, single);
+
+    int kd = kc, sd = 0, slot_d = 0, pending = 0;
+    CbItem d = c;
+    uint32_t flags = 0;  // bit k: this wavefront's copies are in ring slot k
+    auto issue_next = [&]() {
+        if (kd >= nitems) return;
+        const int b = d.kb0 + sd * BPS + j;
+        if (b < d.kb1) {
+            const uint32_t colb = lds0 + C::kRing + slot_d * C::kSlot + j * F::kCol;
+            const uint8_t *src = d.sb + (int64_t)b * F::kCol;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int g0 = 256 * i + 64 * G;    // this wavefront's first granule of round i
+                if (g0 < C::kGran) {
+                    if (g0 + lane < C::kGran)
+                        dma16_stream(src + 16 * (g0 + lane), colb + 16 * g0);
+                }
+            }
+            flags |= 1u << slot_d;
+        } else {
+            flags &= ~(1u << slot_d);
+        }
+        ++pending;
+        slot_d = slot_d + 1 == R ? 0 : slot_d + 1;
+        if (++sd == d.nst) {
+            sd = 0;
+            kd = skip_holes(kd + stride, stride, nitems, g);
+            if (kd < nitems) cb_load_item<F, BPS>(d, kd, g, single);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) issue_next();
+
+    // The decode table, while the first stages are in flight; the first stage
+    // barrier publishes it.
+    F::build_table(tab, (int)threadIdx.x, W * 64);
+
+    float *red = (float *)(smem + C::kRed);
+    int slot_c = 0;
+    for (;;) {
+        float acc = 0.0f;
+        for (int s = 0; s < c.nst; ++s) {
+            const int nxt = slot_c + 1 == R ? 0 : slot_c + 1;
+            int younger = 0;
+            if (R >= 3 && pending > 1) younger = kCp * (int)((flags >> nxt) & 1u);
+            wait_vmcnt_upto(younger);
+            lds_barrier();   // stage in slot_c complete for every wavefront (and the table)
+            issue_next();
+            const int b = c.kb0 + s * BPS + j;
+            if (b < c.kb1)
+                acc = F::template dot<G>(smem + C::kRing + slot_c * C::kSlot + j * F::kCol, lane,
+                                         as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
+            --pending;
+            slot_c = nxt;
+        }
+        red[wave * 64 + lane] = acc;
+        lds_barrier();
+        if (wave == 0) {
+            float tsum = red[lane];
+            for (int w = 1; w < W; ++w) tsum += red[w * 64 + lane];
+            const float total[1] = {tsum};
+            tile_epilogue<1>(c.a, c.tile, c.split, total);
+        }
+        kc = skip_holes(kc + stride, stride, nitems, g);
+        if (kc >= nitems) break;
+        cb_load_item<F, BPS>(c, kc, g, single);
+    }
+}
+
+template <class F, int W, int R>
+__global__ __launch_bounds__(W * 64) void cb_stream_kernel(GroupArgs g, GemvArgs single,
+                                                           const float *tab, int nitems) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
+        case 0: cb_stream<F, 0, W, R>(g, single, tab, nitems, smem); break;
+        case 1: cb_stream<F, 1, W, R>(g, single, tab, nitems, smem); break;
+        case 2: cb_stream<F, 2, W, R>(g, single, tab, nitems, smem); break;
+        default: cb_stream<F, 3, W, R>(g, single, tab, nitems, smem); break;
+    }
+}
+
+constexpr int kCbWaves = 16;
+constexpr int kCbRing = 2;
+
+template <class F>
+int cb_slots_f() {
+    static int slots = 0;
+    if (slots == 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        constexpr size_t lds = CbCfg<F, kCbWaves, kCbRing>::kLds;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, cb_stream_kernel<F, kCbWaves, kCbRing>, kCbWaves * 64, lds) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        slots = per_cu * cus;
+    }
+    return slots;
+}
+
+template <class F>
+hipError_t cb_launch(const GroupArgs &g, const GemvArgs &single, const float *tab, int nitems,
+                     hipStream_t s) {
+    int n = cb_slots_f<F>();
+    if (n > nitems) n = nitems;
+    constexpr size_t lds = CbCfg<F, kCbWaves, kCbRing>::kLds;
+    hipLaunchKernelGGL((cb_stream_kernel<F, kCbWaves, kCbRing>), dim3((unsigned)n),
+                       dim3(kCbWaves * 64), lds, s, g, single, tab, nitems);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_iq3s_dequant(const uint8_t *src, const float *grid, float *dst, int64_t nblocks,
+                               hipStream_t s) {
+    int64_t groups = (nblocks + 3) / 4;
+    if (groups > 65536) groups = 65536;
+    hipLaunchKernelGGL(iq3s_dequant_kernel, dim3((unsigned)groups), dim3(256), 0, s, src, grid, dst,
+                       nblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_iq4xs_dequant(const uint8_t *src, const float *table, float *dst,
+                                int64_t nblocks, hipStream_t s) {
+    int64_t groups = (nblocks + 3) / 4;
+    if (groups > 65536) groups = 65536;
+    hipLaunchKernelGGL(iq4xs_dequant_kernel, dim3((unsigned)groups), dim3(256), 0, s, src, table,
+                       dst, nblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_cb_pack_tiles(int fmt, const uint8_t *src, uint8_t *dst, int nb, int n_out,
+                                hipStream_t s) {
+    const int64_t tiles = ((int64_t)n_out + kTileRows - 1) / kTileRows;
+    const dim3 grid((unsigned)(tiles * nb)), block(256);
+    if (fmt == kFmtIq3s)
+        hipLaunchKernelGGL(cb_pack_tiles_kernel<Iq3sFmt>, grid, block, 0, s, src, dst, nb, n_out);
+    else if (fmt == kFmtIq4xs)
+        hipLaunchKernelGGL(cb_pack_tiles_kernel<Iq4xsFmt>, grid, block, 0, s, src, dst, nb, n_out);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+int cb_stream_slots(int fmt) {
+    if (fmt == kFmtIq3s) return cb_slots_f<Iq3sFmt>();
+    if (fmt == kFmtIq4xs) return cb_slots_f<Iq4xsFmt>();
+    return 0;
+}
+
+int cb_stream_bps() { return kCbWaves / 4; }
+
+hipError_t launch_cb_stream(int fmt, const GroupArgs &g, const GemvArgs &single, const float *tab,
+                            int nitems, hipStream_t s) {
+    if (fmt == kFmtIq3s) return cb_launch<Iq3sFmt>(g, single, tab, nitems, s);
+    if (fmt == kFmtIq4xs) return cb_launch<Iq4xsFmt>(g, single, tab, nitems, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qwg

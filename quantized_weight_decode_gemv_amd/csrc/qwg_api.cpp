@@ -281,16 +281,30 @@ const char *qwg_strerror(int status) {
 
 namespace {
 
+static_assert(QWG_FMT_IQ3_S == kFmtIq3s && QWG_FMT_IQ4_XS == kFmtIq4xs, "format ids");
+
 bool known_format(int fmt) {
-    return fmt == QWG_FMT_Q4K || fmt == QWG_FMT_IQ3 || fmt == QWG_FMT_IQ3_XXS;
+    return fmt == QWG_FMT_Q4K || fmt == QWG_FMT_IQ3 || fmt == QWG_FMT_IQ3_XXS ||
+           fmt == QWG_FMT_IQ3_S || fmt == QWG_FMT_IQ4_XS;
 }
+
+int block_bytes_of(int fmt) {
+    switch (fmt) {
+        case QWG_FMT_Q4K: return kQ4kBytes;
+        case QWG_FMT_IQ3_S: return kIq3sBytes;
+        case QWG_FMT_IQ4_XS: return kIq4xsBytes;
+        default: return kIq3Bytes;
+    }
+}
+
+bool codebook_format(int fmt) { return fmt == QWG_FMT_IQ3_S || fmt == QWG_FMT_IQ4_XS; }
 
 }  // namespace
 
 int64_t qwg_row_bytes(int fmt, int64_t n_in) {
     if (!known_format(fmt)) return -QWG_ERR_FORMAT;
     if (n_in <= 0 || n_in % kQK) return -QWG_ERR_SHAPE;
-    return (n_in / kQK) * (fmt == QWG_FMT_Q4K ? kQ4kBytes : kIq3Bytes);
+    return (n_in / kQK) * block_bytes_of(fmt);
 }
 
 int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
@@ -298,6 +312,11 @@ int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
     int rc = check_gemv_shape(n_in, n_out);
     if (rc) return -rc;
     const int tiles = (int)((n_out + kTileRows - 1) / kTileRows);
+    if (codebook_format(fmt)) {
+        const int slots = cb_stream_slots(fmt);
+        if (slots <= 0) return -QWG_ERR_HIP;
+        return iq3_splits(tiles, (int)(n_in / kQK), slots);
+    }
     if (fmt != QWG_FMT_Q4K) {
         const int slots = iq3_stream_slots(iq3_shape(false, 0), false);
         if (slots <= 0) return -QWG_ERR_HIP;
@@ -407,8 +426,7 @@ int64_t qwg_tiled_bytes(int fmt, int64_t n_in, int64_t n_out) {
     if (!known_format(fmt)) return -QWG_ERR_FORMAT;
     const int rc = check_gemv_shape(n_in, n_out);
     if (rc) return -rc;
-    return ((n_out + kTileRows - 1) / kTileRows) * kTileRows * (n_in / kQK) *
-           (fmt == QWG_FMT_Q4K ? kQ4kBytes : kIq3Bytes);
+    return ((n_out + kTileRows - 1) / kTileRows) * kTileRows * (n_in / kQK) * block_bytes_of(fmt);
 }
 
 int qwg_pack_q4k_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
@@ -529,13 +547,97 @@ int qwg_pack_iq3_xxs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_o
     return iq3_pack(dst, src, n_in, n_out, true, stream);
 }
 
+// ------------------------------------------------------------------ IQ3_S, IQ4_XS
+
+namespace {
+
+int cb_dequant(int fmt, const void *src, const float *tab, float *dst, int64_t n, void *stream) {
+    if (!src || !tab || !dst) return QWG_ERR_NULL;
+    if (n <= 0 || n % kQK) return QWG_ERR_SHAPE;
+    if (!aligned(src, fmt == QWG_FMT_IQ4_XS ? 4 : 2) || !aligned(tab, 16) || !aligned(dst, 16))
+        return QWG_ERR_ALIGN;
+    const hipError_t e =
+        fmt == QWG_FMT_IQ3_S
+            ? launch_iq3s_dequant((const uint8_t *)src, tab, dst, n / kQK, (hipStream_t)stream)
+            : launch_iq4xs_dequant((const uint8_t *)src, tab, dst, n / kQK, (hipStream_t)stream);
+    return hip_status(e);
+}
+
+int cb_pack(int fmt, void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
+    if (!dst || !src) return QWG_ERR_NULL;
+    const int rc = check_gemv_shape(n_in, n_out);
+    if (rc) return rc;
+    if (!aligned(dst, 16) || !aligned(src, 2)) return QWG_ERR_ALIGN;
+    return hip_status(launch_cb_pack_tiles(fmt, (const uint8_t *)src, (uint8_t *)dst,
+                                           (int)(n_in / kQK), (int)n_out, (hipStream_t)stream));
+}
+
+int cb_gemv_tiled(int fmt, float *y, const float *x, const void *w, const float *tab, int64_t n_in,
+                  int64_t n_out, void *stream) {
+    if (!y || !x || !w || !tab) return QWG_ERR_NULL;
+    int rc = check_gemv_shape(n_in, n_out);
+    if (rc) return rc;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(tab, 16) || !aligned(y, 4))
+        return QWG_ERR_ALIGN;
+    GemvArgs a;
+    fill_shape(a, w, x, tab, y, n_in, n_out, block_bytes_of(fmt));
+    a.layout = kLayoutTiles;
+    const int slots = cb_stream_slots(fmt);
+    if (slots <= 0) return QWG_ERR_HIP;
+    if (slots > 2 * a.tiles) {
+        int sp = stream_splits(a.nb, cb_stream_bps(), slots / a.tiles);
+        while (sp > 1 && ((size_t)sp * a.tiles * kTileRows > kWsPartialFloats ||
+                          (size_t)a.tiles > kWsCounters))
+            --sp;
+        a.splits = sp;
+    }
+    if (a.splits > 1) {
+        Workspace ws;
+        rc = get_workspace((hipStream_t)stream, &ws);
+        if (rc) return rc;
+        a.partial = ws.partial;
+        a.counters = ws.counters;
+    }
+    const GroupArgs none = {nullptr, nullptr, nullptr};
+    return hip_status(
+        launch_cb_stream(fmt, none, a, tab, a.tiles * a.splits, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int qwg_dequant_iq3s(const void *src, const float *grid, float *dst, int64_t n, void *stream) {
+    return cb_dequant(QWG_FMT_IQ3_S, src, grid, dst, n, stream);
+}
+
+int qwg_dequant_iq4xs(const void *src, const float *table, float *dst, int64_t n, void *stream) {
+    return cb_dequant(QWG_FMT_IQ4_XS, src, table, dst, n, stream);
+}
+
+int qwg_pack_iq3s_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
+    return cb_pack(QWG_FMT_IQ3_S, dst, src, n_in, n_out, stream);
+}
+
+int qwg_pack_iq4xs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {
+    return cb_pack(QWG_FMT_IQ4_XS, dst, src, n_in, n_out, stream);
+}
+
+int qwg_gemv_iq3s_tiled(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                        int64_t n_out, void *stream) {
+    return cb_gemv_tiled(QWG_FMT_IQ3_S, y, x, w, grid, n_in, n_out, stream);
+}
+
+int qwg_gemv_iq4xs_tiled(float *y, const float *x, const void *w, const float *table,
+                         int64_t n_in, int64_t n_out, void *stream) {
+    return cb_gemv_tiled(QWG_FMT_IQ4_XS, y, x, w, table, n_in, n_out, stream);
+}
+
 // ------------------------------------------------------------------ grouped GEMV
 
 struct qwg_group {
     int device;
-    int fmt;              // QWG_FMT_Q4K or QWG_FMT_IQ3
+    int fmt;              // QWG_FMT_Q4K, QWG_FMT_IQ3, QWG_FMT_IQ3_S or QWG_FMT_IQ4_XS
     int layout;           // kLayoutRows or kLayoutTiles
-    const float *grid;    // IQ3: the grid every member uses
+    const float *grid;    // IQ3 / IQ3_S: the grid, IQ4_XS: the table every member uses
     void *dev_mem;        // GemvArgs[count], uint32_t map[positions] (and tile[positions]),
                           // then the split members' partial sums and tile counters
     GroupArgs args;
@@ -625,8 +727,9 @@ void stream_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> 
 
 int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, const float *grid,
                  qwg_group **out) {
-    const bool iq3 = fmt == QWG_FMT_IQ3;
-    const int block_bytes = iq3 ? kIq3Bytes : kQ4kBytes;
+    const bool cb = codebook_format(fmt);
+    const bool iq3 = fmt == QWG_FMT_IQ3 || cb;   // round-robin schedule, grid/table argument
+    const int block_bytes = block_bytes_of(fmt);
     const uintptr_t w_align = iq3 && layout == kLayoutRows ? 2 : 16;
     std::vector<GemvArgs> probs((size_t)count);
     int64_t total = 0;
@@ -651,7 +754,10 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     int64_t slots = 0, bps = 1;
     int per_cu = 0, cus = 0;
     StreamShape ssh = {4, 2};
-    if (iq3) {
+    if (cb) {
+        slots = cb_stream_slots(fmt);
+        bps = cb_stream_bps();
+    } else if (iq3) {
         const Iq3Shape ish = iq3_shape(true, 0);
         slots = iq3_stream_slots(ish, layout == kLayoutTiles);
         bps = ish.waves / 4;
@@ -792,10 +898,31 @@ int qwg_group_create_iq3_tiled(const qwg_gemv_desc *descs, int count, const floa
     return group_create(QWG_FMT_IQ3, kLayoutTiles, descs, count, grid, out);
 }
 
+int qwg_group_create_iq3s_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
+                                qwg_group **out) {
+    if (!descs || !grid || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    if (!aligned(grid, 16)) return QWG_ERR_ALIGN;
+    return group_create(QWG_FMT_IQ3_S, kLayoutTiles, descs, count, grid, out);
+}
+
+int qwg_group_create_iq4xs_tiled(const qwg_gemv_desc *descs, int count, const float *table,
+                                 qwg_group **out) {
+    if (!descs || !table || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    if (!aligned(table, 16)) return QWG_ERR_ALIGN;
+    return group_create(QWG_FMT_IQ4_XS, kLayoutTiles, descs, count, table, out);
+}
+
 int qwg_group_run(const qwg_group *g, void *stream) {
     if (!g) return QWG_ERR_NULL;
     GemvArgs unused;
     fill_shape(unused, nullptr, nullptr, nullptr, nullptr, kQK, 1, kQ4kBytes);
+    if (codebook_format(g->fmt))
+        return hip_status(launch_cb_stream(g->fmt, g->args, unused, g->grid, g->positions,
+                                           (hipStream_t)stream));
     if (g->fmt == QWG_FMT_IQ3)
         return hip_status(launch_iq3_stream(g->args, unused, g->grid, g->positions,
                                             iq3_shape(true, 0), g->layout == kLayoutTiles,

@@ -10,6 +10,11 @@ namespace qwg {
 constexpr int kQK = 256;
 constexpr int kQ4kBytes = 144;
 constexpr int kIq3Bytes = 98;
+constexpr int kIq3sBytes = 110;   // IQ3_S (codebook formats)
+constexpr int kIq4xsBytes = 136;  // IQ4_XS
+// Format ids shared with the C ABI (QWG_FMT_* in qwg.h).
+constexpr int kFmtIq3s = 3;
+constexpr int kFmtIq4xs = 4;
 constexpr int kTileRows = 64;  // one output row per lane of a wavefront
 
 // One GEMV/GEMM problem as the kernels see it. `splits` workgroups share each
@@ -102,5 +107,19 @@ hipError_t launch_iq3_stream(const GroupArgs &g, const GemvArgs &single, const f
 // layout (dst: tiles*64*nb*98 bytes; the same layout for both orders).
 hipError_t launch_iq3_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n_out, bool xxs,
                                  hipStream_t s);
+
+// Codebook formats IQ3_S / IQ4_XS (codebook.hip). Dequant: bit-exact. GEMV:
+// tile layout only (launch_cb_pack_tiles makes it), 16-wavefront workgroups,
+// one per CU; `tab` is the [512][4] grid (IQ3_S) or the 16-value table (IQ4_XS).
+hipError_t launch_iq3s_dequant(const uint8_t *src, const float *grid, float *dst, int64_t nblocks,
+                               hipStream_t s);
+hipError_t launch_iq4xs_dequant(const uint8_t *src, const float *table, float *dst,
+                                int64_t nblocks, hipStream_t s);
+hipError_t launch_cb_pack_tiles(int fmt, const uint8_t *src, uint8_t *dst, int nb, int n_out,
+                                hipStream_t s);
+int cb_stream_slots(int fmt);   // resident workgroups on the current device (0: unknown format)
+int cb_stream_bps();            // super-blocks per pipeline stage
+hipError_t launch_cb_stream(int fmt, const GroupArgs &g, const GemvArgs &single, const float *tab,
+                            int nitems, hipStream_t s);
 
 }  // namespace qwg

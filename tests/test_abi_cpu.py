@@ -36,7 +36,10 @@ def test_header_declares_the_entry_points():
                  "qwg_group_destroy", "qwg_tiled_bytes", "qwg_pack_q4k_tiles",
                  "qwg_gemv_q4k_tiled", "qwg_group_create_q4k_tiled", "qwg_pack_iq3_tiles",
                  "qwg_gemv_iq3_tiled", "qwg_group_create_iq3_tiled", "qwg_dequant_iq3_xxs",
-                 "qwg_gemv_iq3_xxs", "qwg_pack_iq3_xxs_tiles"):
+                 "qwg_gemv_iq3_xxs", "qwg_pack_iq3_xxs_tiles", "qwg_dequant_iq3s",
+                 "qwg_dequant_iq4xs", "qwg_pack_iq3s_tiles", "qwg_pack_iq4xs_tiles",
+                 "qwg_gemv_iq3s_tiled", "qwg_gemv_iq4xs_tiled", "qwg_group_create_iq3s_tiled",
+                 "qwg_group_create_iq4xs_tiled"):
         assert want in names
 
 
@@ -64,7 +67,9 @@ def test_row_bytes(L):
     assert L.qwg_row_bytes(0, 300) == -2
     assert L.qwg_row_bytes(2, 2048) == 784       # IQ3_XXS: the same 98-byte blocks
     assert L.qwg_row_bytes(2, 5632) == 2156
-    assert L.qwg_row_bytes(3, 256) == -6
+    assert L.qwg_row_bytes(3, 2048) == 880         # IQ3_S
+    assert L.qwg_row_bytes(4, 5632) == 22 * 136    # IQ4_XS
+    assert L.qwg_row_bytes(5, 256) == -6
     assert L.qwg_row_bytes(7, 256) == -6
 
 
@@ -75,7 +80,9 @@ def test_tiled_bytes(L):
     assert L.qwg_tiled_bytes(1, 2048, 64) == 64 * 8 * 98
     assert L.qwg_tiled_bytes(1, 2048, 65) == 128 * 8 * 98
     assert L.qwg_tiled_bytes(2, 2048, 65) == 128 * 8 * 98
-    assert L.qwg_tiled_bytes(3, 2048, 64) == -6
+    assert L.qwg_tiled_bytes(3, 2048, 65) == 128 * 8 * 110
+    assert L.qwg_tiled_bytes(4, 512, 1) == 64 * 2 * 136
+    assert L.qwg_tiled_bytes(5, 2048, 64) == -6
     assert L.qwg_tiled_bytes(0, 300, 64) == -2
 
 
@@ -87,7 +94,7 @@ def test_plan_splits(L):
     assert L.qwg_plan_splits(0, 256, 1 << 20) == 1
     assert L.qwg_plan_splits(0, 257, 64) == -2
     assert L.qwg_plan_splits(0, 65536 + 256, 64) == -2
-    assert L.qwg_plan_splits(3, 256, 64) == -6
+    assert L.qwg_plan_splits(5, 256, 64) == -6
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails validation first
@@ -166,6 +173,24 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE, FAKE, 0, 1, None), 2),
     (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE + 4, FAKE, 256, 1, None), 3),
     (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE, FAKE + 1, 256, 1, None), 3),
+    # IQ3_S / IQ4_XS
+    (lambda L: L.qwg_dequant_iq3s(None, FAKE, FAKE, 256, None), 1),
+    (lambda L: L.qwg_dequant_iq3s(FAKE, FAKE, FAKE, 257, None), 2),
+    (lambda L: L.qwg_dequant_iq3s(FAKE + 1, FAKE, FAKE, 256, None), 3),
+    (lambda L: L.qwg_dequant_iq3s(FAKE, FAKE + 4, FAKE, 256, None), 3),
+    (lambda L: L.qwg_dequant_iq4xs(FAKE, None, FAKE, 256, None), 1),
+    (lambda L: L.qwg_dequant_iq4xs(FAKE + 2, FAKE, FAKE, 256, None), 3),
+    (lambda L: L.qwg_dequant_iq4xs(FAKE, FAKE, FAKE + 8, 256, None), 3),
+    (lambda L: L.qwg_pack_iq3s_tiles(None, FAKE, 256, 1, None), 1),
+    (lambda L: L.qwg_pack_iq3s_tiles(FAKE, FAKE, 300, 1, None), 2),
+    (lambda L: L.qwg_pack_iq3s_tiles(FAKE + 8, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_pack_iq4xs_tiles(FAKE, FAKE + 1, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3s_tiled(FAKE, FAKE, FAKE, None, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_iq3s_tiled(FAKE, FAKE, FAKE, FAKE, 256, 0, None), 2),
+    (lambda L: L.qwg_gemv_iq3s_tiled(FAKE, FAKE, FAKE + 2, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq4xs_tiled(FAKE, FAKE + 4, FAKE, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq4xs_tiled(FAKE, FAKE, FAKE, FAKE + 4, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq4xs_tiled(None, FAKE, FAKE, FAKE, 256, 1, None), 1),
     # IQ3 with an explicit decomposition
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, None, 256, 1, 4, 1, None), 1),
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 384, 1, 4, 1, None), 2),
@@ -230,6 +255,13 @@ def test_tiled_group_validation_errors(L):
     assert L.qwg_group_create_iq3_tiled(arr3, 1, None, ctypes.byref(out)) == 1
     assert L.qwg_group_create_q4k_tiled(None, 1, ctypes.byref(out)) == 1
     assert L.qwg_group_create_q4k_tiled(arr, 0, ctypes.byref(out)) == 2
+    # IQ3_S / IQ4_XS tiled groups: the same member rules, plus the grid/table
+    for create in (L.qwg_group_create_iq3s_tiled, L.qwg_group_create_iq4xs_tiled):
+        assert create(arr3, 1, FAKE, ctypes.byref(out)) == 3
+        assert create(arr3, 1, None, ctypes.byref(out)) == 1
+        assert create(arr, 2, FAKE + 4, ctypes.byref(out)) == 3
+        assert create(arr, 0, FAKE, ctypes.byref(out)) == 2
+        assert out.value is None
 
 
 def test_group_null_and_count_errors(L):

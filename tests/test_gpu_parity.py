@@ -979,3 +979,163 @@ def test_layered_decode_groups_within_bound():
         assert_bound(host(y), yr, sr, "layered " + p.name)
     for g in groups:
         g.close()
+
+
+# ---------------------------------------------------------------- IQ3_S and IQ4_XS
+
+CB = {
+    "iq3s": dict(weights=synth.iq3s_weights, table=synth.iq3s_grid, nbytes=110,
+                 dequant=qwg.dequant_iq3s, pack=qwg.pack_iq3s_tiles, gemv=qwg.gemv_iq3s_tiled,
+                 group=qwg.Iq3sGroup, o_dequant=oracle.dequant_iq3s, o_gemv=oracle.gemv_iq3s,
+                 o_rows=oracle.gemv_iq3s_rows),
+    "iq4xs": dict(weights=synth.iq4xs_weights, table=synth.iq4nl_table, nbytes=136,
+                  dequant=qwg.dequant_iq4xs, pack=qwg.pack_iq4xs_tiles, gemv=qwg.gemv_iq4xs_tiled,
+                  group=qwg.Iq4xsGroup, o_dequant=oracle.dequant_iq4xs, o_gemv=oracle.gemv_iq4xs,
+                  o_rows=oracle.gemv_iq4xs_rows),
+}
+
+
+def _cb_tile_layout(fmt: str, w: np.ndarray, n_in: int) -> np.ndarray:
+    """The tile layouts written out from their description in include/qwg.h."""
+    nbytes = CB[fmt]["nbytes"]
+    n_out, nb = w.shape[0], n_in // 256
+    tiles = (n_out + 63) // 64
+    blk = np.zeros((tiles * 64, nb, nbytes), np.uint8)
+    blk[:n_out] = w.reshape(n_out, nb, nbytes)
+    blk = blk.reshape(tiles, 64, nb, nbytes).transpose(0, 2, 1, 3)       # [t][b][row][bytes]
+
+    def per_g(a, b, width):    # bytes a..b of each block as [G][row][width]
+        return blk[..., a:b].reshape(tiles, nb, 64, 4, width).transpose(0, 1, 3, 2, 4).reshape(tiles, nb, -1)
+
+    def per_row(a, b):
+        return blk[..., a:b].reshape(tiles, nb, -1)
+
+    if fmt == "iq3s":
+        parts = [per_g(2, 66, 16), per_g(74, 106, 8), per_g(66, 74, 2), per_row(106, 110),
+                 per_row(0, 2)]
+    else:
+        parts = [per_g(8, 136, 32), per_row(0, 8)]
+    return np.concatenate(parts, axis=2).reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 768), (5632, 2048), (2048, 5632)])
+def test_dequant_codebook_matches_oracle(fmt, n_out, n_in):
+    c = CB[fmt]
+    tab = c["table"]()
+    w = c["weights"](n_out, n_in, 160, n_out + n_in)
+    got = host(c["dequant"](dev(w), dev(tab)))
+    assert_bits(got, c["o_dequant"](w, tab, n_out * n_in), f"{fmt} {n_out}x{n_in}")
+
+
+def test_dequant_iq3s_two_byte_aligned_base():
+    tab = synth.iq3s_grid()
+    w = synth.iq3s_weights(3, 512, 161, 0)
+    wd = _guarded_iq3(w, 2)
+    assert wd.data_ptr() % 4 == 2
+    assert_bits(host(qwg.dequant_iq3s(wd, dev(tab))), oracle.dequant_iq3s(w, tab, 3 * 512), "2 mod 4")
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (65, 768), (300, 2048), (2048, 5632)])
+def test_pack_codebook_tiles_is_the_layout(fmt, n_out, n_in):
+    c = CB[fmt]
+    w = c["weights"](n_out, n_in, 162, n_out)
+    got = host(c["pack"](dev(w), n_in))
+    assert np.array_equal(got, _cb_tile_layout(fmt, w, n_in))
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 512), (65, 768), (130, 5632), (2048, 2048),
+                                        (5632, 2048), (2048, 5632), (4097, 1280)])
+def test_gemv_codebook_tiled(fmt, n_out, n_in):
+    c = CB[fmt]
+    tab = c["table"]()
+    w = c["weights"](n_out, n_in, 163, n_out)
+    x = synth.activations(n_in, 163, n_out)
+    wt, xd, td = c["pack"](dev(w), n_in), dev(x), dev(tab)
+    y = host(c["gemv"](wt, xd, td, n_out)).copy()
+    yr, sr = c["o_gemv"](w, tab, x, n_in, n_out)
+    assert_bound(y, yr, sr, f"{fmt} tiled {n_out}x{n_in}")
+    assert_bits(host(c["gemv"](wt, xd, td, n_out)), y, f"{fmt} rerun")
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+def test_gemv_codebook_lm_head_sampled(fmt):
+    c = CB[fmt]
+    n_out, n_in = 32000, 2048
+    tab = c["table"]()
+    w = c["weights"](n_out, n_in, 164, 0)
+    x = synth.activations(n_in, 164, 0)
+    y = host(c["gemv"](c["pack"](dev(w), n_in), dev(x), dev(tab), n_out))
+    rows = np.unique(np.concatenate([[0, n_out - 1], np.random.default_rng(3).integers(0, n_out, 96)]))
+    yr, sr = c["o_rows"](w, tab, x, n_in, rows)
+    assert_bound(y[rows], yr, sr, f"{fmt} lm head")
+
+
+def _integer_cb(fmt, n_out, n_in, seed):
+    w = CB[fmt]["weights"](n_out, n_in, 165, seed).reshape(-1, CB[fmt]["nbytes"]).copy()
+    w[:, 0], w[:, 1] = 0x00, 0x3C                   # d = 1
+    if fmt == "iq3s":
+        w[:, 106:110] &= 0x33                       # s in 0..3: eff 1, 3, 5, 7
+    else:
+        w[:, 2:4] = [0xAA, 0xAA]                    # top bits 2: s = 32 + low nibble
+        w[:, 4:8] &= 0x33                           # eff = s - 32 in 0..3
+    return w.reshape(n_out, -1)
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+@pytest.mark.parametrize("n_out,n_in", [(150, 2048), (64, 5632), (7, 256)])
+def test_gemv_codebook_integer_exact(fmt, n_out, n_in):
+    c = CB[fmt]
+    tab = c["table"]()
+    w = _integer_cb(fmt, n_out, n_in, n_out)
+    x = np.random.default_rng(n_in + n_out).integers(-8, 9, n_in).astype(np.float32)
+    yr, _ = c["o_gemv"](w, tab, x, n_in, n_out)
+    y = host(c["gemv"](c["pack"](dev(w), n_in), dev(x), dev(tab), n_out))
+    assert np.array_equal(y.astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+def test_codebook_groups_layer_stream_repeat_runs(fmt):
+    c = CB[fmt]
+    tab = c["table"]()
+    td = dev(tab)
+    # one layer's seven projections (split sums), four runs with new activations
+    probs = synth.config(2)
+    ws = [c["weights"](p.n_out, p.n_in, 166, k) for k, p in enumerate(probs)]
+    W = [c["pack"](dev(w), p.n_in) for p, w in zip(probs, ws)]
+    X = [torch.empty(p.n_in, device=DEV) for p in probs]
+    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    g = c["group"](zip(W, X, Y), td)
+    for run in range(3):
+        xs = [synth.activations(p.n_in, 166, 10 * run + k) for k, p in enumerate(probs)]
+        for xd, x in zip(X, xs):
+            xd.copy_(torch.from_numpy(x))
+        for y in Y:
+            y.fill_(float("nan"))
+        g.run()
+        for p, w, x, y in zip(probs, ws, xs, Y):
+            yr, sr = c["o_gemv"](w, tab, x, p.n_in, p.n_out)
+            assert_bound(host(y), yr, sr, f"{fmt} layer run {run} {p.name}")
+    g.close()
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+def test_codebook_group_stream_sampled_rows(fmt):
+    c = CB[fmt]
+    tab = c["table"]()
+    probs = synth.config(6)
+    rng = np.random.default_rng(33)
+    ws = [c["weights"](p.n_out, p.n_in, 167, k) for k, p in enumerate(probs)]
+    xs = [synth.inputs(p) for p in probs]
+    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    W = [c["pack"](dev(w), p.n_in) for p, w in zip(probs, ws)]
+    g = c["group"](zip(W, [dev(x) for x in xs], Y), dev(tab))
+    for _ in range(2):
+        g.run()
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 8)]))
+        yr, sr = c["o_rows"](w, tab, x, p.n_in, rows)
+        assert_bound(host(y)[rows], yr, sr, f"{fmt} stream {p.name}")
+    g.close()
