@@ -26,11 +26,12 @@ back-to-back launches); and the CPU oracle's throughput on the host cores
 (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--headline-only]
-       python bench.py --workload iq3_stream|iq3_xxs|lm_head [--steps K] [--warmup W]
+       python bench.py --workload iq3_stream|iq3_xxs|codebooks|lm_head [--steps K] [--warmup W]
 The second form measures the other hot-path rows on their own (one JSON line each, for the
 record and for profiling): "iq3_stream" = the same 155 GEMV shapes in the IQ3 container as one
 grouped launch (IQ3 tile layout; the row-major launch beside it); "iq3_xxs" = IQ3_XXS blocks in
-llama.cpp's byte order (single GEMVs row-major and repacked, and the stream repacked); "lm_head" = the 32000x2048 Q4_K LM head at batch 1..8 (qwg_gemv_q4k,
+llama.cpp's byte order (single GEMVs row-major and repacked, and the stream repacked); "codebooks" =
+the same stream and single shapes in IQ3_S and IQ4_XS (tile layout); "lm_head" = the 32000x2048 Q4_K LM head at batch 1..8 (qwg_gemv_q4k,
 qwg_gemv_q4k_tiled, qwg_gemm_q4k), cycling over enough weight copies that every launch streams
 from HBM rather than the last-level cache.
 """
@@ -84,7 +85,7 @@ def parse():
     ap.add_argument("--print-kernel-hash", action="store_true",
                     help="print the hash of the kernel sources the traffic figure is tied to")
     ap.add_argument("--workload", default="q4k_stream",
-                    choices=["q4k_stream", "iq3_stream", "iq3_xxs", "lm_head"],
+                    choices=["q4k_stream", "iq3_stream", "iq3_xxs", "codebooks", "lm_head"],
                     help="q4k_stream: the headline (default); the others: see the module docstring")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline launch (no row-major, layered or per-call "
@@ -128,6 +129,9 @@ def main():
         return
     if args.workload == "iq3_xxs":
         bench_iq3_xxs(args)
+        return
+    if args.workload == "codebooks":
+        bench_codebooks(args)
         return
 
     import numpy as np
@@ -402,6 +406,64 @@ def bench_iq3_xxs(args):
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "kernel": "iq3_stream_kernel<8,2,tile layout> (grouped)",
                      "kernel_us": round(us, 2)}}), flush=True)
+
+
+def bench_codebooks(args):
+    """IQ3_S and IQ4_XS (codebook.py page): the per-token stream's 155 GEMV
+    shapes in each format, repacked to the tile layout, as one grouped launch;
+    and the two single GEMV shapes of the IQ3 configuration with cold weights."""
+    import torch
+    import quantized_weight_decode_gemv_amd as qwg
+    from quantized_weight_decode_gemv_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    fmts = {"iq3s": (synth.iq3s_weights, synth.iq3s_grid, 110, qwg.pack_iq3s_tiles,
+                     qwg.gemv_iq3s_tiled, qwg.Iq3sGroup),
+            "iq4xs": (synth.iq4xs_weights, synth.iq4nl_table, 136, qwg.pack_iq4xs_tiles,
+                      qwg.gemv_iq4xs_tiled, qwg.Iq4xsGroup)}
+    out = {}
+    for name, (weights, table, nbytes, pack, gemv, Group) in fmts.items():
+        tab = torch.from_numpy(table()).to(dev)
+        probs = synth.config(6)
+        X = [torch.from_numpy(synth.inputs(p)).to(dev) for p in probs]
+        Y = [torch.empty(p.n_out, device=dev) for p in probs]
+        W = [pack(torch.from_numpy(weights(p.n_out, p.n_in, p.cfg, p.tensor)).to(dev), p.n_in)
+             for p in probs]
+        group = Group(zip(W, X, Y), tab)
+        step = sum(p.n_out * (p.n_in // 256) * nbytes + 4 * (p.n_in + p.n_out) for p in probs)
+        us = _event_us(lambda: group.run(stream), stream, args.steps, args.warmup)
+        group.close()
+        del W
+        singles = {}
+        copies = 64
+        for p in synth.config(4):
+            wt = pack(torch.from_numpy(weights(p.n_out, p.n_in, p.cfg, p.tensor)).to(dev), p.n_in)
+            WT = torch.stack([wt] * copies)
+            x = torch.from_numpy(synth.inputs(p)).to(dev)
+            y = torch.empty(p.n_out, device=dev)
+            i = [0]
+
+            def run():
+                gemv(WT[i[0] % copies], x, tab, p.n_out, out=y)
+                i[0] += 1
+            u = _event_us(run, stream, args.steps, args.warmup)
+            b = p.n_out * (p.n_in // 256) * nbytes + 4 * (p.n_in + p.n_out)
+            singles[p.name] = {"us": round(u, 2), "GBs": round(b / u / 1e3, 1)}
+            del WT
+        out[name] = {"stream_us": round(us, 2), "stream_GBs": round(step / us / 1e3, 1),
+                     "frac": round(step / us / 1e3 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_step": step, "singles": singles}
+    best = max(out.values(), key=lambda v: v["stream_GBs"])
+    print(json.dumps({
+        "metric": "effective HBM GB/s, IQ3_S / IQ4_XS GEMV stream, batch 1",
+        "value": best["stream_GBs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "TinyLlama-1.1B-shaped per-token stream (155 GEMVs) in the IQ3_S and "
+                               "IQ4_XS formats, tile layout, one grouped launch each; single GEMVs "
+                               "of the IQ3 configuration's shapes, cold weights", **out},
+    }), flush=True)
 
 
 def bench_lm_head(args):

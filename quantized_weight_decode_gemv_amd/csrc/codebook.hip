@@ -11,6 +11,8 @@
 // Dequantization is bit-exact. The GEMV runs on a tile layout (each 64-row
 // block column regrouped by field, as for IQ3) with a 16-wavefront stream
 // engine whose decode table lives in LDS.
+#include <cstdlib>
+
 #include "qwg_device.h"
 
 namespace qwg {
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__res
 // (74+8G..), ninth bits [G][row][2] (66+2G..), sub-scale bytes [row][4]
 // (106..109), d [row][2] (0..1).
 struct Iq3sFmt {
+    static constexpr int kShape = 162;   // 10 * wavefronts + ring stages
     static constexpr int kBytes = kIq3sBytes;
     static constexpr int kCol = kTileRows * kIq3sBytes;
     static constexpr int kIdx = 0, kSign = 4096, kHb = 6144, kScale = 6656, kD = 6912;
@@ -177,6 +180,7 @@ struct Iq3sFmt {
 // IQ4_XS, 8704 bytes: codes [G][row][32] (bytes 8+32G..), header [row][8]
 // (bytes 0..7: d, the scales' top bits, their low nibbles).
 struct Iq4xsFmt {
+    static constexpr int kShape = 162;
     static constexpr int kBytes = kIq4xsBytes;
     static constexpr int kCol = kTileRows * kIq4xsBytes;
     static constexpr int kCodes = 0, kHead = 8192;
@@ -313,7 +317,7 @@ __device__ __forceinline__ void cb_load_item(CbItem &it, int k, const GroupArgs 
 template <class F, int G, int W, int R>
 __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &single,
                                           const float *tab, int nitems, uint8_t *smem) {
-    static_assert(R >= 2 && R <= 3, "ring of two or three stages");
+    static_assert(R >= 2 && R <= 4, "ring of two to four stages");
     using C = CbCfg<F, W, R>;
     constexpr int BPS = C::kBps;
     constexpr int kCp = C::copies(G);
@@ -370,8 +374,11 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
         float acc = 0.0f;
         for (int s = 0; s < c.nst; ++s) {
             const int nxt = slot_c + 1 == R ? 0 : slot_c + 1;
+            // copies of the stages after this one may stay in flight
             int younger = 0;
-            if (R >= 3 && pending > 1) younger = kCp * (int)((flags >> nxt) & 1u);
+            if (R >= 3 && pending > 1) younger += kCp * (int)((flags >> nxt) & 1u);
+            if (R >= 4 && pending > 2)
+                younger += kCp * (int)((flags >> (nxt + 1 == R ? 0 : nxt + 1)) & 1u);
             wait_vmcnt_upto(younger);
             lds_barrier();   // stage in slot_c complete for every wavefront (and the table)
             issue_next();
@@ -408,11 +415,12 @@ __global__ __launch_bounds__(W * 64) void cb_stream_kernel(GroupArgs g, GemvArgs
     }
 }
 
-constexpr int kCbWaves = 16;
-constexpr int kCbRing = 2;
+// Engine shapes (wavefronts, ring stages) that fit the LDS with the 64 KB
+// table. QWG_CB_SHAPE = 10*W + R picks one (tuning experiments).
+#define QWG_CB_SHAPES(X) X(16, 2) X(16, 3) X(12, 3) X(8, 4)
 
-template <class F>
-int cb_slots_f() {
+template <class F, int W, int R>
+int cb_slots_wr() {
     static int slots = 0;
     if (slots == 0) {
         int dev = 0, cus = 0, per_cu = 0;
@@ -420,25 +428,72 @@ int cb_slots_f() {
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus < 1)
             cus = 256;
-        constexpr size_t lds = CbCfg<F, kCbWaves, kCbRing>::kLds;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, cb_stream_kernel<F, kCbWaves, kCbRing>, kCbWaves * 64, lds) != hipSuccess ||
+        constexpr size_t lds = CbCfg<F, W, R>::kLds;
+        if (lds > 160 * 1024 ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cb_stream_kernel<F, W, R>, W * 64,
+                                                         lds) != hipSuccess ||
             per_cu < 1)
-            per_cu = 1;
+            per_cu = lds > 160 * 1024 ? 0 : 1;
         slots = per_cu * cus;
     }
     return slots;
 }
 
+template <class F, int W, int R>
+hipError_t cb_launch_wr(const GroupArgs &g, const GemvArgs &single, const float *tab, int nitems,
+                        hipStream_t s) {
+    int n = cb_slots_wr<F, W, R>();
+    if (n <= 0) return hipErrorInvalidValue;
+    if (n > nitems) n = nitems;
+    constexpr size_t lds = CbCfg<F, W, R>::kLds;
+    hipLaunchKernelGGL((cb_stream_kernel<F, W, R>), dim3((unsigned)n), dim3(W * 64), lds, s, g,
+                       single, tab, nitems);
+    return hipGetLastError();
+}
+
+template <class F>
+int cb_slots_any(int shape) {
+    switch (shape) {
+#define X(w, r) \
+    case 10 * w + r: return cb_slots_wr<F, w, r>();
+        QWG_CB_SHAPES(X)
+#undef X
+        default: return 0;
+    }
+}
+
+template <class F>
+int cb_shape() {
+    static const int v = [] {
+        const char *e = getenv("QWG_CB_SHAPE");
+        const int k = e ? atoi(e) : 0;
+        switch (k) {
+#define X(w, r) case 10 * w + r:
+            QWG_CB_SHAPES(X)
+#undef X
+            return cb_slots_any<F>(k) > 0 ? k : F::kShape;
+            default: return F::kShape;
+        }
+    }();
+    return v;
+}
+
+template <class F>
+int cb_slots_f() { return cb_slots_any<F>(cb_shape<F>()); }
+
+template <class F>
+int cb_bps_f() { return (cb_shape<F>() / 10) / 4; }
+
 template <class F>
 hipError_t cb_launch(const GroupArgs &g, const GemvArgs &single, const float *tab, int nitems,
                      hipStream_t s) {
-    int n = cb_slots_f<F>();
-    if (n > nitems) n = nitems;
-    constexpr size_t lds = CbCfg<F, kCbWaves, kCbRing>::kLds;
-    hipLaunchKernelGGL((cb_stream_kernel<F, kCbWaves, kCbRing>), dim3((unsigned)n),
-                       dim3(kCbWaves * 64), lds, s, g, single, tab, nitems);
-    return hipGetLastError();
+    switch (cb_shape<F>()) {
+#define X(w, r) \
+    case 10 * w + r: return cb_launch_wr<F, w, r>(g, single, tab, nitems, s);
+        QWG_CB_SHAPES(X)
+#undef X
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -480,7 +535,11 @@ int cb_stream_slots(int fmt) {
     return 0;
 }
 
-int cb_stream_bps() { return kCbWaves / 4; }
+int cb_stream_bps(int fmt) {
+    if (fmt == kFmtIq3s) return cb_bps_f<Iq3sFmt>();
+    if (fmt == kFmtIq4xs) return cb_bps_f<Iq4xsFmt>();
+    return 1;
+}
 
 hipError_t launch_cb_stream(int fmt, const GroupArgs &g, const GemvArgs &single, const float *tab,
                             int nitems, hipStream_t s) {

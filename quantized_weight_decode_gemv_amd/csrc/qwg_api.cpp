@@ -585,7 +585,7 @@ int cb_gemv_tiled(int fmt, float *y, const float *x, const void *w, const float 
     const int slots = cb_stream_slots(fmt);
     if (slots <= 0) return QWG_ERR_HIP;
     if (slots > 2 * a.tiles) {
-        int sp = stream_splits(a.nb, cb_stream_bps(), slots / a.tiles);
+        int sp = stream_splits(a.nb, cb_stream_bps(fmt), slots / a.tiles);
         while (sp > 1 && ((size_t)sp * a.tiles * kTileRows > kWsPartialFloats ||
                           (size_t)a.tiles > kWsCounters))
             --sp;
@@ -756,7 +756,7 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     StreamShape ssh = {4, 2};
     if (cb) {
         slots = cb_stream_slots(fmt);
-        bps = cb_stream_bps();
+        bps = cb_stream_bps(fmt);
     } else if (iq3) {
         const Iq3Shape ish = iq3_shape(true, 0);
         slots = iq3_stream_slots(ish, layout == kLayoutTiles);

@@ -118,7 +118,7 @@ hipError_t launch_iq4xs_dequant(const uint8_t *src, const float *table, float *d
 hipError_t launch_cb_pack_tiles(int fmt, const uint8_t *src, uint8_t *dst, int nb, int n_out,
                                 hipStream_t s);
 int cb_stream_slots(int fmt);   // resident workgroups on the current device (0: unknown format)
-int cb_stream_bps();            // super-blocks per pipeline stage
+int cb_stream_bps(int fmt);     // super-blocks per pipeline stage
 hipError_t launch_cb_stream(int fmt, const GroupArgs &g, const GemvArgs &single, const float *tab,
                             int nitems, hipStream_t s);
 
