@@ -12,6 +12,8 @@ What it computes, and where the pages define it:
   docstring, ``get_d``, ``get_s``, ``eff_np`` and ``dequant``.
 * IQ3_S and IQ4_XS: the same page (format table, ``get_s``, ``eff_np``,
   ``dequant``; the IQ3_S branch of ``encode`` for its code bytes).
+* IQ3 encoder: iq3_pack.py page, ``encode()`` (float32, numpy's evaluation
+  order; see ``orc_encode_iq3``).
 * GEMV / GEMM: ``y = W @ x`` over the fp32 dequantized rows, accumulated in fp64
   with k ascending, plus ``s = sum |w * x|`` for the per-row error bound
   (argument order of picoLM's ``matmul(out, x, W, n_in, n_out, type)`` call in
@@ -60,6 +62,9 @@ def lib():
         I64 = ctypes.c_int64
         L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
         L.orc_f16_to_f32.restype = ctypes.c_float
+        L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_encode_iq3.argtypes = [P, P, I64, I64, P]
         L.orc_q4k_unpack_scales.argtypes = [P, P, P]
         L.orc_q4k_pack_scales.argtypes = [P, P, P]
         L.orc_dequant_q4k.argtypes = [P, I64, P]
@@ -82,7 +87,8 @@ def lib():
                      "orc_gemm_q4k", "orc_gemv_q4k_rows", "orc_gemv_iq3_rows",
                      "orc_dequant_iq3_xxs", "orc_gemv_iq3_xxs", "orc_gemv_iq3_xxs_rows",
                      "orc_dequant_iq3s", "orc_gemv_iq3s", "orc_gemv_iq3s_rows",
-                     "orc_dequant_iq4xs", "orc_gemv_iq4xs", "orc_gemv_iq4xs_rows"):
+                     "orc_dequant_iq4xs", "orc_gemv_iq4xs", "orc_gemv_iq4xs_rows",
+                     "orc_encode_iq3"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -248,6 +254,26 @@ def gemv_iq3s_rows(w, grid, x, n_in: int, rows):
 
 def gemv_iq4xs_rows(w, table, x, n_in: int, rows):
     return _tabled_rows("iq4xs", w, table, x, n_in, rows)
+
+
+def f32_to_f16(v: float) -> int:
+    """binary16 bits of the float32 value v, rounded to nearest even."""
+    return int(lib().orc_f32_to_f16(float(np.float32(v))))
+
+
+def encode_iq3(x, grid) -> np.ndarray:
+    """fp32 x [n_rows, n_in] (n_in % 256 == 0, finite) -> uint8 [n_rows, n_in/256*98]
+    98-byte IQ3 blocks (iq3_pack.py page, encode()), grid [256, 4] in weight units."""
+    x = _f32(x)
+    if x.ndim != 2 or x.shape[1] % QK:
+        raise ValueError("x must be [n_rows, n_in] with n_in % 256 == 0")
+    grid = _f32(grid)
+    if grid.shape != (256, 4):
+        raise ValueError("grid must be [256, 4]")
+    out = np.empty((x.shape[0], x.shape[1] // QK * IQ3_BYTES), np.uint8)
+    _check(lib().orc_encode_iq3(_ptr(x), _ptr(grid), x.shape[0], x.shape[1], _ptr(out)),
+           "encode_iq3")
+    return out
 
 
 def gemv_q4k(w, x, n_in: int, n_out: int) -> tuple[np.ndarray, np.ndarray]:

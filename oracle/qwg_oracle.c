@@ -45,6 +45,38 @@ float orc_f16_to_f32(uint16_t h)
     return (float)(sign ? -v : v);
 }
 
+/*
+ * binary32 -> binary16, round to nearest even (IEEE 754): magnitudes from
+ * 65520 up become infinity, those below 2^-14 are multiples of 2^-24, the
+ * rest have 11 significant bits. Evaluated in double, where every step is
+ * exact except rint's rounding, which is the mode's (nearest even).
+ * [iq3pack] stores d as fp16 (astype(np.float16)).
+ */
+uint16_t orc_f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (isnan(f))
+        return sign | 0x7E00;
+    double a = fabs((double)f);
+    if (a >= 65520.0)
+        return sign | 0x7C00;
+    if (a < ldexp(1.0, -14))
+        return sign | (uint16_t)rint(ldexp(a, 24));   /* 1024 is the smallest normal */
+    int e;
+    frexp(a, &e);
+    int E = e - 1;                                      /* 2^E <= a < 2^(E+1) */
+    double n = rint(ldexp(a, 10 - E));                  /* 1024 .. 2048 */
+    if (n >= 2048.0) {
+        n = 1024.0;
+        E += 1;
+    }
+    if (E > 15)
+        return sign | 0x7C00;
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)(n - 1024.0);
+}
+
 /* ------------------------------------------------------------------ Q4_K */
 
 /*
@@ -308,6 +340,163 @@ int orc_dequant_iq4xs(const uint8_t *src, const float *table, int64_t n, float *
         return 2;
     for (int64_t ib = 0; ib < n / ORC_QK; ++ib)
         iq4xs_block(src + ORC_IQ4XS_BYTES * ib, table, dst + ORC_QK * ib);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ IQ3 encoder */
+
+/*
+ * A float32 sum in numpy's pairwise order (its add.reduce over a contiguous
+ * axis): below 8 terms, one running sum from 0; up to 128 terms, eight running
+ * sums r[j] over elements j, j+8, j+16, ..., combined as
+ * ((r0+r1)+(r2+r3))+((r4+r5)+(r6+r7)), then any remainder added in order;
+ * longer runs split at n/2 rounded down to a multiple of 8, halves summed this
+ * way and added.
+ */
+static float np_pairwise(const float *a, int n)
+{
+    if (n < 8) {
+        float r = 0.0f;
+        for (int i = 0; i < n; ++i)
+            r += a[i];
+        return r;
+    }
+    if (n <= 128) {
+        float r[8];
+        for (int j = 0; j < 8; ++j)
+            r[j] = a[j];
+        int i;
+        for (i = 8; i < n - (n % 8); i += 8)
+            for (int j = 0; j < 8; ++j)
+                r[j] += a[i + j];
+        float res = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
+        for (; i < n; ++i)
+            res += a[i];
+        return res;
+    }
+    int n2 = n / 2;
+    n2 -= n2 % 8;
+    return np_pairwise(a, n2) + np_pairwise(a + n2, n - n2);
+}
+
+/*
+ * [iq3pack] encode(), one 256-weight super-block, in float32 as the page's
+ * numpy evaluates it:
+ *  1. signs (negative when x < 0) and magnitudes; in every group of eight
+ *     whose signs multiply to -1, the sign of the first smallest magnitude is
+ *     flipped, so the stored seven signs and their parity describe the group;
+ *  2. d = sqrt(mean(mag^2)) / 20 + 1e-12 (mean: pairwise sum / 256), stored
+ *     as fp16, and the stored value is used from here on;
+ *  3. per 32-weight sub-block, for every code 0..15: db = d*(0.5+code)*0.5,
+ *     each group of four magnitudes divided by max(db, 1e-20) goes to the grid
+ *     row of least g2 - 2*(q.g) (g2 = the row's sum of squares; the first such
+ *     row), and the code's error is the pairwise sum of (grid*db - mag)^2 over
+ *     the 32 weights; the first code of least error is kept;
+ *  4. index bytes, the four 7-bit sign groups and the code form the word.
+ * The page leaves the matrix product's order to its BLAS; here q.g is summed
+ * left to right, product by product, without fused multiply-adds.
+ */
+static void iq3_encode_block(const float *x, const float *grid, const float *g2, uint8_t *out)
+{
+    float sign[256], mag[256], sq[256];
+    for (int t = 0; t < 256; ++t) {
+        sign[t] = x[t] < 0.0f ? -1.0f : 1.0f;
+        mag[t] = fabsf(x[t]);
+    }
+    for (int b = 0; b < 32; ++b) {
+        int neg = 0;
+        for (int j = 0; j < 8; ++j)
+            neg += sign[8 * b + j] < 0.0f;
+        if (neg & 1) {
+            int am = 0;
+            for (int j = 1; j < 8; ++j)
+                if (mag[8 * b + j] < mag[8 * b + am])
+                    am = j;
+            sign[8 * b + am] = -sign[8 * b + am];
+        }
+    }
+    for (int t = 0; t < 256; ++t)
+        sq[t] = mag[t] * mag[t];
+    float mean = np_pairwise(sq, 256) / 256.0f;
+    float d = sqrtf(mean) / 20.0f + 1e-12f;
+    uint16_t dh = orc_f32_to_f16(d);
+    out[96] = (uint8_t)(dh & 0xFF);
+    out[97] = (uint8_t)(dh >> 8);
+    float dv = orc_f16_to_f32(dh);
+    for (int ib = 0; ib < 8; ++ib) {
+        const float *m = mag + 32 * ib;
+        float best_err = 0.0f;
+        int best_code = 0;
+        uint8_t best_idx[8] = {0};
+        for (int code = 0; code < 16; ++code) {
+            float db = dv * (0.5f + (float)code);
+            db = db * 0.5f;
+            float den = db > 1e-20f ? db : 1e-20f;
+            uint8_t idx[8];
+            float terms[32];
+            for (int g = 0; g < 8; ++g) {
+                float q[4];
+                for (int c = 0; c < 4; ++c)
+                    q[c] = m[4 * g + c] / den;
+                int bi = 0;
+                float bs = 0.0f;
+                for (int e = 0; e < 256; ++e) {
+                    const float *ge = grid + 4 * e;
+                    float dot = q[0] * ge[0];
+                    dot = dot + q[1] * ge[1];
+                    dot = dot + q[2] * ge[2];
+                    dot = dot + q[3] * ge[3];
+                    float sc = g2[e] - 2.0f * dot;
+                    if (e == 0 || sc < bs) {
+                        bs = sc;
+                        bi = e;
+                    }
+                }
+                idx[g] = (uint8_t)bi;
+                for (int c = 0; c < 4; ++c) {
+                    float rec = grid[4 * bi + c] * db;
+                    float df = rec - m[4 * g + c];
+                    terms[4 * g + c] = df * df;
+                }
+            }
+            float err = np_pairwise(terms, 32);
+            if (code == 0 || err < best_err) {
+                best_err = err;
+                best_code = code;
+                memcpy(best_idx, idx, 8);
+            }
+        }
+        uint32_t word = (uint32_t)best_code << 28;
+        for (int l = 0; l < 4; ++l) {
+            uint32_t seven = 0;
+            for (int j = 0; j < 7; ++j)
+                seven |= (uint32_t)(sign[32 * ib + 8 * l + j] < 0.0f) << j;
+            word |= seven << (7 * l);
+        }
+        memcpy(out + 8 * ib, best_idx, 8);
+        for (int k = 0; k < 4; ++k)
+            out[64 + 4 * ib + k] = (uint8_t)(word >> (8 * k));
+    }
+}
+
+int orc_encode_iq3(const float *x, const float *grid, int64_t n_rows, int64_t n_in, uint8_t *dst)
+{
+    if (!x || !grid || !dst)
+        return 1;
+    if (n_rows < 1 || n_in <= 0 || n_in % ORC_QK)
+        return 2;
+    float g2[256];
+    for (int e = 0; e < 256; ++e) {
+        float r = 0.0f;   /* numpy's order for four terms: one running sum from 0 */
+        for (int c = 0; c < 4; ++c)
+            r += grid[4 * e + c] * grid[4 * e + c];
+        g2[e] = r;
+    }
+    const int64_t nb = n_in / ORC_QK;
+    int nth = orc_get_threads();
+#pragma omp parallel for num_threads(nth) schedule(static)
+    for (int64_t k = 0; k < n_rows * nb; ++k)
+        iq3_encode_block(x + k * ORC_QK, grid, g2, dst + k * ORC_IQ3_BYTES);
     return 0;
 }
 

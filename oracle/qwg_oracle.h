@@ -36,6 +36,8 @@ extern "C" {
 
 /* IEEE 754 binary16 -> binary32, exact (subnormals, infinities, NaN). */
 float orc_f16_to_f32(uint16_t h);
+/* binary32 -> binary16 bits, round to nearest even. */
+uint16_t orc_f32_to_f16(float f);
 
 /* The 12-byte packed 6-bit scale/min field of a Q4_K block <-> sc[8], mn[8]. */
 void orc_q4k_unpack_scales(const uint8_t p[12], uint8_t sc[8], uint8_t mn[8]);
@@ -80,6 +82,14 @@ int orc_gemv_iq3s_rows(const uint8_t *w, const float *grid, const float *x, int6
                        const int64_t *rows, int64_t nrows, double *y, double *s);
 int orc_gemv_iq4xs_rows(const uint8_t *w, const float *table, const float *x, int64_t n_in,
                         const int64_t *rows, int64_t nrows, double *y, double *s);
+
+/*
+ * The iq3_pack.py page's encode(): x [n_rows][n_in] fp32 (finite, n_in % 256
+ * == 0) -> n_rows rows of n_in/256 98-byte blocks, with `grid` [256][4] in
+ * weight units. Float32 throughout, in the order the function's comment
+ * states.
+ */
+int orc_encode_iq3(const float *x, const float *grid, int64_t n_rows, int64_t n_in, uint8_t *dst);
 
 /* OpenMP thread count used by the GEMVs (rows are independent, so the result
  * does not depend on it). */

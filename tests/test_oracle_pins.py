@@ -501,6 +501,143 @@ def test_gemv_codebook_formats_match_numpy_matmul(fmt):
     assert np.array_equal(yr, y[[8, 0, 3]]) and np.array_equal(sr, s[[8, 0, 3]])
 
 
+# ---------------------------------------------------------------- IQ3 encoder
+# Pins of the iq3_pack.py page's encode(): fp16 rounding against numpy's, the
+# stored d against numpy's float32 RMS formula, the parity-fix rule, the
+# sub-block search against an fp64 brute force (where no near-tie decides),
+# and closed-form special cases.
+
+def test_f32_to_f16_matches_numpy():
+    rng = np.random.default_rng(40)
+    specials = [0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 65536.0, 1e30, -1e30,
+                2.0 ** -14, 2.0 ** -24, 2.0 ** -25, 1.5 * 2.0 ** -24, 2.0 ** -26, 6.1e-5, 1e-12,
+                np.inf, -np.inf, 0.000123, 1024.5, 2049.0, 2051.0, 3.0 * 2.0 ** -25]
+    vals = np.concatenate([np.array(specials, np.float32),
+                           rng.standard_normal(20000).astype(np.float32) * 10.0 ** rng.integers(-9, 6, 20000),
+                           rng.integers(0, 2 ** 32, 20000, dtype=np.uint64).astype(np.uint32).view(np.float32)])
+    vals = vals[~np.isnan(vals)]
+    with np.errstate(over="ignore"):
+        want = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f32_to_f16(v) for v in vals], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def _encode_case(n_rows, n_in, seed, scale=0.02):
+    x = (np.random.default_rng(seed).standard_normal((n_rows, n_in)) * scale).astype(np.float32)
+    grid = synth.iq3_grid()
+    return x, grid, oracle.encode_iq3(x, grid)
+
+
+def test_encode_d_is_the_rms_anchor():
+    x, grid, b = _encode_case(3, 768, 41)
+    blocks = b.reshape(-1, 98)
+    xs = x.reshape(-1, 256)
+    mag = np.abs(xs)
+    d = np.sqrt((mag * mag).mean(-1, keepdims=True)) / 20.0 + 1e-12
+    assert d.dtype == np.float32
+    want = d.astype(np.float16).view(np.uint16)[:, 0]
+    got = blocks[:, 96:98].copy().view(np.uint16)[:, 0]
+    assert np.array_equal(got, want)
+
+
+def test_encode_parity_fix():
+    x, grid, b = _encode_case(4, 512, 42)
+    # decode with an all-ones grid: the output's signs are the stored signs
+    ones = np.ones((256, 4), np.float32)
+    w = oracle.dequant_iq3(b, ones, x.size).reshape(-1, 8)
+    xs = x.reshape(-1, 8)
+    for g in range(xs.shape[0]):
+        want = xs[g] < 0
+        if want.sum() % 2:
+            want = want.copy()
+            am = int(np.argmin(np.abs(xs[g])))
+            want[am] = not want[am]
+        got = w[g] < 0
+        assert np.array_equal(got, want), g
+        assert got.sum() % 2 == 0
+
+
+def test_encode_search_matches_fp64_brute_force():
+    x, grid, b = _encode_case(2, 1024, 43)
+    g64 = grid.astype(np.float64)
+    blocks = b.reshape(-1, 98)
+    xs = np.abs(x.reshape(-1, 256)).astype(np.float64)
+    checked = 0
+    for k in range(blocks.shape[0]):
+        d = float(blocks[k, 96:98].copy().view(np.float16)[0])
+        for ib in range(8):
+            m = xs[k, 32 * ib:32 * ib + 32].reshape(8, 4)
+            errs, idxs = [], []
+            for code in range(16):
+                db = d * (0.5 + code) * 0.5
+                dist = ((g64[None, :, :] * db - m[:, None, :]) ** 2).sum(-1)   # [8 groups, 256]
+                idx = dist.argmin(-1)
+                idxs.append(idx)
+                errs.append(dist[np.arange(8), idx].sum())
+            errs = np.array(errs)
+            best = int(errs.argmin())
+            second = np.partition(errs, 1)[1]
+            if second - errs[best] < 1e-4 * errs[best]:
+                continue          # a near-tie: fp32 may pick either
+            word = int(blocks[k, 64 + 4 * ib:68 + 4 * ib].view("<u4")[0])
+            assert word >> 28 == best, (k, ib)
+            # the chosen rows: nearest per group unless that group is itself near-tied
+            db = d * (0.5 + best) * 0.5
+            dist = ((g64[None, :, :] * db - m[:, None, :]) ** 2).sum(-1)
+            srt = np.sort(dist, -1)
+            for g in range(8):
+                if srt[g, 1] - srt[g, 0] > 1e-5 * max(srt[g, 0], 1e-30):
+                    assert blocks[k, 8 * ib + g] == idxs[best][g], (k, ib, g)
+            checked += 1
+    assert checked >= 24
+
+
+def test_encode_zero_and_exact_grid_cases():
+    grid = synth.iq3_grid()
+    g2 = (grid.astype(np.float32) ** 2).sum(-1)
+    b = oracle.encode_iq3(np.zeros((1, 256), np.float32), grid)[0]
+    # d = fp16(1e-12) = 0, every code reconstructs zero: code 0, the first row of least norm
+    assert b[96] == 0 and b[97] == 0
+    assert (b[:64] == int(np.argmin(g2))).all()
+    assert all(int(b[64 + 4 * ib:68 + 4 * ib].view("<u4")[0]) == 0 for ib in range(8))
+    # every group an exact grid row: the encoder returns those rows and reconstructs the
+    # magnitudes exactly for the code whose db makes them fit
+    rows = np.random.default_rng(44).integers(0, 256, 64)
+    mag = grid[rows].reshape(256).astype(np.float32)
+    d_bits = oracle.f32_to_f16(np.sqrt(np.float32((mag * mag).mean())) / np.float32(20) + np.float32(1e-12))
+    d = float(np.array([d_bits], np.uint16).view(np.float16)[0])
+    b = oracle.encode_iq3(mag.reshape(1, 256), grid)[0]
+    w = oracle.dequant_iq3(b, grid, 256)
+    assert int(b[96]) | int(b[97]) << 8 == d_bits
+    err = np.abs(w - mag)
+    assert (w >= 0).all() and err.max() <= 0.5 * d * 31 * 1.0 + 1e-6
+
+
+def test_encode_ties_go_to_the_first_row():
+    # Duplicate grid rows score identically in any arithmetic: the later copy
+    # must never be chosen (the page's argmin keeps the first minimum).
+    grid = synth.iq3_grid().copy()
+    for a, b in ((3, 200), (17, 18), (0, 255)):
+        grid[b] = grid[a]
+    x = (np.random.default_rng(46).standard_normal((8, 1024)) * 0.02).astype(np.float32)
+    idx = oracle.encode_iq3(x, grid).reshape(-1, 98)[:, :64]
+    used = set(np.unique(idx).tolist())
+    assert used.isdisjoint({200, 18, 255})
+    assert {3, 17, 0} & used
+
+
+def test_encode_roundtrip_error_and_threads():
+    x, grid, b = _encode_case(4, 2048, 45)
+    w = oracle.dequant_iq3(b, grid, x.size).reshape(x.shape)
+    rel = np.sqrt(((w - x) ** 2).mean()) / np.sqrt((x ** 2).mean())
+    assert rel < 0.3
+    oracle.set_threads(1)
+    try:
+        assert np.array_equal(oracle.encode_iq3(x, grid), b)
+    finally:
+        oracle.set_threads(0)
+
+
 # ---------------------------------------------------------------- GEMV / GEMM
 
 def _q4k_case(n_out, n_in, seed):
