@@ -171,6 +171,22 @@ int qwg_gemv_iq3_xxs(float *y, const float *x, const void *w, const float *grid,
                      int64_t n_out, void *stream);
 
 /*
+ * IQ3 container encoder (iq3_pack.py page, encode()): fp32 weights x
+ * [n_rows][n_in] (finite; n_in % 256 == 0; 4-byte aligned) -> n_rows rows of
+ * n_in/256 98-byte blocks at dst (no alignment needed), with the grid [256][4]
+ * in weight units (16-byte aligned). Per 256-weight super-block: the parity
+ * fix (in each group of eight whose signs multiply to -1, the sign of the
+ * first smallest magnitude flips), d = fp16(sqrt(mean(x^2))/20 + 1e-12), and
+ * per 32-weight sub-block the code 0..15 and grid rows of least squared error
+ * (rows by the least g2 - 2 q.g, q = magnitudes / max(db, 1e-20)). Every step
+ * is float32 in a fixed order (numpy's pairwise sums for the mean and the
+ * errors, q.g summed left to right without fused multiply-adds, first minimum
+ * on ties), so the bytes are reproducible and match the CPU reference.
+ */
+int qwg_encode_iq3(void *dst, const float *x, const float *grid, int64_t n_rows, int64_t n_in,
+                   void *stream);
+
+/*
  * IQ3_S and IQ4_XS (codebook.py page; layouts above).
  * qwg_dequant_iq3s: src n/256 blocks of 110 bytes (2-byte aligned), grid
  * [512][4] fp32 (16-byte aligned), dst n fp32 (16-byte aligned).

@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
         L.qwg_dequant_iq3_xxs.argtypes = [P, P, P, I64, P]
         L.qwg_gemv_iq3_xxs.argtypes = [P, P, P, P, I64, I64, P]
         L.qwg_pack_iq3_xxs_tiles.argtypes = [P, P, I64, I64, P]
+        L.qwg_encode_iq3.argtypes = [P, P, P, I64, I64, P]
         for name in ("iq3s", "iq4xs"):
             getattr(L, f"qwg_dequant_{name}").argtypes = [P, P, P, I64, P]
             getattr(L, f"qwg_pack_{name}_tiles").argtypes = [P, P, I64, I64, P]
@@ -316,6 +317,24 @@ def gemv_iq3_xxs(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
         raise ValueError("out has the wrong size")
     _check(lib().qwg_gemv_iq3_xxs(out.data_ptr(), x.data_ptr(), w.data_ptr(), grid.data_ptr(),
                                   n_in, n_out, _stream(x)), "qwg_gemv_iq3_xxs")
+    return out
+
+
+def encode_iq3(x: torch.Tensor, grid: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 weights x [n_rows, n_in] (n_in % 256 == 0) -> uint8 [n_rows, n_in/256*98]
+    IQ3 container blocks (iq3_pack.py page, encode()); grid fp32 [256, 4] in weight units."""
+    _dev(x, "x", torch.float32)
+    _grid(grid)
+    if x.dim() != 2 or x.shape[1] % QK:
+        raise ValueError("x must be [n_rows, n_in] with n_in a multiple of 256")
+    n_rows, n_in = x.shape
+    if out is None:
+        out = torch.empty(n_rows, n_in // QK * IQ3_BYTES, dtype=torch.uint8, device=x.device)
+    _dev(out, "out", torch.uint8)
+    if out.numel() != n_rows * (n_in // QK) * IQ3_BYTES:
+        raise ValueError("out has the wrong size")
+    _check(lib().qwg_encode_iq3(out.data_ptr(), x.data_ptr(), grid.data_ptr(), n_rows, n_in,
+                                _stream(x)), "qwg_encode_iq3")
     return out
 
 

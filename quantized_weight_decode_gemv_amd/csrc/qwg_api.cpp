@@ -547,6 +547,16 @@ int qwg_pack_iq3_xxs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_o
     return iq3_pack(dst, src, n_in, n_out, true, stream);
 }
 
+int qwg_encode_iq3(void *dst, const float *x, const float *grid, int64_t n_rows, int64_t n_in,
+                   void *stream) {
+    if (!dst || !x || !grid) return QWG_ERR_NULL;
+    if (n_rows < 1 || n_rows > QWG_MAX_N_OUT || n_in <= 0 || n_in % kQK || n_in > QWG_MAX_N_IN)
+        return QWG_ERR_SHAPE;
+    if (!aligned(x, 4) || !aligned(grid, 16)) return QWG_ERR_ALIGN;
+    return hip_status(launch_iq3_encode(x, grid, (uint8_t *)dst, n_rows * (n_in / kQK),
+                                        (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------------ IQ3_S, IQ4_XS
 
 namespace {

@@ -122,4 +122,9 @@ int cb_stream_bps(int fmt);     // super-blocks per pipeline stage
 hipError_t launch_cb_stream(int fmt, const GroupArgs &g, const GemvArgs &single, const float *tab,
                             int nitems, hipStream_t s);
 
+// IQ3 container encoder (encode.hip): x [nblocks][256] fp32 -> nblocks 98-byte
+// blocks, grid [256][4] in weight units.
+hipError_t launch_iq3_encode(const float *x, const float *grid, uint8_t *dst, int64_t nblocks,
+                             hipStream_t s);
+
 }  // namespace qwg

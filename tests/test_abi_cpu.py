@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
                  "qwg_gemv_iq3_xxs", "qwg_pack_iq3_xxs_tiles", "qwg_dequant_iq3s",
                  "qwg_dequant_iq4xs", "qwg_pack_iq3s_tiles", "qwg_pack_iq4xs_tiles",
                  "qwg_gemv_iq3s_tiled", "qwg_gemv_iq4xs_tiled", "qwg_group_create_iq3s_tiled",
-                 "qwg_group_create_iq4xs_tiled"):
+                 "qwg_group_create_iq4xs_tiled", "qwg_encode_iq3"):
         assert want in names
 
 
@@ -173,6 +173,14 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE, FAKE, 0, 1, None), 2),
     (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE + 4, FAKE, 256, 1, None), 3),
     (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE, FAKE + 1, 256, 1, None), 3),
+    # IQ3 encoder
+    (lambda L: L.qwg_encode_iq3(None, FAKE, FAKE, 1, 256, None), 1),
+    (lambda L: L.qwg_encode_iq3(FAKE, None, FAKE, 1, 256, None), 1),
+    (lambda L: L.qwg_encode_iq3(FAKE, FAKE, None, 1, 256, None), 1),
+    (lambda L: L.qwg_encode_iq3(FAKE, FAKE, FAKE, 0, 256, None), 2),
+    (lambda L: L.qwg_encode_iq3(FAKE, FAKE, FAKE, 1, 300, None), 2),
+    (lambda L: L.qwg_encode_iq3(FAKE, FAKE + 2, FAKE, 1, 256, None), 3),
+    (lambda L: L.qwg_encode_iq3(FAKE, FAKE, FAKE + 4, 1, 256, None), 3),
     # IQ3_S / IQ4_XS
     (lambda L: L.qwg_dequant_iq3s(None, FAKE, FAKE, 256, None), 1),
     (lambda L: L.qwg_dequant_iq3s(FAKE, FAKE, FAKE, 257, None), 2),

@@ -1139,3 +1139,51 @@ def test_codebook_group_stream_sampled_rows(fmt):
         yr, sr = c["o_rows"](w, tab, x, p.n_in, rows)
         assert_bound(host(y)[rows], yr, sr, f"{fmt} stream {p.name}")
     g.close()
+
+
+# ---------------------------------------------------------------- IQ3 encoder
+# Every step of the encoder is float32 in a fixed order on both sides, so the
+# bytes must be identical.
+
+def _enc_input(n_rows, n_in, seed, scale=0.02):
+    return (np.random.default_rng(seed).standard_normal((n_rows, n_in)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("n_rows,n_in", [(1, 256), (3, 2048), (64, 5632), (200, 768)])
+def test_encode_iq3_bytes_match_oracle(n_rows, n_in):
+    grid = synth.iq3_grid()
+    x = _enc_input(n_rows, n_in, 170 + n_rows)
+    got = host(qwg.encode_iq3(dev(x), dev(grid)))
+    want = oracle.encode_iq3(x, grid)
+    diff = np.nonzero((got != want).any(axis=1))[0]
+    assert diff.size == 0, f"rows {diff[:5]} differ"
+
+
+def test_encode_iq3_edge_values():
+    grid = synth.iq3_grid()
+    rng = np.random.default_rng(171)
+    rows = [np.zeros(512, np.float32),                                  # d = 0
+            (rng.standard_normal(512) * 1e-6).astype(np.float32),      # subnormal fp16 d
+            (rng.standard_normal(512) * 1e5).astype(np.float32),       # large d
+            (rng.standard_normal(512) * 1e7).astype(np.float32),       # d overflows to infinity
+            np.where(rng.random(512) < 0.5, -1.0, 1.0).astype(np.float32),   # equal magnitudes
+            -np.abs(rng.standard_normal(512)).astype(np.float32),      # all negative
+            np.repeat(rng.standard_normal(64), 8).astype(np.float32)]  # ties inside groups
+    x = np.stack(rows)
+    got = host(qwg.encode_iq3(dev(x), dev(grid)))
+    want = oracle.encode_iq3(x, grid)
+    for r in range(len(rows)):
+        assert np.array_equal(got[r], want[r]), f"row {r}"
+
+
+def test_encode_iq3_duplicate_grid_rows_and_gemv_roundtrip():
+    grid = synth.iq3_grid().copy()
+    grid[200] = grid[3]
+    x = _enc_input(96, 2048, 172)
+    b = qwg.encode_iq3(dev(x), dev(grid))
+    assert np.array_equal(host(b), oracle.encode_iq3(x, grid))
+    # the encoded matrix multiplies as its decode
+    v = synth.activations(2048, 172, 0)
+    y = host(qwg.gemv_iq3(b, dev(v), dev(grid)))
+    yr, sr = oracle.gemv_iq3(host(b), grid, v, 2048, 96)
+    assert_bound(y, yr, sr, "encoded gemv")
