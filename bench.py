@@ -26,12 +26,13 @@ back-to-back launches); and the CPU oracle's throughput on the host cores
 (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--headline-only]
-       python bench.py --workload iq3_stream|iq3_xxs|codebooks|lm_head [--steps K] [--warmup W]
+       python bench.py --workload iq3_stream|iq3_xxs|codebooks|encode|lm_head [--steps K] [--warmup W]
 The second form measures the other hot-path rows on their own (one JSON line each, for the
 record and for profiling): "iq3_stream" = the same 155 GEMV shapes in the IQ3 container as one
 grouped launch (IQ3 tile layout; the row-major launch beside it); "iq3_xxs" = IQ3_XXS blocks in
 llama.cpp's byte order (single GEMVs row-major and repacked, and the stream repacked); "codebooks" =
-the same stream and single shapes in IQ3_S and IQ4_XS (tile layout); "lm_head" = the 32000x2048 Q4_K LM head at batch 1..8 (qwg_gemv_q4k,
+the same stream and single shapes in IQ3_S and IQ4_XS (tile layout); "encode" = the IQ3 container
+encoder on the IQ3 configuration's matrices (an ALU-bound roofline); "lm_head" = the 32000x2048 Q4_K LM head at batch 1..8 (qwg_gemv_q4k,
 qwg_gemv_q4k_tiled, qwg_gemm_q4k), cycling over enough weight copies that every launch streams
 from HBM rather than the last-level cache.
 """
@@ -85,7 +86,7 @@ def parse():
     ap.add_argument("--print-kernel-hash", action="store_true",
                     help="print the hash of the kernel sources the traffic figure is tied to")
     ap.add_argument("--workload", default="q4k_stream",
-                    choices=["q4k_stream", "iq3_stream", "iq3_xxs", "codebooks", "lm_head"],
+                    choices=["q4k_stream", "iq3_stream", "iq3_xxs", "codebooks", "encode", "lm_head"],
                     help="q4k_stream: the headline (default); the others: see the module docstring")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline launch (no row-major, layered or per-call "
@@ -132,6 +133,9 @@ def main():
         return
     if args.workload == "codebooks":
         bench_codebooks(args)
+        return
+    if args.workload == "encode":
+        bench_encode(args)
         return
 
     import numpy as np
@@ -463,6 +467,56 @@ def bench_codebooks(args):
         "config": {"workload": "TinyLlama-1.1B-shaped per-token stream (155 GEMVs) in the IQ3_S and "
                                "IQ4_XS formats, tile layout, one grouped launch each; single GEMVs "
                                "of the IQ3 configuration's shapes, cold weights", **out},
+    }), flush=True)
+
+
+# Vector-ALU operations per weight of the IQ3 encoder's search (the rest is
+# negligible): 16 codes x 256 grid rows per group of four weights, each row
+# 4 multiplies + 3 adds (q.g), a doubling and a subtract (g2 - 2 q.g), a
+# compare and two selects (the running minimum) = 12 operations.
+ENCODE_OPS_PER_WEIGHT = 16 * 256 * 12 / 4
+# 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz: a wave64 fp32 instruction issues in
+# two cycles on MI355X (the vendor's 157.3 TFLOP/s fp32 vector figure is this
+# rate counting an FMA as two; the encoder itself sustains 0.45 wave64
+# instructions per SIMD-cycle, more than a four-cycle issue allows). Its
+# search uses no packed or fused forms.
+VALU_PEAK_OPS = 256 * 4 * 32 * 2.4e9
+
+
+def bench_encode(args):
+    """The IQ3 container encoder on the IQ3 configuration's two matrices
+    (5632x2048, 2048x5632) of seeded N(0, 0.02) weights."""
+    import torch
+    import quantized_weight_decode_gemv_amd as qwg
+    from quantized_weight_decode_gemv_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    grid = torch.from_numpy(synth.iq3_grid()).to(dev)
+    res = {}
+    total_w, total_us = 0, 0.0
+    steps, warm = max(3, args.steps // 30), max(2, args.warmup // 100)
+    for p in synth.config(4):
+        g = torch.Generator(device="cpu").manual_seed(180 + p.tensor)
+        x = (torch.randn(p.n_out, p.n_in, generator=g) * 0.02).to(dev)
+        out = torch.empty(p.n_out, p.n_in // 256 * 98, dtype=torch.uint8, device=dev)
+        us = _event_us(lambda: qwg.encode_iq3(x, grid, out=out), stream, steps, warm)
+        n = p.n_out * p.n_in
+        res[p.name] = {"us": round(us, 1), "Mweights_per_s": round(n / us, 1)}
+        total_w += n
+        total_us += us
+    ops = ENCODE_OPS_PER_WEIGHT * total_w / (total_us * 1e-6)
+    print(json.dumps({
+        "metric": "IQ3 container encode throughput (weights/s)",
+        "value": round(total_w / total_us * 1e6, 1), "unit": "weights/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "higher_is_better": True, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qwg_encode_iq3 on 5632x2048 and 2048x5632 N(0, 0.02) fp32 weights",
+                   **res},
+        "roofline": {"bound": "alu", "achieved": round(ops / 1e12, 2), "peak": VALU_PEAK_OPS / 1e12,
+                     "unit": "Tops/s", "frac": round(ops / VALU_PEAK_OPS, 4),
+                     "ops_per_weight": ENCODE_OPS_PER_WEIGHT, "kernel": "iq3_encode_kernel"},
     }), flush=True)
 
 
