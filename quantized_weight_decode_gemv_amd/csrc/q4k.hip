@@ -336,13 +336,16 @@ __global__ __launch_bounds__(W * 64) void q4k_gemv_kernel(GemvArgs a) {
 // lanes 0-31 keep C1's rows 0-7, lanes 32-63 C2's rows 8-15, so each lane ends
 // with one weight row, one sub-block and four batch rows.
 //
-// A stage holds one super-block column: the 64 rows' blocks (9216 B, copied as
-// in the tiled engine) and, per wavefront, its 64 activations of each of the 8
-// batch rows (2 KB, 16-byte granule of (batch b, k/4 = c) at slot
-// 16*(c%8) + 8*(c/8) + b, so that the 16 lanes of a k-group read 16 distinct
-// bank quads). Batch rows past `batch` copy row 0 and are zeroed in A. R stages
-// form a ring, R - 1 of them in flight while one is computed (a workgroup does
-// only a few stages, so the copies, not the math, set its pace).
+// A stage holds H super-block columns (H = 1: 4 wavefronts; H = 2: 8, the
+// second four taking the odd columns of the workgroup's range): per column the
+// 64 rows' blocks (9216 B, copied as in the tiled engine), then per wavefront
+// its 64 activations of each of the 8 batch rows (2 KB, 16-byte granule of
+// (batch b, k/4 = c) at slot 16*(c%8) + 8*(c/8) + b, so that the 16 lanes of a
+// k-group read 16 distinct bank quads). Batch rows past `batch` copy row 0 and
+// are zeroed in A. R stages form a ring, R - 1 of them in flight while one is
+// computed. A workgroup does only a few stages and each is a chain of
+// dependent LDS, MFMA and ALU steps, so the time goes to latency; H = 2 halves
+// the stages and doubles the wavefronts that hide it.
 constexpr int kXSlice = 2048;
 constexpr int kMfmaStage = kStageBytes + 4 * kXSlice;   // 17408
 constexpr int kMfmaScales = 1024;                        // per wavefront: [64 rows][2][d*sc, offset]
@@ -410,13 +413,16 @@ __device__ __forceinline__ void wait_stage_copies(int newer) {
     }
 }
 
-template <int G, int NB, int R>
-__device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, int tile, int split) {
+template <int G, int NB, int R, int H>
+__device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, int tile, int split,
+                                              int h) {
     static_assert(R >= 2 && R <= 4, "ring of two to four stages");
+    static_assert(H == 1 || H == 2, "one or two columns per stage");
+    constexpr int kStage = H * kMfmaStage;
     const int lane = threadIdx.x & 63;
     const int kb0 = (int)((int64_t)split * a.nb / a.splits);
     const int kb1 = (int)((int64_t)(split + 1) * a.nb / a.splits);
-    const int nst = kb1 - kb0;
+    const int nst = (kb1 - kb0 + H - 1) / H;
     const int row0 = tile * kTileRows;
 
     // Copy lanes: weights as in the tiled engine (rows 16G..16G+15, rows past
@@ -437,18 +443,28 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
         xoff[t] = (int64_t)(bt < NB ? bt : 0) * a.n_in + 64 * G + 4 * c;
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-    const uint32_t wdst = lds0 + 2304 * G;
-    const uint32_t xdst = lds0 + kStageBytes + kXSlice * G;
+    const int wave = 4 * h + G;
+    const uint32_t wdst = lds0 + kStageBytes * h + 2304 * G;
+    const uint32_t xdst = lds0 + H * kStageBytes + kXSlice * wave;
+    // Column of this wavefront in step s. With two columns per stage, the last
+    // step of an odd range has none for h = 1: that
+    // wavefront copies the range's last column again (five copies per stage
+    // keep the wait counts uniform) and skips the math.
+    auto column = [&](int s) { return kb0 + H * s + h; };
+    // Activation slots of batch rows past NB are zeroed in A: not copied.
+    const bool xcopy = NB == 8 || (lane & 7) < NB;
     auto issue = [&](int s) {
-        const int b = kb0 + s;
-        const uint32_t off = (uint32_t)(s % R) * kMfmaStage;
+        const int b = min(column(s), kb1 - 1);
+        const uint32_t off = (uint32_t)(s % R) * kStage;
         const uint8_t *wb = a.w + (int64_t)b * kQ4kBytes;
-        dma16(wb + goff[0], wdst + off);
-        dma16(wb + goff[1], wdst + off + 1024);
-        if (lane < 16) dma16(wb + goff[2], wdst + off + 2048);
+        dma16_stream(wb + goff[0], wdst + off);
+        dma16_stream(wb + goff[1], wdst + off + 1024);
+        if (lane < 16) dma16_stream(wb + goff[2], wdst + off + 2048);
         const float *xb = a.x + (int64_t)kQK * b;
-        dma16(xb + xoff[0], xdst + off);
-        dma16(xb + xoff[1], xdst + off + 1024);
+        if (xcopy) {
+            dma16(xb + xoff[0], xdst + off);
+            dma16(xb + xoff[1], xdst + off + 1024);
+        }
     };
 
     // A-operand role of this lane and its activation slots
@@ -460,7 +476,7 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
     const int n = lane & 15;
     const bool upper = lane >= 32;
 
-    float *scales = (float *)(smem + R * kMfmaStage + kMfmaScales * G);
+    float *scales = (float *)(smem + R * kStage + kMfmaScales * wave);
     const uint32_t mask = opaque(0x00780078u);
     const uint32_t bias = opaque(0x41804180u);
     const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -474,7 +490,8 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
         if (s + R - 1 < nst) issue(s + R - 1);   // into the slot computed in step s - 1
         wait_stage_copies(min(R - 1, nst - 1 - s));
         lds_barrier();
-        const uint8_t *stage = smem + (s % R) * kMfmaStage;
+        if (H == 1 || column(s) < kb1) {
+        const uint8_t *stage = smem + (s % R) * kStage + kStageBytes * h;
         // Scale terms of sub-blocks 2G and 2G+1 for every tile row, decoded once
         // (lane r: row r) and read back below by the lanes that hold that row.
         {
@@ -494,7 +511,7 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
             // (read back by other lanes of this wavefront: LDS keeps a wavefront's order)
             asm volatile("" ::: "memory");
         }
-        const float *xs = (const float *)(stage + kStageBytes + kXSlice * G);
+        const float *xs = (const float *)(smem + (s % R) * kStage + H * kStageBytes + kXSlice * wave);
         float xv[8];
         const float4 x0 = *(const float4 *)(xs + 4 * xslot0);
         const float4 x1 = *(const float4 *)(xs + 4 * (xslot0 + 16));
@@ -527,11 +544,12 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
                 acc[g][i] = __builtin_fmaf(-off, sx[i], v);
             }
         }
+        }
         lds_barrier();  // slot s % R may be overwritten
     }
 
-    // Sub-blocks 2G and 2G+1 (lanes l and l^32), then the four wavefronts in
-    // order through LDS (overlaying stage 0, idle after the last barrier).
+    // Sub-blocks 2G and 2G+1 (lanes l and l^32), then the wavefronts in order
+    // through LDS (overlaying stage 0, idle after the last barrier).
     float *red = (float *)smem;  // [wave][batch 8][row 64]
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -539,33 +557,35 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
         for (int i = 0; i < 4; ++i) {
             const float v = acc[g][i] + __shfl_xor(acc[g][i], 32);
             const int bt = 4 * (kg & 1) + i;
-            if (!upper && bt < NB) red[(G * 8 + bt) * 64 + 16 * g + n] = v;
+            if (!upper && bt < NB) red[(wave * 8 + bt) * 64 + 16 * g + n] = v;
         }
     }
     lds_barrier();
-    if (G == 0) {
+    if (wave == 0) {
         float total[NB];
 #pragma unroll
         for (int bt = 0; bt < NB; ++bt) {
             float t = red[bt * 64 + lane];
 #pragma unroll
-            for (int w = 1; w < 4; ++w) t += red[(w * 8 + bt) * 64 + lane];
+            for (int w = 1; w < 4 * H; ++w) t += red[(w * 8 + bt) * 64 + lane];
             total[bt] = t;
         }
         tile_epilogue<NB>(a, tile, split, total);
     }
 }
 
-template <int NB, int R>
-__global__ __launch_bounds__(256) void q4k_mfma_kernel(GemvArgs a) {
+template <int NB, int R, int H>
+__global__ __launch_bounds__(256 * H) void q4k_mfma_kernel(GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tile = blockIdx.x / a.splits;
     const int split = blockIdx.x - tile * a.splits;
-    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-        case 0: q4k_mfma_tile<0, NB, R>(a, smem, tile, split); break;
-        case 1: q4k_mfma_tile<1, NB, R>(a, smem, tile, split); break;
-        case 2: q4k_mfma_tile<2, NB, R>(a, smem, tile, split); break;
-        default: q4k_mfma_tile<3, NB, R>(a, smem, tile, split); break;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = H == 2 ? w >> 2 : 0;
+    switch (w & 3) {
+        case 0: q4k_mfma_tile<0, NB, R, H>(a, smem, tile, split, h); break;
+        case 1: q4k_mfma_tile<1, NB, R, H>(a, smem, tile, split, h); break;
+        case 2: q4k_mfma_tile<2, NB, R, H>(a, smem, tile, split, h); break;
+        default: q4k_mfma_tile<3, NB, R, H>(a, smem, tile, split, h); break;
     }
 }
 
@@ -966,28 +986,29 @@ hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nit
     }
 }
 
-template <int R>
-hipError_t launch_mfma_r(const GemvArgs &a, int batch, hipStream_t s) {
-    const size_t lds = R * (size_t)kMfmaStage + 4 * kMfmaScales;
-    const dim3 grid((unsigned)(a.tiles * a.splits)), block(256);
+template <int R, int H>
+hipError_t launch_mfma_rh(const GemvArgs &a, int batch, hipStream_t s) {
+    const size_t lds = (size_t)R * H * kMfmaStage + 4 * H * kMfmaScales;
+    const dim3 grid((unsigned)(a.tiles * a.splits)), block(256 * H);
     switch (batch) {
-        case 2: hipLaunchKernelGGL((q4k_mfma_kernel<2, R>), grid, block, lds, s, a); break;
-        case 3: hipLaunchKernelGGL((q4k_mfma_kernel<3, R>), grid, block, lds, s, a); break;
-        case 4: hipLaunchKernelGGL((q4k_mfma_kernel<4, R>), grid, block, lds, s, a); break;
-        case 5: hipLaunchKernelGGL((q4k_mfma_kernel<5, R>), grid, block, lds, s, a); break;
-        case 6: hipLaunchKernelGGL((q4k_mfma_kernel<6, R>), grid, block, lds, s, a); break;
-        case 7: hipLaunchKernelGGL((q4k_mfma_kernel<7, R>), grid, block, lds, s, a); break;
-        case 8: hipLaunchKernelGGL((q4k_mfma_kernel<8, R>), grid, block, lds, s, a); break;
+        case 2: hipLaunchKernelGGL((q4k_mfma_kernel<2, R, H>), grid, block, lds, s, a); break;
+        case 3: hipLaunchKernelGGL((q4k_mfma_kernel<3, R, H>), grid, block, lds, s, a); break;
+        case 4: hipLaunchKernelGGL((q4k_mfma_kernel<4, R, H>), grid, block, lds, s, a); break;
+        case 5: hipLaunchKernelGGL((q4k_mfma_kernel<5, R, H>), grid, block, lds, s, a); break;
+        case 6: hipLaunchKernelGGL((q4k_mfma_kernel<6, R, H>), grid, block, lds, s, a); break;
+        case 7: hipLaunchKernelGGL((q4k_mfma_kernel<7, R, H>), grid, block, lds, s, a); break;
+        case 8: hipLaunchKernelGGL((q4k_mfma_kernel<8, R, H>), grid, block, lds, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, hipStream_t s) {
-    switch (ring) {
-        case 2: return launch_mfma_r<2>(a, batch, s);
-        case 3: return launch_mfma_r<3>(a, batch, s);
-        case 4: return launch_mfma_r<4>(a, batch, s);
+hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, int cols, hipStream_t s) {
+    switch (cols * 10 + ring) {
+        case 12: return launch_mfma_rh<2, 1>(a, batch, s);
+        case 13: return launch_mfma_rh<3, 1>(a, batch, s);
+        case 14: return launch_mfma_rh<4, 1>(a, batch, s);
+        case 22: return launch_mfma_rh<2, 2>(a, batch, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -69,13 +69,15 @@ Plan choose_plan(int tiles, int nb, int batch) {
 
 int choose_splits(int tiles, int nb) { return choose_plan(tiles, nb, 1).splits; }
 
-// Splits of a matrix-core GEMM (batch >= 2): at least kMfmaTargetWgs workgroups,
-// at most one split per super-block, partial sums inside the workspace.
-// Measured on the 32000 x 2048 LM head at batch 8 (500 tiles): 1 split 17.0 us,
-// 2 splits 18.1 us, 3 splits 20.7 us; the kernel is bound by its vector-ALU
-// work per weight, which splitting does not reduce, while every split adds a
-// partial-sum round trip. QWG_MFMA_TARGET overrides the target (tuning).
-constexpr int kMfmaTargetWgs = 256;
+// Splits of a matrix-core GEMM (batch >= 2): at least kMfmaTargetWgs
+// workgroups, at most one split per super-block, partial sums inside the
+// workspace. Each workgroup's few stages are latency-bound, so a short launch
+// wants enough workgroups to overlap them but not so many that every one does
+// a single stage. Measured at batch 8 (us, by splits): 2048 x 2048 (32 tiles)
+// 1: 10.9, 2: 9.2, 4: 8.5, 8: 9.9; 5632 x 2048 (88 tiles) 1: 11.1, 2: 9.5,
+// 4: 9.9; the 32000 x 2048 LM head (500 tiles) 1: 15.5, 2: 17.2.
+// QWG_MFMA_TARGET overrides the target (tuning).
+constexpr int kMfmaTargetWgs = 128;
 
 int mfma_splits(int tiles, int nb, int batch) {
     static const int env_target = env_int("QWG_MFMA_TARGET", 0);
@@ -89,8 +91,10 @@ int mfma_splits(int tiles, int nb, int batch) {
     return s;
 }
 
-// waves argument of qwg_gemm_q4k_ex that selects the matrix-core engine
+// waves arguments of qwg_gemm_q4k_ex that select the matrix-core engine with
+// one or two super-block columns per stage
 constexpr int kWavesMfma = 1;
+constexpr int kWavesMfma2 = 2;
 
 // Ring stages of the matrix-core engine. Measured (LM head, batch 8, one
 // split): 2 stages 17.0 us, 3 stages 17.6 us, 4 stages 18.5 us; deeper rings
@@ -101,6 +105,24 @@ int mfma_ring() {
         return r >= 2 && r <= 4 ? r : 2;
     }();
     return v;
+}
+
+// Columns per stage of the matrix-core engine (cols 0 = automatic): two (8
+// wavefronts per tile) when every workgroup's range has at least two
+// super-blocks and either the batch is small or the launch has few
+// workgroups, else one. Measured: LM head batch 2: 15.5 -> 14.7 us, batch 8:
+// 15.5 -> 16.3 us (500 workgroups); 5632 x 2048 at 2 splits, batch 2: 9.3 ->
+// 8.3 us, batch 8: 9.7 -> 9.5 us. QWG_MFMA_COLS forces 1 or 2 for the
+// automatic choice (tuning). Two columns run with a 2-stage ring (deeper
+// rings leave one workgroup per CU).
+hipError_t launch_mfma(const GemvArgs &a, int batch, hipStream_t s, int cols = 0) {
+    static const int env_cols = env_int("QWG_MFMA_COLS", 0);
+    if (cols == 0) {
+        const bool two = a.nb / a.splits >= 2 && (batch <= 4 || a.tiles * a.splits <= 256);
+        cols = two ? 2 : 1;
+        if (env_cols == 1 || env_cols == 2) cols = env_cols;
+    }
+    return launch_q4k_mfma(a, batch, cols == 2 ? 2 : mfma_ring(), cols, s);
 }
 
 // Persistent stream engine shape (wavefronts per workgroup, LDS ring stages).
@@ -371,7 +393,7 @@ int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
             a.partial = ws.partial;
             a.counters = ws.counters;
         }
-        return hip_status(launch_q4k_mfma(a, batch, mfma_ring(), (hipStream_t)stream));
+        return hip_status(launch_mfma(a, batch, (hipStream_t)stream));
     }
     int waves = kQ4kWavesSmall;
     rc = fill_gemv_args(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes, batch, (hipStream_t)stream,
@@ -395,12 +417,12 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
     GemvArgs a;
     fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
-    if (waves == kWavesMfma && batch < 2) return QWG_ERR_SHAPE;
-    if (waves == 0 && batch >= 2) waves = kWavesMfma;
+    const bool mfma = waves == kWavesMfma || waves == kWavesMfma2 || (waves == 0 && batch >= 2);
+    if (mfma && batch < 2) return QWG_ERR_SHAPE;
     const Plan autoplan = choose_plan(a.tiles, a.nb, batch);
-    if (splits == 0) splits = waves == kWavesMfma ? mfma_splits(a.tiles, a.nb, batch) : autoplan.splits;
-    if (waves == 0) waves = autoplan.waves;
-    if (waves != kWavesMfma && waves != 4 && waves != 8 && waves != 16) return QWG_ERR_SHAPE;
+    if (splits == 0) splits = mfma ? mfma_splits(a.tiles, a.nb, batch) : autoplan.splits;
+    if (waves == 0 && !mfma) waves = autoplan.waves;
+    if (!mfma && waves != 4 && waves != 8 && waves != 16) return QWG_ERR_SHAPE;
     if (splits < 1 || splits > a.nb) return QWG_ERR_SHAPE;
     if (splits > 1 && ((size_t)splits * batch * a.tiles * kTileRows > kWsPartialFloats ||
                        (size_t)a.tiles > kWsCounters))
@@ -413,7 +435,7 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
         a.partial = ws.partial;
         a.counters = ws.counters;
     }
-    if (waves == kWavesMfma) return hip_status(launch_q4k_mfma(a, batch, mfma_ring(), (hipStream_t)stream));
+    if (mfma) return hip_status(launch_mfma(a, batch, (hipStream_t)stream, waves));
     return hip_status(launch_q4k_gemv(a, batch, waves, (hipStream_t)stream));
 }
 

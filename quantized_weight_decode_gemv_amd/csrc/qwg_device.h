@@ -197,10 +197,11 @@ __device__ __forceinline__ void tile_epilogue(const GemvArgs &a, int tile, int s
                                      __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);
     if (old != (uint32_t)(a.splits - 1)) return;
-    // Sum in split order. For one vector the partials are fetched eight at a
-    // time by one asm block (agent-coherent loads, one wait): the compiler
-    // keeps atomic loads in order and waited one memory round trip per split
-    // (measured: 15 us for 22 splits of one launch).
+    // Sum in split order. The partials are fetched eight at a time by one asm
+    // block (agent-coherent loads, one wait): eight splits of one vector, or
+    // the NB vectors of one split. The compiler keeps atomic loads in order
+    // and waited one memory round trip per load (measured: 15 us for 22
+    // splits of one launch).
     float acc[NB];
 #pragma unroll
     for (int bt = 0; bt < NB; ++bt) acc[bt] = 0.0f;
@@ -217,11 +218,16 @@ __device__ __forceinline__ void tile_epilogue(const GemvArgs &a, int tile, int s
                 if (s0 + u < a.splits) acc[0] += v[u];
         }
     } else {
+        // one batch of loads per split: its NB values (padded to eight)
         for (int s = 0; s < a.splits; ++s) {
+            const float *p[8];
 #pragma unroll
-            for (int bt = 0; bt < NB; ++bt)
-                acc[bt] += __hip_atomic_load(&a.partial[((int64_t)s * NB + bt) * plane + row],
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int u = 0; u < 8; ++u)
+                p[u] = &a.partial[((int64_t)s * NB + (u < NB ? u : NB - 1)) * plane + row];
+            float v[8];
+            load8_agent(p, v);
+#pragma unroll
+            for (int bt = 0; bt < NB; ++bt) acc[bt] += v[bt];
         }
     }
     if (row < a.n_out) {

@@ -76,9 +76,10 @@ hipError_t launch_iq3_dequant(const uint8_t *src, const float *grid, float *dst,
                               int64_t nblocks, bool xxs, hipStream_t s);
 hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, int waves, hipStream_t s);
 hipError_t launch_q4k_group(const GroupArgs &g, int total_workgroups, int max_nb, hipStream_t s);
-// Batched GEMM on matrix cores (2 <= batch <= 8): 4-wavefront workgroups, one
-// per (tile, split), with a ring of `ring` (2..4) stages.
-hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, hipStream_t s);
+// Batched GEMM on matrix cores (2 <= batch <= 8): one workgroup per (tile,
+// split), `cols` super-block columns per stage (1: 4 wavefronts, ring of 2..4
+// stages; 2: 8 wavefronts, ring of 2).
+hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, int cols, hipStream_t s);
 // Persistent stream engine (batch 1): `nitems` work items of the group
 // (g.problems != nullptr) or of `single`; waves in {4, 8, 16}, ring stages in
 // {2, 3}. split: some problem has splits > 1 (items are tile x range; each such

@@ -126,6 +126,8 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 256, 1, 1, 1, 1, None), 2),
     (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 256, 1, 2, 3, 1, None), 2),
     (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 512, 1, 2, 1, 3, None), 2),
+    (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 256, 1, 1, 2, 1, None), 2),
+    (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 512, 1, 2, 2, 3, None), 2),
     # batch -> 4
     (lambda L: L.qwg_gemm_q4k(FAKE, FAKE, FAKE, 256, 1, 0, None), 4),
     (lambda L: L.qwg_gemm_q4k(FAKE, FAKE, FAKE, 256, 1, 9, None), 4),

@@ -357,9 +357,10 @@ def test_gemm_q4k_mfma_every_split(batch, n_out, n_in):
     wd, xd = dev(w), dev(X)
     nb = n_in // 256
     for splits in sorted({1, 2, nb} & set(range(1, nb + 1))):
-        Y = host(qwg.gemm_q4k(wd, xd, waves=1, splits=splits))
-        assert_bound(Y, Yr, Sr, f"mfma batch {batch} splits {splits}")
-        assert_bits(host(qwg.gemm_q4k(wd, xd, waves=1, splits=splits)), Y, "mfma rerun")
+        for cols in (1, 2):   # super-block columns per stage (waves=1: one, waves=2: two)
+            Y = host(qwg.gemm_q4k(wd, xd, waves=cols, splits=splits))
+            assert_bound(Y, Yr, Sr, f"mfma batch {batch} splits {splits} cols {cols}")
+            assert_bits(host(qwg.gemm_q4k(wd, xd, waves=cols, splits=splits)), Y, "mfma rerun")
     # the vector-ALU engine on the same problem, same bound
     assert_bound(host(qwg.gemm_q4k(wd, xd, waves=4, splits=1)), Yr, Sr, "valu engine")
 
@@ -381,9 +382,10 @@ def test_gemm_q4k_mfma_integer_exact(batch):
     w = _integer_q4k(n_out, n_in, 8 + batch)
     X = np.random.default_rng(batch).integers(-8, 9, (batch, n_in)).astype(np.float32)
     Yr, _ = oracle.gemm_q4k(w, X, n_in, n_out)
-    for splits in (1, 3):
-        Y = host(qwg.gemm_q4k(dev(w), dev(X), waves=1, splits=splits))
-        assert np.array_equal(Y.astype(np.float64), Yr), f"splits {splits}"
+    for splits in (1, 3):   # ranges of 22 and of 7, 7, 8 super-blocks
+        for cols in (1, 2):
+            Y = host(qwg.gemm_q4k(dev(w), dev(X), waves=cols, splits=splits))
+            assert np.array_equal(Y.astype(np.float64), Yr), f"splits {splits} cols {cols}"
 
 
 def test_gemm_q4k_mfma_one_hot_columns():
@@ -395,9 +397,10 @@ def test_gemm_q4k_mfma_one_hot_columns():
     X = np.zeros((8, n_in), np.float32)
     for b, k in enumerate(cols):
         X[b, k] = 1.0
-    Y = host(qwg.gemm_q4k(dev(w), dev(X)))
-    for b, k in enumerate(cols):
-        assert np.array_equal(Y[b], deq[:, k]), f"column {k}"
+    for waves, splits in [(0, 0), (1, 1), (2, 1), (2, 3)]:
+        Y = host(qwg.gemm_q4k(dev(w), dev(X), waves=waves, splits=splits))
+        for b, k in enumerate(cols):
+            assert np.array_equal(Y[b], deq[:, k]), f"column {k} waves {waves} splits {splits}"
 
 
 # ---------------------------------------------------------------- IQ3 GEMV
