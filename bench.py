@@ -54,8 +54,8 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
 # runs of this script, each scaled by the same counter on a plain device copy of known size
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "15dec1d9dae84a6a846f5857f7e01762791fbd0a2b5658303b83877381ee3bc0",
-           "fetch_bytes": 594958800, "write_bytes": 1704960}
+TRAFFIC = {"sources_sha256": "c59e1fa72294ac1a50ec26053cb71f0d1045d3f3e332efb984cf7ab71119cebc",
+           "fetch_bytes": 594932237, "write_bytes": 1704960}
 
 
 def kernel_sources_sha256() -> str:
@@ -119,7 +119,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the GEMV path has no multi-GPU mode in this build "
+        print("bench.py measures one GPU: the GEMV path has no multi-GPU mode "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     if args.workload == "iq3_stream":
