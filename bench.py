@@ -54,8 +54,8 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
 # runs of this script, each scaled by the same counter on a plain device copy of known size
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "c59e1fa72294ac1a50ec26053cb71f0d1045d3f3e332efb984cf7ab71119cebc",
-           "fetch_bytes": 594932237, "write_bytes": 1704960}
+TRAFFIC = {"sources_sha256": "b08aad8ec6e54d8f031546fa8c7ef6282c541b70f11a7f85840762f4207df14c",
+           "fetch_bytes": 594935949, "write_bytes": 1704960}
 
 
 def kernel_sources_sha256() -> str:
