@@ -23,7 +23,7 @@ def _gpu_available() -> bool:
 def pytest_collection_modifyitems(config, items):
     if _gpu_available():
         return
-    skip = pytest.mark.skip(reason="no GPU in this process (run the -m gpu tier on a GPU box)")
+    skip = pytest.mark.skip(reason="no GPU visible in this process")
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
