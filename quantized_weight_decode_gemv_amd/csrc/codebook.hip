@@ -91,6 +91,8 @@ __global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__res
 // (106..109), d [row][2] (0..1).
 struct Iq3sFmt {
     static constexpr int kShape = 162;   // 10 * wavefronts + ring stages
+    static constexpr int kTable = 65536; // decode table bytes at LDS address 0
+    static constexpr bool kCapSgprs = false;  // stream kernel without an SGPR cap
     static constexpr int kBytes = kIq3sBytes;
     static constexpr int kCol = kTileRows * kIq3sBytes;
     static constexpr int kIdx = 0, kSign = 4096, kHb = 6144, kScale = 6656, kD = 6912;
@@ -180,7 +182,13 @@ struct Iq3sFmt {
 // IQ4_XS, 8704 bytes: codes [G][row][32] (bytes 8+32G..), header [row][8]
 // (bytes 0..7: d, the scales' top bits, their low nibbles).
 struct Iq4xsFmt {
-    static constexpr int kShape = 162;
+    // 4-wavefront workgroups, seven per CU (LDS 22.5 KB each), SGPRs capped so
+    // that the register file allows them. Measured on the IQ4_XS stream (us):
+    // 4 x 2 capped 109-112, uncapped 115; 8 x 2 119; 16 x 2 151; the 64 KB pair
+    // table this replaced, one 16-wavefront workgroup per CU: 121.
+    static constexpr int kShape = 42;
+    static constexpr int kTable = 4096;
+    static constexpr bool kCapSgprs = true;   // 96 SGPRs: eight wavefronts per SIMD
     static constexpr int kBytes = kIq4xsBytes;
     static constexpr int kCol = kTileRows * kIq4xsBytes;
     static constexpr int kCodes = 0, kHead = 8192;
@@ -195,21 +203,21 @@ struct Iq4xsFmt {
         }
     }
 
-    // Pair table at LDS address 0, one copy per lane: entry (code byte b,
-    // lane c) at b*256 + 4c holds (table[b & 15], table[b >> 4]) in fp16, so
-    // the 64 lanes of a read always hit 64 different banks. 64 KB.
+    // Table at LDS address 0, one copy per lane: entry (code v, lane c) at
+    // v*256 + 4c holds table[v] in fp16 in both halves, so the 64 lanes of a
+    // read always hit 64 different banks. 4 KB (a pair table indexed by the
+    // whole code byte took 64 KB and left room for one workgroup per CU).
     __device__ static void build_table(const float *table, int t, int nthreads) {
-        for (int e = t; e < 16384; e += nthreads) {
-            const int b = e >> 6;
-            const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)table[b & 15]);
-            const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)table[b >> 4]);
-            *(__attribute__((address_space(3))) uint32_t *)(size_t)(e * 4) = lo | (hi << 16);
+        for (int e = t; e < 1024; e += nthreads) {
+            const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)table[e >> 6]);
+            *(__attribute__((address_space(3))) uint32_t *)(size_t)(e * 4) = h | (h << 16);
         }
     }
 
     // Byte j of sub-block h's sixteen code bytes gives weights j (low nibble)
-    // and j + 16 (high nibble): one v_perm forms b*256 + 4*lane, one LDS read
-    // returns both table values.
+    // and j + 16 (high nibble). The nibbles of four bytes are split into bytes
+    // with two masks; then per weight one v_perm forms v*256 + 4*lane and one
+    // LDS read returns the table value.
     template <int G>
     __device__ static float dot(const uint8_t *col, int lane, cfloat_p xg, float acc) {
         const uint4 qa = *(const uint4 *)(col + kCodes + G * 2048 + 32 * lane);
@@ -229,12 +237,18 @@ struct Iq4xsFmt {
             const cfloat_p x = xg + 32 * h;
             float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t sel = 0x0C0C0004u | ((uint32_t)(j & 3) << 8);
-                const uint32_t ti = __builtin_amdgcn_perm(lofs, Q[j >> 2], sel);
-                const uint32_t v = lds_load<uint32_t>(ti);
-                s0 = __builtin_fmaf(h2f_lo(v), x[j], s0);
-                s1 = __builtin_fmaf(h2f_hi(v), x[16 + j], s1);
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = Q[q] & 0x0F0F0F0Fu;
+                const uint32_t hi = (Q[q] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int j = 4 * q + k;
+                    const uint32_t sel = 0x0C0C0004u | ((uint32_t)k << 8);
+                    const uint32_t a = lds_load<uint32_t>(__builtin_amdgcn_perm(lofs, lo, sel));
+                    const uint32_t b = lds_load<uint32_t>(__builtin_amdgcn_perm(lofs, hi, sel));
+                    s0 = __builtin_fmaf(h2f_lo(a), x[j], s0);
+                    s1 = __builtin_fmaf(h2f_lo(b), x[16 + j], s1);
+                }
             }
             acc = __builtin_fmaf(eff, s0 + s1, acc);
         }
@@ -269,13 +283,14 @@ __global__ __launch_bounds__(256) void cb_pack_tiles_kernel(const uint8_t *__res
 // (64-row tile x super-block range); wavefront 4j + G computes sub-blocks 2G,
 // 2G+1 of super-block j of each stage for the 64 rows (lane = row), with the
 // activations as scalar operands; an R-slot ring filled by LDS-DMA runs ahead
-// across items. 16 wavefronts (four super-blocks per stage) share the 64 KB
-// decode table: one workgroup per CU.
+// across items. The decode table sits at LDS address 0: IQ3_S's 64 KB table
+// leaves one 16-wavefront workgroup per CU (four super-blocks per stage);
+// IQ4_XS's 4 KB one seven 4-wavefront workgroups.
 template <class F, int W, int R>
 struct CbCfg {
     static constexpr int kBps = W / 4;
     static constexpr int kGran = F::kCol / 16;        // 16-byte granules per column
-    static constexpr int kTable = 65536;              // at LDS address 0
+    static constexpr int kTable = F::kTable;          // at LDS address 0
     static constexpr int kRing = kTable;
     static constexpr int kSlot = kBps * F::kCol;
     static constexpr int kRed = kRing + R * kSlot;    // [W][64] fp32 row sums
@@ -404,8 +419,8 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
 }
 
 template <class F, int W, int R>
-__global__ __launch_bounds__(W * 64) void cb_stream_kernel(GroupArgs g, GemvArgs single,
-                                                           const float *tab, int nitems) {
+__device__ __forceinline__ void cb_stream_entry(GroupArgs g, GemvArgs single, const float *tab,
+                                                int nitems) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
         case 0: cb_stream<F, 0, W, R>(g, single, tab, nitems, smem); break;
@@ -415,9 +430,31 @@ __global__ __launch_bounds__(W * 64) void cb_stream_kernel(GroupArgs g, GemvArgs
     }
 }
 
-// Engine shapes (wavefronts, ring stages) that fit the LDS with the 64 KB
+// The same kernel with and without an SGPR cap (the attribute takes no
+// template argument); F::kCapSgprs picks one.
+template <class F, int W, int R>
+__global__ __launch_bounds__(W * 64) void cb_stream_kernel(GroupArgs g, GemvArgs single,
+                                                           const float *tab, int nitems) {
+    cb_stream_entry<F, W, R>(g, single, tab, nitems);
+}
+
+template <class F, int W, int R>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_num_sgpr(96))) void cb_stream_kernel96(
+    GroupArgs g, GemvArgs single, const float *tab, int nitems) {
+    cb_stream_entry<F, W, R>(g, single, tab, nitems);
+}
+
+template <class F, int W, int R>
+constexpr auto cb_kernel() {
+    if constexpr (F::kCapSgprs)
+        return cb_stream_kernel96<F, W, R>;
+    else
+        return cb_stream_kernel<F, W, R>;
+}
+
+// Engine shapes (wavefronts, ring stages) that fit the LDS beside a 64 KB
 // table. QWG_CB_SHAPE = 10*W + R picks one (tuning experiments).
-#define QWG_CB_SHAPES(X) X(16, 2) X(16, 3) X(12, 3) X(8, 4)
+#define QWG_CB_SHAPES(X) X(16, 2) X(16, 3) X(12, 3) X(8, 2) X(8, 3) X(8, 4) X(4, 2) X(4, 3)
 
 template <class F, int W, int R>
 int cb_slots_wr() {
@@ -430,7 +467,7 @@ int cb_slots_wr() {
             cus = 256;
         constexpr size_t lds = CbCfg<F, W, R>::kLds;
         if (lds > 160 * 1024 ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cb_stream_kernel<F, W, R>, W * 64,
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cb_kernel<F, W, R>(), W * 64,
                                                          lds) != hipSuccess ||
             per_cu < 1)
             per_cu = lds > 160 * 1024 ? 0 : 1;
@@ -446,7 +483,7 @@ hipError_t cb_launch_wr(const GroupArgs &g, const GemvArgs &single, const float 
     if (n <= 0) return hipErrorInvalidValue;
     if (n > nitems) n = nitems;
     constexpr size_t lds = CbCfg<F, W, R>::kLds;
-    hipLaunchKernelGGL((cb_stream_kernel<F, W, R>), dim3((unsigned)n), dim3(W * 64), lds, s, g,
+    hipLaunchKernelGGL((cb_kernel<F, W, R>()), dim3((unsigned)n), dim3(W * 64), lds, s, g,
                        single, tab, nitems);
     return hipGetLastError();
 }
