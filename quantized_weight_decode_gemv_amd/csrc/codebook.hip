@@ -90,8 +90,12 @@ __global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__res
 // (74+8G..), ninth bits [G][row][2] (66+2G..), sub-scale bytes [row][4]
 // (106..109), d [row][2] (0..1).
 struct Iq3sFmt {
-    static constexpr int kShape = 162;   // 10 * wavefronts + ring stages
-    static constexpr int kTable = 65536; // decode table bytes at LDS address 0
+    // 4-wavefront workgroups, five per CU beside the 16 KB table. Measured on
+    // the IQ3_S stream (us): 4 x 2 119.1, 4 x 3 125.7, 8 x 2 124.9, 16 x 2 162
+    // (the 64 KB four-sign table, one 16-wavefront workgroup per CU: 127.0);
+    // an SGPR cap changes nothing at this occupancy.
+    static constexpr int kShape = 42;         // 10 * wavefronts + ring stages
+    static constexpr int kTable = 16384;      // decode table bytes at LDS address 0
     static constexpr bool kCapSgprs = false;  // stream kernel without an SGPR cap
     static constexpr int kBytes = kIq3sBytes;
     static constexpr int kCol = kTileRows * kIq3sBytes;
@@ -120,27 +124,28 @@ struct Iq3sFmt {
         }
     }
 
-    // Sign-folded fp16 grid table at LDS address 0: entry e = (s4 << 9) | i
-    // (8 bytes at e*8) holds grid row i with component c negated when bit c of
-    // s4 is set. 8192 entries, 64 KB.
+    // Half-group table at LDS address 0, 4 bytes per entry: entry
+    // e = (s2 << 10) | (p << 9) | i holds components 2p and 2p+1 of grid row i
+    // (nine bits) in fp16, each negated when its bit of s2 is set. 4096
+    // entries, 16 KB (folding all four signs of a group into 8-byte entries
+    // took 64 KB and left room for one workgroup per CU).
     __device__ static void build_table(const float *grid, int t, int nthreads) {
-        for (int e = t; e < 8192; e += nthreads) {
-            const float4 g = *(const float4 *)(grid + 4 * (e & 511));
-            const int s4 = e >> 9;
-            const float v[4] = {(s4 & 1) ? -g.x : g.x, (s4 & 2) ? -g.y : g.y,
-                                (s4 & 4) ? -g.z : g.z, (s4 & 8) ? -g.w : g.w};
-            uint32_t hb[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) hb[c] = __builtin_bit_cast(uint16_t, (_Float16)v[c]);
-            const u32x2 ent = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-            *(__attribute__((address_space(3))) u32x2 *)(size_t)(e * 8) = ent;
+        for (int e = t; e < 4096; e += nthreads) {
+            const int s2 = e >> 10, p = (e >> 9) & 1;
+            const float2 g = *(const float2 *)(grid + 4 * (e & 511) + 2 * p);
+            const float v0 = (s2 & 1) ? -g.x : g.x;
+            const float v1 = (s2 & 2) ? -g.y : g.y;
+            const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)v0);
+            const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)v1);
+            *(__attribute__((address_space(3))) uint32_t *)(size_t)(e * 4) = h0 | (h1 << 16);
         }
     }
 
     // acc + this lane's row sum over wavefront G's 64 weights. Group k (four
-    // weights) of sub-block h: table entry ((sign nibble k) << 9 | ninth bit <<
-    // 8 | index byte), assembled by one v_perm from the index dword and a
-    // dword of bytes (sign nibble << 1 | ninth bit) built once per sub-block.
+    // weights) of sub-block h reads two entries, halves p = 0 and 1: ((two
+    // sign bits of nibble k) << 10 | p << 9 | ninth bit << 8 | index byte),
+    // each assembled by one v_perm from the index dword and a dword of bytes
+    // (s2 << 2 | p << 1 | ninth bit) built once per sub-block.
     template <int G>
     __device__ static float dot(const uint8_t *col, int lane, cfloat_p xg, float acc) {
         const uint4 q = *(const uint4 *)(col + kIdx + G * 1024 + 16 * lane);
@@ -152,13 +157,19 @@ struct Iq3sFmt {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t S = h ? sg.y : sg.x;
-            const uint32_t e2 = (S << 1) & 0x1E1E1E1Eu;   // nibbles 0, 2, 4, 6, doubled
-            const uint32_t o2 = (S >> 3) & 0x1E1E1E1Eu;   // nibbles 1, 3, 5, 7, doubled
+            // byte b of S holds sign nibbles 2b (bits 0-3) and 2b+1 (bits 4-7);
+            // bring each pair of sign bits to bits 2-3 of a byte
+            const uint32_t le = (S << 2) & 0x0C0C0C0Cu;   // nibbles 0, 2, 4, 6: bits 0-1
+            const uint32_t lo = (S >> 2) & 0x0C0C0C0Cu;   // nibbles 1, 3, 5, 7: bits 0-1
+            const uint32_t he = S & 0x0C0C0C0Cu;          // nibbles 0, 2, 4, 6: bits 2-3
+            const uint32_t ho = (S >> 4) & 0x0C0C0C0Cu;   // nibbles 1, 3, 5, 7: bits 2-3
             const uint32_t H = hb >> (8 * h);
-            const uint32_t ca = __builtin_amdgcn_perm(o2, e2, 0x05010400u) |
-                                (((H & 15u) * 0x00204081u) & 0x01010101u);
-            const uint32_t cb = __builtin_amdgcn_perm(o2, e2, 0x07030602u) |
-                                ((((H >> 4) & 15u) * 0x00204081u) & 0x01010101u);
+            const uint32_t n03 = ((H & 15u) * 0x00204081u) & 0x01010101u;
+            const uint32_t n47 = (((H >> 4) & 15u) * 0x00204081u) & 0x01010101u;
+            const uint32_t ca0 = __builtin_amdgcn_perm(lo, le, 0x05010400u) | n03;
+            const uint32_t cb0 = __builtin_amdgcn_perm(lo, le, 0x07030602u) | n47;
+            const uint32_t ca1 = __builtin_amdgcn_perm(ho, he, 0x05010400u) | n03 | 0x02020202u;
+            const uint32_t cb1 = __builtin_amdgcn_perm(ho, he, 0x07030602u) | n47 | 0x02020202u;
             const uint32_t s = (sc >> (8 * G + 4 * h)) & 15u;
             const float eff = d * (1.0f + 2.0f * (float)s);
             const cfloat_p x = xg + 32 * h;
@@ -166,12 +177,15 @@ struct Iq3sFmt {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint32_t sel = (uint32_t)(k & 3) | ((uint32_t)(4 + (k & 3)) << 8) | 0x0C0C0000u;
-                const uint32_t ti = __builtin_amdgcn_perm(k < 4 ? ca : cb, idx[2 * h + (k >> 2)], sel);
-                const u32x2 v = lds_load<u32x2>(ti << 3);
-                s0 = __builtin_fmaf(h2f_lo(v.x), x[4 * k + 0], s0);
-                s1 = __builtin_fmaf(h2f_hi(v.x), x[4 * k + 1], s1);
-                s0 = __builtin_fmaf(h2f_lo(v.y), x[4 * k + 2], s0);
-                s1 = __builtin_fmaf(h2f_hi(v.y), x[4 * k + 3], s1);
+                const uint32_t iw = idx[2 * h + (k >> 2)];
+                const uint32_t t0 = __builtin_amdgcn_perm(k < 4 ? ca0 : cb0, iw, sel);
+                const uint32_t t1 = __builtin_amdgcn_perm(k < 4 ? ca1 : cb1, iw, sel);
+                const uint32_t v0 = lds_load<uint32_t>(t0 << 2);
+                const uint32_t v1 = lds_load<uint32_t>(t1 << 2);
+                s0 = __builtin_fmaf(h2f_lo(v0), x[4 * k + 0], s0);
+                s1 = __builtin_fmaf(h2f_hi(v0), x[4 * k + 1], s1);
+                s0 = __builtin_fmaf(h2f_lo(v1), x[4 * k + 2], s0);
+                s1 = __builtin_fmaf(h2f_hi(v1), x[4 * k + 3], s1);
             }
             acc = __builtin_fmaf(eff, s0 + s1, acc);
         }
@@ -283,9 +297,8 @@ __global__ __launch_bounds__(256) void cb_pack_tiles_kernel(const uint8_t *__res
 // (64-row tile x super-block range); wavefront 4j + G computes sub-blocks 2G,
 // 2G+1 of super-block j of each stage for the 64 rows (lane = row), with the
 // activations as scalar operands; an R-slot ring filled by LDS-DMA runs ahead
-// across items. The decode table sits at LDS address 0: IQ3_S's 64 KB table
-// leaves one 16-wavefront workgroup per CU (four super-blocks per stage);
-// IQ4_XS's 4 KB one seven 4-wavefront workgroups.
+// across items. The decode table sits at LDS address 0 (IQ3_S 16 KB, IQ4_XS
+// 4 KB), small enough for five or seven 4-wavefront workgroups per CU.
 template <class F, int W, int R>
 struct CbCfg {
     static constexpr int kBps = W / 4;
@@ -452,8 +465,8 @@ constexpr auto cb_kernel() {
         return cb_stream_kernel<F, W, R>;
 }
 
-// Engine shapes (wavefronts, ring stages) that fit the LDS beside a 64 KB
-// table. QWG_CB_SHAPE = 10*W + R picks one (tuning experiments).
+// Engine shapes (wavefronts, ring stages). QWG_CB_SHAPE = 10*W + R picks one
+// for both formats (tuning experiments).
 #define QWG_CB_SHAPES(X) X(16, 2) X(16, 3) X(12, 3) X(8, 2) X(8, 3) X(8, 4) X(4, 2) X(4, 3)
 
 template <class F, int W, int R>
