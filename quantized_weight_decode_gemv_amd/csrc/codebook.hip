@@ -250,18 +250,35 @@ struct Iq4xsFmt {
                                    h ? qb.w : qa.w};
             const cfloat_p x = xg + 32 * h;
             float s0 = 0.0f, s1 = 0.0f;
+            // The 16 table reads of two code words and their 16 activations are
+            // issued before the FMAs (LDS and scalar loads share one wait
+            // counter; interleaved, each pair waited out a round trip).
+            // Measured: IQ4_XS stream 111.1 -> 108.5-109.5 us.
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t lo = Q[q] & 0x0F0F0F0Fu;
-                const uint32_t hi = (Q[q] >> 4) & 0x0F0F0F0Fu;
+            for (int qq = 0; qq < 4; qq += 2) {
+                uint32_t va[8], vb[8];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int j = 4 * q + k;
-                    const uint32_t sel = 0x0C0C0004u | ((uint32_t)k << 8);
-                    const uint32_t a = lds_load<uint32_t>(__builtin_amdgcn_perm(lofs, lo, sel));
-                    const uint32_t b = lds_load<uint32_t>(__builtin_amdgcn_perm(lofs, hi, sel));
-                    s0 = __builtin_fmaf(h2f_lo(a), x[j], s0);
-                    s1 = __builtin_fmaf(h2f_lo(b), x[16 + j], s1);
+                for (int q = qq; q < qq + 2; ++q) {
+                    const uint32_t lo = Q[q] & 0x0F0F0F0Fu;
+                    const uint32_t hi = (Q[q] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t sel = 0x0C0C0004u | ((uint32_t)k << 8);
+                        va[4 * (q - qq) + k] = lds_load<uint32_t>(__builtin_amdgcn_perm(lofs, lo, sel));
+                        vb[4 * (q - qq) + k] = lds_load<uint32_t>(__builtin_amdgcn_perm(lofs, hi, sel));
+                    }
+                }
+                float xa[8], xb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    xa[i] = x[4 * qq + i];
+                    xb[i] = x[16 + 4 * qq + i];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    s0 = __builtin_fmaf(h2f_lo(va[i]), xa[i], s0);
+                    s1 = __builtin_fmaf(h2f_lo(vb[i]), xb[i], s1);
                 }
             }
             acc = __builtin_fmaf(eff, s0 + s1, acc);
