@@ -185,15 +185,42 @@ def main():
     def step_grouped():
         group.run(stream)
 
-    def step_layered():
+    def step_layered(s=stream):
         for g in layered:
-            g.run(stream)
+            g.run(s)
 
-    def step_per_call():
+    def step_per_call(s=stream):
+        sp = ctypes.c_void_p(s.cuda_stream)
         for yp, xp, wp, n_in, n_out in calls:
-            rc = gemv(yp, xp, wp, n_in, n_out, sptr)
+            rc = gemv(yp, xp, wp, n_in, n_out, sp)
             if rc:
                 raise RuntimeError(f"qwg_gemv_q4k_tiled failed: {rc}")
+
+    def graph_of(fn):
+        """fn(stream) captured once in a HIP graph on a side stream; one eager call
+        there first sets up that stream's split-sum workspace (no allocation or
+        memset is recorded). Returns the graph and whether three replays, with
+        eager runs in between, each reproduced the eager outputs bit for bit."""
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            fn(side)
+        torch.cuda.synchronize()
+        ok = True
+        for _ in range(3):
+            fn(stream)
+            torch.cuda.synchronize()
+            ref = [y.clone() for y in Y]
+            for y in Y:
+                y.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            ok = ok and all(torch.equal(a, b) for a, b in zip(ref, Y))
+        return graph, ok
 
     def timed(fn, steps, warmup):
         for _ in range(warmup):
@@ -231,6 +258,12 @@ def main():
         sec_rows = timed(lambda: group_rows.run(stream), args.steps, args.warmup)
         sec_layered = timed(step_layered, max(5, args.steps // 5), 2)
         sec_percall = timed(step_per_call, max(5, args.steps // 5), 2)
+        # The same two schedules replayed from HIP graphs (the launches are
+        # recorded once; the GPU still runs one kernel per launch).
+        graph_layered, ok_layered = graph_of(step_layered)
+        graph_percall, ok_percall = graph_of(step_per_call)
+        sec_layered_g = timed(graph_layered.replay, max(5, args.steps // 5), 2)
+        sec_percall_g = timed(graph_percall.replay, max(5, args.steps // 5), 2)
 
     def sched(sec_, launches):
         return {"us_per_step": round(1e6 * sec_, 1), "GBps": round(step_bytes / sec_ / 1e9, 1),
@@ -242,6 +275,10 @@ def main():
         schedules["grouped_row_major"] = sched(sec_rows, 1)
         schedules["layered"] = sched(sec_layered, len(layered))
         schedules["per_call"] = sched(sec_percall, len(calls))
+        schedules["layered_graph"] = dict(sched(sec_layered_g, len(layered)),
+                                          replays_match_eager=ok_layered)
+        schedules["per_call_graph"] = dict(sched(sec_percall_g, len(calls)),
+                                           replays_match_eager=ok_percall)
 
     result = {
         "metric": "effective HBM GB/s (% of MI355X peak) for Q4_K/IQ3 GEMV, batch 1",

@@ -984,6 +984,62 @@ def test_layered_decode_groups_within_bound():
         g.close()
 
 
+def test_graph_replays_match_eager():
+    # A decoder layer's launches (split groups on tile-layout weights, per-call
+    # GEMVs on the per-stream split workspace, a batched GEMM, an IQ3 GEMV)
+    # captured once in a HIP graph after one eager call on the capture stream.
+    # Three replays, each after an eager run on another stream, must reproduce
+    # the eager outputs bit for bit.
+    probs = synth.config(2)
+    W = [qwg.pack_q4k_tiles(dev(synth.weights(p)), p.n_in) for p in probs]
+    X = [dev(synth.inputs(p)) for p in probs]
+    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    names = [p.name.split(".")[-1] for p in probs]
+    parts = [[0, 1, 2], [3], [4, 5], [6]] if names[:4] == ["q", "k", "v", "o"] else \
+        [[i] for i in range(len(probs))]
+    groups = [qwg.Q4kGroup([(W[i], X[i], Y[i]) for i in part], tiled=True) for part in parts]
+    wr, xr = dev(synth.weights(probs[0])), X[0]
+    yr = torch.empty(probs[0].n_out, device=DEV)
+    wg = dev(synth.q4k_weights(512, 2048, 104, 1))
+    xg = dev(synth.activations(2048, 104, 2, batch=4))
+    yg = torch.empty(4, 512, device=DEV)
+    grid = dev(synth.iq3_grid())
+    w3 = dev(synth.iq3_weights(300, 5632, 104, 3))
+    x3 = dev(synth.activations(5632, 104, 4))
+    y3 = torch.empty(300, device=DEV)
+    outs = Y + [yr, yg, y3]
+
+    def step(s):
+        for g in groups:
+            g.run(s)
+        with torch.cuda.stream(s):
+            qwg.gemv_q4k(wr, xr, out=yr)
+            qwg.gemm_q4k(wg, xg, out=yg)
+            qwg.gemv_iq3(w3, x3, grid, out=y3)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    step(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(side)
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    for r in range(3):
+        step(main)
+        torch.cuda.synchronize()
+        ref = [o.clone() for o in outs]
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(ref, outs)):
+            assert torch.equal(a, b), f"replay {r}, output {i}"
+    for g in groups:
+        g.close()
+
+
 # ---------------------------------------------------------------- IQ3_S and IQ4_XS
 
 CB = {
