@@ -494,59 +494,59 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
         wait_stage_copies(min(R - 1, nst - 1 - s));
         lds_barrier();
         if (H == 1 || column(s) < kb1) {
-        const uint8_t *stage = smem + (s % R) * kStage + kStageBytes * h;
-        // Scale terms of sub-blocks 2G and 2G+1 for every tile row, decoded once
-        // (lane r: row r) and read back below by the lanes that hold that row.
-        {
-            const uint4 h = *(const uint4 *)(stage + lane * kQ4kBytes);
-            uint32_t sc0, sc1, mn0, mn1;
-            q4k_scales<G>(h, sc0, sc1, mn0, mn1);
-            const float d = h2f_lo(h.x);
-            const float dmin = h2f_hi(h.x);
-            const float dsc0 = d * (float)sc0;
-            const float dsc1 = d * (float)sc1;
-            float4 t;
-            t.x = dsc0;
-            t.y = __builtin_fmaf(dmin, (float)mn0, 16.0f * dsc0);
-            t.z = dsc1;
-            t.w = __builtin_fmaf(dmin, (float)mn1, 16.0f * dsc1);
-            *(float4 *)(scales + 4 * lane) = t;
-            // (read back by other lanes of this wavefront: LDS keeps a wavefront's order)
-            asm volatile("" ::: "memory");
-        }
-        const float *xs = (const float *)(smem + (s % R) * kStage + H * kStageBytes + kXSlice * wave);
-        float xv[8];
-        const float4 x0 = *(const float4 *)(xs + 4 * xslot0);
-        const float4 x1 = *(const float4 *)(xs + 4 * (xslot0 + 16));
-        xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
-        xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
-        u32x4_t ah, am_, al;
-        split_x(xv, alive, ah, am_, al);
-        f32x4_t sx = mfma_bf16(ah, ones, zero4);
-        sx = mfma_bf16(am_, ones, sx);
-        sx = mfma_bf16(al, ones, sx);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const uint8_t *rowp = stage + (16 * g + n) * kQ4kBytes;
-            const uint2 e = *(const uint2 *)(rowp + 16 + 32 * G + 8 * kg);
-            u32x4_t b_lo, b_hi;
-            q4k_bf16_quants(e, mask, bias, b_lo, b_hi);
-            f32x4_t c1 = mfma_bf16(ah, b_lo, zero4);
-            c1 = mfma_bf16(am_, b_lo, c1);
-            c1 = mfma_bf16(al, b_lo, c1);
-            f32x4_t c2 = mfma_bf16(ah, b_hi, zero4);
-            c2 = mfma_bf16(am_, b_hi, c2);
-            c2 = mfma_bf16(al, b_hi, c2);
-            const float2 so = *(const float2 *)(scales + 4 * (16 * g + n) + 2 * (int)upper);
-            const float dsc = so.x;
-            const float off = so.y;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float c = upper ? c2[i] : c1[i];
-                float v = __builtin_fmaf(dsc, c, acc[g][i]);
-                acc[g][i] = __builtin_fmaf(-off, sx[i], v);
+            const uint8_t *stage = smem + (s % R) * kStage + kStageBytes * h;
+            // Scale terms of sub-blocks 2G and 2G+1 for every tile row, decoded once
+            // (lane r: row r) and read back below by the lanes that hold that row.
+            {
+                const uint4 h = *(const uint4 *)(stage + lane * kQ4kBytes);
+                uint32_t sc0, sc1, mn0, mn1;
+                q4k_scales<G>(h, sc0, sc1, mn0, mn1);
+                const float d = h2f_lo(h.x);
+                const float dmin = h2f_hi(h.x);
+                const float dsc0 = d * (float)sc0;
+                const float dsc1 = d * (float)sc1;
+                float4 t;
+                t.x = dsc0;
+                t.y = __builtin_fmaf(dmin, (float)mn0, 16.0f * dsc0);
+                t.z = dsc1;
+                t.w = __builtin_fmaf(dmin, (float)mn1, 16.0f * dsc1);
+                *(float4 *)(scales + 4 * lane) = t;
+                // (read back by other lanes of this wavefront: LDS keeps a wavefront's order)
+                asm volatile("" ::: "memory");
             }
-        }
+            const float *xs = (const float *)(smem + (s % R) * kStage + H * kStageBytes + kXSlice * wave);
+            float xv[8];
+            const float4 x0 = *(const float4 *)(xs + 4 * xslot0);
+            const float4 x1 = *(const float4 *)(xs + 4 * (xslot0 + 16));
+            xv[0] = x0.x; xv[1] = x0.y; xv[2] = x0.z; xv[3] = x0.w;
+            xv[4] = x1.x; xv[5] = x1.y; xv[6] = x1.z; xv[7] = x1.w;
+            u32x4_t ah, am_, al;
+            split_x(xv, alive, ah, am_, al);
+            f32x4_t sx = mfma_bf16(ah, ones, zero4);
+            sx = mfma_bf16(am_, ones, sx);
+            sx = mfma_bf16(al, ones, sx);
+    #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint8_t *rowp = stage + (16 * g + n) * kQ4kBytes;
+                const uint2 e = *(const uint2 *)(rowp + 16 + 32 * G + 8 * kg);
+                u32x4_t b_lo, b_hi;
+                q4k_bf16_quants(e, mask, bias, b_lo, b_hi);
+                f32x4_t c1 = mfma_bf16(ah, b_lo, zero4);
+                c1 = mfma_bf16(am_, b_lo, c1);
+                c1 = mfma_bf16(al, b_lo, c1);
+                f32x4_t c2 = mfma_bf16(ah, b_hi, zero4);
+                c2 = mfma_bf16(am_, b_hi, c2);
+                c2 = mfma_bf16(al, b_hi, c2);
+                const float2 so = *(const float2 *)(scales + 4 * (16 * g + n) + 2 * (int)upper);
+                const float dsc = so.x;
+                const float off = so.y;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float c = upper ? c2[i] : c1[i];
+                    float v = __builtin_fmaf(dsc, c, acc[g][i]);
+                    acc[g][i] = __builtin_fmaf(-off, sx[i], v);
+                }
+            }
         }
         lds_barrier();  // slot s % R may be overwritten
     }
