@@ -86,7 +86,8 @@ def parse():
     ap.add_argument("--print-kernel-hash", action="store_true",
                     help="print the hash of the kernel sources the traffic figure is tied to")
     ap.add_argument("--workload", default="q4k_stream",
-                    choices=["q4k_stream", "iq3_stream", "iq3_xxs", "codebooks", "encode", "lm_head"],
+                    choices=["q4k_stream", "iq3_stream", "iq3_xxs", "codebooks", "encode", "lm_head",
+                             "batched"],
                     help="q4k_stream: the headline (default); the others: see the module docstring")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline launch (no row-major, layered or per-call "
@@ -136,6 +137,9 @@ def main():
         return
     if args.workload == "encode":
         bench_encode(args)
+        return
+    if args.workload == "batched":
+        bench_batched(args)
         return
 
     import numpy as np
@@ -604,6 +608,48 @@ def bench_lm_head(args):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "Q4_K LM head 2048->32000, cold weights (16 copies cycled)", **out,
                    "b8_TFLOPs": round(flops8 / b8 / 1e6, 2)},
+    }), flush=True)
+
+
+def bench_batched(args):
+    """The per-token stream's 155 products for a batch of 2, 4 or 8 sequences at
+    once: one batched group launch (qwg_group_create_q4k_batched) on the matrix
+    cores, row-major weights. A step reads every weight once and the batch's
+    activations and outputs: its algorithmic bytes are the weights plus
+    4 * batch * (n_in + n_out) per GEMV."""
+    import torch
+    import quantized_weight_decode_gemv_amd as qwg
+    from quantized_weight_decode_gemv_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    probs = synth.config(5)
+    W = [torch.from_numpy(synth.weights(p)).to(dev) for p in probs]
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for batch in (2, 4, 8):
+        X = [torch.from_numpy(synth.activations(p.n_in, 5, k, batch=batch)).to(dev)
+             for k, p in enumerate(probs)]
+        Y = [torch.empty(batch, p.n_out, device=dev) for p in probs]
+        group = qwg.Q4kBatchedGroup(zip(W, X, Y))
+        us = _event_us(lambda: group.run(stream), stream, args.steps, args.warmup)
+        nbytes = sum(p.weight_bytes + 4 * batch * (p.n_in + p.n_out) for p in probs)
+        out[f"b{batch}"] = {"us_per_step": round(us, 2), "tokens_per_s": round(batch / us * 1e6, 1),
+                            "GBs": round(nbytes / us / 1e3, 1),
+                            "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                            "algorithmic_bytes_per_step": nbytes,
+                            "workgroups": group.workgroups}
+        group.close()
+    b8 = out["b8"]
+    print(json.dumps({
+        "metric": "tokens/s, Q4_K per-token stream for a batch of sequences (matrix cores)",
+        "value": b8["tokens_per_s"], "unit": "tokens/s (batch 8)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "TinyLlama-1.1B Q4_K per-token stream (155 products) for 2, 4 or 8 "
+                               "sequences, one batched group launch, row-major weights", **out},
+        "roofline": {"bound": "hbm", "achieved": b8["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": b8["frac"], "traffic": None,
+                     "kernel": "q4k_mfma_group_kernel<8,1> (batch 8, one launch)"},
     }), flush=True)
 
 

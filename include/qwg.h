@@ -343,6 +343,19 @@ int qwg_group_create_iq3(const qwg_gemv_desc *descs, int count, const float *gri
 /* As qwg_group_create_q4k / _iq3, every member's weights in the tile layout
  * (16-byte aligned). */
 int qwg_group_create_q4k_tiled(const qwg_gemv_desc *descs, int count, qwg_group **group);
+/*
+ * Batched group: Y_i[b, r] = sum_k W_i[r, k] X_i[b, k] for every member i and
+ * 2 <= batch <= QWG_MAX_BATCH activation rows, one launch per run (e.g. every
+ * projection of a decoding step for `batch` sequences at once). Each member's
+ * x points at [batch][n_in] fp32 row-major (16-byte aligned) and y at
+ * [batch][n_out] fp32 row-major (4-byte aligned); w holds row-major Q4_K
+ * blocks (16-byte aligned). The matrix-core engine of qwg_gemm_q4k runs one
+ * workgroup per 64-row tile of every member (no split sums), within the same
+ * bound as qwg_gemm_q4k. Returns QWG_ERR_BATCH for a batch outside 2..8;
+ * otherwise as qwg_group_create_q4k. Runs may overlap (no shared scratch).
+ */
+int qwg_group_create_q4k_batched(const qwg_gemv_desc *descs, int count, int batch,
+                                 qwg_group **group);
 int qwg_group_create_iq3_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
                                qwg_group **group);
 /* Tiled groups of IQ3_S (grid [512][4]) or IQ4_XS (table [16]) members, rules

@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.qwg_gemv_iq3_ex.argtypes = [P, P, P, P, I64, I64, I, I, P]
         L.qwg_group_create_q4k.argtypes = [P, I, ctypes.POINTER(P)]
         L.qwg_group_create_q4k_tiled.argtypes = [P, I, ctypes.POINTER(P)]
+        L.qwg_group_create_q4k_batched.argtypes = [P, I, I, ctypes.POINTER(P)]
         L.qwg_tiled_bytes.argtypes = [I, I64, I64]
         L.qwg_tiled_bytes.restype = I64
         L.qwg_pack_q4k_tiles.argtypes = [P, P, I64, I64, P]
@@ -84,7 +85,7 @@ def lib() -> ctypes.CDLL:
                   "qwg_group_create_q4k_tiled", "qwg_pack_q4k_tiles", "qwg_gemv_q4k_tiled",
                   "qwg_pack_iq3_tiles", "qwg_gemv_iq3_tiled", "qwg_group_create_iq3_tiled",
                   "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
-                  "qwg_group_destroy"):
+                  "qwg_group_destroy", "qwg_group_create_q4k_batched"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -550,6 +551,44 @@ class Q4kGroup(Group):
 
     def __init__(self, members, tiled: bool = False):
         super().__init__(members, QWG_FMT_Q4K, tiled=tiled)
+
+
+class Q4kBatchedGroup(Group):
+    """Group of batched Q4_K products Y_i = X_i W_i^T run by one launch on the
+    matrix cores: members (w, x, y) with row-major Q4_K weights w, x fp32
+    [batch, n_in] and y fp32 [batch, n_out], every member with the same batch
+    (2..8). run() recomputes every Y_i from the current X_i."""
+
+    def __init__(self, members):
+        members = list(members)
+        if not members:
+            raise ValueError("a group needs at least one member")
+        batch = None
+        descs = (GemvDesc * len(members))()
+        for i, (w, x, y) in enumerate(members):
+            _dev(x, "x", torch.float32)
+            _dev(y, "y", torch.float32)
+            if x.dim() != 2 or y.dim() != 2:
+                raise ValueError(f"member {i}: x and y must be [batch, n]")
+            if batch is None:
+                batch = x.shape[0]
+                if not 2 <= batch <= MAX_BATCH:
+                    raise ValueError("batch must be 2..8")
+            if x.shape[0] != batch or y.shape[0] != batch:
+                raise ValueError(f"member {i}: every member needs the same batch ({batch})")
+            n_in = x.shape[1]
+            n_out = _weights(w, n_in, Q4K_BYTES)
+            if y.shape[1] != n_out:
+                raise ValueError(f"member {i}: y has {y.shape[1]} columns, expected {n_out}")
+            descs[i] = GemvDesc(y.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out)
+        self._members = members
+        self._grid = None
+        self._device = members[0][1].device
+        self.batch = batch
+        handle = ctypes.c_void_p()
+        _check(lib().qwg_group_create_q4k_batched(descs, len(members), batch, ctypes.byref(handle)),
+               "qwg_group_create_q4k_batched")
+        self._handle = handle
 
 
 class Iq3Group(Group):

@@ -592,6 +592,26 @@ __global__ __launch_bounds__(256 * H) void q4k_mfma_kernel(GemvArgs a) {
     }
 }
 
+// Batched grouped launch on the matrix cores: one workgroup per 64-row tile of
+// every member (no splits; members of `batch` activation rows), the problem
+// found through the group's map with scalar loads, then the tile pipeline
+// above with a 2-stage ring.
+template <int NB, int H>
+__global__ __launch_bounds__(256 * H) void q4k_mfma_group_kernel(GroupArgs g) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    GemvArgs a;
+    load_args(a, (cargs_p)g.problems + ((cu32_p)g.map)[blockIdx.x]);
+    const int tile = blockIdx.x - a.wg_begin;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = H == 2 ? w >> 2 : 0;
+    switch (w & 3) {
+        case 0: q4k_mfma_tile<0, NB, 2, H>(a, smem, tile, 0, h); break;
+        case 1: q4k_mfma_tile<1, NB, 2, H>(a, smem, tile, 0, h); break;
+        case 2: q4k_mfma_tile<2, NB, 2, H>(a, smem, tile, 0, h); break;
+        default: q4k_mfma_tile<3, NB, 2, H>(a, smem, tile, 0, h); break;
+    }
+}
+
 // Grouped launch (one workgroup per item): each workgroup reads its problem
 // index and descriptor with scalar loads, then runs the same tile pipeline.
 
@@ -1014,6 +1034,29 @@ hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, int cols, hip
         case 22: return launch_mfma_rh<2, 2>(a, batch, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int H>
+hipError_t launch_mfma_group_h(const GroupArgs &g, int nwg, int batch, hipStream_t s) {
+    const size_t lds = 2 * (size_t)H * kMfmaStage + 4 * H * kMfmaScales;
+    const dim3 grid((unsigned)nwg), block(256 * H);
+    switch (batch) {
+        case 2: hipLaunchKernelGGL((q4k_mfma_group_kernel<2, H>), grid, block, lds, s, g); break;
+        case 3: hipLaunchKernelGGL((q4k_mfma_group_kernel<3, H>), grid, block, lds, s, g); break;
+        case 4: hipLaunchKernelGGL((q4k_mfma_group_kernel<4, H>), grid, block, lds, s, g); break;
+        case 5: hipLaunchKernelGGL((q4k_mfma_group_kernel<5, H>), grid, block, lds, s, g); break;
+        case 6: hipLaunchKernelGGL((q4k_mfma_group_kernel<6, H>), grid, block, lds, s, g); break;
+        case 7: hipLaunchKernelGGL((q4k_mfma_group_kernel<7, H>), grid, block, lds, s, g); break;
+        case 8: hipLaunchKernelGGL((q4k_mfma_group_kernel<8, H>), grid, block, lds, s, g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_mfma_group(const GroupArgs &g, int nwg, int batch, int cols, hipStream_t s) {
+    if (nwg < 1) return hipErrorInvalidValue;
+    return cols == 2 ? launch_mfma_group_h<2>(g, nwg, batch, s)
+                     : launch_mfma_group_h<1>(g, nwg, batch, s);
 }
 
 int q4k_stream_residency(int waves, int ring, int *cus) {

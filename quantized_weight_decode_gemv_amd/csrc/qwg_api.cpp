@@ -679,6 +679,8 @@ struct qwg_group {
     int max_nb;
     bool split;           // some member splits its rows' sums
     int waves, ring;      // Q4_K stream engine shape of the launch
+    int batch;            // activation rows per member (2..8: the matrix-core engine)
+    int cols;             // its super-block columns per stage
 };
 
 namespace {
@@ -758,7 +760,7 @@ void stream_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> 
 }
 
 int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, const float *grid,
-                 qwg_group **out) {
+                 qwg_group **out, int batch = 1) {
     const bool cb = codebook_format(fmt);
     const bool iq3 = fmt == QWG_FMT_IQ3 || cb;   // round-robin schedule, grid/table argument
     const int block_bytes = block_bytes_of(fmt);
@@ -778,7 +780,10 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
         if (probs[i].nb > max_nb) max_nb = probs[i].nb;
     }
     if (total > (int64_t)1 << 30) return QWG_ERR_SHAPE;
-    const bool stream = !iq3 && (layout == kLayoutTiles || use_stream_engine());
+    // Batched members run on the matrix-core engine, one workgroup per tile
+    // (a stream has thousands of tiles, so none of them splits).
+    const bool batched = batch >= 2;
+    const bool stream = !batched && !iq3 && (layout == kLayoutTiles || use_stream_engine());
     // Launches with fewer tiles than resident workgroups split the row sums of
     // their members (at most one pipeline stage per item), as a single GEMV
     // does; a member's partial sums and tile counters live in the group's
@@ -812,7 +817,8 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     int64_t items = 0;
     bool split = false;
     for (int i = 0; i < count; ++i) {
-        if (slots > 2 * total) probs[i].splits = stream_splits(probs[i].nb, (int)bps, slots / total);
+        if (!batched && slots > 2 * total)
+            probs[i].splits = stream_splits(probs[i].nb, (int)bps, slots / total);
         if (probs[i].splits > 1) {
             split = true;
             partial_floats += (size_t)probs[i].splits * probs[i].tiles * kTileRows;
@@ -892,6 +898,14 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     g->split = split;
     g->waves = ssh.waves;
     g->ring = ssh.ring;
+    g->batch = batch;
+    // One column per stage: a group has thousands of workgroups, and the
+    // 8-wavefront two-column shape that helps short single launches measured
+    // slower on the 155-product stream (us, one column / two): batch 2 151.5 /
+    // 166.1, batch 4 167.0 / 185.7, batch 8 176.1 / 196.6. QWG_MFMA_COLS forces
+    // 1 or 2 (tuning).
+    static const int env_cols = env_int("QWG_MFMA_COLS", 0);
+    g->cols = env_cols == 1 || env_cols == 2 ? env_cols : 1;
     *out = g;
     return QWG_OK;
 }
@@ -903,6 +917,15 @@ int qwg_group_create_q4k(const qwg_gemv_desc *descs, int count, qwg_group **out)
     *out = nullptr;
     if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
     return group_create(QWG_FMT_Q4K, kLayoutRows, descs, count, nullptr, out);
+}
+
+int qwg_group_create_q4k_batched(const qwg_gemv_desc *descs, int count, int batch,
+                                 qwg_group **out) {
+    if (!descs || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    if (batch < 2 || batch > QWG_MAX_BATCH) return QWG_ERR_BATCH;
+    return group_create(QWG_FMT_Q4K, kLayoutRows, descs, count, nullptr, out, batch);
 }
 
 int qwg_group_create_q4k_tiled(const qwg_gemv_desc *descs, int count, qwg_group **out) {
@@ -952,6 +975,9 @@ int qwg_group_run(const qwg_group *g, void *stream) {
     if (!g) return QWG_ERR_NULL;
     GemvArgs unused;
     fill_shape(unused, nullptr, nullptr, nullptr, nullptr, kQK, 1, kQ4kBytes);
+    if (g->batch >= 2)
+        return hip_status(
+            launch_q4k_mfma_group(g->args, g->workgroups, g->batch, g->cols, (hipStream_t)stream));
     if (codebook_format(g->fmt))
         return hip_status(launch_cb_stream(g->fmt, g->args, unused, g->grid, g->positions,
                                            (hipStream_t)stream));

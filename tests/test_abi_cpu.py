@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
                  "qwg_gemv_iq3_xxs", "qwg_pack_iq3_xxs_tiles", "qwg_dequant_iq3s",
                  "qwg_dequant_iq4xs", "qwg_pack_iq3s_tiles", "qwg_pack_iq4xs_tiles",
                  "qwg_gemv_iq3s_tiled", "qwg_gemv_iq4xs_tiled", "qwg_group_create_iq3s_tiled",
-                 "qwg_group_create_iq4xs_tiled", "qwg_encode_iq3"):
+                 "qwg_group_create_iq4xs_tiled", "qwg_encode_iq3",
+                 "qwg_group_create_q4k_batched"):
         assert want in names
 
 
@@ -271,6 +272,21 @@ def test_tiled_group_validation_errors(L):
         assert create(arr3, 1, None, ctypes.byref(out)) == 1
         assert create(arr, 2, FAKE + 4, ctypes.byref(out)) == 3
         assert create(arr, 0, FAKE, ctypes.byref(out)) == 2
+        assert out.value is None
+
+
+def test_batched_group_validation_errors(L):
+    out = ctypes.c_void_p(123)
+    ok = (_Desc * 1)(_Desc(FAKE, FAKE, FAKE, 256, 64))
+    assert L.qwg_group_create_q4k_batched(None, 1, 4, ctypes.byref(out)) == 1
+    assert L.qwg_group_create_q4k_batched(ok, 1, 4, None) == 1
+    assert L.qwg_group_create_q4k_batched(ok, 0, 4, ctypes.byref(out)) == 2
+    for batch in (-1, 0, 1, 9):
+        assert L.qwg_group_create_q4k_batched(ok, 1, batch, ctypes.byref(out)) == 4
+    for desc, status in [((0, FAKE, FAKE, 256, 1), 1), ((FAKE, FAKE, FAKE, 300, 1), 2),
+                         ((FAKE, FAKE + 4, FAKE, 256, 1), 3), ((FAKE, FAKE, FAKE + 8, 256, 1), 3)]:
+        arr = (_Desc * 2)(_Desc(FAKE, FAKE, FAKE, 256, 64), _Desc(*desc))
+        assert L.qwg_group_create_q4k_batched(arr, 2, 8, ctypes.byref(out)) == status
         assert out.value is None
 
 

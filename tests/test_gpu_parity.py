@@ -403,6 +403,61 @@ def test_gemm_q4k_mfma_one_hot_columns():
             assert np.array_equal(Y[b], deq[:, k]), f"column {k} waves {waves} splits {splits}"
 
 
+# ---------------------------------------------------------------- batched groups (matrix cores)
+
+BATCHED_SHAPES = [(333, 1536), (64, 256), (130, 5632), (1, 512), (2000, 2048), (65, 768)]
+
+
+@pytest.mark.parametrize("batch", [2, 3, 5, 8])
+def test_batched_group_within_bound_and_equal_to_gemm(batch):
+    ws = [synth.q4k_weights(o, i, 105, k) for k, (o, i) in enumerate(BATCHED_SHAPES)]
+    Xs = [synth.activations(i, 105, 10 * batch + k, batch=batch) for k, (o, i) in enumerate(BATCHED_SHAPES)]
+    W = [dev(w) for w in ws]
+    X = [dev(x) for x in Xs]
+    Y = [torch.full((batch, o), float("nan"), device=DEV) for o, _ in BATCHED_SHAPES]
+    g = qwg.Q4kBatchedGroup(zip(W, X, Y))
+    assert g.workgroups == sum((o + 63) // 64 for o, _ in BATCHED_SHAPES)
+    g.run()
+    cols = 1   # the group's columns per stage; a single launch with the same shape matches it
+    for k, ((o, i), w, x, y) in enumerate(zip(BATCHED_SHAPES, ws, Xs, Y)):
+        Yr, Sr = oracle.gemm_q4k(w, x, i, o)
+        got = host(y)
+        assert_bound(got, Yr, Sr, f"member {k} batch {batch}")
+        single = host(qwg.gemm_q4k(W[k], X[k], waves=cols, splits=1))
+        assert_bits(got, single, f"member {k}: group vs single launch")
+    # a second run, after new activations, recomputes every member
+    X[0].copy_(dev(synth.activations(BATCHED_SHAPES[0][1], 106, 1, batch=batch)))
+    g.run()
+    Yr, Sr = oracle.gemm_q4k(ws[0], host(X[0]), BATCHED_SHAPES[0][1], BATCHED_SHAPES[0][0])
+    assert_bound(host(Y[0]), Yr, Sr, "rerun")
+    g.close()
+
+
+@pytest.mark.parametrize("batch", [2, 7])
+def test_batched_group_integer_exact(batch):
+    shapes = [(190, 5632), (64, 2048), (3, 256)]
+    ws = [_integer_q4k(o, i, 30 + k) for k, (o, i) in enumerate(shapes)]
+    g_ = np.random.default_rng(batch)
+    Xs = [g_.integers(-8, 9, (batch, i)).astype(np.float32) for _, i in shapes]
+    Y = [torch.empty(batch, o, device=DEV) for o, _ in shapes]
+    g = qwg.Q4kBatchedGroup(zip([dev(w) for w in ws], [dev(x) for x in Xs], Y))
+    g.run()
+    for (o, i), w, x, y in zip(shapes, ws, Xs, Y):
+        Yr, _ = oracle.gemm_q4k(w, x, i, o)
+        assert np.array_equal(host(y).astype(np.float64), Yr)
+    g.close()
+
+
+def test_batched_group_rejects_mixed_batches():
+    w = dev(synth.q4k_weights(64, 256, 105, 0))
+    a = (w, torch.zeros(2, 256, device=DEV), torch.zeros(2, 64, device=DEV))
+    b = (w, torch.zeros(3, 256, device=DEV), torch.zeros(3, 64, device=DEV))
+    with pytest.raises(ValueError):
+        qwg.Q4kBatchedGroup([a, b])
+    with pytest.raises(ValueError):
+        qwg.Q4kBatchedGroup([(w, torch.zeros(1, 256, device=DEV), torch.zeros(1, 64, device=DEV))])
+
+
 # ---------------------------------------------------------------- IQ3 GEMV
 
 @pytest.mark.parametrize("p", synth.config(4), ids=lambda p: p.name)
