@@ -54,7 +54,7 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
 # runs of this script, each scaled by the same counter on a plain device copy of known size
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "4a3cdd9bf7357860ed37f40f2f37cf4004e009741c3669903dc3040b0484490f",
+TRAFFIC = {"sources_sha256": "fc85b63c1c56ea560d0040cadcb5af471eccb46ee2a36c793b990ffc2adb21c3",
            "fetch_bytes": 594935949, "write_bytes": 1704960}
 
 
