@@ -54,7 +54,7 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
 # runs of this script, each scaled by the same counter on a plain device copy of known size
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "fc85b63c1c56ea560d0040cadcb5af471eccb46ee2a36c793b990ffc2adb21c3",
+TRAFFIC = {"sources_sha256": "c82664eb870aaacc89b46b6d87c62d6dec06f5a587d5cb469d2ecaaa9be7f568",
            "fetch_bytes": 594935949, "write_bytes": 1704960}
 
 
@@ -597,6 +597,9 @@ def bench_lm_head(args):
         else:
             us = _event_us(cycle(lambda k: qwg.gemm_q4k(wr[k].view(p.n_out, -1), x, out=y)),
                            stream, args.steps, args.warmup)
+            ust = _event_us(cycle(lambda k: qwg.gemm_q4k_tiled(wt[k], x, p.n_out, out=y)),
+                            stream, args.steps, args.warmup)
+            out[f"b{batch}_tiled_us"] = round(ust, 2)
         nbytes = wbytes + 4 * batch * (p.n_in + p.n_out)
         out[f"b{batch}_us"] = round(us, 2)
         out[f"b{batch}_GBs"] = round(nbytes / us / 1e3, 1)
@@ -613,8 +616,8 @@ def bench_lm_head(args):
 
 def bench_batched(args):
     """The per-token stream's 155 products for a batch of 2, 4 or 8 sequences at
-    once: one batched group launch (qwg_group_create_q4k_batched) on the matrix
-    cores, row-major weights. A step reads every weight once and the batch's
+    once: one batched group launch (qwg_group_create_q4k_batched[_tiled]) on the
+    matrix cores, tile-layout and row-major weights. A step reads every weight once and the batch's
     activations and outputs: its algorithmic bytes are the weights plus
     4 * batch * (n_in + n_out) per GEMV."""
     import torch
@@ -625,31 +628,33 @@ def bench_batched(args):
     torch.cuda.set_device(dev)
     probs = synth.config(5)
     W = [torch.from_numpy(synth.weights(p)).to(dev) for p in probs]
+    WT = [qwg.pack_q4k_tiles(w, p.n_in) for p, w in zip(probs, W)]
     stream = torch.cuda.current_stream(dev)
     out = {}
     for batch in (2, 4, 8):
         X = [torch.from_numpy(synth.activations(p.n_in, 5, k, batch=batch)).to(dev)
              for k, p in enumerate(probs)]
         Y = [torch.empty(batch, p.n_out, device=dev) for p in probs]
-        group = qwg.Q4kBatchedGroup(zip(W, X, Y))
-        us = _event_us(lambda: group.run(stream), stream, args.steps, args.warmup)
         nbytes = sum(p.weight_bytes + 4 * batch * (p.n_in + p.n_out) for p in probs)
-        out[f"b{batch}"] = {"us_per_step": round(us, 2), "tokens_per_s": round(batch / us * 1e6, 1),
-                            "GBs": round(nbytes / us / 1e3, 1),
-                            "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
-                            "algorithmic_bytes_per_step": nbytes,
-                            "workgroups": group.workgroups}
-        group.close()
+        for tiled, key in ((True, f"b{batch}"), (False, f"b{batch}_row_major")):
+            group = qwg.Q4kBatchedGroup(zip(WT if tiled else W, X, Y), tiled=tiled)
+            us = _event_us(lambda: group.run(stream), stream, args.steps, args.warmup)
+            out[key] = {"us_per_step": round(us, 2), "tokens_per_s": round(batch / us * 1e6, 1),
+                        "GBs": round(nbytes / us / 1e3, 1),
+                        "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes_per_step": nbytes, "workgroups": group.workgroups}
+            group.close()
     b8 = out["b8"]
     print(json.dumps({
         "metric": "tokens/s, Q4_K per-token stream for a batch of sequences (matrix cores)",
         "value": b8["tokens_per_s"], "unit": "tokens/s (batch 8)", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "higher_is_better": True, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "TinyLlama-1.1B Q4_K per-token stream (155 products) for 2, 4 or 8 "
-                               "sequences, one batched group launch, row-major weights", **out},
+                               "sequences, one batched group launch, tile-layout weights (row-major "
+                               "beside it)", **out},
         "roofline": {"bound": "hbm", "achieved": b8["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": b8["frac"], "traffic": None,
-                     "kernel": "q4k_mfma_group_kernel<8,1> (batch 8, one launch)"},
+                     "kernel": "q4k_mfma_group_kernel<8,1,tile layout> (batch 8, one launch)"},
     }), flush=True)
 
 

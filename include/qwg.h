@@ -279,6 +279,9 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
  * layout, qwg_tiled_bytes bytes); both 16-byte aligned, must not overlap.
  * qwg_gemv_q4k_tiled: qwg_gemv_q4k on tile-layout weights (same arguments,
  * alignment and accuracy).
+ * qwg_gemm_q4k_tiled: qwg_gemm_q4k on tile-layout weights (same arguments,
+ * alignment and accuracy; batch 1 is qwg_gemv_q4k_tiled). For batch >= 2 the
+ * result is bit-identical to qwg_gemm_q4k on the row-major weights.
  * qwg_pack_iq3_tiles: as qwg_pack_q4k_tiles for IQ3 (src 2-byte aligned, dst
  * 16-byte aligned).
  * qwg_gemv_iq3_tiled: qwg_gemv_iq3 on tile-layout weights (w 16-byte aligned;
@@ -290,6 +293,8 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
  */
 int64_t qwg_tiled_bytes(int fmt, int64_t n_in, int64_t n_out);
 int qwg_pack_q4k_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
+int qwg_gemm_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                       int batch, void *stream);
 int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
                        void *stream);
 int qwg_pack_iq3_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
@@ -356,6 +361,11 @@ int qwg_group_create_q4k_tiled(const qwg_gemv_desc *descs, int count, qwg_group 
  */
 int qwg_group_create_q4k_batched(const qwg_gemv_desc *descs, int count, int batch,
                                  qwg_group **group);
+/* As qwg_group_create_q4k_batched, every member's weights in the tile layout
+ * (qwg_pack_q4k_tiles, 16-byte aligned): each pipeline stage is one contiguous
+ * 9216-byte run. Bit-identical to the row-major group on the same weights. */
+int qwg_group_create_q4k_batched_tiled(const qwg_gemv_desc *descs, int count, int batch,
+                                       qwg_group **group);
 int qwg_group_create_iq3_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
                                qwg_group **group);
 /* Tiled groups of IQ3_S (grid [512][4]) or IQ4_XS (table [16]) members, rules

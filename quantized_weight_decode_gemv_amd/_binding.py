@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.qwg_group_create_q4k.argtypes = [P, I, ctypes.POINTER(P)]
         L.qwg_group_create_q4k_tiled.argtypes = [P, I, ctypes.POINTER(P)]
         L.qwg_group_create_q4k_batched.argtypes = [P, I, I, ctypes.POINTER(P)]
+        L.qwg_group_create_q4k_batched_tiled.argtypes = [P, I, I, ctypes.POINTER(P)]
+        L.qwg_gemm_q4k_tiled.argtypes = [P, P, P, I64, I64, I, P]
         L.qwg_tiled_bytes.argtypes = [I, I64, I64]
         L.qwg_tiled_bytes.restype = I64
         L.qwg_pack_q4k_tiles.argtypes = [P, P, I64, I64, P]
@@ -85,7 +87,8 @@ def lib() -> ctypes.CDLL:
                   "qwg_group_create_q4k_tiled", "qwg_pack_q4k_tiles", "qwg_gemv_q4k_tiled",
                   "qwg_pack_iq3_tiles", "qwg_gemv_iq3_tiled", "qwg_group_create_iq3_tiled",
                   "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
-                  "qwg_group_destroy", "qwg_group_create_q4k_batched"):
+                  "qwg_group_destroy", "qwg_group_create_q4k_batched",
+                  "qwg_group_create_q4k_batched_tiled", "qwg_gemm_q4k_tiled"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -427,6 +430,27 @@ def gemv_iq4xs_tiled(w: torch.Tensor, x: torch.Tensor, table: torch.Tensor, n_ou
     return _cb_gemv_tiled(QWG_FMT_IQ4_XS, w, x, table, n_out, out)
 
 
+def gemm_q4k_tiled(w: torch.Tensor, x: torch.Tensor, n_out: int,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X W^T for tile-layout Q4_K weights (pack_q4k_tiles) and X fp32
+    [batch, n_in] (1 <= batch <= 8) -> [batch, n_out]."""
+    _dev(x, "x", torch.float32)
+    _dev(w, "w", torch.uint8)
+    if x.dim() != 2 or not 1 <= x.shape[0] <= MAX_BATCH:
+        raise ValueError("x must be [batch, n_in] with 1 <= batch <= 8")
+    batch, n_in = x.shape
+    if w.numel() != tiled_bytes(n_in, n_out):
+        raise ValueError("w is not a tile-layout matrix of this shape")
+    if out is None:
+        out = torch.empty(batch, n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.shape != (batch, n_out):
+        raise ValueError("out has the wrong shape")
+    _check(lib().qwg_gemm_q4k_tiled(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out, batch,
+                                    _stream(x)), "qwg_gemm_q4k_tiled")
+    return out
+
+
 def gemm_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
              waves: int = 0, splits: int = 0) -> torch.Tensor:
     """Y = X W^T for X fp32 [batch, n_in] (1 <= batch <= 8) -> [batch, n_out].
@@ -555,11 +579,12 @@ class Q4kGroup(Group):
 
 class Q4kBatchedGroup(Group):
     """Group of batched Q4_K products Y_i = X_i W_i^T run by one launch on the
-    matrix cores: members (w, x, y) with row-major Q4_K weights w, x fp32
-    [batch, n_in] and y fp32 [batch, n_out], every member with the same batch
-    (2..8). run() recomputes every Y_i from the current X_i."""
+    matrix cores: members (w, x, y) with Q4_K weights w (row-major, or the tile
+    layout with tiled=True), x fp32 [batch, n_in] and y fp32 [batch, n_out],
+    every member with the same batch (2..8). run() recomputes every Y_i from
+    the current X_i."""
 
-    def __init__(self, members):
+    def __init__(self, members, tiled: bool = False):
         members = list(members)
         if not members:
             raise ValueError("a group needs at least one member")
@@ -577,7 +602,13 @@ class Q4kBatchedGroup(Group):
             if x.shape[0] != batch or y.shape[0] != batch:
                 raise ValueError(f"member {i}: every member needs the same batch ({batch})")
             n_in = x.shape[1]
-            n_out = _weights(w, n_in, Q4K_BYTES)
+            if tiled:
+                _dev(w, "w", torch.uint8)
+                n_out = y.shape[1]
+                if w.numel() != tiled_bytes(n_in, n_out):
+                    raise ValueError(f"member {i}: w is not a tile-layout matrix of this shape")
+            else:
+                n_out = _weights(w, n_in, Q4K_BYTES)
             if y.shape[1] != n_out:
                 raise ValueError(f"member {i}: y has {y.shape[1]} columns, expected {n_out}")
             descs[i] = GemvDesc(y.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out)
@@ -586,8 +617,8 @@ class Q4kBatchedGroup(Group):
         self._device = members[0][1].device
         self.batch = batch
         handle = ctypes.c_void_p()
-        _check(lib().qwg_group_create_q4k_batched(descs, len(members), batch, ctypes.byref(handle)),
-               "qwg_group_create_q4k_batched")
+        fn = "qwg_group_create_q4k_batched_tiled" if tiled else "qwg_group_create_q4k_batched"
+        _check(getattr(lib(), fn)(descs, len(members), batch, ctypes.byref(handle)), fn)
         self._handle = handle
 
 

@@ -413,7 +413,7 @@ __device__ __forceinline__ void wait_stage_copies(int newer) {
     }
 }
 
-template <int G, int NB, int R, int H>
+template <int G, int NB, int R, int H, bool TL>
 __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, int tile, int split,
                                               int h) {
     static_assert(R >= 2 && R <= 4, "ring of two to four stages");
@@ -425,15 +425,19 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
     const int nst = (kb1 - kb0 + H - 1) / H;
     const int row0 = tile * kTileRows;
 
-    // Copy lanes: weights as in the tiled engine (rows 16G..16G+15, rows past
-    // n_out re-read the last row); activations: slots 64t + lane.
+    // Copy lanes: rows 16G..16G+15 of the column, 16-byte chunk k of them at
+    // LDS byte 2304G + 16k. Row-major weights: rows past n_out re-read the
+    // last row. Tile layout (TL): the column is one contiguous 9216-byte run
+    // (rows past n_out are zero blocks there).
     int64_t goff[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         const int k = (i < 2 || lane < 16) ? 64 * i + lane : 128;
         const int r = 16 * G + k / 9;
-        goff[i] = (int64_t)min(row0 + r, a.n_out - 1) * a.row_bytes + 16 * (k % 9);
+        goff[i] = TL ? (int64_t)(2304 * G + 16 * k)
+                     : (int64_t)min(row0 + r, a.n_out - 1) * a.row_bytes + 16 * (k % 9);
     }
+    const uint8_t *wtile = a.w + (TL ? (int64_t)tile * a.nb * kStageBytes : 0);
     int64_t xoff[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -456,13 +460,21 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
     auto issue = [&](int s) {
         const int b = min(column(s), kb1 - 1);
         const uint32_t off = (uint32_t)(s % R) * kStage;
-        const uint8_t *wb = a.w + (int64_t)b * kQ4kBytes;
-        // (plain copies: the next stage reads the neighbouring 144-byte block of
-        // each row, often from the same line; the non-temporal hint measured
-        // 0.4-0.8 us slower on the LM head)
-        dma16(wb + goff[0], wdst + off);
-        dma16(wb + goff[1], wdst + off + 1024);
-        if (lane < 16) dma16(wb + goff[2], wdst + off + 2048);
+        if constexpr (TL) {
+            // whole lines read once: the non-temporal hint, as in the stream engine
+            const uint8_t *wb = wtile + (int64_t)b * kStageBytes;
+            dma16_stream(wb + goff[0], wdst + off);
+            dma16_stream(wb + goff[1], wdst + off + 1024);
+            if (lane < 16) dma16_stream(wb + goff[2], wdst + off + 2048);
+        } else {
+            // plain copies: the next stage reads the neighbouring 144-byte block
+            // of each row, often from the same line; the non-temporal hint
+            // measured 0.4-0.8 us slower on the LM head
+            const uint8_t *wb = a.w + (int64_t)b * kQ4kBytes;
+            dma16(wb + goff[0], wdst + off);
+            dma16(wb + goff[1], wdst + off + 1024);
+            if (lane < 16) dma16(wb + goff[2], wdst + off + 2048);
+        }
         const float *xb = a.x + (int64_t)kQK * b;
         if (xcopy) {
             dma16(xb + xoff[0], xdst + off);
@@ -577,7 +589,7 @@ __device__ __forceinline__ void q4k_mfma_tile(const GemvArgs &a, uint8_t *smem, 
     }
 }
 
-template <int NB, int R, int H>
+template <int NB, int R, int H, bool TL>
 __global__ __launch_bounds__(256 * H) void q4k_mfma_kernel(GemvArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tile = blockIdx.x / a.splits;
@@ -585,10 +597,10 @@ __global__ __launch_bounds__(256 * H) void q4k_mfma_kernel(GemvArgs a) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = H == 2 ? w >> 2 : 0;
     switch (w & 3) {
-        case 0: q4k_mfma_tile<0, NB, R, H>(a, smem, tile, split, h); break;
-        case 1: q4k_mfma_tile<1, NB, R, H>(a, smem, tile, split, h); break;
-        case 2: q4k_mfma_tile<2, NB, R, H>(a, smem, tile, split, h); break;
-        default: q4k_mfma_tile<3, NB, R, H>(a, smem, tile, split, h); break;
+        case 0: q4k_mfma_tile<0, NB, R, H, TL>(a, smem, tile, split, h); break;
+        case 1: q4k_mfma_tile<1, NB, R, H, TL>(a, smem, tile, split, h); break;
+        case 2: q4k_mfma_tile<2, NB, R, H, TL>(a, smem, tile, split, h); break;
+        default: q4k_mfma_tile<3, NB, R, H, TL>(a, smem, tile, split, h); break;
     }
 }
 
@@ -596,7 +608,7 @@ __global__ __launch_bounds__(256 * H) void q4k_mfma_kernel(GemvArgs a) {
 // every member (no splits; members of `batch` activation rows), the problem
 // found through the group's map with scalar loads, then the tile pipeline
 // above with a 2-stage ring.
-template <int NB, int H>
+template <int NB, int H, bool TL>
 __global__ __launch_bounds__(256 * H) void q4k_mfma_group_kernel(GroupArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     GemvArgs a;
@@ -605,10 +617,10 @@ __global__ __launch_bounds__(256 * H) void q4k_mfma_group_kernel(GroupArgs g) {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = H == 2 ? w >> 2 : 0;
     switch (w & 3) {
-        case 0: q4k_mfma_tile<0, NB, 2, H>(a, smem, tile, 0, h); break;
-        case 1: q4k_mfma_tile<1, NB, 2, H>(a, smem, tile, 0, h); break;
-        case 2: q4k_mfma_tile<2, NB, 2, H>(a, smem, tile, 0, h); break;
-        default: q4k_mfma_tile<3, NB, 2, H>(a, smem, tile, 0, h); break;
+        case 0: q4k_mfma_tile<0, NB, 2, H, TL>(a, smem, tile, 0, h); break;
+        case 1: q4k_mfma_tile<1, NB, 2, H, TL>(a, smem, tile, 0, h); break;
+        case 2: q4k_mfma_tile<2, NB, 2, H, TL>(a, smem, tile, 0, h); break;
+        default: q4k_mfma_tile<3, NB, 2, H, TL>(a, smem, tile, 0, h); break;
     }
 }
 
@@ -1009,54 +1021,60 @@ hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nit
     }
 }
 
-template <int R, int H>
+template <int R, int H, bool TL>
 hipError_t launch_mfma_rh(const GemvArgs &a, int batch, hipStream_t s) {
     const size_t lds = (size_t)R * H * kMfmaStage + 4 * H * kMfmaScales;
     const dim3 grid((unsigned)(a.tiles * a.splits)), block(256 * H);
     switch (batch) {
-        case 2: hipLaunchKernelGGL((q4k_mfma_kernel<2, R, H>), grid, block, lds, s, a); break;
-        case 3: hipLaunchKernelGGL((q4k_mfma_kernel<3, R, H>), grid, block, lds, s, a); break;
-        case 4: hipLaunchKernelGGL((q4k_mfma_kernel<4, R, H>), grid, block, lds, s, a); break;
-        case 5: hipLaunchKernelGGL((q4k_mfma_kernel<5, R, H>), grid, block, lds, s, a); break;
-        case 6: hipLaunchKernelGGL((q4k_mfma_kernel<6, R, H>), grid, block, lds, s, a); break;
-        case 7: hipLaunchKernelGGL((q4k_mfma_kernel<7, R, H>), grid, block, lds, s, a); break;
-        case 8: hipLaunchKernelGGL((q4k_mfma_kernel<8, R, H>), grid, block, lds, s, a); break;
+#define QWG_MFMA_CASE(nb) \
+    case nb: hipLaunchKernelGGL((q4k_mfma_kernel<nb, R, H, TL>), grid, block, lds, s, a); break;
+        QWG_MFMA_CASE(2) QWG_MFMA_CASE(3) QWG_MFMA_CASE(4) QWG_MFMA_CASE(5) QWG_MFMA_CASE(6)
+        QWG_MFMA_CASE(7) QWG_MFMA_CASE(8)
+#undef QWG_MFMA_CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, int cols, hipStream_t s) {
+hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, int cols, bool tiled,
+                           hipStream_t s) {
+    if (tiled) {   // tile layout: 2-stage ring only
+        if (ring != 2) return hipErrorInvalidValue;
+        return cols == 2 ? launch_mfma_rh<2, 2, true>(a, batch, s)
+                         : launch_mfma_rh<2, 1, true>(a, batch, s);
+    }
     switch (cols * 10 + ring) {
-        case 12: return launch_mfma_rh<2, 1>(a, batch, s);
-        case 13: return launch_mfma_rh<3, 1>(a, batch, s);
-        case 14: return launch_mfma_rh<4, 1>(a, batch, s);
-        case 22: return launch_mfma_rh<2, 2>(a, batch, s);
+        case 12: return launch_mfma_rh<2, 1, false>(a, batch, s);
+        case 13: return launch_mfma_rh<3, 1, false>(a, batch, s);
+        case 14: return launch_mfma_rh<4, 1, false>(a, batch, s);
+        case 22: return launch_mfma_rh<2, 2, false>(a, batch, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int H>
+template <int H, bool TL>
 hipError_t launch_mfma_group_h(const GroupArgs &g, int nwg, int batch, hipStream_t s) {
     const size_t lds = 2 * (size_t)H * kMfmaStage + 4 * H * kMfmaScales;
     const dim3 grid((unsigned)nwg), block(256 * H);
     switch (batch) {
-        case 2: hipLaunchKernelGGL((q4k_mfma_group_kernel<2, H>), grid, block, lds, s, g); break;
-        case 3: hipLaunchKernelGGL((q4k_mfma_group_kernel<3, H>), grid, block, lds, s, g); break;
-        case 4: hipLaunchKernelGGL((q4k_mfma_group_kernel<4, H>), grid, block, lds, s, g); break;
-        case 5: hipLaunchKernelGGL((q4k_mfma_group_kernel<5, H>), grid, block, lds, s, g); break;
-        case 6: hipLaunchKernelGGL((q4k_mfma_group_kernel<6, H>), grid, block, lds, s, g); break;
-        case 7: hipLaunchKernelGGL((q4k_mfma_group_kernel<7, H>), grid, block, lds, s, g); break;
-        case 8: hipLaunchKernelGGL((q4k_mfma_group_kernel<8, H>), grid, block, lds, s, g); break;
+#define QWG_MFMA_CASE(nb) \
+    case nb: hipLaunchKernelGGL((q4k_mfma_group_kernel<nb, H, TL>), grid, block, lds, s, g); break;
+        QWG_MFMA_CASE(2) QWG_MFMA_CASE(3) QWG_MFMA_CASE(4) QWG_MFMA_CASE(5) QWG_MFMA_CASE(6)
+        QWG_MFMA_CASE(7) QWG_MFMA_CASE(8)
+#undef QWG_MFMA_CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_q4k_mfma_group(const GroupArgs &g, int nwg, int batch, int cols, hipStream_t s) {
+hipError_t launch_q4k_mfma_group(const GroupArgs &g, int nwg, int batch, int cols, bool tiled,
+                                 hipStream_t s) {
     if (nwg < 1) return hipErrorInvalidValue;
-    return cols == 2 ? launch_mfma_group_h<2>(g, nwg, batch, s)
-                     : launch_mfma_group_h<1>(g, nwg, batch, s);
+    if (tiled)
+        return cols == 2 ? launch_mfma_group_h<2, true>(g, nwg, batch, s)
+                         : launch_mfma_group_h<1, true>(g, nwg, batch, s);
+    return cols == 2 ? launch_mfma_group_h<2, false>(g, nwg, batch, s)
+                     : launch_mfma_group_h<1, false>(g, nwg, batch, s);
 }
 
 int q4k_stream_residency(int waves, int ring, int *cus) {

@@ -115,14 +115,16 @@ int mfma_ring() {
 // 8.3 us, batch 8: 9.7 -> 9.5 us. QWG_MFMA_COLS forces 1 or 2 for the
 // automatic choice (tuning). Two columns run with a 2-stage ring (deeper
 // rings leave one workgroup per CU).
-hipError_t launch_mfma(const GemvArgs &a, int batch, hipStream_t s, int cols = 0) {
+hipError_t launch_mfma(const GemvArgs &a, int batch, hipStream_t s, int cols = 0,
+                       bool tiled = false) {
     static const int env_cols = env_int("QWG_MFMA_COLS", 0);
     if (cols == 0) {
         const bool two = a.nb / a.splits >= 2 && (batch <= 4 || a.tiles * a.splits <= 256);
         cols = two ? 2 : 1;
         if (env_cols == 1 || env_cols == 2) cols = env_cols;
     }
-    return launch_q4k_mfma(a, batch, cols == 2 ? 2 : mfma_ring(), cols, s);
+    const int ring = cols == 2 || tiled ? 2 : mfma_ring();
+    return launch_q4k_mfma(a, batch, ring, cols, tiled, s);
 }
 
 // Persistent stream engine shape (wavefronts per workgroup, LDS ring stages).
@@ -458,6 +460,28 @@ int qwg_pack_q4k_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, 
     if (!aligned(dst, 16) || !aligned(src, 16)) return QWG_ERR_ALIGN;
     return hip_status(launch_q4k_pack_tiles((const uint8_t *)src, (uint8_t *)dst, (int)(n_in / kQK),
                                             (int)n_out, (hipStream_t)stream));
+}
+
+int qwg_gemm_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                       int batch, void *stream) {
+    if (!y || !x || !w) return QWG_ERR_NULL;
+    const int rc = check_gemv_shape(n_in, n_out);
+    if (rc) return rc;
+    if (batch < 1 || batch > QWG_MAX_BATCH) return QWG_ERR_BATCH;
+    if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
+    if (batch == 1) return qwg_gemv_q4k_tiled(y, x, w, n_in, n_out, stream);
+    GemvArgs a;
+    fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
+    a.layout = kLayoutTiles;
+    a.splits = mfma_splits(a.tiles, a.nb, batch);
+    if (a.splits > 1) {
+        Workspace ws;
+        const int wrc = get_workspace((hipStream_t)stream, &ws);
+        if (wrc) return wrc;
+        a.partial = ws.partial;
+        a.counters = ws.counters;
+    }
+    return hip_status(launch_mfma(a, batch, (hipStream_t)stream, 0, true));
 }
 
 int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
@@ -928,6 +952,15 @@ int qwg_group_create_q4k_batched(const qwg_gemv_desc *descs, int count, int batc
     return group_create(QWG_FMT_Q4K, kLayoutRows, descs, count, nullptr, out, batch);
 }
 
+int qwg_group_create_q4k_batched_tiled(const qwg_gemv_desc *descs, int count, int batch,
+                                       qwg_group **out) {
+    if (!descs || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    if (batch < 2 || batch > QWG_MAX_BATCH) return QWG_ERR_BATCH;
+    return group_create(QWG_FMT_Q4K, kLayoutTiles, descs, count, nullptr, out, batch);
+}
+
 int qwg_group_create_q4k_tiled(const qwg_gemv_desc *descs, int count, qwg_group **out) {
     if (!descs || !out) return QWG_ERR_NULL;
     *out = nullptr;
@@ -977,7 +1010,8 @@ int qwg_group_run(const qwg_group *g, void *stream) {
     fill_shape(unused, nullptr, nullptr, nullptr, nullptr, kQK, 1, kQ4kBytes);
     if (g->batch >= 2)
         return hip_status(
-            launch_q4k_mfma_group(g->args, g->workgroups, g->batch, g->cols, (hipStream_t)stream));
+            launch_q4k_mfma_group(g->args, g->workgroups, g->batch, g->cols,
+                                  g->layout == kLayoutTiles, (hipStream_t)stream));
     if (codebook_format(g->fmt))
         return hip_status(launch_cb_stream(g->fmt, g->args, unused, g->grid, g->positions,
                                            (hipStream_t)stream));

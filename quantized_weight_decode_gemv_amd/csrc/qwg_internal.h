@@ -78,12 +78,15 @@ hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, int waves, hipStream_t 
 hipError_t launch_q4k_group(const GroupArgs &g, int total_workgroups, int max_nb, hipStream_t s);
 // Batched GEMM on matrix cores (2 <= batch <= 8): one workgroup per (tile,
 // split), `cols` super-block columns per stage (1: 4 wavefronts, ring of 2..4
-// stages; 2: 8 wavefronts, ring of 2).
-hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, int cols, hipStream_t s);
+// stages; 2: 8 wavefronts, ring of 2); `tiled`: weights in the Q4_K tile
+// layout (ring of 2).
+hipError_t launch_q4k_mfma(const GemvArgs &a, int batch, int ring, int cols, bool tiled,
+                           hipStream_t s);
 // The same engine over a group (g.problems with splits == 1, g.map item ->
 // problem, problems[p].wg_begin its first item): `nwg` workgroups, one per
 // 64-row tile of every member.
-hipError_t launch_q4k_mfma_group(const GroupArgs &g, int nwg, int batch, int cols, hipStream_t s);
+hipError_t launch_q4k_mfma_group(const GroupArgs &g, int nwg, int batch, int cols, bool tiled,
+                                 hipStream_t s);
 // Persistent stream engine (batch 1): `nitems` work items of the group
 // (g.problems != nullptr) or of `single`; waves in {4, 8, 16}, ring stages in
 // {2, 3}. split: some problem has splits > 1 (items are tile x range; each such

@@ -40,7 +40,8 @@ def test_header_declares_the_entry_points():
                  "qwg_dequant_iq4xs", "qwg_pack_iq3s_tiles", "qwg_pack_iq4xs_tiles",
                  "qwg_gemv_iq3s_tiled", "qwg_gemv_iq4xs_tiled", "qwg_group_create_iq3s_tiled",
                  "qwg_group_create_iq4xs_tiled", "qwg_encode_iq3",
-                 "qwg_group_create_q4k_batched"):
+                 "qwg_group_create_q4k_batched", "qwg_group_create_q4k_batched_tiled",
+                 "qwg_gemm_q4k_tiled"):
         assert want in names
 
 
@@ -273,6 +274,24 @@ def test_tiled_group_validation_errors(L):
         assert create(arr, 2, FAKE + 4, ctypes.byref(out)) == 3
         assert create(arr, 0, FAKE, ctypes.byref(out)) == 2
         assert out.value is None
+
+
+def test_gemm_tiled_validation_errors(L):
+    f = L.qwg_gemm_q4k_tiled
+    assert f(None, FAKE, FAKE, 256, 1, 2, None) == 1
+    assert f(FAKE, FAKE, FAKE, 300, 1, 2, None) == 2
+    assert f(FAKE, FAKE, FAKE, 256, 0, 2, None) == 2
+    for batch in (0, 9):
+        assert f(FAKE, FAKE, FAKE, 256, 1, batch, None) == 4
+    assert f(FAKE, FAKE + 4, FAKE, 256, 1, 2, None) == 3
+    assert f(FAKE, FAKE, FAKE + 8, 256, 1, 2, None) == 3
+    out = ctypes.c_void_p(123)
+    ok = (_Desc * 1)(_Desc(FAKE, FAKE, FAKE, 256, 64))
+    for batch in (1, 9):
+        assert L.qwg_group_create_q4k_batched_tiled(ok, 1, batch, ctypes.byref(out)) == 4
+    bad = (_Desc * 1)(_Desc(FAKE, FAKE, FAKE + 8, 256, 64))
+    assert L.qwg_group_create_q4k_batched_tiled(bad, 1, 4, ctypes.byref(out)) == 3
+    assert out.value is None
 
 
 def test_batched_group_validation_errors(L):

@@ -433,6 +433,40 @@ def test_batched_group_within_bound_and_equal_to_gemm(batch):
     g.close()
 
 
+@pytest.mark.parametrize("batch", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("n_out,n_in", [(333, 1536), (64, 256), (130, 5632), (1, 512), (2000, 2048)])
+def test_gemm_q4k_tiled_equals_row_major(batch, n_out, n_in):
+    # the same decomposition on both layouts: only where a stage is copied from differs
+    w = synth.q4k_weights(n_out, n_in, 107, batch)
+    X = dev(synth.activations(n_in, 107, 20 + batch, batch=batch))
+    wd = dev(w)
+    wt = qwg.pack_q4k_tiles(wd, n_in)
+    got = host(qwg.gemm_q4k_tiled(wt, X, n_out))
+    if batch == 1:
+        assert_bits(got[0], host(qwg.gemv_q4k_tiled(wt, X[0], n_out)), "batch 1 = tiled GEMV")
+    else:
+        assert_bits(got, host(qwg.gemm_q4k(wd, X)), f"tiled vs row-major, batch {batch}")
+    Yr, Sr = oracle.gemm_q4k(w, host(X), n_in, n_out)
+    assert_bound(got, Yr, Sr, f"tiled gemm batch {batch}")
+
+
+@pytest.mark.parametrize("batch", [3, 8])
+def test_batched_group_tiled_equals_row_major(batch):
+    ws = [dev(synth.q4k_weights(o, i, 108, k)) for k, (o, i) in enumerate(BATCHED_SHAPES)]
+    X = [dev(synth.activations(i, 108, k, batch=batch)) for k, (o, i) in enumerate(BATCHED_SHAPES)]
+    Y = [torch.empty(batch, o, device=DEV) for o, _ in BATCHED_SHAPES]
+    Yt = [torch.empty(batch, o, device=DEV) for o, _ in BATCHED_SHAPES]
+    WT = [qwg.pack_q4k_tiles(w, i) for w, (_, i) in zip(ws, BATCHED_SHAPES)]
+    g = qwg.Q4kBatchedGroup(zip(ws, X, Y))
+    gt = qwg.Q4kBatchedGroup(zip(WT, X, Yt), tiled=True)
+    g.run()
+    gt.run()
+    for k, (a, b) in enumerate(zip(Y, Yt)):
+        assert_bits(host(b), host(a), f"member {k}")
+    g.close()
+    gt.close()
+
+
 @pytest.mark.parametrize("batch", [2, 7])
 def test_batched_group_integer_exact(batch):
     shapes = [(190, 5632), (64, 2048), (3, 256)]
