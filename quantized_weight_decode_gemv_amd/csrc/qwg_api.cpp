@@ -721,8 +721,11 @@ namespace {
 // Positions past the end of a workgroup's list hold kNoItem. Measured on the
 // 155-GEMV TinyLlama stream: skew 0 (plain longest-first balance) 106.4 us,
 // 0.3 104.3, 0.5 102.3, 0.7 101.7, 0.85 101.9; equal round-robin shares 104.8.
-// QWG_STREAM_SKEW overrides it (tuning experiments).
-constexpr double kAgeSkew = 0.7;
+// Re-measured with the tile layout (same box, two rounds): 0.5 88.6 / 88.6 us,
+// 0.6 88.5 / 88.1, 0.7 89.0 / 89.0, 0.8 89.0 / 89.0. A per-wavefront cycle
+// count still shows the youngest workgroup of each CU (one item) finishing
+// ~25% before the others. QWG_STREAM_SKEW overrides it (tuning experiments).
+constexpr double kAgeSkew = 0.6;
 
 double skew_env(const char *name, double dflt) {
     const char *e = getenv(name);
