@@ -55,7 +55,7 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
 TRAFFIC = {"sources_sha256": "c82664eb870aaacc89b46b6d87c62d6dec06f5a587d5cb469d2ecaaa9be7f568",
-           "fetch_bytes": 594935949, "write_bytes": 1704960}
+           "fetch_bytes": 594795923, "write_bytes": 1704960}
 
 
 def kernel_sources_sha256() -> str:
