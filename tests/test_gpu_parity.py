@@ -1096,10 +1096,13 @@ def test_graph_replays_match_eager():
     w3 = dev(synth.iq3_weights(300, 5632, 104, 3))
     x3 = dev(synth.activations(5632, 104, 4))
     y3 = torch.empty(300, device=DEV)
-    outs = Y + [yr, yg, y3]
+    xb = [dev(synth.activations(p.n_in, 104, 10 + i, batch=3)) for i, p in enumerate(probs[:3])]
+    yb = [torch.empty(3, p.n_out, device=DEV) for p in probs[:3]]
+    batched = qwg.Q4kBatchedGroup(zip(W[:3], xb, yb), tiled=True)
+    outs = Y + [yr, yg, y3] + yb
 
     def step(s):
-        for g in groups:
+        for g in groups + [batched]:
             g.run(s)
         with torch.cuda.stream(s):
             qwg.gemv_q4k(wr, xr, out=yr)
@@ -1125,7 +1128,7 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(ref, outs)):
             assert torch.equal(a, b), f"replay {r}, output {i}"
-    for g in groups:
+    for g in groups + [batched]:
         g.close()
 
 
