@@ -28,15 +28,23 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every translation unit (in parallel, one hipcc per source) and
+    link libqwg.so in-tree; raises CalledProcessError on a compile error."""
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
+    jobs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.check_call(cmd)
-        objs.append(obj)
+        jobs.append((cmd, obj))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        for f in [pool.submit(subprocess.check_call, cmd) for cmd, _ in jobs]:
+            f.result()
+    objs = [obj for _, obj in jobs]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
