@@ -346,6 +346,39 @@ def _event_us(fn, stream, steps, warmup):
     return 1e3 * a.elapsed_time(b) / steps
 
 
+def _graph_us(call, n, stream, rounds):
+    """Device time per call of call(0..n-1) captured once in a HIP graph (on a side
+    stream, after one eager pass there sets up its split-sum workspace) and
+    replayed `rounds` times back to back, from HIP events on `stream`: the
+    kernels' own rate without the host's per-call cost. Also returns whether a
+    replay left the outputs the eager pass wrote."""
+    import torch
+    side = torch.cuda.Stream(stream.device)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        outs = [call(k) for k in range(n)]
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for k in range(n):
+            call(k)
+    torch.cuda.synchronize()
+    for o in outs:
+        o.fill_(float("nan"))
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(ref, outs))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(rounds):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / (rounds * n), same
+
+
 def bench_iq3_stream(args):
     import torch
     import quantized_weight_decode_gemv_amd as qwg
@@ -388,7 +421,8 @@ def bench_iq3_xxs(args):
     """IQ3_XXS blocks in llama.cpp's byte order: the two single GEMV shapes of the
     IQ3 configuration (5632x2048, 2048x5632; cold weights, copies cycled), row-major
     in that order, row-major in the container order, and repacked to the tile
-    layout; then the per-token stream's 155 GEMVs repacked from that order as one
+    layout (also replayed from a HIP graph, which leaves out the host's per-call
+    cost); then the per-token stream's 155 GEMVs repacked from that order as one
     grouped launch."""
     import torch
     import quantized_weight_decode_gemv_amd as qwg
@@ -422,10 +456,19 @@ def bench_iq3_xxs(args):
                          args.steps, args.warmup)
         us_t = _event_us(cycle(lambda k: qwg.gemv_iq3_tiled(WT[k], x, grid, p.n_out, out=y)),
                          stream, args.steps, args.warmup)
+        # the same calls replayed from a HIP graph (one output per copy, so the
+        # replay can be checked against the eager pass)
+        YG = torch.empty(copies, p.n_out, device=dev)
+        us_g, same = _graph_us(lambda k: qwg.gemv_iq3_tiled(WT[k], x, grid, p.n_out, out=YG[k]),
+                               copies, stream, max(1, args.steps // copies) * 4)
         b = p.algorithmic_bytes
         singles[p.name] = {"xxs_rows_us": round(us_x, 2), "xxs_rows_GBs": round(b / us_x / 1e3, 1),
                            "container_rows_us": round(us_5, 2),
-                           "xxs_tiled_us": round(us_t, 2), "xxs_tiled_GBs": round(b / us_t / 1e3, 1)}
+                           "xxs_tiled_us": round(us_t, 2), "xxs_tiled_GBs": round(b / us_t / 1e3, 1),
+                           "xxs_tiled_graph_us": round(us_g, 2),
+                           "xxs_tiled_graph_GBs": round(b / us_g / 1e3, 1),
+                           "graph_replays_match_eager": same}
+        del YG
         del WX, W5, WT
 
     probs = synth.config(6)
