@@ -54,7 +54,7 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/q4k.hip",
 # runs of this script, each scaled by the same counter on a plain device copy of known size
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_stream_c5_grouped.md). Valid only for
 # the kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "4257eb6f914d593956b087c766155ef0b6b240245273820601fffe05c3d85f68",
+TRAFFIC = {"sources_sha256": "8a57f09c07b571c93b58da4189b9872cba6a05b5229ec48c661a85c9721536bc",
            "fetch_bytes": 594760417, "write_bytes": 1704960}
 
 

@@ -488,8 +488,8 @@ constexpr auto cb_kernel() {
 
 template <class F, int W, int R>
 int cb_slots_wr() {
-    static int slots = 0;
-    if (slots == 0) {
+    // a function-local static: initialised once even under concurrent first calls
+    static const int slots = [] {
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -501,8 +501,8 @@ int cb_slots_wr() {
                                                          lds) != hipSuccess ||
             per_cu < 1)
             per_cu = lds > 160 * 1024 ? 0 : 1;
-        slots = per_cu * cus;
-    }
+        return per_cu * cus;
+    }();
     return slots;
 }
 

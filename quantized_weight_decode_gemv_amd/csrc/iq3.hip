@@ -519,8 +519,8 @@ __global__ __launch_bounds__(W * 64) void iq3_stream_kernel(GroupArgs g, GemvArg
 // Resident workgroups of one kernel variant on the current device (cached).
 template <int W, int R, bool TL>
 int iq3_slots() {
-    static int slots = 0;
-    if (slots == 0) {
+    // a function-local static: initialised once even under concurrent first calls
+    static const int slots = [] {
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -531,8 +531,8 @@ int iq3_slots() {
                                                          W * 64, lds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
-        slots = per_cu * cus;
-    }
+        return per_cu * cus;
+    }();
     return slots;
 }
 

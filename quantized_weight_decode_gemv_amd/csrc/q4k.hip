@@ -981,19 +981,25 @@ hipError_t launch_q4k_gemv(const GemvArgs &a, int batch, int waves, hipStream_t 
 template <int W, int R>
 int stream_residency(int *cus_out) {
     using C = StreamCfg<W, R>;
-    static int per_cu = -1, cus = 0;
-    if (per_cu < 0) {
-        int dev = 0;
+    struct Residency {
+        int per_cu, cus;
+    };
+    // Queried once per process (a function-local static: initialised once even
+    // when several host threads make the first call together).
+    static const Residency r = [] {
+        int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, q4k_stream_kernel<W, R, false>,
+            cus < 1)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, q4k_stream_kernel<W, R, false>,
                                                          W * 64, C::kLds) != hipSuccess ||
             per_cu < 1)
             per_cu = 1;
-        if (cus < 1) cus = 256;
-    }
-    *cus_out = cus;
-    return per_cu;
+        return Residency{per_cu, cus};
+    }();
+    *cus_out = r.cus;
+    return r.per_cu;
 }
 
 template <int W, int R>
