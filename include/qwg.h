@@ -45,12 +45,20 @@
  *     X is [batch, n_in], Y is [batch, n_out].
  *   - The caller owns every buffer. Calls only enqueue work on `stream` and
  *     return; the caller synchronizes. Outputs must not alias inputs.
- *   - GEMV/GEMM with n_out rows may split the n_in sum across workgroups.
- *     The partial sums then go through a small per-(device, stream) workspace
- *     that the library allocates on the first such call on that stream
- *     (hipMalloc + hipMemset, synchronous) and keeps until the process ends.
- *     Concurrent calls on different streams never share a workspace. The
- *     summation order is fixed by the shapes, so results are deterministic.
+ *   - GEMV/GEMM with few 64-row tiles split the n_in sum across workgroups.
+ *     The partial sums then go through a per-(device, stream) workspace
+ *     (8 MiB + 16 KiB) that the library allocates on the first such call on
+ *     that stream (hipMalloc + hipMemset, synchronous) and keeps until
+ *     qwg_workspace_release or the end of the process. This is the one place
+ *     where the single-matrix calls allocate and keep state. A first such call
+ *     on a stream that is being captured into a graph allocates nothing and
+ *     returns QWG_ERR_CAPTURE: reserve the workspace before capture
+ *     (qwg_workspace_reserve). Calls on one
+ *     stream share its workspace in stream order; a graph captured on a
+ *     stream keeps that stream's workspace, so its replays must not overlap
+ *     one another or calls on that stream. Concurrent calls on different
+ *     streams never share a workspace. The summation order is fixed by the
+ *     shapes, so results are deterministic.
  *   - Errors are reported by the returned status (QWG_* below); the library
  *     never aborts, never throws and writes nothing on a validation error.
  *     Validation happens on the host before any HIP call.
@@ -72,6 +80,7 @@ extern "C" {
 #define QWG_ERR_BATCH 4    /* batch outside 1..QWG_MAX_BATCH */
 #define QWG_ERR_HIP 5      /* the HIP runtime reported an error (launch, allocation) */
 #define QWG_ERR_FORMAT 6   /* unknown format id */
+#define QWG_ERR_CAPTURE 7  /* the stream is capturing and a call would have to allocate */
 
 /* format ids */
 #define QWG_FMT_Q4K 0
@@ -106,6 +115,18 @@ int64_t qwg_row_bytes(int fmt, int64_t n_in);
  * the n_in sum (1 = no split), or a negative status for invalid sizes.
  */
 int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out);
+
+/*
+ * Split-sum workspace of `stream` on the current device (see the conventions
+ * above). qwg_workspace_reserve creates it now if it does not exist yet
+ * (synchronous; QWG_ERR_CAPTURE while the stream is being captured), so that
+ * later calls on the stream, including calls recorded into a graph, allocate
+ * nothing. qwg_workspace_release frees it (hipFree waits for the device);
+ * no work that uses it, and no graph captured with it, may run afterwards.
+ * Releasing a stream that has none is a no-op (QWG_OK).
+ */
+int qwg_workspace_reserve(void *stream);
+int qwg_workspace_release(void *stream);
 
 /*
  * Q4_K dequantization ("用 Python 重写 picoLM", dequantize_q4_K listing).

@@ -10,7 +10,8 @@ from ._binding import (Group, Iq3Group, Iq3sGroup, Iq4xsGroup, MAX_BATCH, Q4kBat
                        encode_iq3, gemm_q4k, gemm_q4k_tiled, gemv_iq3, gemv_iq3_tiled, gemv_iq3_xxs,
                        gemv_iq3s_tiled, gemv_iq4xs_tiled, gemv_q4k, gemv_q4k_tiled, lib,
                        pack_iq3_tiles, pack_iq3_xxs_tiles, pack_iq3s_tiles, pack_iq4xs_tiles,
-                       pack_q4k_tiles, plan_splits, row_bytes, tiled_bytes)
+                       pack_q4k_tiles, plan_splits, row_bytes, tiled_bytes, workspace_release,
+                       workspace_reserve)
 
 __all__ = ["Group", "Iq3Group", "Iq3sGroup", "Iq4xsGroup", "MAX_BATCH", "Q4kBatchedGroup", "Q4kGroup", "QWG_FMT_IQ3",
            "QWG_FMT_IQ3_S", "QWG_FMT_IQ3_XXS", "QWG_FMT_IQ4_XS", "QWG_FMT_Q4K", "QwgError",
@@ -18,4 +19,5 @@ __all__ = ["Group", "Iq3Group", "Iq3sGroup", "Iq4xsGroup", "MAX_BATCH", "Q4kBatc
            "encode_iq3", "gemm_q4k", "gemm_q4k_tiled", "gemv_iq3", "gemv_iq3_tiled", "gemv_iq3_xxs",
            "gemv_iq3s_tiled", "gemv_iq4xs_tiled", "gemv_q4k", "gemv_q4k_tiled", "lib",
            "pack_iq3_tiles", "pack_iq3_xxs_tiles", "pack_iq3s_tiles", "pack_iq4xs_tiles",
-           "pack_q4k_tiles", "plan_splits", "row_bytes", "tiled_bytes"]
+           "pack_q4k_tiles", "plan_splits", "row_bytes", "tiled_bytes", "workspace_release",
+           "workspace_reserve"]

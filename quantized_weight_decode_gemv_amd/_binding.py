@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.qwg_gemv_iq3.argtypes = [P, P, P, P, I64, I64, P]
         L.qwg_gemm_q4k.argtypes = [P, P, P, I64, I64, I, P]
         L.qwg_gemm_q4k_ex.argtypes = [P, P, P, I64, I64, I, I, I, P]
+        L.qwg_workspace_reserve.argtypes = [P]
+        L.qwg_workspace_release.argtypes = [P]
         L.qwg_gemv_iq3_ex.argtypes = [P, P, P, P, I64, I64, I, I, P]
         L.qwg_group_create_q4k.argtypes = [P, I, ctypes.POINTER(P)]
         L.qwg_group_create_q4k_tiled.argtypes = [P, I, ctypes.POINTER(P)]
@@ -88,7 +90,8 @@ def lib() -> ctypes.CDLL:
                   "qwg_pack_iq3_tiles", "qwg_gemv_iq3_tiled", "qwg_group_create_iq3_tiled",
                   "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
                   "qwg_group_destroy", "qwg_group_create_q4k_batched",
-                  "qwg_group_create_q4k_batched_tiled", "qwg_gemm_q4k_tiled"):
+                  "qwg_group_create_q4k_batched_tiled", "qwg_gemm_q4k_tiled",
+                  "qwg_workspace_reserve", "qwg_workspace_release"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -472,6 +475,20 @@ def gemm_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
         _check(lib().qwg_gemm_q4k(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out, batch,
                                   _stream(x)), "qwg_gemm_q4k")
     return out
+
+
+def workspace_reserve(stream: torch.cuda.Stream) -> None:
+    """Create the split-sum workspace of `stream` now (not under capture)."""
+    with torch.cuda.device(stream.device):
+        _check(lib().qwg_workspace_reserve(ctypes.c_void_p(stream.cuda_stream)),
+               "qwg_workspace_reserve")
+
+
+def workspace_release(stream: torch.cuda.Stream) -> None:
+    """Free the split-sum workspace of `stream` (waits for the device)."""
+    with torch.cuda.device(stream.device):
+        _check(lib().qwg_workspace_release(ctypes.c_void_p(stream.cuda_stream)),
+               "qwg_workspace_release")
 
 
 class GemvDesc(ctypes.Structure):

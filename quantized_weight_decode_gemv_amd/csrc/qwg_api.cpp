@@ -193,6 +193,10 @@ size_t workspace_counters() { return kWsCounters; }
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
+// The workspace of (current device, stream), created on first use. Creation
+// allocates and clears device memory synchronously, which a stream under graph
+// capture cannot do: such a call gets QWG_ERR_CAPTURE and nothing is
+// allocated (qwg_workspace_reserve prepares a stream before capture).
 int get_workspace(hipStream_t stream, Workspace *out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return QWG_ERR_HIP;
@@ -203,6 +207,9 @@ int get_workspace(hipStream_t stream, Workspace *out) {
         *out = it->second;
         return QWG_OK;
     }
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return QWG_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return QWG_ERR_CAPTURE;
     const size_t pbytes = workspace_partial_floats() * sizeof(float);
     const size_t cbytes = workspace_counters() * sizeof(uint32_t);
     void *mem = nullptr;
@@ -236,23 +243,6 @@ void fill_shape(GemvArgs &a, const void *w, const float *x, const float *grid, f
     a.partial = nullptr;
     a.counters = nullptr;
     a.layout = kLayoutRows;
-}
-
-int fill_gemv_args(GemvArgs &a, const void *w, const float *x, const float *grid, float *y,
-                   int64_t n_in, int64_t n_out, int block_bytes, int batch, hipStream_t stream,
-                   int *waves) {
-    fill_shape(a, w, x, grid, y, n_in, n_out, block_bytes);
-    const Plan plan = choose_plan(a.tiles, a.nb, batch);
-    a.splits = plan.splits;
-    if (waves) *waves = plan.waves;
-    if (a.splits > 1) {
-        Workspace ws;
-        int rc = get_workspace(stream, &ws);
-        if (rc != QWG_OK) return rc;
-        a.partial = ws.partial;
-        a.counters = ws.counters;
-    }
-    return QWG_OK;
 }
 
 // Splits of an IQ3 GEMV: enough work items (tiles x splits) to give every
@@ -299,6 +289,9 @@ const char *qwg_strerror(int status) {
         case QWG_ERR_BATCH: return "batch must be in 1..8";
         case QWG_ERR_HIP: return "HIP runtime error";
         case QWG_ERR_FORMAT: return "unknown format id";
+        case QWG_ERR_CAPTURE:
+            return "the stream is being captured and has no split-sum workspace yet "
+                   "(qwg_workspace_reserve it before capture)";
         default: return "unknown status";
     }
 }
@@ -349,6 +342,26 @@ int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
     return choose_splits(tiles, (int)(n_in / kQK));
 }
 
+int qwg_workspace_reserve(void *stream) {
+    Workspace ws;
+    return get_workspace((hipStream_t)stream, &ws);
+}
+
+int qwg_workspace_release(void *stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QWG_ERR_HIP;
+    void *mem = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mu);
+        auto it = g_ws.find(std::make_pair(dev, (hipStream_t)stream));
+        if (it == g_ws.end()) return QWG_OK;
+        mem = it->second.partial;
+        g_ws.erase(it);
+    }
+    // hipFree waits for the device to finish the work that may still use it
+    return hip_status(hipFree(mem));
+}
+
 int qwg_dequant_q4k(const void *src, float *dst, int64_t n, void *stream) {
     if (!src || !dst) return QWG_ERR_NULL;
     if (n <= 0 || n % kQK) return QWG_ERR_SHAPE;
@@ -377,37 +390,51 @@ int qwg_dequant_iq3_xxs(const void *src, const float *grid, float *dst, int64_t 
     return iq3_dequant(src, grid, dst, n, true, stream);
 }
 
-int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out, int batch,
-                 void *stream) {
+}  // extern "C"
+
+namespace {
+
+// qwg_gemm_q4k, its split sums in the stream's workspace.
+int gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out, int batch,
+             hipStream_t stream) {
     if (!y || !x || !w) return QWG_ERR_NULL;
     int rc = check_gemv_shape(n_in, n_out);
     if (rc) return rc;
     if (batch < 1 || batch > QWG_MAX_BATCH) return QWG_ERR_BATCH;
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
     GemvArgs a;
-    if (batch >= 2) {
-        fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
-        a.splits = mfma_splits(a.tiles, a.nb, batch);
-        if (a.splits > 1) {
-            Workspace ws;
-            rc = get_workspace((hipStream_t)stream, &ws);
-            if (rc) return rc;
-            a.partial = ws.partial;
-            a.counters = ws.counters;
-        }
-        return hip_status(launch_mfma(a, batch, (hipStream_t)stream));
-    }
+    fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
     int waves = kQ4kWavesSmall;
-    rc = fill_gemv_args(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes, batch, (hipStream_t)stream,
-                        &waves);
-    if (rc) return rc;
-    if (batch == 1 && a.splits == 1 && use_stream_engine()) {
+    if (batch >= 2) {
+        a.splits = mfma_splits(a.tiles, a.nb, batch);
+    } else {
+        const Plan plan = choose_plan(a.tiles, a.nb, batch);
+        a.splits = plan.splits;
+        waves = plan.waves;
+    }
+    if (a.splits > 1) {
+        Workspace ws;
+        rc = get_workspace(stream, &ws);
+        if (rc) return rc;
+        a.partial = ws.partial;
+        a.counters = ws.counters;
+    }
+    if (batch >= 2) return hip_status(launch_mfma(a, batch, stream));
+    if (a.splits == 1 && use_stream_engine()) {
         const StreamShape sh = stream_shape(false);
         const GroupArgs none = {nullptr, nullptr, nullptr};
-        return hip_status(
-            launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, false, (hipStream_t)stream));
+        return hip_status(launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, false, stream));
     }
-    return hip_status(launch_q4k_gemv(a, batch, waves, (hipStream_t)stream));
+    return hip_status(launch_q4k_gemv(a, batch, waves, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out, int batch,
+                 void *stream) {
+    return gemm_q4k(y, x, w, n_in, n_out, batch, (hipStream_t)stream);
 }
 
 int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,

@@ -41,7 +41,8 @@ def test_header_declares_the_entry_points():
                  "qwg_gemv_iq3s_tiled", "qwg_gemv_iq4xs_tiled", "qwg_group_create_iq3s_tiled",
                  "qwg_group_create_iq4xs_tiled", "qwg_encode_iq3",
                  "qwg_group_create_q4k_batched", "qwg_group_create_q4k_batched_tiled",
-                 "qwg_gemm_q4k_tiled"):
+                 "qwg_gemm_q4k_tiled", "qwg_workspace_reserve",
+                 "qwg_workspace_release"):
         assert want in names
 
 
@@ -57,7 +58,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_version_and_strerror(L):
     assert L.qwg_version() >= 100
-    for st in range(0, 8):
+    for st in range(0, 9):
         assert len(L.qwg_strerror(st)) > 0
 
 

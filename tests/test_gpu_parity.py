@@ -51,6 +51,38 @@ def assert_bits(a, b, what=""):
     assert diff.size == 0, f"{what}: {diff.size} mismatching words, first at {diff[:5]}"
 
 
+_STREAMS = {}
+
+
+def stream_case(key, make):
+    """Host weights and inputs of a whole per-token stream and the oracle's full
+    result (y, s) for every GEMV of it, computed once per module: make() returns
+    (problems, weights, inputs, oracle_fn) with oracle_fn(p, w, x) -> (y, s)."""
+    if key not in _STREAMS:
+        probs, ws, xs, fn = make()
+        refs = [fn(p, w, x) for p, w, x in zip(probs, ws, xs)]
+        _STREAMS[key] = (probs, ws, xs, refs)
+    return _STREAMS[key]
+
+
+def q4k_c5():
+    return stream_case("q4k_c5", lambda: (
+        synth.config(5), [synth.weights(p) for p in synth.config(5)],
+        [synth.inputs(p) for p in synth.config(5)],
+        lambda p, w, x: oracle.gemv_q4k(w, x, p.n_in, p.n_out)))
+
+
+def nan_outputs(probs):
+    return [torch.full((p.n_out,), float("nan"), device=DEV) for p in probs]
+
+
+def assert_stream(probs, refs, Y, what):
+    """Every row of every GEMV of a stream within the bound (NaN rows, left
+    unwritten, fail it)."""
+    for p, (yr, sr), y in zip(probs, refs, Y):
+        assert_bound(host(y), yr, sr, f"{what} {p.name}")
+
+
 # ---------------------------------------------------------------- dequant
 
 def test_dequant_q4k_hand_blocks():
@@ -219,20 +251,47 @@ def test_gemv_q4k_deterministic_and_stream_aware():
     assert_bits(y1, host(y3))
 
 
-def test_gemv_q4k_c5_stream_sampled_rows():
+def test_gemv_q4k_c5_stream_all_rows():
     # The full per-token stream (22 layers x 7 projections + LM head) at its real
-    # shapes, launched back to back as bench.py does; the oracle checks sampled rows.
-    probs = synth.config(5)
-    rng = np.random.default_rng(5)
-    outs = []
-    for p in probs:
-        w, x = synth.weights(p), synth.inputs(p)
-        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 24)]))
-        outs.append((p, w, x, rows, qwg.gemv_q4k(dev(w), dev(x))))
+    # shapes, 155 qwg_gemv_q4k calls back to back on row-major weights; every
+    # row of every output (NaN-filled first) against the oracle.
+    probs, ws, xs, refs = q4k_c5()
+    Y = nan_outputs(probs)
+    for p, w, x, y in zip(probs, ws, xs, Y):
+        qwg.gemv_q4k(dev(w), dev(x), out=y)
+    assert_stream(probs, refs, Y, "single call")
+
+
+def test_first_split_call_under_capture_returns_a_status():
+    # A stream without a split workspace, being captured: the call must not
+    # allocate (it cannot, under capture) and reports QWG_ERR_CAPTURE. After
+    # qwg_workspace_reserve the same capture records the kernels, and replays
+    # reproduce the eager result.
+    n_out, n_in = 2048, 2048
+    assert qwg.plan_splits(0, n_in, n_out) > 1
+    w, x = _gemv_q4k_case(n_out, n_in, 97, 3)
+    wd, xd = dev(w), dev(x)
+    y = torch.full((n_out,), float("nan"), device=DEV)
+    side = torch.cuda.Stream()
+    qwg.workspace_release(side)
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(qwg.QwgError) as e:
+        with torch.cuda.graph(graph, stream=side):
+            qwg.gemv_q4k(wd, xd, out=y)
+    assert e.value.status == 7
     torch.cuda.synchronize()
-    for p, w, x, rows, y in outs:
-        yr, sr = oracle.gemv_q4k_rows(w, x, p.n_in, rows)
-        assert_bound(y.cpu().numpy()[rows], yr, sr, p.name)
+    qwg.workspace_reserve(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        qwg.gemv_q4k(wd, xd, out=y)
+    ref = host(qwg.gemv_q4k(wd, xd)).copy()
+    for _ in range(2):
+        y.fill_(float("nan"))
+        graph.replay()
+        assert_bits(host(y), ref, "replay after reserve")
+    yr, sr = oracle.gemv_q4k(w, x, n_in, n_out)
+    assert_bound(ref, yr, sr, "eager")
 
 
 def test_gemv_q4k_misaligned_input_is_an_error():
@@ -300,19 +359,20 @@ def test_group_ragged_members():
         assert_bound(host(y), yr, sr, f"group member {o}x{i}")
 
 
-def test_group_c5_stream_sampled_rows():
-    probs = synth.config(5)
-    rng = np.random.default_rng(6)
-    ws = [synth.weights(p) for p in probs]
-    xs = [synth.inputs(p) for p in probs]
-    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+def test_group_c5_stream_all_rows():
+    # The 155 GEMVs as one grouped launch on row-major weights: every row, after
+    # the first run and again after two more runs into NaN-filled outputs.
+    probs, ws, xs, refs = q4k_c5()
+    Y = nan_outputs(probs)
     g = qwg.Q4kGroup(zip([dev(w) for w in ws], [dev(x) for x in xs], Y))
-    for _ in range(3):
+    g.run()
+    assert_stream(probs, refs, Y, "group")
+    for y in Y:
+        y.fill_(float("nan"))
+    for _ in range(2):
         g.run()
-    for p, w, x, y in zip(probs, ws, xs, Y):
-        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 24)]))
-        yr, sr = oracle.gemv_q4k_rows(w, x, p.n_in, rows)
-        assert_bound(host(y)[rows], yr, sr, "group " + p.name)
+    assert_stream(probs, refs, Y, "group rerun")
+    g.close()
 
 
 # ---------------------------------------------------------------- GEMM
@@ -680,20 +740,26 @@ def test_iq3_group_ragged_members_at_odd_offsets():
         assert_bound(host(y), yr, sr, f"iq3 group member {o}x{i}")
 
 
-def test_iq3_group_stream_sampled_rows():
-    probs = synth.config(6)
+def iq3_c6():
     grid = synth.iq3_grid()
-    rng = np.random.default_rng(7)
-    ws = [synth.weights(p) for p in probs]
-    xs = [synth.inputs(p) for p in probs]
-    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    return grid, stream_case("iq3_c6", lambda: (
+        synth.config(6), [synth.weights(p) for p in synth.config(6)],
+        [synth.inputs(p) for p in synth.config(6)],
+        lambda p, w, x: oracle.gemv_iq3(w, grid, x, p.n_in, p.n_out)))
+
+
+def test_iq3_group_stream_all_rows():
+    grid, (probs, ws, xs, refs) = iq3_c6()
+    Y = nan_outputs(probs)
     g = qwg.Iq3Group(zip([dev(w) for w in ws], [dev(x) for x in xs], Y), dev(grid))
-    for _ in range(3):
+    g.run()
+    assert_stream(probs, refs, Y, "iq3 group")
+    for y in Y:
+        y.fill_(float("nan"))
+    for _ in range(2):
         g.run()
-    for p, w, x, y in zip(probs, ws, xs, Y):
-        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 16)]))
-        yr, sr = oracle.gemv_iq3_rows(w, grid, x, p.n_in, rows)
-        assert_bound(host(y)[rows], yr, sr, "iq3 group " + p.name)
+    assert_stream(probs, refs, Y, "iq3 group rerun")
+    g.close()
 
 
 # ---------------------------------------------------------------- Q4_K tile layout
@@ -750,20 +816,27 @@ def test_q4k_tiled_group_layer_and_integer_exact():
     assert np.array_equal(host(y).astype(np.float64), yr)
 
 
-def test_q4k_tiled_group_stream_sampled_rows():
-    probs = synth.config(5)
-    rng = np.random.default_rng(8)
-    ws = [synth.weights(p) for p in probs]
-    xs = [synth.inputs(p) for p in probs]
-    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+def test_q4k_tiled_group_stream_all_rows():
+    # The launch bench.py times for the independent-input stream: 155 members on
+    # tile-layout weights, the weighted static schedule with its hole table.
+    # Every row of every member (426,240 rows) against the full oracle, from
+    # NaN-filled outputs, on the first run and on a later one; runs are
+    # bitwise reproducible.
+    probs, ws, xs, refs = q4k_c5()
+    Y = nan_outputs(probs)
     W = [qwg.pack_q4k_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
     g = qwg.Q4kGroup(zip(W, [dev(x) for x in xs], Y), tiled=True)
+    assert g.workgroups == sum((p.n_out + 63) // 64 for p in probs)
+    g.run()
+    assert_stream(probs, refs, Y, "tiled group")
+    first = [host(y).copy() for y in Y]
+    for y in Y:
+        y.fill_(float("nan"))
     for _ in range(3):
         g.run()
-    for p, w, x, y in zip(probs, ws, xs, Y):
-        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 16)]))
-        yr, sr = oracle.gemv_q4k_rows(w, x, p.n_in, rows)
-        assert_bound(host(y)[rows], yr, sr, "tiled group " + p.name)
+    for p, y, y0 in zip(probs, Y, first):
+        assert_bits(host(y), y0, "tiled group rerun " + p.name)
+    g.close()
 
 
 @pytest.mark.parametrize("tiled", [False, True])
@@ -779,7 +852,6 @@ def test_q4k_group_many_items_repeat_runs(tiled):
     Y = [torch.empty(n_out, device=DEV) for n_out, _ in shapes]
     g = qwg.Q4kGroup(zip(W, X, Y), tiled=tiled)
     assert g.workgroups > 4 * 2048
-    rng = np.random.default_rng(13)
     for run in range(4):
         xs = [synth.activations(n_in, 123, 10 * run + i) for i, (_, n_in) in enumerate(shapes)]
         for xd, x in zip(X, xs):
@@ -790,9 +862,8 @@ def test_q4k_group_many_items_repeat_runs(tiled):
         for (n_out, n_in), w, x, y in zip(shapes, ws, xs, Y):
             yh = host(y)
             assert not np.isnan(yh).any(), f"run {run}: rows left unwritten"
-            rows = np.unique(np.concatenate([[0, n_out - 1], rng.integers(0, n_out, 24)]))
-            yr, sr = oracle.gemv_q4k_rows(w, x, n_in, rows)
-            assert_bound(yh[rows], yr, sr, f"run {run} {n_out}x{n_in}")
+            yr, sr = oracle.gemv_q4k(w, x, n_in, n_out)
+            assert_bound(yh, yr, sr, f"run {run} {n_out}x{n_in}")
     g.close()
 
 
@@ -863,21 +934,18 @@ def test_iq3_tiled_integer_exact_and_group_layer():
     g.close()
 
 
-def test_iq3_tiled_group_stream_sampled_rows():
-    grid = synth.iq3_grid()
-    probs = synth.config(6)
-    rng = np.random.default_rng(31)
-    ws = [synth.weights(p) for p in probs]
-    xs = [synth.inputs(p) for p in probs]
-    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+def test_iq3_tiled_group_stream_all_rows():
+    grid, (probs, ws, xs, refs) = iq3_c6()
+    Y = nan_outputs(probs)
     W = [qwg.pack_iq3_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
     g = qwg.Iq3Group(zip(W, [dev(x) for x in xs], Y), dev(grid), tiled=True)
-    for _ in range(2):
-        g.run()
-    for p, w, x, y in zip(probs, ws, xs, Y):
-        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 12)]))
-        yr, sr = oracle.gemv_iq3_rows(w, grid, x, p.n_in, rows)
-        assert_bound(host(y)[rows], yr, sr, "iq3 tiled stream " + p.name)
+    g.run()
+    assert_stream(probs, refs, Y, "iq3 tiled stream")
+    for y in Y:
+        y.fill_(float("nan"))
+    g.run()
+    assert_stream(probs, refs, Y, "iq3 tiled stream rerun")
+    g.close()
 
 
 # ---------------------------------------------------------------- IQ3_XXS, llama.cpp byte order
@@ -918,15 +986,10 @@ def test_gemv_iq3_xxs_ragged(n_out, n_in):
     grid = synth.iq3_xxs_grid()
     w = synth.iq3_xxs_weights(n_out, n_in, 142, n_out)
     x = synth.activations(n_in, 142, n_out)
-    y = host(qwg.gemv_iq3_xxs(dev(w), dev(x), dev(grid)))
-    if n_out > 4096:
-        rows = np.unique(np.concatenate([[0, n_out - 1],
-                                         np.random.default_rng(n_out).integers(0, n_out, 64)]))
-        yr, sr = oracle.gemv_iq3_xxs_rows(w, grid, x, n_in, rows)
-        assert_bound(y[rows], yr, sr, f"{n_out}x{n_in} sampled")
-    else:
-        yr, sr = oracle.gemv_iq3_xxs(w, grid, x, n_in, n_out)
-        assert_bound(y, yr, sr, f"{n_out}x{n_in}")
+    y = torch.full((n_out,), float("nan"), device=DEV)
+    qwg.gemv_iq3_xxs(dev(w), dev(x), dev(grid), out=y)
+    yr, sr = oracle.gemv_iq3_xxs(w, grid, x, n_in, n_out)
+    assert_bound(host(y), yr, sr, f"{n_out}x{n_in}")
 
 
 @pytest.mark.parametrize("offset", [0, 2, 4, 6, 8, 10, 12, 14, 18, 30])
@@ -1212,16 +1275,16 @@ def test_gemv_codebook_tiled(fmt, n_out, n_in):
 
 
 @pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
-def test_gemv_codebook_lm_head_sampled(fmt):
+def test_gemv_codebook_lm_head_all_rows(fmt):
     c = CB[fmt]
     n_out, n_in = 32000, 2048
     tab = c["table"]()
     w = c["weights"](n_out, n_in, 164, 0)
     x = synth.activations(n_in, 164, 0)
-    y = host(c["gemv"](c["pack"](dev(w), n_in), dev(x), dev(tab), n_out))
-    rows = np.unique(np.concatenate([[0, n_out - 1], np.random.default_rng(3).integers(0, n_out, 96)]))
-    yr, sr = c["o_rows"](w, tab, x, n_in, rows)
-    assert_bound(y[rows], yr, sr, f"{fmt} lm head")
+    y = torch.full((n_out,), float("nan"), device=DEV)
+    c["gemv"](c["pack"](dev(w), n_in), dev(x), dev(tab), n_out, out=y)
+    yr, sr = c["o_gemv"](w, tab, x, n_in, n_out)
+    assert_bound(host(y), yr, sr, f"{fmt} lm head")
 
 
 def _integer_cb(fmt, n_out, n_in, seed):
@@ -1273,22 +1336,19 @@ def test_codebook_groups_layer_stream_repeat_runs(fmt):
 
 
 @pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
-def test_codebook_group_stream_sampled_rows(fmt):
+def test_codebook_group_stream_all_rows(fmt):
     c = CB[fmt]
     tab = c["table"]()
-    probs = synth.config(6)
-    rng = np.random.default_rng(33)
-    ws = [c["weights"](p.n_out, p.n_in, 167, k) for k, p in enumerate(probs)]
-    xs = [synth.inputs(p) for p in probs]
-    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    probs, ws, xs, refs = stream_case(fmt + "_c6", lambda: (
+        synth.config(6), [c["weights"](p.n_out, p.n_in, 167, k) for k, p in enumerate(synth.config(6))],
+        [synth.inputs(p) for p in synth.config(6)],
+        lambda p, w, x: c["o_gemv"](w, tab, x, p.n_in, p.n_out)))
+    Y = nan_outputs(probs)
     W = [c["pack"](dev(w), p.n_in) for p, w in zip(probs, ws)]
     g = c["group"](zip(W, [dev(x) for x in xs], Y), dev(tab))
     for _ in range(2):
         g.run()
-    for p, w, x, y in zip(probs, ws, xs, Y):
-        rows = np.unique(np.concatenate([[0, p.n_out - 1], rng.integers(0, p.n_out, 8)]))
-        yr, sr = c["o_rows"](w, tab, x, p.n_in, rows)
-        assert_bound(host(y)[rows], yr, sr, f"{fmt} stream {p.name}")
+    assert_stream(probs, refs, Y, f"{fmt} stream")
     g.close()
 
 
