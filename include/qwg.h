@@ -53,7 +53,7 @@
  *     where the single-matrix calls allocate and keep state. A first such call
  *     on a stream that is being captured into a graph allocates nothing and
  *     returns QWG_ERR_CAPTURE: reserve the workspace before capture
- *     (qwg_workspace_reserve). Calls on one
+ *     (qwg_workspace_reserve), or use qwg_gemm_q4k_noalloc. Calls on one
  *     stream share its workspace in stream order; a graph captured on a
  *     stream keeps that stream's workspace, so its replays must not overlap
  *     one another or calls on that stream. Concurrent calls on different
@@ -262,6 +262,23 @@ int qwg_gemv_iq3_ex(float *y, const float *x, const void *w, const float *grid, 
  */
 int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
                  int batch, void *stream);
+
+/*
+ * qwg_gemm_q4k for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, kernels, work decomposition and results (bit-identical to
+ * qwg_gemm_q4k), but split sums go through a fixed scratch array that the
+ * library's code object holds on every GPU (1 MiB of partial sums and 4096
+ * tile counters, held until the process ends) instead of the per-stream
+ * workspace, so no call allocates or frees anything. The first call on a
+ * device also enqueues a small kernel that zeroes the counters. Every shape
+ * the plans produce fits; a plan that did not fit the scratch would return
+ * QWG_ERR_SHAPE. All calls on one GPU share the one scratch array: calls that
+ * overlap in time on that GPU (on different streams, or replays of graphs
+ * that contain such calls) race and must not be made.
+ */
+int qwg_gemm_q4k_noalloc(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                         int batch, void *stream);
 
 /*
  * qwg_gemm_q4k with an explicit work decomposition (tuning and testing):

@@ -65,6 +65,7 @@ def lib() -> ctypes.CDLL:
         L.qwg_gemv_iq3.argtypes = [P, P, P, P, I64, I64, P]
         L.qwg_gemm_q4k.argtypes = [P, P, P, I64, I64, I, P]
         L.qwg_gemm_q4k_ex.argtypes = [P, P, P, I64, I64, I, I, I, P]
+        L.qwg_gemm_q4k_noalloc.argtypes = [P, P, P, I64, I64, I, P]
         L.qwg_workspace_reserve.argtypes = [P]
         L.qwg_workspace_release.argtypes = [P]
         L.qwg_gemv_iq3_ex.argtypes = [P, P, P, P, I64, I64, I, I, P]
@@ -91,7 +92,7 @@ def lib() -> ctypes.CDLL:
                   "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
                   "qwg_group_destroy", "qwg_group_create_q4k_batched",
                   "qwg_group_create_q4k_batched_tiled", "qwg_gemm_q4k_tiled",
-                  "qwg_workspace_reserve", "qwg_workspace_release"):
+                  "qwg_gemm_q4k_noalloc", "qwg_workspace_reserve", "qwg_workspace_release"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -474,6 +475,25 @@ def gemm_q4k(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
     else:
         _check(lib().qwg_gemm_q4k(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out, batch,
                                   _stream(x)), "qwg_gemm_q4k")
+    return out
+
+
+def gemm_q4k_noalloc(w: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm_q4k through qwg_gemm_q4k_noalloc (split sums in the library's static
+    scratch: the call allocates nothing). x fp32 [batch, n_in]; `out` is
+    [batch, n_out] (allocated here if None, before the call)."""
+    _dev(x, "x", torch.float32)
+    if x.dim() != 2 or not 1 <= x.shape[0] <= MAX_BATCH:
+        raise ValueError("x must be [batch, n_in] with 1 <= batch <= 8")
+    batch, n_in = x.shape
+    n_out = _weights(w, n_in, Q4K_BYTES)
+    if out is None:
+        out = torch.empty(batch, n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.shape != (batch, n_out):
+        raise ValueError("out has the wrong shape")
+    _check(lib().qwg_gemm_q4k_noalloc(out.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out,
+                                      batch, _stream(x)), "qwg_gemm_q4k_noalloc")
     return out
 
 

@@ -291,7 +291,7 @@ const char *qwg_strerror(int status) {
         case QWG_ERR_FORMAT: return "unknown format id";
         case QWG_ERR_CAPTURE:
             return "the stream is being captured and has no split-sum workspace yet "
-                   "(qwg_workspace_reserve it before capture)";
+                   "(qwg_workspace_reserve it before capture, or call qwg_gemm_q4k_noalloc)";
         default: return "unknown status";
     }
 }
@@ -394,9 +394,55 @@ int qwg_dequant_iq3_xxs(const void *src, const float *grid, float *dst, int64_t 
 
 namespace {
 
-// qwg_gemm_q4k, its split sums in the stream's workspace.
+// Split-sum scratch of qwg_gemm_q4k_noalloc: partial sums (kScratchFloats) then
+// tile counters (kScratchCounters), one copy per GPU in the library's code
+// object. Host code never uses the array's name as an address: each device's
+// address comes from hipGetSymbolAddress (scratch_of). The counters start at
+// zero (cleared when a device is first used) and every launch leaves them at
+// zero. The largest split plan of qwg_gemm_q4k needs fewer than 2,304 x 64
+// partial sums (batch 1) and fewer than 256 tiles, so these sizes cover every
+// shape; a plan that did not fit would be rejected (QWG_ERR_SHAPE).
+constexpr size_t kScratchFloats = (size_t)4096 * kTileRows;
+constexpr size_t kScratchCounters = 4096;
+static __device__ __align__(256) uint32_t scratch[kScratchFloats + kScratchCounters];
+
+__global__ void zero_u32_kernel(uint32_t *p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+std::map<int, uint32_t *> g_scratch;
+
+// This device's copy of `scratch` (set up on the first call on the device:
+// symbol address, then a fill kernel that zeroes the counters, enqueued on the
+// caller's stream ahead of the call's own kernels).
+int scratch_of(hipStream_t stream, Workspace *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QWG_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch.find(dev);
+    uint32_t *base = nullptr;
+    if (it != g_scratch.end()) {
+        base = it->second;
+    } else {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return QWG_ERR_HIP;
+        base = (uint32_t *)ptr;
+        hipLaunchKernelGGL(zero_u32_kernel, dim3(16), dim3(256), 0, stream,
+                           base + kScratchFloats, (int)kScratchCounters);
+        if (hipGetLastError() != hipSuccess) return QWG_ERR_HIP;
+        g_scratch.emplace(dev, base);
+    }
+    out->partial = (float *)base;
+    out->counters = base + kScratchFloats;
+    return QWG_OK;
+}
+
+// qwg_gemm_q4k, its split sums in the stream's workspace (noalloc = false) or
+// in the static scratch (noalloc = true).
 int gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out, int batch,
-             hipStream_t stream) {
+             hipStream_t stream, bool noalloc) {
     if (!y || !x || !w) return QWG_ERR_NULL;
     int rc = check_gemv_shape(n_in, n_out);
     if (rc) return rc;
@@ -414,7 +460,14 @@ int gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_ou
     }
     if (a.splits > 1) {
         Workspace ws;
-        rc = get_workspace(stream, &ws);
+        if (noalloc) {
+            if ((size_t)a.splits * batch * a.tiles * kTileRows > kScratchFloats ||
+                (size_t)a.tiles > kScratchCounters)
+                return QWG_ERR_SHAPE;
+            rc = scratch_of(stream, &ws);
+        } else {
+            rc = get_workspace(stream, &ws);
+        }
         if (rc) return rc;
         a.partial = ws.partial;
         a.counters = ws.counters;
@@ -434,7 +487,12 @@ extern "C" {
 
 int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out, int batch,
                  void *stream) {
-    return gemm_q4k(y, x, w, n_in, n_out, batch, (hipStream_t)stream);
+    return gemm_q4k(y, x, w, n_in, n_out, batch, (hipStream_t)stream, false);
+}
+
+int qwg_gemm_q4k_noalloc(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,
+                         int batch, void *stream) {
+    return gemm_q4k(y, x, w, n_in, n_out, batch, (hipStream_t)stream, true);
 }
 
 int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64_t n_out,

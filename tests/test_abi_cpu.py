@@ -41,7 +41,7 @@ def test_header_declares_the_entry_points():
                  "qwg_gemv_iq3s_tiled", "qwg_gemv_iq4xs_tiled", "qwg_group_create_iq3s_tiled",
                  "qwg_group_create_iq4xs_tiled", "qwg_encode_iq3",
                  "qwg_group_create_q4k_batched", "qwg_group_create_q4k_batched_tiled",
-                 "qwg_gemm_q4k_tiled", "qwg_workspace_reserve",
+                 "qwg_gemm_q4k_tiled", "qwg_gemm_q4k_noalloc", "qwg_workspace_reserve",
                  "qwg_workspace_release"):
         assert want in names
 
@@ -178,6 +178,14 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE, FAKE, 0, 1, None), 2),
     (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE + 4, FAKE, 256, 1, None), 3),
     (lambda L: L.qwg_pack_iq3_xxs_tiles(FAKE, FAKE + 1, 256, 1, None), 3),
+    # the allocation-free GEMM: the same validation as qwg_gemm_q4k
+    (lambda L: L.qwg_gemm_q4k_noalloc(None, FAKE, FAKE, 256, 1, 1, None), 1),
+    (lambda L: L.qwg_gemm_q4k_noalloc(FAKE, FAKE, FAKE, 300, 1, 1, None), 2),
+    (lambda L: L.qwg_gemm_q4k_noalloc(FAKE, FAKE, FAKE, 256, 0, 1, None), 2),
+    (lambda L: L.qwg_gemm_q4k_noalloc(FAKE, FAKE, FAKE, 256, 1, 0, None), 4),
+    (lambda L: L.qwg_gemm_q4k_noalloc(FAKE, FAKE, FAKE, 256, 1, 9, None), 4),
+    (lambda L: L.qwg_gemm_q4k_noalloc(FAKE, FAKE + 4, FAKE, 256, 1, 1, None), 3),
+    (lambda L: L.qwg_gemm_q4k_noalloc(FAKE, FAKE, FAKE + 8, 256, 1, 1, None), 3),
     # IQ3 encoder
     (lambda L: L.qwg_encode_iq3(None, FAKE, FAKE, 1, 256, None), 1),
     (lambda L: L.qwg_encode_iq3(FAKE, None, FAKE, 1, 256, None), 1),
