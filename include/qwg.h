@@ -81,6 +81,7 @@ extern "C" {
 #define QWG_ERR_HIP 5      /* the HIP runtime reported an error (launch, allocation) */
 #define QWG_ERR_FORMAT 6   /* unknown format id */
 #define QWG_ERR_CAPTURE 7  /* the stream is capturing and a call would have to allocate */
+#define QWG_ERR_TIMEOUT 8  /* a wait of a layer-chain launch gave up (qwg_chain_status) */
 
 /* format ids */
 #define QWG_FMT_Q4K 0
@@ -415,6 +416,56 @@ int qwg_group_create_iq4xs_tiled(const qwg_gemv_desc *descs, int count, const fl
 int qwg_group_run(const qwg_group *group, void *stream);
 int qwg_group_workgroups(const qwg_group *group);
 int qwg_group_destroy(qwg_group *group);
+
+/*
+ * Layer chain: a decoder's per-token weight stream as one launch whose phases
+ * run in dependency order ("用 Python 重写 picoLM" page, model_forward and
+ * forward listings: per layer the q/k/v products read the normalized x, the
+ * output projection reads the attention output, gate/up read the normalized
+ * residual, down reads the SwiGLU activation, the next layer reads the updated
+ * x, the LM head reads the final norm). The operations between the products
+ * (norms, attention, activation) are outside this library, so the launch
+ * treats each phase as depending on all outputs of the phase before it: no
+ * product of phase p+1 reads its activations before every member of phase p
+ * has stored its result. Weights do not depend on activations and are
+ * fetched ahead across phases.
+ *
+ * qwg_chain_create_q4k: `count` members (qwg_gemv_desc, Q4_K weights in the
+ * tile layout of qwg_pack_q4k_tiles, 16-byte aligned; x 16-byte aligned, y
+ * 4-byte aligned; shape rules as qwg_gemv_q4k) in phase order: the first
+ * phase_sizes[0] members form phase 0, the next phase_sizes[1] phase 1, and so
+ * on (n_phases >= 1, every size >= 1, the sizes summing to count). A member's
+ * x may be (or overlap) the y of a member of an earlier phase: it is then read
+ * only after that phase has completed. QWG_ERR_SHAPE if an x overlaps a y of
+ * the same phase. Validation happens before anything is allocated; then the
+ * plan (one workgroup per compute unit, each phase's work spread over all of
+ * them) is copied to a device buffer owned by the chain (hipMalloc + hipMemcpy:
+ * synchronous). The member pointers are baked into the plan; reuse the same
+ * buffers on every run (e.g. fixed activation/output buffers of a decode loop).
+ * qwg_chain_run: enqueues the whole chain on `stream` (asynchronous). The
+ * launch holds one workgroup on every compute unit and its phases wait for one
+ * another, so it needs the whole device: run nothing else on the device at the
+ * same time, and do not overlap two runs of one chain. Every wait is bounded
+ * (0.2 s): a wait that gives up marks the chain's error word and the launch
+ * ends early (outputs then undefined).
+ * qwg_chain_status: waits for the device (hipDeviceSynchronize), then returns
+ * QWG_OK, or QWG_ERR_TIMEOUT if a wait of an earlier run gave up (the chain is
+ * re-armed and can run again).
+ * qwg_chain_phases: number of phases of one launch (a phase with more work
+ * than the device's compute units take at once runs as several), or a negative
+ * status.
+ * qwg_chain_destroy: frees the plan (hipFree: synchronous). NULL is accepted.
+ * Results meet the same bound as qwg_gemv_q4k for every member and are
+ * bitwise reproducible (fixed summation order).
+ */
+typedef struct qwg_chain qwg_chain;
+
+int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase_sizes,
+                         int n_phases, qwg_chain **chain);
+int qwg_chain_run(const qwg_chain *chain, void *stream);
+int qwg_chain_status(qwg_chain *chain);
+int qwg_chain_phases(const qwg_chain *chain);
+int qwg_chain_destroy(qwg_chain *chain);
 
 #ifdef __cplusplus
 }

@@ -66,6 +66,11 @@ def lib() -> ctypes.CDLL:
         L.qwg_gemm_q4k.argtypes = [P, P, P, I64, I64, I, P]
         L.qwg_gemm_q4k_ex.argtypes = [P, P, P, I64, I64, I, I, I, P]
         L.qwg_gemm_q4k_noalloc.argtypes = [P, P, P, I64, I64, I, P]
+        L.qwg_chain_create_q4k.argtypes = [P, I, P, I, ctypes.POINTER(P)]
+        L.qwg_chain_run.argtypes = [P, P]
+        L.qwg_chain_status.argtypes = [P]
+        L.qwg_chain_phases.argtypes = [P]
+        L.qwg_chain_destroy.argtypes = [P]
         L.qwg_workspace_reserve.argtypes = [P]
         L.qwg_workspace_release.argtypes = [P]
         L.qwg_gemv_iq3_ex.argtypes = [P, P, P, P, I64, I64, I, I, P]
@@ -92,7 +97,9 @@ def lib() -> ctypes.CDLL:
                   "qwg_group_create_iq3", "qwg_group_run", "qwg_group_workgroups",
                   "qwg_group_destroy", "qwg_group_create_q4k_batched",
                   "qwg_group_create_q4k_batched_tiled", "qwg_gemm_q4k_tiled",
-                  "qwg_gemm_q4k_noalloc", "qwg_workspace_reserve", "qwg_workspace_release"):
+                  "qwg_gemm_q4k_noalloc", "qwg_workspace_reserve", "qwg_workspace_release",
+                  "qwg_chain_create_q4k", "qwg_chain_run", "qwg_chain_status", "qwg_chain_phases",
+                  "qwg_chain_destroy"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -679,3 +686,63 @@ class Iq4xsGroup(Group):
 
     def __init__(self, members, table: torch.Tensor):
         super().__init__(members, QWG_FMT_IQ4_XS, table, tiled=True)
+
+
+class Q4kChain:
+    """A decoder's weight stream as one launch whose phases run in order: phase
+    p+1's products read their activations only after every member of phase p
+    has stored its output (qwg_chain_create_q4k).
+
+    phases: sequence of phases, each a sequence of members (w, x, y): Q4_K
+    weights in the tile layout (pack_q4k_tiles), fp32 x [n_in], fp32 y [n_out].
+    A member's x may be the y tensor of a member of an earlier phase. The
+    tensors are referenced by the plan (kept alive here) and must stay in place.
+    """
+
+    def __init__(self, phases):
+        phases = [list(ph) for ph in phases]
+        if not phases or any(not ph for ph in phases):
+            raise ValueError("a chain needs at least one phase, each with at least one member")
+        members = [m for ph in phases for m in ph]
+        descs = (GemvDesc * len(members))()
+        for i, (w, x, y) in enumerate(members):
+            _dev(x, "x", torch.float32)
+            _dev(y, "y", torch.float32)
+            _dev(w, "w", torch.uint8)
+            n_in, n_out = x.numel(), y.numel()
+            if w.numel() != tiled_bytes(n_in, n_out):
+                raise ValueError(f"member {i}: w is not a tile-layout matrix of this shape")
+            descs[i] = GemvDesc(y.data_ptr(), x.data_ptr(), w.data_ptr(), n_in, n_out)
+        sizes = (ctypes.c_int * len(phases))(*[len(ph) for ph in phases])
+        self._members = members
+        self._device = members[0][1].device
+        handle = ctypes.c_void_p()
+        _check(lib().qwg_chain_create_q4k(descs, len(members), sizes, len(phases),
+                                          ctypes.byref(handle)), "qwg_chain_create_q4k")
+        self._handle = handle
+
+    @property
+    def launch_phases(self) -> int:
+        return lib().qwg_chain_phases(self._handle)
+
+    def run(self, stream=None) -> None:
+        if self._handle is None:
+            raise RuntimeError("chain destroyed")
+        s = stream if stream is not None else torch.cuda.current_stream(self._device)
+        _check(lib().qwg_chain_run(self._handle, ctypes.c_void_p(s.cuda_stream)), "qwg_chain_run")
+
+    def status(self) -> None:
+        """Wait for the device; raise QwgError if a wait of an earlier run gave up."""
+        _check(lib().qwg_chain_status(self._handle), "qwg_chain_status")
+
+    def close(self) -> None:
+        if self._handle is not None:
+            torch.cuda.synchronize(self._device)
+            _check(lib().qwg_chain_destroy(self._handle), "qwg_chain_destroy")
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

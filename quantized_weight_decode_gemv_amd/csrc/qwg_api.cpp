@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cstdlib>
 #include <new>
 #include <vector>
@@ -289,6 +290,8 @@ const char *qwg_strerror(int status) {
         case QWG_ERR_BATCH: return "batch must be in 1..8";
         case QWG_ERR_HIP: return "HIP runtime error";
         case QWG_ERR_FORMAT: return "unknown format id";
+        case QWG_ERR_TIMEOUT:
+            return "a wait of the layer-chain launch gave up (its flags have been reset)";
         case QWG_ERR_CAPTURE:
             return "the stream is being captured and has no split-sum workspace yet "
                    "(qwg_workspace_reserve it before capture, or call qwg_gemm_q4k_noalloc)";
@@ -1114,6 +1117,237 @@ int qwg_group_run(const qwg_group *g, void *stream) {
 }
 
 int qwg_group_workgroups(const qwg_group *g) { return g ? g->workgroups : -QWG_ERR_NULL; }
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ layer chain
+
+struct qwg_chain {
+    int device;
+    void *dev_mem;   // members, units, phases, fin, partial sums, counters, flags, error word
+    uint32_t *counters;
+    ChainArgs args;
+    int count;
+    int launch_phases;
+};
+
+namespace {
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+// Workgroups of a chain launch: one per compute unit, a multiple of 8 (the
+// XCDs), at most 256 (one flag per poll lane word).
+int chain_workgroups() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (cus > 256) cus = 256;
+    return cus - cus % 8;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase_sizes,
+                         int n_phases, qwg_chain **out) {
+    if (!descs || !phase_sizes || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP || n_phases < 1 || n_phases > count)
+        return QWG_ERR_SHAPE;
+    std::vector<int> phase_of((size_t)count);
+    {
+        int k = 0;
+        for (int p = 0; p < n_phases; ++p) {
+            if (phase_sizes[p] < 1 || k + phase_sizes[p] > count) return QWG_ERR_SHAPE;
+            for (int i = 0; i < phase_sizes[p]; ++i) phase_of[(size_t)k++] = p;
+        }
+        if (k != count) return QWG_ERR_SHAPE;
+    }
+    std::vector<ChainMember> mem((size_t)count);
+    for (int i = 0; i < count; ++i) {
+        const qwg_gemv_desc &d = descs[i];
+        if (!d.y || !d.x || !d.w) return QWG_ERR_NULL;
+        const int rc = check_gemv_shape(d.n_in, d.n_out);
+        if (rc) return rc;
+        if (!aligned(d.w, 16) || !aligned(d.x, 16) || !aligned(d.y, 4)) return QWG_ERR_ALIGN;
+        ChainMember &m = mem[(size_t)i];
+        m.w = (const uint8_t *)d.w;
+        m.x = d.x;
+        m.y = d.y;
+        m.partial = nullptr;
+        m.counters = nullptr;
+        m.n_out = (int)d.n_out;
+        m.nb = (int)(d.n_in / kQK);
+        m.tiles = (int)((d.n_out + kTileRows - 1) / kTileRows);
+        m.splits = 1;
+        m.mode = kChainDirect;
+        m.pad = 0;
+    }
+    // A member's activations may be the output of a member of an earlier phase
+    // (read after that phase completed); they must not overlap an output of
+    // the same phase.
+    std::vector<bool> wired((size_t)count, false);
+    for (int i = 0; i < count; ++i)
+        for (int j = 0; j < count; ++j) {
+            if (!overlaps(descs[j].x, (size_t)descs[j].n_in * 4, descs[i].y, (size_t)descs[i].n_out * 4))
+                continue;
+            if (phase_of[(size_t)i] >= phase_of[(size_t)j]) {
+                if (phase_of[(size_t)i] == phase_of[(size_t)j]) return QWG_ERR_SHAPE;
+                continue;   // written after it was read
+            }
+            wired[(size_t)i] = true;
+        }
+    const int nwg = chain_workgroups();
+    if (nwg < 8) return QWG_ERR_HIP;
+    const int64_t Q = (int64_t)nwg * kChainQuads;
+    // Units: per phase, L = ceil(columns / quads) super-block columns per unit
+    // (at most kChainMaxSteps), every quad at most one unit; a phase with more
+    // units than quads runs as several launch phases of which only the first
+    // waits for the previous phase.
+    std::vector<uint32_t> units, phases, fin;
+    size_t partial_floats = 0, counters = 0;
+    int launch_phases = 0;
+    int first = 0;
+    for (int p = 0; p < n_phases; ++p) {
+        const int last = first + phase_sizes[p];
+        int64_t cols = 0;
+        for (int i = first; i < last; ++i) cols += (int64_t)mem[(size_t)i].tiles * mem[(size_t)i].nb;
+        int64_t L = (cols + Q - 1) / Q;
+        if (L > kChainMaxSteps) L = kChainMaxSteps;
+        if (L < 1) L = 1;
+        std::vector<std::array<uint32_t, 4>> list;
+        for (int i = first; i < last; ++i) {
+            ChainMember &m = mem[(size_t)i];
+            m.splits = (int)((m.nb + L - 1) / L);
+            if (m.splits > 1) {
+                m.mode = wired[(size_t)i] ? kChainWired : kChainDeferred;
+                partial_floats += (size_t)m.splits * m.tiles * kTileRows;
+                if (m.mode == kChainWired) counters += (size_t)m.tiles;
+            }
+            for (int t = 0; t < m.tiles; ++t) {
+                for (int sp = 0; sp < m.splits; ++sp) {
+                    const int b0 = (int)(sp * L);
+                    const int nblk = (int)std::min<int64_t>(L, m.nb - b0);
+                    list.push_back({(uint32_t)i, (uint32_t)t,
+                                    (uint32_t)b0 | (uint32_t)nblk << 8 | (uint32_t)sp << 16, 0u});
+                }
+                if (m.mode == kChainDeferred) {
+                    fin.push_back((uint32_t)i);
+                    fin.push_back((uint32_t)t);
+                }
+            }
+        }
+        for (size_t c0 = 0; c0 < list.size(); c0 += (size_t)Q) {
+            const size_t row = units.size();
+            units.resize(row + (size_t)Q * 4, 0u);
+            for (int64_t k = 0; k < Q; ++k) units[row + (size_t)k * 4] = kNoItem;
+            for (size_t k = c0; k < std::min(list.size(), c0 + (size_t)Q); ++k) {
+                // spread a phase's units over every workgroup first
+                const int64_t i = (int64_t)(k - c0);
+                const int64_t colx = (i % nwg) * kChainQuads + (i / nwg) % kChainQuads;
+                for (int f = 0; f < 4; ++f) units[row + (size_t)colx * 4 + f] = list[k][(size_t)f];
+            }
+            phases.push_back((uint32_t)L);
+            phases.push_back(p > 0 && c0 == 0 ? 1u : 0u);
+            ++launch_phases;
+        }
+        first = last;
+    }
+    if (launch_phases > (1 << 20) || fin.size() / 2 > (size_t)INT32_MAX) return QWG_ERR_SHAPE;
+    // device memory
+    auto align256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    const size_t off_members = 0;
+    const size_t off_units = align256(off_members + sizeof(ChainMember) * mem.size());
+    const size_t off_phases = align256(off_units + sizeof(uint32_t) * units.size());
+    const size_t off_fin = align256(off_phases + sizeof(uint32_t) * phases.size());
+    const size_t off_partial = align256(off_fin + sizeof(uint32_t) * fin.size());
+    const size_t off_counters = align256(off_partial + sizeof(float) * partial_floats);
+    const size_t off_flags = align256(off_counters + sizeof(uint32_t) * counters);
+    const size_t off_err = align256(off_flags + sizeof(uint32_t) * 256);
+    const size_t all = off_err + 256;
+    qwg_chain *ch = new (std::nothrow) qwg_chain();
+    if (!ch) return QWG_ERR_HIP;
+    if (hipGetDevice(&ch->device) != hipSuccess || hipMalloc(&ch->dev_mem, all) != hipSuccess) {
+        delete ch;
+        return QWG_ERR_HIP;
+    }
+    uint8_t *base = (uint8_t *)ch->dev_mem;
+    {
+        size_t pf = 0, ct = 0;
+        for (ChainMember &m : mem) {
+            if (m.splits < 2) continue;
+            m.partial = (float *)(base + off_partial) + pf;
+            pf += (size_t)m.splits * m.tiles * kTileRows;
+            if (m.mode == kChainWired) {
+                m.counters = (uint32_t *)(base + off_counters) + ct;
+                ct += (size_t)m.tiles;
+            }
+        }
+    }
+    // Counters, flags and the error word start at zero; every run leaves the
+    // counters at zero and all flags equal.
+    if (hipMemset(base + off_counters, 0, off_err + 256 - off_counters) != hipSuccess ||
+        hipMemcpy(base + off_members, mem.data(), sizeof(ChainMember) * mem.size(),
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(base + off_units, units.data(), sizeof(uint32_t) * units.size(),
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(base + off_phases, phases.data(), sizeof(uint32_t) * phases.size(),
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        (!fin.empty() && hipMemcpy(base + off_fin, fin.data(), sizeof(uint32_t) * fin.size(),
+                                   hipMemcpyHostToDevice) != hipSuccess)) {
+        (void)hipFree(ch->dev_mem);
+        delete ch;
+        return QWG_ERR_HIP;
+    }
+    ch->counters = (uint32_t *)(base + off_counters);
+    ch->args.members = (const ChainMember *)(base + off_members);
+    ch->args.units = (const uint32_t *)(base + off_units);
+    ch->args.phases = (const uint32_t *)(base + off_phases);
+    ch->args.fin = (const uint32_t *)(base + off_fin);
+    ch->args.flags = (uint32_t *)(base + off_flags);
+    ch->args.err = (uint32_t *)(base + off_err);
+    ch->args.nphases = launch_phases;
+    ch->args.nfin = (int)(fin.size() / 2);
+    ch->args.nwg = nwg;
+    ch->count = count;
+    ch->launch_phases = launch_phases;
+    *out = ch;
+    return QWG_OK;
+}
+
+int qwg_chain_run(const qwg_chain *c, void *stream) {
+    if (!c) return QWG_ERR_NULL;
+    return hip_status(launch_q4k_chain(c->args, (hipStream_t)stream));
+}
+
+int qwg_chain_phases(const qwg_chain *c) { return c ? c->launch_phases : -QWG_ERR_NULL; }
+
+int qwg_chain_status(qwg_chain *c) {
+    if (!c) return QWG_ERR_NULL;
+    if (hipDeviceSynchronize() != hipSuccess) return QWG_ERR_HIP;
+    uint32_t err = 0;
+    if (hipMemcpy(&err, c->args.err, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess)
+        return QWG_ERR_HIP;
+    if (err == 0) return QWG_OK;
+    // A wait gave up: tile counters, flags and the error word are re-armed (they
+    // lie back to back, the counters first).
+    if (hipMemset(c->counters, 0, (uint8_t *)c->args.err + sizeof(uint32_t) - (uint8_t *)c->counters) !=
+        hipSuccess)
+        return QWG_ERR_HIP;
+    return QWG_ERR_TIMEOUT;
+}
+
+int qwg_chain_destroy(qwg_chain *c) {
+    if (!c) return QWG_OK;
+    const hipError_t e = hipFree(c->dev_mem);
+    delete c;
+    return hip_status(e);
+}
 
 int qwg_group_destroy(qwg_group *g) {
     if (!g) return QWG_OK;

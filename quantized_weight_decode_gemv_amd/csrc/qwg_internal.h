@@ -130,6 +130,55 @@ int cb_stream_bps(int fmt);     // super-blocks per pipeline stage
 hipError_t launch_cb_stream(int fmt, const GroupArgs &g, const GemvArgs &single, const float *tab,
                             int nitems, hipStream_t s);
 
+// Layer-chain launch (chain.hip): a decoder's Q4_K weight stream in phases that
+// run in dependency order inside one persistent launch (tile-layout weights).
+// One workgroup of kChainQuads x 4 wavefronts per compute unit; each quad
+// computes at most one unit per phase: one 64-row tile of one member over
+// nblk <= kChainMaxSteps consecutive super-block columns.
+constexpr int kChainQuads = 4;
+constexpr int kChainRing = 4;      // LDS ring slots (columns per quad)
+constexpr int kChainMaxSteps = 2;  // columns per unit
+// How a member's rows are completed: a unit covers whole rows (direct); units
+// store partial sums that the launch adds up at its end (deferred); or, for a
+// member whose y a later phase reads, the tile's last unit adds them up at
+// once (wired).
+constexpr int kChainDirect = 0;
+constexpr int kChainDeferred = 1;
+constexpr int kChainWired = 2;
+
+struct ChainMember {
+    const uint8_t *w;     // tile layout
+    const float *x;
+    float *y;
+    float *partial;       // [splits][tiles*64] fp32 (splits > 1)
+    uint32_t *counters;   // [tiles] (wired members)
+    int n_out;
+    int nb;
+    int tiles;
+    int splits;           // units per tile
+    int mode;
+    int pad;
+};
+
+// units: [nphases][nwg*kChainQuads] entries of four uint32 (member or kNoItem,
+// tile, b0 | nblk << 8 | split << 16, 0); phases: [nphases] pairs (columns of
+// the phase, 1 if it waits for the previous phase); fin: [nfin] pairs (member,
+// tile) of the deferred members' tiles; flags: one per workgroup (phases
+// completed, counted across runs); err: set when a wait gave up.
+struct ChainArgs {
+    const ChainMember *members;
+    const uint32_t *units;
+    const uint32_t *phases;
+    const uint32_t *fin;
+    uint32_t *flags;
+    uint32_t *err;
+    int nphases;
+    int nfin;
+    int nwg;
+};
+hipError_t launch_q4k_chain(const ChainArgs &c, hipStream_t s);
+int chain_lds_bytes();
+
 // IQ3 container encoder (encode.hip): x [nblocks][256] fp32 -> nblocks 98-byte
 // blocks, grid [256][4] in weight units.
 hipError_t launch_iq3_encode(const float *x, const float *grid, uint8_t *dst, int64_t nblocks,

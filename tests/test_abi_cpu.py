@@ -42,6 +42,8 @@ def test_header_declares_the_entry_points():
                  "qwg_group_create_iq4xs_tiled", "qwg_encode_iq3",
                  "qwg_group_create_q4k_batched", "qwg_group_create_q4k_batched_tiled",
                  "qwg_gemm_q4k_tiled", "qwg_gemm_q4k_noalloc", "qwg_workspace_reserve",
+                 "qwg_chain_create_q4k", "qwg_chain_run", "qwg_chain_status", "qwg_chain_phases",
+                 "qwg_chain_destroy",
                  "qwg_workspace_release"):
         assert want in names
 
@@ -58,7 +60,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_version_and_strerror(L):
     assert L.qwg_version() >= 100
-    for st in range(0, 9):
+    for st in range(0, 10):
         assert len(L.qwg_strerror(st)) > 0
 
 
@@ -347,3 +349,32 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         _binding.lib()
+
+
+def test_chain_validation_errors(L):
+    # Rejected on the host before any HIP call: NULL pointers, phase sizes that
+    # do not add up, bad shapes or alignment, and an input that overlaps an
+    # output of the same phase.
+    out = ctypes.c_void_p()
+    one = (ctypes.c_int * 1)(1)
+    good = _Desc(FAKE, FAKE + 4096, FAKE + 8192, 256, 64)
+    assert L.qwg_chain_create_q4k(None, 1, one, 1, ctypes.byref(out)) == 1
+    assert L.qwg_chain_create_q4k((_Desc * 1)(good), 1, None, 1, ctypes.byref(out)) == 1
+    assert L.qwg_chain_create_q4k((_Desc * 1)(good), 1, one, 1, None) == 1
+    assert L.qwg_chain_create_q4k((_Desc * 1)(good), 0, one, 1, ctypes.byref(out)) == 2
+    assert L.qwg_chain_create_q4k((_Desc * 1)(good), 1, (ctypes.c_int * 1)(2), 1, ctypes.byref(out)) == 2
+    assert L.qwg_chain_create_q4k((_Desc * 2)(good, good), 2, one, 1, ctypes.byref(out)) == 2
+    assert L.qwg_chain_create_q4k((_Desc * 1)(_Desc(FAKE, FAKE + 4096, FAKE + 8192, 300, 64)), 1, one,
+                                  1, ctypes.byref(out)) == 2
+    assert L.qwg_chain_create_q4k((_Desc * 1)(_Desc(FAKE, FAKE + 4100, FAKE + 8192, 256, 64)), 1, one,
+                                  1, ctypes.byref(out)) == 3
+    assert L.qwg_chain_create_q4k((_Desc * 1)(_Desc(FAKE, FAKE + 4096, FAKE + 8200, 256, 64)), 1, one,
+                                  1, ctypes.byref(out)) == 3
+    # x of the second member is the y of the first, both in one phase
+    a = _Desc(FAKE, FAKE + 4096, FAKE + 8192, 256, 256)
+    b = _Desc(FAKE + 65536, FAKE, FAKE + 8192, 256, 64)
+    assert L.qwg_chain_create_q4k((_Desc * 2)(a, b), 2, (ctypes.c_int * 1)(2), 1, ctypes.byref(out)) == 2
+    assert L.qwg_chain_run(None, None) == 1
+    assert L.qwg_chain_status(None) == 1
+    assert L.qwg_chain_phases(None) == -1
+    assert L.qwg_chain_destroy(None) == 0

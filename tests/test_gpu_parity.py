@@ -1195,6 +1195,130 @@ def test_graph_replays_match_eager():
         g.close()
 
 
+# ---------------------------------------------------------------- layer chain
+
+def layer_phases(probs):
+    """The per-token stream's problems grouped into the phases of a decoder's
+    dependency chain (picoLM's model_forward: per layer q|k|v, o, gate|up,
+    down; then the LM head), as lists of indices."""
+    phases, i = [], 0
+    while i < len(probs):
+        name = probs[i].name.split(".")[-1]
+        n = 3 if name == "q" else 2 if name == "gate" else 1
+        phases.append(list(range(i, i + n)))
+        i += n
+    return phases
+
+
+def test_chain_c5_all_rows_and_repeat_runs():
+    # The launch the bench times for the dependency-respecting stream: 89
+    # phases over the 155 GEMVs, independent inputs. Every row of every output
+    # (NaN-filled first) against the oracle; later runs bitwise equal.
+    probs, ws, xs, refs = q4k_c5()
+    W = [qwg.pack_q4k_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
+    X = [dev(x) for x in xs]
+    Y = nan_outputs(probs)
+    phases = layer_phases(probs)
+    assert len(phases) == 89
+    ch = qwg.Q4kChain([[(W[i], X[i], Y[i]) for i in ph] for ph in phases])
+    assert ch.launch_phases >= 89
+    ch.run()
+    ch.status()
+    assert_stream(probs, refs, Y, "chain")
+    first = [host(y).copy() for y in Y]
+    for y in Y:
+        y.fill_(float("nan"))
+    for _ in range(3):
+        ch.run()
+    ch.status()
+    for p, y, y0 in zip(probs, Y, first):
+        assert_bits(host(y), y0, "chain rerun " + p.name)
+    ch.close()
+
+
+def _small_q4k(n_out, n_in, seed, d=2e-5):
+    """Q4_K weights with d and dmin near `d` (fp16), so that products chained
+    over many phases stay far inside the fp32 range."""
+    w = synth.q4k_weights(n_out, n_in, 201, seed).reshape(-1, 144).copy()
+    rng = np.random.default_rng(seed)
+    w[:, 0:2] = (rng.uniform(0.5, 1.5, len(w)) * d).astype(np.float16).view(np.uint8).reshape(-1, 2)
+    w[:, 2:4] = (rng.uniform(0.5, 1.5, len(w)) * d).astype(np.float16).view(np.uint8).reshape(-1, 2)
+    return w.reshape(n_out, -1)
+
+
+def test_chain_wired_phases_read_the_previous_outputs():
+    # Each phase reads what the phase before it wrote: q|k|v read x (then the
+    # previous down's y), o reads y_q, gate|up read y_o, down reads y_gate, and
+    # an LM-head-shaped last phase reads the last y_down. Outputs start as NaN
+    # and the input changes every run, so a phase that read its input before
+    # the producer finished (or a stale copy of an earlier run) fails the bound
+    # against the oracle applied to the producer's final output.
+    layers = 4
+    shapes = {"q": (2048, 2048), "k": (256, 2048), "v": (256, 2048), "o": (2048, 2048),
+              "gate": (5632, 2048), "up": (5632, 2048), "down": (2048, 5632)}
+    x0 = torch.empty(2048, device=DEV)
+    members, phases = [], []
+    src = x0
+    for l in range(layers):
+        mk = {}
+        for k, name in enumerate(shapes):
+            n_out, n_in = shapes[name]
+            w = _small_q4k(n_out, n_in, 10 * l + k)
+            mk[name] = [w, qwg.pack_q4k_tiles(dev(w), n_in), None,
+                        torch.empty(n_out, device=DEV)]
+        for name in ("q", "k", "v"):
+            mk[name][2] = src
+        mk["o"][2] = mk["q"][3]
+        mk["gate"][2] = mk["o"][3]
+        mk["up"][2] = mk["o"][3]
+        mk["down"][2] = mk["gate"][3]
+        src = mk["down"][3]
+        for group in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+            phases.append([len(members) + i for i in range(len(group))])
+            members += [mk[name] for name in group]
+    wh = _small_q4k(32000, 2048, 99)
+    members.append([wh, qwg.pack_q4k_tiles(dev(wh), 2048), src, torch.empty(32000, device=DEV)])
+    phases.append([len(members) - 1])
+    ch = qwg.Q4kChain([[tuple(members[i][1:]) for i in ph] for ph in phases])
+    for run in range(3):
+        x0.copy_(torch.from_numpy(synth.activations(2048, 201, run)))
+        for m in members:
+            m[3].fill_(float("nan"))
+        ch.run()
+        ch.status()
+        for i, (w, _, x, y) in enumerate(members):
+            xh = host(x).copy()
+            assert not np.isnan(xh).any(), f"run {run} member {i}: input left unwritten"
+            yr, sr = oracle.gemv_q4k(w, xh, x.numel(), y.numel())
+            assert_bound(host(y), yr, sr, f"run {run} wired member {i}")
+    ch.close()
+
+
+def test_chain_ragged_members_and_one_phase():
+    # Ragged row counts, one-block rows, 256-block rows (256 units per tile),
+    # several members in a phase, and a chain of a single phase.
+    shapes = [[(1, 256), (65, 512)], [(300, 65536)], [(4097, 768), (64, 2048), (129, 5632)]]
+    members, refs = [], []
+    for pi, ph in enumerate(shapes):
+        row = []
+        for k, (n_out, n_in) in enumerate(ph):
+            w = synth.q4k_weights(n_out, n_in, 202, 10 * pi + k)
+            x = synth.activations(n_in, 202, 10 * pi + k)
+            y = torch.full((n_out,), float("nan"), device=DEV)
+            row.append((qwg.pack_q4k_tiles(dev(w), n_in), dev(x), y))
+            refs.append((w, x, y, n_in, n_out))
+        members.append(row)
+    for chain_phases in (members, [members[2]]):
+        ch = qwg.Q4kChain(chain_phases)
+        for _ in range(2):
+            ch.run()
+        ch.status()
+        for w, x, y, n_in, n_out in refs if chain_phases is members else refs[3:]:
+            yr, sr = oracle.gemv_q4k(w, x, n_in, n_out)
+            assert_bound(host(y), yr, sr, f"chain {n_out}x{n_in}")
+        ch.close()
+
+
 # ---------------------------------------------------------------- IQ3_S and IQ4_XS
 
 CB = {
