@@ -64,7 +64,8 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/chain.hip",
 # WRITE_SIZE runs of this script, each scaled by the same counter on a plain device copy of known
 # size (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_chain_c5.md). Valid only for the
 # kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "", "fetch_bytes": None, "write_bytes": None}
+TRAFFIC = {"sources_sha256": "33da8adc5c1f443e8dbe2a73667b7f546a1421b71a378d4dd08aca8b0e418764",
+           "fetch_bytes": 603433370, "write_bytes": 14128128}
 
 
 def kernel_sources_sha256() -> str:
@@ -95,8 +96,8 @@ def parse():
     ap.add_argument("--print-kernel-hash", action="store_true",
                     help="print the hash of the kernel sources the traffic figure is tied to")
     ap.add_argument("--workload", default="q4k_stream",
-                    choices=["q4k_stream", "iq3_stream", "iq3_xxs", "codebooks", "encode", "lm_head",
-                             "batched"],
+                    choices=["q4k_stream", "configs", "iq3_stream", "iq3_xxs", "codebooks", "encode",
+                             "lm_head", "batched"],
                     help="q4k_stream: the headline (default); the others: see the module docstring")
     ap.add_argument("--headline-only", action="store_true",
                     help="run and time only the headline launch (no other schedules, no "
@@ -132,6 +133,9 @@ def main():
         print("bench.py measures one GPU: the GEMV path has no multi-GPU mode "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "configs":
+        bench_configs(args)
+        return
     if args.workload == "iq3_stream":
         bench_iq3_stream(args)
         return
@@ -380,6 +384,32 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def bench_configs(args):
+    """One JSON line per configuration C1-C4 (single calls through the C ABI,
+    cold weights): per call median / p10 / p90, GB/s, % of peak, the parity max
+    ratio over all rows and the dequant bit-mismatch count (the per-config
+    records of the default run, printed on their own)."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    gpu = run_configs(dev, stream, args)
+    if args.no_cpu:
+        recs = {k: v["rec"] for k, v in gpu.items()}
+    else:
+        recs = cpu_baseline_leg(None, None, None, {}, gpu, 0.0, configs_only=True)
+    for cfg in ("C1", "C2", "C3", "C4"):
+        members = {k: v for k, v in recs.items() if v["config"] == cfg}
+        total_bytes = sum(v["algorithmic_bytes"] for v in members.values())
+        total_us = sum(v["median_us"] for v in members.values())
+        print(json.dumps({
+            "metric": "effective HBM GB/s (% of MI355X peak) for Q4_K/IQ3 GEMV, batch 1",
+            "config": cfg, "value": round(total_bytes / total_us / 1e3, 2), "unit": "GB/s",
+            "n_gpus": 1, "dtype": "f32", "data": "synthetic", "higher_is_better": True,
+            "pct_of_hbm_peak": round(100 * total_bytes / total_us / 1e3 / HBM_PEAK_GBS, 2),
+            "calls": members}), flush=True)
+
+
 def layer_phases(probs):
     """The per-token stream's GEMVs grouped into the phases of a decode step
     (picoLM model_forward: per layer q|k|v read the normalized x, o the attention
@@ -500,7 +530,7 @@ def cpu_info():
             "cpus_online": os.cpu_count()}
 
 
-def cpu_baseline_leg(probs, host_w, host_x, gpu_out, per_config_gpu, budget_s):
+def cpu_baseline_leg(probs, host_w, host_x, gpu_out, per_config_gpu, budget_s, configs_only=False):
     """Everything that runs the oracle (plain C, fp64 dot, OpenMP over rows):
     (1) the full oracle result of the per-token stream, against which every row
     of every schedule's GPU output is checked (the bench stops if any row is
@@ -514,9 +544,9 @@ def cpu_baseline_leg(probs, host_w, host_x, gpu_out, per_config_gpu, budget_s):
 
     oracle.build(force=False)
     threads0 = oracle.get_threads()
-    step_bytes = sum(p.algorithmic_bytes for p in probs)
-    ref = [oracle.gemv_q4k(w, x, p.n_in, p.n_out) for p, w, x in zip(probs, host_w, host_x)]
     parity = {}
+    ref = [] if configs_only else [oracle.gemv_q4k(w, x, p.n_in, p.n_out)
+                                   for p, w, x in zip(probs, host_w, host_x)]
     for name, outs in gpu_out.items():
         worst = 0.0
         for (yr, sr), yg in zip(ref, outs):
@@ -552,6 +582,9 @@ def cpu_baseline_leg(probs, host_w, host_x, gpu_out, per_config_gpu, budget_s):
                 rec["dequant_bit_mismatches"] = int(np.count_nonzero(
                     dq.reshape(-1).view(np.uint32) != item["deq_bits"]))
             per_config[key] = rec
+    if configs_only:
+        return per_config
+    step_bytes = sum(p.algorithmic_bytes for p in probs)
 
     def run_for(seconds):
         runs, t = 0, 0.0
