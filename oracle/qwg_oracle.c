@@ -154,6 +154,22 @@ int orc_dequant_q4k(const uint8_t *src, int64_t n, float *dst)
 /* ------------------------------------------------------------------ IQ3 */
 
 /*
+ * 1 if weight t (0..31) of a sub-block is negative, from the sub-block's
+ * uint32: weight t belongs to group t/8, whose seven stored sign bits sit at
+ * bits 7*(t/8) .. 7*(t/8)+6; position j = t%8 < 7 reads bit j of them, and the
+ * eighth position carries their parity, so that every group of eight has an
+ * even number of negatives.
+ */
+static int container_weight_negative(uint32_t word, int t)
+{
+    uint32_t stored = (word >> (7 * (t >> 3))) & 0x7Fu;
+    int j = t & 7;
+    if (j < 7)
+        return (int)((stored >> j) & 1u);
+    return __builtin_popcount(stored) & 1;
+}
+
+/*
  * [iq3pack] one block: bytes 0..63 are grid indices (one per 4 weights), bytes
  * 64..95 eight little-endian uint32 words (one per 32-weight sub-block), bytes
  * 96..97 the fp16 super-scale d. In word ib, bits 7l..7l+6 (l = 0..3) are the
@@ -161,9 +177,8 @@ int orc_dequant_q4k(const uint8_t *src, int64_t n, float *dst)
  * weight 8l+7 is the XOR of those seven bits, and bits 28..31 are the sub-scale
  * code. Sub-block scale db = d * (0.5 + code) * 0.5, and weight t of sub-block ib
  * is grid[idx[8ib + t/4]][t % 4] * sign_t * db, with the grid in weight units.
- * decode() forms db in double (0.5 + an integer promotes), multiplies
- * magnitude by sign in fp32 and stores the double product as fp32; this does the
- * same.
+ * decode() forms db in double (0.5 + an integer promotes), signs the
+ * magnitude in fp32 and stores the double product as fp32; this does the same.
  */
 static void iq3_block(const uint8_t *b, const float *grid, float *out)
 {
@@ -174,22 +189,12 @@ static void iq3_block(const uint8_t *b, const float *grid, float *out)
                         ((uint32_t)wp[3] << 24);
         uint32_t code = (word >> 28) & 0xF;
         double db = d * (0.5 + (double)code) * 0.5;
-        float sgn[32];
-        for (int l = 0; l < 4; ++l) {
-            uint32_t seven = (word >> (7 * l)) & 0x7F;
-            int par = 0;
-            for (int j = 0; j < 7; ++j) {
-                int bit = (seven >> j) & 1;
-                sgn[8 * l + j] = bit ? -1.0f : 1.0f;
-                par ^= bit;
-            }
-            sgn[8 * l + 7] = par ? -1.0f : 1.0f;
-        }
         for (int t = 0; t < 32; ++t) {
-            int idx = b[8 * ib + t / 4];
-            float mag = grid[4 * idx + t % 4];
-            float ms = mag * sgn[t];
-            out[32 * ib + t] = (float)((double)ms * db);
+            float mag = grid[4 * b[8 * ib + t / 4] + t % 4];
+            /* the signed magnitude is exact in fp32; the product with db is
+             * formed in double and stored as fp32 */
+            float signed_mag = container_weight_negative(word, t) ? -mag : mag;
+            out[32 * ib + t] = (float)((double)signed_mag * db);
         }
     }
 }
@@ -233,22 +238,10 @@ static void iq3_xxs_block(const uint8_t *b, const float *grid, float *out)
         uint32_t s = word >> 28;
         float eff = d * (0.5f + (float)s);
         eff = eff * 0.5f;
-        for (int l = 0; l < 4; ++l) {
-            uint32_t seven = (word >> (7 * l)) & 0x7F;
-            int negatives = 0;
-            for (int j = 0; j < 8; ++j) {
-                int neg;
-                if (j < 7) {
-                    neg = (seven >> j) & 1;
-                    negatives += neg;
-                } else {
-                    neg = negatives & 1;   /* makes the count even */
-                }
-                int t = 8 * l + j;
-                float entry = grid[4 * b[2 + 8 * ib + t / 4] + t % 4];
-                float v = neg ? -entry : entry;
-                out[32 * ib + t] = v * eff;
-            }
+        for (int t = 0; t < 32; ++t) {
+            float entry = grid[4 * b[2 + 8 * ib + t / 4] + t % 4];
+            float v = container_weight_negative(word, t) ? -entry : entry;
+            out[32 * ib + t] = v * eff;
         }
     }
 }
