@@ -82,6 +82,7 @@ extern "C" {
 #define QWG_ERR_FORMAT 6   /* unknown format id */
 #define QWG_ERR_CAPTURE 7  /* the stream is capturing and a call would have to allocate */
 #define QWG_ERR_TIMEOUT 8  /* a wait of a layer-chain launch gave up (qwg_chain_status) */
+#define QWG_ERR_GRID 9     /* a codebook value is not exactly representable in fp16 */
 
 /* format ids */
 #define QWG_FMT_Q4K 0
@@ -177,7 +178,10 @@ int qwg_gemv_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
  * never one that reaches outside [w, w + n_out*row_bytes).
  * grid: [256][4] fp32 magnitudes, 16-byte aligned; every magnitude must be
  * exactly representable in fp16 (true for the integer magnitudes IQ3 grids
- * use), otherwise the result is the product with the fp16-rounded grid.
+ * use): the kernels keep the grid in fp16, and if a value is not exact they
+ * store NaN in every output row of the call (the call itself cannot report it:
+ * it only enqueues). Group creation checks the grid on the host and returns
+ * QWG_ERR_GRID instead.
  * x: n_in fp32, 16-byte aligned. y: n_out fp32, 4-byte aligned.
  * Shape limits and accuracy as qwg_gemv_q4k.
  */
@@ -228,9 +232,9 @@ int qwg_encode_iq3(void *dst, const float *x, const float *grid, int64_t n_rows,
  * qwg_gemv_iq3s_tiled / qwg_gemv_iq4xs_tiled: y = W x on that layout (w
  * 16-byte aligned; x 16-byte aligned, y 4-byte aligned, the grid/table
  * 16-byte aligned). Every grid or table value must be exactly representable
- * in fp16 (true for the integer values of these codebooks), otherwise the
- * result uses the fp16-rounded values. Shape limits and accuracy as
- * qwg_gemv_q4k.
+ * in fp16 (true for the integer values of these codebooks); otherwise every
+ * output row of the call is NaN (group creation returns QWG_ERR_GRID).
+ * Shape limits and accuracy as qwg_gemv_q4k.
  */
 int qwg_dequant_iq3s(const void *src, const float *grid, float *dst, int64_t n, void *stream);
 int qwg_dequant_iq4xs(const void *src, const float *table, float *dst, int64_t n, void *stream);
@@ -353,8 +357,10 @@ int qwg_pack_iq3_xxs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_o
  * qwg_gemv_desc: one member, fields as the qwg_gemv_q4k / qwg_gemv_iq3
  * arguments (device pointers, same alignment and shape rules).
  * qwg_group_create_q4k / qwg_group_create_iq3: validate every member (the
- * first failing member's status is returned, nothing is allocated), then copy
- * the launch plan to a device buffer owned by the group (hipMalloc +
+ * first failing member's status is returned, nothing is allocated) and, for
+ * the codebook formats, copy the grid or table to the host and check that
+ * every value is exactly representable in fp16 (QWG_ERR_GRID otherwise), then
+ * copy the launch plan to a device buffer owned by the group (hipMalloc +
  * hipMemcpy: synchronous). `descs` is a host array of `count` members
  * (1..QWG_MAX_GROUP) and is not kept. The member pointers (and the IQ3 grid,
  * shared by all members, rules as for qwg_gemv_iq3) are baked into the plan:

@@ -9,8 +9,8 @@
 //          codes at 8-135 (byte 8+16ib+j: weight j in the low nibble, weight
 //          j+16 in the high one); eff = d*(s-32), weight = table[q] * eff.
 // Dequantization is bit-exact. The GEMV runs on a tile layout (each 64-row
-// block column regrouped by field, as for IQ3) with a 16-wavefront stream
-// engine whose decode table lives in LDS.
+// block column regrouped by field, as for IQ3) with a stream engine of
+// 4-wavefront workgroups whose decode table (fp16) lives in LDS.
 #include <cstdlib>
 
 #include "qwg_device.h"
@@ -129,7 +129,9 @@ struct Iq3sFmt {
     // (nine bits) in fp16, each negated when its bit of s2 is set. 4096
     // entries, 16 KB (folding all four signs of a group into 8-byte entries
     // took 64 KB and left room for one workgroup per CU).
-    __device__ static void build_table(const float *grid, int t, int nthreads) {
+    // Returns false if a grid value this thread stored is not exactly fp16.
+    __device__ static bool build_table(const float *grid, int t, int nthreads) {
+        bool exact = true;
         for (int e = t; e < 4096; e += nthreads) {
             const int s2 = e >> 10, p = (e >> 9) & 1;
             const float2 g = *(const float2 *)(grid + 4 * (e & 511) + 2 * p);
@@ -138,7 +140,9 @@ struct Iq3sFmt {
             const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)v0);
             const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)v1);
             *(__attribute__((address_space(3))) uint32_t *)(size_t)(e * 4) = h0 | (h1 << 16);
+            exact = exact && fp16_exact(g.x) && fp16_exact(g.y);
         }
+        return exact;
     }
 
     // acc + this lane's row sum over wavefront G's 64 weights. Group k (four
@@ -221,11 +225,16 @@ struct Iq4xsFmt {
     // v*256 + 4c holds table[v] in fp16 in both halves, so the 64 lanes of a
     // read always hit 64 different banks. 4 KB (a pair table indexed by the
     // whole code byte took 64 KB and left room for one workgroup per CU).
-    __device__ static void build_table(const float *table, int t, int nthreads) {
+    // Returns false if a table value this thread stored is not exactly fp16.
+    __device__ static bool build_table(const float *table, int t, int nthreads) {
+        bool exact = true;
         for (int e = t; e < 1024; e += nthreads) {
-            const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)table[e >> 6]);
+            const float v = table[e >> 6];
+            const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)v);
             *(__attribute__((address_space(3))) uint32_t *)(size_t)(e * 4) = h | (h << 16);
+            exact = exact && fp16_exact(v);
         }
+        return exact;
     }
 
     // Byte j of sub-block h's sixteen code bytes gives weights j (low nibble)
@@ -409,9 +418,18 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
 #pragma unroll
     for (int i = 0; i < R - 1; ++i) issue_next();
 
-    // The decode table, while the first stages are in flight; the first stage
-    // barrier publishes it.
-    F::build_table(tab, (int)threadIdx.x, W * 64);
+    // The decode table, while the first stages are in flight. A value that
+    // fp16 cannot hold would be rounded in it: the workgroup then stores NaN in
+    // every row instead (host code that creates a group rejects such a table
+    // up front). The vote goes through a word of the row-sum buffer, idle
+    // until the first item ends.
+    volatile uint32_t *vote = (volatile uint32_t *)(smem + C::kRed);
+    if (threadIdx.x == 0) *vote = 0u;
+    lds_barrier();
+    const bool exact = F::build_table(tab, (int)threadIdx.x, W * 64);
+    if (__builtin_amdgcn_ballot_w64(!exact) != 0 && lane == 0) *vote = 1u;
+    lds_barrier();
+    const bool grid_bad = __builtin_amdgcn_readfirstlane(*vote) != 0u;
 
     float *red = (float *)(smem + C::kRed);
     int slot_c = 0;
@@ -439,6 +457,7 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
         if (wave == 0) {
             float tsum = red[lane];
             for (int w = 1; w < W; ++w) tsum += red[w * 64 + lane];
+            if (grid_bad) tsum = __builtin_nanf("");
             const float total[1] = {tsum};
             tile_epilogue<1>(c.a, c.tile, c.split, total);
         }

@@ -435,7 +435,13 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
     for (int i = 0; i < R - 1; ++i) issue_next();
 
     // Grid staged (this wavefront's part: its stage copies, two per stage, may
-    // stay in flight), then the sign-folded table from it.
+    // stay in flight), then the sign-folded table from it. A grid value that
+    // fp16 cannot hold would be rounded in the table: the workgroup then
+    // stores NaN in every row instead (host code that creates a group rejects
+    // such a grid up front). The vote goes through a word of the row-sum
+    // buffer, idle until the first item ends.
+    volatile uint32_t *vote = (volatile uint32_t *)(smem + C::kRed);
+    if (threadIdx.x == 0) *vote = 0u;
     if (wave < 4) wait_vmcnt_upto(2 * __builtin_popcount(flags));
     lds_barrier();
     {
@@ -443,7 +449,12 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
         const int i = t & 255;
         const float4 gv = *(const float4 *)(smem + C::kGrid + 16 * i);
         for (int s = t >> 8; s < 16; s += W / 4) iq3_table_entry(s, i, gv);
+        const bool exact =
+            fp16_exact(gv.x) && fp16_exact(gv.y) && fp16_exact(gv.z) && fp16_exact(gv.w);
+        if (__builtin_amdgcn_ballot_w64(!exact) != 0 && lane == 0) *vote = 1u;
     }
+    lds_barrier();
+    const bool grid_bad = __builtin_amdgcn_readfirstlane(*vote) != 0u;
 
     float *red = (float *)(smem + C::kRed);
     int slot_c = 0;
@@ -495,6 +506,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
         if (wave == 0) {
             float tsum = red[lane];
             for (int w = 1; w < W; ++w) tsum += red[w * 64 + lane];
+            if (grid_bad) tsum = __builtin_nanf("");
             const float total[1] = {tsum};
             tile_epilogue<1>(c.a, c.tile, c.split, total);
         }

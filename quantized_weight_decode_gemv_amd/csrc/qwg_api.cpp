@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <array>
 #include <cstdlib>
+#include <cstring>
 #include <new>
 #include <vector>
 #include <map>
@@ -290,6 +291,9 @@ const char *qwg_strerror(int status) {
         case QWG_ERR_BATCH: return "batch must be in 1..8";
         case QWG_ERR_HIP: return "HIP runtime error";
         case QWG_ERR_FORMAT: return "unknown format id";
+        case QWG_ERR_GRID:
+            return "a codebook value is not exactly representable in fp16 (the GEMV keeps the "
+                   "codebook in fp16)";
         case QWG_ERR_TIMEOUT:
             return "a wait of the layer-chain launch gave up (its flags have been reset)";
         case QWG_ERR_CAPTURE:
@@ -874,6 +878,35 @@ void stream_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> 
         }
 }
 
+// True if v converts to binary16 and back unchanged: zero; a normal fp16
+// magnitude (2^-14 .. 65504) whose significand fits 11 bits; or a subnormal
+// fp16 value (a multiple of 2^-24 below 2^-14). Infinities and NaN are
+// rejected.
+bool fp16_exact_host(float v) {
+    if (v == 0.0f) return true;
+    float a = v < 0.0f ? -v : v;
+    if (!(a <= 65504.0f)) return false;
+    if (a < 6.103515625e-05f) {
+        const float m = a * 16777216.0f;   // exact (power-of-two scale)
+        return m == (float)(int64_t)m;
+    }
+    uint32_t bits;
+    memcpy(&bits, &a, sizeof bits);
+    return (bits & 0x1FFFu) == 0;
+}
+
+// The codebook of an IQ3 / IQ3_S / IQ4_XS group, copied to the host and
+// checked: the GEMV engines hold it in fp16.
+int check_codebook(int fmt, const float *grid) {
+    const size_t n = fmt == QWG_FMT_IQ3_S ? 512 * 4 : fmt == QWG_FMT_IQ4_XS ? 16 : 256 * 4;
+    std::vector<float> h(n);
+    if (hipMemcpy(h.data(), grid, n * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess)
+        return QWG_ERR_HIP;
+    for (float v : h)
+        if (!fp16_exact_host(v)) return QWG_ERR_GRID;
+    return QWG_OK;
+}
+
 int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, const float *grid,
                  qwg_group **out, int batch = 1) {
     const bool cb = codebook_format(fmt);
@@ -895,6 +928,10 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
         if (probs[i].nb > max_nb) max_nb = probs[i].nb;
     }
     if (total > (int64_t)1 << 30) return QWG_ERR_SHAPE;
+    if (iq3) {
+        const int rc = check_codebook(fmt, grid);
+        if (rc) return rc;
+    }
     // Batched members run on the matrix-core engine, one workgroup per tile
     // (a stream has thousands of tiles, so none of them splits).
     const bool batched = batch >= 2;

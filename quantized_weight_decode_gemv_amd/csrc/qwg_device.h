@@ -18,6 +18,10 @@ __device__ __forceinline__ float h2f_hi(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
+// True if v converts to fp16 and back unchanged (the GEMV engines keep their
+// codebook tables in fp16; a value that fp16 cannot hold would be rounded).
+__device__ __forceinline__ bool fp16_exact(float v) { return (float)(_Float16)v == v; }
+
 // Wave-uniform read-only activations are read through the constant address
 // space, so the compiler fetches them with scalar loads into SGPRs (one operand
 // of every VALU FMA) instead of per-lane vector loads.

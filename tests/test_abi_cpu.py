@@ -60,7 +60,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_version_and_strerror(L):
     assert L.qwg_version() >= 100
-    for st in range(0, 10):
+    for st in range(0, 11):
         assert len(L.qwg_strerror(st)) > 0
 
 

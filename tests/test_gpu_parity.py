@@ -104,6 +104,36 @@ def test_dequant_q4k_matches_oracle(n_out, n_in):
     assert_bits(got, oracle.dequant_q4k(w, n_out * n_in), f"{n_out}x{n_in}")
 
 
+# Past one grid's worth of blocks: the dequant launchers cap the grid at 65,536
+# four-wavefront workgroups (262,144 blocks), and wavefronts walk further
+# blocks in a grid-stride loop. The C3 LM head (256,000 blocks) is just below
+# the cap; 266,241 blocks take a second, partial trip; 786,433 a third.
+@pytest.mark.parametrize("nblocks", [256000, 262144 + 4097, 3 * 262144 + 1])
+def test_dequant_q4k_grid_stride(nblocks):
+    w = synth.q4k_weights(nblocks, 256, 93, nblocks % 1000)
+    got = qwg.dequant_q4k(dev(w))
+    ref = oracle.dequant_q4k(w, nblocks * 256)
+    bad = int((host(got).view(np.uint32) != ref.view(np.uint32)).sum())
+    assert bad == 0, f"{bad} mismatching weights"
+
+
+@pytest.mark.parametrize("fmt", ["iq3", "iq3_xxs", "iq3s", "iq4xs"])
+def test_dequant_codebooks_grid_stride(fmt):
+    nblocks = 262144 + 4097
+    if fmt == "iq3":
+        w, tab = synth.iq3_weights(nblocks, 256, 94, 0), synth.iq3_grid()
+        got, ref = qwg.dequant_iq3(dev(w), dev(tab)), oracle.dequant_iq3(w, tab, nblocks * 256)
+    elif fmt == "iq3_xxs":
+        w, tab = synth.iq3_xxs_weights(nblocks, 256, 94, 1), synth.iq3_xxs_grid()
+        got, ref = qwg.dequant_iq3_xxs(dev(w), dev(tab)), oracle.dequant_iq3_xxs(w, tab, nblocks * 256)
+    else:
+        c = CB[fmt]
+        w, tab = c["weights"](nblocks, 256, 94, 2), c["table"]()
+        got, ref = c["dequant"](dev(w), dev(tab)), c["o_dequant"](w, tab, nblocks * 256)
+    bad = int((host(got).reshape(-1).view(np.uint32) != ref.reshape(-1).view(np.uint32)).sum())
+    assert bad == 0, f"{fmt}: {bad} mismatching weights"
+
+
 def test_dequant_q4k_special_scales():
     # subnormal, negative, zero and large fp16 d / dmin
     rng = np.random.default_rng(11)
@@ -1474,6 +1504,44 @@ def test_codebook_group_stream_all_rows(fmt):
         g.run()
     assert_stream(probs, refs, Y, f"{fmt} stream")
     g.close()
+
+
+# ---------------------------------------------------------------- codebooks fp16 cannot hold
+
+@pytest.mark.parametrize("fmt", ["iq3", "iq3s", "iq4xs"])
+def test_codebook_not_fp16_exact_is_reported(fmt):
+    # The GEMV engines keep the codebook in fp16. A value fp16 cannot hold
+    # (2 + 2^-20) makes every output row of a single call NaN, and group
+    # creation return QWG_ERR_GRID; the same call with the value rounded to
+    # fp16 (2.0) is within the bound.
+    n_out, n_in = 130, 768
+    x = synth.activations(n_in, 220, 0)
+    if fmt == "iq3":
+        tab = synth.iq3_grid().copy()
+        w = synth.iq3_weights(n_out, n_in, 220, 1)
+        call = lambda t: qwg.gemv_iq3(dev(w), dev(x), dev(t))   # noqa: E731
+        group = lambda t: qwg.Iq3Group([(dev(w), dev(x), torch.empty(n_out, device=DEV))], dev(t))   # noqa: E731
+        ref = lambda t: oracle.gemv_iq3(w, t, x, n_in, n_out)   # noqa: E731
+    else:
+        c = CB[fmt]
+        tab = c["table"]().copy()
+        w = c["weights"](n_out, n_in, 220, 2)
+        wt = c["pack"](dev(w), n_in)
+        call = lambda t: c["gemv"](wt, dev(x), dev(t), n_out)   # noqa: E731
+        group = lambda t: c["group"]([(wt, dev(x), torch.empty(n_out, device=DEV))], dev(t))   # noqa: E731
+        ref = lambda t: c["o_gemv"](w, t, x, n_in, n_out)   # noqa: E731
+    bad = tab.copy()
+    bad.reshape(-1)[5] = np.float32(2.0 + 2.0 ** -20)
+    assert float(np.float16(bad.reshape(-1)[5])) != float(bad.reshape(-1)[5])
+    y = host(call(bad))
+    assert np.isnan(y).all(), f"{fmt}: {int((~np.isnan(y)).sum())} rows not NaN"
+    with pytest.raises(qwg.QwgError) as e:
+        group(bad)
+    assert e.value.status == 9
+    good = bad.copy()
+    good.reshape(-1)[5] = np.float32(2.0)
+    yr, sr = ref(good)
+    assert_bound(host(call(good)), yr, sr, f"{fmt} exact codebook")
 
 
 # ---------------------------------------------------------------- IQ3 encoder
