@@ -66,10 +66,17 @@ __device__ __forceinline__ void stf_agent(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Position of workgroup b's flag: the flags of the workgroups on one XCD
-// (workgroup b runs on XCD b % 8) share cache lines. Measured against
-// workgroup order: 2.0 against 3.3 us per handoff.
+// Flags: one copy of all nwg flags per reader XCD (workgroup b runs on XCD
+// b % 8), copies kFlagCopyWords apart; a workgroup stores its flag into every
+// copy and polls the copy of its own XCD, so each copy's lines are read by
+// the 32 workgroups of one XCD only. Within a copy the flags of the
+// workgroups on one XCD share cache lines. Measured in a probe (flags only,
+// idle chip): workgroup order 3.3 us per handoff, grouped by XCD 2.0 us,
+// grouped and copied per reader XCD 1.86 us.
 __device__ __forceinline__ int flag_pos(int b, int nwg) { return (b & 7) * (nwg >> 3) + (b >> 3); }
+__device__ __forceinline__ uint32_t *flag_copy(const ChainArgs &c, int xcd) {
+    return c.flags + xcd * kFlagCopyWords;
+}
 
 // True once every one of the nwg (<= 256) flags has reached `target`: one
 // 16-byte agent-coherent load per lane.
@@ -96,8 +103,9 @@ __device__ __forceinline__ bool flags_reached(const uint32_t *flags, int nwg, ui
 // us); the error word is read every 16th poll only (each read is another
 // round trip).
 __device__ bool wait_flags(const ChainArgs &c, uint32_t target, uint64_t t0) {
+    const uint32_t *mine = flag_copy(c, blockIdx.x & 7);
     for (int i = 0;; ++i) {
-        if (flags_reached(c.flags, c.nwg, target)) return true;
+        if (flags_reached(mine, c.nwg, target)) return true;
         if ((i & 15) == 15) {
             if (ld_agent(c.err) != 0u) return false;
             if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
@@ -208,24 +216,26 @@ __device__ void chain_body(const ChainArgs &c, uint8_t *smem) {
     // Every workgroup's flag holds the same count at the start (every earlier
     // run completed all its phases).
     uint32_t base = 0;
-    if (wave == 0) base = ld_agent(&c.flags[flag_pos(wg, c.nwg)]);
+    if (wave == 0) base = ld_agent(&flag_copy(c, wg & 7)[flag_pos(wg, c.nwg)]);
 
-    // Copies of a unit's columns into ring slots slot0, slot0 + 1, ...: this
-    // wavefront moves rows 16G..16G+15 of each column (16-byte chunks
-    // k = 64i + lane; the third instruction: lanes 0..15). Returns the number
-    // of copy instructions issued.
-    const uint32_t coff = 2304 * G + 16 * lane;
+    // Copies of a unit's columns into ring slots slot0, slot0 + 1, ...: the
+    // quad's wavefronts 1..3 move bytes 3072(G-1) .. 3072G - 1 of each
+    // 9216-byte column (three instructions of 64 lanes x 16 bytes). Wavefront
+    // 0, which stores the quad's sums at the end of a phase, copies no
+    // weights, so that its wait for those stores does not also wait for the
+    // next phase's columns. Returns the number of copy instructions issued.
+    const uint32_t coff = 3072 * (G > 0 ? G - 1 : 0) + 16 * lane;
     auto issue_unit = [&](const Unit &u, int slot0) {
-        if (u.member < 0) return 0;
+        if (G == 0 || u.member < 0) return 0;
         const cmember_p mp = (cmember_p)c.members + u.member;
         const uint8_t *colp = mp->w + ((int64_t)u.tile * mp->nb + u.b0) * kColBytes + coff;
         for (int s = 0; s < u.nblk; ++s) {
-            const uint32_t dst =
-                lds0 + ((slot0 + s) & (kChainRing - 1)) * kSlotBytes + quad * kColBytes + 2304 * G;
+            const uint32_t dst = lds0 + ((slot0 + s) & (kChainRing - 1)) * kSlotBytes +
+                                 quad * kColBytes + 3072 * (G - 1);
             const uint8_t *src = colp + (int64_t)s * kColBytes;
             dma16_stream(src, dst);
             dma16_stream(src + 1024, dst + 1024);
-            if (lane < 16) dma16_stream(src + 2048, dst + 2048);
+            dma16_stream(src + 2048, dst + 2048);
         }
         return 3 * u.nblk;
     };
@@ -293,12 +303,14 @@ __device__ void chain_body(const ChainArgs &c, uint8_t *smem) {
         // The unit after next: its descriptor loads overlap the wait below.
         const int Lp = (int)((cu32_p)c.phases)[2 * p];
         Unit unn = load_unit(c, p + 2, col);
-        // Every store of this phase has completed (and the next phase's
-        // columns have landed) before the workgroup counts the phase as done.
-        wait_vmcnt<0>();
+        // Every store of this phase has completed before the workgroup counts
+        // the phase as done (the stores are wavefront 0's of each quad; the
+        // next phase's columns may still be in flight).
+        if (G == 0) wait_vmcnt<0>();
         lds_barrier();
         if (wave == 0) {
-            if (lane == 0) st_agent(&c.flags[flag_pos(wg, c.nwg)], base + (uint32_t)p + 1u);
+            if (lane < kFlagCopies)
+                st_agent(&flag_copy(c, lane)[flag_pos(wg, c.nwg)], base + (uint32_t)p + 1u);
             const bool wait_next = p + 1 < c.nphases && ((cu32_p)c.phases)[2 * (p + 1) + 1] != 0u;
             const bool last = p + 1 == c.nphases && c.nfin > 0;
             if ((wait_next || last) && !wait_flags(c, base + (uint32_t)p + 1u, t0)) *abort_word = 1u;

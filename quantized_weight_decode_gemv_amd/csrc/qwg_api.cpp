@@ -1305,7 +1305,7 @@ int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase
     const size_t off_partial = align256(off_fin + sizeof(uint32_t) * fin.size());
     const size_t off_counters = align256(off_partial + sizeof(float) * partial_floats);
     const size_t off_flags = align256(off_counters + sizeof(uint32_t) * counters);
-    const size_t off_err = align256(off_flags + sizeof(uint32_t) * 256);
+    const size_t off_err = align256(off_flags + sizeof(uint32_t) * kFlagCopies * kFlagCopyWords);
     const size_t all = off_err + 256;
     qwg_chain *ch = new (std::nothrow) qwg_chain();
     if (!ch) return QWG_ERR_HIP;

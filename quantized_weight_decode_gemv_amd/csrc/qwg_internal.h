@@ -138,6 +138,8 @@ hipError_t launch_cb_stream(int fmt, const GroupArgs &g, const GemvArgs &single,
 constexpr int kChainQuads = 4;
 constexpr int kChainRing = 4;      // LDS ring slots (columns per quad)
 constexpr int kChainMaxSteps = 2;  // columns per unit
+constexpr int kFlagCopies = 8;     // one copy of the flags per XCD
+constexpr int kFlagCopyWords = 1024;   // 4 KB apart
 // How a member's rows are completed: a unit covers whole rows (direct); units
 // store partial sums that the launch adds up at its end (deferred); or, for a
 // member whose y a later phase reads, the tile's last unit adds them up at
@@ -164,7 +166,8 @@ struct ChainMember {
 // tile, b0 | nblk << 8 | split << 16, 0); phases: [nphases] pairs (columns of
 // the phase, 1 if it waits for the previous phase); fin: [nfin] pairs (member,
 // tile) of the deferred members' tiles; flags: one per workgroup (phases
-// completed, counted across runs); err: set when a wait gave up.
+// completed, counted across runs), kFlagCopies copies kFlagCopyWords apart;
+// err: set when a wait gave up.
 struct ChainArgs {
     const ChainMember *members;
     const uint32_t *units;
