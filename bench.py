@@ -802,40 +802,51 @@ def bench_codebooks(args):
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     fmts = {"iq3s": (synth.iq3s_weights, synth.iq3s_grid, 110, qwg.pack_iq3s_tiles,
-                     qwg.gemv_iq3s_tiled, qwg.Iq3sGroup),
+                     qwg.gemv_iq3s_tiled, qwg.gemv_iq3s, qwg.Iq3sGroup),
             "iq4xs": (synth.iq4xs_weights, synth.iq4nl_table, 136, qwg.pack_iq4xs_tiles,
-                      qwg.gemv_iq4xs_tiled, qwg.Iq4xsGroup)}
+                      qwg.gemv_iq4xs_tiled, qwg.gemv_iq4xs, qwg.Iq4xsGroup)}
     out = {}
-    for name, (weights, table, nbytes, pack, gemv, Group) in fmts.items():
+    for name, (weights, table, nbytes, pack, gemv, gemv_rows, Group) in fmts.items():
         tab = torch.from_numpy(table()).to(dev)
         probs = synth.config(6)
         X = [torch.from_numpy(synth.inputs(p)).to(dev) for p in probs]
         Y = [torch.empty(p.n_out, device=dev) for p in probs]
-        W = [pack(torch.from_numpy(weights(p.n_out, p.n_in, p.cfg, p.tensor)).to(dev), p.n_in)
-             for p in probs]
-        group = Group(zip(W, X, Y), tab)
         step = sum(p.n_out * (p.n_in // 256) * nbytes + 4 * (p.n_in + p.n_out) for p in probs)
-        us = _event_us(lambda: group.run(stream), stream, args.steps, args.warmup)
-        group.close()
-        del W
+        res = {}
+        for layout in ("tiled", "rows"):
+            W = [torch.from_numpy(weights(p.n_out, p.n_in, p.cfg, p.tensor)).to(dev) for p in probs]
+            if layout == "tiled":
+                W = [pack(w, p.n_in) for w, p in zip(W, probs)]
+            group = Group(zip(W, X, Y), tab, tiled=layout == "tiled")
+            us = _event_us(lambda: group.run(stream), stream, args.steps, args.warmup)
+            group.close()
+            del W
+            res[layout] = us
         singles = {}
         copies = 64
         for p in synth.config(4):
-            wt = pack(torch.from_numpy(weights(p.n_out, p.n_in, p.cfg, p.tensor)).to(dev), p.n_in)
-            WT = torch.stack([wt] * copies)
+            w = torch.from_numpy(weights(p.n_out, p.n_in, p.cfg, p.tensor)).to(dev)
             x = torch.from_numpy(synth.inputs(p)).to(dev)
             y = torch.empty(p.n_out, device=dev)
-            i = [0]
-
-            def run():
-                gemv(WT[i[0] % copies], x, tab, p.n_out, out=y)
-                i[0] += 1
-            u = _event_us(run, stream, args.steps, args.warmup)
             b = p.n_out * (p.n_in // 256) * nbytes + 4 * (p.n_in + p.n_out)
-            singles[p.name] = {"us": round(u, 2), "GBs": round(b / u / 1e3, 1)}
-            del WT
+            for layout in ("tiled", "rows"):
+                WT = torch.stack([pack(w, p.n_in) if layout == "tiled" else w] * copies)
+                i = [0]
+
+                def run():
+                    if layout == "tiled":
+                        gemv(WT[i[0] % copies], x, tab, p.n_out, out=y)
+                    else:
+                        gemv_rows(WT[i[0] % copies], x, tab, out=y)
+                    i[0] += 1
+                u = _event_us(run, stream, args.steps, args.warmup)
+                singles[f"{p.name} {layout}"] = {"us": round(u, 2), "GBs": round(b / u / 1e3, 1)}
+                del WT
+        us = res["tiled"]
         out[name] = {"stream_us": round(us, 2), "stream_GBs": round(step / us / 1e3, 1),
                      "frac": round(step / us / 1e3 / HBM_PEAK_GBS, 4),
+                     "stream_rows_us": round(res["rows"], 2),
+                     "stream_rows_GBs": round(step / res["rows"] / 1e3, 1),
                      "algorithmic_bytes_per_step": step, "singles": singles}
     best = max(out.values(), key=lambda v: v["stream_GBs"])
     print(json.dumps({
@@ -843,8 +854,9 @@ def bench_codebooks(args):
         "value": best["stream_GBs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "higher_is_better": True, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "TinyLlama-1.1B-shaped per-token stream (155 GEMVs) in the IQ3_S and "
-                               "IQ4_XS formats, tile layout, one grouped launch each; single GEMVs "
-                               "of the IQ3 configuration's shapes, cold weights", **out},
+                               "IQ4_XS formats, one grouped launch each on the tile layout (value) "
+                               "and on row-major blocks (stream_rows_*); single GEMVs of the IQ3 "
+                               "configuration's shapes on both layouts, cold weights", **out},
     }), flush=True)
 
 

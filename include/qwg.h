@@ -220,7 +220,14 @@ int qwg_encode_iq3(void *dst, const float *x, const float *grid, int64_t n_rows,
  * [16] fp32 (16-byte aligned), dst as above.
  * Both bit-identical to (sign * entry) * eff rounded to fp32, eff exact.
  *
- * The GEMVs of these formats run on a tile layout made once at load time:
+ * qwg_gemv_iq3s / qwg_gemv_iq4xs: y = W x on row-major blocks as a file stores
+ * them (n_out rows of n_in/256 blocks, rows back to back; w 16-byte aligned,
+ * the row length need not be a multiple of 16 bytes), x 16-byte aligned, y
+ * 4-byte aligned, the grid/table 16-byte aligned. Each 64-row tile's blocks
+ * are copied to LDS 16-byte granule by granule and read at their offsets; no
+ * byte outside w's n_out*row_bytes is read.
+ *
+ * The same GEMVs also run on a tile layout made once at load time:
  * qwg_pack_iq3s_tiles / qwg_pack_iq4xs_tiles take row-major blocks (src
  * 2-byte aligned, n_out rows of n_in/256 blocks) and write
  * qwg_tiled_bytes(fmt, n_in, n_out) bytes (dst 16-byte aligned): for each
@@ -230,8 +237,8 @@ int qwg_encode_iq3(void *dst, const float *x, const float *grid, int64_t n_rows,
  * [G][row][32], bytes 0-7 [row][8]; G = 0..3 is the pair of sub-blocks 2G,
  * 2G+1); rows past n_out are zero blocks. Every byte of every block is kept.
  * qwg_gemv_iq3s_tiled / qwg_gemv_iq4xs_tiled: y = W x on that layout (w
- * 16-byte aligned; x 16-byte aligned, y 4-byte aligned, the grid/table
- * 16-byte aligned). Every grid or table value must be exactly representable
+ * 16-byte aligned; x, y, grid/table as above).
+ * For all four GEMVs every grid or table value must be exactly representable
  * in fp16 (true for the integer values of these codebooks); otherwise every
  * output row of the call is NaN (group creation returns QWG_ERR_GRID).
  * Shape limits and accuracy as qwg_gemv_q4k.
@@ -240,6 +247,10 @@ int qwg_dequant_iq3s(const void *src, const float *grid, float *dst, int64_t n, 
 int qwg_dequant_iq4xs(const void *src, const float *table, float *dst, int64_t n, void *stream);
 int qwg_pack_iq3s_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
 int qwg_pack_iq4xs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream);
+int qwg_gemv_iq3s(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                  int64_t n_out, void *stream);
+int qwg_gemv_iq4xs(float *y, const float *x, const void *w, const float *table, int64_t n_in,
+                   int64_t n_out, void *stream);
 int qwg_gemv_iq3s_tiled(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                         int64_t n_out, void *stream);
 int qwg_gemv_iq4xs_tiled(float *y, const float *x, const void *w, const float *table,
@@ -413,8 +424,14 @@ int qwg_group_create_q4k_batched_tiled(const qwg_gemv_desc *descs, int count, in
                                        qwg_group **group);
 int qwg_group_create_iq3_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
                                qwg_group **group);
-/* Tiled groups of IQ3_S (grid [512][4]) or IQ4_XS (table [16]) members, rules
- * as for the tiled IQ3 group; the grid/table is shared by all members. */
+/* Groups of IQ3_S (grid [512][4]) or IQ4_XS (table [16]) members, on
+ * row-major blocks (every member's w 16-byte aligned, as for qwg_gemv_iq3s) or
+ * in the tile layout (_tiled), rules as for the IQ3 groups; the grid/table is
+ * shared by all members. */
+int qwg_group_create_iq3s(const qwg_gemv_desc *descs, int count, const float *grid,
+                          qwg_group **group);
+int qwg_group_create_iq4xs(const qwg_gemv_desc *descs, int count, const float *table,
+                           qwg_group **group);
 int qwg_group_create_iq3s_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
                                 qwg_group **group);
 int qwg_group_create_iq4xs_tiled(const qwg_gemv_desc *descs, int count, const float *table,

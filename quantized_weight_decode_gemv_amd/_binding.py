@@ -59,7 +59,9 @@ def lib() -> ctypes.CDLL:
         for name in ("iq3s", "iq4xs"):
             getattr(L, f"qwg_dequant_{name}").argtypes = [P, P, P, I64, P]
             getattr(L, f"qwg_pack_{name}_tiles").argtypes = [P, P, I64, I64, P]
+            getattr(L, f"qwg_gemv_{name}").argtypes = [P, P, P, P, I64, I64, P]
             getattr(L, f"qwg_gemv_{name}_tiled").argtypes = [P, P, P, P, I64, I64, P]
+            getattr(L, f"qwg_group_create_{name}").argtypes = [P, I, P, ctypes.POINTER(P)]
             getattr(L, f"qwg_group_create_{name}_tiled").argtypes = [P, I, P, ctypes.POINTER(P)]
         L.qwg_gemv_q4k.argtypes = [P, P, P, I64, I64, P]
         L.qwg_gemv_iq3.argtypes = [P, P, P, P, I64, I64, P]
@@ -390,6 +392,23 @@ def _cb_pack(fmt, w, n_in, out):
     return out
 
 
+def _cb_gemv(fmt, w, x, tab, out):
+    name, _, nbytes, _ = _CB[fmt]
+    _dev(x, "x", torch.float32)
+    _cb_table(fmt, tab)
+    n_in = x.numel()
+    n_out = _weights(w, n_in, nbytes)
+    if out is None:
+        out = torch.empty(n_out, dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.numel() != n_out:
+        raise ValueError("out has the wrong size")
+    _check(getattr(lib(), f"qwg_gemv_{name}")(out.data_ptr(), x.data_ptr(), w.data_ptr(),
+                                               tab.data_ptr(), n_in, n_out, _stream(x)),
+           f"qwg_gemv_{name}")
+    return out
+
+
 def _cb_gemv_tiled(fmt, w, x, tab, n_out, out):
     name = _CB[fmt][0]
     _dev(w, "w", torch.uint8)
@@ -427,6 +446,20 @@ def pack_iq3s_tiles(w: torch.Tensor, n_in: int, out: torch.Tensor | None = None)
 def pack_iq4xs_tiles(w: torch.Tensor, n_in: int, out: torch.Tensor | None = None) -> torch.Tensor:
     """Row-major IQ4_XS weights -> the IQ4_XS tile layout that gemv_iq4xs_tiled takes."""
     return _cb_pack(QWG_FMT_IQ4_XS, w, n_in, out)
+
+
+def gemv_iq3s(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x for row-major IQ3_S weights; w uint8 [n_out, row_bytes] (or flat,
+    16-byte aligned), x fp32 [n_in], grid fp32 [512, 4]."""
+    return _cb_gemv(QWG_FMT_IQ3_S, w, x, grid, out)
+
+
+def gemv_iq4xs(w: torch.Tensor, x: torch.Tensor, table: torch.Tensor,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W x for row-major IQ4_XS weights; w uint8 [n_out, row_bytes] (or flat,
+    16-byte aligned), x fp32 [n_in], table fp32 [16]."""
+    return _cb_gemv(QWG_FMT_IQ4_XS, w, x, table, out)
 
 
 def gemv_iq3s_tiled(w: torch.Tensor, x: torch.Tensor, grid: torch.Tensor, n_out: int,
@@ -529,8 +562,8 @@ class Group:
 
     members: sequence of (w, x, y) device tensors (uint8 weights, fp32 x [n_in],
     fp32 y [n_out]); fmt QWG_FMT_Q4K, QWG_FMT_IQ3 (then `grid`, fp32 [256, 4], is
-    shared by every member), or, tiled only, QWG_FMT_IQ3_S (grid [512, 4]) or
-    QWG_FMT_IQ4_XS (`grid` is the 16-value table). The tensors are referenced by the plan (kept
+    shared by every member), QWG_FMT_IQ3_S (grid [512, 4]) or QWG_FMT_IQ4_XS
+    (`grid` is the 16-value table). The tensors are referenced by the plan (kept
     alive here) and must stay in place; run() recomputes every y_i from the
     current x_i.
     """
@@ -543,8 +576,6 @@ class Group:
         if fmt not in (QWG_FMT_Q4K, QWG_FMT_IQ3, QWG_FMT_IQ3_S, QWG_FMT_IQ4_XS):
             raise ValueError(f"unknown format {fmt}")
         if fmt in _CB:
-            if not tiled:
-                raise ValueError("IQ3_S and IQ4_XS groups take tile-layout weights")
             if grid is None:
                 raise ValueError("the group needs its grid or table")
             _cb_table(fmt, grid)
@@ -552,7 +583,7 @@ class Group:
             if grid is None:
                 raise ValueError("an IQ3 group needs the grid")
             _grid(grid)
-        block_bytes = Q4K_BYTES if fmt == QWG_FMT_Q4K else IQ3_BYTES
+        block_bytes = {QWG_FMT_Q4K: Q4K_BYTES, QWG_FMT_IQ3: IQ3_BYTES}.get(fmt) or _CB[fmt][2]
         descs = (GemvDesc * len(members))()
         for i, (w, x, y) in enumerate(members):
             _dev(x, "x", torch.float32)
@@ -573,7 +604,7 @@ class Group:
         self._device = members[0][1].device
         handle = ctypes.c_void_p()
         if fmt in _CB:
-            fn = f"qwg_group_create_{_CB[fmt][0]}_tiled"
+            fn = f"qwg_group_create_{_CB[fmt][0]}" + ("_tiled" if tiled else "")
             _check(getattr(lib(), fn)(descs, len(members), grid.data_ptr(), ctypes.byref(handle)), fn)
         elif fmt == QWG_FMT_Q4K and tiled:
             _check(lib().qwg_group_create_q4k_tiled(descs, len(members), ctypes.byref(handle)),
@@ -675,17 +706,19 @@ class Iq3Group(Group):
 
 
 class Iq3sGroup(Group):
-    """Group of IQ3_S GEMVs on tile-layout weights sharing one [512, 4] grid."""
+    """Group of IQ3_S GEMVs sharing one [512, 4] grid (tiled: weights in the
+    IQ3_S tile layout; otherwise row-major, each w 16-byte aligned)."""
 
-    def __init__(self, members, grid: torch.Tensor):
-        super().__init__(members, QWG_FMT_IQ3_S, grid, tiled=True)
+    def __init__(self, members, grid: torch.Tensor, tiled: bool = True):
+        super().__init__(members, QWG_FMT_IQ3_S, grid, tiled=tiled)
 
 
 class Iq4xsGroup(Group):
-    """Group of IQ4_XS GEMVs on tile-layout weights sharing one 16-value table."""
+    """Group of IQ4_XS GEMVs sharing one 16-value table (tiled: weights in the
+    IQ4_XS tile layout; otherwise row-major, each w 16-byte aligned)."""
 
-    def __init__(self, members, table: torch.Tensor):
-        super().__init__(members, QWG_FMT_IQ4_XS, table, tiled=True)
+    def __init__(self, members, table: torch.Tensor, tiled: bool = True):
+        super().__init__(members, QWG_FMT_IQ4_XS, table, tiled=tiled)
 
 
 class Q4kChain:

@@ -8,9 +8,10 @@
 //          bits 2ib of the uint16 at 2-3, low four as nibbles at 4-7), 4-bit
 //          codes at 8-135 (byte 8+16ib+j: weight j in the low nibble, weight
 //          j+16 in the high one); eff = d*(s-32), weight = table[q] * eff.
-// Dequantization is bit-exact. The GEMV runs on a tile layout (each 64-row
-// block column regrouped by field, as for IQ3) with a stream engine of
-// 4-wavefront workgroups whose decode table (fp16) lives in LDS.
+// Dequantization is bit-exact. The GEMV runs on row-major blocks as a file
+// stores them, or on a tile layout (each 64-row block column regrouped by
+// field, as for IQ3), with a stream engine of 4-wavefront workgroups whose
+// decode table (fp16) lives in LDS.
 #include <cstdlib>
 
 #include "qwg_device.h"
@@ -93,8 +94,13 @@ struct Iq3sFmt {
     // 4-wavefront workgroups, five per CU beside the 16 KB table. Measured on
     // the IQ3_S stream (us): 4 x 2 119.1, 4 x 3 125.7, 8 x 2 124.9, 16 x 2 162
     // (the 64 KB four-sign table, one 16-wavefront workgroup per CU: 127.0);
-    // an SGPR cap changes nothing at this occupancy.
+    // an SGPR cap changes nothing at this occupancy. Launches too short to
+    // fill the chip without splitting their sums run 8 x 2 (two super-blocks
+    // per stage): single GEMVs 5632 x 2048 / 2048 x 5632, tile layout, 11.4 /
+    // 14.8 us with 4 x 2, 9.7 / 10.3 us with 8 x 2 (row-major 12.9 / 15.9 ->
+    // 10.3 / 11.6 us).
     static constexpr int kShape = 42;         // 10 * wavefronts + ring stages
+    static constexpr int kShapeSplit = 82;    // launches that split their sums
     static constexpr int kTable = 16384;      // decode table bytes at LDS address 0
     static constexpr bool kCapSgprs = false;  // stream kernel without an SGPR cap
     static constexpr int kBytes = kIq3sBytes;
@@ -145,19 +151,84 @@ struct Iq3sFmt {
         return exact;
     }
 
+    // The bytes of one block that wavefront G uses: index bytes 2+16G..17+16G,
+    // sign bytes 74+8G..81+8G, ninth-bit bytes 66+2G and 67+2G (low half),
+    // sub-scale bytes 106..109 and d (low half).
+    struct Raw {
+        uint32_t q[4], sg[2], hb, sc, d16;
+    };
+    // Row windows (row-major weights): granules 0..7 of a 144-byte window hold
+    // the block (it starts at an even window byte sh <= 14 and ends by 124).
+    static constexpr int kWinGran = 8;
+
+    // From a tile-layout column (this lane's row).
+    template <int G>
+    __device__ static void fetch_tiled(const uint8_t *col, int lane, Raw &r) {
+        const uint4 q = *(const uint4 *)(col + kIdx + G * 1024 + 16 * lane);
+        const uint2 sg = *(const uint2 *)(col + kSign + G * 512 + 8 * lane);
+        r.q[0] = q.x;
+        r.q[1] = q.y;
+        r.q[2] = q.z;
+        r.q[3] = q.w;
+        r.sg[0] = sg.x;
+        r.sg[1] = sg.y;
+        r.hb = ld_u16(col + kHb + G * 128 + 2 * lane);
+        r.sc = *(const uint32_t *)(col + kScale + 4 * lane);
+        r.d16 = ld_u16(col + kD + 2 * lane);
+    }
+
+    // From a row window in LDS (16-byte aligned; the block starts at byte sh,
+    // even). Every field starts 0 or 2 bytes into a dword: whole dwords are
+    // read and realigned with v_alignbyte (the dword past a field is read only
+    // to supply bytes that the shift drops when the offset is 0).
+    template <int G>
+    __device__ static void fetch_window(const uint8_t *win, uint32_t sh, Raw &r) {
+        const uint32_t *p = (const uint32_t *)win;
+        const uint32_t o = sh + 2u;                 // indices at block byte 2 + 16G
+        const uint32_t sft = o & 3u;                // = (sh + 74) & 3 = (sh + 106) & 3
+        const uint32_t qd = (o >> 2) + 4 * G;
+        uint32_t a[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) a[i] = p[qd + i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.q[i] = __builtin_amdgcn_alignbyte(a[i + 1], a[i], sft);
+        const uint32_t sd = ((sh + 74u) >> 2) + 2 * G;
+        const uint32_t v0 = p[sd], v1 = p[sd + 1], v2 = p[sd + 2];
+        r.sg[0] = __builtin_amdgcn_alignbyte(v1, v0, sft);
+        r.sg[1] = __builtin_amdgcn_alignbyte(v2, v1, sft);
+        const uint32_t oh = sh + 66u + 2 * G;
+        r.hb = (p[oh >> 2] >> ((oh & 2u) << 3)) & 0xFFFFu;
+        const uint32_t cd = (sh + 106u) >> 2;
+        r.sc = __builtin_amdgcn_alignbyte(p[cd + 1], p[cd], sft);
+        r.d16 = (p[sh >> 2] >> ((sh & 2u) << 3)) & 0xFFFFu;
+    }
+
+    // From global memory, 2 bytes at a time (the block is 2-byte aligned).
+    template <int G>
+    __device__ static void fetch_direct(const uint8_t *blk, Raw &r) {
+        const uint16_t *h = (const uint16_t *)blk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r.q[i] = (uint32_t)h[1 + 8 * G + 2 * i] | ((uint32_t)h[2 + 8 * G + 2 * i] << 16);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            r.sg[i] = (uint32_t)h[37 + 4 * G + 2 * i] | ((uint32_t)h[38 + 4 * G + 2 * i] << 16);
+        r.hb = h[33 + G];
+        r.sc = (uint32_t)h[53] | ((uint32_t)h[54] << 16);
+        r.d16 = h[0];
+    }
+
     // acc + this lane's row sum over wavefront G's 64 weights. Group k (four
     // weights) of sub-block h reads two entries, halves p = 0 and 1: ((two
     // sign bits of nibble k) << 10 | p << 9 | ninth bit << 8 | index byte),
     // each assembled by one v_perm from the index dword and a dword of bytes
     // (s2 << 2 | p << 1 | ninth bit) built once per sub-block.
     template <int G>
-    __device__ static float dot(const uint8_t *col, int lane, cfloat_p xg, float acc) {
-        const uint4 q = *(const uint4 *)(col + kIdx + G * 1024 + 16 * lane);
-        const uint2 sg = *(const uint2 *)(col + kSign + G * 512 + 8 * lane);
-        const uint32_t hb = ld_u16(col + kHb + G * 128 + 2 * lane);
-        const uint32_t sc = *(const uint32_t *)(col + kScale + 4 * lane);
-        const float d = h2f_lo(ld_u16(col + kD + 2 * lane));
-        const uint32_t idx[4] = {q.x, q.y, q.z, q.w};
+    __device__ static float dot(const Raw &r, int, cfloat_p xg, float acc) {
+        const uint2 sg = {r.sg[0], r.sg[1]};
+        const uint32_t hb = r.hb, sc = r.sc;
+        const float d = h2f_lo(r.d16);
+        const uint32_t idx[4] = {r.q[0], r.q[1], r.q[2], r.q[3]};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t S = h ? sg.y : sg.x;
@@ -203,8 +274,10 @@ struct Iq4xsFmt {
     // 4-wavefront workgroups, seven per CU (LDS 22.5 KB each), SGPRs capped so
     // that the register file allows them. Measured on the IQ4_XS stream (us):
     // 4 x 2 capped 109-112, uncapped 115; 8 x 2 119; 16 x 2 151; the 64 KB pair
-    // table this replaced, one 16-wavefront workgroup per CU: 121.
+    // table this replaced, one 16-wavefront workgroup per CU: 121. Split
+    // launches 8 x 2: single GEMVs (tile layout) 10.7 / 12.4 us -> 9.7 / 9.7 us.
     static constexpr int kShape = 42;
+    static constexpr int kShapeSplit = 82;
     static constexpr int kTable = 4096;
     static constexpr bool kCapSgprs = true;   // 96 SGPRs: eight wavefronts per SIMD
     static constexpr int kBytes = kIq4xsBytes;
@@ -237,15 +310,68 @@ struct Iq4xsFmt {
         return exact;
     }
 
+    // The bytes of one block that wavefront G uses: code bytes 8+32G..39+32G
+    // and header bytes 0..7.
+    struct Raw {
+        uint32_t q[8];
+        uint2 hd;
+    };
+    // Row windows (row-major weights): the block starts at window byte 0 or 8
+    // (the weights 16-byte aligned, blocks 8 bytes apart) and takes all nine
+    // granules of the 144-byte window.
+    static constexpr int kWinGran = 9;
+
+    template <int G>
+    __device__ static void fetch_tiled(const uint8_t *col, int lane, Raw &r) {
+        const uint4 qa = *(const uint4 *)(col + kCodes + G * 2048 + 32 * lane);
+        const uint4 qb = *(const uint4 *)(col + kCodes + G * 2048 + 32 * lane + 16);
+        r.q[0] = qa.x;
+        r.q[1] = qa.y;
+        r.q[2] = qa.z;
+        r.q[3] = qa.w;
+        r.q[4] = qb.x;
+        r.q[5] = qb.y;
+        r.q[6] = qb.z;
+        r.q[7] = qb.w;
+        r.hd = *(const uint2 *)(col + kHead + 8 * lane);
+    }
+
+    // From a row window in LDS (sh = 0 or 8: every field 8-byte aligned).
+    template <int G>
+    __device__ static void fetch_window(const uint8_t *win, uint32_t sh, Raw &r) {
+        const u32x2 *p = (const u32x2 *)(win + sh + 8 + 32 * G);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x2 v = p[i];
+            r.q[2 * i] = v.x;
+            r.q[2 * i + 1] = v.y;
+        }
+        const u32x2 h = *(const u32x2 *)(win + sh);
+        r.hd = make_uint2(h.x, h.y);
+    }
+
+    // From global memory (the block is 8-byte aligned).
+    template <int G>
+    __device__ static void fetch_direct(const uint8_t *blk, Raw &r) {
+        const uint2 *p = (const uint2 *)(blk + 8 + 32 * G);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint2 v = p[i];
+            r.q[2 * i] = v.x;
+            r.q[2 * i + 1] = v.y;
+        }
+        r.hd = *(const uint2 *)blk;
+    }
+
     // Byte j of sub-block h's sixteen code bytes gives weights j (low nibble)
     // and j + 16 (high nibble). The nibbles of four bytes are split into bytes
     // with two masks; then per weight one v_perm forms v*256 + 4*lane and one
     // LDS read returns the table value.
     template <int G>
-    __device__ static float dot(const uint8_t *col, int lane, cfloat_p xg, float acc) {
-        const uint4 qa = *(const uint4 *)(col + kCodes + G * 2048 + 32 * lane);
-        const uint4 qb = *(const uint4 *)(col + kCodes + G * 2048 + 32 * lane + 16);
-        const uint2 hd = *(const uint2 *)(col + kHead + 8 * lane);
+    __device__ static float dot(const Raw &r, int lane, cfloat_p xg, float acc) {
+        const uint2 hd = r.hd;
+        const uint4 qa = {r.q[0], r.q[1], r.q[2], r.q[3]};
+        const uint4 qb = {r.q[4], r.q[5], r.q[6], r.q[7]};
         const float d = h2f_lo(hd.x);
         const uint32_t sh = hd.x >> 16;
         const uint32_t lofs = (uint32_t)lane * 4u;
@@ -319,24 +445,37 @@ __global__ __launch_bounds__(256) void cb_pack_tiles_kernel(const uint8_t *__res
 
 // ------------------------------------------------------------------ stream engine
 //
-// As the IQ3 engine on its tile layout: persistent workgroups walk work items
-// (64-row tile x super-block range); wavefront 4j + G computes sub-blocks 2G,
-// 2G+1 of super-block j of each stage for the 64 rows (lane = row), with the
+// As the IQ3 engine: persistent workgroups walk work items (64-row tile x
+// super-block range); wavefront 4j + G computes sub-blocks 2G, 2G+1 of
+// super-block j of each stage for the 64 rows (lane = row), with the
 // activations as scalar operands; an R-slot ring filled by LDS-DMA runs ahead
 // across items. The decode table sits at LDS address 0 (IQ3_S 16 KB, IQ4_XS
 // 4 KB), small enough for five or seven 4-wavefront workgroups per CU.
-template <class F, int W, int R>
+//
+// Two weight layouts (TL): the tile layout, whose stage columns are copied
+// whole; and row-major blocks as a file stores them, where each stage copies
+// for every row the 16-byte granules that hold its block into a 144-byte row
+// window (nine granules: 36 dwords apart, so the 64 lanes' reads spread over
+// the banks). The weights must then start on a 16-byte boundary (so no block
+// starts before it); a granule past the buffer's end is clamped to the last
+// whole one inside, and the one block that such a granule can hold (the last
+// row's last block, when the buffer ends off a boundary) is read directly
+// from memory by its lane.
+template <class F, int W, int R, bool TL>
 struct CbCfg {
     static constexpr int kBps = W / 4;
-    static constexpr int kGran = F::kCol / 16;        // 16-byte granules per column
-    static constexpr int kTable = F::kTable;          // at LDS address 0
+    static constexpr int kWin = 144;                              // row window bytes
+    static constexpr int kCol = TL ? F::kCol : kTileRows * kWin;  // one block column in LDS
+    static constexpr int kGran = kCol / 16;                       // 16-byte granules per column
+    static constexpr int kTable = F::kTable;                      // at LDS address 0
     static constexpr int kRing = kTable;
-    static constexpr int kSlot = kBps * F::kCol;
+    static constexpr int kSlot = kBps * kCol;
     static constexpr int kRed = kRing + R * kSlot;    // [W][64] fp32 row sums
     static constexpr int kLds = kRed + W * 64 * 4;
-    static_assert(F::kCol % 16 == 0, "columns are whole granules");
+    static_assert(kCol % 16 == 0, "columns are whole granules");
     static_assert(kGran <= 3 * 256, "a column takes at most three copy rounds");
     // copy instructions per stage of wavefront G: rounds i with 256i + 64G < kGran
+    // (in a row window some lanes of a round may idle, never all of them)
     static constexpr int copies(int G) {
         return (64 * G < kGran) + (256 + 64 * G < kGran) + (512 + 64 * G < kGran);
     }
@@ -344,11 +483,14 @@ struct CbCfg {
 
 struct CbItem {
     GemvArgs a;
-    const uint8_t *sb;   // the tile's column 0
-    int tile, split, kb0, kb1, nst;
+    const uint8_t *sb;   // tile layout: the tile's column 0; rows: its first row, rounded down to 16 bytes
+    uint32_t sb_off;     // rows: that row's offset from sb (0..15)
+    uint32_t hi;         // rows: last 16-byte granule wholly inside the weights, relative to sb (capped)
+    int tile, split, kb0, kb1, nst, row0;
+    bool tail;           // rows: holds the last row's last block and the buffer ends off a granule
 };
 
-template <class F, int BPS>
+template <class F, int BPS, bool TL>
 __device__ __forceinline__ void cb_load_item(CbItem &it, int k, const GroupArgs &g,
                                              const GemvArgs &single) {
     int local;
@@ -365,14 +507,32 @@ __device__ __forceinline__ void cb_load_item(CbItem &it, int k, const GroupArgs 
     it.kb0 = it.split * it.a.nb / splits;
     it.kb1 = (it.split + 1) * it.a.nb / splits;
     it.nst = (it.kb1 - it.kb0 + BPS - 1) / BPS;
-    it.sb = it.a.w + (int64_t)it.tile * it.a.nb * F::kCol;
+    it.row0 = it.tile * kTileRows;
+    if constexpr (TL) {
+        it.sb = it.a.w + (int64_t)it.tile * it.a.nb * F::kCol;
+        it.sb_off = 0;
+        it.hi = 0;
+        it.tail = false;
+        return;
+    }
+    const uintptr_t wb = (uintptr_t)it.a.w;   // 16-byte aligned
+    const uintptr_t we = wb + (uintptr_t)it.a.n_out * (uintptr_t)it.a.row_bytes;
+    const uintptr_t base0 = wb + (uintptr_t)it.row0 * (uintptr_t)it.a.row_bytes;
+    const uintptr_t sb = base0 & ~(uintptr_t)15;
+    it.sb = (const uint8_t *)sb;
+    it.sb_off = (uint32_t)(base0 & 15);
+    // The tile's first row starts at least one block (>= 110 bytes) before the
+    // end, so the last whole granule lies at or after sb.
+    const uintptr_t hi16 = (we & ~(uintptr_t)15) - 16;
+    it.hi = hi16 - sb < 0x40000000u ? (uint32_t)(hi16 - sb) : 0x40000000u;
+    it.tail = (we & 15) != 0 && it.row0 + kTileRows >= it.a.n_out && it.kb1 == it.a.nb;
 }
 
-template <class F, int G, int W, int R>
+template <class F, int G, int W, int R, bool TL>
 __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &single,
                                           const float *tab, int nitems, uint8_t *smem) {
     static_assert(R >= 2 && R <= 4, "ring of two to four stages");
-    using C = CbCfg<F, W, R>;
+    using C = CbCfg<F, W, R, TL>;
     constexpr int BPS = C::kBps;
     constexpr int kCp = C::copies(G);
     const int lane = threadIdx.x & 63;
@@ -384,23 +544,62 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
     int kc = skip_holes(blockIdx.x, stride, nitems, g);
     if (kc >= nitems) return;
     CbItem c;
-    cb_load_item<F, BPS>(c, kc, g, single);
+    cb_load_item<F, BPS, TL>(c, kc, g, single);
+
+    // Row windows: round i of this wavefront copies granule k = 256i + 64G + lane
+    // of the column, granule k % 9 of row k / 9's window (LDS byte 16k).
+    int crow[3];
+    uint32_t cgran[3];
+    bool cact[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int k = 256 * i + 64 * G + lane;
+        crow[i] = min(k / 9, kTileRows - 1);
+        cgran[i] = 16u * (uint32_t)(k % 9);
+        cact[i] = k < C::kGran && k % 9 < F::kWinGran;
+    }
 
     int kd = kc, sd = 0, slot_d = 0, pending = 0;
     CbItem d = c;
+    uint32_t doff[3];  // rows: this lane's granule of block 0 of its row, relative to d.sb
+    auto prep_copy = [&]() {
+        if constexpr (TL) return;
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            doff[i] = d.sb_off +
+                      (uint32_t)(min(d.row0 + crow[i], d.a.n_out - 1) - d.row0) *
+                          (uint32_t)d.a.row_bytes +
+                      cgran[i];
+    };
+    prep_copy();
     uint32_t flags = 0;  // bit k: this wavefront's copies are in ring slot k
     auto issue_next = [&]() {
         if (kd >= nitems) return;
         const int b = d.kb0 + sd * BPS + j;
         if (b < d.kb1) {
-            const uint32_t colb = lds0 + C::kRing + slot_d * C::kSlot + j * F::kCol;
-            const uint8_t *src = d.sb + (int64_t)b * F::kCol;
+            const uint32_t colb = lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol;
+            if constexpr (TL) {
+                const uint8_t *src = d.sb + (int64_t)b * F::kCol;
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const int g0 = 256 * i + 64 * G;    // this wavefront's first granule of round i
-                if (g0 < C::kGran) {
-                    if (g0 + lane < C::kGran)
-                        dma16_stream(src + 16 * (g0 + lane), colb + 16 * g0);
+                for (int i = 0; i < 3; ++i) {
+                    const int g0 = 256 * i + 64 * G;    // this wavefront's first granule of round i
+                    if (g0 < C::kGran) {
+                        if (g0 + lane < C::kGran)
+                            dma16_stream(src + 16 * (g0 + lane), colb + 16 * g0);
+                    }
+                }
+            } else {
+                const uint32_t boff = (uint32_t)(F::kBytes * b);
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    const int g0 = 256 * i + 64 * G;
+                    if (g0 < C::kGran) {
+                        if (cact[i]) {
+                            // (offset + a multiple of 16) & ~15 keeps the granule index
+                            const uint32_t off = min((doff[i] + boff) & ~15u, d.hi);
+                            dma16(d.sb, off, colb + 16 * g0);
+                        }
+                    }
                 }
             }
             flags |= 1u << slot_d;
@@ -412,7 +611,10 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
         if (++sd == d.nst) {
             sd = 0;
             kd = skip_holes(kd + stride, stride, nitems, g);
-            if (kd < nitems) cb_load_item<F, BPS>(d, kd, g, single);
+            if (kd < nitems) {
+                cb_load_item<F, BPS, TL>(d, kd, g, single);
+                prep_copy();
+            }
         }
     };
 #pragma unroll
@@ -434,6 +636,10 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
     float *red = (float *)(smem + C::kRed);
     int slot_c = 0;
     for (;;) {
+        const int row = c.row0 + lane;
+        // rows: low bits of this lane's row address (block offsets within granules)
+        const uint32_t rlo = (uint32_t)(uintptr_t)c.a.w +
+                             (uint32_t)min(row, c.a.n_out - 1) * (uint32_t)c.a.row_bytes;
         float acc = 0.0f;
         for (int s = 0; s < c.nst; ++s) {
             const int nxt = slot_c + 1 == R ? 0 : slot_c + 1;
@@ -446,9 +652,23 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
             lds_barrier();   // stage in slot_c complete for every wavefront (and the table)
             issue_next();
             const int b = c.kb0 + s * BPS + j;
-            if (b < c.kb1)
-                acc = F::template dot<G>(smem + C::kRing + slot_c * C::kSlot + j * F::kCol, lane,
-                                         as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
+            if (b < c.kb1) {
+                const uint8_t *col = smem + C::kRing + slot_c * C::kSlot + j * C::kCol;
+                typename F::Raw raw;
+                if constexpr (TL) {
+                    F::template fetch_tiled<G>(col, lane, raw);
+                } else {
+                    const uint32_t sh = (rlo + (uint32_t)(F::kBytes * b)) & 15u;
+                    F::template fetch_window<G>(col + C::kWin * lane, sh, raw);
+                    if (c.tail && b == c.a.nb - 1) {   // wave-uniform, once per matrix
+                        if (row == c.a.n_out - 1)
+                            F::template fetch_direct<G>(
+                                c.a.w + (int64_t)row * c.a.row_bytes + (int64_t)F::kBytes * b, raw);
+                    }
+                }
+                acc = F::template dot<G>(raw, lane, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G,
+                                         acc);
+            }
             --pending;
             slot_c = nxt;
         }
@@ -463,49 +683,49 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
         }
         kc = skip_holes(kc + stride, stride, nitems, g);
         if (kc >= nitems) break;
-        cb_load_item<F, BPS>(c, kc, g, single);
+        cb_load_item<F, BPS, TL>(c, kc, g, single);
     }
 }
 
-template <class F, int W, int R>
+template <class F, int W, int R, bool TL>
 __device__ __forceinline__ void cb_stream_entry(GroupArgs g, GemvArgs single, const float *tab,
                                                 int nitems) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
-        case 0: cb_stream<F, 0, W, R>(g, single, tab, nitems, smem); break;
-        case 1: cb_stream<F, 1, W, R>(g, single, tab, nitems, smem); break;
-        case 2: cb_stream<F, 2, W, R>(g, single, tab, nitems, smem); break;
-        default: cb_stream<F, 3, W, R>(g, single, tab, nitems, smem); break;
+        case 0: cb_stream<F, 0, W, R, TL>(g, single, tab, nitems, smem); break;
+        case 1: cb_stream<F, 1, W, R, TL>(g, single, tab, nitems, smem); break;
+        case 2: cb_stream<F, 2, W, R, TL>(g, single, tab, nitems, smem); break;
+        default: cb_stream<F, 3, W, R, TL>(g, single, tab, nitems, smem); break;
     }
 }
 
 // The same kernel with and without an SGPR cap (the attribute takes no
 // template argument); F::kCapSgprs picks one.
-template <class F, int W, int R>
+template <class F, int W, int R, bool TL>
 __global__ __launch_bounds__(W * 64) void cb_stream_kernel(GroupArgs g, GemvArgs single,
                                                            const float *tab, int nitems) {
-    cb_stream_entry<F, W, R>(g, single, tab, nitems);
+    cb_stream_entry<F, W, R, TL>(g, single, tab, nitems);
 }
 
-template <class F, int W, int R>
+template <class F, int W, int R, bool TL>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_num_sgpr(96))) void cb_stream_kernel96(
     GroupArgs g, GemvArgs single, const float *tab, int nitems) {
-    cb_stream_entry<F, W, R>(g, single, tab, nitems);
+    cb_stream_entry<F, W, R, TL>(g, single, tab, nitems);
 }
 
-template <class F, int W, int R>
+template <class F, int W, int R, bool TL>
 constexpr auto cb_kernel() {
     if constexpr (F::kCapSgprs)
-        return cb_stream_kernel96<F, W, R>;
+        return cb_stream_kernel96<F, W, R, TL>;
     else
-        return cb_stream_kernel<F, W, R>;
+        return cb_stream_kernel<F, W, R, TL>;
 }
 
 // Engine shapes (wavefronts, ring stages). QWG_CB_SHAPE = 10*W + R picks one
-// for both formats (tuning experiments).
+// for both formats and layouts (tuning experiments).
 #define QWG_CB_SHAPES(X) X(16, 2) X(16, 3) X(12, 3) X(8, 2) X(8, 3) X(8, 4) X(4, 2) X(4, 3)
 
-template <class F, int W, int R>
+template <class F, int W, int R, bool TL>
 int cb_slots_wr() {
     // a function-local static: initialised once even under concurrent first calls
     static const int slots = [] {
@@ -514,9 +734,9 @@ int cb_slots_wr() {
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus < 1)
             cus = 256;
-        constexpr size_t lds = CbCfg<F, W, R>::kLds;
+        constexpr size_t lds = CbCfg<F, W, R, TL>::kLds;
         if (lds > 160 * 1024 ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cb_kernel<F, W, R>(), W * 64,
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cb_kernel<F, W, R, TL>(), W * 64,
                                                          lds) != hipSuccess ||
             per_cu < 1)
             per_cu = lds > 160 * 1024 ? 0 : 1;
@@ -525,31 +745,33 @@ int cb_slots_wr() {
     return slots;
 }
 
-template <class F, int W, int R>
+template <class F, int W, int R, bool TL>
 hipError_t cb_launch_wr(const GroupArgs &g, const GemvArgs &single, const float *tab, int nitems,
                         hipStream_t s) {
-    int n = cb_slots_wr<F, W, R>();
+    int n = cb_slots_wr<F, W, R, TL>();
     if (n <= 0) return hipErrorInvalidValue;
     if (n > nitems) n = nitems;
-    constexpr size_t lds = CbCfg<F, W, R>::kLds;
-    hipLaunchKernelGGL((cb_kernel<F, W, R>()), dim3((unsigned)n), dim3(W * 64), lds, s, g,
+    constexpr size_t lds = CbCfg<F, W, R, TL>::kLds;
+    hipLaunchKernelGGL((cb_kernel<F, W, R, TL>()), dim3((unsigned)n), dim3(W * 64), lds, s, g,
                        single, tab, nitems);
     return hipGetLastError();
 }
 
-template <class F>
+template <class F, bool TL>
 int cb_slots_any(int shape) {
     switch (shape) {
 #define X(w, r) \
-    case 10 * w + r: return cb_slots_wr<F, w, r>();
+    case 10 * w + r: return cb_slots_wr<F, w, r, TL>();
         QWG_CB_SHAPES(X)
 #undef X
         default: return 0;
     }
 }
 
+// QWG_CB_SHAPE = 10*W + R overrides the shape of every launch of both formats
+// and layouts (tuning experiments); 0 if unset or not a valid shape.
 template <class F>
-int cb_shape() {
+int cb_env_shape() {
     static const int v = [] {
         const char *e = getenv("QWG_CB_SHAPE");
         const int k = e ? atoi(e) : 0;
@@ -557,25 +779,25 @@ int cb_shape() {
 #define X(w, r) case 10 * w + r:
             QWG_CB_SHAPES(X)
 #undef X
-            return cb_slots_any<F>(k) > 0 ? k : F::kShape;
-            default: return F::kShape;
+            return cb_slots_any<F, true>(k) > 0 && cb_slots_any<F, false>(k) > 0 ? k : 0;
+            default: return 0;
         }
     }();
     return v;
 }
 
 template <class F>
-int cb_slots_f() { return cb_slots_any<F>(cb_shape<F>()); }
+int cb_shape_f(bool split) {
+    const int e = cb_env_shape<F>();
+    return e ? e : split ? F::kShapeSplit : F::kShape;
+}
 
-template <class F>
-int cb_bps_f() { return (cb_shape<F>() / 10) / 4; }
-
-template <class F>
-hipError_t cb_launch(const GroupArgs &g, const GemvArgs &single, const float *tab, int nitems,
-                     hipStream_t s) {
-    switch (cb_shape<F>()) {
+template <class F, bool TL>
+hipError_t cb_launch(int shape, const GroupArgs &g, const GemvArgs &single, const float *tab,
+                     int nitems, hipStream_t s) {
+    switch (shape) {
 #define X(w, r) \
-    case 10 * w + r: return cb_launch_wr<F, w, r>(g, single, tab, nitems, s);
+    case 10 * w + r: return cb_launch_wr<F, w, r, TL>(g, single, tab, nitems, s);
         QWG_CB_SHAPES(X)
 #undef X
         default: return hipErrorInvalidValue;
@@ -615,22 +837,28 @@ hipError_t launch_cb_pack_tiles(int fmt, const uint8_t *src, uint8_t *dst, int n
     return hipGetLastError();
 }
 
-int cb_stream_slots(int fmt) {
-    if (fmt == kFmtIq3s) return cb_slots_f<Iq3sFmt>();
-    if (fmt == kFmtIq4xs) return cb_slots_f<Iq4xsFmt>();
+int cb_stream_shape(int fmt, bool split) {
+    if (fmt == kFmtIq3s) return cb_shape_f<Iq3sFmt>(split);
+    if (fmt == kFmtIq4xs) return cb_shape_f<Iq4xsFmt>(split);
     return 0;
 }
 
-int cb_stream_bps(int fmt) {
-    if (fmt == kFmtIq3s) return cb_bps_f<Iq3sFmt>();
-    if (fmt == kFmtIq4xs) return cb_bps_f<Iq4xsFmt>();
-    return 1;
+int cb_stream_slots(int fmt, bool tiled, int shape) {
+    if (fmt == kFmtIq3s)
+        return tiled ? cb_slots_any<Iq3sFmt, true>(shape) : cb_slots_any<Iq3sFmt, false>(shape);
+    if (fmt == kFmtIq4xs)
+        return tiled ? cb_slots_any<Iq4xsFmt, true>(shape) : cb_slots_any<Iq4xsFmt, false>(shape);
+    return 0;
 }
 
-hipError_t launch_cb_stream(int fmt, const GroupArgs &g, const GemvArgs &single, const float *tab,
-                            int nitems, hipStream_t s) {
-    if (fmt == kFmtIq3s) return cb_launch<Iq3sFmt>(g, single, tab, nitems, s);
-    if (fmt == kFmtIq4xs) return cb_launch<Iq4xsFmt>(g, single, tab, nitems, s);
+hipError_t launch_cb_stream(int fmt, bool tiled, int shape, const GroupArgs &g,
+                            const GemvArgs &single, const float *tab, int nitems, hipStream_t s) {
+    if (fmt == kFmtIq3s)
+        return tiled ? cb_launch<Iq3sFmt, true>(shape, g, single, tab, nitems, s)
+                     : cb_launch<Iq3sFmt, false>(shape, g, single, tab, nitems, s);
+    if (fmt == kFmtIq4xs)
+        return tiled ? cb_launch<Iq4xsFmt, true>(shape, g, single, tab, nitems, s)
+                     : cb_launch<Iq4xsFmt, false>(shape, g, single, tab, nitems, s);
     return hipErrorInvalidValue;
 }
 

@@ -274,6 +274,30 @@ int stream_splits(int nb, int bps, int64_t factor) {
     return s < 1 ? 1 : s;
 }
 
+// Splits and engine shape of a single IQ3_S / IQ4_XS GEMV on the tile layout
+// (tiled) or on row-major blocks: none when the tiles alone give every
+// resident workgroup of the engine two items; otherwise the split shape and
+// as many splits as stream_splits allows within the workspace. Splits 0 when
+// the engine's residency is unknown.
+struct CbPlan {
+    int splits, shape;
+};
+
+CbPlan cb_plan(int fmt, bool tiled, int nb, int tiles) {
+    CbPlan p = {1, cb_stream_shape(fmt, false)};
+    const int slots = cb_stream_slots(fmt, tiled, p.shape);
+    if (slots <= 0) return {0, p.shape};
+    if (slots <= 2 * tiles) return p;
+    p.shape = cb_stream_shape(fmt, true);
+    const int ss = cb_stream_slots(fmt, tiled, p.shape);
+    if (ss <= 0) return {0, p.shape};
+    int sp = stream_splits(nb, p.shape / 40, ss / tiles);
+    while (sp > 1 && ((size_t)sp * tiles * kTileRows > kWsPartialFloats || (size_t)tiles > kWsCounters))
+        --sp;
+    p.splits = sp;
+    return p;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? QWG_OK : QWG_ERR_HIP; }
 
 }  // namespace
@@ -337,9 +361,8 @@ int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
     if (rc) return -rc;
     const int tiles = (int)((n_out + kTileRows - 1) / kTileRows);
     if (codebook_format(fmt)) {
-        const int slots = cb_stream_slots(fmt);
-        if (slots <= 0) return -QWG_ERR_HIP;
-        return iq3_splits(tiles, (int)(n_in / kQK), slots);
+        const int sp = cb_plan(fmt, false, (int)(n_in / kQK), tiles).splits;
+        return sp > 0 ? sp : -QWG_ERR_HIP;
     }
     if (fmt != QWG_FMT_Q4K) {
         const int slots = iq3_stream_slots(iq3_shape(false, 0), false);
@@ -720,8 +743,8 @@ int cb_pack(int fmt, void *dst, const void *src, int64_t n_in, int64_t n_out, vo
                                            (int)(n_in / kQK), (int)n_out, (hipStream_t)stream));
 }
 
-int cb_gemv_tiled(int fmt, float *y, const float *x, const void *w, const float *tab, int64_t n_in,
-                  int64_t n_out, void *stream) {
+int cb_gemv(int fmt, bool tiled, float *y, const float *x, const void *w, const float *tab,
+            int64_t n_in, int64_t n_out, void *stream) {
     if (!y || !x || !w || !tab) return QWG_ERR_NULL;
     int rc = check_gemv_shape(n_in, n_out);
     if (rc) return rc;
@@ -729,16 +752,10 @@ int cb_gemv_tiled(int fmt, float *y, const float *x, const void *w, const float 
         return QWG_ERR_ALIGN;
     GemvArgs a;
     fill_shape(a, w, x, tab, y, n_in, n_out, block_bytes_of(fmt));
-    a.layout = kLayoutTiles;
-    const int slots = cb_stream_slots(fmt);
-    if (slots <= 0) return QWG_ERR_HIP;
-    if (slots > 2 * a.tiles) {
-        int sp = stream_splits(a.nb, cb_stream_bps(fmt), slots / a.tiles);
-        while (sp > 1 && ((size_t)sp * a.tiles * kTileRows > kWsPartialFloats ||
-                          (size_t)a.tiles > kWsCounters))
-            --sp;
-        a.splits = sp;
-    }
+    a.layout = tiled ? kLayoutTiles : kLayoutRows;
+    const CbPlan plan = cb_plan(fmt, tiled, a.nb, a.tiles);
+    if (plan.splits <= 0) return QWG_ERR_HIP;
+    a.splits = plan.splits;
     if (a.splits > 1) {
         Workspace ws;
         rc = get_workspace((hipStream_t)stream, &ws);
@@ -748,7 +765,8 @@ int cb_gemv_tiled(int fmt, float *y, const float *x, const void *w, const float 
     }
     const GroupArgs none = {nullptr, nullptr, nullptr};
     return hip_status(
-        launch_cb_stream(fmt, none, a, tab, a.tiles * a.splits, (hipStream_t)stream));
+        launch_cb_stream(fmt, tiled, plan.shape, none, a, tab, a.tiles * a.splits,
+                         (hipStream_t)stream));
 }
 
 }  // namespace
@@ -769,14 +787,24 @@ int qwg_pack_iq4xs_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out
     return cb_pack(QWG_FMT_IQ4_XS, dst, src, n_in, n_out, stream);
 }
 
+int qwg_gemv_iq3s(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
+                  int64_t n_out, void *stream) {
+    return cb_gemv(QWG_FMT_IQ3_S, false, y, x, w, grid, n_in, n_out, stream);
+}
+
+int qwg_gemv_iq4xs(float *y, const float *x, const void *w, const float *table, int64_t n_in,
+                   int64_t n_out, void *stream) {
+    return cb_gemv(QWG_FMT_IQ4_XS, false, y, x, w, table, n_in, n_out, stream);
+}
+
 int qwg_gemv_iq3s_tiled(float *y, const float *x, const void *w, const float *grid, int64_t n_in,
                         int64_t n_out, void *stream) {
-    return cb_gemv_tiled(QWG_FMT_IQ3_S, y, x, w, grid, n_in, n_out, stream);
+    return cb_gemv(QWG_FMT_IQ3_S, true, y, x, w, grid, n_in, n_out, stream);
 }
 
 int qwg_gemv_iq4xs_tiled(float *y, const float *x, const void *w, const float *table,
                          int64_t n_in, int64_t n_out, void *stream) {
-    return cb_gemv_tiled(QWG_FMT_IQ4_XS, y, x, w, table, n_in, n_out, stream);
+    return cb_gemv(QWG_FMT_IQ4_XS, true, y, x, w, table, n_in, n_out, stream);
 }
 
 // ------------------------------------------------------------------ grouped GEMV
@@ -795,6 +823,7 @@ struct qwg_group {
     int max_nb;
     bool split;           // some member splits its rows' sums
     int waves, ring;      // Q4_K stream engine shape of the launch
+    int cb_shape;         // IQ3_S / IQ4_XS engine shape of the launch (10 * waves + ring)
     int batch;            // activation rows per member (2..8: the matrix-core engine)
     int cols;             // its super-block columns per stage
 };
@@ -912,7 +941,9 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     const bool cb = codebook_format(fmt);
     const bool iq3 = fmt == QWG_FMT_IQ3 || cb;   // round-robin schedule, grid/table argument
     const int block_bytes = block_bytes_of(fmt);
-    const uintptr_t w_align = iq3 && layout == kLayoutRows ? 2 : 16;
+    // row-major IQ3 blocks need 2-byte alignment; tile layouts and row-major
+    // IQ3_S / IQ4_XS (whose engine copies 16-byte granules from the start) 16
+    const uintptr_t w_align = iq3 && !cb && layout == kLayoutRows ? 2 : 16;
     std::vector<GemvArgs> probs((size_t)count);
     int64_t total = 0;
     int max_nb = 1;
@@ -943,9 +974,18 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     int64_t slots = 0, bps = 1;
     int per_cu = 0, cus = 0;
     StreamShape ssh = {4, 2};
+    int cb_shape = 0;
     if (cb) {
-        slots = cb_stream_slots(fmt);
-        bps = cb_stream_bps(fmt);
+        // as a single GEMV: the split shape when the members' tiles leave
+        // resident workgroups idle
+        cb_shape = cb_stream_shape(fmt, false);
+        slots = cb_stream_slots(fmt, layout == kLayoutTiles, cb_shape);
+        if (slots > 2 * total) {
+            cb_shape = cb_stream_shape(fmt, true);
+            slots = cb_stream_slots(fmt, layout == kLayoutTiles, cb_shape);
+        }
+        if (slots <= 0) return QWG_ERR_HIP;
+        bps = cb_shape / 40;
     } else if (iq3) {
         const Iq3Shape ish = iq3_shape(true, 0);
         slots = iq3_stream_slots(ish, layout == kLayoutTiles);
@@ -1050,6 +1090,7 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     g->split = split;
     g->waves = ssh.waves;
     g->ring = ssh.ring;
+    g->cb_shape = cb_shape;
     g->batch = batch;
     // One column per stage: a group has thousands of workgroups, and the
     // 8-wavefront two-column shape that helps short single launches measured
@@ -1114,6 +1155,24 @@ int qwg_group_create_iq3_tiled(const qwg_gemv_desc *descs, int count, const floa
     return group_create(QWG_FMT_IQ3, kLayoutTiles, descs, count, grid, out);
 }
 
+int qwg_group_create_iq3s(const qwg_gemv_desc *descs, int count, const float *grid,
+                          qwg_group **out) {
+    if (!descs || !grid || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    if (!aligned(grid, 16)) return QWG_ERR_ALIGN;
+    return group_create(QWG_FMT_IQ3_S, kLayoutRows, descs, count, grid, out);
+}
+
+int qwg_group_create_iq4xs(const qwg_gemv_desc *descs, int count, const float *table,
+                           qwg_group **out) {
+    if (!descs || !table || !out) return QWG_ERR_NULL;
+    *out = nullptr;
+    if (count < 1 || count > QWG_MAX_GROUP) return QWG_ERR_SHAPE;
+    if (!aligned(table, 16)) return QWG_ERR_ALIGN;
+    return group_create(QWG_FMT_IQ4_XS, kLayoutRows, descs, count, table, out);
+}
+
 int qwg_group_create_iq3s_tiled(const qwg_gemv_desc *descs, int count, const float *grid,
                                 qwg_group **out) {
     if (!descs || !grid || !out) return QWG_ERR_NULL;
@@ -1141,7 +1200,8 @@ int qwg_group_run(const qwg_group *g, void *stream) {
             launch_q4k_mfma_group(g->args, g->workgroups, g->batch, g->cols,
                                   g->layout == kLayoutTiles, (hipStream_t)stream));
     if (codebook_format(g->fmt))
-        return hip_status(launch_cb_stream(g->fmt, g->args, unused, g->grid, g->positions,
+        return hip_status(launch_cb_stream(g->fmt, g->layout == kLayoutTiles, g->cb_shape,
+                                           g->args, unused, g->grid, g->positions,
                                            (hipStream_t)stream));
     if (g->fmt == QWG_FMT_IQ3)
         return hip_status(launch_iq3_stream(g->args, unused, g->grid, g->positions,

@@ -117,18 +117,24 @@ hipError_t launch_iq3_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n
                                  hipStream_t s);
 
 // Codebook formats IQ3_S / IQ4_XS (codebook.hip). Dequant: bit-exact. GEMV:
-// tile layout only (launch_cb_pack_tiles makes it), 16-wavefront workgroups,
-// one per CU; `tab` is the [512][4] grid (IQ3_S) or the 16-value table (IQ4_XS).
+// persistent 4-wavefront workgroups on the tile layout (launch_cb_pack_tiles
+// makes it) or on row-major blocks; `tab` is the [512][4] grid (IQ3_S) or the
+// 16-value table (IQ4_XS).
 hipError_t launch_iq3s_dequant(const uint8_t *src, const float *grid, float *dst, int64_t nblocks,
                                hipStream_t s);
 hipError_t launch_iq4xs_dequant(const uint8_t *src, const float *table, float *dst,
                                 int64_t nblocks, hipStream_t s);
 hipError_t launch_cb_pack_tiles(int fmt, const uint8_t *src, uint8_t *dst, int nb, int n_out,
                                 hipStream_t s);
-int cb_stream_slots(int fmt);   // resident workgroups on the current device (0: unknown format)
-int cb_stream_bps(int fmt);     // super-blocks per pipeline stage
-hipError_t launch_cb_stream(int fmt, const GroupArgs &g, const GemvArgs &single, const float *tab,
-                            int nitems, hipStream_t s);
+// Engine shape (10 * wavefronts + ring stages; wavefronts / 4 super-blocks per
+// pipeline stage) of a launch that splits its sums (split) or not.
+int cb_stream_shape(int fmt, bool split);
+// resident workgroups of the tile-layout (tiled) or row-major engine of that
+// shape on the current device (0: unknown format or shape)
+int cb_stream_slots(int fmt, bool tiled, int shape);
+// tiled: the tile layout; otherwise row-major blocks, w 16-byte aligned
+hipError_t launch_cb_stream(int fmt, bool tiled, int shape, const GroupArgs &g,
+                            const GemvArgs &single, const float *tab, int nitems, hipStream_t s);
 
 // Layer-chain launch (chain.hip): a decoder's Q4_K weight stream in phases that
 // run in dependency order inside one persistent launch (tile-layout weights).

@@ -39,6 +39,8 @@ def test_header_declares_the_entry_points():
                  "qwg_gemv_iq3_xxs", "qwg_pack_iq3_xxs_tiles", "qwg_dequant_iq3s",
                  "qwg_dequant_iq4xs", "qwg_pack_iq3s_tiles", "qwg_pack_iq4xs_tiles",
                  "qwg_gemv_iq3s_tiled", "qwg_gemv_iq4xs_tiled", "qwg_group_create_iq3s_tiled",
+                 "qwg_gemv_iq3s", "qwg_gemv_iq4xs", "qwg_group_create_iq3s",
+                 "qwg_group_create_iq4xs",
                  "qwg_group_create_iq4xs_tiled", "qwg_encode_iq3",
                  "qwg_group_create_q4k_batched", "qwg_group_create_q4k_batched_tiled",
                  "qwg_gemm_q4k_tiled", "qwg_gemm_q4k_noalloc", "qwg_workspace_reserve",
@@ -214,6 +216,17 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_gemv_iq4xs_tiled(FAKE, FAKE + 4, FAKE, FAKE, 256, 1, None), 3),
     (lambda L: L.qwg_gemv_iq4xs_tiled(FAKE, FAKE, FAKE, FAKE + 4, 256, 1, None), 3),
     (lambda L: L.qwg_gemv_iq4xs_tiled(None, FAKE, FAKE, FAKE, 256, 1, None), 1),
+    # row-major IQ3_S / IQ4_XS: weights 16-byte aligned like the tile layout
+    (lambda L: L.qwg_gemv_iq3s(FAKE, FAKE, FAKE, None, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_iq3s(FAKE, FAKE, None, FAKE, 256, 1, None), 1),
+    (lambda L: L.qwg_gemv_iq3s(FAKE, FAKE, FAKE, FAKE, 384, 1, None), 2),
+    (lambda L: L.qwg_gemv_iq3s(FAKE, FAKE, FAKE, FAKE, 256, 0, None), 2),
+    (lambda L: L.qwg_gemv_iq3s(FAKE, FAKE, FAKE + 2, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3s(FAKE, FAKE + 4, FAKE, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq3s(FAKE + 2, FAKE, FAKE, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq4xs(FAKE, FAKE, FAKE + 8, FAKE, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq4xs(FAKE, FAKE, FAKE, FAKE + 4, 256, 1, None), 3),
+    (lambda L: L.qwg_gemv_iq4xs(None, FAKE, FAKE, FAKE, 256, 1, None), 1),
     # IQ3 with an explicit decomposition
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, None, 256, 1, 4, 1, None), 1),
     (lambda L: L.qwg_gemv_iq3_ex(FAKE, FAKE, FAKE, FAKE, 384, 1, 4, 1, None), 2),
@@ -279,7 +292,8 @@ def test_tiled_group_validation_errors(L):
     assert L.qwg_group_create_q4k_tiled(None, 1, ctypes.byref(out)) == 1
     assert L.qwg_group_create_q4k_tiled(arr, 0, ctypes.byref(out)) == 2
     # IQ3_S / IQ4_XS tiled groups: the same member rules, plus the grid/table
-    for create in (L.qwg_group_create_iq3s_tiled, L.qwg_group_create_iq4xs_tiled):
+    for create in (L.qwg_group_create_iq3s_tiled, L.qwg_group_create_iq4xs_tiled,
+                   L.qwg_group_create_iq3s, L.qwg_group_create_iq4xs):
         assert create(arr3, 1, FAKE, ctypes.byref(out)) == 3
         assert create(arr3, 1, None, ctypes.byref(out)) == 1
         assert create(arr, 2, FAKE + 4, ctypes.byref(out)) == 3

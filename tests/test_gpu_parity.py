@@ -1351,13 +1351,16 @@ def test_chain_ragged_members_and_one_phase():
 
 # ---------------------------------------------------------------- IQ3_S and IQ4_XS
 
+CB_FMT = {"iq3s": qwg.QWG_FMT_IQ3_S, "iq4xs": qwg.QWG_FMT_IQ4_XS}
 CB = {
     "iq3s": dict(weights=synth.iq3s_weights, table=synth.iq3s_grid, nbytes=110,
                  dequant=qwg.dequant_iq3s, pack=qwg.pack_iq3s_tiles, gemv=qwg.gemv_iq3s_tiled,
+                 rows=qwg.gemv_iq3s,
                  group=qwg.Iq3sGroup, o_dequant=oracle.dequant_iq3s, o_gemv=oracle.gemv_iq3s,
                  o_rows=oracle.gemv_iq3s_rows),
     "iq4xs": dict(weights=synth.iq4xs_weights, table=synth.iq4nl_table, nbytes=136,
                   dequant=qwg.dequant_iq4xs, pack=qwg.pack_iq4xs_tiles, gemv=qwg.gemv_iq4xs_tiled,
+                  rows=qwg.gemv_iq4xs,
                   group=qwg.Iq4xsGroup, o_dequant=oracle.dequant_iq4xs, o_gemv=oracle.gemv_iq4xs,
                   o_rows=oracle.gemv_iq4xs_rows),
 }
@@ -1426,6 +1429,124 @@ def test_gemv_codebook_tiled(fmt, n_out, n_in):
     yr, sr = c["o_gemv"](w, tab, x, n_in, n_out)
     assert_bound(y, yr, sr, f"{fmt} tiled {n_out}x{n_in}")
     assert_bits(host(c["gemv"](wt, xd, td, n_out)), y, f"{fmt} rerun")
+
+
+def _guarded_cb(w: np.ndarray, offset: int):
+    """Row-major codebook weights at `offset` (a multiple of 16) past a 256-byte
+    boundary, with 0xFF bytes (an fp16 NaN scale) before and after them, so that
+    a byte used from outside w shows as NaN rows."""
+    buf = torch.full((w.size + offset + 160,), 0xFF, dtype=torch.uint8, device=DEV)
+    buf[offset:offset + w.size] = dev(w.reshape(-1))
+    wd = buf[offset:offset + w.size]
+    assert wd.data_ptr() % 256 == offset
+    return wd
+
+
+# Row-major blocks as a file stores them. (n_out * n_in/256) odd: the buffer
+# ends off a 16-byte boundary (the last row's last block is read directly);
+# 130 x 5632 and 7 x 2816 rows are not multiples of 16 bytes, so every row's
+# blocks start at a different offset within their granules.
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 768), (65, 768), (7, 2816), (130, 5632),
+                                        (2048, 2048), (5632, 2048), (2048, 5632), (4097, 1280)])
+def test_gemv_codebook_rows(fmt, n_out, n_in):
+    c = CB[fmt]
+    tab = c["table"]()
+    w = c["weights"](n_out, n_in, 168, n_out)
+    x = synth.activations(n_in, 168, n_out)
+    wd, xd, td = dev(w), dev(x), dev(tab)
+    y = torch.full((n_out,), float("nan"), device=DEV)
+    c["rows"](wd, xd, td, out=y)
+    y = host(y).copy()
+    yr, sr = c["o_gemv"](w, tab, x, n_in, n_out)
+    assert_bound(y, yr, sr, f"{fmt} rows {n_out}x{n_in} splits={qwg.plan_splits(CB_FMT[fmt], n_in, n_out)}")
+    assert_bits(host(c["rows"](wd, xd, td)), y, f"{fmt} rows rerun")
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+@pytest.mark.parametrize("offset", [0, 16, 48, 240])
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (3, 768), (65, 1280), (129, 2048)])
+def test_gemv_codebook_rows_reads_only_the_weights(fmt, offset, n_out, n_in):
+    c = CB[fmt]
+    tab = c["table"]()
+    w = c["weights"](n_out, n_in, 169, offset + n_out)
+    x = synth.activations(n_in, 169, n_out)
+    y = host(c["rows"](_guarded_cb(w, offset), dev(x), dev(tab)))
+    yr, sr = c["o_gemv"](w, tab, x, n_in, n_out)
+    assert_bound(y, yr, sr, f"{fmt} rows at +{offset} {n_out}x{n_in}")
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+def test_gemv_codebook_rows_misaligned_weights_rejected(fmt):
+    c = CB[fmt]
+    w = c["weights"](2, 256, 170, 0)
+    buf = torch.zeros(w.size + 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(qwg.QwgError) as e:
+        c["rows"](buf[8:8 + w.size], dev(synth.activations(256, 170, 0)), dev(c["table"]()))
+    assert e.value.status == 3
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+def test_gemv_codebook_rows_lm_head_all_rows(fmt):
+    c = CB[fmt]
+    n_out, n_in = 32000, 2048
+    tab = c["table"]()
+    w = c["weights"](n_out, n_in, 171, 0)
+    x = synth.activations(n_in, 171, 0)
+    y = torch.full((n_out,), float("nan"), device=DEV)
+    c["rows"](dev(w), dev(x), dev(tab), out=y)
+    yr, sr = c["o_gemv"](w, tab, x, n_in, n_out)
+    assert_bound(host(y), yr, sr, f"{fmt} rows lm head")
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+@pytest.mark.parametrize("n_out,n_in", [(150, 2048), (64, 5632), (7, 256), (33, 2816)])
+def test_gemv_codebook_rows_integer_exact(fmt, n_out, n_in):
+    c = CB[fmt]
+    tab = c["table"]()
+    w = _integer_cb(fmt, n_out, n_in, n_out + 1)
+    x = np.random.default_rng(n_in + n_out + 1).integers(-8, 9, n_in).astype(np.float32)
+    yr, _ = c["o_gemv"](w, tab, x, n_in, n_out)
+    y = host(c["rows"](dev(w), dev(x), dev(tab)))
+    assert np.array_equal(y.astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+def test_codebook_rows_group_stream_all_rows(fmt):
+    c = CB[fmt]
+    tab = c["table"]()
+    probs, ws, xs, refs = stream_case(fmt + "_c6", lambda: (
+        synth.config(6), [c["weights"](p.n_out, p.n_in, 167, k) for k, p in enumerate(synth.config(6))],
+        [synth.inputs(p) for p in synth.config(6)],
+        lambda p, w, x: c["o_gemv"](w, tab, x, p.n_in, p.n_out)))
+    Y = nan_outputs(probs)
+    g = c["group"](zip([dev(w) for w in ws], [dev(x) for x in xs], Y), dev(tab), tiled=False)
+    for _ in range(2):
+        g.run()
+    assert_stream(probs, refs, Y, f"{fmt} rows stream")
+    g.close()
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+def test_codebook_rows_groups_layer_repeat_runs(fmt):
+    c = CB[fmt]
+    tab = c["table"]()
+    probs = synth.config(2)
+    ws = [c["weights"](p.n_out, p.n_in, 172, k) for k, p in enumerate(probs)]
+    X = [torch.empty(p.n_in, device=DEV) for p in probs]
+    Y = [torch.empty(p.n_out, device=DEV) for p in probs]
+    g = c["group"](zip([dev(w) for w in ws], X, Y), dev(tab), tiled=False)
+    for run in range(3):
+        xs = [synth.activations(p.n_in, 172, 10 * run + k) for k, p in enumerate(probs)]
+        for xd, x in zip(X, xs):
+            xd.copy_(torch.from_numpy(x))
+        for y in Y:
+            y.fill_(float("nan"))
+        g.run()
+        for p, w, x, y in zip(probs, ws, xs, Y):
+            yr, sr = c["o_gemv"](w, tab, x, p.n_in, p.n_out)
+            assert_bound(host(y), yr, sr, f"{fmt} rows layer run {run} {p.name}")
+    g.close()
 
 
 @pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
@@ -1516,6 +1637,7 @@ def test_codebook_not_fp16_exact_is_reported(fmt):
     # fp16 (2.0) is within the bound.
     n_out, n_in = 130, 768
     x = synth.activations(n_in, 220, 0)
+    rows = None
     if fmt == "iq3":
         tab = synth.iq3_grid().copy()
         w = synth.iq3_weights(n_out, n_in, 220, 1)
@@ -1528,20 +1650,23 @@ def test_codebook_not_fp16_exact_is_reported(fmt):
         w = c["weights"](n_out, n_in, 220, 2)
         wt = c["pack"](dev(w), n_in)
         call = lambda t: c["gemv"](wt, dev(x), dev(t), n_out)   # noqa: E731
+        rows = lambda t: c["rows"](dev(w), dev(x), dev(t))   # noqa: E731
         group = lambda t: c["group"]([(wt, dev(x), torch.empty(n_out, device=DEV))], dev(t))   # noqa: E731
         ref = lambda t: c["o_gemv"](w, t, x, n_in, n_out)   # noqa: E731
     bad = tab.copy()
     bad.reshape(-1)[5] = np.float32(2.0 + 2.0 ** -20)
     assert float(np.float16(bad.reshape(-1)[5])) != float(bad.reshape(-1)[5])
-    y = host(call(bad))
-    assert np.isnan(y).all(), f"{fmt}: {int((~np.isnan(y)).sum())} rows not NaN"
+    for f in (call, rows) if rows else (call,):
+        y = host(f(bad))
+        assert np.isnan(y).all(), f"{fmt}: {int((~np.isnan(y)).sum())} rows not NaN"
     with pytest.raises(qwg.QwgError) as e:
         group(bad)
     assert e.value.status == 9
     good = bad.copy()
     good.reshape(-1)[5] = np.float32(2.0)
     yr, sr = ref(good)
-    assert_bound(host(call(good)), yr, sr, f"{fmt} exact codebook")
+    for f in (call, rows) if rows else (call,):
+        assert_bound(host(f(good)), yr, sr, f"{fmt} exact codebook")
 
 
 # ---------------------------------------------------------------- IQ3 encoder
