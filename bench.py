@@ -34,7 +34,7 @@ the headline, in GB/s; roofline = the same bytes / the chain kernel's average
 duration from HIP events on its stream around the timed loop.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--headline-only]
-       python bench.py --workload iq3_stream|iq3_xxs|codebooks|encode|lm_head|batched [--steps K] [--warmup W]
+       python bench.py --workload iq3_stream|iq3_xxs|codebooks|encode|lm_head|batched|gemm_ab [--steps K] [--warmup W]
 The second form measures the other hot-path rows on their own (one JSON line each, for the
 record and for profiling): "iq3_stream" = the same 155 GEMV shapes in the IQ3 container as one
 grouped launch (IQ3 tile layout; the row-major launch beside it); "iq3_xxs" = IQ3_XXS blocks in
@@ -43,7 +43,10 @@ the same stream and single shapes in IQ3_S and IQ4_XS (tile layout); "encode" = 
 encoder on the IQ3 configuration's matrices (an ALU-bound roofline); "lm_head" = the 32000x2048 Q4_K
 LM head at batch 1..8 (qwg_gemv_q4k, qwg_gemv_q4k_tiled, qwg_gemm_q4k), cycling over enough weight
 copies that every launch streams from HBM rather than the last-level cache; "batched" = the
-per-token stream for 2, 4 and 8 sequences as one batched group launch.
+per-token stream for 2, 4 and 8 sequences as one batched group launch; "gemm_ab" = an A/B of
+the batched-GEMM engines (matrix-core pipeline with one or two columns per stage, the persistent
+matrix-core stream, the vector-ALU engine with 4, 8 or 16 wavefronts per tile, and the automatic
+choice) at batch 2..8 on the LM head and the layer shapes, cold weights.
 """
 from __future__ import annotations
 
@@ -97,7 +100,7 @@ def parse():
                     help="print the hash of the kernel sources the traffic figure is tied to")
     ap.add_argument("--workload", default="q4k_stream",
                     choices=["q4k_stream", "configs", "iq3_stream", "iq3_xxs", "codebooks", "encode",
-                             "lm_head", "batched"],
+                             "lm_head", "batched", "gemm_ab"],
                     help="q4k_stream: the headline (default); the others: see the module docstring")
     ap.add_argument("--headline-only", action="store_true",
                     help="run and time only the headline launch (no other schedules, no "
@@ -153,6 +156,9 @@ def main():
         return
     if args.workload == "batched":
         bench_batched(args)
+        return
+    if args.workload == "gemm_ab":
+        bench_gemm_ab(args)
         return
 
     import numpy as np
@@ -960,6 +966,59 @@ def bench_lm_head(args):
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "Q4_K LM head 2048->32000, cold weights (16 copies cycled)", **out,
                    "b8_TFLOPs": round(flops8 / b8 / 1e6, 2)},
+    }), flush=True)
+
+
+# Engines of qwg_gemm_q4k_ex by its `waves` argument (0: the automatic choice).
+GEMM_ENGINES = {"auto": 0, "mfma_1col": 1, "mfma_2col": 2, "mfma_stream": 3, "valu_4w": 4,
+                "valu_8w": 8, "valu_16w": 16}
+
+
+def bench_gemm_ab(args):
+    """Every batched-GEMM engine at batch 2..8 on the LM head and the layer
+    shapes (qwg_gemm_q4k_ex with the engine forced and its own automatic
+    splits), weights cycled over enough copies to stream from HBM."""
+    import torch
+    import quantized_weight_decode_gemv_amd as qwg
+    from quantized_weight_decode_gemv_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for n_out, n_in in ((32000, 2048), (2048, 2048), (5632, 2048), (2048, 5632)):
+        w = torch.from_numpy(synth.q4k_weights(n_out, n_in, 1, 0)).to(dev)
+        copies = max(2, (1 << 30) // w.numel())
+        W = w.reshape(1, -1).repeat(copies, 1)
+        nbytes = w.numel()
+        for batch in range(2, 9):
+            x = torch.from_numpy(synth.activations(n_in, 1, batch, batch=batch)).to(dev)
+            y = torch.empty(batch, n_out, device=dev)
+            row = {}
+            # three rounds over the engines, the least time of each (clock and
+            # ordering effects of one pass reach 1-2 us)
+            for _ in range(3):
+                for name, waves in GEMM_ENGINES.items():
+                    i = [0]
+
+                    def run():
+                        qwg.gemm_q4k(W[i[0] % copies].view(n_out, -1), x, out=y, waves=waves)
+                        i[0] += 1
+                    t = round(_event_us(run, stream, args.steps, args.warmup), 2)
+                    row[name] = min(row.get(name, t), t)
+            best = min((k for k in row if k != "auto"), key=row.get)
+            row["best"] = best
+            row["best_GBs"] = round((nbytes + 4 * batch * (n_in + n_out)) / row[best] / 1e3, 1)
+            out[f"{n_out}x{n_in}_b{batch}"] = row
+            print(f"# {n_out}x{n_in} b{batch} {row}", file=sys.stderr, flush=True)
+    lm8 = out["32000x2048_b8"]
+    print(json.dumps({
+        "metric": "batched Q4_K GEMM time per call by engine (us), batch 2..8", "value": lm8["auto"],
+        "unit": "us (LM head, batch 8, automatic engine)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": False, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "Q4_K GEMM (row-major weights, cold), LM head 32000x2048 and layer "
+                               "shapes 2048x2048, 5632x2048, 2048x5632, batch 2..8, every engine",
+                   **out},
     }), flush=True)
 
 

@@ -299,9 +299,12 @@ int qwg_gemm_q4k_noalloc(float *y, const float *x, const void *w, int64_t n_in, 
 /*
  * qwg_gemm_q4k with an explicit work decomposition (tuning and testing):
  * `waves` selects the engine: 4, 8 or 16 wavefronts per 64-row tile on the
- * vector ALUs; 1 or 2 = the matrix-core engine (batch >= 2 only) taking one
- * super-block column per stage with 4 wavefronts per tile, or two columns with
- * 8; 0 = automatic (matrix cores for batch >= 2); `splits`
+ * vector ALUs; 1 or 2 = the matrix-core pipeline (batch >= 2 only), one
+ * workgroup per (tile, split) taking one super-block column per stage with 4
+ * wavefronts, or two columns with 8; 3 = the persistent matrix-core stream
+ * (batch >= 2 only: resident workgroups walk the (tile, split) items with a
+ * ring of stages that runs ahead across them); 0 = automatic (the persistent
+ * stream for batch >= 2); `splits`
  * workgroups sharing each tile's n_in sum (1..n_in/256; 0 = automatic). The
  * result satisfies the same bound for every choice; the summation order (so
  * the rounding) depends on it. Returns QWG_ERR_SHAPE for an unsupported

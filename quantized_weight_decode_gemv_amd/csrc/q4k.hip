@@ -525,16 +525,18 @@ __global__ __launch_bounds__(256 * H) void q4k_mfma_kernel(GemvArgs a) {
     }
 }
 
-// Batched grouped launch on the matrix cores: one workgroup per 64-row tile of
-// every member (no splits; members of `batch` activation rows), the problem
-// found through the group's map with scalar loads, then the tile pipeline
-// above with a 2-stage ring.
+// Batched grouped launch on the matrix cores: one workgroup per position of the
+// group's work list (a 64-row tile of a member, or a hole; no splits; members
+// of `batch` activation rows), the problem and tile found through the list
+// with scalar loads, then the tile pipeline above with a 2-stage ring.
 template <int NB, int H, bool TL>
 __global__ __launch_bounds__(256 * H) void q4k_mfma_group_kernel(GroupArgs g) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const uint32_t pi = ((cu32_p)g.map)[blockIdx.x];
+    if (pi == kNoItem) return;   // a hole of the work list
     GemvArgs a;
-    load_args(a, (cargs_p)g.problems + ((cu32_p)g.map)[blockIdx.x]);
-    const int tile = blockIdx.x - a.wg_begin;
+    load_args(a, (cargs_p)g.problems + pi);
+    const int tile = g.tile != nullptr ? (int)((cu32_p)g.tile)[blockIdx.x] : blockIdx.x - a.wg_begin;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = H == 2 ? w >> 2 : 0;
     switch (w & 3) {
@@ -832,6 +834,240 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_num_sgpr(96))) void q
     }
 }
 
+// ------------------------------------------------------------------ batched stream on matrix cores
+//
+// Persistent form of the matrix-core pipeline above for 2 <= batch <= 8: a grid
+// of resident 4-wavefront workgroups walks the item list as the batch-1 stream
+// engine does (item k, k + gridDim.x, ...), and an R-slot ring of stages runs
+// ahead across item boundaries, so the copies of the next tile's columns are in
+// flight while a tile ends. A stage is one super-block column of the tile (the
+// 64 rows' blocks, 9216 B) and each wavefront's 64 activations of every batch
+// row (2 KB, laid out as above); the arithmetic per stage is the one above. A
+// tile's row sums meet in LDS over the stage slot just computed (not refilled
+// before the next barrier) and leave through tile_epilogue (SPLIT) or straight
+// stores.
+template <int R>
+struct MStreamCfg {
+    static constexpr int kSlot = kMfmaStage;                  // weights, then [wave] x slices
+    static constexpr int kLds = R * kSlot;
+};
+
+template <int G, int NB, int R, bool SPLIT>
+__device__ __forceinline__ void q4k_mstream(const GroupArgs &g, const GemvArgs &single, int nitems,
+                                            uint8_t *smem) {
+    static_assert(R >= 2 && R <= 4, "ring of two to four stages");
+    using C = MStreamCfg<R>;
+    const int lane = threadIdx.x & 63;
+    const int stride = gridDim.x;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+
+    // Weight copy lanes as in the pipeline above: chunk k = 64i + lane (i < 2,
+    // or lanes 0..15 for i = 2) of rows 16G..16G+15, LDS byte 2304G + 16k.
+    int crow[3], cpart[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int k = (i < 2 || lane < 16) ? 64 * i + lane : 128;
+        crow[i] = 16 * G + k / 9;
+        cpart[i] = 16 * (k % 9);
+    }
+    // Activation copy lanes: 16-byte granule t of this lane holds x[bt][256b +
+    // 64G + 4c .. +3] (batch rows past NB copy row 0 and are zeroed in A).
+    int xbt[2], xc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int sl = 64 * t + lane;
+        const int bt = sl & 7;
+        xbt[t] = bt < NB ? bt : 0;
+        xc[t] = 8 * ((sl >> 3) & 1) + (sl >> 4);
+    }
+
+    int kc = skip_holes(blockIdx.x, stride, nitems, g);
+    if (kc >= nitems) return;
+    Item c;
+    load_item<1, SPLIT>(c, kc, g, single);
+
+    int kd = kc, sd = 0, slot_d = 0, pending = 0;
+    Item d = c;
+    int64_t doff[3], xoff[2];
+    const uint8_t *dbase = nullptr;
+    int dstride = 0;
+    auto prep_copy = [&]() {
+        if (d.layout == kLayoutTiles) {
+            dbase = d.w + (int64_t)(d.row0 / kTileRows) * d.nb * kStageBytes;
+            dstride = kStageBytes;
+#pragma unroll
+            for (int i = 0; i < 3; ++i) doff[i] = (int64_t)crow[i] * kQ4kBytes + cpart[i];
+        } else {
+            dbase = d.w;
+            dstride = kQ4kBytes;
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+                doff[i] = (int64_t)min(d.row0 + crow[i], d.n_out - 1) * d.row_bytes + cpart[i];
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+            xoff[t] = 4 * ((int64_t)xbt[t] * d.nb * kQK + 64 * G + 4 * xc[t]);
+    };
+    prep_copy();
+    // Every stage is five copy instructions per wavefront (three of weights,
+    // two of activations), so waits count stages.
+    auto issue_next = [&]() {
+        if (kd >= nitems) return;
+        const int b = d.kb0 + sd;
+        const uint32_t base = lds0 + slot_d * C::kSlot;
+        const uint8_t *wb = dbase + (int64_t)b * dstride;
+        const uint32_t wdst = base + 2304 * G;
+        if (d.layout == kLayoutTiles) {
+            dma16_stream(wb + doff[0], wdst);
+            dma16_stream(wb + doff[1], wdst + 1024);
+            if (lane < 16) dma16_stream(wb + doff[2], wdst + 2048);
+        } else {
+            dma16(wb + doff[0], wdst);
+            dma16(wb + doff[1], wdst + 1024);
+            if (lane < 16) dma16(wb + doff[2], wdst + 2048);
+        }
+        const uint8_t *xb = (const uint8_t *)d.x + (int64_t)(kQK * 4) * b;
+        const uint32_t xdst = base + kStageBytes + kXSlice * G;
+        dma16(xb + xoff[0], xdst);
+        dma16(xb + xoff[1], xdst + 1024);
+        ++pending;
+        slot_d = slot_d + 1 == R ? 0 : slot_d + 1;
+        if (++sd == d.nst) {
+            sd = 0;
+            kd = skip_holes(kd + stride, stride, nitems, g);
+            if (kd < nitems) {
+                load_item<1, SPLIT>(d, kd, g, single);
+                prep_copy();
+            }
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) issue_next();
+
+    // A-operand role of this lane and its activation slots; C role (as above)
+    const int am = lane & 15;
+    const int kg = lane >> 4;
+    const bool alive = (am & 7) < NB;
+    const uint32_t xslot0 = 16u * (2 * kg) + 8u * (am >> 3) + (am & 7);
+    const int n = lane & 15;
+    const bool upper = lane >= 32;
+    const uint32_t mask = opaque(0x00780078u);
+    const uint32_t bias = opaque(0x41804180u);
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    int slot_c = 0;
+    for (;;) {
+        f32x4_t acc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = zero4;
+        int last = slot_c;
+        for (int s = 0; s < c.nst; ++s) {
+            // copies of the stages issued after this one may stay in flight
+            wait_stage_copies(pending - 1);
+            lds_barrier();   // stage in slot_c complete for every wavefront
+            issue_next();    // refill the slot computed in the previous step
+            const uint8_t *stage = smem + slot_c * C::kSlot;
+            // Every LDS read of the step first, then one wait: the headers and
+            // quant bytes of this lane's four rows (16q + n) and its
+            // activation slots. Each lane decodes the scales of its own rows
+            // and sub-block (no round trip through LDS to share them).
+            uint4 hd[4];
+            uint2 e[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint8_t *rowp = stage + (16 * q + n) * kQ4kBytes;
+                hd[q] = *(const uint4 *)rowp;
+                e[q] = *(const uint2 *)(rowp + 16 + 32 * G + 8 * kg);
+            }
+            const float *xs = (const float *)(stage + kStageBytes + kXSlice * G);
+            const float4 x0 = *(const float4 *)(xs + 4 * xslot0);
+            const float4 x1 = *(const float4 *)(xs + 4 * (xslot0 + 16));
+            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            u32x4_t ah, am_, al;
+            split_x(xv, alive, ah, am_, al);
+            f32x4_t sx = mfma_bf16(ah, ones, zero4);
+            sx = mfma_bf16(am_, ones, sx);
+            sx = mfma_bf16(al, ones, sx);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x4_t b_lo, b_hi;
+                q4k_bf16_quants(e[q], mask, bias, b_lo, b_hi);
+                f32x4_t c1 = mfma_bf16(ah, b_lo, zero4);
+                c1 = mfma_bf16(am_, b_lo, c1);
+                c1 = mfma_bf16(al, b_lo, c1);
+                f32x4_t c2 = mfma_bf16(ah, b_hi, zero4);
+                c2 = mfma_bf16(am_, b_hi, c2);
+                c2 = mfma_bf16(al, b_hi, c2);
+                uint32_t sc0, sc1, mn0, mn1;
+                q4k_scales<G>(hd[q], sc0, sc1, mn0, mn1);
+                const float dsc = h2f_lo(hd[q].x) * (float)(upper ? sc1 : sc0);
+                const float off =
+                    __builtin_fmaf(h2f_hi(hd[q].x), (float)(upper ? mn1 : mn0), 16.0f * dsc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float cv = upper ? c2[i] : c1[i];
+                    const float v = __builtin_fmaf(dsc, cv, acc[q][i]);
+                    acc[q][i] = __builtin_fmaf(-off, sx[i], v);
+                }
+            }
+            --pending;
+            last = slot_c;
+            slot_c = slot_c + 1 == R ? 0 : slot_c + 1;
+        }
+        // Sub-blocks 2G and 2G+1 (lanes l and l^32), then the wavefronts in
+        // order, through the slot just computed: every wavefront is past its
+        // reads, and it is refilled only after the next barrier.
+        lds_barrier();
+        float *red = (float *)(smem + last * C::kSlot);   // [wave][batch 8][row 64]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = acc[q][i] + __shfl_xor(acc[q][i], 32);
+                const int bt = 4 * (kg & 1) + i;
+                if (!upper && bt < NB) red[(G * 8 + bt) * 64 + 16 * q + n] = v;
+            }
+        }
+        lds_barrier();
+        if (G == 0) {
+            float total[NB];
+#pragma unroll
+            for (int bt = 0; bt < NB; ++bt) {
+                float t = red[bt * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < 4; ++w) t += red[(w * 8 + bt) * 64 + lane];
+                total[bt] = t;
+            }
+            if (SPLIT) {
+                GemvArgs ea;
+                if (c.prob >= 0)
+                    load_args(ea, (cargs_p)g.problems + c.prob);
+                else
+                    ea = single;
+                tile_epilogue<NB>(ea, c.row0 / kTileRows, c.split, total);
+            } else if (c.row0 + lane < c.n_out) {
+#pragma unroll
+                for (int bt = 0; bt < NB; ++bt) c.y[(int64_t)bt * c.n_out + c.row0 + lane] = total[bt];
+            }
+        }
+        kc = skip_holes(kc + stride, stride, nitems, g);
+        if (kc >= nitems) break;
+        load_item<1, SPLIT>(c, kc, g, single);
+    }
+}
+
+template <int NB, int R, bool SPLIT>
+__global__ __launch_bounds__(256) void q4k_mstream_kernel(GroupArgs g, GemvArgs single, int nitems) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    switch (__builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3)) {
+        case 0: q4k_mstream<0, NB, R, SPLIT>(g, single, nitems, smem); break;
+        case 1: q4k_mstream<1, NB, R, SPLIT>(g, single, nitems, smem); break;
+        case 2: q4k_mstream<2, NB, R, SPLIT>(g, single, nitems, smem); break;
+        default: q4k_mstream<3, NB, R, SPLIT>(g, single, nitems, smem); break;
+    }
+}
+
 template <int W>
 size_t q4k_lds_bytes(int batch, int max_blk) {
     const int sxb = ((512 / batch) / (W / 4)) * (W / 4);
@@ -991,6 +1227,69 @@ hipError_t launch_q4k_mfma_group(const GroupArgs &g, int nwg, int batch, int col
                          : launch_mfma_group_h<1, true>(g, nwg, batch, s);
     return cols == 2 ? launch_mfma_group_h<2, false>(g, nwg, batch, s)
                      : launch_mfma_group_h<1, false>(g, nwg, batch, s);
+}
+
+// Resident workgroups of the batched matrix-core stream (ring R) on the current
+// device, queried once per process.
+template <int R>
+int mstream_slots_r() {
+    static const int slots = [] {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, q4k_mstream_kernel<8, R, true>,
+                                                         256, MStreamCfg<R>::kLds) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        return per_cu * cus;
+    }();
+    return slots;
+}
+
+int q4k_mstream_slots(int ring) {
+    switch (ring) {
+        case 2: return mstream_slots_r<2>();
+        case 3: return mstream_slots_r<3>();
+        case 4: return mstream_slots_r<4>();
+        default: return 0;
+    }
+}
+
+template <int R, bool SPLIT>
+hipError_t launch_mstream_rs(const GroupArgs &g, const GemvArgs &single, int nitems, int batch,
+                             hipStream_t s) {
+    int n = mstream_slots_r<R>();
+    if (n > nitems) n = nitems;
+    const dim3 grid((unsigned)n), block(256);
+    const size_t lds = MStreamCfg<R>::kLds;
+    switch (batch) {
+#define QWG_MSTREAM_CASE(nb)                                                                     \
+    case nb:                                                                                     \
+        hipLaunchKernelGGL((q4k_mstream_kernel<nb, R, SPLIT>), grid, block, lds, s, g, single,   \
+                           nitems);                                                              \
+        break;
+        QWG_MSTREAM_CASE(2) QWG_MSTREAM_CASE(3) QWG_MSTREAM_CASE(4) QWG_MSTREAM_CASE(5)
+        QWG_MSTREAM_CASE(6) QWG_MSTREAM_CASE(7) QWG_MSTREAM_CASE(8)
+#undef QWG_MSTREAM_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_mstream(const GroupArgs &g, const GemvArgs &single, int nitems, int batch,
+                              int ring, bool split, hipStream_t s) {
+    if (nitems < 1) return hipErrorInvalidValue;
+    switch (ring * 2 + (split ? 1 : 0)) {
+        case 4: return launch_mstream_rs<2, false>(g, single, nitems, batch, s);
+        case 5: return launch_mstream_rs<2, true>(g, single, nitems, batch, s);
+        case 6: return launch_mstream_rs<3, false>(g, single, nitems, batch, s);
+        case 7: return launch_mstream_rs<3, true>(g, single, nitems, batch, s);
+        case 8: return launch_mstream_rs<4, false>(g, single, nitems, batch, s);
+        case 9: return launch_mstream_rs<4, true>(g, single, nitems, batch, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 int q4k_stream_residency(int waves, int ring, int *cus) {

@@ -93,10 +93,59 @@ int mfma_splits(int tiles, int nb, int batch) {
     return s;
 }
 
-// waves arguments of qwg_gemm_q4k_ex that select the matrix-core engine with
-// one or two super-block columns per stage
+// Batch-2 GEMMs of at least this many 64-row tiles run on the vector ALUs.
+constexpr int kValuBatch2Tiles = 256;
+
+// waves arguments of qwg_gemm_q4k_ex that select the matrix-core engines: the
+// one-workgroup-per-tile pipeline with one or two super-block columns per
+// stage, or the persistent batched stream
 constexpr int kWavesMfma = 1;
 constexpr int kWavesMfma2 = 2;
+constexpr int kWavesMstream = 3;
+
+// Batch 2..8 runs on the one-workgroup-per-tile pipeline (q4k_mfma_kernel /
+// q4k_mfma_group_kernel) unless QWG_MFMA_ENGINE=1 selects the persistent
+// batched stream (q4k_mstream_kernel) for every call and group (A/B tuning).
+// Measured A/B (cold weights, us, per-tile pipeline / persistent stream): LM
+// head 32000 x 2048 at batch 8 15.1-16.7 / 15.8 (whole rows, 2-stage ring;
+// 17-33 with split rows); 5632 x 2048 9.3-9.6 / 9.5-11; 2048 x 5632 11.6 /
+// 11.2-24 (by splits); the 155-product batched stream at batch 8 180 / 192.
+// The stream's ring hides no more than the pipeline already does: each stage
+// is a long chain of dependent LDS, MFMA and ALU steps, and both engines issue
+// the same 27 MFMAs and ~200-260 vector instructions per stage and wavefront.
+bool mfma_tile_engine() {
+    static const int v = env_int("QWG_MFMA_ENGINE", 0);
+    return v != 1;
+}
+
+// Ring stages of the batched stream (QWG_MSTREAM_RING overrides, tuning):
+// two, measured best (more workgroups per CU; LM head at batch 8 15.8 us with
+// two stages, 17.0 with three, 17.7 with four).
+int mstream_ring() {
+    static const int v = [] {
+        const int r = env_int("QWG_MSTREAM_RING", 2);
+        return r >= 2 && r <= 4 ? r : 2;
+    }();
+    return v;
+}
+
+// Splits of a single batched-stream GEMM: about one item per compute unit
+// (split rows end in an epilogue round trip per item), at most one split per
+// super-block, partial sums inside the workspace. Measured (us, by splits):
+// LM head (500 tiles) 1: 15.8, 2: 17.9; 5632 x 2048 (88 tiles) 1: 11.1, 2-4:
+// 9.7; 2048 x 5632 (32 tiles) 1: 24.1, 4: 11.8, 6: 11.2 (QWG_MSTREAM_SPLITS
+// overrides, tuning).
+int mstream_splits(int tiles, int nb, int batch, int slots) {
+    static const int env = env_int("QWG_MSTREAM_SPLITS", 0);
+    (void)slots;
+    int s = env > 0 ? env : (256 + tiles - 1) / tiles;
+    if (s > nb) s = nb;
+    if (s < 1) s = 1;
+    while (s > 1 && ((size_t)s * batch * tiles * kTileRows > kWsPartialFloats ||
+                     (size_t)tiles > kWsCounters))
+        --s;
+    return s;
+}
 
 // Ring stages of the matrix-core engine. Measured (LM head, batch 8, one
 // split): 2 stages 17.0 us, 3 stages 17.6 us, 4 stages 18.5 us; deeper rings
@@ -480,13 +529,25 @@ int gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_ou
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
     GemvArgs a;
     fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
+    // Engine: the vector ALUs for batch 1, and for batch 2 on a matrix of many
+    // tiles (8 wavefronts per tile; measured on the LM head, 500 tiles, cold
+    // weights: 12.4 us against 14.2-15.8 us on the matrix cores, while on the
+    // layer shapes of 32-88 tiles and at batch 3..8 the matrix cores win or
+    // tie: bench.py --workload gemm_ab); otherwise the matrix cores.
+    const bool valu = batch == 1 || (batch == 2 && a.tiles >= kValuBatch2Tiles);
+    const bool mstream = !valu && !mfma_tile_engine();
+    const int ring = mstream_ring();
     int waves = kQ4kWavesSmall;
-    if (batch >= 2) {
-        a.splits = mfma_splits(a.tiles, a.nb, batch);
-    } else {
+    if (valu) {
         const Plan plan = choose_plan(a.tiles, a.nb, batch);
         a.splits = plan.splits;
-        waves = plan.waves;
+        waves = batch == 1 ? plan.waves : 8;
+    } else if (mstream) {
+        const int slots = q4k_mstream_slots(ring);
+        if (slots <= 0) return QWG_ERR_HIP;
+        a.splits = mstream_splits(a.tiles, a.nb, batch, slots);
+    } else {
+        a.splits = mfma_splits(a.tiles, a.nb, batch);
     }
     if (a.splits > 1) {
         Workspace ws;
@@ -502,8 +563,13 @@ int gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_ou
         a.partial = ws.partial;
         a.counters = ws.counters;
     }
-    if (batch >= 2) return hip_status(launch_mfma(a, batch, stream));
-    if (a.splits == 1 && use_stream_engine()) {
+    if (mstream) {
+        const GroupArgs none = {nullptr, nullptr, nullptr};
+        return hip_status(launch_q4k_mstream(none, a, a.tiles * a.splits, batch, ring, a.splits > 1,
+                                             stream));
+    }
+    if (!valu) return hip_status(launch_mfma(a, batch, stream));
+    if (batch == 1 && a.splits == 1 && use_stream_engine()) {
         const StreamShape sh = stream_shape(false);
         const GroupArgs none = {nullptr, nullptr, nullptr};
         return hip_status(launch_q4k_stream(none, a, a.tiles, sh.waves, sh.ring, false, stream));
@@ -534,12 +600,23 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
     if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4)) return QWG_ERR_ALIGN;
     GemvArgs a;
     fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
-    const bool mfma = waves == kWavesMfma || waves == kWavesMfma2 || (waves == 0 && batch >= 2);
-    if (mfma && batch < 2) return QWG_ERR_SHAPE;
+    const int ring = mstream_ring();
+    const bool mstream = waves == kWavesMstream || (waves == 0 && batch >= 2 && !mfma_tile_engine());
+    const bool mfma = !mstream && (waves == kWavesMfma || waves == kWavesMfma2 ||
+                                   (waves == 0 && batch >= 2));
+    if ((mfma || mstream) && batch < 2) return QWG_ERR_SHAPE;
     const Plan autoplan = choose_plan(a.tiles, a.nb, batch);
-    if (splits == 0) splits = mfma ? mfma_splits(a.tiles, a.nb, batch) : autoplan.splits;
+    if (splits == 0) {
+        if (mstream) {
+            const int slots = q4k_mstream_slots(ring);
+            if (slots <= 0) return QWG_ERR_HIP;
+            splits = mstream_splits(a.tiles, a.nb, batch, slots);
+        } else {
+            splits = mfma ? mfma_splits(a.tiles, a.nb, batch) : autoplan.splits;
+        }
+    }
     if (waves == 0 && !mfma) waves = autoplan.waves;
-    if (!mfma && waves != 4 && waves != 8 && waves != 16) return QWG_ERR_SHAPE;
+    if (!mfma && !mstream && waves != 4 && waves != 8 && waves != 16) return QWG_ERR_SHAPE;
     if (splits < 1 || splits > a.nb) return QWG_ERR_SHAPE;
     if (splits > 1 && ((size_t)splits * batch * a.tiles * kTileRows > kWsPartialFloats ||
                        (size_t)a.tiles > kWsCounters))
@@ -551,6 +628,11 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
         if (rc) return rc;
         a.partial = ws.partial;
         a.counters = ws.counters;
+    }
+    if (mstream) {
+        const GroupArgs none = {nullptr, nullptr, nullptr};
+        return hip_status(launch_q4k_mstream(none, a, a.tiles * a.splits, batch, ring, a.splits > 1,
+                                             (hipStream_t)stream));
     }
     if (mfma) return hip_status(launch_mfma(a, batch, (hipStream_t)stream, waves));
     return hip_status(launch_q4k_gemv(a, batch, waves, (hipStream_t)stream));
@@ -588,13 +670,26 @@ int qwg_gemm_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, in
     GemvArgs a;
     fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
     a.layout = kLayoutTiles;
-    a.splits = mfma_splits(a.tiles, a.nb, batch);
+    const bool mstream = !mfma_tile_engine();
+    const int ring = mstream_ring();
+    if (mstream) {
+        const int slots = q4k_mstream_slots(ring);
+        if (slots <= 0) return QWG_ERR_HIP;
+        a.splits = mstream_splits(a.tiles, a.nb, batch, slots);
+    } else {
+        a.splits = mfma_splits(a.tiles, a.nb, batch);
+    }
     if (a.splits > 1) {
         Workspace ws;
         const int wrc = get_workspace((hipStream_t)stream, &ws);
         if (wrc) return wrc;
         a.partial = ws.partial;
         a.counters = ws.counters;
+    }
+    if (mstream) {
+        const GroupArgs none = {nullptr, nullptr, nullptr};
+        return hip_status(launch_q4k_mstream(none, a, a.tiles * a.splits, batch, ring, a.splits > 1,
+                                             (hipStream_t)stream));
     }
     return hip_status(launch_mfma(a, batch, (hipStream_t)stream, 0, true));
 }
@@ -824,6 +919,7 @@ struct qwg_group {
     bool split;           // some member splits its rows' sums
     int waves, ring;      // Q4_K stream engine shape of the launch
     int cb_shape;         // IQ3_S / IQ4_XS engine shape of the launch (10 * waves + ring)
+    int mring;            // batched: ring stages of the persistent stream (0: per-tile pipeline)
     int batch;            // activation rows per member (2..8: the matrix-core engine)
     int cols;             // its super-block columns per stage
 };
@@ -936,6 +1032,40 @@ int check_codebook(int fmt, const float *grid) {
     return QWG_OK;
 }
 
+// Work list of a batched group. Workgroup b runs on XCD b % 8 (workgroups are
+// dispatched round-robin over the eight XCDs, each with its own L2) and takes
+// position b (one workgroup per position) or, on the persistent stream whose
+// grid is a multiple of 8, positions b, b + n, ...: always positions
+// 8j + b % 8. Each XCD gets a contiguous run of the
+// member-major item list holding about an eighth of the weight bytes, so a
+// member's activations (up to 8 x 22 KB per member) are fetched into one or
+// two L2s rather than all eight; within a run, members keep the longest-rows-
+// first order. Shorter runs end in holes (kNoItem).
+void xcd_schedule(const std::vector<GemvArgs> &probs, const std::vector<int> &order,
+                  std::vector<uint32_t> &map, std::vector<uint32_t> &tile) {
+    int64_t total = 0;
+    for (int i : order) total += (int64_t)probs[i].tiles * probs[i].nb;
+    std::vector<std::vector<std::pair<uint32_t, uint32_t>>> run(8);
+    int64_t cum = 0;
+    for (int i : order) {
+        for (int t = 0; t < probs[i].tiles; ++t) {
+            const int64_t mid2 = 2 * cum + probs[i].nb;   // twice the item's cost midpoint
+            const int x = (int)std::min<int64_t>(7, mid2 * 8 / (2 * std::max<int64_t>(total, 1)));
+            run[(size_t)x].push_back({(uint32_t)i, (uint32_t)t});
+            cum += probs[i].nb;
+        }
+    }
+    size_t len = 0;
+    for (const auto &r : run) len = std::max(len, r.size());
+    map.assign(8 * len, kNoItem);
+    tile.assign(8 * len, 0u);
+    for (size_t x = 0; x < 8; ++x)
+        for (size_t j = 0; j < run[x].size(); ++j) {
+            map[8 * j + x] = run[x][j].first;
+            tile[8 * j + x] = run[x][j].second;
+        }
+}
+
 int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, const float *grid,
                  qwg_group **out, int batch = 1) {
     const bool cb = codebook_format(fmt);
@@ -1033,7 +1163,11 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     // stream (two workgroups per CU) the balanced schedule ran 126 us against
     // 114 us, and any age skew only slowed it further.
     std::vector<uint32_t> map, tile;
-    if (stream) {
+    const bool mstream = batched && !mfma_tile_engine();
+    static const int env_xcd = env_int("QWG_XCD_MAP", 1);   // 0: plain list (A/B tuning)
+    if (batched && env_xcd) {
+        xcd_schedule(probs, order, map, tile);
+    } else if (stream) {
         static const double skew = skew_env("QWG_STREAM_SKEW", kAgeSkew);
         stream_schedule(probs, order, items, per_cu, cus, skew, map, tile);
     } else {
@@ -1091,6 +1225,7 @@ int group_create(int fmt, int layout, const qwg_gemv_desc *descs, int count, con
     g->waves = ssh.waves;
     g->ring = ssh.ring;
     g->cb_shape = cb_shape;
+    g->mring = mstream ? mstream_ring() : 0;
     g->batch = batch;
     // One column per stage: a group has thousands of workgroups, and the
     // 8-wavefront two-column shape that helps short single launches measured
@@ -1195,9 +1330,12 @@ int qwg_group_run(const qwg_group *g, void *stream) {
     if (!g) return QWG_ERR_NULL;
     GemvArgs unused;
     fill_shape(unused, nullptr, nullptr, nullptr, nullptr, kQK, 1, kQ4kBytes);
+    if (g->batch >= 2 && g->mring)
+        return hip_status(launch_q4k_mstream(g->args, unused, g->positions, g->batch, g->mring,
+                                             false, (hipStream_t)stream));
     if (g->batch >= 2)
         return hip_status(
-            launch_q4k_mfma_group(g->args, g->workgroups, g->batch, g->cols,
+            launch_q4k_mfma_group(g->args, g->positions, g->batch, g->cols,
                                   g->layout == kLayoutTiles, (hipStream_t)stream));
     if (codebook_format(g->fmt))
         return hip_status(launch_cb_stream(g->fmt, g->layout == kLayoutTiles, g->cb_shape,

@@ -97,6 +97,13 @@ hipError_t launch_q4k_stream(const GroupArgs &g, const GemvArgs &single, int nit
 // (the launch grid is their product, capped by the item count); 0 if the
 // variant does not exist.
 int q4k_stream_residency(int waves, int ring, int *cus);
+// Batched (2..8) persistent stream on the matrix cores: items of `single` (no
+// group) or of a group's work list, an LDS ring of `ring` (2..4) stages across
+// items; split: items may cover part of a row (partial sums meet through the
+// problem's workspace).
+int q4k_mstream_slots(int ring);
+hipError_t launch_q4k_mstream(const GroupArgs &g, const GemvArgs &single, int nitems, int batch,
+                              int ring, bool split, hipStream_t s);
 
 // IQ3 stream engine shape: wavefronts per workgroup (4, 8, 16) and LDS ring
 // stages (2, 3; 4 with 4 wavefronts).

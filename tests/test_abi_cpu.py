@@ -131,7 +131,9 @@ FAKE = 0x10000  # never dereferenced: every call below fails validation first
     (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE + 4, FAKE, 256, 1, 1, 4, 1, None), 3),
     # matrix-core engine (waves = 1) needs batch >= 2; other wave counts are invalid
     (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 256, 1, 1, 1, 1, None), 2),
-    (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 256, 1, 2, 3, 1, None), 2),
+    (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 256, 1, 2, 5, 1, None), 2),
+    (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 256, 1, 1, 3, 1, None), 2),   # stream: batch >= 2
+    (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 512, 1, 2, 3, 3, None), 2),
     (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 512, 1, 2, 1, 3, None), 2),
     (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 256, 1, 1, 2, 1, None), 2),
     (lambda L: L.qwg_gemm_q4k_ex(FAKE, FAKE, FAKE, 512, 1, 2, 2, 3, None), 2),

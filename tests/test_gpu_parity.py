@@ -493,7 +493,75 @@ def test_gemm_q4k_mfma_one_hot_columns():
             assert np.array_equal(Y[b], deq[:, k]), f"column {k} waves {waves} splits {splits}"
 
 
+@pytest.mark.parametrize("batch", [2, 3, 5, 8])
+@pytest.mark.parametrize("n_out,n_in", [(333, 1536), (64, 256), (130, 5632), (1, 512), (700, 2048)])
+def test_gemm_q4k_mstream_every_split(batch, n_out, n_in):
+    # the persistent matrix-core stream (waves=3): whole rows and split ranges
+    # (two, three: 7/7/8-style uneven ranges, and one super-block each)
+    w, _ = _gemv_q4k_case(n_out, n_in, 109, batch)
+    X = synth.activations(n_in, 109, 70 + batch, batch=batch)
+    Yr, Sr = oracle.gemm_q4k(w, X, n_in, n_out)
+    wd, xd = dev(w), dev(X)
+    nb = n_in // 256
+    for splits in sorted({1, 2, 3, nb} & set(range(1, nb + 1))):
+        out = torch.full((batch, n_out), float("nan"), device=DEV)
+        Y = host(qwg.gemm_q4k(wd, xd, out=out, waves=3, splits=splits)).copy()
+        assert_bound(Y, Yr, Sr, f"mstream batch {batch} splits {splits}")
+        assert_bits(host(qwg.gemm_q4k(wd, xd, waves=3, splits=splits)), Y, "mstream rerun")
+    # whole rows: the same sums in the same order as the per-tile pipeline
+    assert_bits(host(qwg.gemm_q4k(wd, xd, waves=3, splits=1)),
+                host(qwg.gemm_q4k(wd, xd, waves=1, splits=1)), "mstream vs per-tile pipeline")
+
+
+@pytest.mark.parametrize("batch", [2, 6, 8])
+def test_gemm_q4k_mstream_integer_exact(batch):
+    n_out, n_in = 190, 5632
+    w = _integer_q4k(n_out, n_in, 40 + batch)
+    X = np.random.default_rng(40 + batch).integers(-8, 9, (batch, n_in)).astype(np.float32)
+    Yr, _ = oracle.gemm_q4k(w, X, n_in, n_out)
+    for splits in (1, 3, 22):
+        Y = host(qwg.gemm_q4k(dev(w), dev(X), waves=3, splits=splits))
+        assert np.array_equal(Y.astype(np.float64), Yr), f"splits {splits}"
+
+
+def test_gemm_q4k_batch2_many_tiles_runs_on_the_vector_alus():
+    # batch 2 with >= 256 tiles takes the vector-ALU engine (8 wavefronts per tile)
+    p = synth.config(3)[1]
+    w = synth.weights(p)
+    X = synth.activations(p.n_in, 3, 2, batch=2)
+    wd, xd = dev(w), dev(X)
+    Y = host(qwg.gemm_q4k(wd, xd)).copy()
+    Yr, Sr = oracle.gemm_q4k(w, X, p.n_in, p.n_out)
+    assert_bound(Y, Yr, Sr, "lm_head b2")
+    assert_bits(host(qwg.gemm_q4k(wd, xd, waves=8)), Y, "the vector-ALU engine's result")
+
+
+def test_gemm_q4k_lm_head_b8_tiled_all_rows():
+    p = synth.config(3)[1]
+    w, X = synth.weights(p), synth.inputs(p)
+    out = torch.full((8, p.n_out), float("nan"), device=DEV)
+    qwg.gemm_q4k_tiled(qwg.pack_q4k_tiles(dev(w), p.n_in), dev(X), p.n_out, out=out)
+    Yr, Sr = oracle.gemm_q4k(w, X, p.n_in, p.n_out)
+    assert_bound(host(out), Yr, Sr, "lm_head b8 tiled")
+
+
 # ---------------------------------------------------------------- batched groups (matrix cores)
+
+def test_batched_group_c5_stream_all_rows():
+    # the per-token stream's 155 products for 8 sequences, tile layout, as the
+    # batched bench runs them (XCD-ordered work list); every row of every member
+    probs = synth.config(5)
+    ws = [synth.weights(p) for p in probs]
+    Xs = [synth.activations(p.n_in, 5, k, batch=8) for k, p in enumerate(probs)]
+    WT = [qwg.pack_q4k_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
+    Y = [torch.full((8, p.n_out), float("nan"), device=DEV) for p in probs]
+    g = qwg.Q4kBatchedGroup(zip(WT, [dev(x) for x in Xs], Y), tiled=True)
+    g.run()
+    for p, w, x, y in zip(probs, ws, Xs, Y):
+        Yr, Sr = oracle.gemm_q4k(w, x, p.n_in, p.n_out)
+        assert_bound(host(y), Yr, Sr, f"batched stream {p.name}")
+    g.close()
+
 
 BATCHED_SHAPES = [(333, 1536), (64, 256), (130, 5632), (1, 512), (2000, 2048), (65, 768)]
 
