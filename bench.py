@@ -173,7 +173,9 @@ def main():
 
     probs = synth.config(5)
     t0 = time.time()
-    host_w = [synth.weights(p) for p in probs]
+    # Weights whose chained products keep their norms (the chain feeds each
+    # product's output to the next); the other schedules use the same weights.
+    host_w = [synth.q4k_chain_weights(p.n_out, p.n_in, p.cfg, p.tensor) for p in probs]
     host_x = [synth.inputs(p) for p in probs]
     W = [torch.from_numpy(w).to(dev) for w in host_w]
     X = [torch.from_numpy(x).to(dev) for x in host_x]
@@ -192,7 +194,11 @@ def main():
     # Every schedule writes its own outputs, so each can be checked on its own.
     Y = {name: outputs() for name in ("chain", "layered", "per_call", "grouped_independent",
                                       "grouped_independent_row_major")}
-    chain = qwg.Q4kChain([[(WT[i], X[i], Y["chain"][i]) for i in ph] for ph in phases])
+    # The chain as a decode step: each product reads the output of the product
+    # that stands in for its input (layer 0's q, k, v read the step input).
+    src = synth.chain_sources(probs)
+    XC = [X[0] if j < 0 else Y["chain"][j] for j in src]
+    chain = qwg.Q4kChain([[(WT[i], XC[i], Y["chain"][i]) for i in ph] for ph in phases])
     layered = [qwg.Q4kGroup([(WT[i], X[i], Y["layered"][i]) for i in ph], tiled=True)
                for ph in phases]
     calls = [(y.data_ptr(), x.data_ptr(), w.data_ptr(), p.n_in, p.n_out)
@@ -230,12 +236,14 @@ def main():
     torch.cuda.synchronize()
     chain.status()
     gpu_out = {name: [y.cpu().numpy() for y in Y[name]] for name in runners}
+    # the chain's actual inputs: the step input, or the producer's output
+    chain_in = [host_x[0] if j < 0 else gpu_out["chain"][j] for j in src]
     per_config_gpu = None if args.headline_only else run_configs(dev, stream, args)
 
     parity, cpu, per_config = None, None, None
     if not args.no_cpu:
         cpu, parity, per_config = cpu_baseline_leg(probs, host_w, host_x, gpu_out, per_config_gpu,
-                                                   args.cpu_seconds)
+                                                   args.cpu_seconds, inputs={"chain": chain_in})
 
     def graph_of(fn, outs):
         """fn(stream) captured once in a HIP graph on a side stream (after one
@@ -334,7 +342,9 @@ def main():
     value = step_bytes / sec / 1e9
     achieved = step_bytes / (kernel_ms * 1e-3) / 1e9
     schedules["chain"] = sched(sec, 1, True, kernel_us=round(1e3 * kernel_ms, 2),
-                               phases=chain.launch_phases)
+                               phases=chain.launch_phases,
+                               waits="tagged done words" if chain.tagged else "flag barriers",
+                               inputs="each product reads its producer's output")
 
     result = {
         "metric": "effective HBM GB/s (% of MI355X peak) for Q4_K/IQ3 GEMV, batch 1",
@@ -353,8 +363,12 @@ def main():
             "workload": "TinyLlama-1.1B Q4_K per-token weight stream, batch 1: 22 layers x "
                         "(q,o 2048x2048; k,v 256x2048; gate,up 5632x2048; down 2048x5632) + "
                         "LM head 32000x2048 = 155 GEMVs in the dependency order of a decode step "
-                        "(per layer q|k|v, o, gate|up, down; then the LM head: 89 phases), one "
-                        "layer-chain launch (qwg_chain_run), weights in tile-major order",
+                        "(per layer q|k|v, o, gate|up, down; then the LM head: 89 phases, each "
+                        "starting when every tile of the phase before it is finished), each "
+                        "product reading the output of the product standing in for its input "
+                        "(q|k|v the previous layer's down, o q, gate|up o, down gate, the LM head "
+                        "the last down), one layer-chain launch (qwg_chain_run), weights in "
+                        "tile-major order",
             "layout": "tile-major Q4_K (qwg_pack_q4k_tiles, repacked once before timing)",
             "weight_bytes": weight_bytes,
             "algorithmic_bytes_per_step": step_bytes,
@@ -536,7 +550,8 @@ def cpu_info():
             "cpus_online": os.cpu_count()}
 
 
-def cpu_baseline_leg(probs, host_w, host_x, gpu_out, per_config_gpu, budget_s, configs_only=False):
+def cpu_baseline_leg(probs, host_w, host_x, gpu_out, per_config_gpu, budget_s, configs_only=False,
+                     inputs=None):
     """Everything that runs the oracle (plain C, fp64 dot, OpenMP over rows):
     (1) the full oracle result of the per-token stream, against which every row
     of every schedule's GPU output is checked (the bench stops if any row is
@@ -555,7 +570,11 @@ def cpu_baseline_leg(probs, host_w, host_x, gpu_out, per_config_gpu, budget_s, c
                                    for p, w, x in zip(probs, host_w, host_x)]
     for name, outs in gpu_out.items():
         worst = 0.0
-        for (yr, sr), yg in zip(ref, outs):
+        mine = ref
+        if inputs and name in inputs:   # a schedule with its own inputs (the chained stream)
+            mine = [oracle.gemv_q4k(w, np.ascontiguousarray(x), p.n_in, p.n_out)
+                    for p, w, x in zip(probs, host_w, inputs[name])]
+        for (yr, sr), yg in zip(mine, outs):
             d = np.abs(yg.astype(np.float64) - yr)
             worst = max(worst, float(np.max(np.where(np.isnan(d), np.inf, d) / np.maximum(sr, 1e-300))))
         parity[name] = worst

@@ -456,6 +456,19 @@ int qwg_group_destroy(qwg_group *group);
  * has stored its result. Weights do not depend on activations and are
  * fetched ahead across phases.
  *
+ * How the phases wait (chosen at creation): tagged, when every x that
+ * overlaps a y of the chain lies wholly inside the y of one member of an
+ * earlier phase, no two members' y overlap and no y overlaps the x of a member
+ * of an earlier phase (nothing is overwritten that an earlier phase reads):
+ * the unit that finishes a tile of a phase stores a tagged done word (8
+ * bytes: the tile's sum of squares of y, and the run's tag for that phase),
+ * a member whose y a later member reads also stores its rows as tagged
+ * 8-byte words, and a phase waits until it has loaded the done words of every
+ * tile of the phase before it with this run's tag, reading activations made
+ * by the chain as tagged words. Otherwise (or with QWG_CHAIN_TAGGED=0 in the
+ * environment at creation) every workgroup publishes a flag per phase and
+ * polls all flags before a dependent phase. Both give the same results.
+ *
  * qwg_chain_create_q4k: `count` members (qwg_gemv_desc, Q4_K weights in the
  * tile layout of qwg_pack_q4k_tiles, 16-byte aligned; x 16-byte aligned, y
  * 4-byte aligned; shape rules as qwg_gemv_q4k) in phase order: the first
@@ -480,6 +493,8 @@ int qwg_group_destroy(qwg_group *group);
  * qwg_chain_phases: number of phases of one launch (a phase with more work
  * than the device's compute units take at once runs as several), or a negative
  * status.
+ * qwg_chain_tagged: 1 if the phases wait on tagged done words, 0 if on flags,
+ * or a negative status.
  * qwg_chain_destroy: frees the plan (hipFree: synchronous). NULL is accepted.
  * Results meet the same bound as qwg_gemv_q4k for every member and are
  * bitwise reproducible (fixed summation order).
@@ -491,6 +506,7 @@ int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase
 int qwg_chain_run(const qwg_chain *chain, void *stream);
 int qwg_chain_status(qwg_chain *chain);
 int qwg_chain_phases(const qwg_chain *chain);
+int qwg_chain_tagged(const qwg_chain *chain);
 int qwg_chain_destroy(qwg_chain *chain);
 
 #ifdef __cplusplus

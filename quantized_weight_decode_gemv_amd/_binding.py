@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.qwg_chain_run.argtypes = [P, P]
         L.qwg_chain_status.argtypes = [P]
         L.qwg_chain_phases.argtypes = [P]
+        L.qwg_chain_tagged.argtypes = [P]
         L.qwg_chain_destroy.argtypes = [P]
         L.qwg_workspace_reserve.argtypes = [P]
         L.qwg_workspace_release.argtypes = [P]
@@ -757,6 +758,12 @@ class Q4kChain:
     @property
     def launch_phases(self) -> int:
         return lib().qwg_chain_phases(self._handle)
+
+    @property
+    def tagged(self) -> bool:
+        """True if the phases wait on tagged done words (see qwg_chain_create_q4k),
+        False if on a flag barrier per phase."""
+        return lib().qwg_chain_tagged(self._handle) == 1
 
     def run(self, stream=None) -> None:
         if self._handle is None:

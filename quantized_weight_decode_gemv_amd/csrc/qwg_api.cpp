@@ -1421,6 +1421,13 @@ int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase
         m.tiles = (int)((d.n_out + kTileRows - 1) / kTileRows);
         m.splits = 1;
         m.mode = kChainDirect;
+        m.ll = nullptr;
+        m.xll = nullptr;
+        m.done = nullptr;
+        m.xsplits = 0;
+        m.xstride = 0;
+        m.tag = 0;
+        m.xtag = 0;
         m.pad = 0;
     }
     // A member's activations may be the output of a member of an earlier phase
@@ -1437,63 +1444,139 @@ int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase
             }
             wired[(size_t)i] = true;
         }
+    // Tagged ordering (done words per tile, activations as tagged rows) needs
+    // every activation read from the chain inside one earlier member's output,
+    // and no output overlapping another output or an activation read in an
+    // earlier phase (no phase may write what an earlier one still reads, since
+    // workgroups no longer finish phases together). Otherwise the launch keeps
+    // a flag barrier per phase. QWG_CHAIN_TAGGED=0 forces the barriers (A/B).
+    const char *env_tg = getenv("QWG_CHAIN_TAGGED");
+    bool dataflow = !(env_tg && env_tg[0] == '0');
+    std::vector<int> producer((size_t)count, -1);
+    for (int j = 0; j < count && dataflow; ++j) {
+        const uintptr_t x0 = (uintptr_t)descs[j].x, x1 = x0 + (uintptr_t)descs[j].n_in * 4;
+        for (int i = 0; i < count; ++i) {
+            if (!overlaps(descs[j].x, (size_t)descs[j].n_in * 4, descs[i].y, (size_t)descs[i].n_out * 4))
+                continue;
+            const uintptr_t y0 = (uintptr_t)descs[i].y, y1 = y0 + (uintptr_t)descs[i].n_out * 4;
+            if (phase_of[(size_t)i] < phase_of[(size_t)j] && y0 <= x0 && x1 <= y1 &&
+                (x0 - y0) % 4 == 0 && producer[(size_t)j] < 0)
+                producer[(size_t)j] = i;
+            else
+                dataflow = false;   // written after it was read, partly inside, or two producers
+        }
+    }
+    for (int i = 0; i < count && dataflow; ++i)
+        for (int k = i + 1; k < count; ++k)
+            if (overlaps(descs[i].y, (size_t)descs[i].n_out * 4, descs[k].y, (size_t)descs[k].n_out * 4)) {
+                dataflow = false;
+                break;
+            }
     const int nwg = chain_workgroups();
     if (nwg < 8) return QWG_ERR_HIP;
     const int64_t Q = (int64_t)nwg * kChainQuads;
-    // Units: per phase, L = ceil(columns / quads) super-block columns per unit
-    // (at most kChainMaxSteps), every quad at most one unit; a phase with more
-    // units than quads runs as several launch phases of which only the first
-    // waits for the previous phase.
+    // Units: per phase a workgroup takes one chunk of C = 4 L consecutive
+    // super-block columns of one 64-row tile of one member, L = 1 or 2 columns
+    // for each of its four quads, whose sums meet in LDS; a tile's chunks are
+    // its splits. L = 1 when the phase's chunks then fit the workgroups (more
+    // of the chip computes each phase), else 2. Split partial sums meet in
+    // split order: tagged launches let the consumers add a producer's partials
+    // (tagged rows) and the launch's end finish y; barrier launches finish a
+    // consumed member's tiles at once through a counter (wired), the others at
+    // the end (deferred). A phase with more chunks than workgroups runs as
+    // several launch phases of which only the first waits for the previous
+    // phase.
     std::vector<uint32_t> units, phases, fin;
     size_t partial_floats = 0, counters = 0;
     int launch_phases = 0;
     int first = 0;
+    // tagged launches: done words of every (tile, split) of every phase but the last
+    std::vector<int64_t> done_off((size_t)count, -1), phase_done_off((size_t)n_phases, 0),
+        phase_done_n((size_t)n_phases, 0);
+    int64_t done_words = 0;
     for (int p = 0; p < n_phases; ++p) {
         const int last = first + phase_sizes[p];
-        int64_t cols = 0;
-        for (int i = first; i < last; ++i) cols += (int64_t)mem[(size_t)i].tiles * mem[(size_t)i].nb;
-        int64_t L = (cols + Q - 1) / Q;
-        if (L > kChainMaxSteps) L = kChainMaxSteps;
-        if (L < 1) L = 1;
-        std::vector<std::array<uint32_t, 4>> list;
+        int L = 1;
+        {
+            int64_t chunks = 0;
+            for (int i = first; i < last; ++i)
+                chunks += (int64_t)mem[(size_t)i].tiles * ((mem[(size_t)i].nb + kChainQuads - 1) / kChainQuads);
+            if (chunks > nwg) L = kChainMaxSteps;
+        }
+        const int C = kChainQuads * L;
+        std::vector<std::array<uint32_t, 3>> list;   // (member, tile, split)
+        phase_done_off[(size_t)p] = done_words;
         for (int i = first; i < last; ++i) {
             ChainMember &m = mem[(size_t)i];
-            m.splits = (int)((m.nb + L - 1) / L);
+            m.splits = (m.nb + C - 1) / C;
+            if (dataflow && p + 1 < n_phases) {
+                done_off[(size_t)i] = done_words;
+                done_words += (int64_t)m.tiles * m.splits;
+            }
             if (m.splits > 1) {
-                m.mode = wired[(size_t)i] ? kChainWired : kChainDeferred;
-                partial_floats += (size_t)m.splits * m.tiles * kTileRows;
+                // tagged launches: a consumed member's partials are its tagged
+                // rows; every split member's y is finished at the end
+                m.mode = !dataflow && wired[(size_t)i] ? kChainWired : kChainDeferred;
+                if (!(dataflow && wired[(size_t)i]))
+                    partial_floats += (size_t)m.splits * m.tiles * kTileRows;
                 if (m.mode == kChainWired) counters += (size_t)m.tiles;
             }
             for (int t = 0; t < m.tiles; ++t) {
-                for (int sp = 0; sp < m.splits; ++sp) {
-                    const int b0 = (int)(sp * L);
-                    const int nblk = (int)std::min<int64_t>(L, m.nb - b0);
-                    list.push_back({(uint32_t)i, (uint32_t)t,
-                                    (uint32_t)b0 | (uint32_t)nblk << 8 | (uint32_t)sp << 16, 0u});
-                }
+                for (int sp = 0; sp < m.splits; ++sp)
+                    list.push_back({(uint32_t)i, (uint32_t)t, (uint32_t)sp});
                 if (m.mode == kChainDeferred) {
                     fin.push_back((uint32_t)i);
                     fin.push_back((uint32_t)t);
                 }
             }
         }
-        for (size_t c0 = 0; c0 < list.size(); c0 += (size_t)Q) {
+        for (size_t c0 = 0; c0 < list.size(); c0 += (size_t)nwg) {
             const size_t row = units.size();
             units.resize(row + (size_t)Q * 4, 0u);
             for (int64_t k = 0; k < Q; ++k) units[row + (size_t)k * 4] = kNoItem;
-            for (size_t k = c0; k < std::min(list.size(), c0 + (size_t)Q); ++k) {
-                // spread a phase's units over every workgroup first
-                const int64_t i = (int64_t)(k - c0);
-                const int64_t colx = (i % nwg) * kChainQuads + (i / nwg) % kChainQuads;
-                for (int f = 0; f < 4; ++f) units[row + (size_t)colx * 4 + f] = list[k][(size_t)f];
+            for (size_t k = c0; k < std::min(list.size(), c0 + (size_t)nwg); ++k) {
+                const int64_t wgi = (int64_t)(k - c0);
+                const ChainMember &m = mem[(size_t)list[k][0]];
+                const int sp = (int)list[k][2];
+                for (int q = 0; q < kChainQuads; ++q) {
+                    const int b0 = sp * C + q * L;
+                    if (b0 >= m.nb) break;
+                    const int nblk = std::min(L, m.nb - b0);
+                    uint32_t *e = &units[row + (size_t)(wgi * kChainQuads + q) * 4];
+                    e[0] = list[k][0];
+                    e[1] = list[k][1];
+                    e[2] = (uint32_t)b0 | (uint32_t)nblk << 8 | (uint32_t)sp << 16;
+                    e[3] = 0u;
+                }
             }
+            const bool waits = p > 0 && c0 == 0;
             phases.push_back((uint32_t)L);
-            phases.push_back(p > 0 && c0 == 0 ? 1u : 0u);
+            if (dataflow) {
+                // the done words of logical phase p - 1, tagged base + p
+                phases.push_back(waits ? (uint32_t)p : 0u);
+                phases.push_back(waits ? (uint32_t)phase_done_n[(size_t)(p - 1)] : 0u);
+                phases.push_back(waits ? (uint32_t)phase_done_off[(size_t)(p - 1)] : 0u);
+            } else {
+                phases.push_back(waits ? 1u : 0u);
+                phases.push_back(0u);
+                phases.push_back(0u);
+            }
             ++launch_phases;
         }
+        phase_done_n[(size_t)p] = done_words - phase_done_off[(size_t)p];
         first = last;
     }
     if (launch_phases > (1 << 20) || fin.size() / 2 > (size_t)INT32_MAX) return QWG_ERR_SHAPE;
+    // tagged rows of the producers' outputs: [splits][n_out] each
+    std::vector<int64_t> ll_off((size_t)count, -1);
+    int64_t ll_rows = 0;
+    if (dataflow)
+        for (int j = 0; j < count; ++j) {
+            const int i = producer[(size_t)j];
+            if (i < 0 || ll_off[(size_t)i] >= 0) continue;
+            ll_off[(size_t)i] = ll_rows;
+            ll_rows += (int64_t)mem[(size_t)i].splits * descs[i].n_out;
+        }
     // device memory
     auto align256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
     const size_t off_members = 0;
@@ -1502,7 +1585,9 @@ int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase
     const size_t off_fin = align256(off_phases + sizeof(uint32_t) * phases.size());
     const size_t off_partial = align256(off_fin + sizeof(uint32_t) * fin.size());
     const size_t off_counters = align256(off_partial + sizeof(float) * partial_floats);
-    const size_t off_flags = align256(off_counters + sizeof(uint32_t) * counters);
+    const size_t off_ll = align256(off_counters + sizeof(uint32_t) * counters);
+    const size_t off_done = align256(off_ll + sizeof(uint64_t) * (size_t)ll_rows);
+    const size_t off_flags = align256(off_done + sizeof(uint64_t) * (size_t)done_words);
     const size_t off_err = align256(off_flags + sizeof(uint32_t) * kFlagCopies * kFlagCopyWords);
     const size_t all = off_err + 256;
     qwg_chain *ch = new (std::nothrow) qwg_chain();
@@ -1514,8 +1599,9 @@ int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase
     uint8_t *base = (uint8_t *)ch->dev_mem;
     {
         size_t pf = 0, ct = 0;
-        for (ChainMember &m : mem) {
-            if (m.splits < 2) continue;
+        for (size_t i = 0; i < mem.size(); ++i) {
+            ChainMember &m = mem[i];
+            if (m.splits < 2 || (dataflow && ll_off[i] >= 0)) continue;
             m.partial = (float *)(base + off_partial) + pf;
             pf += (size_t)m.splits * m.tiles * kTileRows;
             if (m.mode == kChainWired) {
@@ -1523,9 +1609,28 @@ int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase
                 ct += (size_t)m.tiles;
             }
         }
+        // Tags: a producer of logical phase P tags its rows base + P + 1 (the
+        // run's base grows by the launch-phase count, at least the number of
+        // logical phases, so consecutive runs never share a tag).
+        uint64_t *ll = (uint64_t *)(base + off_ll);
+        uint64_t *dw = (uint64_t *)(base + off_done);
+        for (int i = 0; i < count; ++i) {
+            mem[(size_t)i].tag = phase_of[(size_t)i] + 1;
+            if (ll_off[(size_t)i] >= 0) mem[(size_t)i].ll = ll + ll_off[(size_t)i];
+            if (done_off[(size_t)i] >= 0) mem[(size_t)i].done = dw + done_off[(size_t)i];
+        }
+        for (int j = 0; j < count; ++j) {
+            const int i = producer[(size_t)j];
+            if (!dataflow || i < 0) continue;
+            mem[(size_t)j].xll = mem[(size_t)i].ll + ((const float *)descs[j].x - (const float *)descs[i].y);
+            mem[(size_t)j].xtag = mem[(size_t)i].tag;
+            mem[(size_t)j].xsplits = mem[(size_t)i].splits;
+            mem[(size_t)j].xstride = mem[(size_t)i].n_out;
+        }
     }
-    // Counters, flags and the error word start at zero; every run leaves the
-    // counters at zero and all flags equal.
+    // Counters, tagged rows and done words (tag 0: never a run's), flags and
+    // the error word start at zero; every run leaves the counters at zero and
+    // all flags equal.
     if (hipMemset(base + off_counters, 0, off_err + 256 - off_counters) != hipSuccess ||
         hipMemcpy(base + off_members, mem.data(), sizeof(ChainMember) * mem.size(),
                   hipMemcpyHostToDevice) != hipSuccess ||
@@ -1548,7 +1653,9 @@ int qwg_chain_create_q4k(const qwg_gemv_desc *descs, int count, const int *phase
     ch->args.err = (uint32_t *)(base + off_err);
     ch->args.nphases = launch_phases;
     ch->args.nfin = (int)(fin.size() / 2);
+    ch->args.done = (const uint64_t *)(base + off_done);
     ch->args.nwg = nwg;
+    ch->args.tagged = dataflow ? 1 : 0;
     ch->count = count;
     ch->launch_phases = launch_phases;
     *out = ch;
@@ -1562,6 +1669,8 @@ int qwg_chain_run(const qwg_chain *c, void *stream) {
 
 int qwg_chain_phases(const qwg_chain *c) { return c ? c->launch_phases : -QWG_ERR_NULL; }
 
+int qwg_chain_tagged(const qwg_chain *c) { return c ? c->args.tagged : -QWG_ERR_NULL; }
+
 int qwg_chain_status(qwg_chain *c) {
     if (!c) return QWG_ERR_NULL;
     if (hipDeviceSynchronize() != hipSuccess) return QWG_ERR_HIP;
@@ -1569,8 +1678,10 @@ int qwg_chain_status(qwg_chain *c) {
     if (hipMemcpy(&err, c->args.err, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess)
         return QWG_ERR_HIP;
     if (err == 0) return QWG_OK;
-    // A wait gave up: tile counters, flags and the error word are re-armed (they
-    // lie back to back, the counters first).
+    // A wait gave up: tile counters, tagged rows, done words, flags and the
+    // error word are re-armed (they lie back to back, the counters first; the
+    // flags restart at zero, so no tagged word may keep a tag of the run that
+    // gave up).
     if (hipMemset(c->counters, 0, (uint8_t *)c->args.err + sizeof(uint32_t) - (uint8_t *)c->counters) !=
         hipSuccess)
         return QWG_ERR_HIP;

@@ -167,30 +167,49 @@ struct ChainMember {
     float *y;
     float *partial;       // [splits][tiles*64] fp32 (splits > 1)
     uint32_t *counters;   // [tiles] (wired members)
+    // Tagged launches: a member whose y a later member reads publishes each
+    // row (each row's partial sum per split) as a tagged pair, fp32 bits | tag
+    // << 32, in `ll` [splits][n_out]; a member that reads such a y finds
+    // activation k of split s at xll[s * xstride + k], sums the xsplits
+    // partials in split order and waits for the tags. A member of any phase
+    // but the last marks each finished (tile, split) with a tagged done word.
+    uint64_t *ll;         // [splits][n_out] (producers), else null
+    const uint64_t *xll;  // the producer's ll at this member's x (consumers), else null
+    uint64_t *done;       // [tiles][splits], else null
+    int xsplits;          // consumers: the producer's splits
+    int xstride;          // consumers: the producer's n_out
     int n_out;
     int nb;
     int tiles;
     int splits;           // units per tile
     int mode;
+    int tag;              // producers: the tag written is run base + tag
+    int xtag;             // consumers: the producer's tag
     int pad;
 };
 
 // units: [nphases][nwg*kChainQuads] entries of four uint32 (member or kNoItem,
-// tile, b0 | nblk << 8 | split << 16, 0); phases: [nphases] pairs (columns of
-// the phase, 1 if it waits for the previous phase); fin: [nfin] pairs (member,
-// tile) of the deferred members' tiles; flags: one per workgroup (phases
-// completed, counted across runs), kFlagCopies copies kFlagCopyWords apart;
-// err: set when a wait gave up.
+// tile, b0 | nblk << 8 | split << 16, 0); phases: [nphases] entries of four
+// uint32 (columns of the phase; barrier launches: 1 if it waits for the
+// previous phase, tagged launches: the tag offset of the done words it waits
+// for; how many done words; their first index in `done`); fin: [nfin] pairs
+// (member, tile) of the deferred members' tiles; flags: one per workgroup
+// (phases completed, counted across runs), kFlagCopies copies kFlagCopyWords
+// apart; err: set when a wait gave up. tagged: a phase waits for the done
+// words of the previous phase's tiles and reads activations produced in the
+// chain as tagged rows, instead of a flag barrier over every workgroup.
 struct ChainArgs {
     const ChainMember *members;
     const uint32_t *units;
     const uint32_t *phases;
     const uint32_t *fin;
+    const uint64_t *done;
     uint32_t *flags;
     uint32_t *err;
     int nphases;
     int nfin;
     int nwg;
+    int tagged;
 };
 hipError_t launch_q4k_chain(const ChainArgs &c, hipStream_t s);
 int chain_lds_bytes();

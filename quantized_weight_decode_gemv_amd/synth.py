@@ -28,6 +28,11 @@ role])``, role 0 = weight fields, 1 = activations, 2 = IQ3 grid):
 * IQ4_XS blocks (136 B): fp16 d as above, bytes 2..135 uniform (uniform 6-bit
   sub-scales and 4-bit codes). Table: 16 distinct integers in [-127, 127],
   ascending (the published table is absent).
+* Q4_K blocks of a chained stream (a product's output is the next one's
+  input, ``q4k_chain_weights``): as above, but d and dmin are fp16 draws of
+  random sign and magnitude U[0.5, 1.5] / (336.7 sqrt(n_out)): zero-mean
+  weights whose products keep the norm of their input, so that 89 chained
+  products stay inside the fp32 range (a decoder's norms do this in the model).
 * Activations: fp32 standard normal.
 
 The published TinyLlama-1.1B Q4_K_M weights and real IQ3 tensors are absent; the
@@ -66,6 +71,34 @@ def q4k_weights(n_out: int, n_in: int, cfg: int, tensor: int) -> np.ndarray:
     g = rng(cfg, tensor, ROLE_W)
     d = _fp16_uniform(g, nb)
     dmin = _fp16_uniform(g, nb)
+    blocks = np.empty((nb, Q4K_BYTES), np.uint8)
+    blocks[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
+    blocks[:, 2:4] = dmin.view(np.uint8).reshape(nb, 2)
+    blocks[:, 4:] = g.integers(0, 256, (nb, Q4K_BYTES - 4), dtype=np.uint8)
+    return blocks.reshape(n_out, -1)
+
+
+# Mean square of a Q4_K weight per unit of d^2 when d and dmin have the same
+# magnitude distribution (U[0.5, 1.5] x scale, independent random signs) and the
+# 6-bit scales/mins and 4-bit quants are uniform: E[a^2] (E[sc^2] E[q^2] +
+# E[mn^2]) = (13/12) * 1333.5 * 78.5 = 113,370 (sqrt 336.7).
+CHAIN_W_RMS_PER_SCALE = 336.7
+
+
+def q4k_chain_weights(n_out: int, n_in: int, cfg: int, tensor: int) -> np.ndarray:
+    """Q4_K blocks for a product whose output is the next product's input: as
+    q4k_weights, but d and dmin are fp16 draws of random sign and magnitude
+    U[0.5, 1.5] / (336.7 sqrt(n_out)), so that the weights have zero mean and
+    a product's output has about the norm of its input (a chain of many such
+    products stays inside the fp32 range, as a decoder's normalized layers
+    do). uint8 [n_out, n_in/256*144]."""
+    if n_in % QK:
+        raise ValueError("n_in must be a multiple of 256")
+    nb = n_out * (n_in // QK)
+    g = rng(cfg, tensor, ROLE_W)
+    scale = 1.0 / (CHAIN_W_RMS_PER_SCALE * np.sqrt(n_out))
+    d = (g.choice([-1.0, 1.0], nb) * g.uniform(0.5, 1.5, nb) * scale).astype(np.float16)
+    dmin = (g.choice([-1.0, 1.0], nb) * g.uniform(0.5, 1.5, nb) * scale).astype(np.float16)
     blocks = np.empty((nb, Q4K_BYTES), np.uint8)
     blocks[:, 0:2] = d.view(np.uint8).reshape(nb, 2)
     blocks[:, 2:4] = dmin.view(np.uint8).reshape(nb, 2)
@@ -219,6 +252,37 @@ def config(cfg: int) -> list[Problem]:
     if cfg == 7:
         return [Problem(n, "iq3", o, i, 1, 7, t) for t, (n, o, i) in enumerate(PROJ)]
     raise ValueError(cfg)
+
+
+def chain_sources(probs: list[Problem]) -> list[int]:
+    """For a per-token stream (config 5 or 6 order: per layer q, k, v, o, gate,
+    up, down, then the LM head), the index of the product whose output stands
+    in for each product's input in a decode step, or -1 for the step's own
+    input (one vector): q, k and v read the previous layer's down (layer 0:
+    the step's input), o reads q (standing in for
+    the attention output), gate and up read o (the normalized residual), down
+    reads gate (the SwiGLU activation), the LM head reads the last down. The
+    operations between the products are not part of this workload."""
+    src, last_down, mine = [], -1, {}
+    for i, p in enumerate(probs):
+        name = p.name.split(".")[-1]
+        if name in ("q", "k", "v"):
+            if name == "q":
+                mine = {"q": i}
+            src.append(last_down)
+        elif name == "o":
+            src.append(mine["q"])
+            mine["o"] = i
+        elif name in ("gate", "up"):
+            src.append(mine["o"])
+            if name == "gate":
+                mine["gate"] = i
+        elif name == "down":
+            src.append(mine["gate"])
+            last_down = i
+        else:
+            src.append(last_down)
+    return src
 
 
 def weights(p: Problem) -> np.ndarray:

@@ -45,7 +45,7 @@ def test_header_declares_the_entry_points():
                  "qwg_group_create_q4k_batched", "qwg_group_create_q4k_batched_tiled",
                  "qwg_gemm_q4k_tiled", "qwg_gemm_q4k_noalloc", "qwg_workspace_reserve",
                  "qwg_chain_create_q4k", "qwg_chain_run", "qwg_chain_status", "qwg_chain_phases",
-                 "qwg_chain_destroy",
+                 "qwg_chain_destroy", "qwg_chain_tagged",
                  "qwg_workspace_release"):
         assert want in names
 
@@ -393,4 +393,5 @@ def test_chain_validation_errors(L):
     assert L.qwg_chain_run(None, None) == 1
     assert L.qwg_chain_status(None) == 1
     assert L.qwg_chain_phases(None) == -1
+    assert L.qwg_chain_tagged(None) == -1
     assert L.qwg_chain_destroy(None) == 0

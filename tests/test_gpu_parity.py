@@ -5,6 +5,8 @@ Bars: dequantization is bit-exact; a GEMV/GEMM output passes when
 |y_gpu - y_oracle| <= 2e-6 * sum_k |w_k x_k| for every row (the oracle sums in
 fp64); integer-valued and one-hot cases must match exactly.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -1308,29 +1310,142 @@ def layer_phases(probs):
     return phases
 
 
-def test_chain_c5_all_rows_and_repeat_runs():
-    # The launch the bench times for the dependency-respecting stream: 89
-    # phases over the 155 GEMVs, independent inputs. Every row of every output
-    # (NaN-filled first) against the oracle; later runs bitwise equal.
+def c5_decode_step_chain(tagged=True):
+    """The chain the bench times: the per-token stream's 155 products in the 89
+    phases of a decode step, each product reading the output of the product
+    that stands in for its input (synth.chain_sources; layer 0 reads the step's
+    input x0), weights that keep the chained norms in range
+    (synth.q4k_chain_weights), outputs NaN-filled. Returns the chain, the host
+    weights, x0, the sources and the outputs."""
+    probs = synth.config(5)
+    ws = _C5_CHAIN_W.setdefault("w", [synth.q4k_chain_weights(p.n_out, p.n_in, p.cfg, p.tensor)
+                                      for p in probs])
+    x0 = synth.activations(2048, 5, 0)
+    src = synth.chain_sources(probs)
+    X0 = dev(x0)
+    Y = nan_outputs(probs)
+    X = [X0 if j < 0 else Y[j] for j in src]
+    W = [qwg.pack_q4k_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
+    phases = layer_phases(probs)
+    assert len(phases) == 89
+    env = os.environ.pop("QWG_CHAIN_TAGGED", None)
+    if not tagged:
+        os.environ["QWG_CHAIN_TAGGED"] = "0"
+    try:
+        ch = qwg.Q4kChain([[(W[i], X[i], Y[i]) for i in ph] for ph in phases])
+    finally:
+        os.environ.pop("QWG_CHAIN_TAGGED", None)
+        if env is not None:
+            os.environ["QWG_CHAIN_TAGGED"] = env
+    assert ch.tagged == tagged
+    return ch, probs, ws, x0, src, Y, (W, X0)
+
+
+_C5_CHAIN_W = {}
+
+
+def test_chain_c5_decode_step_all_rows_and_repeat_runs():
+    # The headline launch: every row of every product against the oracle applied
+    # to that product's actual input (the step input or its producer's output);
+    # later runs bitwise equal; the same chain with a flag barrier per phase
+    # gives the same bits.
+    ch, probs, ws, x0, src, Y, keep = c5_decode_step_chain()
+    assert ch.launch_phases >= 89
+    ch.run()
+    ch.status()
+    out = [host(y).copy() for y in Y]
+    for k, (p, w) in enumerate(zip(probs, ws)):
+        xin = x0 if src[k] < 0 else out[src[k]]
+        assert not np.isnan(xin).any(), f"{p.name}: input left unwritten"
+        yr, sr = oracle.gemv_q4k(w, xin, p.n_in, p.n_out)
+        assert_bound(out[k], yr, sr, "chain " + p.name)
+    assert 1.0 < np.linalg.norm(out[-2]) < 1e4   # the chained norms stay in range
+    for y in Y:
+        y.fill_(float("nan"))
+    for _ in range(3):
+        ch.run()
+    ch.status()
+    for p, y, y0 in zip(probs, Y, out):
+        assert_bits(host(y), y0, "chain rerun " + p.name)
+    ch.close()
+    cb, _, _, _, _, Yb, keep_b = c5_decode_step_chain(tagged=False)
+    cb.run()
+    cb.status()
+    for p, y, y0 in zip(probs, Yb, out):
+        assert_bits(host(y), y0, "flag-barrier chain " + p.name)
+    cb.close()
+
+
+def test_chain_c5_independent_inputs_all_rows():
+    # The same 89 phases with an independent input per product (done-word waits
+    # only, no tagged rows): every row against the oracle, reruns bitwise equal.
     probs, ws, xs, refs = q4k_c5()
     W = [qwg.pack_q4k_tiles(dev(w), p.n_in) for p, w in zip(probs, ws)]
     X = [dev(x) for x in xs]
     Y = nan_outputs(probs)
     phases = layer_phases(probs)
-    assert len(phases) == 89
     ch = qwg.Q4kChain([[(W[i], X[i], Y[i]) for i in ph] for ph in phases])
-    assert ch.launch_phases >= 89
+    assert ch.tagged
     ch.run()
     ch.status()
     assert_stream(probs, refs, Y, "chain")
     first = [host(y).copy() for y in Y]
     for y in Y:
         y.fill_(float("nan"))
-    for _ in range(3):
+    for _ in range(2):
         ch.run()
     ch.status()
     for p, y, y0 in zip(probs, Y, first):
         assert_bits(host(y), y0, "chain rerun " + p.name)
+    ch.close()
+
+
+def test_chain_overwriting_an_earlier_input_uses_flag_barriers():
+    # Phase 1 writes the buffer phase 0 read: a tagged launch could let a fast
+    # workgroup overwrite it early, so the chain falls back to flag barriers.
+    n = 2048
+    wa, wb = _small_q4k(n, n, 301), _small_q4k(n, n, 302)
+    x0 = synth.activations(n, 203, 0)
+    xd, ya = dev(x0), torch.full((n,), float("nan"), device=DEV)
+    ch = qwg.Q4kChain([[(qwg.pack_q4k_tiles(dev(wa), n), xd, ya)],
+                       [(qwg.pack_q4k_tiles(dev(wb), n), ya, xd)]])
+    assert not ch.tagged
+    ch.run()
+    ch.status()
+    yah = host(ya).copy()
+    yr, sr = oracle.gemv_q4k(wa, x0, n, n)
+    assert_bound(yah, yr, sr, "phase 0")
+    yr, sr = oracle.gemv_q4k(wb, yah, n, n)
+    assert_bound(host(xd), yr, sr, "phase 1 (written over phase 0's input)")
+    ch.close()
+
+
+def test_chain_input_inside_a_larger_output():
+    # A consumer reads 2048 rows at an offset inside a 5632-row output (tagged
+    # rows read at that offset), another the output's head; a third phase
+    # reads both consumers' outputs through one more producer.
+    wp = _small_q4k(5632, 2048, 303)
+    wc1, wc2 = _small_q4k(2048, 2048, 304), _small_q4k(256, 2048, 305)
+    wl = _small_q4k(1000, 2048, 306)
+    x0 = synth.activations(2048, 204, 0)
+    xd = dev(x0)
+    yp = torch.full((5632,), float("nan"), device=DEV)
+    y1 = torch.full((2048,), float("nan"), device=DEV)
+    y2 = torch.full((256,), float("nan"), device=DEV)
+    yl = torch.full((1000,), float("nan"), device=DEV)
+    pk = lambda w, k: qwg.pack_q4k_tiles(dev(w), k)   # noqa: E731
+    ch = qwg.Q4kChain([[(pk(wp, 2048), xd, yp)],
+                       [(pk(wc1, 2048), yp[1024:3072], y1), (pk(wc2, 2048), yp[:2048], y2)],
+                       [(pk(wl, 2048), y1, yl)]])
+    assert ch.tagged
+    for _ in range(2):
+        ch.run()
+    ch.status()
+    yph = host(yp).copy()
+    for w, xin, y, n_out in ((wp, x0, yp, 5632), (wc1, yph[1024:3072], y1, 2048),
+                             (wc2, yph[:2048], y2, 256), (wl, host(y1).copy(), yl, 1000)):
+        yr, sr = oracle.gemv_q4k(w, np.ascontiguousarray(xin), 2048, n_out)
+        assert_bound(host(y), yr, sr, f"member with {n_out} rows")
     ch.close()
 
 
@@ -1378,6 +1493,7 @@ def test_chain_wired_phases_read_the_previous_outputs():
     members.append([wh, qwg.pack_q4k_tiles(dev(wh), 2048), src, torch.empty(32000, device=DEV)])
     phases.append([len(members) - 1])
     ch = qwg.Q4kChain([[tuple(members[i][1:]) for i in ph] for ph in phases])
+    assert ch.tagged
     for run in range(3):
         x0.copy_(torch.from_numpy(synth.activations(2048, 201, run)))
         for m in members:
