@@ -67,8 +67,8 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/chain.hip",
 # WRITE_SIZE runs of this script, each scaled by the same counter on a plain device copy of known
 # size (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_chain_c5.md). Valid only for the
 # kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "44bed15b0bb900963fa2a3f6456814a01e6a29a6bff39c2368ecd6b07d784e1c",
-           "fetch_bytes": 603125914, "write_bytes": 19289088}
+TRAFFIC = {"sources_sha256": "5dcff5c223a368c22def3b78f34f70f07b9996fde2648ac281c21d795dd8f38b",
+           "fetch_bytes": 620858880, "write_bytes": 6816768}
 
 
 def kernel_sources_sha256() -> str:
