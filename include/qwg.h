@@ -47,7 +47,7 @@
  *     return; the caller synchronizes. Outputs must not alias inputs.
  *   - GEMV/GEMM with few 64-row tiles split the n_in sum across workgroups.
  *     The partial sums then go through a per-(device, stream) workspace
- *     (8 MiB + 16 KiB) that the library allocates on the first such call on
+ *     (9 MiB + 17 KiB) that the library allocates on the first such call on
  *     that stream (hipMalloc + hipMemset, synchronous) and keeps until
  *     qwg_workspace_release or the end of the process. This is the one place
  *     where the single-matrix calls allocate and keep state. A first such call
@@ -59,6 +59,11 @@
  *     one another or calls on that stream. Concurrent calls on different
  *     streams never share a workspace. The summation order is fixed by the
  *     shapes, so results are deterministic.
+ *   - Short batch-1 Q4_K calls (at most one workgroup per compute unit) whose
+ *     rows are split add the partial sums through tagged words: the last
+ *     split's workgroup waits for its peers' words, which relies on all of a
+ *     launch's workgroups becoming resident. The wait is bounded (1 s); if it
+ *     gives up, the tile's rows are stored as NaN.
  *   - Errors are reported by the returned status (QWG_* below); the library
  *     never aborts, never throws and writes nothing on a validation error.
  *     Validation happens on the host before any HIP call.
@@ -114,7 +119,9 @@ int64_t qwg_row_bytes(int fmt, int64_t n_in);
 /*
  * How a GEMV/GEMM of this shape is decomposed (introspection for tests and
  * tuning): the number of workgroups that share each 64-row tile by splitting
- * the n_in sum (1 = no split), or a negative status for invalid sizes.
+ * the n_in sum (1 = no split), or a negative status for invalid sizes. For
+ * Q4_K the plan of the short-call kernel depends on the current device's
+ * compute-unit count; with no device the vector engine's plan is returned.
  */
 int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out);
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqwg.so")
-SOURCES = ["qwg_api.cpp", "q4k.hip", "chain.hip", "iq3.hip", "codebook.hip", "encode.hip"]
+SOURCES = ["qwg_api.cpp", "q4k.hip", "short.hip", "chain.hip", "iq3.hip", "codebook.hip", "encode.hip"]
 ARCH = os.environ.get("QWG_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -16,6 +16,7 @@
 
 #include "../../include/qwg.h"
 #include "qwg_internal.h"
+#include "short_call.h"
 
 using namespace qwg;
 
@@ -210,6 +211,43 @@ bool use_stream_engine() {
     return v;
 }
 
+// Compute units of the current device (0 on error), cached per device.
+int device_cus() {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    cache.emplace(dev, cus);
+    return cus;
+}
+
+// Splits of a batch-1 Q4_K or IQ3 call on the short-call kernels, or 0 for the
+// other engines: matrices whose tiles x splits fit one workgroup per compute
+// unit.
+// QWG_SHORT=0 turns the short-call kernel off (A/B measurements).
+int short_splits(int tiles, int nb) {
+    static const bool off = [] {
+        const char *e = getenv("QWG_SHORT");
+        return e != nullptr && e[0] == '0';
+    }();
+    if (off) return 0;
+    const int cus = device_cus();
+    const int sp = cus > 0 ? short_plan_splits(tiles, nb, cus) : 0;
+    // QWG_SHORT_SPLITS caps the splits (tuning experiments)
+    static const int cap = env_int("QWG_SHORT_SPLITS", 0);
+    if (sp > 0 && cap > 0 && sp > cap) {
+        if ((nb + cap - 1) / cap > kShortMaxBlocks) return sp;
+        return cap;
+    }
+    return sp;
+}
+
 // IQ3 stream engine shape. Measured on MI355X: grouped streams run best with
 // 8-wavefront workgroups (two per CU), single GEMVs with 16 (one per CU, four
 // super-blocks per stage), both with a 2-stage ring. `waves` (if nonzero)
@@ -236,6 +274,7 @@ Iq3Shape iq3_shape(bool grouped, int waves) {
 struct Workspace {
     float *partial = nullptr;
     uint32_t *counters = nullptr;
+    ShortState sh = {nullptr, nullptr};
 };
 
 size_t workspace_partial_floats() { return kWsPartialFloats; }
@@ -262,17 +301,23 @@ int get_workspace(hipStream_t stream, Workspace *out) {
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return QWG_ERR_HIP;
     if (cap != hipStreamCaptureStatusNone) return QWG_ERR_CAPTURE;
     const size_t pbytes = workspace_partial_floats() * sizeof(float);
+    const size_t wbytes = kShortWords * sizeof(uint64_t);
     const size_t cbytes = workspace_counters() * sizeof(uint32_t);
+    const size_t ebytes = kShortEpochs * sizeof(uint32_t);
     void *mem = nullptr;
-    if (hipMalloc(&mem, pbytes + cbytes) != hipSuccess) return QWG_ERR_HIP;
-    // Counters start at zero; every launch leaves them at zero again.
-    if (hipMemset((uint8_t *)mem + pbytes, 0, cbytes) != hipSuccess) {
+    if (hipMalloc(&mem, pbytes + wbytes + cbytes + ebytes) != hipSuccess) return QWG_ERR_HIP;
+    // Counters start at zero and every launch leaves them at zero again; the
+    // short calls' tagged words and epochs start at zero (no word carries a
+    // tag a call waits for).
+    if (hipMemset((uint8_t *)mem + pbytes, 0, wbytes + cbytes + ebytes) != hipSuccess) {
         (void)hipFree(mem);
         return QWG_ERR_HIP;
     }
     Workspace ws;
     ws.partial = (float *)mem;
-    ws.counters = (uint32_t *)((uint8_t *)mem + pbytes);
+    ws.sh.words = (uint64_t *)((uint8_t *)mem + pbytes);
+    ws.counters = (uint32_t *)((uint8_t *)mem + pbytes + wbytes);
+    ws.sh.epochs = (uint32_t *)((uint8_t *)mem + pbytes + wbytes + cbytes);
     g_ws.emplace(key, ws);
     *out = ws;
     return QWG_OK;
@@ -414,11 +459,14 @@ int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
         return sp > 0 ? sp : -QWG_ERR_HIP;
     }
     if (fmt != QWG_FMT_Q4K) {
+        const int ss = short_splits(tiles, (int)(n_in / kQK));
+        if (ss > 0) return ss;
         const int slots = iq3_stream_slots(iq3_shape(false, 0), false);
         if (slots <= 0) return -QWG_ERR_HIP;
         return iq3_splits(tiles, (int)(n_in / kQK), slots);
     }
-    return choose_splits(tiles, (int)(n_in / kQK));
+    const int ss = short_splits(tiles, (int)(n_in / kQK));
+    return ss > 0 ? ss : choose_splits(tiles, (int)(n_in / kQK));
 }
 
 int qwg_workspace_reserve(void *stream) {
@@ -473,17 +521,19 @@ int qwg_dequant_iq3_xxs(const void *src, const float *grid, float *dst, int64_t 
 
 namespace {
 
-// Split-sum scratch of qwg_gemm_q4k_noalloc: partial sums (kScratchFloats) then
-// tile counters (kScratchCounters), one copy per GPU in the library's code
-// object. Host code never uses the array's name as an address: each device's
-// address comes from hipGetSymbolAddress (scratch_of). The counters start at
-// zero (cleared when a device is first used) and every launch leaves them at
-// zero. The largest split plan of qwg_gemm_q4k needs fewer than 2,304 x 64
+// Split-sum scratch of qwg_gemm_q4k_noalloc: partial sums (kScratchFloats),
+// the short calls' tagged words (kShortWords x 8 bytes), tile counters
+// (kScratchCounters) and the short calls' tile epochs (kShortEpochs), one copy
+// per GPU in the library's code object. Host code never uses the array's name
+// as an address: each device's address comes from hipGetSymbolAddress
+// (scratch_of). Everything after the partial sums starts at zero (cleared when a
+// device is first used); every launch leaves the counters at zero. The largest split plan of qwg_gemm_q4k needs fewer than 2,304 x 64
 // partial sums (batch 1) and fewer than 256 tiles, so these sizes cover every
 // shape; a plan that did not fit would be rejected (QWG_ERR_SHAPE).
 constexpr size_t kScratchFloats = (size_t)4096 * kTileRows;
 constexpr size_t kScratchCounters = 4096;
-static __device__ __align__(256) uint32_t scratch[kScratchFloats + kScratchCounters];
+constexpr size_t kScratchZeroed = 2 * kShortWords + kScratchCounters + kShortEpochs;
+static __device__ __align__(256) uint32_t scratch[kScratchFloats + kScratchZeroed];
 
 __global__ void zero_u32_kernel(uint32_t *p, int n) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
@@ -508,13 +558,15 @@ int scratch_of(hipStream_t stream, Workspace *out) {
         if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
             return QWG_ERR_HIP;
         base = (uint32_t *)ptr;
-        hipLaunchKernelGGL(zero_u32_kernel, dim3(16), dim3(256), 0, stream,
-                           base + kScratchFloats, (int)kScratchCounters);
+        hipLaunchKernelGGL(zero_u32_kernel, dim3(64), dim3(256), 0, stream,
+                           base + kScratchFloats, (int)kScratchZeroed);
         if (hipGetLastError() != hipSuccess) return QWG_ERR_HIP;
         g_scratch.emplace(dev, base);
     }
     out->partial = (float *)base;
-    out->counters = base + kScratchFloats;
+    out->sh.words = (uint64_t *)(base + kScratchFloats);
+    out->counters = base + kScratchFloats + 2 * kShortWords;
+    out->sh.epochs = out->counters + kScratchCounters;
     return QWG_OK;
 }
 
@@ -534,6 +586,18 @@ int gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_ou
     // weights: 12.4 us against 14.2-15.8 us on the matrix cores, while on the
     // layer shapes of 32-88 tiles and at batch 3..8 the matrix cores win or
     // tie: bench.py --workload gemm_ab); otherwise the matrix cores.
+    if (batch == 1) {
+        const int ss = short_splits(a.tiles, a.nb);
+        if (ss > 0) {
+            a.splits = ss;
+            Workspace ws;
+            if (ss > 1) {
+                rc = noalloc ? scratch_of(stream, &ws) : get_workspace(stream, &ws);
+                if (rc) return rc;
+            }
+            return hip_status(launch_q4k_short(a, ws.sh, false, stream));
+        }
+    }
     const bool valu = batch == 1 || (batch == 2 && a.tiles >= kValuBatch2Tiles);
     const bool mstream = !valu && !mfma_tile_engine();
     const int ring = mstream_ring();
@@ -703,6 +767,16 @@ int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, in
     GemvArgs a;
     fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
     a.layout = kLayoutTiles;
+    const int ss = short_splits(a.tiles, a.nb);
+    if (ss > 0) {
+        a.splits = ss;
+        Workspace ws;
+        if (ss > 1) {
+            const int wrc = get_workspace((hipStream_t)stream, &ws);
+            if (wrc) return wrc;
+        }
+        return hip_status(launch_q4k_short(a, ws.sh, true, (hipStream_t)stream));
+    }
     const StreamShape sh = stream_shape(false);
     int cus = 0;
     const int64_t slots = (int64_t)q4k_stream_residency(sh.waves, sh.ring, &cus) * cus;
@@ -743,6 +817,19 @@ int iq3_gemv(float *y, const float *x, const void *w, const float *grid, int64_t
                        (size_t)a.tiles > kWsCounters))
         return QWG_ERR_SHAPE;
     a.layout = layout;
+    if (waves == 0 && splits == 0) {
+        // automatic plan: the short-call kernel when the matrix fits it
+        const int ss = short_splits(a.tiles, a.nb);
+        if (ss > 0) {
+            a.splits = ss;
+            Workspace ws;
+            if (ss > 1) {
+                rc = get_workspace((hipStream_t)stream, &ws);
+                if (rc) return rc;
+            }
+            return hip_status(launch_iq3_short(a, ws.sh, grid, (hipStream_t)stream));
+        }
+    }
     const Iq3Shape sh = iq3_shape(false, waves);
     const int slots = iq3_stream_slots(sh, tiled);
     if (slots <= 0) return QWG_ERR_HIP;

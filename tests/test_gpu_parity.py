@@ -233,9 +233,41 @@ def test_gemm_q4k_ex_rejects_bad_plans():
 
 
 def test_gemv_q4k_covers_split_and_unsplit_plans():
+    # vector engine: many tiles (no split), a long row (split); short-call
+    # kernel: up to one workgroup per compute unit, at most 8 splits
     assert qwg.plan_splits(0, 256, 131072 + 5) == 1
-    assert qwg.plan_splits(0, 2048, 2048) > 1
     assert qwg.plan_splits(0, 65536, 3) > 8
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for n_in, n_out in [(2048, 2048), (5632, 2048), (5632, 200), (2048, 5632), (256, 64)]:
+        tiles, nb = -(-n_out // 64), n_in // 256
+        assert qwg.plan_splits(0, n_in, n_out) == min(cus // tiles, nb, 8), (n_in, n_out)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(64, 3584), (64, 3840), (200, 5632), (2048, 5632),
+                                        (100, 28672), (1, 7168), (130, 3328)])
+def test_gemv_q4k_short_calls_split_and_repeat(n_out, n_in):
+    # Short-call kernel: rows split into tagged words that the last split adds
+    # up (up to 8 splits of 1..4 columns), on row-major and tile-layout
+    # weights; repeated calls, with another shape in between on the same
+    # stream, advance the tiles' epochs and give the same bits. (100 x 28672
+    # has more columns per split than the kernel holds: the vector engine.)
+    w, x = _gemv_q4k_case(n_out, n_in, 109, n_in // 256)
+    wd, xd = dev(w), dev(x)
+    wt = qwg.pack_q4k_tiles(wd, n_in)
+    yr, sr = oracle.gemv_q4k(w, x, n_in, n_out)
+    y1 = host(qwg.gemv_q4k(wd, xd)).copy()
+    assert_bound(y1, yr, sr, f"{n_out}x{n_in} splits={qwg.plan_splits(0, n_in, n_out)}")
+    t1 = host(qwg.gemv_q4k_tiled(wt, xd, n_out)).copy()
+    assert_bound(t1, yr, sr, "tile layout")
+    if n_in <= 8192:   # one kernel for both layouts: the same bits
+        assert_bits(t1, y1, "tile layout")
+    wo, xo = _gemv_q4k_case(300, 7168, 110, 0)
+    other = qwg.gemv_q4k(dev(wo), dev(xo))
+    for _ in range(3):
+        assert_bits(host(qwg.gemv_q4k(wd, xd)), y1, "repeat")
+        assert_bits(host(qwg.gemv_q4k_tiled(wt, xd, n_out)), t1, "repeat, tile layout")
+    yo, so = oracle.gemv_q4k(wo, xo, 7168, 300)
+    assert_bound(host(other), yo, so, "other shape")
 
 
 def _integer_q4k(n_out, n_in, seed):
@@ -299,7 +331,7 @@ def test_first_split_call_under_capture_returns_a_status():
     # allocate (it cannot, under capture) and reports QWG_ERR_CAPTURE. After
     # qwg_workspace_reserve the same capture records the kernels, and replays
     # reproduce the eager result.
-    n_out, n_in = 2048, 2048
+    n_out, n_in = 2048, 5632
     assert qwg.plan_splits(0, n_in, n_out) > 1
     w, x = _gemv_q4k_case(n_out, n_in, 97, 3)
     wd, xd = dev(w), dev(x)
@@ -318,10 +350,13 @@ def test_first_split_call_under_capture_returns_a_status():
     with torch.cuda.graph(graph, stream=side):
         qwg.gemv_q4k(wd, xd, out=y)
     ref = host(qwg.gemv_q4k(wd, xd)).copy()
-    for _ in range(2):
+    for _ in range(3):
         y.fill_(float("nan"))
         graph.replay()
         assert_bits(host(y), ref, "replay after reserve")
+        # eager calls on the same stream between replays advance the split epochs
+        with torch.cuda.stream(side):
+            assert_bits(host(qwg.gemv_q4k(wd, xd)), ref, "eager between replays")
     yr, sr = oracle.gemv_q4k(w, x, n_in, n_out)
     assert_bound(ref, yr, sr, "eager")
 
@@ -1003,6 +1038,41 @@ def test_gemv_iq3_tiled(n_out, n_in):
     y = host(qwg.gemv_iq3_tiled(wt, xd, gd, n_out))
     assert_bound(y, yr, sr, f"iq3 tiled {n_out}x{n_in}")
     assert_bits(host(qwg.gemv_iq3_tiled(wt, xd, gd, n_out)), y, "iq3 tiled rerun")
+
+
+@pytest.mark.parametrize("n_out,n_in", [(2048, 2048), (5632, 2048), (2048, 5632), (256, 2048),
+                                        (130, 3328), (1, 7168), (64, 3840)])
+def test_gemv_iq3_short_calls_layouts_and_repeat(n_out, n_in):
+    # The short-call IQ3 kernel (split rows through tagged words) on row-major,
+    # llama.cpp-order and tile-layout weights: the same kernel, so the same
+    # bits for the container and its tile layout, the llama.cpp order with the
+    # doubled grid exactly twice that; repeated calls give the same bits.
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 133, n_in // 256)
+    x = synth.activations(n_in, 133, n_out)
+    wd, xd, gd = dev(w), dev(x), dev(grid)
+    yr, sr = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    y = host(qwg.gemv_iq3(wd, xd, gd)).copy()
+    assert_bound(y, yr, sr, f"iq3 {n_out}x{n_in} splits={qwg.plan_splits(1, n_in, n_out)}")
+    t = host(qwg.gemv_iq3_tiled(qwg.pack_iq3_tiles(wd, n_in), xd, gd, n_out))
+    assert_bits(t, y, "tile layout")
+    wx = dev(synth.iq3_xxs_weights(n_out, n_in, 133, n_in // 256))
+    gx = dev(synth.iq3_xxs_grid())
+    assert_bits(host(qwg.gemv_iq3_xxs(wx, xd, gx)), 2 * y, "llama.cpp order, doubled grid")
+    for _ in range(2):
+        assert_bits(host(qwg.gemv_iq3(wd, xd, gd)), y, "repeat")
+
+
+@pytest.mark.parametrize("waves", [0, 16])
+def test_gemv_iq3_inexact_grid_gives_nan_rows(waves):
+    # A grid value that fp16 cannot hold: every engine stores NaN in every row.
+    grid = synth.iq3_grid().copy()
+    grid[17, 2] = 0.1
+    n_out, n_in = 300, 2048
+    w = synth.iq3_weights(n_out, n_in, 134, 0)
+    x = synth.activations(n_in, 134, 0)
+    y = host(qwg.gemv_iq3(dev(w), dev(x), dev(grid), waves=waves, splits=1 if waves else 0))
+    assert np.isnan(y).all()
 
 
 def test_iq3_tiled_integer_exact_and_group_layer():
