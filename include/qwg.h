@@ -291,10 +291,11 @@ int qwg_gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t 
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same arguments, kernels, work decomposition and results (bit-identical to
  * qwg_gemm_q4k), but split sums go through a fixed scratch array that the
- * library's code object holds on every GPU (1 MiB of partial sums and 4096
- * tile counters, held until the process ends) instead of the per-stream
- * workspace, so no call allocates or frees anything. The first call on a
- * device also enqueues a small kernel that zeroes the counters. Every shape
+ * library's code object holds on every GPU (1 MiB of partial sums, 1 MiB of
+ * tagged split words, 4096 tile counters and 256 tile epochs, held until the
+ * process ends) instead of the per-stream workspace, so no call allocates or
+ * frees anything. The first call on a device also enqueues a small kernel
+ * that zeroes everything but the partial sums. Every shape
  * the plans produce fits; a plan that did not fit the scratch would return
  * QWG_ERR_SHAPE. All calls on one GPU share the one scratch array: calls that
  * overlap in time on that GPU (on different streams, or replays of graphs
