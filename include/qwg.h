@@ -311,8 +311,9 @@ int qwg_gemm_q4k_noalloc(float *y, const float *x, const void *w, int64_t n_in, 
  * workgroup per (tile, split) taking one super-block column per stage with 4
  * wavefronts, or two columns with 8; 3 = the persistent matrix-core stream
  * (batch >= 2 only: resident workgroups walk the (tile, split) items with a
- * ring of stages that runs ahead across them); 0 = automatic (the persistent
- * stream for batch >= 2); `splits`
+ * ring of stages that runs ahead across them); 0 = automatic among these
+ * engines (the persistent stream for batch >= 2; qwg_gemm_q4k itself runs a
+ * batch-1 matrix of up to 256 tiles on the short-call kernel instead); `splits`
  * workgroups sharing each tile's n_in sum (1..n_in/256; 0 = automatic). The
  * result satisfies the same bound for every choice; the summation order (so
  * the rounding) depends on it. Returns QWG_ERR_SHAPE for an unsupported

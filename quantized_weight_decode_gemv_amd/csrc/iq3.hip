@@ -570,55 +570,55 @@ hipError_t iq3_launch(const GroupArgs &g, const GemvArgs &single, const float *g
 //
 // A single IQ3 GEMV of a few MB (the short-call scheme of short.hip): each
 // 64-row tile's super-blocks are split over S workgroups (tiles x S <= compute
-// units), a workgroup holds C <= kShortMaxBlocks columns with 4H wavefronts per
-// column (H = 2: one 32-weight sub-block per wavefront; H = 1 for three or four
-// columns: a quant chunk of two sub-blocks), and every byte a workgroup needs
-// is requested at its start: the fp32 grid (4 KB), each column (row-major: the
-// seven 16-byte granules of each row's block window, clamped into the buffer
-// as in the stream engine; tile layout: the 6272-byte column), the
-// activations as scalar loads. No sign-folded table is built (that takes a
-// workgroup ~0.8 us): each group of four weights reads its grid row (fp32)
-// from LDS and flips the signs by XOR. (Reading the four signs' masks from a
-// 16-entry LDS table as well doubled the LDS traffic, which bounds these
-// kernels.) The grid must be fp16-exact as for the other IQ3 GEMV engines
-// (checked; NaN rows otherwise).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kIq3ShortGrid = 0;       // fp32 grid [256][4]
-constexpr int kIq3ShortVote = 4096;    // grid-exactness vote
-constexpr int kIq3ShortCols = 4112;    // columns (16-byte aligned)
+// units), a workgroup holds C <= kShortMaxBlocks columns with four wavefronts
+// per column (wavefront 4j + G: quant chunk G of column j), and every byte a
+// workgroup needs is requested at its start: the fp32 grid (4 KB, first), each
+// column (row-major: the seven 16-byte granules of each row's block window,
+// clamped into the buffer as in the stream engine; tile layout: the 6272-byte
+// column), the activations as scalar loads. The sign-folded table of the
+// stream engine is built while the columns are in flight: the grid arrives
+// from L2 well before them, so waiting for it leaves the columns' copies
+// outstanding (per-wavefront memory counters complete in order). A version
+// that read the fp32 grid rows and flipped the signs per weight instead of the
+// table (no build, 16-byte LDS reads, three more VALU ops per weight) took
+// 7.8 / 7.1 us for the two 4.4 MB shapes of the IQ3 configuration.
+constexpr int kIq3ShortGrid = 32768;   // staged fp32 grid [256][4], after the table
+constexpr int kIq3ShortVote = kIq3ShortGrid + 4096;    // grid-exactness vote
+constexpr int kIq3ShortCols = kIq3ShortVote + 16;      // columns (16-byte aligned)
 constexpr int iq3_short_col(bool tl) { return tl ? kIq3TileCol : kTileRows * 112; }
-constexpr int iq3_short_lds(int c, int h, bool tl) {
-    return kIq3ShortCols + c * iq3_short_col(tl) + 4 * h * c * kTileRows * 4;
+constexpr int iq3_short_lds(int c, bool tl) {
+    return kIq3ShortCols + c * iq3_short_col(tl) + 4 * c * kTileRows * 4;
 }
 
-// One 32-weight sub-block (index dwords i0, i1: groups 0-3, 4-7; its sign /
-// scale word) of this lane's row against 32 activations. Weight t's sign bit
-// (bit t of the expanded sign word) is moved to bit 31 and XORed into the
-// grid value (exact for any fp32 grid).
-template <typename XAt>
-__device__ __forceinline__ float iq3_short_sub(uint32_t i0, uint32_t i1, uint32_t word, float dq,
-                                               XAt xat) {
-    const uint32_t s8 = iq3_signs(word);
-    const float db = dq * (float)(2u * (word >> 28) + 1u);
-    u32x4 g[8];
+// iq3_dot with the chunk's 64 activations already in registers.
+template <int G, typename XAt>
+__device__ __forceinline__ float iq3_dot_regs(const Iq3Raw &r, XAt xat, float acc) {
+    const float dq = h2f_lo(r.d16) * 0.25f;   // d*(0.5+code)*0.5 == (d/4)*(2*code+1), exact
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t idx = ((k < 4 ? i0 : i1) >> (8 * (k & 3))) & 255u;
-        g[k] = lds_load<u32x4>(kIq3ShortGrid + 16 * idx);
-    }
-    const uint32_t top = opaque(0x80000000u);
-    auto w = [&](uint32_t gv, int t) {
-        return __builtin_bit_cast(float, gv ^ ((s8 << (31 - t)) & top));
-    };
-    float s0 = 0.0f, s1 = 0.0f;
+    for (int half = 0; half < 2; ++half) {
+        const uint32_t word = r.words[half];
+        const uint32_t s8 = iq3_signs(word);
+        const uint32_t ne = s8 & 0x0F0F0F0Fu;
+        const uint32_t no = (s8 >> 4) & 0x0F0F0F0Fu;
+        const float db = dq * (float)(2u * (word >> 28) + 1u);
+        u32x2 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        s0 = __builtin_fmaf(w(g[k].x, 4 * k + 0), xat(4 * k + 0), s0);
-        s1 = __builtin_fmaf(w(g[k].y, 4 * k + 1), xat(4 * k + 1), s1);
-        s0 = __builtin_fmaf(w(g[k].z, 4 * k + 2), xat(4 * k + 2), s0);
-        s1 = __builtin_fmaf(w(g[k].w, 4 * k + 3), xat(4 * k + 3), s1);
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t sel = (uint32_t)(k & 3) | ((uint32_t)(4 + (k >> 1)) << 8) | 0x0C0C0000u;
+            const uint32_t ti = __builtin_amdgcn_perm((k & 1) ? no : ne, r.idx[2 * half + (k >> 2)], sel);
+            v[k] = lds_load<u32x2>(ti << 3);
+        }
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            s0 = __builtin_fmaf(h2f_lo(v[k].x), xat(32 * half + 4 * k + 0), s0);
+            s1 = __builtin_fmaf(h2f_hi(v[k].x), xat(32 * half + 4 * k + 1), s1);
+            s0 = __builtin_fmaf(h2f_lo(v[k].y), xat(32 * half + 4 * k + 2), s0);
+            s1 = __builtin_fmaf(h2f_hi(v[k].y), xat(32 * half + 4 * k + 3), s1);
+        }
+        acc = __builtin_fmaf(db, s0 + s1, acc);
     }
-    return db * (s0 + s1);
+    return acc;
 }
 
 template <int G>
@@ -632,18 +632,39 @@ __device__ __forceinline__ void iq3_short_fetch(const uint8_t *col, int layout, 
         iq3_fetch<G>(col + 112 * lane + (sh & 12u), sh, r);
 }
 
-template <int C, int H>
-__global__ __launch_bounds__(256 * C * H) void iq3_short_kernel(GemvArgs a, ShortState st,
-                                                                const float *grid) {
+template <int G>
+__device__ __forceinline__ float iq3_short_column(const GemvArgs &a, const uint8_t *col, int row,
+                                                  int b, int lane, const float (&xs)[64]) {
+    const bool tl = a.layout == kLayoutTiles;
+    const uintptr_t wb = (uintptr_t)a.w;
+    const uintptr_t we = wb + (uintptr_t)a.n_out * (uintptr_t)a.row_bytes;
+    const uintptr_t start = wb + (uintptr_t)min(row, a.n_out - 1) * (uintptr_t)a.row_bytes +
+                            (uintptr_t)kIq3Bytes * b;
+    Iq3Raw raw;
+    iq3_short_fetch<G>(col, a.layout, (uint32_t)start & 15u, lane, raw);
+    if (!tl) {
+        // a window granule that lies partly outside the buffer was clamped:
+        // that row's block comes from 2-byte loads instead (at most twice per matrix)
+        const bool head = (wb & 15) != 0 && row == 0 && b == 0;
+        const bool tail = (we & 15) != 0 && row == a.n_out - 1 && b == a.nb - 1;
+        if (head || tail)
+            iq3_fetch_direct<G>(a.w + (int64_t)row * a.row_bytes + kIq3Bytes * b,
+                                a.layout == kLayoutRowsXxs, raw);
+    }
+    return iq3_dot_regs<G>(raw, [&](int i) { return xs[i]; }, 0.0f);
+}
+
+template <int C>
+__global__ __launch_bounds__(256 * C) void iq3_short_kernel(GemvArgs a, ShortState st,
+                                                            const float *grid) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    constexpr int WPC = 4 * H;
+    constexpr int W = 4 * C;
     const bool tl = a.layout == kLayoutTiles;
     const int colsz = tl ? kIq3TileCol : kTileRows * 112;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int j = wave / WPC;
-    const int G = (wave / H) & 3;
-    const int hh = wave % H;
+    const int j = wave >> 2;
+    const int G = wave & 3;
     int tile, split;
     if (!short_item(a, tile, split)) return;
     const int kb0 = split * a.nb / a.splits;
@@ -654,14 +675,20 @@ __global__ __launch_bounds__(256 * C * H) void iq3_short_kernel(GemvArgs a, Shor
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     const uint32_t colb = lds0 + kIq3ShortCols + j * colsz;
 
+    // The tile's epoch (split launches; used at the end), the grid (wavefronts
+    // 0..3, 1 KB each), then the columns: copies G and G + 4 of each column's
+    // seven 1 KB pieces.
+    uint32_t epoch = 0;
+    if (a.splits > 1 && wave == 0)
+        epoch = __hip_atomic_load(&st.epochs[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (wave < 4) dma16((const uint8_t *)grid + 16 * (64 * wave + lane), lds0 + kIq3ShortGrid + 1024 * wave);
-    // This lane's row block window (row-major), for the copies and the fetch.
-    const uintptr_t wb = (uintptr_t)a.w;
-    const uintptr_t we = wb + (uintptr_t)a.n_out * (uintptr_t)a.row_bytes;
-    const uintptr_t lo16 = (wb + 15) & ~(uintptr_t)15;    // first whole granule
-    const uintptr_t hi16 = (we & ~(uintptr_t)15) - 16;    // last whole granule
+    int ncopy = 0;
     if (live) {
-        for (int q = wave % WPC; q < 7; q += WPC) {
+        const uintptr_t wb = (uintptr_t)a.w;
+        const uintptr_t we = wb + (uintptr_t)a.n_out * (uintptr_t)a.row_bytes;
+        const uintptr_t lo16 = (wb + 15) & ~(uintptr_t)15;    // first whole granule
+        const uintptr_t hi16 = (we & ~(uintptr_t)15) - 16;    // last whole granule
+        for (int q = G; q < 7; q += 4) {
             const uint32_t dst = colb + 1024 * q;
             if (tl) {
                 if (q < 6 || lane < 8)
@@ -675,64 +702,42 @@ __global__ __launch_bounds__(256 * C * H) void iq3_short_kernel(GemvArgs a, Shor
                 gaddr = gaddr < lo16 ? lo16 : (gaddr > hi16 ? hi16 : gaddr);
                 dma16((const void *)gaddr, dst);
             }
+            ++ncopy;
         }
     }
-    if (threadIdx.x == 0) lds_store<uint32_t>(kIq3ShortVote, 0u);
-    constexpr int NX = 64 / H;
     const int xb = live ? b : kb0;
-    const cfloat_p xg = as_scalar(a.x) + (int64_t)kQK * xb + 64 * G + NX * hh;
-    float xs[NX];
+    const cfloat_p xg = as_scalar(a.x) + (int64_t)kQK * xb + 64 * G;
+    float xs[64];
 #pragma unroll
-    for (int i = 0; i < NX; ++i) xs[i] = xg[i];
-    uint32_t epoch = 0;
-    if (a.splits > 1 && wave == 0)
-        epoch = __hip_atomic_load(&st.epochs[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_vmcnt<0>();
-    lds_barrier();
+    for (int i = 0; i < 64; ++i) xs[i] = xg[i];
+    volatile __attribute__((address_space(3))) uint32_t *vote =
+        (volatile __attribute__((address_space(3))) uint32_t *)(size_t)(lds0 + kIq3ShortVote);
+    if (threadIdx.x == 0) *vote = 0u;
 
-    // grid exactness (wavefronts 0..3: one grid row per lane)
-    if (wave < 4) {
-        const f32x4 gv = lds_load<f32x4>(kIq3ShortGrid + 16 * (64 * wave + lane));
+    // The grid is in LDS once this wavefront's column copies (issued after it)
+    // are the only ones outstanding.
+    if (wave < 4) wait_vmcnt_upto(ncopy);
+    lds_barrier();
+    {
+        const int t = threadIdx.x;
+        const int i = t & 255;
+        const f32x4 gv = lds_load<f32x4>(kIq3ShortGrid + 16 * i);
+        const float4 g4 = {gv[0], gv[1], gv[2], gv[3]};
+        for (int s = t >> 8; s < 16; s += W / 4) iq3_table_entry(s, i, g4);
         const bool exact = fp16_exact(gv[0]) && fp16_exact(gv[1]) && fp16_exact(gv[2]) && fp16_exact(gv[3]);
-        if (__builtin_amdgcn_ballot_w64(!exact) != 0 && lane == 0) lds_store<uint32_t>(kIq3ShortVote, 1u);
+        if (__builtin_amdgcn_ballot_w64(!exact) != 0 && lane == 0) *vote = 1u;
     }
+    wait_vmcnt<0>();
+    lds_barrier();   // the columns and the table
+
     float acc = 0.0f;
     if (live) {
-        const uintptr_t start = wb + (uintptr_t)min(row, a.n_out - 1) * (uintptr_t)a.row_bytes +
-                                (uintptr_t)kIq3Bytes * b;
-        const uint32_t sh = (uint32_t)start & 15u;
         const uint8_t *col = smem + (colb - lds0);
-        Iq3Raw raw;
         switch (G) {
-            case 0: iq3_short_fetch<0>(col, a.layout, sh, lane, raw); break;
-            case 1: iq3_short_fetch<1>(col, a.layout, sh, lane, raw); break;
-            case 2: iq3_short_fetch<2>(col, a.layout, sh, lane, raw); break;
-            default: iq3_short_fetch<3>(col, a.layout, sh, lane, raw); break;
-        }
-        if (!tl) {
-            // a window granule that lies partly outside the buffer was clamped:
-            // that row's block comes from 2-byte loads instead (at most twice per matrix)
-            const bool head = (wb & 15) != 0 && row == 0 && b == 0;
-            const bool tail = (we & 15) != 0 && row == a.n_out - 1 && b == a.nb - 1;
-            if (head || tail) {
-                const bool xxs = a.layout == kLayoutRowsXxs;
-                const uint8_t *blk = a.w + (int64_t)row * a.row_bytes + kIq3Bytes * b;
-                switch (G) {
-                    case 0: iq3_fetch_direct<0>(blk, xxs, raw); break;
-                    case 1: iq3_fetch_direct<1>(blk, xxs, raw); break;
-                    case 2: iq3_fetch_direct<2>(blk, xxs, raw); break;
-                    default: iq3_fetch_direct<3>(blk, xxs, raw); break;
-                }
-            }
-        }
-        const float dq = h2f_lo(raw.d16) * 0.25f;   // d*(0.5+code)*0.5 == (d/4)*(2*code+1)
-        if constexpr (H == 2) {
-            const bool hi = hh != 0;
-            acc = iq3_short_sub(hi ? raw.idx[2] : raw.idx[0], hi ? raw.idx[3] : raw.idx[1],
-                                hi ? raw.words[1] : raw.words[0], dq, [&](int i) { return xs[i]; });
-        } else {
-            acc = iq3_short_sub(raw.idx[0], raw.idx[1], raw.words[0], dq, [&](int i) { return xs[i]; });
-            acc += iq3_short_sub(raw.idx[2], raw.idx[3], raw.words[1], dq, [&](int i) { return xs[32 + i]; });
+            case 0: acc = iq3_short_column<0>(a, col, row, b, lane, xs); break;
+            case 1: acc = iq3_short_column<1>(a, col, row, b, lane, xs); break;
+            case 2: acc = iq3_short_column<2>(a, col, row, b, lane, xs); break;
+            default: acc = iq3_short_column<3>(a, col, row, b, lane, xs); break;
         }
     }
     float *red = (float *)(smem + kIq3ShortCols + C * colsz);
@@ -740,8 +745,11 @@ __global__ __launch_bounds__(256 * C * H) void iq3_short_kernel(GemvArgs a, Shor
     lds_barrier();
     if (wave != 0) return;
     float total = red[lane];
-    for (int w = 1; w < WPC * C; ++w) total += red[w * 64 + lane];
-    if (lds_load<uint32_t>(kIq3ShortVote) != 0u) total = __builtin_nanf("");
+    for (int w = 1; w < W; ++w) total += red[w * 64 + lane];
+    if (*vote != 0u) total = __builtin_nanf("");
+    // (the epoch's first use: the compiler's wait for its load goes here, not
+    // ahead of the table build)
+    asm volatile("" : "+v"(epoch));
     short_epilogue(a, st, tile, split, epoch, total);
 }
 
@@ -806,14 +814,11 @@ hipError_t launch_iq3_short(const GemvArgs &a, const ShortState &st, const float
     const int cols = (a.nb + a.splits - 1) / a.splits;
     const dim3 grid_dim(short_grid(a.tiles, a.splits));
     if (cols == 1)
-        hipLaunchKernelGGL((iq3_short_kernel<1, 2>), grid_dim, dim3(512), iq3_short_lds(1, 2, tl), s,
-                           a, st, grid);
+        hipLaunchKernelGGL((iq3_short_kernel<1>), grid_dim, dim3(256), iq3_short_lds(1, tl), s, a, st, grid);
     else if (cols == 2)
-        hipLaunchKernelGGL((iq3_short_kernel<2, 2>), grid_dim, dim3(1024), iq3_short_lds(2, 2, tl), s,
-                           a, st, grid);
+        hipLaunchKernelGGL((iq3_short_kernel<2>), grid_dim, dim3(512), iq3_short_lds(2, tl), s, a, st, grid);
     else
-        hipLaunchKernelGGL((iq3_short_kernel<4, 1>), grid_dim, dim3(1024), iq3_short_lds(4, 1, tl), s,
-                           a, st, grid);
+        hipLaunchKernelGGL((iq3_short_kernel<4>), grid_dim, dim3(1024), iq3_short_lds(4, tl), s, a, st, grid);
     return hipGetLastError();
 }
 
