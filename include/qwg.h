@@ -59,11 +59,15 @@
  *     one another or calls on that stream. Concurrent calls on different
  *     streams never share a workspace. The summation order is fixed by the
  *     shapes, so results are deterministic.
- *   - Short batch-1 Q4_K calls (at most one workgroup per compute unit) whose
- *     rows are split add the partial sums through tagged words: the last
- *     split's workgroup waits for its peers' words, which relies on all of a
- *     launch's workgroups becoming resident. The wait is bounded (1 s); if it
- *     gives up, the tile's rows are stored as NaN.
+ *   - Short batch-1 Q4_K and IQ3 calls (at most one workgroup per compute
+ *     unit) whose rows are split add the partial sums through tagged words:
+ *     the last split's workgroup waits for its peers' words, which relies on
+ *     all of a launch's workgroups becoming resident (true on a device that
+ *     runs nothing else that holds its compute units for long). The wait is
+ *     bounded (1 s); if it gives up, the tile's rows are stored as NaN, and
+ *     later split calls on that stream's workspace may read words left by the
+ *     late workgroups: release the workspace (qwg_workspace_release) after
+ *     such a result.
  *   - Errors are reported by the returned status (QWG_* below); the library
  *     never aborts, never throws and writes nothing on a validation error.
  *     Validation happens on the host before any HIP call.
