@@ -127,13 +127,17 @@ template <int W, int R, bool TL>
 struct Iq3Cfg {
     static constexpr int kBps = W / 4;                   // super-blocks per stage
     static constexpr int kWin = 112;                     // bytes per row window
-    static constexpr int kCol = TL ? kIq3TileCol : kTileRows * kWin;  // one super-block of a tile
+    // one super-block of a tile (tile layout: the column, then a private copy of
+    // its 128 d bytes for each of the four quant-chunk wavefronts)
+    static constexpr int kCol = TL ? kIq3TileCol + 4 * 128 : kTileRows * kWin;
     static constexpr int kSlot = kBps * kCol;
     static constexpr int kTable = 32768;                 // at LDS address 0
     static constexpr int kGrid = kTable;                 // staged fp32 grid, 4 KB
     static constexpr int kRing = kGrid + 256 * 16;
-    static constexpr int kRed = kRing + R * kSlot;       // [W][64] fp32 row sums
-    static constexpr int kLds = kRed + W * 64 * 4;
+    static constexpr int kRed = kRing + R * kSlot;       // [2][W][64] fp32 row sums
+    static constexpr int kLds = kRed + 2 * W * 64 * 4;
+    // copy instructions per wavefront and stage (tile layout: indices, words, d)
+    static constexpr int kCps = TL ? 3 : 2;
 };
 
 // One work item as a cursor sees it.
@@ -263,6 +267,22 @@ __device__ __forceinline__ void iq3_fetch_tiled(const uint8_t *col, int lane, Iq
     r.d16 = *(const uint16_t *)(col + kIq3TileD + 2 * lane);
 }
 
+// The same with this wavefront's private copy of the column's d bytes at
+// col + dcopy (the stream engine's barrier-free tile-layout stages).
+template <int G>
+__device__ __forceinline__ void iq3_fetch_tiled_own_d(const uint8_t *col, int lane, uint32_t dcopy,
+                                                      Iq3Raw &r) {
+    const uint4 q = *(const uint4 *)(col + G * 1024 + 16 * lane);
+    const uint2 w = *(const uint2 *)(col + kIq3TileWords + G * 512 + 8 * lane);
+    r.idx[0] = q.x;
+    r.idx[1] = q.y;
+    r.idx[2] = q.z;
+    r.idx[3] = q.w;
+    r.words[0] = w.x;
+    r.words[1] = w.y;
+    r.d16 = *(const uint16_t *)(col + dcopy + 2 * lane);
+}
+
 // From global memory, 2 bytes at a time (the block is 2-byte aligned), in
 // either byte order.
 template <int G>
@@ -388,12 +408,15 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
                           (uint32_t)d.a.row_bytes +
                       cgran[i];
     };
-    // Tile layout: wavefront G copies its index bytes (1 KB, every lane) and its
-    // words (512 B, lanes 0..31); wavefront 3's lanes 32..39 also copy the d
-    // values, which follow its words in the column.
+    // Tile layout: wavefront G copies its index bytes (1 KB, every lane), its
+    // words (512 B, lanes 0..31) and its own copy of the column's d bytes (128
+    // B, lanes 0..7, after the column): every byte a wavefront reads in a stage
+    // is one it copied, so stages need no workgroup barrier, only the
+    // wavefront's own wait for its copies.
     const uint32_t t_off0 = (uint32_t)(G * 1024 + 16 * lane);
     const uint32_t t_off1 = (uint32_t)(kIq3TileWords + G * 512 + 16 * lane);
-    const bool t_second = lane < (G == 3 ? 40 : 32);
+    const uint32_t t_off2 = (uint32_t)(kIq3TileD + 16 * lane);
+    constexpr uint32_t t_dcopy = (uint32_t)(kIq3TileCol + 128 * G);
     prep_copy();
     uint32_t flags = 0;  // bit k: this wavefront's copies are in ring slot k
     auto issue_next = [&]() {
@@ -404,7 +427,8 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
                 const uint32_t colb = lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol;
                 const uint8_t *src = d.sb + (int64_t)b * kIq3TileCol;
                 dma16_stream(src + t_off0, colb + G * 1024);
-                if (t_second) dma16_stream(src + t_off1, colb + kIq3TileWords + G * 512);
+                if (lane < 32) dma16_stream(src + t_off1, colb + kIq3TileWords + G * 512);
+                if (lane < 8) dma16_stream(src + t_off2, colb + t_dcopy);
             } else {
                 const uint32_t base =
                     lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol + G * (16 * C::kWin);
@@ -443,7 +467,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
     // buffer, idle until the first item ends.
     volatile uint32_t *vote = (volatile uint32_t *)(smem + C::kRed);
     if (threadIdx.x == 0) *vote = 0u;
-    if (wave < 4) wait_vmcnt_upto(2 * __builtin_popcount(flags));
+    if (wave < 4) wait_vmcnt_upto(C::kCps * __builtin_popcount(flags));
     lds_barrier();
     {
         const int t = threadIdx.x;
@@ -459,6 +483,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
 
     float *red = (float *)(smem + C::kRed);
     int slot_c = 0;
+    int parity = 0;   // row-sum buffer of this item (two, alternating)
     for (;;) {
         const int row = c.row0 + lane;
         // low bits of this lane's row address (block offsets within granules)
@@ -469,15 +494,22 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
             // Copies of the stages after this one may stay in flight.
             const int nxt = slot_c + 1 == R ? 0 : slot_c + 1;
             int younger = 0;
-            if (R >= 3 && pending > 1) younger += 2 * (int)((flags >> nxt) & 1u);
-            if (R >= 4 && pending > 2) younger += 2 * (int)((flags >> (nxt + 1 == R ? 0 : nxt + 1)) & 1u);
+            if (R >= 3 && pending > 1) younger += C::kCps * (int)((flags >> nxt) & 1u);
+            if (R >= 4 && pending > 2) younger += C::kCps * (int)((flags >> (nxt + 1 == R ? 0 : nxt + 1)) & 1u);
             wait_vmcnt_upto(younger);
-            lds_barrier();   // stage in slot_c complete for every wavefront (and the table)
+            if constexpr (TL) {
+                // this wavefront's own copies of the stage are in; its reads of
+                // the slot refilled below (the previous step's) are complete
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            } else {
+                lds_barrier();   // stage in slot_c complete for every wavefront (and the table)
+            }
             issue_next();    // refill the slot computed in the previous step
             const int b = c.kb0 + s * BPS + j;
             if (TL && b < c.kb1) {
                 Iq3Raw raw;
-                iq3_fetch_tiled<G>(smem + C::kRing + slot_c * C::kSlot + j * C::kCol, lane, raw);
+                iq3_fetch_tiled_own_d<G>(smem + C::kRing + slot_c * C::kSlot + j * C::kCol, lane,
+                                         t_dcopy, raw);
                 acc = iq3_dot<G>(raw, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
             } else if (b < c.kb1) {
                 const uint32_t sh = (rlo + (uint32_t)(kIq3Bytes * b)) & 15u;
@@ -501,12 +533,16 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
             --pending;
             slot_c = nxt;
         }
-        // row sums of the W wavefronts, in wavefront order
-        red[wave * 64 + lane] = acc;
+        // row sums of the W wavefronts, in wavefront order (two buffers: with no
+        // barrier between stages, a wavefront can reach the next item's end
+        // while wavefront 0 still reads this one's)
+        float *rb = red + parity * W * 64;
+        parity ^= 1;
+        rb[wave * 64 + lane] = acc;
         lds_barrier();
         if (wave == 0) {
-            float tsum = red[lane];
-            for (int w = 1; w < W; ++w) tsum += red[w * 64 + lane];
+            float tsum = rb[lane];
+            for (int w = 1; w < W; ++w) tsum += rb[w * 64 + lane];
             if (grid_bad) tsum = __builtin_nanf("");
             const float total[1] = {tsum};
             tile_epilogue<1>(c.a, c.tile, c.split, total);
