@@ -59,7 +59,10 @@
  *     one another or calls on that stream. Concurrent calls on different
  *     streams never share a workspace. The summation order is fixed by the
  *     shapes, so results are deterministic.
- *   - Short batch-1 Q4_K and IQ3 calls (at most one workgroup per compute
+ *   - Short batch-1 Q4_K calls (at most one 64-row tile per compute unit)
+ *     whose rows hold at most 8 super-blocks (n_in <= 2048) take whole rows
+ *     per workgroup: no split and no workspace.
+ *   - Other short batch-1 Q4_K and IQ3 calls (at most one workgroup per compute
  *     unit) whose rows are split add the partial sums through tagged words:
  *     the last split's workgroup waits for its peers' words, which relies on
  *     all of a launch's workgroups becoming resident (true on a device that
@@ -124,7 +127,7 @@ int64_t qwg_row_bytes(int fmt, int64_t n_in);
  * How a GEMV/GEMM of this shape is decomposed (introspection for tests and
  * tuning): the number of workgroups that share each 64-row tile by splitting
  * the n_in sum (1 = no split), or a negative status for invalid sizes. For
- * Q4_K the plan of the short-call kernel depends on the current device's
+ * Q4_K the plan of the short-call kernels depends on the current device's
  * compute-unit count; with no device the vector engine's plan is returned.
  */
 int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out);
@@ -317,7 +320,7 @@ int qwg_gemm_q4k_noalloc(float *y, const float *x, const void *w, int64_t n_in, 
  * (batch >= 2 only: resident workgroups walk the (tile, split) items with a
  * ring of stages that runs ahead across them); 0 = automatic among these
  * engines (the persistent stream for batch >= 2; qwg_gemm_q4k itself runs a
- * batch-1 matrix of up to 256 tiles on the short-call kernel instead); `splits`
+ * batch-1 matrix of up to 256 tiles on the short-call kernels instead); `splits`
  * workgroups sharing each tile's n_in sum (1..n_in/256; 0 = automatic). The
  * result satisfies the same bound for every choice; the summation order (so
  * the rounding) depends on it. Returns QWG_ERR_SHAPE for an unsupported

@@ -248,6 +248,19 @@ int short_splits(int tiles, int nb) {
     return sp;
 }
 
+// Batch-1 Q4_K calls on the row-group kernel: the short-call matrices whose
+// rows hold at most eight super-blocks. (Not larger matrices: the LM head,
+// 32000 x 2048, took 17.4 us per call on row groups against 11.0 us on the
+// stream engine, event time on one box.) QWG_ROWS=0 turns it off (A/B
+// measurements: those matrices then run on the split short-call kernel).
+bool rows_engine(int tiles, int nb) {
+    static const bool off = [] {
+        const char *e = getenv("QWG_ROWS");
+        return e != nullptr && e[0] == '0';
+    }();
+    return !off && q4k_rows_fits(nb) && short_splits(tiles, nb) > 0;
+}
+
 // IQ3 stream engine shape. Measured on MI355X: grouped streams run best with
 // 8-wavefront workgroups (two per CU), single GEMVs with 16 (one per CU, four
 // super-blocks per stage), both with a 2-stage ring. `waves` (if nonzero)
@@ -465,6 +478,7 @@ int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
         if (slots <= 0) return -QWG_ERR_HIP;
         return iq3_splits(tiles, (int)(n_in / kQK), slots);
     }
+    if (rows_engine(tiles, (int)(n_in / kQK))) return 1;
     const int ss = short_splits(tiles, (int)(n_in / kQK));
     return ss > 0 ? ss : choose_splits(tiles, (int)(n_in / kQK));
 }
@@ -586,6 +600,7 @@ int gemm_q4k(float *y, const float *x, const void *w, int64_t n_in, int64_t n_ou
     // weights: 12.4 us against 14.2-15.8 us on the matrix cores, while on the
     // layer shapes of 32-88 tiles and at batch 3..8 the matrix cores win or
     // tie: bench.py --workload gemm_ab); otherwise the matrix cores.
+    if (batch == 1 && rows_engine(a.tiles, a.nb)) return hip_status(launch_q4k_rows(a, false, stream));
     if (batch == 1) {
         const int ss = short_splits(a.tiles, a.nb);
         if (ss > 0) {
@@ -767,6 +782,7 @@ int qwg_gemv_q4k_tiled(float *y, const float *x, const void *w, int64_t n_in, in
     GemvArgs a;
     fill_shape(a, w, x, nullptr, y, n_in, n_out, kQ4kBytes);
     a.layout = kLayoutTiles;
+    if (rows_engine(a.tiles, a.nb)) return hip_status(launch_q4k_rows(a, true, (hipStream_t)stream));
     const int ss = short_splits(a.tiles, a.nb);
     if (ss > 0) {
         a.splits = ss;

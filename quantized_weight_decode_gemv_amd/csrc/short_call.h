@@ -41,6 +41,10 @@ struct ShortState {
 int short_plan_splits(int tiles, int nb, int cus);
 // a.splits set by the caller (short_plan_splits); st needed when a.splits > 1.
 hipError_t launch_q4k_short(const GemvArgs &a, const ShortState &st, bool tiled, hipStream_t s);
+// Row-group kernel (Q4_K, batch 1, rows of nb <= 8 super-blocks): eight whole
+// rows per workgroup, no split sums (so no workspace).
+bool q4k_rows_fits(int nb);
+hipError_t launch_q4k_rows(const GemvArgs &a, bool tiled, hipStream_t s);
 // IQ3 (a.layout: rows, llama.cpp-order rows or tiles), the same plan rule.
 hipError_t launch_iq3_short(const GemvArgs &a, const ShortState &st, const float *grid,
                             hipStream_t s);

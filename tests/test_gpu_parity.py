@@ -234,13 +234,42 @@ def test_gemm_q4k_ex_rejects_bad_plans():
 
 def test_gemv_q4k_covers_split_and_unsplit_plans():
     # vector engine: many tiles (no split), a long row (split); short-call
-    # kernel: up to one workgroup per compute unit, at most 8 splits
+    # kernel: up to one workgroup per compute unit, at most 8 splits; rows of
+    # at most 8 super-blocks on those matrices: the row-group kernel (no split)
     assert qwg.plan_splits(0, 256, 131072 + 5) == 1
     assert qwg.plan_splits(0, 65536, 3) > 8
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for n_in, n_out in [(2048, 2048), (5632, 2048), (5632, 200), (2048, 5632), (256, 64)]:
+    for n_in, n_out in [(2048, 2048), (5632, 2048), (5632, 200), (2048, 5632), (256, 64),
+                        (3072, 640)]:
         tiles, nb = -(-n_out // 64), n_in // 256
-        assert qwg.plan_splits(0, n_in, n_out) == min(cus // tiles, nb, 8), (n_in, n_out)
+        want = 1 if nb <= 8 else min(cus // tiles, nb, 8)
+        assert qwg.plan_splits(0, n_in, n_out) == want, (n_in, n_out)
+
+
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (7, 512), (9, 2048), (63, 1792), (65, 768),
+                                        (1000, 2048), (2047, 1280), (8192, 2048)])
+def test_gemv_q4k_row_groups(n_out, n_in):
+    # Row-group kernel (batch 1, at most 8 super-blocks per row, a matrix the
+    # split short-call plan covers: at least two workgroups per tile fit the
+    # compute units): eight whole rows per workgroup, lanes over (row,
+    # super-block); ragged last groups, rows past n_out untouched, both layouts
+    # with the same bits, repeat calls with the same bits.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert -(-n_out // 64) <= cus // 2
+    assert qwg.plan_splits(0, n_in, n_out) == 1
+    w, x = _gemv_q4k_case(n_out, n_in, 111, n_in // 256)
+    wd, xd = dev(w), dev(x)
+    yr, sr = oracle.gemv_q4k(w, x, n_in, n_out)
+    buf = torch.full((n_out + 16,), float("nan"), device="cuda")
+    qwg.gemv_q4k(wd, xd, out=buf[:n_out])
+    y = host(buf)
+    assert np.isnan(y[n_out:]).all()
+    assert_bound(y[:n_out], yr, sr, f"{n_out}x{n_in}")
+    wt = qwg.pack_q4k_tiles(wd, n_in)
+    t = host(qwg.gemv_q4k_tiled(wt, xd, n_out))
+    assert_bits(t, y[:n_out], "tile layout")
+    for _ in range(2):
+        assert_bits(host(qwg.gemv_q4k(wd, xd)), y[:n_out], "repeat")
 
 
 @pytest.mark.parametrize("n_out,n_in", [(64, 3584), (64, 3840), (200, 5632), (2048, 5632),

@@ -42,8 +42,9 @@ def _ready():
 
 
 @pytest.mark.parametrize("first,second", [
-    # (n_out, n_in, batch): split plans on the vector engine (batch 1) and on
-    # the matrix cores (batch >= 2), then a smaller input
+    # (n_out, n_in, batch): split plans on the batch-1 engines and on the
+    # matrix cores (batch >= 2), then a smaller input
+    ((2048, 5632, 1), (200, 5632, 1)),
     ((2048, 5632, 1), (256, 2048, 1)),
     ((2048, 2048, 8), (130, 768, 3)),
     ((5632, 2048, 1), (7, 256, 1)),
