@@ -67,8 +67,8 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/chain.hip",
 # WRITE_SIZE runs of this script, each scaled by the same counter on a plain device copy of known
 # size (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_chain_c5.md). Valid only for the
 # kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "5dcff5c223a368c22def3b78f34f70f07b9996fde2648ac281c21d795dd8f38b",
-           "fetch_bytes": 620858880, "write_bytes": 6816768}
+TRAFFIC = {"sources_sha256": "1be5b49d00b0b8dd51b9be1b287dc8519067ddad506dbe4ed965040349fd4a6c",
+           "fetch_bytes": 620770944, "write_bytes": 6816768}
 
 
 def kernel_sources_sha256() -> str:

@@ -108,6 +108,41 @@ __device__ __forceinline__ void load8_tagged(const uint64_t *const (&p)[8], uint
         : "memory");
 }
 
+// Two, three or four agent-coherent 8-byte loads back to back, one wait.
+__device__ __forceinline__ void load2_tagged(const uint64_t *p0, const uint64_t *p1, uint64_t &v0,
+                                             uint64_t &v1) {
+    asm volatile(
+        "global_load_dwordx2 %0, %2, off sc1\n\t"
+        "global_load_dwordx2 %1, %3, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v0), "=&v"(v1)
+        : "v"(p0), "v"(p1)
+        : "memory");
+}
+__device__ __forceinline__ void load3_tagged(const uint64_t *p0, const uint64_t *p1,
+                                             const uint64_t *p2, uint64_t &v0, uint64_t &v1,
+                                             uint64_t &v2) {
+    asm volatile(
+        "global_load_dwordx2 %0, %3, off sc1\n\t"
+        "global_load_dwordx2 %1, %4, off sc1\n\t"
+        "global_load_dwordx2 %2, %5, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2)
+        : "v"(p0), "v"(p1), "v"(p2)
+        : "memory");
+}
+__device__ __forceinline__ void load4_tagged(const uint64_t *const (&p)[4], uint64_t (&v)[4]) {
+    asm volatile(
+        "global_load_dwordx2 %0, %4, off sc1\n\t"
+        "global_load_dwordx2 %1, %5, off sc1\n\t"
+        "global_load_dwordx2 %2, %6, off sc1\n\t"
+        "global_load_dwordx2 %3, %7, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+        : "memory");
+}
+
 // Flags: one copy of all nwg flags per reader XCD (workgroup b runs on XCD
 // b % 8), copies kFlagCopyWords apart; a workgroup stores its flag into every
 // copy and polls the copy of its own XCD, so each copy's lines are read by
@@ -169,6 +204,8 @@ __device__ bool wait_done(const ChainArgs &c, const uint64_t *done, int n, uint3
             // up to eight 8-byte loads per lane (64 words each) in flight, one
             // wait; rounds of fewer words load fewer
             const int m = min(n - j0, 512);
+            // as many loads as the round has 64-word groups (no repeated
+            // reads of the last word: every workgroup polls these lines)
             if (m <= 64) {
                 uint64_t v;
                 asm volatile("global_load_dwordx2 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)"
@@ -176,6 +213,26 @@ __device__ bool wait_done(const ChainArgs &c, const uint64_t *done, int n, uint3
                              : "v"(done + j0 + min(lane, m - 1))
                              : "memory");
                 ok = ok && (int)((uint32_t)(v >> 32) - tag) >= 0;
+            } else if (m <= 128) {
+                uint64_t v0, v1;
+                load2_tagged(done + j0 + lane, done + j0 + min(64 + lane, m - 1), v0, v1);
+                ok = ok && (int)((uint32_t)(v0 >> 32) - tag) >= 0 &&
+                     (int)((uint32_t)(v1 >> 32) - tag) >= 0;
+            } else if (m <= 192) {
+                uint64_t v0, v1, v2;
+                load3_tagged(done + j0 + lane, done + j0 + 64 + lane,
+                             done + j0 + min(128 + lane, m - 1), v0, v1, v2);
+                ok = ok && (int)((uint32_t)(v0 >> 32) - tag) >= 0 &&
+                     (int)((uint32_t)(v1 >> 32) - tag) >= 0 &&
+                     (int)((uint32_t)(v2 >> 32) - tag) >= 0;
+            } else if (m <= 256) {
+                const uint64_t *p[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) p[k] = done + j0 + min(64 * k + lane, m - 1);
+                uint64_t v[4];
+                load4_tagged(p, v);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ok = ok && (int)((uint32_t)(v[k] >> 32) - tag) >= 0;
             } else {
                 const uint64_t *p[8];
 #pragma unroll
