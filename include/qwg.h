@@ -59,8 +59,8 @@
  *     one another or calls on that stream. Concurrent calls on different
  *     streams never share a workspace. The summation order is fixed by the
  *     shapes, so results are deterministic.
- *   - Short batch-1 Q4_K calls (at most one 64-row tile per compute unit)
- *     whose rows hold at most 8 super-blocks (n_in <= 2048) take whole rows
+ *   - Short batch-1 Q4_K and IQ3 calls (at most one 64-row tile per compute
+ *     unit) whose rows hold at most 8 blocks (n_in <= 2048) take whole rows
  *     per workgroup: no split and no workspace.
  *   - Other short batch-1 Q4_K and IQ3 calls (at most one workgroup per compute
  *     unit) whose rows are split add the partial sums through tagged words:

@@ -789,6 +789,161 @@ __global__ __launch_bounds__(256 * C) void iq3_short_kernel(GemvArgs a, ShortSta
     short_epilogue(a, st, tile, split, epoch, total);
 }
 
+// ------------------------------------------------------------------ row groups
+//
+// Rows of at most eight blocks (n_in <= 2048) on the short-call matrices: a
+// workgroup of four wavefronts takes eight whole rows, so no split sums meet
+// through memory (the Q4_K row-group kernel's scheme). Wavefront G takes quant
+// chunk G of every block, lane r + 8s row r's block s with its 64 activations
+// in registers (sixteen 16-byte loads, issued first: the grid's copy and the
+// rows' copies queue behind them, so waiting for the grid waits for them too).
+// The rows arrive as one contiguous run of 16-byte granules (row-major, either
+// byte order: 8 x nb x 98 bytes from the group's first block, granules that
+// reach outside the buffer clamped and the two blocks they hold read directly
+// as in the stream engine) or as the eight rows' slices of each tile-layout
+// column (784 bytes: index, word and d runs). The grid staging, sign-folded
+// table and exactness vote are the short-call kernel's.
+constexpr int kIq3RgRows = 8;
+constexpr int kIq3RgMaxBlocks = 8;
+constexpr int kIq3RgSlice = 784;                        // 8 rows of a tile-layout column
+constexpr int kIq3RgRegion = 448 * 16;                  // the rows' granules
+constexpr int kIq3RgRed = kIq3ShortCols + kIq3RgRegion; // [4 wavefronts][8 rows] fp32
+constexpr int kIq3RgLds = kIq3RgRed + 4 * kIq3RgRows * 4;
+static_assert(kIq3RgSlice * kIq3RgMaxBlocks <= kIq3RgRegion, "tile slices fit");
+static_assert((15 + kIq3RgRows * kIq3RgMaxBlocks * kIq3Bytes + 15) / 16 + 1 <= 448, "row runs fit");
+
+// Byte offset in a tile-layout column of granule g (0..48) of the eight-row
+// slice starting at row rit (a multiple of 8): index runs, word runs, d.
+__device__ __forceinline__ int iq3_rg_tile_off(int g, int rit) {
+    if (g < 32) return (g >> 3) * 1024 + 16 * rit + 16 * (g & 7);
+    if (g < 48) return kIq3TileWords + ((g - 32) >> 2) * 512 + 8 * rit + 16 * ((g - 32) & 3);
+    return kIq3TileD + 2 * rit;
+}
+
+template <int G>
+__device__ __forceinline__ float iq3_rows_dot(const GemvArgs &a, const uint8_t *rg, uint32_t o,
+                                              int row, int b, int r, const f32x4 (&xv)[16]) {
+    Iq3Raw raw;
+    if (a.layout == kLayoutTiles) {
+        const uint8_t *sl = rg + b * kIq3RgSlice;
+        const uint4 q = *(const uint4 *)(sl + G * 128 + 16 * r);
+        const uint2 w = *(const uint2 *)(sl + 512 + G * 64 + 8 * r);
+        raw.idx[0] = q.x;
+        raw.idx[1] = q.y;
+        raw.idx[2] = q.z;
+        raw.idx[3] = q.w;
+        raw.words[0] = w.x;
+        raw.words[1] = w.y;
+        raw.d16 = *(const uint16_t *)(sl + 768 + 2 * r);
+    } else {
+        const bool xxs = a.layout == kLayoutRowsXxs;
+        const uint8_t *win = rg + (o & ~3u);
+        if (xxs)
+            iq3_fetch_xxs<G>(win, o, raw);
+        else
+            iq3_fetch<G>(win, o, raw);
+        const uintptr_t wb = (uintptr_t)a.w;
+        const uintptr_t we = wb + (uintptr_t)a.n_out * (uintptr_t)a.row_bytes;
+        const bool head = (wb & 15) != 0 && row == 0 && b == 0;
+        const bool tail = (we & 15) != 0 && row == a.n_out - 1 && b == a.nb - 1;
+        if (head || tail) iq3_fetch_direct<G>(a.w + (int64_t)row * a.row_bytes + kIq3Bytes * b, xxs, raw);
+    }
+    return iq3_dot_regs<G>(raw, [&](int i) { return xv[i >> 2][i & 3]; }, 0.0f);
+}
+
+__global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *grid) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int R = kIq3RgRows;
+    const bool tl = a.layout == kLayoutTiles;
+    const int lane = threadIdx.x & 63;
+    const int G = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nb = a.nb;
+    const int row0 = blockIdx.x * R;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const uint32_t rgb = lds0 + kIq3ShortCols;
+    const int r = lane & (R - 1);
+    const int b = lane >> 3;
+
+    // The activations first (see above).
+    f32x4 xv[16];
+    {
+        const f32x4 *xp = (const f32x4 *)(a.x + (int64_t)kQK * min(b, nb - 1) + 64 * G);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) xv[q] = xp[q];
+    }
+    dma16((const uint8_t *)grid + 16 * (64 * G + lane), lds0 + kIq3ShortGrid + 1024 * G);
+    int ncopy = 0;
+    uint32_t o0 = 0;   // the group's first block in the copied run (row-major)
+    if (tl) {
+        const int nk = 49 * nb;
+        const int rit = row0 & 63;
+        for (int k0 = 64 * G; k0 < nk; k0 += 256) {
+            const int k = min(k0 + lane, nk - 1);
+            const int bb = k / 49;
+            dma16(a.w + ((int64_t)(row0 >> 6) * nb + bb) * kIq3TileCol + iq3_rg_tile_off(k - 49 * bb, rit),
+                  rgb + 16 * k0);
+            ++ncopy;
+        }
+    } else {
+        const uintptr_t wb = (uintptr_t)a.w;
+        const uintptr_t we = wb + (uintptr_t)a.n_out * (uintptr_t)a.row_bytes;
+        const uintptr_t lo16 = (wb + 15) & ~(uintptr_t)15;   // first whole granule
+        const uintptr_t hi16 = (we & ~(uintptr_t)15) - 16;   // last whole granule
+        const uintptr_t start = wb + (uintptr_t)row0 * (uintptr_t)a.row_bytes;
+        const uintptr_t base16 = start & ~(uintptr_t)15;
+        o0 = (uint32_t)(start & 15);
+        const int ngr = (int)((o0 + (uint32_t)(R * a.row_bytes) + 15) / 16) + 1;
+        for (int k0 = 64 * G; k0 < ngr; k0 += 256) {
+            uintptr_t g = base16 + 16 * (uintptr_t)(k0 + lane);
+            g = g < lo16 ? lo16 : (g > hi16 ? hi16 : g);
+            dma16((const void *)g, rgb + 16 * k0);
+            ++ncopy;
+        }
+    }
+    volatile __attribute__((address_space(3))) uint32_t *vote =
+        (volatile __attribute__((address_space(3))) uint32_t *)(size_t)(lds0 + kIq3ShortVote);
+    if (threadIdx.x == 0) *vote = 0u;
+    // The grid (and the activations) are in once only the rows' copies are
+    // outstanding.
+    wait_vmcnt_upto(ncopy);
+    lds_barrier();
+    {
+        const int i = threadIdx.x;   // grid row
+        const f32x4 gv = lds_load<f32x4>(kIq3ShortGrid + 16 * i);
+        const float4 g4 = {gv[0], gv[1], gv[2], gv[3]};
+        for (int sg = 0; sg < 16; ++sg) iq3_table_entry(sg, i, g4);
+        const bool exact = fp16_exact(gv[0]) && fp16_exact(gv[1]) && fp16_exact(gv[2]) && fp16_exact(gv[3]);
+        if (__builtin_amdgcn_ballot_w64(!exact) != 0 && lane == 0) *vote = 1u;
+    }
+    wait_vmcnt<0>();
+    lds_barrier();   // the rows and the table
+
+    float acc = 0.0f;
+    const int row = row0 + r;
+    if (b < nb) {
+        const uint8_t *rg = smem + kIq3ShortCols;
+        const uint32_t o = o0 + (uint32_t)((r * nb + b) * kIq3Bytes);
+        switch (G) {
+            case 0: acc = iq3_rows_dot<0>(a, rg, o, row, b, r, xv); break;
+            case 1: acc = iq3_rows_dot<1>(a, rg, o, row, b, r, xv); break;
+            case 2: acc = iq3_rows_dot<2>(a, rg, o, row, b, r, xv); break;
+            default: acc = iq3_rows_dot<3>(a, rg, o, row, b, r, xv); break;
+        }
+    }
+    acc += __shfl_xor(acc, 8);
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    float *red = (float *)(smem + kIq3RgRed);
+    if (lane < R) red[G * R + lane] = acc;
+    lds_barrier();
+    if (G != 0 || lane >= R) return;
+    float total = red[lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) total += red[w * R + lane];
+    if (*vote != 0u) total = __builtin_nanf("");
+    if (row0 + lane < a.n_out) a.y[row0 + lane] = total;
+}
+
 // Row-major IQ3 weights -> tile layout, one workgroup per (tile, block column),
 // 2-byte units (the source blocks are only 2-byte aligned).
 __global__ __launch_bounds__(256) void iq3_pack_tiles_kernel(const uint8_t *__restrict__ src,
@@ -841,6 +996,15 @@ hipError_t launch_iq3_pack_tiles(const uint8_t *src, uint8_t *dst, int nb, int n
     const int64_t tiles = ((int64_t)n_out + kTileRows - 1) / kTileRows;
     hipLaunchKernelGGL(iq3_pack_tiles_kernel, dim3((unsigned)(tiles * nb)), dim3(256), 0, s, src,
                        dst, nb, n_out, xxs);
+    return hipGetLastError();
+}
+
+bool iq3_rows_fits(int nb) { return nb <= kIq3RgMaxBlocks; }
+
+hipError_t launch_iq3_rows(const GemvArgs &a, const float *grid, hipStream_t s) {
+    if (a.nb > kIq3RgMaxBlocks) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(iq3_rows_kernel, dim3((a.n_out + kIq3RgRows - 1) / kIq3RgRows), dim3(256),
+                       kIq3RgLds, s, a, grid);
     return hipGetLastError();
 }
 

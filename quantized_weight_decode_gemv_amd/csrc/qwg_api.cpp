@@ -248,17 +248,23 @@ int short_splits(int tiles, int nb) {
     return sp;
 }
 
-// Batch-1 Q4_K calls on the row-group kernel: the short-call matrices whose
-// rows hold at most eight super-blocks. (Not larger matrices: the LM head,
-// 32000 x 2048, took 17.4 us per call on row groups against 11.0 us on the
-// stream engine, event time on one box.) QWG_ROWS=0 turns it off (A/B
-// measurements: those matrices then run on the split short-call kernel).
-bool rows_engine(int tiles, int nb) {
+// Batch-1 Q4_K and IQ3 calls on the row-group kernels: the short-call matrices
+// whose rows hold at most eight blocks. (Not larger matrices: the Q4_K LM
+// head, 32000 x 2048, took 17.4 us per call on row groups against 11.0 us on
+// the stream engine, event time on one box.) QWG_ROWS=0 turns them off (A/B
+// measurements: those matrices then run on the split short-call kernels).
+bool rows_off() {
     static const bool off = [] {
         const char *e = getenv("QWG_ROWS");
         return e != nullptr && e[0] == '0';
     }();
-    return !off && q4k_rows_fits(nb) && short_splits(tiles, nb) > 0;
+    return off;
+}
+bool rows_engine(int tiles, int nb) {
+    return !rows_off() && q4k_rows_fits(nb) && short_splits(tiles, nb) > 0;
+}
+bool rows_engine_iq3(int tiles, int nb) {
+    return !rows_off() && iq3_rows_fits(nb) && short_splits(tiles, nb) > 0;
 }
 
 // IQ3 stream engine shape. Measured on MI355X: grouped streams run best with
@@ -472,6 +478,7 @@ int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
         return sp > 0 ? sp : -QWG_ERR_HIP;
     }
     if (fmt != QWG_FMT_Q4K) {
+        if (rows_engine_iq3(tiles, (int)(n_in / kQK))) return 1;
         const int ss = short_splits(tiles, (int)(n_in / kQK));
         if (ss > 0) return ss;
         const int slots = iq3_stream_slots(iq3_shape(false, 0), false);
@@ -834,7 +841,8 @@ int iq3_gemv(float *y, const float *x, const void *w, const float *grid, int64_t
         return QWG_ERR_SHAPE;
     a.layout = layout;
     if (waves == 0 && splits == 0) {
-        // automatic plan: the short-call kernel when the matrix fits it
+        // automatic plan: the short-call kernels when the matrix fits them
+        if (rows_engine_iq3(a.tiles, a.nb)) return hip_status(launch_iq3_rows(a, grid, (hipStream_t)stream));
         const int ss = short_splits(a.tiles, a.nb);
         if (ss > 0) {
             a.splits = ss;

@@ -1072,8 +1072,9 @@ def test_gemv_iq3_tiled(n_out, n_in):
 @pytest.mark.parametrize("n_out,n_in", [(2048, 2048), (5632, 2048), (2048, 5632), (256, 2048),
                                         (130, 3328), (1, 7168), (64, 3840)])
 def test_gemv_iq3_short_calls_layouts_and_repeat(n_out, n_in):
-    # The short-call IQ3 kernel (split rows through tagged words) on row-major,
-    # llama.cpp-order and tile-layout weights: the same kernel, so the same
+    # The short-call IQ3 kernels (row groups for rows of at most 8 blocks, else
+    # split rows through tagged words) on row-major, llama.cpp-order and
+    # tile-layout weights: the same kernel, so the same
     # bits for the container and its tile layout, the llama.cpp order with the
     # doubled grid exactly twice that; repeated calls give the same bits.
     grid = synth.iq3_grid()
@@ -1090,6 +1091,39 @@ def test_gemv_iq3_short_calls_layouts_and_repeat(n_out, n_in):
     assert_bits(host(qwg.gemv_iq3_xxs(wx, xd, gx)), 2 * y, "llama.cpp order, doubled grid")
     for _ in range(2):
         assert_bits(host(qwg.gemv_iq3(wd, xd, gd)), y, "repeat")
+
+
+@pytest.mark.parametrize("offset", [0, 2, 6, 14])
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (7, 512), (9, 2048), (63, 1792), (65, 768),
+                                        (1000, 2048), (5632, 2048)])
+def test_gemv_iq3_row_groups(offset, n_out, n_in):
+    # Row-group IQ3 kernel (batch 1, at most 8 blocks per row, a matrix the
+    # split short-call plan covers): eight whole rows per workgroup; row-major
+    # weights at 2-byte offsets from a 16-byte boundary (the contiguous granule
+    # run of each group, clamped at the buffer's ends), ragged last groups,
+    # rows past n_out untouched; the tile layout and the llama.cpp order with
+    # the same (doubled) bits; repeat calls with the same bits.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert -(-n_out // 64) <= cus // 2
+    assert qwg.plan_splits(1, n_in, n_out) == 1
+    grid = synth.iq3_grid()
+    w = synth.iq3_weights(n_out, n_in, 135, offset)
+    x = synth.activations(n_in, 135, n_out)
+    wd, xd, gd = _guarded_iq3(w, offset), dev(x), dev(grid)
+    yr, sr = oracle.gemv_iq3(w, grid, x, n_in, n_out)
+    ybuf = torch.full((n_out + 128,), float("nan"), device=DEV)
+    qwg.gemv_iq3(wd, xd, gd, out=ybuf[64:64 + n_out])
+    yb = host(ybuf)
+    assert np.isnan(yb[:64]).all() and np.isnan(yb[64 + n_out:]).all(), "write outside y"
+    y = yb[64:64 + n_out]
+    assert_bound(y, yr, sr, f"iq3 rows {n_out}x{n_in} offset {offset}")
+    t = host(qwg.gemv_iq3_tiled(qwg.pack_iq3_tiles(dev(w), n_in), xd, gd, n_out))
+    assert_bits(t, y, "tile layout")
+    wx = synth.iq3_xxs_weights(n_out, n_in, 135, offset)
+    gx = dev(synth.iq3_xxs_grid())
+    assert_bits(host(qwg.gemv_iq3_xxs(_guarded_iq3(wx, offset), xd, gx)), 2 * y,
+                "llama.cpp order, doubled grid")
+    assert_bits(host(qwg.gemv_iq3(wd, xd, gd)), y, "repeat")
 
 
 @pytest.mark.parametrize("waves", [0, 16])
