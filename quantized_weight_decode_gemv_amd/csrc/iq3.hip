@@ -349,15 +349,23 @@ __device__ __forceinline__ void lds_store(uint32_t addr, T v) {
     *(__attribute__((address_space(3))) T *)(size_t)addr = v;
 }
 
-// Entry (s, i) of the sign-folded table (at LDS address 0) from grid row g.
-__device__ __forceinline__ void iq3_table_entry(int s, int i, float4 g) {
-    const float v[4] = {(s & 1) ? -g.x : g.x, (s & 2) ? -g.y : g.y, (s & 4) ? -g.z : g.z,
-                        (s & 8) ? -g.w : g.w};
-    uint32_t hb[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) hb[c] = __builtin_bit_cast(uint16_t, (_Float16)v[c]);
-    const u32x2 e = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-    lds_store<u32x2>(s * 2048 + i * 8, e);
+// Entries (s, i), s = s0, s0 + ds, ... < 16, of the sign-folded table from
+// grid row g: the four fp16 magnitudes converted once, each sign pattern made
+// by flipping their sign bits (conversion to fp16 rounds symmetrically, so
+// this is the fp16 of each signed value). Measured against converting every
+// entry (IQ3 5632 x 2048 row groups, 16 entries per thread): see below.
+__device__ __forceinline__ void iq3_table_row(int i, float4 g, int s0, int ds) {
+    const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)g.x);
+    const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)g.y);
+    const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)g.z);
+    const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)g.w);
+    const uint32_t lo = h0 | (h1 << 16), hi = h2 | (h3 << 16);
+    for (int s = s0; s < 16; s += ds) {
+        const uint32_t mlo = ((uint32_t)(s & 1) << 15) | ((uint32_t)(s & 2) << 30);
+        const uint32_t mhi = ((uint32_t)(s & 4) << 13) | ((uint32_t)(s & 8) << 28);
+        const u32x2 e = {lo ^ mlo, hi ^ mhi};
+        lds_store<u32x2>(s * 2048 + i * 8, e);
+    }
 }
 
 template <int G, int W, int R, bool TL>
@@ -473,7 +481,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
         const int t = threadIdx.x;
         const int i = t & 255;
         const float4 gv = *(const float4 *)(smem + C::kGrid + 16 * i);
-        for (int s = t >> 8; s < 16; s += W / 4) iq3_table_entry(s, i, gv);
+        iq3_table_row(i, gv, t >> 8, W / 4);
         const bool exact =
             fp16_exact(gv.x) && fp16_exact(gv.y) && fp16_exact(gv.z) && fp16_exact(gv.w);
         if (__builtin_amdgcn_ballot_w64(!exact) != 0 && lane == 0) *vote = 1u;
@@ -759,7 +767,7 @@ __global__ __launch_bounds__(256 * C) void iq3_short_kernel(GemvArgs a, ShortSta
         const int i = t & 255;
         const f32x4 gv = lds_load<f32x4>(kIq3ShortGrid + 16 * i);
         const float4 g4 = {gv[0], gv[1], gv[2], gv[3]};
-        for (int s = t >> 8; s < 16; s += W / 4) iq3_table_entry(s, i, g4);
+        iq3_table_row(i, g4, t >> 8, W / 4);
         const bool exact = fp16_exact(gv[0]) && fp16_exact(gv[1]) && fp16_exact(gv[2]) && fp16_exact(gv[3]);
         if (__builtin_amdgcn_ballot_w64(!exact) != 0 && lane == 0) *vote = 1u;
     }
@@ -795,14 +803,14 @@ __global__ __launch_bounds__(256 * C) void iq3_short_kernel(GemvArgs a, ShortSta
 // workgroup of four wavefronts takes eight whole rows, so no split sums meet
 // through memory (the Q4_K row-group kernel's scheme). Wavefront G takes quant
 // chunk G of every block, lane r + 8s row r's block s with its 64 activations
-// in registers (sixteen 16-byte loads, issued first: the grid's copy and the
-// rows' copies queue behind them, so waiting for the grid waits for them too).
+// in registers (sixteen 16-byte loads). Each thread loads one grid row into
+// registers and builds its table entries from it as soon as it arrives.
 // The rows arrive as one contiguous run of 16-byte granules (row-major, either
 // byte order: 8 x nb x 98 bytes from the group's first block, granules that
 // reach outside the buffer clamped and the two blocks they hold read directly
 // as in the stream engine) or as the eight rows' slices of each tile-layout
-// column (784 bytes: index, word and d runs). The grid staging, sign-folded
-// table and exactness vote are the short-call kernel's.
+// column (784 bytes: index, word and d runs). The sign-folded table and the
+// exactness vote are the short-call kernel's.
 constexpr int kIq3RgRows = 8;
 constexpr int kIq3RgMaxBlocks = 8;
 constexpr int kIq3RgSlice = 784;                        // 8 rows of a tile-layout column
@@ -864,15 +872,17 @@ __global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *
     const int r = lane & (R - 1);
     const int b = lane >> 3;
 
-    // The activations first (see above).
+    // This thread's grid row (its table entries), then the activations, then
+    // the rows' copies: the table is built as soon as the grid row is in, with
+    // no barrier before it.
+    const f32x4 gv = *(const f32x4 *)(grid + 4 * threadIdx.x);
+    __builtin_amdgcn_sched_barrier(0);   // (kept the oldest load: its wait then lets the rest fly)
     f32x4 xv[16];
     {
         const f32x4 *xp = (const f32x4 *)(a.x + (int64_t)kQK * min(b, nb - 1) + 64 * G);
 #pragma unroll
         for (int q = 0; q < 16; ++q) xv[q] = xp[q];
     }
-    dma16((const uint8_t *)grid + 16 * (64 * G + lane), lds0 + kIq3ShortGrid + 1024 * G);
-    int ncopy = 0;
     uint32_t o0 = 0;   // the group's first block in the copied run (row-major)
     if (tl) {
         const int nk = 49 * nb;
@@ -882,7 +892,6 @@ __global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *
             const int bb = k / 49;
             dma16(a.w + ((int64_t)(row0 >> 6) * nb + bb) * kIq3TileCol + iq3_rg_tile_off(k - 49 * bb, rit),
                   rgb + 16 * k0);
-            ++ncopy;
         }
     } else {
         const uintptr_t wb = (uintptr_t)a.w;
@@ -897,23 +906,16 @@ __global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *
             uintptr_t g = base16 + 16 * (uintptr_t)(k0 + lane);
             g = g < lo16 ? lo16 : (g > hi16 ? hi16 : g);
             dma16((const void *)g, rgb + 16 * k0);
-            ++ncopy;
         }
     }
-    volatile __attribute__((address_space(3))) uint32_t *vote =
-        (volatile __attribute__((address_space(3))) uint32_t *)(size_t)(lds0 + kIq3ShortVote);
-    if (threadIdx.x == 0) *vote = 0u;
-    // The grid (and the activations) are in once only the rows' copies are
-    // outstanding.
-    wait_vmcnt_upto(ncopy);
-    lds_barrier();
+    // Sign-folded table (grid row threadIdx.x); each wavefront's exactness
+    // vote in a word of its own.
     {
-        const int i = threadIdx.x;   // grid row
-        const f32x4 gv = lds_load<f32x4>(kIq3ShortGrid + 16 * i);
         const float4 g4 = {gv[0], gv[1], gv[2], gv[3]};
-        for (int sg = 0; sg < 16; ++sg) iq3_table_entry(sg, i, g4);
+        iq3_table_row(threadIdx.x, g4, 0, 1);
         const bool exact = fp16_exact(gv[0]) && fp16_exact(gv[1]) && fp16_exact(gv[2]) && fp16_exact(gv[3]);
-        if (__builtin_amdgcn_ballot_w64(!exact) != 0 && lane == 0) *vote = 1u;
+        const bool any = __builtin_amdgcn_ballot_w64(!exact) != 0;
+        if (lane == 0) *(volatile __attribute__((address_space(3))) uint32_t *)(size_t)(lds0 + kIq3ShortVote + 4 * G) = any ? 1u : 0u;
     }
     wait_vmcnt<0>();
     lds_barrier();   // the rows and the table
@@ -940,7 +942,9 @@ __global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *
     float total = red[lane];
 #pragma unroll
     for (int w = 1; w < 4; ++w) total += red[w * R + lane];
-    if (*vote != 0u) total = __builtin_nanf("");
+    const volatile __attribute__((address_space(3))) uint32_t *vote =
+        (const volatile __attribute__((address_space(3))) uint32_t *)(size_t)(lds0 + kIq3ShortVote);
+    if ((vote[0] | vote[1] | vote[2] | vote[3]) != 0u) total = __builtin_nanf("");
     if (row0 + lane < a.n_out) a.y[row0 + lane] = total;
 }
 
