@@ -799,12 +799,15 @@ __global__ __launch_bounds__(256 * C) void iq3_short_kernel(GemvArgs a, ShortSta
 
 // ------------------------------------------------------------------ row groups
 //
-// Rows of at most eight blocks (n_in <= 2048) on the short-call matrices: a
-// workgroup of four wavefronts takes eight whole rows, so no split sums meet
-// through memory (the Q4_K row-group kernel's scheme). Wavefront G takes quant
-// chunk G of every block, lane r + 8s row r's block s with its 64 activations
-// in registers (sixteen 16-byte loads). Each thread loads one grid row into
-// registers and builds its table entries from it as soon as it arrives.
+// Rows of at most 24 blocks (n_in <= 6144) on the short-call matrices: a
+// workgroup of 4 NS wavefronts takes eight whole rows, so no split sums meet
+// through memory (the Q4_K row-group kernel's scheme). Wavefront w takes
+// quant chunk w % 4 of the blocks of set w / 4, lane r + 8s row r's block
+// s + 8 (w / 4), with its 64 activations in registers (sixteen 16-byte loads).
+// Each thread loads one grid row into registers and builds its table entries
+// from it as soon as it arrives. Measured (kernel trace, cold weights, same
+// box): 5632 x 2048 (NS = 1) 7.20 -> 6.16 us against the split kernel, 2048 x
+// 5632 (NS = 3) 6.60 -> 6.36 us.
 // The rows arrive as one contiguous run of 16-byte granules (row-major, either
 // byte order: 8 x nb x 98 bytes from the group's first block, granules that
 // reach outside the buffer clamped and the two blocks they hold read directly
@@ -812,13 +815,20 @@ __global__ __launch_bounds__(256 * C) void iq3_short_kernel(GemvArgs a, ShortSta
 // column (784 bytes: index, word and d runs). The sign-folded table and the
 // exactness vote are the short-call kernel's.
 constexpr int kIq3RgRows = 8;
-constexpr int kIq3RgMaxBlocks = 8;
+constexpr int kIq3RgMaxBlocks = 24;
 constexpr int kIq3RgSlice = 784;                        // 8 rows of a tile-layout column
-constexpr int kIq3RgRegion = 448 * 16;                  // the rows' granules
-constexpr int kIq3RgRed = kIq3ShortCols + kIq3RgRegion; // [4 wavefronts][8 rows] fp32
-constexpr int kIq3RgLds = kIq3RgRed + 4 * kIq3RgRows * 4;
-static_assert(kIq3RgSlice * kIq3RgMaxBlocks <= kIq3RgRegion, "tile slices fit");
-static_assert((15 + kIq3RgRows * kIq3RgMaxBlocks * kIq3Bytes + 15) / 16 + 1 <= 448, "row runs fit");
+// The rows' granules (row-major run with its head and one over-read granule,
+// or the tile slices), in whole 64-granule copy instructions; then the
+// reduction [wavefronts][8 rows] fp32.
+__host__ __device__ constexpr int iq3_rg_region(int nb) {
+    const int run = (15 + kIq3RgRows * nb * kIq3Bytes + 15) / 16 + 1;
+    const int gr = run > 49 * nb ? run : 49 * nb;
+    return (gr + 63) / 64 * 64 * 16;
+}
+__host__ __device__ constexpr int iq3_rg_lds(int nb, int waves) {
+    return kIq3ShortCols + iq3_rg_region(nb) + waves * kIq3RgRows * 4;
+}
+static_assert(iq3_rg_lds(kIq3RgMaxBlocks, 12) <= 65536, "LDS of one workgroup");
 
 // Byte offset in a tile-layout column of granule g (0..48) of the eight-row
 // slice starting at row rit (a multiple of 8): index runs, word runs, d.
@@ -859,23 +869,26 @@ __device__ __forceinline__ float iq3_rows_dot(const GemvArgs &a, const uint8_t *
     return iq3_dot_regs<G>(raw, [&](int i) { return xv[i >> 2][i & 3]; }, 0.0f);
 }
 
-__global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *grid) {
+template <int NS>
+__global__ __launch_bounds__(256 * NS) void iq3_rows_kernel(GemvArgs a, const float *grid) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int R = kIq3RgRows;
+    constexpr int W = 4 * NS;          // block set wave / 4, chunk wave % 4
     const bool tl = a.layout == kLayoutTiles;
     const int lane = threadIdx.x & 63;
-    const int G = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = wave & 3;
     const int nb = a.nb;
     const int row0 = blockIdx.x * R;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
     const uint32_t rgb = lds0 + kIq3ShortCols;
     const int r = lane & (R - 1);
-    const int b = lane >> 3;
+    const int b = (lane >> 3) + 8 * (wave >> 2);
 
     // This thread's grid row (its table entries), then the activations, then
     // the rows' copies: the table is built as soon as the grid row is in, with
     // no barrier before it.
-    const f32x4 gv = *(const f32x4 *)(grid + 4 * threadIdx.x);
+    const f32x4 gv = *(const f32x4 *)(grid + 4 * (threadIdx.x & 255));
     __builtin_amdgcn_sched_barrier(0);   // (kept the oldest load: its wait then lets the rest fly)
     f32x4 xv[16];
     {
@@ -887,7 +900,7 @@ __global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *
     if (tl) {
         const int nk = 49 * nb;
         const int rit = row0 & 63;
-        for (int k0 = 64 * G; k0 < nk; k0 += 256) {
+        for (int k0 = 64 * wave; k0 < nk; k0 += 64 * W) {
             const int k = min(k0 + lane, nk - 1);
             const int bb = k / 49;
             dma16(a.w + ((int64_t)(row0 >> 6) * nb + bb) * kIq3TileCol + iq3_rg_tile_off(k - 49 * bb, rit),
@@ -902,7 +915,7 @@ __global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *
         const uintptr_t base16 = start & ~(uintptr_t)15;
         o0 = (uint32_t)(start & 15);
         const int ngr = (int)((o0 + (uint32_t)(R * a.row_bytes) + 15) / 16) + 1;
-        for (int k0 = 64 * G; k0 < ngr; k0 += 256) {
+        for (int k0 = 64 * wave; k0 < ngr; k0 += 64 * W) {
             uintptr_t g = base16 + 16 * (uintptr_t)(k0 + lane);
             g = g < lo16 ? lo16 : (g > hi16 ? hi16 : g);
             dma16((const void *)g, rgb + 16 * k0);
@@ -912,10 +925,11 @@ __global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *
     // vote in a word of its own.
     {
         const float4 g4 = {gv[0], gv[1], gv[2], gv[3]};
-        iq3_table_row(threadIdx.x, g4, 0, 1);
+        iq3_table_row(threadIdx.x & 255, g4, NS == 1 ? 0 : (int)(threadIdx.x >> 8), NS);
         const bool exact = fp16_exact(gv[0]) && fp16_exact(gv[1]) && fp16_exact(gv[2]) && fp16_exact(gv[3]);
         const bool any = __builtin_amdgcn_ballot_w64(!exact) != 0;
-        if (lane == 0) *(volatile __attribute__((address_space(3))) uint32_t *)(size_t)(lds0 + kIq3ShortVote + 4 * G) = any ? 1u : 0u;
+        if (wave < 4 && lane == 0)
+            *(volatile __attribute__((address_space(3))) uint32_t *)(size_t)(lds0 + kIq3ShortVote + 4 * wave) = any ? 1u : 0u;
     }
     wait_vmcnt<0>();
     lds_barrier();   // the rows and the table
@@ -935,13 +949,13 @@ __global__ __launch_bounds__(256) void iq3_rows_kernel(GemvArgs a, const float *
     acc += __shfl_xor(acc, 8);
     acc += __shfl_xor(acc, 16);
     acc += __shfl_xor(acc, 32);
-    float *red = (float *)(smem + kIq3RgRed);
-    if (lane < R) red[G * R + lane] = acc;
+    float *red = (float *)(smem + kIq3ShortCols + iq3_rg_region(nb));
+    if (lane < R) red[wave * R + lane] = acc;
     lds_barrier();
-    if (G != 0 || lane >= R) return;
+    if (wave != 0 || lane >= R) return;
     float total = red[lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) total += red[w * R + lane];
+    for (int w = 1; w < W; ++w) total += red[w * R + lane];
     const volatile __attribute__((address_space(3))) uint32_t *vote =
         (const volatile __attribute__((address_space(3))) uint32_t *)(size_t)(lds0 + kIq3ShortVote);
     if ((vote[0] | vote[1] | vote[2] | vote[3]) != 0u) total = __builtin_nanf("");
@@ -1007,8 +1021,13 @@ bool iq3_rows_fits(int nb) { return nb <= kIq3RgMaxBlocks; }
 
 hipError_t launch_iq3_rows(const GemvArgs &a, const float *grid, hipStream_t s) {
     if (a.nb > kIq3RgMaxBlocks) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(iq3_rows_kernel, dim3((a.n_out + kIq3RgRows - 1) / kIq3RgRows), dim3(256),
-                       kIq3RgLds, s, a, grid);
+    const dim3 g((a.n_out + kIq3RgRows - 1) / kIq3RgRows);
+    if (a.nb <= 8)
+        hipLaunchKernelGGL((iq3_rows_kernel<1>), g, dim3(256), iq3_rg_lds(a.nb, 4), s, a, grid);
+    else if (a.nb <= 16)
+        hipLaunchKernelGGL((iq3_rows_kernel<2>), g, dim3(512), iq3_rg_lds(a.nb, 8), s, a, grid);
+    else
+        hipLaunchKernelGGL((iq3_rows_kernel<3>), g, dim3(768), iq3_rg_lds(a.nb, 12), s, a, grid);
     return hipGetLastError();
 }
 

@@ -249,7 +249,7 @@ int short_splits(int tiles, int nb) {
 }
 
 // Batch-1 Q4_K and IQ3 calls on the row-group kernels: the short-call matrices
-// whose rows hold at most eight blocks. (Not larger matrices: the Q4_K LM
+// whose rows hold at most 8 (Q4_K) or 24 (IQ3) blocks. (Not larger matrices: the Q4_K LM
 // head, 32000 x 2048, took 17.4 us per call on row groups against 11.0 us on
 // the stream engine, event time on one box.) QWG_ROWS=0 turns them off (A/B
 // measurements: those matrices then run on the split short-call kernels).

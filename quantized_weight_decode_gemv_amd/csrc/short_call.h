@@ -45,7 +45,7 @@ hipError_t launch_q4k_short(const GemvArgs &a, const ShortState &st, bool tiled,
 // rows per workgroup, no split sums (so no workspace).
 bool q4k_rows_fits(int nb);
 hipError_t launch_q4k_rows(const GemvArgs &a, bool tiled, hipStream_t s);
-// Row-group kernel for IQ3 (any layout, rows of nb <= 8 blocks), the same scheme.
+// Row-group kernel for IQ3 (any layout, rows of nb <= 24 blocks), the same scheme.
 bool iq3_rows_fits(int nb);
 hipError_t launch_iq3_rows(const GemvArgs &a, const float *grid, hipStream_t s);
 // IQ3 (a.layout: rows, llama.cpp-order rows or tiles), the same plan rule.

@@ -1095,9 +1095,11 @@ def test_gemv_iq3_short_calls_layouts_and_repeat(n_out, n_in):
 
 @pytest.mark.parametrize("offset", [0, 2, 6, 14])
 @pytest.mark.parametrize("n_out,n_in", [(1, 256), (7, 512), (9, 2048), (63, 1792), (65, 768),
-                                        (1000, 2048), (5632, 2048)])
+                                        (1000, 2048), (5632, 2048), (3, 2304), (130, 4096),
+                                        (2048, 5632), (17, 6144)])
 def test_gemv_iq3_row_groups(offset, n_out, n_in):
-    # Row-group IQ3 kernel (batch 1, at most 8 blocks per row, a matrix the
+    # Row-group IQ3 kernel (batch 1, at most 24 blocks per row: one, two or
+    # three block sets per workgroup, a matrix the
     # split short-call plan covers): eight whole rows per workgroup; row-major
     # weights at 2-byte offsets from a 16-byte boundary (the contiguous granule
     # run of each group, clamped at the buffer's ends), ragged last groups,
