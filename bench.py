@@ -455,7 +455,7 @@ def run_configs(dev, stream, args):
     """GPU side of the per-configuration records (C1-C4 as single calls through
     the C ABI): each call's duration from a HIP event pair around it, on
     weights cycled over enough copies (>= 1 GiB) that every call reads HBM;
-    200 timed calls after 20 warm-up calls. Also one call into NaN-filled
+    200 timed calls after 200 warm-up calls. Also one call into NaN-filled
     outputs, and the bit patterns of the dequantized matrix, for the oracle
     leg. Returns {name: {...}}."""
     import numpy as np
@@ -464,7 +464,9 @@ def run_configs(dev, stream, args):
     from quantized_weight_decode_gemv_amd import synth
 
     out = {}
-    timed_calls, warm = 200, 20
+    # (200 warm-up calls per case: these records are taken right after setup,
+    # before the clocks have come up; with 20 the first case read 9.0 against 6.2 us)
+    timed_calls, warm = 200, 200
 
     def cycle_time(call, copies):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
