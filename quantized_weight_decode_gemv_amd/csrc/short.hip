@@ -181,11 +181,13 @@ __global__ __launch_bounds__(256 * C * H) void q4k_short_kernel(GemvArgs a, Shor
 // 16-byte loads; the wavefront's lanes read eight distinct 128-byte pieces,
 // which is what limits this mapping to short rows: at 22 super-blocks per row
 // a split tile with scalar activations measured faster, 7.8 against 8.2 us per
-// call). A lane's sum meets its row's other super-blocks across the wavefront
-// (xor shuffles over lanes r + 8s), the eight wavefronts' in LDS in wavefront
-// order. Measured against the split short-call kernel (event time per call,
-// cold weights, alternating runs): 2048 x 2048 6.56 -> 6.04 us, 5632 x 2048
-// 7.92 -> 7.36 us, 256 x 2048 6.24-6.4 -> 6.12-6.16 us.
+// call, and 5.96 against 6.62 us of kernel time for block sets of four chunk
+// wavefronts). A lane's sum meets its row's other super-blocks across the
+// wavefront (xor shuffles over lanes r + 8s), the eight wavefronts' in LDS in
+// wavefront order. Measured against the split short-call kernel (kernel
+// trace, cold weights): 2048 x 2048 4.72 -> 4.24 us, 5632 x 2048 6.16 -> 5.80
+// us, 256 x 2048 4.08 either way; event time per call, alternating runs on one
+// box: 6.56 -> 6.04, 7.92 -> 7.36, 6.24-6.4 -> 6.12-6.16 us.
 constexpr int kRgRows = 8;
 constexpr int kRgWaves = 8;
 constexpr int kRgMaxBlocks = 8;
