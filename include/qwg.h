@@ -59,10 +59,10 @@
  *     one another or calls on that stream. Concurrent calls on different
  *     streams never share a workspace. The summation order is fixed by the
  *     shapes, so results are deterministic.
- *   - Short batch-1 Q4_K and IQ3 calls (at most one 64-row tile per compute
- *     unit) whose rows hold at most 8 (Q4_K: n_in <= 2048) or 24 (IQ3: n_in
- *     <= 6144) blocks take whole rows per workgroup: no split and no
- *     workspace.
+ *   - Short batch-1 calls (at most one 64-row tile per compute unit) whose
+ *     rows hold at most 8 (Q4_K: n_in <= 2048) or 24 (IQ3, IQ3_XXS, IQ3_S,
+ *     IQ4_XS: n_in <= 6144) blocks take whole rows per workgroup: no split
+ *     and no workspace.
  *   - Other short batch-1 Q4_K and IQ3 calls (at most one workgroup per compute
  *     unit) whose rows are split add the partial sums through tagged words:
  *     the last split's workgroup waits for its peers' words, which relies on

@@ -136,16 +136,19 @@ struct Iq3sFmt {
     // entries, 16 KB (folding all four signs of a group into 8-byte entries
     // took 64 KB and left room for one workgroup per CU).
     // Returns false if a grid value this thread stored is not exactly fp16.
+    // Each (p, i) pair's two fp16 magnitudes are converted once and its four
+    // sign patterns made by flipping sign bits (conversion to fp16 rounds
+    // symmetrically, so this is the fp16 of each signed value).
     __device__ static bool build_table(const float *grid, int t, int nthreads) {
         bool exact = true;
-        for (int e = t; e < 4096; e += nthreads) {
-            const int s2 = e >> 10, p = (e >> 9) & 1;
-            const float2 g = *(const float2 *)(grid + 4 * (e & 511) + 2 * p);
-            const float v0 = (s2 & 1) ? -g.x : g.x;
-            const float v1 = (s2 & 2) ? -g.y : g.y;
-            const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)v0);
-            const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)v1);
-            *(__attribute__((address_space(3))) uint32_t *)(size_t)(e * 4) = h0 | (h1 << 16);
+        for (int q = t; q < 1024; q += nthreads) {   // q = (p << 9) | i
+            const float2 g = *(const float2 *)(grid + 4 * (q & 511) + 2 * (q >> 9));
+            const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)g.x) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)g.y) << 16);
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+                *(__attribute__((address_space(3))) uint32_t *)(size_t)(((s2 << 10) | q) * 4) =
+                    h ^ ((s2 & 1) ? 0x8000u : 0u) ^ ((s2 & 2) ? 0x80000000u : 0u);
             exact = exact && fp16_exact(g.x) && fp16_exact(g.y);
         }
         return exact;
@@ -218,13 +221,42 @@ struct Iq3sFmt {
         r.d16 = h[0];
     }
 
+    // Eight rows rit..rit+7 (rit a multiple of 8) of a tile-layout column as
+    // 55 granules: index runs [G][8][16], sign runs [G][8][8], ninth-bit runs
+    // [G][8][2], sub-scales [8][4], d [8][2] (880 bytes); the byte offset in
+    // the column of granule g, and the fields of slice row r.
+    static constexpr int kSliceGran = 55;
+    __device__ static int slice_off(int g, int rit) {
+        if (g < 32) return kIdx + (g >> 3) * 1024 + 16 * rit + 16 * (g & 7);
+        if (g < 48) return kSign + ((g - 32) >> 2) * 512 + 8 * rit + 16 * ((g - 32) & 3);
+        if (g < 52) return kHb + (g - 48) * 128 + 2 * rit;
+        if (g < 54) return kScale + 4 * rit + 16 * (g - 52);
+        return kD + 2 * rit;
+    }
+    template <int G>
+    __device__ static void fetch_slice(const uint8_t *sl, int r, Raw &raw) {
+        const uint4 q = *(const uint4 *)(sl + G * 128 + 16 * r);
+        const uint2 sg = *(const uint2 *)(sl + 512 + G * 64 + 8 * r);
+        raw.q[0] = q.x;
+        raw.q[1] = q.y;
+        raw.q[2] = q.z;
+        raw.q[3] = q.w;
+        raw.sg[0] = sg.x;
+        raw.sg[1] = sg.y;
+        raw.hb = ld_u16(sl + 768 + G * 16 + 2 * r);
+        raw.sc = *(const uint32_t *)(sl + 832 + 4 * r);
+        raw.d16 = ld_u16(sl + 864 + 2 * r);
+    }
+
     // acc + this lane's row sum over wavefront G's 64 weights. Group k (four
     // weights) of sub-block h reads two entries, halves p = 0 and 1: ((two
     // sign bits of nibble k) << 10 | p << 9 | ninth bit << 8 | index byte),
     // each assembled by one v_perm from the index dword and a dword of bytes
     // (s2 << 2 | p << 1 | ninth bit) built once per sub-block.
-    template <int G>
-    __device__ static float dot(const Raw &r, int, cfloat_p xg, float acc) {
+    // (xat(i): activation i of the wavefront's 64: scalar loads in the
+    // stream, registers in the row-group kernel)
+    template <int G, typename XAt>
+    __device__ static float dot(const Raw &r, int, XAt xat, float acc) {
         const uint2 sg = {r.sg[0], r.sg[1]};
         const uint32_t hb = r.hb, sc = r.sc;
         const float d = h2f_lo(r.d16);
@@ -247,7 +279,7 @@ struct Iq3sFmt {
             const uint32_t cb1 = __builtin_amdgcn_perm(ho, he, 0x07030602u) | n47 | 0x02020202u;
             const uint32_t s = (sc >> (8 * G + 4 * h)) & 15u;
             const float eff = d * (1.0f + 2.0f * (float)s);
-            const cfloat_p x = xg + 32 * h;
+            auto x = [&](int i) { return xat(32 * h + i); };
             float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -257,10 +289,10 @@ struct Iq3sFmt {
                 const uint32_t t1 = __builtin_amdgcn_perm(k < 4 ? ca1 : cb1, iw, sel);
                 const uint32_t v0 = lds_load<uint32_t>(t0 << 2);
                 const uint32_t v1 = lds_load<uint32_t>(t1 << 2);
-                s0 = __builtin_fmaf(h2f_lo(v0), x[4 * k + 0], s0);
-                s1 = __builtin_fmaf(h2f_hi(v0), x[4 * k + 1], s1);
-                s0 = __builtin_fmaf(h2f_lo(v1), x[4 * k + 2], s0);
-                s1 = __builtin_fmaf(h2f_hi(v1), x[4 * k + 3], s1);
+                s0 = __builtin_fmaf(h2f_lo(v0), x(4 * k + 0), s0);
+                s1 = __builtin_fmaf(h2f_hi(v0), x(4 * k + 1), s1);
+                s0 = __builtin_fmaf(h2f_lo(v1), x(4 * k + 2), s0);
+                s1 = __builtin_fmaf(h2f_hi(v1), x(4 * k + 3), s1);
             }
             acc = __builtin_fmaf(eff, s0 + s1, acc);
         }
@@ -363,12 +395,34 @@ struct Iq4xsFmt {
         r.hd = *(const uint2 *)blk;
     }
 
+    // Eight rows rit..rit+7 of a tile-layout column as 68 granules: code runs
+    // [G][8][32], then bytes 0-7 [8][8] (1088 bytes).
+    static constexpr int kSliceGran = 68;
+    __device__ static int slice_off(int g, int rit) {
+        if (g < 64) return kCodes + (g >> 4) * 2048 + 32 * rit + 16 * (g & 15);
+        return kHead + 8 * rit + 16 * (g - 64);
+    }
+    template <int G>
+    __device__ static void fetch_slice(const uint8_t *sl, int r, Raw &raw) {
+        const uint4 qa = *(const uint4 *)(sl + G * 256 + 32 * r);
+        const uint4 qb = *(const uint4 *)(sl + G * 256 + 32 * r + 16);
+        raw.q[0] = qa.x;
+        raw.q[1] = qa.y;
+        raw.q[2] = qa.z;
+        raw.q[3] = qa.w;
+        raw.q[4] = qb.x;
+        raw.q[5] = qb.y;
+        raw.q[6] = qb.z;
+        raw.q[7] = qb.w;
+        raw.hd = *(const uint2 *)(sl + 1024 + 8 * r);
+    }
+
     // Byte j of sub-block h's sixteen code bytes gives weights j (low nibble)
     // and j + 16 (high nibble). The nibbles of four bytes are split into bytes
     // with two masks; then per weight one v_perm forms v*256 + 4*lane and one
     // LDS read returns the table value.
-    template <int G>
-    __device__ static float dot(const Raw &r, int lane, cfloat_p xg, float acc) {
+    template <int G, typename XAt>
+    __device__ static float dot(const Raw &r, int lane, XAt xat, float acc) {
         const uint2 hd = r.hd;
         const uint4 qa = {r.q[0], r.q[1], r.q[2], r.q[3]};
         const uint4 qb = {r.q[4], r.q[5], r.q[6], r.q[7]};
@@ -383,7 +437,7 @@ struct Iq4xsFmt {
             const float eff = d * ((float)s - 32.0f);
             const uint32_t Q[4] = {h ? qb.x : qa.x, h ? qb.y : qa.y, h ? qb.z : qa.z,
                                    h ? qb.w : qa.w};
-            const cfloat_p x = xg + 32 * h;
+            auto x = [&](int i) { return xat(32 * h + i); };
             float s0 = 0.0f, s1 = 0.0f;
             // The 16 table reads of two code words and their 16 activations are
             // issued before the FMAs (LDS and scalar loads share one wait
@@ -406,8 +460,8 @@ struct Iq4xsFmt {
                 float xa[8], xb[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    xa[i] = x[4 * qq + i];
-                    xb[i] = x[16 + 4 * qq + i];
+                    xa[i] = x(4 * qq + i);
+                    xb[i] = x(16 + 4 * qq + i);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -666,8 +720,8 @@ __device__ __forceinline__ void cb_stream(const GroupArgs &g, const GemvArgs &si
                                 c.a.w + (int64_t)row * c.a.row_bytes + (int64_t)F::kBytes * b, raw);
                     }
                 }
-                acc = F::template dot<G>(raw, lane, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G,
-                                         acc);
+                const cfloat_p xg = as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G;
+                acc = F::template dot<G>(raw, lane, [&](int i) { return xg[i]; }, acc);
             }
             --pending;
             slot_c = nxt;
@@ -804,6 +858,152 @@ hipError_t cb_launch(int shape, const GroupArgs &g, const GemvArgs &single, cons
     }
 }
 
+// ------------------------------------------------------------------ row groups
+//
+// Single GEMVs of at most 24 blocks per row on up to one 64-row tile per
+// compute unit (the Q4_K and IQ3 row-group scheme): a workgroup of 4 NS
+// wavefronts takes eight whole rows, so no split sums meet through memory.
+// Wavefront w takes pair G = w % 4 of sub-blocks of the blocks of set w / 4,
+// lane r + 8s row r's block s + 8 (w / 4), its 64 activations in registers.
+// The table is built first (it reads the grid or table from global memory);
+// row-major rows arrive as one contiguous run of 16-byte granules (w is
+// 16-byte aligned; granules past the buffer's end are clamped and the last
+// block, if it reaches into a clamped granule, is read directly), tile-layout
+// rows as each column's eight-row slice.
+constexpr int kCbRgRows = 8;
+constexpr int kCbRgMaxBlocks = 24;
+template <class F>
+__host__ __device__ constexpr int cb_rg_region(int nb) {
+    const int run = (15 + kCbRgRows * nb * F::kBytes + 15) / 16 + 1;
+    const int gr = run > F::kSliceGran * nb ? run : F::kSliceGran * nb;
+    return (gr + 63) / 64 * 64 * 16;
+}
+template <class F>
+__host__ __device__ constexpr int cb_rg_lds(int nb, int waves) {
+    return F::kTable + cb_rg_region<F>(nb) + waves * kCbRgRows * 4 + 64;
+}
+static_assert(cb_rg_lds<Iq3sFmt>(kCbRgMaxBlocks, 12) <= 65536, "LDS of one workgroup");
+static_assert(cb_rg_lds<Iq4xsFmt>(kCbRgMaxBlocks, 12) <= 65536, "LDS of one workgroup");
+
+template <class F, int G>
+__device__ __forceinline__ float cb_rows_dot(const GemvArgs &a, const uint8_t *rg, uint32_t o,
+                                             int row, int b, int r, int lane,
+                                             const f32x4 (&xv)[16]) {
+    typename F::Raw raw;
+    if (a.layout == kLayoutTiles) {
+        F::template fetch_slice<G>(rg + b * (kCbRgRows * F::kBytes), r, raw);
+    } else {
+        F::template fetch_window<G>(rg + (o & ~15u), o & 15u, raw);
+        const uintptr_t we = (uintptr_t)a.w + (uintptr_t)a.n_out * (uintptr_t)a.row_bytes;
+        if ((we & 15) != 0 && row == a.n_out - 1 && b == a.nb - 1)
+            F::template fetch_direct<G>(a.w + (int64_t)row * a.row_bytes + F::kBytes * b, raw);
+    }
+    return F::template dot<G>(raw, lane, [&](int i) { return xv[i >> 2][i & 3]; }, 0.0f);
+}
+
+template <class F, int NS>
+__global__ __launch_bounds__(256 * NS) void cb_rows_kernel(GemvArgs a, const float *tab) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int R = kCbRgRows;
+    constexpr int W = 4 * NS;
+    const bool tl = a.layout == kLayoutTiles;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = wave & 3;
+    const int nb = a.nb;
+    const int row0 = blockIdx.x * R;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const uint32_t rgb = lds0 + F::kTable;
+    const int r = lane & (R - 1);
+    const int b = (lane >> 3) + 8 * (wave >> 2);
+
+    f32x4 xv[16];
+    {
+        const f32x4 *xp = (const f32x4 *)(a.x + (int64_t)kQK * min(b, nb - 1) + 64 * G);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) xv[q] = xp[q];
+    }
+    uint32_t o0 = 0;
+    if (tl) {
+        constexpr int GPB = F::kSliceGran;
+        const int nk = GPB * nb;
+        const int rit = row0 & 63;
+        for (int k0 = 64 * wave; k0 < nk; k0 += 64 * W) {
+            const int k = min(k0 + lane, nk - 1);
+            const int bb = k / GPB;
+            dma16(a.w + ((int64_t)(row0 >> 6) * nb + bb) * F::kCol + F::slice_off(k - GPB * bb, rit),
+                  rgb + 16 * k0);
+        }
+    } else {
+        const uintptr_t wb = (uintptr_t)a.w;
+        const uintptr_t we = wb + (uintptr_t)a.n_out * (uintptr_t)a.row_bytes;
+        const uintptr_t hi16 = (we & ~(uintptr_t)15) - 16;   // last whole granule
+        const uintptr_t start = wb + (uintptr_t)row0 * (uintptr_t)a.row_bytes;
+        const uintptr_t base16 = start & ~(uintptr_t)15;
+        o0 = (uint32_t)(start & 15);
+        const int ngr = (int)((o0 + (uint32_t)(R * a.row_bytes) + 15) / 16) + 1;
+        for (int k0 = 64 * wave; k0 < ngr; k0 += 64 * W) {
+            uintptr_t g = base16 + 16 * (uintptr_t)(k0 + lane);
+            g = g > hi16 ? hi16 : g;
+            dma16((const void *)g, rgb + 16 * k0);
+        }
+    }
+    // The table (this thread's entries) and its exactness vote, while the
+    // rows are in flight.
+    {
+        const bool exact = F::build_table(tab, threadIdx.x, 256 * NS);
+        const bool any = __builtin_amdgcn_ballot_w64(!exact) != 0;
+        if (lane == 0)
+            *(volatile __attribute__((address_space(3))) uint32_t *)(size_t)(
+                lds0 + F::kTable + cb_rg_region<F>(nb) + W * R * 4 + 4 * wave) = any ? 1u : 0u;
+    }
+    wait_vmcnt<0>();
+    lds_barrier();   // the rows, the table and the votes
+
+    float acc = 0.0f;
+    const int row = row0 + r;
+    if (b < nb) {
+        const uint8_t *rg = smem + F::kTable;
+        const uint32_t o = o0 + (uint32_t)((r * nb + b) * F::kBytes);
+        switch (G) {
+            case 0: acc = cb_rows_dot<F, 0>(a, rg, o, row, b, r, lane, xv); break;
+            case 1: acc = cb_rows_dot<F, 1>(a, rg, o, row, b, r, lane, xv); break;
+            case 2: acc = cb_rows_dot<F, 2>(a, rg, o, row, b, r, lane, xv); break;
+            default: acc = cb_rows_dot<F, 3>(a, rg, o, row, b, r, lane, xv); break;
+        }
+    }
+    acc += __shfl_xor(acc, 8);
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    float *red = (float *)(smem + F::kTable + cb_rg_region<F>(nb));
+    if (lane < R) red[wave * R + lane] = acc;
+    lds_barrier();
+    if (wave != 0 || lane >= R) return;
+    float total = red[lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) total += red[w * R + lane];
+    const volatile __attribute__((address_space(3))) uint32_t *vote =
+        (const volatile __attribute__((address_space(3))) uint32_t *)(size_t)(
+            lds0 + F::kTable + cb_rg_region<F>(nb) + W * R * 4);
+    uint32_t bad = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) bad |= vote[w];
+    if (bad != 0u) total = __builtin_nanf("");
+    if (row0 + lane < a.n_out) a.y[row0 + lane] = total;
+}
+
+template <class F>
+hipError_t cb_rows_launch(const GemvArgs &a, const float *tab, hipStream_t s) {
+    const dim3 g((a.n_out + kCbRgRows - 1) / kCbRgRows);
+    if (a.nb <= 8)
+        hipLaunchKernelGGL((cb_rows_kernel<F, 1>), g, dim3(256), cb_rg_lds<F>(a.nb, 4), s, a, tab);
+    else if (a.nb <= 16)
+        hipLaunchKernelGGL((cb_rows_kernel<F, 2>), g, dim3(512), cb_rg_lds<F>(a.nb, 8), s, a, tab);
+    else
+        hipLaunchKernelGGL((cb_rows_kernel<F, 3>), g, dim3(768), cb_rg_lds<F>(a.nb, 12), s, a, tab);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_iq3s_dequant(const uint8_t *src, const float *grid, float *dst, int64_t nblocks,
@@ -859,6 +1059,15 @@ hipError_t launch_cb_stream(int fmt, bool tiled, int shape, const GroupArgs &g,
     if (fmt == kFmtIq4xs)
         return tiled ? cb_launch<Iq4xsFmt, true>(shape, g, single, tab, nitems, s)
                      : cb_launch<Iq4xsFmt, false>(shape, g, single, tab, nitems, s);
+    return hipErrorInvalidValue;
+}
+
+bool cb_rows_fits(int nb) { return nb <= kCbRgMaxBlocks; }
+
+hipError_t launch_cb_rows(int fmt, const GemvArgs &a, const float *tab, hipStream_t s) {
+    if (a.nb > kCbRgMaxBlocks) return hipErrorInvalidValue;
+    if (fmt == kFmtIq3s) return cb_rows_launch<Iq3sFmt>(a, tab, s);
+    if (fmt == kFmtIq4xs) return cb_rows_launch<Iq4xsFmt>(a, tab, s);
     return hipErrorInvalidValue;
 }
 

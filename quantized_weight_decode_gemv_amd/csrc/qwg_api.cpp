@@ -248,8 +248,9 @@ int short_splits(int tiles, int nb) {
     return sp;
 }
 
-// Batch-1 Q4_K and IQ3 calls on the row-group kernels: the short-call matrices
-// whose rows hold at most 8 (Q4_K) or 24 (IQ3) blocks. (Not larger matrices: the Q4_K LM
+// Batch-1 Q4_K, IQ3, IQ3_S and IQ4_XS calls on the row-group kernels: the
+// short-call matrices whose rows hold at most 8 (Q4_K) or 24 (the others)
+// blocks. (Not larger matrices: the Q4_K LM
 // head, 32000 x 2048, took 17.4 us per call on row groups against 11.0 us on
 // the stream engine, event time on one box.) QWG_ROWS=0 turns them off (A/B
 // measurements: those matrices then run on the split short-call kernels).
@@ -265,6 +266,9 @@ bool rows_engine(int tiles, int nb) {
 }
 bool rows_engine_iq3(int tiles, int nb) {
     return !rows_off() && iq3_rows_fits(nb) && short_splits(tiles, nb) > 0;
+}
+bool rows_engine_cb(int tiles, int nb) {
+    return !rows_off() && cb_rows_fits(nb) && short_splits(tiles, nb) > 0;
 }
 
 // IQ3 stream engine shape. Measured on MI355X: grouped streams run best with
@@ -474,6 +478,7 @@ int qwg_plan_splits(int fmt, int64_t n_in, int64_t n_out) {
     if (rc) return -rc;
     const int tiles = (int)((n_out + kTileRows - 1) / kTileRows);
     if (codebook_format(fmt)) {
+        if (rows_engine_cb(tiles, (int)(n_in / kQK))) return 1;
         const int sp = cb_plan(fmt, false, (int)(n_in / kQK), tiles).splits;
         return sp > 0 ? sp : -QWG_ERR_HIP;
     }
@@ -959,6 +964,7 @@ int cb_gemv(int fmt, bool tiled, float *y, const float *x, const void *w, const 
     GemvArgs a;
     fill_shape(a, w, x, tab, y, n_in, n_out, block_bytes_of(fmt));
     a.layout = tiled ? kLayoutTiles : kLayoutRows;
+    if (rows_engine_cb(a.tiles, a.nb)) return hip_status(launch_cb_rows(fmt, a, tab, (hipStream_t)stream));
     const CbPlan plan = cb_plan(fmt, tiled, a.nb, a.tiles);
     if (plan.splits <= 0) return QWG_ERR_HIP;
     a.splits = plan.splits;

@@ -140,6 +140,10 @@ int cb_stream_shape(int fmt, bool split);
 // shape on the current device (0: unknown format or shape)
 int cb_stream_slots(int fmt, bool tiled, int shape);
 // tiled: the tile layout; otherwise row-major blocks, w 16-byte aligned
+// Row-group kernel for IQ3_S / IQ4_XS single GEMVs (a.layout rows or tiles,
+// rows of nb <= 24 blocks): eight whole rows per workgroup, no split sums.
+bool cb_rows_fits(int nb);
+hipError_t launch_cb_rows(int fmt, const GemvArgs &a, const float *tab, hipStream_t s);
 hipError_t launch_cb_stream(int fmt, bool tiled, int shape, const GroupArgs &g,
                             const GemvArgs &single, const float *tab, int nitems, hipStream_t s);
 

@@ -1796,6 +1796,36 @@ def test_gemv_codebook_rows_reads_only_the_weights(fmt, offset, n_out, n_in):
 
 
 @pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
+@pytest.mark.parametrize("n_out,n_in", [(1, 256), (9, 2048), (63, 1792), (1000, 2048),
+                                        (5632, 2048), (3, 2304), (130, 4096), (2048, 5632),
+                                        (17, 6144)])
+def test_gemv_codebook_row_groups(fmt, n_out, n_in):
+    # Row-group kernel for IQ3_S / IQ4_XS single GEMVs (at most 24 blocks per
+    # row, a matrix the split short-call plan covers): eight whole rows per
+    # workgroup; row-major weights between guard bytes, ragged last groups,
+    # rows past n_out untouched; the tile layout with the same bits (the same
+    # kernel and order); repeat calls with the same bits.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert -(-n_out // 64) <= cus // 2
+    assert qwg.plan_splits(CB_FMT[fmt], n_in, n_out) == 1
+    c = CB[fmt]
+    tab = c["table"]()
+    w = c["weights"](n_out, n_in, 172, n_out)
+    x = synth.activations(n_in, 172, n_out)
+    wd, xd, td = _guarded_cb(w, 16), dev(x), dev(tab)
+    yr, sr = c["o_gemv"](w, tab, x, n_in, n_out)
+    ybuf = torch.full((n_out + 128,), float("nan"), device=DEV)
+    c["rows"](wd, xd, td, out=ybuf[64:64 + n_out])
+    yb = host(ybuf)
+    assert np.isnan(yb[:64]).all() and np.isnan(yb[64 + n_out:]).all(), "write outside y"
+    y = yb[64:64 + n_out]
+    assert_bound(y, yr, sr, f"{fmt} row groups {n_out}x{n_in}")
+    t = host(c["gemv"](c["pack"](dev(w), n_in), xd, td, n_out))
+    assert_bits(t, y, f"{fmt} tile layout")
+    assert_bits(host(c["rows"](wd, xd, td)), y, f"{fmt} repeat")
+
+
+@pytest.mark.parametrize("fmt", ["iq3s", "iq4xs"])
 def test_gemv_codebook_rows_misaligned_weights_rejected(fmt):
     c = CB[fmt]
     w = c["weights"](2, 256, 170, 0)
