@@ -67,8 +67,8 @@ KERNEL_SOURCES = ["quantized_weight_decode_gemv_amd/csrc/chain.hip",
 # WRITE_SIZE runs of this script, each scaled by the same counter on a plain device copy of known
 # size (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0; see profiles/q4k_chain_c5.md). Valid only for the
 # kernel sources with this hash; otherwise traffic is reported as null.
-TRAFFIC = {"sources_sha256": "1be5b49d00b0b8dd51b9be1b287dc8519067ddad506dbe4ed965040349fd4a6c",
-           "fetch_bytes": 620770944, "write_bytes": 6816768}
+TRAFFIC = {"sources_sha256": "37d4448fcc5fa42791aced621d92b98d21b982e4f78577b6fa069164e4b8a3aa",
+           "fetch_bytes": 620764864, "write_bytes": 6816768}
 
 
 def kernel_sources_sha256() -> str:
