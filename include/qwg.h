@@ -340,12 +340,16 @@ int qwg_gemm_q4k_ex(float *y, const float *x, const void *w, int64_t n_in, int64
  * A stage of the GEMV then copies one contiguous 9216-byte run instead of 64
  * rows' 144-byte pieces.
  *
- * Tile layout for IQ3: the same tile and column order (column (t, b) at
- * (t*(n_in/256) + b)*6272), each 6272-byte column regrouped by field so that
- * every read of the GEMV is aligned and conflict-free: the 64 rows' index
- * bytes 16G..16G+15 for G = 0..3 ([G][row][16], 4096 bytes), their sign/scale
- * words 2G, 2G+1 ([G][row][8], 2048 bytes), then their d ([row][2], 128 bytes).
- * The bytes of every block are kept, only regrouped.
+ * Tile layout for IQ3 (102 bytes per block): the same tile and column order
+ * (column (t, b) at (t*(n_in/256) + b)*6528), each 6528-byte column regrouped
+ * by field so that every read of the GEMV is aligned and conflict-free: the 64
+ * rows' index bytes 16G..16G+15 for G = 0..3 ([G][row][16], 4096 bytes); the
+ * sign groups of their words 2G, 2G+1 as sign bytes ([G][row][8], 2048 bytes:
+ * byte k of a word's four is its group k's seven stored signs with, in bit 7,
+ * the eighth that the even-count rule implies); the words' 4-bit scales
+ * ([G][row], 256 bytes: word 2G's in the low nibble, 2G+1's in the high one);
+ * then their d ([row][2], 128 bytes). Every stored bit of every block is kept;
+ * the implied signs are written out so that the GEMV need not recover them.
  *
  * qwg_tiled_bytes: bytes of the tile layout (ceil(n_out/64)*64 rows) for
  * any QWG_FMT_* format, or a negative status.

@@ -113,31 +113,47 @@ __global__ __launch_bounds__(256) void iq3_dequant_kernel(const uint8_t *__restr
 // with the address straight out of the v_perm (entry at i*256 + s*16) measured
 // slower: its bank depends on s alone, so lanes collide far more often.
 // Tile layout (qwg_pack_iq3_tiles): for each 64-row tile and block column b,
-// 6272 bytes = the 64 rows' blocks regrouped by field and wavefront role:
-// index bytes [G][row][16] (bytes 16G..16G+15 of each block, 4 x 1024 B), sign/
-// scale words [G][row][8] (words 2G, 2G+1, 4 x 512 B), then d [row][2] (128 B).
-// Column (t, b) starts at (t*nb + b) * 6272; rows past n_out are zero blocks.
+// 6528 bytes = the 64 rows' blocks regrouped by field and wavefront role, with
+// the signs written out: index bytes [G][row][16] (bytes 16G..16G+15 of each
+// block, 4 x 1024 B); sign bytes [G][row][8] (sub-blocks 2G and 2G+1, four
+// bytes each: byte k holds group k's seven stored signs and, in bit 7, the
+// eighth, the one the even-count rule implies; 4 x 512 B); sub-block scales
+// [G][row] (scale of sub-block 2G in the low nibble, 2G+1 in the high one;
+// 4 x 64 B); then d [row][2] (128 B). 102 bytes per block against the
+// container's 98: the 32 implied signs are stored, so the dot takes each sign
+// nibble with one mask instead of the ~11 VALU ops per word that recover the
+// eighth sign and move the 7-bit groups apart (measured on the grouped IQ3
+// stream, a copy of the kernel that skipped that step: 90.6 -> 81.6 us).
+// Column (t, b) starts at (t*nb + b) * 6528; rows past n_out are zero blocks.
 // A stage copy is contiguous, and wavefront G's lanes (rows) read consecutive
-// 16-, 8- and 2-byte pieces: no realignment, no bank conflicts, no clamping.
-constexpr int kIq3TileCol = kTileRows * kIq3Bytes;   // 6272
-constexpr int kIq3TileWords = 4096;
-constexpr int kIq3TileD = 6144;
+// 16-, 8-, 1- and 2-byte pieces: no realignment, no bank conflicts, no clamping.
+constexpr int kIq3TileSigns = 4096;
+constexpr int kIq3TileScales = 6144;
+constexpr int kIq3TileD = 6400;
+constexpr int kIq3TileCol = 6528;
+static_assert(kIq3TileCol == kTileRows * kIq3TileBlock, "tile column = 64 tile-layout blocks");
+// A stream stage column in LDS: the index bytes at the column's layout, then
+// for each wavefront G a private run of kIq3Own bytes (its sign bytes, its
+// scale bytes, its own copy of the column's d) that only it copies and reads,
+// so the stream engine's tile-layout stages need no workgroup barrier.
+constexpr int kIq3Own = 512 + 64 + 128;
 
 template <int W, int R, bool TL>
 struct Iq3Cfg {
     static constexpr int kBps = W / 4;                   // super-blocks per stage
     static constexpr int kWin = 112;                     // bytes per row window
-    // one super-block of a tile (tile layout: the column, then a private copy of
-    // its 128 d bytes for each of the four quant-chunk wavefronts)
-    static constexpr int kCol = TL ? kIq3TileCol + 4 * 128 : kTileRows * kWin;
+    // one super-block of a tile (tile layout: the index bytes, then the four
+    // quant-chunk wavefronts' private runs)
+    static constexpr int kCol = TL ? kIq3TileSigns + 4 * kIq3Own : kTileRows * kWin;
     static constexpr int kSlot = kBps * kCol;
     static constexpr int kTable = 32768;                 // at LDS address 0
     static constexpr int kGrid = kTable;                 // staged fp32 grid, 4 KB
     static constexpr int kRing = kGrid + 256 * 16;
     static constexpr int kRed = kRing + R * kSlot;       // [2][W][64] fp32 row sums
     static constexpr int kLds = kRed + 2 * W * 64 * 4;
-    // copy instructions per wavefront and stage (tile layout: indices, words, d)
-    static constexpr int kCps = TL ? 3 : 2;
+    // copy instructions per wavefront and stage (tile layout: the indices, then
+    // the private run)
+    static constexpr int kCps = 2;
 };
 
 // One work item as a cursor sees it.
@@ -205,10 +221,13 @@ __device__ __forceinline__ void iq3_load_item(Iq3Item &it, int k, const GroupArg
 
 // The bytes of one block that wavefront G uses, 32-bit aligned to the block:
 // index bytes 16G..16G+15, sign/scale words 2G and 2G+1, and d (low 16 bits).
+// From the tile layout, words[] holds the sign bytes of sub-blocks 2G and 2G+1
+// (eight signs per byte) and sc their scales (low nibble 2G, high 2G+1).
 struct Iq3Raw {
     uint32_t idx[4];
     uint32_t words[2];
     uint32_t d16;
+    uint32_t sc;
 };
 
 // From a row window in LDS: `win` = window + (sh & 12), sh = block offset in it
@@ -253,34 +272,35 @@ __device__ __forceinline__ void iq3_fetch_xxs(const uint8_t *win, uint32_t sh, I
     r.d16 = p[0] >> ((sh & 2u) << 3);
 }
 
-// From a tile-layout stage column (this lane's row).
+// From a tile-layout column copied whole (this lane's row).
 template <int G>
 __device__ __forceinline__ void iq3_fetch_tiled(const uint8_t *col, int lane, Iq3Raw &r) {
     const uint4 q = *(const uint4 *)(col + G * 1024 + 16 * lane);
-    const uint2 w = *(const uint2 *)(col + kIq3TileWords + G * 512 + 8 * lane);
+    const uint2 w = *(const uint2 *)(col + kIq3TileSigns + G * 512 + 8 * lane);
     r.idx[0] = q.x;
     r.idx[1] = q.y;
     r.idx[2] = q.z;
     r.idx[3] = q.w;
     r.words[0] = w.x;
     r.words[1] = w.y;
+    r.sc = col[kIq3TileScales + G * 64 + lane];
     r.d16 = *(const uint16_t *)(col + kIq3TileD + 2 * lane);
 }
 
-// The same with this wavefront's private copy of the column's d bytes at
-// col + dcopy (the stream engine's barrier-free tile-layout stages).
+// From a stream stage column (this lane's row; wavefront G's private run).
 template <int G>
-__device__ __forceinline__ void iq3_fetch_tiled_own_d(const uint8_t *col, int lane, uint32_t dcopy,
-                                                      Iq3Raw &r) {
+__device__ __forceinline__ void iq3_fetch_tiled_own(const uint8_t *col, int lane, Iq3Raw &r) {
     const uint4 q = *(const uint4 *)(col + G * 1024 + 16 * lane);
-    const uint2 w = *(const uint2 *)(col + kIq3TileWords + G * 512 + 8 * lane);
+    const uint8_t *own = col + kIq3TileSigns + G * kIq3Own;
+    const uint2 w = *(const uint2 *)(own + 8 * lane);
     r.idx[0] = q.x;
     r.idx[1] = q.y;
     r.idx[2] = q.z;
     r.idx[3] = q.w;
     r.words[0] = w.x;
     r.words[1] = w.y;
-    r.d16 = *(const uint16_t *)(col + dcopy + 2 * lane);
+    r.sc = own[512 + lane];
+    r.d16 = *(const uint16_t *)(own + 576 + 2 * lane);
 }
 
 // From global memory, 2 bytes at a time (the block is 2-byte aligned), in
@@ -298,21 +318,55 @@ __device__ __forceinline__ void iq3_fetch_direct(const uint8_t *blk, bool xxs, I
     r.d16 = h[hd];
 }
 
+// 8 x the low / high 16 bits of v (one v_mad_u32_u16 each).
+__device__ __forceinline__ uint32_t lo16_x8(uint32_t v) {
+    uint32_t r;
+    asm("v_mad_u32_u16 %0, %1, 8, 0" : "=v"(r) : "v"(v));
+    return r;
+}
+__device__ __forceinline__ uint32_t hi16_x8(uint32_t v) {
+    uint32_t r;
+    asm("v_mad_u32_u16 %0, %1, 8, 0 op_sel:[1,0,0,0]" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// The sign-folded table entries of the eight 4-weight groups of sub-block
+// half of the chunk: group k's entry (nibble*256 + index byte) * 8, its index
+// byte k & 3 of word idx[2 half + k / 4], its sign nibble byte k / 2 of ne
+// (k even) or no (k odd). One v_perm forms the entry numbers of groups k and
+// k + 2 in the two 16-bit halves (same index word, same nibble word), and one
+// multiply-add per half scales each to a byte address: three VALU ops per two
+// groups instead of a perm and a shift per group.
+__device__ __forceinline__ void iq3_table_reads(const Iq3Raw &r, int half, uint32_t ne,
+                                                uint32_t no, u32x2 (&v)[8]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int k = (p & 1) | ((p & 2) << 1);   // 0, 1, 4, 5
+        const uint32_t sel = (uint32_t)(k & 3) | ((uint32_t)(4 + (k >> 1)) << 8) |
+                             ((uint32_t)((k + 2) & 3) << 16) | ((uint32_t)(4 + ((k + 2) >> 1)) << 24);
+        const uint32_t pr = __builtin_amdgcn_perm((k & 1) ? no : ne, r.idx[2 * half + (k >> 2)], sel);
+        v[k] = lds_load<u32x2>(lo16_x8(pr));
+        v[k + 2] = lds_load<u32x2>(hi16_x8(pr));
+    }
+}
+
 // acc + sum over wavefront G's 64 weights of this lane's row of w*x.
 // xg: x[256*b + 64*G] (wave-uniform). The sign-folded grid table sits at LDS
 // address 0. Two interleaved partial sums per sub-block keep consecutive FMAs
-// independent.
-template <int G>
+// independent. SX: the raw block comes from the tile layout (signs written
+// out, scales apart).
+template <int G, bool SX>
 __device__ __forceinline__ float iq3_dot(const Iq3Raw &r, cfloat_p xg, float acc) {
     const float dq = h2f_lo(r.d16) * 0.25f;   // d*(0.5+code)*0.5 == (d/4)*(2*code+1), exact
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const uint32_t word = r.words[half];
-        const uint32_t s8 = iq3_signs(word);
+        const uint32_t s8 = SX ? word : iq3_signs(word);
+        const uint32_t code = SX ? (r.sc >> (4 * half)) & 15u : word >> 28;
         // sign nibble of 4-weight group k: low nibble of byte k/2 of ne (k even) or no (k odd)
         const uint32_t ne = s8 & 0x0F0F0F0Fu;
         const uint32_t no = (s8 >> 4) & 0x0F0F0F0Fu;
-        const float db = dq * (float)(2u * (word >> 28) + 1u);
+        const float db = dq * (float)(2u * code + 1u);
         const cfloat_p xs = xg + 32 * half;
         // All eight table reads and the 32 activations (scalar loads) are issued
         // before the first FMA: LDS and scalar loads share one wait counter, and
@@ -320,13 +374,7 @@ __device__ __forceinline__ float iq3_dot(const Iq3Raw &r, cfloat_p xg, float acc
         // reads waited out a full round trip (measured: tile-layout stream
         // 95 -> 93 us, row-major 138 -> 132 us).
         u32x2 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            // byte 0 = index byte, byte 1 = nibble: entry (s*256 + i) * 8
-            const uint32_t sel = (uint32_t)(k & 3) | ((uint32_t)(4 + (k >> 1)) << 8) | 0x0C0C0000u;
-            const uint32_t ti = __builtin_amdgcn_perm((k & 1) ? no : ne, r.idx[2 * half + (k >> 2)], sel);
-            v[k] = lds_load<u32x2>(ti << 3);
-        }
+        iq3_table_reads(r, half, ne, no, v);
         float xv[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) xv[i] = xs[i];
@@ -416,15 +464,16 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
                           (uint32_t)d.a.row_bytes +
                       cgran[i];
     };
-    // Tile layout: wavefront G copies its index bytes (1 KB, every lane), its
-    // words (512 B, lanes 0..31) and its own copy of the column's d bytes (128
-    // B, lanes 0..7, after the column): every byte a wavefront reads in a stage
-    // is one it copied, so stages need no workgroup barrier, only the
-    // wavefront's own wait for its copies.
+    // Tile layout: wavefront G copies its index bytes (1 KB, every lane) and
+    // its private run (lanes 0..31 its sign bytes, 32..35 its scale bytes,
+    // 36..43 the column's d): every byte a wavefront reads in a stage is one it
+    // copied, so stages need no workgroup barrier, only the wavefront's own
+    // wait for its copies.
     const uint32_t t_off0 = (uint32_t)(G * 1024 + 16 * lane);
-    const uint32_t t_off1 = (uint32_t)(kIq3TileWords + G * 512 + 16 * lane);
-    const uint32_t t_off2 = (uint32_t)(kIq3TileD + 16 * lane);
-    constexpr uint32_t t_dcopy = (uint32_t)(kIq3TileCol + 128 * G);
+    const uint32_t t_off1 =
+        lane < 32 ? (uint32_t)(kIq3TileSigns + G * 512 + 16 * lane)
+                  : lane < 36 ? (uint32_t)(kIq3TileScales + G * 64 + 16 * (lane - 32))
+                              : (uint32_t)(kIq3TileD + 16 * (lane - 36));
     prep_copy();
     uint32_t flags = 0;  // bit k: this wavefront's copies are in ring slot k
     auto issue_next = [&]() {
@@ -435,8 +484,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
                 const uint32_t colb = lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol;
                 const uint8_t *src = d.sb + (int64_t)b * kIq3TileCol;
                 dma16_stream(src + t_off0, colb + G * 1024);
-                if (lane < 32) dma16_stream(src + t_off1, colb + kIq3TileWords + G * 512);
-                if (lane < 8) dma16_stream(src + t_off2, colb + t_dcopy);
+                if (lane < kIq3Own / 16) dma16_stream(src + t_off1, colb + kIq3TileSigns + G * kIq3Own);
             } else {
                 const uint32_t base =
                     lds0 + C::kRing + slot_d * C::kSlot + j * C::kCol + G * (16 * C::kWin);
@@ -516,9 +564,8 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
             const int b = c.kb0 + s * BPS + j;
             if (TL && b < c.kb1) {
                 Iq3Raw raw;
-                iq3_fetch_tiled_own_d<G>(smem + C::kRing + slot_c * C::kSlot + j * C::kCol, lane,
-                                         t_dcopy, raw);
-                acc = iq3_dot<G>(raw, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
+                iq3_fetch_tiled_own<G>(smem + C::kRing + slot_c * C::kSlot + j * C::kCol, lane, raw);
+                acc = iq3_dot<G, true>(raw, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
             } else if (b < c.kb1) {
                 const uint32_t sh = (rlo + (uint32_t)(kIq3Bytes * b)) & 15u;
                 const uint8_t *win = smem + C::kRing + slot_c * C::kSlot + j * C::kCol +
@@ -536,7 +583,7 @@ __device__ __forceinline__ void iq3_stream(const GroupArgs &g, const GemvArgs &s
                         iq3_fetch_direct<G>(c.a.w + (int64_t)row * c.a.row_bytes + kIq3Bytes * b,
                                             xxs, raw);
                 }
-                acc = iq3_dot<G>(raw, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
+                acc = iq3_dot<G, false>(raw, as_scalar(c.a.x) + (int64_t)kQK * b + 64 * G, acc);
             }
             --pending;
             slot_c = nxt;
@@ -635,23 +682,19 @@ constexpr int iq3_short_lds(int c, bool tl) {
 }
 
 // iq3_dot with the chunk's 64 activations already in registers.
-template <int G, typename XAt>
+template <int G, bool SX, typename XAt>
 __device__ __forceinline__ float iq3_dot_regs(const Iq3Raw &r, XAt xat, float acc) {
     const float dq = h2f_lo(r.d16) * 0.25f;   // d*(0.5+code)*0.5 == (d/4)*(2*code+1), exact
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const uint32_t word = r.words[half];
-        const uint32_t s8 = iq3_signs(word);
+        const uint32_t s8 = SX ? word : iq3_signs(word);
         const uint32_t ne = s8 & 0x0F0F0F0Fu;
         const uint32_t no = (s8 >> 4) & 0x0F0F0F0Fu;
-        const float db = dq * (float)(2u * (word >> 28) + 1u);
+        const uint32_t code = SX ? (r.sc >> (4 * half)) & 15u : word >> 28;
+        const float db = dq * (float)(2u * code + 1u);
         u32x2 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t sel = (uint32_t)(k & 3) | ((uint32_t)(4 + (k >> 1)) << 8) | 0x0C0C0000u;
-            const uint32_t ti = __builtin_amdgcn_perm((k & 1) ? no : ne, r.idx[2 * half + (k >> 2)], sel);
-            v[k] = lds_load<u32x2>(ti << 3);
-        }
+        iq3_table_reads(r, half, ne, no, v);
         float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -686,16 +729,15 @@ __device__ __forceinline__ float iq3_short_column(const GemvArgs &a, const uint8
                             (uintptr_t)kIq3Bytes * b;
     Iq3Raw raw;
     iq3_short_fetch<G>(col, a.layout, (uint32_t)start & 15u, lane, raw);
-    if (!tl) {
-        // a window granule that lies partly outside the buffer was clamped:
-        // that row's block comes from 2-byte loads instead (at most twice per matrix)
-        const bool head = (wb & 15) != 0 && row == 0 && b == 0;
-        const bool tail = (we & 15) != 0 && row == a.n_out - 1 && b == a.nb - 1;
-        if (head || tail)
-            iq3_fetch_direct<G>(a.w + (int64_t)row * a.row_bytes + kIq3Bytes * b,
-                                a.layout == kLayoutRowsXxs, raw);
-    }
-    return iq3_dot_regs<G>(raw, [&](int i) { return xs[i]; }, 0.0f);
+    if (tl) return iq3_dot_regs<G, true>(raw, [&](int i) { return xs[i]; }, 0.0f);
+    // a window granule that lies partly outside the buffer was clamped: that
+    // row's block comes from 2-byte loads instead (at most twice per matrix)
+    const bool head = (wb & 15) != 0 && row == 0 && b == 0;
+    const bool tail = (we & 15) != 0 && row == a.n_out - 1 && b == a.nb - 1;
+    if (head || tail)
+        iq3_fetch_direct<G>(a.w + (int64_t)row * a.row_bytes + kIq3Bytes * b,
+                            a.layout == kLayoutRowsXxs, raw);
+    return iq3_dot_regs<G, false>(raw, [&](int i) { return xs[i]; }, 0.0f);
 }
 
 template <int C>
@@ -721,7 +763,7 @@ __global__ __launch_bounds__(256 * C) void iq3_short_kernel(GemvArgs a, ShortSta
 
     // The tile's epoch (split launches; used at the end), the grid (wavefronts
     // 0..3, 1 KB each), then the columns: copies G and G + 4 of each column's
-    // seven 1 KB pieces.
+    // seven 1 KB pieces (the last one 384 bytes on the tile layout).
     uint32_t epoch = 0;
     if (a.splits > 1 && wave == 0)
         epoch = __hip_atomic_load(&st.epochs[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -735,7 +777,7 @@ __global__ __launch_bounds__(256 * C) void iq3_short_kernel(GemvArgs a, ShortSta
         for (int q = G; q < 7; q += 4) {
             const uint32_t dst = colb + 1024 * q;
             if (tl) {
-                if (q < 6 || lane < 8)
+                if (q < 6 || lane < (kIq3TileCol - 6144) / 16)
                     dma16(a.w + ((int64_t)tile * a.nb + b) * kIq3TileCol + 1024 * q + 16 * lane, dst);
             } else {
                 const int k = 64 * q + lane;          // granule k % 7 of row k / 7's window
@@ -812,17 +854,19 @@ __global__ __launch_bounds__(256 * C) void iq3_short_kernel(GemvArgs a, ShortSta
 // byte order: 8 x nb x 98 bytes from the group's first block, granules that
 // reach outside the buffer clamped and the two blocks they hold read directly
 // as in the stream engine) or as the eight rows' slices of each tile-layout
-// column (784 bytes: index, word and d runs). The sign-folded table and the
+// column (848 bytes: index, sign, scale and d runs; the scale runs are the
+// 16-byte granules that hold the rows' 8 bytes). The sign-folded table and the
 // exactness vote are the short-call kernel's.
 constexpr int kIq3RgRows = 8;
 constexpr int kIq3RgMaxBlocks = 24;
-constexpr int kIq3RgSlice = 784;                        // 8 rows of a tile-layout column
+constexpr int kIq3RgGran = 53;                          // granules of one slice
+constexpr int kIq3RgSlice = 16 * kIq3RgGran;            // 8 rows of a tile-layout column
 // The rows' granules (row-major run with its head and one over-read granule,
 // or the tile slices), in whole 64-granule copy instructions; then the
 // reduction [wavefronts][8 rows] fp32.
 __host__ __device__ constexpr int iq3_rg_region(int nb) {
     const int run = (15 + kIq3RgRows * nb * kIq3Bytes + 15) / 16 + 1;
-    const int gr = run > 49 * nb ? run : 49 * nb;
+    const int gr = run > kIq3RgGran * nb ? run : kIq3RgGran * nb;
     return (gr + 63) / 64 * 64 * 16;
 }
 __host__ __device__ constexpr int iq3_rg_lds(int nb, int waves) {
@@ -830,11 +874,13 @@ __host__ __device__ constexpr int iq3_rg_lds(int nb, int waves) {
 }
 static_assert(iq3_rg_lds(kIq3RgMaxBlocks, 12) <= 65536, "LDS of one workgroup");
 
-// Byte offset in a tile-layout column of granule g (0..48) of the eight-row
-// slice starting at row rit (a multiple of 8): index runs, word runs, d.
+// Byte offset in a tile-layout column of granule g (0..52) of the eight-row
+// slice starting at row rit (a multiple of 8): index runs, sign runs, the
+// granule of each scale run that holds the rows' bytes (at byte rit & 8), d.
 __device__ __forceinline__ int iq3_rg_tile_off(int g, int rit) {
     if (g < 32) return (g >> 3) * 1024 + 16 * rit + 16 * (g & 7);
-    if (g < 48) return kIq3TileWords + ((g - 32) >> 2) * 512 + 8 * rit + 16 * ((g - 32) & 3);
+    if (g < 48) return kIq3TileSigns + ((g - 32) >> 2) * 512 + 8 * rit + 16 * ((g - 32) & 3);
+    if (g < 52) return kIq3TileScales + (g - 48) * 64 + (rit & ~15);
     return kIq3TileD + 2 * rit;
 }
 
@@ -852,7 +898,9 @@ __device__ __forceinline__ float iq3_rows_dot(const GemvArgs &a, const uint8_t *
         raw.idx[3] = q.w;
         raw.words[0] = w.x;
         raw.words[1] = w.y;
-        raw.d16 = *(const uint16_t *)(sl + 768 + 2 * r);
+        raw.sc = sl[768 + G * 16 + (row & 8) + r];
+        raw.d16 = *(const uint16_t *)(sl + 832 + 2 * r);
+        return iq3_dot_regs<G, true>(raw, [&](int i) { return xv[i >> 2][i & 3]; }, 0.0f);
     } else {
         const bool xxs = a.layout == kLayoutRowsXxs;
         const uint8_t *win = rg + (o & ~3u);
@@ -866,7 +914,7 @@ __device__ __forceinline__ float iq3_rows_dot(const GemvArgs &a, const uint8_t *
         const bool tail = (we & 15) != 0 && row == a.n_out - 1 && b == a.nb - 1;
         if (head || tail) iq3_fetch_direct<G>(a.w + (int64_t)row * a.row_bytes + kIq3Bytes * b, xxs, raw);
     }
-    return iq3_dot_regs<G>(raw, [&](int i) { return xv[i >> 2][i & 3]; }, 0.0f);
+    return iq3_dot_regs<G, false>(raw, [&](int i) { return xv[i >> 2][i & 3]; }, 0.0f);
 }
 
 template <int NS>
@@ -898,12 +946,13 @@ __global__ __launch_bounds__(256 * NS) void iq3_rows_kernel(GemvArgs a, const fl
     }
     uint32_t o0 = 0;   // the group's first block in the copied run (row-major)
     if (tl) {
-        const int nk = 49 * nb;
+        const int nk = kIq3RgGran * nb;
         const int rit = row0 & 63;
         for (int k0 = 64 * wave; k0 < nk; k0 += 64 * W) {
             const int k = min(k0 + lane, nk - 1);
-            const int bb = k / 49;
-            dma16(a.w + ((int64_t)(row0 >> 6) * nb + bb) * kIq3TileCol + iq3_rg_tile_off(k - 49 * bb, rit),
+            const int bb = k / kIq3RgGran;
+            dma16(a.w + ((int64_t)(row0 >> 6) * nb + bb) * kIq3TileCol +
+                      iq3_rg_tile_off(k - kIq3RgGran * bb, rit),
                   rgb + 16 * k0);
         }
     } else {
@@ -963,7 +1012,15 @@ __global__ __launch_bounds__(256 * NS) void iq3_rows_kernel(GemvArgs a, const fl
 }
 
 // Row-major IQ3 weights -> tile layout, one workgroup per (tile, block column),
-// 2-byte units (the source blocks are only 2-byte aligned).
+// one 4-byte unit of the column per thread and step (the source blocks are
+// only 2-byte aligned: 2-byte loads). Index bytes and d are copied; each sign
+// word becomes its four sign bytes (iq3_signs) and its scale nibble moves to
+// the scale run.
+__device__ __forceinline__ uint32_t iq3_ld32(const uint8_t *p) {
+    const uint16_t *h = (const uint16_t *)p;
+    return (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+}
+
 __global__ __launch_bounds__(256) void iq3_pack_tiles_kernel(const uint8_t *__restrict__ src,
                                                              uint8_t *__restrict__ dst, int nb,
                                                              int n_out, bool xxs) {
@@ -971,24 +1028,41 @@ __global__ __launch_bounds__(256) void iq3_pack_tiles_kernel(const uint8_t *__re
     const int b = blockIdx.x % nb;
     const int tile = blockIdx.x / nb;
     const int64_t row_bytes = (int64_t)nb * kIq3Bytes;
-    uint16_t *out = (uint16_t *)(dst + (int64_t)blockIdx.x * kIq3TileCol);
-    for (int u = threadIdx.x; u < kIq3TileCol / 2; u += blockDim.x) {
-        const int o = 2 * u;
-        int rr, sbyte;
-        if (o < kIq3TileWords) {
-            rr = (o & 1023) >> 4;
-            sbyte = fo.idx + 16 * (o >> 10) + (o & 15);
-        } else if (o < kIq3TileD) {
-            const int o2 = o - kIq3TileWords;
-            rr = (o2 & 511) >> 3;
-            sbyte = fo.words + 8 * (o2 >> 9) + (o2 & 7);
-        } else {
-            rr = (o - kIq3TileD) >> 1;
-            sbyte = fo.d;
-        }
+    // block b of tile row rr, or null past n_out (zero blocks)
+    auto blk = [&](int rr) -> const uint8_t * {
         const int r = tile * kTileRows + rr;
-        uint16_t v = 0;
-        if (r < n_out) v = *(const uint16_t *)(src + r * row_bytes + (int64_t)b * kIq3Bytes + sbyte);
+        return r < n_out ? src + r * row_bytes + (int64_t)b * kIq3Bytes : nullptr;
+    };
+    uint32_t *out = (uint32_t *)(dst + (int64_t)blockIdx.x * kIq3TileCol);
+    for (int u = threadIdx.x; u < kIq3TileCol / 4; u += blockDim.x) {
+        const int o = 4 * u;
+        uint32_t v = 0;
+        if (o < kIq3TileSigns) {            // [G][row][16] index bytes
+            const uint8_t *p = blk((o & 1023) >> 4);
+            if (p) v = iq3_ld32(p + fo.idx + 16 * (o >> 10) + (o & 15));
+        } else if (o < kIq3TileScales) {    // [G][row][8] sign bytes of words 2G, 2G+1
+            const int o2 = o - kIq3TileSigns;
+            const uint8_t *p = blk((o2 & 511) >> 3);
+            if (p) v = iq3_signs(iq3_ld32(p + fo.words + 8 * (o2 >> 9) + (o2 & 7)));
+        } else if (o < kIq3TileD) {         // [G][row] scales of words 2G, 2G+1, four rows
+            const int o2 = o - kIq3TileScales;
+            const int g = o2 >> 6;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint8_t *p = blk((o2 & 63) + i);
+                if (p) {
+                    const uint32_t s0 = iq3_ld32(p + fo.words + 8 * g) >> 28;
+                    const uint32_t s1 = iq3_ld32(p + fo.words + 8 * g + 4) >> 28;
+                    v |= (s0 | (s1 << 4)) << (8 * i);
+                }
+            }
+        } else {                            // [row][2] d, two rows
+            const int rr = (o - kIq3TileD) >> 1;
+            const uint8_t *p0 = blk(rr);
+            const uint8_t *p1 = blk(rr + 1);
+            if (p0) v = *(const uint16_t *)(p0 + fo.d);
+            if (p1) v |= (uint32_t)*(const uint16_t *)(p1 + fo.d) << 16;
+        }
         out[u] = v;
     }
 }

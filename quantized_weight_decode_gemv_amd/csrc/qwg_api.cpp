@@ -738,7 +738,8 @@ int64_t qwg_tiled_bytes(int fmt, int64_t n_in, int64_t n_out) {
     if (!known_format(fmt)) return -QWG_ERR_FORMAT;
     const int rc = check_gemv_shape(n_in, n_out);
     if (rc) return -rc;
-    return ((n_out + kTileRows - 1) / kTileRows) * kTileRows * (n_in / kQK) * block_bytes_of(fmt);
+    const int tb = (fmt == QWG_FMT_IQ3 || fmt == QWG_FMT_IQ3_XXS) ? kIq3TileBlock : block_bytes_of(fmt);
+    return ((n_out + kTileRows - 1) / kTileRows) * kTileRows * (n_in / kQK) * tb;
 }
 
 int qwg_pack_q4k_tiles(void *dst, const void *src, int64_t n_in, int64_t n_out, void *stream) {

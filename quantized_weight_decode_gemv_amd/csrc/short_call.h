@@ -46,6 +46,10 @@ hipError_t launch_q4k_short(const GemvArgs &a, const ShortState &st, bool tiled,
 bool q4k_rows_fits(int nb);
 hipError_t launch_q4k_rows(const GemvArgs &a, bool tiled, hipStream_t s);
 // Row-group kernel for IQ3 (any layout, rows of nb <= 24 blocks), the same scheme.
+// Bytes per block of the IQ3 tile layout (qwg_pack_iq3_tiles): the 98-byte
+// block's fields regrouped, with the sign bit that each group's even-count
+// rule implies written out (32 more bits per block).
+constexpr int kIq3TileBlock = 102;
 bool iq3_rows_fits(int nb);
 hipError_t launch_iq3_rows(const GemvArgs &a, const float *grid, hipStream_t s);
 // IQ3 (a.layout: rows, llama.cpp-order rows or tiles), the same plan rule.

@@ -84,9 +84,9 @@ def test_tiled_bytes(L):
     assert L.qwg_tiled_bytes(0, 2048, 2048) == 2048 * 1152
     assert L.qwg_tiled_bytes(0, 2048, 65) == 128 * 1152      # rows rounded up to whole tiles
     assert L.qwg_tiled_bytes(0, 5632, 1) == 64 * 3168
-    assert L.qwg_tiled_bytes(1, 2048, 64) == 64 * 8 * 98
-    assert L.qwg_tiled_bytes(1, 2048, 65) == 128 * 8 * 98
-    assert L.qwg_tiled_bytes(2, 2048, 65) == 128 * 8 * 98
+    assert L.qwg_tiled_bytes(1, 2048, 64) == 64 * 8 * 102     # IQ3: the implied signs written out
+    assert L.qwg_tiled_bytes(1, 2048, 65) == 128 * 8 * 102
+    assert L.qwg_tiled_bytes(2, 2048, 65) == 128 * 8 * 102
     assert L.qwg_tiled_bytes(3, 2048, 65) == 128 * 8 * 110
     assert L.qwg_tiled_bytes(4, 512, 1) == 64 * 2 * 136
     assert L.qwg_tiled_bytes(5, 2048, 64) == -6

@@ -1033,19 +1033,39 @@ def test_q4k_group_many_items_repeat_runs(tiled):
 
 # ---------------------------------------------------------------- IQ3 tile layout
 
+def _sign_bytes(words: np.ndarray) -> np.ndarray:
+    """Each 32-bit sign/scale word -> its four groups of eight signs as bytes:
+    the seven stored bits, then the eighth that makes the count of set bits
+    even (the container's sign rule)."""
+    out = np.zeros(words.shape, np.uint32)
+    for k in range(4):
+        g = (words >> np.uint32(7 * k)) & np.uint32(0x7F)
+        odd = np.zeros_like(g)
+        for bit in range(7):
+            odd ^= (g >> np.uint32(bit)) & np.uint32(1)
+        out |= (g | (odd << np.uint32(7))) << np.uint32(8 * k)
+    return out
+
+
 def _iq3_tile_layout(w: np.ndarray, n_in: int) -> np.ndarray:
     """The IQ3 tile layout written out: per (tile, block column), index bytes
-    [G][row][16], words [G][row][8], d [row][2]; rows past n_out as zero blocks."""
+    [G][row][16], sign bytes [G][row][8] (words 2G, 2G+1 as eight signs per
+    byte), scales [G][row] (word 2G's in the low nibble, 2G+1's in the high
+    one), d [row][2]; rows past n_out as zero blocks."""
     n_out, nb = w.shape[0], n_in // 256
     tiles = (n_out + 63) // 64
     blk = np.zeros((tiles * 64, nb, 98), np.uint8)
     blk[:n_out] = w.reshape(n_out, nb, 98)
     blk = blk.reshape(tiles, 64, nb, 98).transpose(0, 2, 1, 3)       # [t][b][row][98]
     idx = blk[..., :64].reshape(tiles, nb, 64, 4, 16).transpose(0, 1, 3, 2, 4)
-    words = blk[..., 64:96].reshape(tiles, nb, 64, 4, 8).transpose(0, 1, 3, 2, 4)
+    words = np.ascontiguousarray(blk[..., 64:96]).view("<u4")       # [t][b][row][8]
+    signs = _sign_bytes(words).view(np.uint8).reshape(tiles, nb, 64, 4, 8).transpose(0, 1, 3, 2, 4)
+    code = (words >> np.uint32(28)).astype(np.uint8)
+    scales = (code[..., 0::2] | (code[..., 1::2] << 4)).transpose(0, 1, 3, 2)   # [t][b][G][row]
     d = blk[..., 96:98]
-    return np.concatenate([idx.reshape(tiles, nb, -1), words.reshape(tiles, nb, -1),
-                           d.reshape(tiles, nb, -1)], axis=2).reshape(-1)
+    return np.concatenate([idx.reshape(tiles, nb, -1), signs.reshape(tiles, nb, -1),
+                           scales.reshape(tiles, nb, -1), d.reshape(tiles, nb, -1)],
+                          axis=2).reshape(-1)
 
 
 @pytest.mark.parametrize("n_out,n_in", [(1, 256), (64, 512), (65, 768), (300, 2048), (2048, 5632)])
