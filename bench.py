@@ -892,11 +892,12 @@ def bench_codebooks(args):
 # 4 multiplies + 3 adds (q.g), a doubling and a subtract (g2 - 2 q.g), a
 # compare and two selects (the running minimum) = 12 operations.
 ENCODE_OPS_PER_WEIGHT = 16 * 256 * 12 / 4
-# 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz: a wave64 fp32 instruction issues in
-# two cycles on MI355X (the vendor's 157.3 TFLOP/s fp32 vector figure is this
-# rate counting an FMA as two; the encoder itself sustains 0.45 wave64
-# instructions per SIMD-cycle, more than a four-cycle issue allows). Its
-# search uses no packed or fused forms.
+# 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz: a two-operand wave64 fp32 instruction
+# issues in two cycles on MI355X (the vendor's 157.3 TFLOP/s fp32 vector figure
+# is this rate counting an FMA as two; the encoder, whose search is multiplies,
+# adds, compares and selects with no packed or fused forms, sustains 0.45
+# wave64 instructions per SIMD-cycle). Three-operand forms (FMA, v_perm) take
+# about four cycles, so this peak is the encoder's, not the GEMV dots'.
 VALU_PEAK_OPS = 256 * 4 * 32 * 2.4e9
 
 
