@@ -34,7 +34,7 @@ the headline, in GB/s; roofline = the same bytes / the chain kernel's average
 duration from HIP events on its stream around the timed loop.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--headline-only]
-       python bench.py --workload iq3_stream|iq3_xxs|codebooks|encode|lm_head|batched|gemm_ab [--steps K] [--warmup W]
+       python bench.py --workload iq3_stream|iq3_xxs|codebooks|encode|lm_head|batched|gemm_ab|dequant [--steps K] [--warmup W]
 The second form measures the other hot-path rows on their own (one JSON line each, for the
 record and for profiling): "iq3_stream" = the same 155 GEMV shapes in the IQ3 container as one
 grouped launch (IQ3 tile layout; the row-major launch beside it); "iq3_xxs" = IQ3_XXS blocks in
@@ -46,7 +46,9 @@ copies that every launch streams from HBM rather than the last-level cache; "bat
 per-token stream for 2, 4 and 8 sequences as one batched group launch; "gemm_ab" = an A/B of
 the batched-GEMM engines (matrix-core pipeline with one or two columns per stage, the persistent
 matrix-core stream, the vector-ALU engine with 4, 8 or 16 wavefronts per tile, and the automatic
-choice) at batch 2..8 on the LM head and the layer shapes, cold weights.
+choice) at batch 2..8 on the LM head and the layer shapes, cold weights; "dequant" =
+dequant_q4k and dequant_iq3 of the 32000x2048 LM-head matrix to fp32 (write-bound: 262 MB
+written per call), checked bit for bit against the oracle's decode before timing.
 """
 from __future__ import annotations
 
@@ -100,7 +102,7 @@ def parse():
                     help="print the hash of the kernel sources the traffic figure is tied to")
     ap.add_argument("--workload", default="q4k_stream",
                     choices=["q4k_stream", "configs", "iq3_stream", "iq3_xxs", "codebooks", "encode",
-                             "lm_head", "batched", "gemm_ab"],
+                             "lm_head", "batched", "gemm_ab", "dequant"],
                     help="q4k_stream: the headline (default); the others: see the module docstring")
     ap.add_argument("--headline-only", action="store_true",
                     help="run and time only the headline launch (no other schedules, no "
@@ -159,6 +161,9 @@ def main():
         return
     if args.workload == "gemm_ab":
         bench_gemm_ab(args)
+        return
+    if args.workload == "dequant":
+        bench_dequant(args)
         return
 
     import numpy as np
@@ -815,6 +820,61 @@ def bench_iq3_xxs(args):
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "kernel": "iq3_stream_kernel<8,2,tile layout> (grouped)",
                      "kernel_us": round(us, 2)}}), flush=True)
+
+
+def bench_dequant(args):
+    """dequant_q4k and dequant_iq3 (whole blocks to fp32, row-major) over the
+    32000 x 2048 LM-head matrix: write-bound (1,024 bytes written per 144- or
+    98-byte block). The outputs of one call into NaN-filled buffers are checked
+    bit for bit against the oracle's decode before anything is timed."""
+    import numpy as np
+    import torch
+    import quantized_weight_decode_gemv_amd as qwg
+    from quantized_weight_decode_gemv_amd import synth
+    import oracle
+
+    oracle.build(force=False)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    p = synth.config(3)[0]
+    n = p.n_out * p.n_in
+    grid_np = synth.iq3_grid()
+    grid = torch.from_numpy(grid_np).to(dev)
+    cases = {"q4k": (synth.weights(p), 144, lambda w, o: qwg.dequant_q4k(w, out=o),
+                     lambda w: oracle.dequant_q4k(w, n)),
+             "iq3": (synth.iq3_weights(p.n_out, p.n_in, p.cfg, p.tensor), 98,
+                     lambda w, o: qwg.dequant_iq3(w, grid, out=o),
+                     lambda w: oracle.dequant_iq3(w, grid_np, n))}
+    res = {}
+    for name, (w, block, call, ref) in cases.items():
+        wd = torch.from_numpy(w).to(dev)
+        out = torch.full((n,), float("nan"), device=dev)
+        call(wd, out)
+        torch.cuda.synchronize()
+        bad = int(np.count_nonzero(host_bits(out) != ref(w).reshape(-1).view(np.uint32)))
+        if bad:
+            raise SystemExit(f"dequant_{name}: {bad} values differ from the oracle's decode")
+        us = _event_us(lambda: call(wd, out), stream, args.steps, args.warmup)
+        nbytes = (n // 256) * (block + 1024)
+        res[name] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+                     "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                     "bytes_per_call": nbytes, "bit_mismatches": bad}
+        del wd, out
+    print(json.dumps({
+        "metric": "dequant to fp32, effective HBM GB/s (bytes read + written)",
+        "value": res["q4k"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "qwg_dequant_q4k / qwg_dequant_iq3 of the 32000 x 2048 LM-head "
+                               "matrix (256,000 blocks -> 65,536,000 fp32 weights)", **res},
+        "roofline": {"bound": "hbm", "achieved": res["q4k"]["GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": res["q4k"]["frac_of_hbm_peak"],
+                     "kernel": "q4k_dequant_kernel", "kernel_us": res["q4k"]["us"]}}), flush=True)
+
+
+def host_bits(t):
+    """fp32 device tensor -> its bit patterns (uint32 numpy array)."""
+    return t.detach().cpu().numpy().reshape(-1).view("<u4")
 
 
 def bench_codebooks(args):

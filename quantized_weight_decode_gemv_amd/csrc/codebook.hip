@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void iq3s_dequant_kernel(const uint8_t *__rest
         o.y = __fmul_rn((sg & 2u) ? -g.y : g.y, eff);
         o.z = __fmul_rn((sg & 4u) ? -g.z : g.z, eff);
         o.w = __fmul_rn((sg & 8u) ? -g.w : g.w, eff);
-        *(float4 *)(dst + blk * kQK + 4 * lane) = o;
+        // written once: non-temporal, as the Q4_K dequant's stores
+        __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, (f32x4 *)(dst + blk * kQK + 4 * lane));
     }
 }
 
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__res
         o.y = __fmul_rn(table[(word >> (8 + sh)) & 15u], eff);
         o.z = __fmul_rn(table[(word >> (16 + sh)) & 15u], eff);
         o.w = __fmul_rn(table[(word >> (24 + sh)) & 15u], eff);
-        *(float4 *)(dst + blk * kQK + 32 * ib + 4 * m) = o;
+        __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, (f32x4 *)(dst + blk * kQK + 32 * ib + 4 * m));
     }
 }
 

@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void iq3_dequant_kernel(const uint8_t *__restr
         o.y = __fmul_rn(((s8 >> (t0 + 1)) & 1u) ? -g.y : g.y, db);
         o.z = __fmul_rn(((s8 >> (t0 + 2)) & 1u) ? -g.z : g.z, db);
         o.w = __fmul_rn(((s8 >> (t0 + 3)) & 1u) ? -g.w : g.w, db);
-        *(float4 *)(dst + blk * kQK + 4 * lane) = o;
+        // written once: non-temporal, as the Q4_K dequant's stores
+        __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, (f32x4 *)(dst + blk * kQK + 4 * lane));
     }
 }
 
