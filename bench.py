@@ -47,7 +47,7 @@ per-token stream for 2, 4 and 8 sequences as one batched group launch; "gemm_ab"
 the batched-GEMM engines (matrix-core pipeline with one or two columns per stage, the persistent
 matrix-core stream, the vector-ALU engine with 4, 8 or 16 wavefronts per tile, and the automatic
 choice) at batch 2..8 on the LM head and the layer shapes, cold weights; "dequant" =
-dequant_q4k and dequant_iq3 of the 32000x2048 LM-head matrix to fp32 (write-bound: 262 MB
+dequant_q4k, _iq3, _iq3s and _iq4xs of the 32000x2048 LM-head matrix to fp32 (write-bound: 262 MB
 written per call), checked bit for bit against the oracle's decode before timing.
 """
 from __future__ import annotations
@@ -823,9 +823,9 @@ def bench_iq3_xxs(args):
 
 
 def bench_dequant(args):
-    """dequant_q4k and dequant_iq3 (whole blocks to fp32, row-major) over the
-    32000 x 2048 LM-head matrix: write-bound (1,024 bytes written per 144- or
-    98-byte block). The outputs of one call into NaN-filled buffers are checked
+    """dequant_q4k, dequant_iq3, dequant_iq3s and dequant_iq4xs (whole blocks to
+    fp32, row-major) over the 32000 x 2048 LM-head matrix: write-bound (1,024
+    bytes written per 144-, 98-, 110- or 136-byte block). The outputs of one call into NaN-filled buffers are checked
     bit for bit against the oracle's decode before anything is timed."""
     import numpy as np
     import torch
@@ -841,11 +841,19 @@ def bench_dequant(args):
     n = p.n_out * p.n_in
     grid_np = synth.iq3_grid()
     grid = torch.from_numpy(grid_np).to(dev)
+    grid_s_np, table_np = synth.iq3s_grid(), synth.iq4nl_table()
+    grid_s, table = torch.from_numpy(grid_s_np).to(dev), torch.from_numpy(table_np).to(dev)
     cases = {"q4k": (synth.weights(p), 144, lambda w, o: qwg.dequant_q4k(w, out=o),
                      lambda w: oracle.dequant_q4k(w, n)),
              "iq3": (synth.iq3_weights(p.n_out, p.n_in, p.cfg, p.tensor), 98,
                      lambda w, o: qwg.dequant_iq3(w, grid, out=o),
-                     lambda w: oracle.dequant_iq3(w, grid_np, n))}
+                     lambda w: oracle.dequant_iq3(w, grid_np, n)),
+             "iq3s": (synth.iq3s_weights(p.n_out, p.n_in, p.cfg, p.tensor), 110,
+                      lambda w, o: qwg.dequant_iq3s(w, grid_s, out=o),
+                      lambda w: oracle.dequant_iq3s(w, grid_s_np, n)),
+             "iq4xs": (synth.iq4xs_weights(p.n_out, p.n_in, p.cfg, p.tensor), 136,
+                       lambda w, o: qwg.dequant_iq4xs(w, table, out=o),
+                       lambda w: oracle.dequant_iq4xs(w, table_np, n))}
     res = {}
     for name, (w, block, call, ref) in cases.items():
         wd = torch.from_numpy(w).to(dev)
@@ -865,7 +873,7 @@ def bench_dequant(args):
         "metric": "dequant to fp32, effective HBM GB/s (bytes read + written)",
         "value": res["q4k"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "higher_is_better": True, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "qwg_dequant_q4k / qwg_dequant_iq3 of the 32000 x 2048 LM-head "
+        "config": {"workload": "qwg_dequant_q4k / _iq3 / _iq3s / _iq4xs of the 32000 x 2048 LM-head "
                                "matrix (256,000 blocks -> 65,536,000 fp32 weights)", **res},
         "roofline": {"bound": "hbm", "achieved": res["q4k"]["GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": res["q4k"]["frac_of_hbm_peak"],
