@@ -62,6 +62,9 @@ __global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__res
     const int lane = threadIdx.x & 63;
     const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
     const int ib = lane >> 3, m = lane & 7;
+    // lane i holds value i % 16 of the table: a lookup is one cross-lane read
+    // instead of a second memory round trip after the code word
+    const float tv = table[lane & 15];
     for (int64_t blk = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
          blk < nblocks; blk += nwaves) {
         const uint8_t *b = src + blk * kIq4xsBytes;
@@ -73,10 +76,10 @@ __global__ __launch_bounds__(256) void iq4xs_dequant_kernel(const uint8_t *__res
         const uint32_t word = *(const uint32_t *)(b + 8 + 16 * ib + 4 * (m & 3));
         const uint32_t sh = m >= 4 ? 4u : 0u;
         float4 o;
-        o.x = __fmul_rn(table[(word >> sh) & 15u], eff);
-        o.y = __fmul_rn(table[(word >> (8 + sh)) & 15u], eff);
-        o.z = __fmul_rn(table[(word >> (16 + sh)) & 15u], eff);
-        o.w = __fmul_rn(table[(word >> (24 + sh)) & 15u], eff);
+        o.x = __fmul_rn(__shfl(tv, (int)((word >> sh) & 15u)), eff);
+        o.y = __fmul_rn(__shfl(tv, (int)((word >> (8 + sh)) & 15u)), eff);
+        o.z = __fmul_rn(__shfl(tv, (int)((word >> (16 + sh)) & 15u)), eff);
+        o.w = __fmul_rn(__shfl(tv, (int)((word >> (24 + sh)) & 15u)), eff);
         __builtin_nontemporal_store(f32x4{o.x, o.y, o.z, o.w}, (f32x4 *)(dst + blk * kQK + 32 * ib + 4 * m));
     }
 }
